@@ -1,0 +1,205 @@
+"""CPU oracle for D = act(alpha * op(A) * op(B) + beta * C + bias): TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may import this
+package.  The product path (the HIP library and its binding) never does, and shares no code
+with it.  The arithmetic lives in oracle.c (plain C, fp64 / int64); this module only marshals
+numpy arrays.
+
+What it computes (cited by page title and section):
+  * "CUTLASS: Fast Linear Algebra in CUDA C++", "Efficient Matrix Multiplication on GPUs":
+    C = alpha*A*B + beta*C, summed by the naive, k-outermost or tiled loop nest (order 0/1/2),
+    all with ascending k per element.
+  * same page, "Fusing Element-wise Operations": alpha*acc + bias + beta*c, then max(0, .).
+  * "Flexible Performant GEMM Kernels on GPUs", section 5.3: the bias vector is added to every
+    row (bias[j] for output column j).
+Readings where the pages are silent (all matrices row-major, op T = the stored array is the
+transpose, beta == 0 means C is not read, RNE to the output type) are stated in oracle.c.
+
+Raw operand formats (the exact bits a kernel receives): f32 -> numpy float32, f16 and bf16 ->
+numpy uint16 bit patterns, i8 -> int8, i32 -> int32.  Matrices are flat or 2-D C-contiguous
+arrays with an explicit leading dimension.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# ORACLE_LIB lets the mutation tests load a deliberately broken build of oracle.c
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+
+DT = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "f64": 5}
+RAW_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "i32": np.int32,
+          "f64": np.float64}
+ORDERS = {"ijk": 0, "kij": 1, "tiled": 2}
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, vp, dbl, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
+        L.oracle_decode_f64.argtypes = [ci, vp, i64, vp]
+        L.oracle_decode_i64.argtypes = [ci, vp, i64, vp]
+        L.oracle_round_to.argtypes = [ci, vp, i64, vp]
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f64.restype = dbl
+        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f64.restype = dbl
+        L.oracle_f64_to_f16.argtypes = [dbl]
+        L.oracle_f64_to_f16.restype = ctypes.c_uint16
+        L.oracle_f64_to_bf16.argtypes = [dbl]
+        L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        L.oracle_gather_f64.argtypes = [ci, i64, i64, vp, i64, vp]
+        L.oracle_gather_i64.argtypes = [ci, i64, i64, vp, i64, vp]
+        L.oracle_matmul_f64.argtypes = [ci, i64, i64, i64, vp, vp, vp, i64, i64, ci]
+        L.oracle_matmul_i64.argtypes = [ci, i64, i64, i64, vp, vp, vp, i64, i64, ci]
+        L.oracle_epilogue_f64.argtypes = [i64, i64, vp, dbl, vp, dbl, vp, ci, vp]
+        L.oracle_epilogue_i64.argtypes = [i64, i64, vp, i64, vp, i64, vp, ci, vp]
+        L.oracle_epilogue_i64.restype = ci
+        for name, acc in (("oracle_points_f64", dbl), ("oracle_points_i64", i64)):
+            getattr(L, name).argtypes = [i64, vp, vp, i64, ci, ci, ci, vp, i64, vp, i64, ci, vp, i64,
+                                         ci, vp, acc, acc, ci, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _raw(dtype, a):
+    a = np.ascontiguousarray(a)
+    want = RAW_NP[dtype]
+    if a.dtype != want:
+        if dtype in ("f16", "bf16") and a.dtype.itemsize == 2:
+            a = a.view(np.uint16)
+        else:
+            raise TypeError(f"raw {dtype} data must be {np.dtype(want)}, got {a.dtype}")
+    return a.reshape(-1)
+
+
+def is_int(dtype):
+    return dtype in ("i8", "i32")
+
+
+def decode(dtype, a):
+    """Exact value of every element: float64 for float types, int64 for integer types."""
+    shape = np.shape(a)
+    r = _raw(dtype, a)
+    if is_int(dtype):
+        out = np.empty(r.size, np.int64)
+        rc = lib().oracle_decode_i64(DT[dtype], _ptr(r), r.size, _ptr(out))
+    else:
+        out = np.empty(r.size, np.float64)
+        rc = lib().oracle_decode_f64(DT[dtype], _ptr(r), r.size, _ptr(out))
+    assert rc == 0
+    return out.reshape(shape)
+
+
+def round_to(dtype, x):
+    """Round exact float64 values to `dtype` (RNE); returns the raw array (uint16 bits for
+    f16/bf16, float32 for f32)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, RAW_NP[dtype])
+    assert lib().oracle_round_to(DT[dtype], _ptr(x), x.size, _ptr(out)) == 0
+    return out
+
+
+def _dense_op(op, rows, cols, X, ldx, integer):
+    """Dense rows x cols copy of op(X) from a decoded stored array X (flat, leading dim ldx)."""
+    out = np.empty(rows * cols, np.int64 if integer else np.float64)
+    if rows and cols:
+        f = lib().oracle_gather_i64 if integer else lib().oracle_gather_f64
+        f(1 if op == "T" else 0, rows, cols, _ptr(X), ldx, _ptr(out))
+    return out
+
+
+def _span(op, rows, cols, ld):
+    """Number of stored elements that op(X) (rows x cols) touches."""
+    if rows == 0 or cols == 0:
+        return 0
+    return (cols - 1) * ld + rows if op == "T" else (rows - 1) * ld + cols
+
+
+def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
+         bias_dt=None, alpha=1.0, beta=0.0, relu=False, order="tiled", rows=None, threads=None):
+    """Exact (unrounded) result rows x N of act(alpha*op(A)op(B) + beta*C + bias).
+
+    ab: input dtype; cd: C/D dtype; bias_dt: bias dtype (default f32, i32 for i8 inputs).
+    rows: optional (r0, r1) to compute only those output rows.  Returns float64, or int64
+    when the inputs are int8."""
+    integer = is_int(ab)
+    r0, r1 = (0, M) if rows is None else rows
+    mr = r1 - r0
+    threads = threads or os.cpu_count() or 1
+    Ar, Br = _raw(ab, A), _raw(ab, B)
+    # decode only the stored rows that op(A)[r0:r1] touches
+    if op_a == "N":
+        Asub = Ar[r0 * lda: r0 * lda + _span("N", mr, K, lda)]
+    else:
+        Asub = Ar[r0: r0 + _span("T", mr, K, lda)]
+    Ad = decode(ab, Asub)
+    Bd = decode(ab, Br[: _span(op_b, K, N, ldb)])
+    Aop = _dense_op(op_a, mr, K, Ad, lda, integer)
+    Bop = _dense_op(op_b, K, N, Bd, ldb, integer)
+    acc = np.zeros(mr * N, np.int64 if integer else np.float64)
+    if mr and N and K:
+        f = lib().oracle_matmul_i64 if integer else lib().oracle_matmul_f64
+        assert f(ORDERS[order], mr, N, K, _ptr(Aop), _ptr(Bop), _ptr(acc), 0, mr, threads) == 0
+    Cd = None
+    if beta != 0:
+        Cr = _raw(cd, C)
+        Cd = np.empty(mr * N, np.int64 if integer else np.float64)
+        for i in range(mr):
+            Cd[i * N:(i + 1) * N] = decode(cd, Cr[(r0 + i) * ldc:(r0 + i) * ldc + N])
+    bd = None
+    if bias is not None:
+        bias_dt = bias_dt or ("i32" if integer else "f32")
+        bd = decode(bias_dt, _raw(bias_dt, bias)[:N])
+    out = np.empty(mr * N, np.int64 if integer else np.float64)
+    if integer:
+        assert float(alpha) == int(alpha) and float(beta) == int(beta)
+        lib().oracle_epilogue_i64(mr, N, _ptr(acc), int(alpha), _ptr(Cd), int(beta), _ptr(bd),
+                                  1 if relu else 0, _ptr(out))
+    else:
+        lib().oracle_epilogue_f64(mr, N, _ptr(acc), float(alpha), _ptr(Cd), float(beta),
+                                  _ptr(bd), 1 if relu else 0, _ptr(out))
+    return out.reshape(mr, N)
+
+
+def points(ii, jj, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=0, cd="f32", bias=None,
+           bias_dt=None, alpha=1.0, beta=0.0, relu=False):
+    """Exact result at the output points (ii[p], jj[p]), straight from the raw stored operands
+    (naive ascending-k sum per point)."""
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    integer = is_int(ab)
+    Ar, Br = _raw(ab, A), _raw(ab, B)
+    Cr = _raw(cd, C) if (C is not None and beta != 0) else None
+    bias_dt = bias_dt or ("i32" if integer else "f32")
+    br = _raw(bias_dt, bias) if bias is not None else None
+    out = np.empty(ii.size, np.int64 if integer else np.float64)
+    f = lib().oracle_points_i64 if integer else lib().oracle_points_f64
+    conv = int if integer else float
+    f(ii.size, _ptr(ii), _ptr(jj), K, 1 if op_a == "T" else 0, 1 if op_b == "T" else 0, DT[ab],
+      _ptr(Ar), lda, _ptr(Br), ldb, DT[cd], _ptr(Cr), ldc, DT[bias_dt], _ptr(br), conv(alpha),
+      conv(beta), 1 if relu else 0, _ptr(out))
+    return out
+
+
+def max_abs_op(dtype, X, op, rows, cols, ld):
+    """max |op(X)| over the decoded elements op(X) uses (the tolerance's normaliser)."""
+    if rows == 0 or cols == 0:
+        return 0.0
+    d = decode(dtype, _raw(dtype, X)[: _span(op, rows, cols, ld)])
+    if op == "N":
+        idx_ok = (np.arange(d.size) % ld) < cols
+    else:
+        idx_ok = (np.arange(d.size) % ld) < rows
+    return float(np.max(np.abs(d[idx_ok]))) if idx_ok.any() else 0.0

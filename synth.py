@@ -1,0 +1,222 @@
+"""Seeded synthetic inputs for the fused-epilogue GEMM: shared by the tests, the smoke check and
+the benchmark.  This module only draws and stores numbers; it holds none of the GEMM's
+arithmetic, and neither the HIP path nor the oracle imports it.
+
+Every draw comes from numpy's PCG64 seeded by SeedSequence([workload id, shape index, operand
+id]) with operand ids A=0, B=1, C=2, bias=3.  A logical op(A) (M x K) and op(B) (K x N) are drawn
+once per shape and then stored in the requested physical layout, so all four N/T layouts of one
+shape hold the same logical problem.  Float values are drawn in float64 and quantised once to
+the storage type with round-to-nearest-even; the raw arrays (uint16 bit patterns for f16 and
+bf16) are exactly what both the GPU and the oracle receive.  Leading dimensions are tight
+unless a padded ld is asked for.
+"""
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+RAW_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "i32": np.int32}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4}
+
+
+def rng(*key):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def quantize(dtype, x):
+    """float64 values -> raw storage array of `dtype` (RNE)."""
+    x = np.asarray(x)
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float32).astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        # float64 -> float32 (RNE), then float32 -> bfloat16 by rounding the 32-bit pattern to
+        # its upper 16 bits, ties to even (inputs here are finite).
+        u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+        u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        return u.astype(np.uint16)
+    if dtype in ("i8", "i32"):
+        return x.astype(RAW_NP[dtype])
+    raise ValueError(dtype)
+
+
+def draw(g, dist, n):
+    kind = dist[0]
+    if kind == "uniform":
+        return g.uniform(dist[1], dist[2], n)
+    if kind == "normal":
+        return g.standard_normal(n) * dist[1]
+    if kind == "int":          # integers in [lo, hi] inclusive
+        return g.integers(dist[1], dist[2], n, endpoint=True).astype(np.float64)
+    raise ValueError(kind)
+
+
+@dataclass
+class Problem:
+    M: int
+    N: int
+    K: int
+    op_a: str = "N"
+    op_b: str = "N"
+    ab: str = "f16"
+    cd: str = "f16"
+    epi: str = "none"            # none | relu | bias | bias_relu
+    alpha: float = 1.0
+    beta: float = 0.0
+    lda: int = 0                 # 0 -> tight
+    ldb: int = 0
+    ldc: int = 0
+    a_dist: tuple = ("uniform", -1.0, 1.0)
+    b_dist: tuple = ("uniform", -1.0, 1.0)
+    c_dist: tuple = ("uniform", -1.0, 1.0)
+    bias_dist: tuple = ("uniform", -0.5, 0.5)
+    key: tuple = (0, 0)
+    name: str = ""
+
+    def __post_init__(self):
+        if not self.lda:
+            self.lda = max(1, self.K if self.op_a == "N" else self.M)
+        if not self.ldb:
+            self.ldb = max(1, self.N if self.op_b == "N" else self.K)
+        if not self.ldc:
+            self.ldc = max(1, self.N)
+
+    @property
+    def bias_dt(self):
+        return "i32" if self.ab == "i8" else "f32"
+
+    @property
+    def has_bias(self):
+        return self.epi in ("bias", "bias_relu")
+
+    @property
+    def relu(self):
+        return self.epi in ("relu", "bias_relu")
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def a_shape(self):   # stored 2-D shape (rows, ld)
+        return (self.M, self.lda) if self.op_a == "N" else (self.K, self.lda)
+
+    def b_shape(self):
+        return (self.K, self.ldb) if self.op_b == "N" else (self.N, self.ldb)
+
+    def algorithmic_bytes(self):
+        """Compulsory HBM traffic: op(A), op(B) read once, C if beta != 0, bias, D written once."""
+        eb, ec = ELEM_BYTES[self.ab], ELEM_BYTES[self.cd]
+        b = (self.M * self.K + self.K * self.N) * eb + self.M * self.N * ec
+        if self.beta != 0:
+            b += self.M * self.N * ec
+        if self.has_bias:
+            b += self.N * 4
+        return b
+
+    def label(self):
+        return (f"{self.name or 'gemm'}:{self.M}x{self.N}x{self.K}:{self.op_a}{self.op_b}:"
+                f"{self.ab}->{self.cd}:{self.epi}:a{self.alpha:g}b{self.beta:g}")
+
+
+def _store(logical, op, ld, fill):
+    """Store a logical rows x cols matrix as a row-major array with leading dim ld (op N) or its
+    transpose (op T).  Padding columns hold `fill`."""
+    rows, cols = logical.shape
+    if op == "N":
+        out = np.full((rows, ld), fill, dtype=logical.dtype)
+        out[:, :cols] = logical
+    else:
+        out = np.full((cols, ld), fill, dtype=logical.dtype)
+        out[:, :rows] = logical.T
+    return out
+
+
+def make_inputs(p: Problem, pad_fill=0):
+    """Raw stored arrays {A, B, C, bias} (C and bias None when unused) for problem p."""
+    cfg, shp = p.key
+    ga, gb, gc, gbias = (rng(cfg, shp, i) for i in range(4))
+    a = quantize(p.ab, draw(ga, p.a_dist, p.M * p.K)).reshape(p.M, p.K)
+    b = quantize(p.ab, draw(gb, p.b_dist, p.K * p.N)).reshape(p.K, p.N)
+    A = _store(a, p.op_a, p.lda, pad_fill)
+    B = _store(b, p.op_b, p.ldb, pad_fill)
+    C = None
+    if p.beta != 0:
+        c = quantize(p.cd, draw(gc, p.c_dist, p.M * p.N)).reshape(p.M, p.N)
+        C = _store(c, "N", p.ldc, pad_fill)
+    bias = quantize(p.bias_dt, draw(gbias, p.bias_dist, p.N)) if p.has_bias else None
+    return {"A": A, "B": B, "C": C, "bias": bias}
+
+
+# ---- the workloads ---------------------------------------------------------------------------
+
+def sgemm_256():
+    """fp32 256^3, NN, alpha=1, beta=0, A,B ~ U[-1,1], no epilogue."""
+    return [Problem(256, 256, 256, "N", "N", "f32", "f32", "none", 1.0, 0.0, key=(1, 0),
+                    name="sgemm_256")]
+
+
+def fp16_8192_bias_relu():
+    """fp16 8192^3 NN, A,B ~ N(0,1)/sqrt(K), C absent (beta=0), D = ReLU(acc + bias[N]) -> fp16,
+    bias fp32 ~ U[-0.5,0.5]."""
+    K = 8192
+    s = 1.0 / math.sqrt(K)
+    return [Problem(8192, 8192, K, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                    a_dist=("normal", s), b_dist=("normal", s), key=(2, 0),
+                    name="fp16_8192_bias_relu")]
+
+
+def bf16_layout_sweep():
+    """bf16 in, fp32 C/D, alpha=1.5, beta=-0.5, A,B,C ~ U[-1,1], NN/NT/TN/TT on the ragged
+    shapes 4095x3073x2047 and 5000^3."""
+    out = []
+    for si, (M, N, K) in enumerate([(4095, 3073, 2047), (5000, 5000, 5000)]):
+        for la in "NT":
+            for lb in "NT":
+                out.append(Problem(M, N, K, la, lb, "bf16", "f32", "none", 1.5, -0.5,
+                                   key=(3, si), name="bf16_layout_sweep"))
+    return out
+
+
+def int8_4096_bias():
+    """int8 4096^3 NN, A,B integers in [-128,127], int32 accumulate, D = acc + bias_i32[N],
+    bias ~ integers in [-2^20, 2^20]."""
+    return [Problem(4096, 4096, 4096, "N", "N", "i8", "i32", "bias", 1.0, 0.0,
+                    a_dist=("int", -128, 127), b_dist=("int", -128, 127),
+                    bias_dist=("int", -(1 << 20), 1 << 20), key=(4, 0), name="int8_4096_bias")]
+
+
+def fc_layers(layouts=("NN",)):
+    """Fully-connected shapes, fp16 in / fp32 acc / fp16 out with bias+ReLU: activations A ~
+    N(0,1), weights B ~ N(0,1/K), bias fp32 ~ U[-0.5,0.5]."""
+    out = []
+    for si, (M, N, K) in enumerate([(16, 4096, 4096), (8192, 16384, 4096), (8192, 4096, 16384)]):
+        for lay in layouts:
+            out.append(Problem(M, N, K, lay[0], lay[1], "f16", "f16", "bias_relu", 1.0, 0.0,
+                               a_dist=("normal", 1.0), b_dist=("normal", 1.0 / math.sqrt(K)),
+                               key=(5, si), name="fc_layers"))
+    return out
+
+
+WORKLOADS = {
+    "sgemm_256": sgemm_256,
+    "fp16_8192_bias_relu": fp16_8192_bias_relu,
+    "bf16_layout_sweep": bf16_layout_sweep,
+    "int8_4096_bias": int8_4096_bias,
+    "fc_layers": fc_layers,
+}
+
+
+def exact_integer_problem(M, N, K, op_a, op_b, ab, cd, epi, alpha, beta, key, ld_pad=0):
+    """Inputs whose every partial sum is an integer of magnitude <= 16*K + small, so fp32
+    accumulation (any order) and the fp32 epilogue are exact whenever 16*K < 2^24 and alpha,
+    beta are small powers of two: A,B integers in [-4,4], C integers in [-8,8], bias integers in
+    [-8,8]."""
+    p = Problem(M, N, K, op_a, op_b, ab, cd, epi, alpha, beta,
+                a_dist=("int", -4, 4), b_dist=("int", -4, 4), c_dist=("int", -8, 8),
+                bias_dist=("int", -8, 8), key=key, name="exact_int")
+    if ld_pad:
+        p.lda += ld_pad
+        p.ldb += ld_pad
+        p.ldc += ld_pad
+    return p

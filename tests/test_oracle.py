@@ -1,0 +1,279 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself: IEEE format
+definitions (exhaustive decoder checks against numpy / torch), library products on tiny inputs,
+loop-order invariance, identities, the transpose law (AB)^T = B^T A^T, alpha/beta linearity and
+a hand-worked epilogue instance."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---- decoders and rounding --------------------------------------------------------------------
+
+def test_f16_decoder_exhaustive():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode("f16", bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decoder_exhaustive():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode("bf16", bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def _finite_patterns(dtype):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = oracle.decode(dtype, bits)
+    keep = np.isfinite(v)
+    return bits[keep], v[keep]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_round_is_inverse_of_decode(dtype):
+    bits, v = _finite_patterns(dtype)
+    assert np.array_equal(oracle.round_to(dtype, v), bits)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_round_ties_to_even_and_neighbours(dtype):
+    # positive finite values in increasing order: every midpoint goes to the even pattern and
+    # points just off the midpoint go to the nearer neighbour
+    bits, v = _finite_patterns(dtype)
+    pos = (v > 0)
+    b, x = bits[pos], v[pos]
+    order = np.argsort(x)
+    b, x = b[order], x[order]
+    lo, hi, blo, bhi = x[:-1], x[1:], b[:-1], b[1:]
+    mid = (lo + hi) / 2                       # exact in float64
+    got = oracle.round_to(dtype, mid)
+    even = np.where((blo & 1) == 0, blo, bhi)
+    assert np.array_equal(got, even)
+    eps = (hi - lo) * 1e-6
+    assert np.array_equal(oracle.round_to(dtype, mid - eps), blo)
+    assert np.array_equal(oracle.round_to(dtype, mid + eps), bhi)
+
+
+def test_f16_round_matches_numpy_random():
+    g = np.random.default_rng(7)
+    x = np.concatenate([g.standard_normal(200000) * 10.0 ** g.integers(-9, 6, 200000),
+                        g.uniform(-70000, 70000, 10000)])
+    assert np.array_equal(oracle.round_to("f16", x), x.astype(np.float16).view(np.uint16))
+
+
+def test_bf16_round_matches_torch_on_float32_values():
+    g = np.random.default_rng(8)
+    x = (g.standard_normal(200000) * 10.0 ** g.integers(-30, 30, 200000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round_to("bf16", x.astype(np.float64)), ref)
+
+
+def test_round_overflow_and_signed_zero():
+    r = oracle.round_to("f16", np.array([65504.0, 65519.99, 65520.0, -1e9, -0.0, 2.0 ** -26]))
+    assert list(r) == [0x7BFF, 0x7BFF, 0x7C00, 0xFC00, 0x8000, 0x0000]
+
+
+# ---- the product ------------------------------------------------------------------------------
+
+def _random_problem(g, M, N, K, la, lb, integer, pad=0):
+    lda = (K if la == "N" else M) + pad
+    ldb = (N if lb == "N" else K) + pad
+    if integer:
+        X = g.integers(-128, 128, (M, K)).astype(np.int8)
+        Y = g.integers(-128, 128, (K, N)).astype(np.int8)
+    else:
+        X = g.uniform(-1, 1, (M, K)).astype(np.float32)
+        Y = g.uniform(-1, 1, (K, N)).astype(np.float32)
+    A = np.zeros((M, lda) if la == "N" else (K, lda), X.dtype)
+    B = np.zeros((K, ldb) if lb == "N" else (N, ldb), Y.dtype)
+    if la == "N":
+        A[:, :K] = X
+    else:
+        A[:, :M] = X.T
+    if lb == "N":
+        B[:, :N] = Y
+    else:
+        B[:, :K] = Y.T
+    return X, Y, A, lda, B, ldb
+
+
+@pytest.mark.parametrize("shape", [(64, 48, 80), (37, 53, 129)])
+@pytest.mark.parametrize("ab", ["f32", "i8"])
+def test_loop_orders_bit_identical(shape, ab):
+    M, N, K = shape
+    g = np.random.default_rng(11)
+    X, Y, A, lda, B, ldb = _random_problem(g, M, N, K, "N", "N", ab == "i8")
+    outs = [oracle.gemm(M, N, K, "N", "N", A, lda, B, ldb, ab, order=o, threads=t)
+            for o in ("ijk", "kij", "tiled") for t in (1, 3)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+def test_brute_force_tiny_against_numpy(lay):
+    g = np.random.default_rng(12)
+    for M in (1, 2, 3):
+        for N in (1, 2, 3):
+            for K in (1, 2, 3):
+                # int8 in {-2..2}: exact in int64
+                X = g.integers(-2, 3, (M, K)).astype(np.int8)
+                Y = g.integers(-2, 3, (K, N)).astype(np.int8)
+                A = X if lay[0] == "N" else np.ascontiguousarray(X.T)
+                B = Y if lay[1] == "N" else np.ascontiguousarray(Y.T)
+                lda = A.shape[1]
+                ldb = B.shape[1]
+                got = oracle.gemm(M, N, K, lay[0], lay[1], A, lda, B, ldb, "i8")
+                assert np.array_equal(got, X.astype(np.int64) @ Y.astype(np.int64))
+                # float32 inputs: K <= 3 products of float32 values are exact in float64 and
+                # the sum of <= 3 such products differs from numpy's only by summation order,
+                # so compare to an expansion that adds in ascending k
+                Xf = g.uniform(-1, 1, (M, K)).astype(np.float32)
+                Yf = g.uniform(-1, 1, (K, N)).astype(np.float32)
+                A = Xf if lay[0] == "N" else np.ascontiguousarray(Xf.T)
+                B = Yf if lay[1] == "N" else np.ascontiguousarray(Yf.T)
+                got = oracle.gemm(M, N, K, lay[0], lay[1], A, A.shape[1], B, B.shape[1], "f32")
+                ref = np.zeros((M, N))
+                for k in range(K):
+                    ref = ref + np.outer(Xf[:, k].astype(np.float64), Yf[k, :].astype(np.float64))
+                assert np.array_equal(got, ref)
+                np.testing.assert_allclose(got, Xf.astype(np.float64) @ Yf.astype(np.float64),
+                                           rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+def test_layouts_against_numpy_with_padded_ld(lay):
+    g = np.random.default_rng(13)
+    for (M, N, K) in [(5, 7, 3), (1, 9, 4), (8, 1, 6), (6, 6, 1), (13, 11, 17)]:
+        X, Y, A, lda, B, ldb = _random_problem(g, M, N, K, lay[0], lay[1], True, pad=3)
+        got = oracle.gemm(M, N, K, lay[0], lay[1], A, lda, B, ldb, "i8")
+        assert np.array_equal(got, X.astype(np.int64) @ Y.astype(np.int64))
+
+
+def test_identity_and_zero():
+    g = np.random.default_rng(14)
+    M = K = N = 24
+    X = g.uniform(-1, 1, (M, K)).astype(np.float32)
+    I = np.eye(K, dtype=np.float32)
+    assert np.array_equal(oracle.gemm(M, N, K, "N", "N", X, K, I, N, "f32"), X.astype(np.float64))
+    assert np.array_equal(oracle.gemm(M, N, K, "N", "N", I, K, X, N, "f32"), X.astype(np.float64))
+    Z = np.zeros((M, K), np.float32)
+    C = g.uniform(-1, 1, (M, N)).astype(np.float32)
+    bias = g.uniform(-1, 1, N).astype(np.float32)
+    got = oracle.gemm(M, N, K, "N", "N", Z, K, X, N, "f32", C=C, ldc=N, cd="f32", bias=bias,
+                      alpha=3.0, beta=0.5, relu=False)
+    assert np.array_equal(got, 0.5 * C.astype(np.float64) + bias.astype(np.float64)[None, :])
+
+
+@pytest.mark.parametrize("ab", ["f32", "i8"])
+def test_transpose_law(ab):
+    # (XY)^T = Y^T X^T: the TT problem on the same stored arrays gives the transpose bit for bit
+    g = np.random.default_rng(15)
+    M, N, K = 29, 41, 67
+    X, Y, A, lda, B, ldb = _random_problem(g, M, N, K, "N", "N", ab == "i8")
+    R = oracle.gemm(M, N, K, "N", "N", A, lda, B, ldb, ab)
+    RT = oracle.gemm(N, M, K, "T", "T", B, ldb, A, lda, ab)
+    assert np.array_equal(RT, R.T)
+
+
+def test_alpha_beta_linearity():
+    g = np.random.default_rng(16)
+    M, N, K = 33, 21, 45
+    X, Y, A, lda, B, ldb = _random_problem(g, M, N, K, "T", "N", False)
+    C = g.uniform(-1, 1, (M, N)).astype(np.float32)
+    base = oracle.gemm(M, N, K, "T", "N", A, lda, B, ldb, "f32")
+    got = oracle.gemm(M, N, K, "T", "N", A, lda, B, ldb, "f32", C=C, ldc=N, cd="f32",
+                      alpha=1.5, beta=-0.5)
+    np.testing.assert_allclose(got, 1.5 * base - 0.5 * C.astype(np.float64), rtol=1e-15, atol=1e-15)
+
+
+def test_epilogue_hand_worked_instance():
+    d = json.load(open(os.path.join(GOLDEN, "epilogue_2x2.json")))
+    A = np.array(d["A"], np.float32)
+    B = np.array(d["B"], np.float32)
+    C = np.array(d["C"], np.float32)
+    bias = np.array(d["bias"], np.float32)
+    M, N, K = d["M"], d["N"], d["K"]
+    common = dict(C=C, ldc=N, cd="f32", alpha=d["alpha"], beta=d["beta"])
+    got = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "f32", bias=bias, relu=False, **common)
+    assert np.array_equal(got, np.array(d["expected_none"]))
+    got = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "f32", bias=bias, relu=True, **common)
+    assert np.array_equal(got, np.array(d["expected_relu"]))
+    got = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "f32", relu=True, **common)
+    assert np.array_equal(got, np.array(d["expected_no_bias_relu"]))
+
+
+def test_bias_is_per_column_and_beta_zero_ignores_c():
+    M, N, K = 5, 7, 3
+    A = np.zeros((M, K), np.float32)
+    B = np.ones((K, N), np.float32)
+    bias = np.arange(N, dtype=np.float32) - 3
+    C = np.full((M, N), np.nan, np.float32)
+    got = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "f32", C=C, ldc=N, cd="f32", bias=bias,
+                      alpha=1.0, beta=0.0, relu=True)
+    assert np.array_equal(got, np.tile(np.maximum(bias.astype(np.float64), 0), (M, 1)))
+
+
+def test_int8_full_range_exact():
+    g = np.random.default_rng(17)
+    M, N, K = 16, 16, 512
+    A = np.full((M, K), -128, np.int8)
+    B = np.full((K, N), -128, np.int8)
+    bias = g.integers(-(1 << 20), (1 << 20) + 1, N).astype(np.int32)
+    got = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "i8", bias=bias)
+    assert np.array_equal(got, np.full((M, N), 128 * 128 * K, np.int64) + bias.astype(np.int64))
+
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("bf16", "f32"), ("i8", "i32")])
+def test_points_equal_full_result(lay, ab, cd):
+    p = synth.Problem(37, 45, 70, lay[0], lay[1], ab, cd, "bias_relu" if ab != "i8" else "bias",
+                      1.5 if ab != "i8" else 1.0, -0.5 if ab != "i8" else 1.0, key=(99, 1),
+                      a_dist=("int", -100, 100) if ab == "i8" else ("uniform", -1, 1),
+                      b_dist=("int", -100, 100) if ab == "i8" else ("uniform", -1, 1),
+                      c_dist=("int", -1000, 1000) if ab == "i8" else ("uniform", -1, 1),
+                      bias_dist=("int", -1000, 1000) if ab == "i8" else ("uniform", -0.5, 0.5))
+    x = synth.make_inputs(p)
+    kw = dict(C=x["C"], ldc=p.ldc, cd=cd, bias=x["bias"], alpha=p.alpha, beta=p.beta, relu=p.relu)
+    full = oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, ab,
+                       order="ijk", **kw)
+    g = np.random.default_rng(3)
+    ii = g.integers(0, p.M, 200)
+    jj = g.integers(0, p.N, 200)
+    pts = oracle.points(ii, jj, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, ab, **kw)
+    assert np.array_equal(pts, full[ii, jj])
+
+
+def test_row_subset_equals_full():
+    p = synth.Problem(70, 33, 51, "T", "N", "f16", "f16", "bias_relu", key=(98, 0))
+    x = synth.make_inputs(p)
+    full = oracle.gemm(p.M, p.N, p.K, "T", "N", x["A"], p.lda, x["B"], p.ldb, "f16",
+                       bias=x["bias"], relu=True)
+    part = oracle.gemm(p.M, p.N, p.K, "T", "N", x["A"], p.lda, x["B"], p.ldb, "f16",
+                       bias=x["bias"], relu=True, rows=(13, 47))
+    assert np.array_equal(part, full[13:47])
+
+
+def test_exact_integer_inputs_are_integers():
+    p = synth.exact_integer_problem(20, 30, 40, "N", "T", "bf16", "bf16", "bias_relu", 2.0, -1.0,
+                                    key=(97, 0))
+    x = synth.make_inputs(p)
+    for k in ("A", "B"):
+        v = oracle.decode("bf16", x[k])
+        assert np.array_equal(v, np.round(v)) and np.abs(v).max() <= 4
+    ref = oracle.gemm(p.M, p.N, p.K, "N", "T", x["A"], p.lda, x["B"], p.ldb, "bf16", C=x["C"],
+                      ldc=p.ldc, cd="bf16", bias=x["bias"], alpha=2.0, beta=-1.0, relu=True)
+    assert np.array_equal(ref, np.round(ref))

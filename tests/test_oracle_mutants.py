@@ -1,0 +1,49 @@
+"""The oracle's pins must catch plausible mistakes: each case plants one mistake in a copy of
+oracle.c (on the CPU), builds it, and checks that the pin suite fails against that build."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "drop_last_k": ("k < K; ++k", "k + 1 < K; ++k"),
+    "transposed_gather": ("out[r * cols + c] = op ? X[c * ldx + r] : X[r * ldx + c];",
+                          "out[r * cols + c] = op ? X[r * ldx + c] : X[r * ldx + c];"),
+    "bias_by_row": ("if (bias) t += bias[j];\n            if (relu && !(t > 0.0))",
+                    "if (bias) t += bias[i % N];\n            if (relu && !(t > 0.0))"),
+    "beta_sign": ("if (beta != 0.0) t += beta * C[i * N + j];",
+                  "if (beta != 0.0) t -= beta * C[i * N + j];"),
+    "alpha_scales_bias": ("if (bias) t += bias[j];\n            if (relu && !(t > 0.0))",
+                          "if (bias) t += alpha * bias[j];\n            if (relu && !(t > 0.0))"),
+    "f16_exponent_bias": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
+    "relu_threshold": ("if (relu && !(t > 0.0)) t = 0.0;\n            out[i * N + j] = t;",
+                       "if (relu && t < -0.25) t = 0.0;\n            out[i * N + j] = t;"),
+    "round_truncates": ("double m = rint(a / ldexp(1.0, ue - 10));",
+                        "double m = floor(a / ldexp(1.0, ue - 10));"),
+    "points_b_index": ("oracle_elem_f64(ab_dt, B, opb ? j * ldb + k : k * ldb + j)",
+                       "oracle_elem_f64(ab_dt, B, opb ? k * ldb + j : k * ldb + j)"),
+    "tile_skips_rows": ("for (int64_t i = m; i < me; ++i) {\n                    double a",
+                        "for (int64_t i = m + (me - m > 1); i < me; ++i) {\n                    double a"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert old in src, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    c = tmp_path / "oracle_mut.c"
+    c.write_text(mutated)
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-o",
+                    str(so), str(c), "-lpthread", "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")], env=env, cwd=ROOT,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"planted mistake {name} passed every pin:\n{r.stdout[-2000:]}"
