@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-epilogue GEMM on one MI355X.
+
+One step = one launch of D = ReLU(op(A) op(B) + bias[N]) on the headline workload, fp16 8192^3
+NN with fp32 accumulation and fp16 output (inputs resident in HBM before the timed region).
+Prints one JSON line with TFLOP/s, the roofline position of the kernel (its average duration
+from HIP events recorded on the launch stream) and the CPU oracle timed on a bounded row sample
+of the same workload on this host's cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME[:IDX]] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s (and % of MFMA peak) fp16->fp32 GEMM 8192^3 with bias+ReLU epilogue"
+# MI355X published dense peaks (TFLOP/s, TOP/s for int8) and HBM bandwidth (GB/s)
+PEAK = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f32": 157.3}
+HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit():
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def pick_workload(spec):
+    import synth
+    name, _, idx = spec.partition(":")
+    probs = synth.WORKLOADS[name]()
+    return probs[int(idx) if idx else 0]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="fp16_8192_bias_relu")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this GEMM runs on one GPU; multi-GPU runs are not part of this "
+              "build (the path shards by output rows or columns with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import tiled_gemm_epilogues_amd as tge
+    from tiled_gemm_epilogues_amd import Plan
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    p = pick_workload(args.workload)
+    log(f"[bench] workload {p.label()}")
+    t0 = time.time()
+    x = synth.make_inputs(p)
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    def dev(dtype, raw):
+        flat = np.ascontiguousarray(raw).reshape(-1)
+        if dtype in ("f16", "bf16"):
+            t = torch.from_numpy(flat.view(np.int16)).view(
+                {"f16": torch.float16, "bf16": torch.bfloat16}[dtype])
+        else:
+            t = torch.from_numpy(flat)
+        return t.to("cuda:0")
+
+    A = dev(p.ab, x["A"])
+    B = dev(p.ab, x["B"])
+    C = dev(p.cd, x["C"]) if x["C"] is not None else None
+    bias = dev(p.bias_dt, x["bias"]) if x["bias"] is not None else None
+    D = torch.empty(p.M * p.ldc, dtype={"f16": torch.float16, "bf16": torch.bfloat16,
+                                        "f32": torch.float32, "i32": torch.int32}[p.cd],
+                    device="cuda:0")
+    plan = Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    log(f"[bench] kernel: {plan.describe()}")
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.run(A, B, C, D, bias, p.alpha, p.beta)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        plan.run(A, B, C, D, bias, p.alpha, p.beta)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_events = ev0.elapsed_time(ev1) / max(1, args.steps)
+    ms_wall = wall * 1e3 / max(1, args.steps)
+    log(f"[bench] {args.steps} steps: {ms_events:.4f} ms/launch (events), {ms_wall:.4f} ms/step (wall)")
+
+    flops = p.flops
+    tflops = flops / (ms_events * 1e-3) / 1e12
+    peak = PEAK[p.ab]
+    bytes_alg = p.algorithmic_bytes()
+
+    # the skinny shapes are bound by HBM; the rest by MFMA
+    ai = flops / bytes_alg
+    ridge = peak * 1e12 / (HBM_GBS * 1e9)
+    if ai < ridge:
+        gbs = bytes_alg / (ms_events * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": None}
+
+    # parity of the timed output on a row band and a sample of points (not timed)
+    import oracle
+    Dh = D.view(torch.int16).cpu().numpy().view(np.uint16) if p.cd in ("f16", "bf16") \
+        else D.cpu().numpy()
+    Dh = Dh.reshape(p.M, p.ldc)
+
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        threads = host_threads()
+        # pilot on 32 rows, then size the sample for about --cpu-seconds of oracle work
+        r_pilot = min(32, p.M)
+        t0 = time.perf_counter()
+        oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab, C=x["C"],
+                    ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha, beta=p.beta, relu=p.relu,
+                    rows=(0, r_pilot), threads=threads)
+        pilot = time.perf_counter() - t0
+        rows = r_pilot
+        if pilot < args.cpu_seconds:
+            rows = int(r_pilot * args.cpu_seconds / max(pilot, 1e-3)) // 32 * 32
+            rows = max(r_pilot, min(p.M, rows))
+        t0 = time.perf_counter()
+        ref = oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab,
+                          C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
+                          beta=p.beta, relu=p.relu, rows=(0, rows), threads=threads)
+        t_cpu = time.perf_counter() - t0
+        sample_flops = 2.0 * rows * p.N * p.K
+        cpu = {"value": round(sample_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"output rows 0..{rows - 1} of {p.M} (all {p.N} columns, full K={p.K}): "
+                         f"{sample_flops:.3e} flop in {t_cpu:.1f}s, fp64/int64 accumulation"}
+        log(f"[bench] cpu oracle: {cpu['sample']}")
+        got = oracle.decode(p.cd, Dh[:rows, : p.N]) if p.cd != "i32" else Dh[:rows, : p.N].astype(np.int64)
+        maxa = oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda)
+        maxb = oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb)
+        den = p.K * maxa * maxb
+        err = float(np.max(np.abs(got - ref)) / den) if den else float(np.max(np.abs(got - ref)))
+        parity = {"rows_checked": rows, "max_normalised_error": err, "tolerance": 2e-3,
+                  "ok": bool(err <= 2e-3) if p.cd != "i32" else bool(err == 0)}
+        log(f"[bench] parity on rows 0..{rows - 1}: {parity}")
+
+    out = {
+        "metric": METRIC if args.workload == "fp16_8192_bias_relu" else
+        f"TFLOP/s {p.label()}",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s" if p.ab != "i8" else "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_events, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.ab,
+        "data": "synthetic",
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "layout": p.op_a + p.op_b,
+                   "ab": p.ab, "cd": p.cd, "epilogue": p.epi, "alpha": p.alpha, "beta": p.beta,
+                   "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * gemm.h: C ABI of the MI355X (gfx950) tiled GEMM with a fused register epilogue.
+ *
+ *   D = act(alpha * op(A) * op(B) + beta * C + bias[j])
+ *
+ * The operation is the GEMM C = alpha*A*B + beta*C of "CUTLASS: Fast Linear Algebra in CUDA
+ * C++" (section "Efficient Matrix Multiplication on GPUs"), with the element-wise post-processing
+ * of that page's section "Fusing Element-wise Operations: An Example with SGEMM" (scale by alpha,
+ * add a bias term and beta times the C element, clamp with max(0, .)) and the bias vector of
+ * "Flexible Performant GEMM Kernels on GPUs", section 5.3, added to every row of the product.
+ * Mixed precision follows that paper's section 2.3: 16-bit inputs with 32-bit accumulation
+ * (fp16/bf16 -> fp32; int8 -> int32 here).  The API has two steps, as that paper's section 6
+ * describes for cuBLASLt: build a plan for one problem description, then launch it any number of
+ * times with different buffers and scalars.
+ *
+ * Storage: every matrix is ROW-MAJOR.  op = GEMM_OP_N uses the stored array as is; GEMM_OP_T
+ * means the stored array is the transpose of the operand.
+ *   op_a = N: A is M x K, element (i,k) at A[i*lda + k], lda >= K.
+ *   op_a = T: A is stored K x M, op(A)(i,k) = A[k*lda + i], lda >= M.
+ *   op_b = N: B is K x N, element (k,j) at B[k*ldb + j], ldb >= N.
+ *   op_b = T: B is stored N x K, op(B)(k,j) = B[j*ldb + k], ldb >= K.
+ *   C and D are M x N with the same leading dimension ldc >= N.
+ * Leading dimensions are counted in elements of each matrix's own type.  No alignment is
+ * required; 16-byte aligned pointers and leading dimensions take the faster load paths.
+ *
+ * Supported type combinations (ab_type -> cd_type); bias is fp32 for float inputs and int32
+ * for int8 inputs; C has the type of D; accumulation is fp32 (int32 for int8):
+ *   F32 -> F32,  F16 -> F16 | F32,  BF16 -> BF16 | F32,  I8 -> I32.
+ * Conversion to a 16-bit output rounds to nearest even.
+ *
+ * Ownership: the caller owns every device buffer and keeps it alive until the stream work that
+ * uses it has finished.  A plan is a small immutable host object: it holds no device memory and
+ * no workspace, may be shared between host threads and streams, and must be destroyed with
+ * gemm_plan_destroy.
+ *
+ * Errors: every function returns a status; nothing throws across this boundary.  gemm_run is
+ * asynchronous: it validates, enqueues one kernel on `stream` and returns; faults during
+ * execution surface at the caller's next synchronisation.
+ */
+#ifndef TGE_GEMM_H
+#define TGE_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
+
+typedef enum {
+    GEMM_F32 = 0,
+    GEMM_F16 = 1,
+    GEMM_BF16 = 2,
+    GEMM_I8 = 3,
+    GEMM_I32 = 4
+} gemm_dtype_t;
+
+/* bias: bias[j] added to every row; relu: max(0, .) applied last. */
+typedef enum {
+    GEMM_EPI_NONE = 0,
+    GEMM_EPI_RELU = 1,
+    GEMM_EPI_BIAS = 2,
+    GEMM_EPI_BIAS_RELU = 3
+} gemm_epilogue_t;
+
+typedef enum {
+    GEMM_STATUS_SUCCESS = 0,
+    GEMM_STATUS_INVALID_VALUE = 1, /* a bad argument: negative size, ld too small, NULL pointer */
+    GEMM_STATUS_NOT_SUPPORTED = 2, /* a valid request this library does not implement */
+    GEMM_STATUS_HIP_ERROR = 3,     /* the HIP runtime reported an error at launch */
+    GEMM_STATUS_ALLOC_FAILED = 4   /* host memory for the plan could not be allocated */
+} gemm_status_t;
+
+typedef struct gemm_plan *gemm_plan_t;
+
+/*
+ * Builds a plan for one problem description.  Host-only: makes no HIP call.
+ *   out            receives the plan; set to NULL on any failure.
+ *   M, N, K        problem size, each >= 0.  M == 0 or N == 0 is a valid empty problem;
+ *                  K == 0 gives D = act(beta*C + bias).
+ *   op_a, op_b     GEMM_OP_N or GEMM_OP_T (see the storage rules above).
+ *   lda, ldb, ldc  leading dimensions in elements, at least the stored row length (and >= 1).
+ *   ab_type        type of A and B;  cd_type: type of C and D (see the supported table).
+ *   epi            epilogue kind.
+ * Returns INVALID_VALUE for negative sizes, leading dimensions below the minimum, an enum out of
+ * range or out == NULL; NOT_SUPPORTED for a type pair outside the table or when a matrix spans
+ * 2^31 bytes or more.
+ * The workgroup tile is chosen from the shape; the environment variable TGE_FORCE_TILE=256, 128
+ * or 64, read at plan creation, pins it (for tests and tuning sweeps).
+ */
+gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K, gemm_op_t op_a,
+                               gemm_op_t op_b, int64_t lda, int64_t ldb, int64_t ldc,
+                               gemm_dtype_t ab_type, gemm_dtype_t cd_type, gemm_epilogue_t epi);
+
+/*
+ * Enqueues D = act(alpha*op(A)*op(B) + beta*C + bias) on `stream` (a hipStream_t; NULL is the
+ * null stream of the current device).  All pointers are device pointers on the current device.
+ *   A, B     operands (may be NULL only if the product is empty: M, N or K == 0).
+ *   C        read only when beta != 0 (may be NULL, or hold NaN, when beta == 0).  C == D is
+ *            allowed (in-place update); any other overlap between D and an input is undefined.
+ *   D        output, required when M > 0 and N > 0.
+ *   bias     N elements (fp32, or int32 for int8 inputs); required when the plan's epilogue
+ *            includes a bias, ignored otherwise.
+ *   alpha, beta  scalars applied in fp32 (int8 plans require alpha == 1 and beta in {0, 1}).
+ * Returns INVALID_VALUE for a NULL plan or a missing required pointer, NOT_SUPPORTED for int8
+ * scalars outside the rule above, HIP_ERROR when the launch fails.  M == 0 or N == 0 returns
+ * SUCCESS without launching.
+ */
+gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const void *C, void *D,
+                       const void *bias, float alpha, float beta, void *stream);
+
+/* Frees a plan.  NULL is a no-op.  Always returns SUCCESS. */
+gemm_status_t gemm_plan_destroy(gemm_plan_t plan);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *gemm_status_string(gemm_status_t status);
+
+/*
+ * Describes the kernel a plan launches: writes a NUL-terminated text such as
+ * "mfma f16->f16 NN tile 256x256x64 waves 2x2 grid 1024" into buf (at most len bytes).
+ * Returns INVALID_VALUE for a NULL plan or buffer.
+ */
+gemm_status_t gemm_plan_describe(gemm_plan_t plan, char *buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGE_GEMM_H */

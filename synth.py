@@ -29,7 +29,9 @@ def quantize(dtype, x):
     if dtype == "f32":
         return x.astype(np.float32)
     if dtype == "f16":
-        return x.astype(np.float32).astype(np.float16).view(np.uint16)
+        import torch  # vectorised float32 -> float16 RNE, far faster than numpy's on big arrays
+        return torch.from_numpy(x.astype(np.float32)).to(torch.float16).view(torch.int16) \
+            .numpy().view(np.uint16)
     if dtype == "bf16":
         # float64 -> float32 (RNE), then float32 -> bfloat16 by rounding the 32-bit pattern to
         # its upper 16 bits, ties to even (inputs here are finite).

@@ -1,0 +1,120 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/gemm.h declares, and
+its host-side validation returns the documented status codes.  None of these calls reaches the
+GPU (plan creation is host-only; the rejected or empty runs return before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_gemm_epilogues_amd as tge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "gemm.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(tge.EXPORTED)
+    lib = ctypes.CDLL(tge.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert tge.gemm_status_string(s).startswith("GEMM_STATUS_")
+    assert tge.gemm_status_string(99) == "GEMM_STATUS_UNKNOWN"
+
+
+def _create(**kw):
+    a = dict(M=64, N=64, K=64, op_a="N", op_b="N", lda=64, ldb=64, ldc=64, ab_type="f16",
+             cd_type="f16", epilogue="none")
+    a.update(kw)
+    return tge.gemm_plan_create(**a)
+
+
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(N=-1), dict(K=-1), dict(lda=63), dict(ldb=63),
+                                dict(ldc=63), dict(op_a="T", lda=63), dict(op_b="T", ldb=63),
+                                dict(op_a=2), dict(ab_type=7), dict(cd_type=-1), dict(epilogue=4),
+                                dict(M=0, N=0, K=0, lda=0, ldb=0, ldc=0)])
+def test_invalid_values(kw):
+    st, h = _create(**kw)
+    assert st == tge.STATUS_INVALID_VALUE and h is None
+
+
+@pytest.mark.parametrize("ab,cd", [("f16", "bf16"), ("bf16", "f16"), ("i8", "f32"), ("f32", "f16"),
+                                   ("i32", "i32"), ("i8", "i8"), ("f16", "i32")])
+def test_unsupported_pairs(ab, cd):
+    st, h = _create(ab_type=ab, cd_type=cd)
+    assert st == tge.STATUS_NOT_SUPPORTED and h is None
+
+
+def test_span_limit():
+    st, _ = _create(M=40000, N=40000, K=64, ldb=40000, ldc=40000, cd_type="f32", ab_type="f16")
+    assert st == tge.STATUS_NOT_SUPPORTED
+
+
+@pytest.mark.parametrize("ab,cd", [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"),
+                                   ("bf16", "f32"), ("i8", "i32")])
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+def test_supported_pairs_and_describe(ab, cd, lay):
+    p = tge.Plan(300, 200, 100, lay[0], lay[1], ab=ab, cd=cd, epilogue="bias_relu")
+    d = p.describe()
+    assert f"{ab}->{cd} {lay}" in d and "grid" in d
+
+
+def test_null_out_pointer():
+    lib = ctypes.CDLL(tge.LIB_PATH)
+    lib.gemm_plan_create.restype = ctypes.c_int
+    st = lib.gemm_plan_create(None, ctypes.c_int64(1), ctypes.c_int64(1), ctypes.c_int64(1), 0, 0,
+                              ctypes.c_int64(1), ctypes.c_int64(1), ctypes.c_int64(1), 1, 1, 0)
+    assert st == tge.STATUS_INVALID_VALUE
+
+
+def test_run_rejections_before_launch():
+    assert tge.gemm_run(None, 1, 1, None, 1, None, 1.0, 0.0, None) == tge.STATUS_INVALID_VALUE
+    st, h = _create(epilogue="bias")
+    try:
+        # D missing
+        assert tge.gemm_run(h, 16, 16, None, None, 16, 1.0, 0.0, None) == tge.STATUS_INVALID_VALUE
+        # bias missing for a bias epilogue
+        assert tge.gemm_run(h, 16, 16, None, 16, None, 1.0, 0.0, None) == tge.STATUS_INVALID_VALUE
+        # C missing with beta != 0
+        assert tge.gemm_run(h, 16, 16, None, 16, 16, 1.0, 0.5, None) == tge.STATUS_INVALID_VALUE
+        # A missing with K > 0
+        assert tge.gemm_run(h, None, 16, None, 16, 16, 1.0, 0.0, None) == tge.STATUS_INVALID_VALUE
+        # NaN scalar
+        assert tge.gemm_run(h, 16, 16, None, 16, 16, float("nan"), 0.0, None) == tge.STATUS_INVALID_VALUE
+    finally:
+        tge.gemm_plan_destroy(h)
+    st, h = _create(ab_type="i8", cd_type="i32")
+    try:
+        assert tge.gemm_run(h, 16, 16, None, 16, None, 2.0, 0.0, None) == tge.STATUS_NOT_SUPPORTED
+        assert tge.gemm_run(h, 16, 16, 16, 16, None, 1.0, 0.5, None) == tge.STATUS_NOT_SUPPORTED
+    finally:
+        tge.gemm_plan_destroy(h)
+
+
+def test_empty_problem_returns_without_launch():
+    st, h = _create(M=0, lda=64)
+    assert st == tge.STATUS_SUCCESS
+    try:
+        assert tge.gemm_run(h, None, None, None, None, None, 1.0, 0.0, None) == tge.STATUS_SUCCESS
+    finally:
+        tge.gemm_plan_destroy(h)
+
+
+def test_destroy_null_is_noop():
+    assert tge.gemm_plan_destroy(None) == tge.STATUS_SUCCESS
+
+
+def test_forced_tile(monkeypatch):
+    for t in (256, 128, 64):
+        monkeypatch.setenv("TGE_FORCE_TILE", str(t))
+        assert f"tile {t}x{t}" in tge.Plan(100, 100, 100).describe()

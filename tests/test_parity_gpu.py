@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+* exact-integer inputs (every fp32 partial sum exact, so D must equal RNE(ref) bit for bit) on
+  every type pair, layout and tile size, at shapes spanning several tiles with ragged M/N/K;
+* random inputs within the normalised tolerance on every pair and layout;
+* edge cases: K = 0, single rows/columns, beta = 0 with NaN in C, in-place C == D, padded and
+  odd leading dimensions, unaligned pointers, guard bands, determinism;
+* the five workloads at full size on sampled outputs, plus properties that hold everywhere.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import check, check_points, reference, run
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"),
+         ("i8", "i32")]
+LAYOUTS = ["NN", "NT", "TN", "TT"]
+BK = {"f32": 32, "f16": 64, "bf16": 64, "i8": 128}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _exact(M, N, K, lay, ab, cd, epi, alpha, beta, key, ld_pad=0):
+    if ab == "i8":
+        p = synth.Problem(M, N, K, lay[0], lay[1], "i8", "i32", epi, 1.0, 1.0 if beta else 0.0,
+                          a_dist=("int", -128, 127), b_dist=("int", -128, 127),
+                          c_dist=("int", -1000, 1000), bias_dist=("int", -(1 << 20), 1 << 20),
+                          key=key, name="exact_int")
+        if ld_pad:
+            p.lda += ld_pad; p.ldb += ld_pad; p.ldc += ld_pad
+        return p
+    return synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta, key,
+                                       ld_pad=ld_pad)
+
+
+EPIS = ["none", "relu", "bias", "bias_relu"]
+SCALARS = [(1.0, 0.0), (2.0, -1.0), (-0.5, 0.5), (1.0, 1.0)]
+
+
+@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("ab,cd", PAIRS)
+def test_exact_integer_all_tiles(ab, cd, lay, tile, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_TILE", str(tile))
+    i = PAIRS.index((ab, cd)) * 4 + LAYOUTS.index(lay)
+    M, N, K = 2 * tile + 7, tile + 33, 2 * BK[ab] + 5
+    epi = EPIS[i % 4]
+    alpha, beta = SCALARS[(i // 4 + tile) % 4]
+    p = _exact(M, N, K, lay, ab, cd, epi, alpha, beta, key=(100, i))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert f"tile {tile}x{tile}" in pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("ab,cd", PAIRS)
+def test_random_within_tolerance(ab, cd, lay):
+    i = PAIRS.index((ab, cd)) * 4 + LAYOUTS.index(lay)
+    M, N, K = 333, 517, 301
+    if ab == "i8":
+        p = _exact(M, N, K, lay, ab, cd, "bias_relu", 1.0, 1.0, key=(101, i))
+    else:
+        p = synth.Problem(M, N, K, lay[0], lay[1], ab, cd, "bias_relu", 1.5, -0.5, key=(101, i))
+    x = synth.make_inputs(p)
+    D, _ = run(p, x)
+    err = check(p, x, D, reference(p, x))
+    if cd != "i32":
+        assert err < 1e-4, f"error {err:.2e} is far above what fp32 accumulation gives"
+
+
+SHAPES = [(1, 1, 1), (1, 64, 64), (64, 1, 64), (5, 7, 3), (31, 33, 17), (64, 64, 64),
+          (65, 63, 129), (127, 129, 1), (200, 3, 300), (3, 200, 300), (257, 255, 200)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("bf16", "f32"), ("i8", "i32"), ("f32", "f32")])
+def test_shape_sweep_exact(ab, cd, shape):
+    M, N, K = shape
+    for j, lay in enumerate(LAYOUTS):
+        p = _exact(M, N, K, lay, ab, cd, "bias_relu", 2.0, -1.0, key=(102, SHAPES.index(shape), j))
+        x = synth.make_inputs(p)
+        D, _ = run(p, x)
+        check(p, x, D, reference(p, x), exact=True)
+
+
+@pytest.mark.parametrize("ab,cd", PAIRS)
+def test_k_zero(ab, cd):
+    p = _exact(70, 90, 0, "NN", ab, cd, "bias_relu", 2.0, -1.0, key=(103, 0))
+    x = synth.make_inputs(p)
+    D, _ = run(p, x)
+    check(p, x, D, reference(p, x), exact=True)
+
+
+@pytest.mark.parametrize("ab,cd", PAIRS)
+def test_padded_and_odd_leading_dims_unaligned_pointers(ab, cd):
+    for j, (pad, off) in enumerate([(8, 0), (3, 0), (1, 1), (5, 3)]):
+        p = _exact(150, 130, 170, ["NN", "NT", "TN", "TT"][j], ab, cd, "bias", 0.5, 2.0,
+                   key=(104, j), ld_pad=pad)
+        x = synth.make_inputs(p)
+        D, _ = run(p, x, offset=off, d_rows_extra=3)
+        check(p, x, D, reference(p, x)[:, :], rows=slice(0, p.M), exact=True)
+        # guard bands: padding columns and rows past M keep the sentinel
+        tail = D[:, p.N:]
+        below = D[p.M:, :]
+        for blk in (tail, below):
+            if blk.size:
+                if cd == "i32":
+                    assert (blk == -0x5A5A5A5A).all()
+                elif cd == "f32":
+                    assert np.isnan(blk).all()
+                else:
+                    assert (blk == {"f16": 0x7E00, "bf16": 0x7FC0}[cd]).all()
+
+
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("bf16", "f32"), ("f32", "f32")])
+def test_beta_zero_does_not_read_c(ab, cd):
+    p = synth.Problem(100, 120, 80, "N", "T", ab, cd, "relu", 1.0, 0.0, key=(105, 0))
+    x = synth.make_inputs(p)
+    x["C"] = np.full((p.M, p.ldc), np.nan if cd == "f32" else 0x7E00,
+                     dtype=synth.RAW_NP[cd])
+    D, _ = run(p, x)
+    x["C"] = None
+    check(p, x, D, reference(p, x))
+
+
+@pytest.mark.parametrize("ab,cd", [("f16", "f32"), ("bf16", "bf16"), ("i8", "i32")])
+def test_in_place_c_equals_d(ab, cd):
+    p = _exact(140, 260, 96, "TN", ab, cd, "bias_relu", 1.0, 1.0, key=(106, 0))
+    x = synth.make_inputs(p)
+    D, _ = run(p, x, c_is_d=True)
+    check(p, x, D, reference(p, x), exact=True)
+
+
+def test_deterministic_and_stream():
+    p = synth.Problem(1000, 1100, 900, "T", "N", "f16", "f16", "bias_relu", key=(107, 0))
+    x = synth.make_inputs(p)
+    s = torch.cuda.Stream()
+    D1, pl = run(p, x)
+    D2, _ = run(p, x, plan=pl, stream=s)
+    assert np.array_equal(D1, D2)
+
+
+def test_nn_equals_tt_of_transposed_problem():
+    # (XY)^T = Y^T X^T: the TT problem on the same stored arrays gives the transposed result
+    p = synth.Problem(300, 200, 250, "N", "N", "bf16", "f32", "none", key=(108, 0))
+    x = synth.make_inputs(p)
+    D, _ = run(p, x)
+    q = synth.Problem(200, 300, 250, "T", "T", "bf16", "f32", "none", lda=p.ldb, ldb=p.lda,
+                      key=(108, 0))
+    y = {"A": x["B"], "B": x["A"], "C": None, "bias": None}
+    DT, _ = run(q, y)
+    np.testing.assert_allclose(DT, D.T, rtol=0, atol=1e-5)
+
+
+# ---- the five workloads at full size -----------------------------------------------------------
+
+FULL = [(name, i) for name, fn in synth.WORKLOADS.items() for i in range(len(fn()))]
+
+
+@pytest.mark.parametrize("name,idx", FULL)
+def test_workload_full_size_sampled(name, idx):
+    p = synth.WORKLOADS[name]()[idx]
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    print(f"{p.label()} -> {pl.describe()}", flush=True)
+    if p.M * p.N * p.K <= 256 ** 3:
+        check(p, x, D, reference(p, x))
+    else:
+        check_points(p, x, D)
+        # a whole row band through the oracle as well (first and last rows)
+        for r0 in (0, p.M - 2):
+            ref = reference(p, x, rows=(r0, r0 + 2))
+            check(p, x, D, ref, rows=slice(r0, r0 + 2))
+    Dv = D[:, : p.N]
+    if p.relu:
+        assert (synth_decode(p.cd, Dv) >= 0).all()
+
+
+def synth_decode(cd, raw):
+    import oracle
+    return oracle.decode(cd, raw) if cd != "i32" else raw

@@ -1,0 +1,189 @@
+// C ABI of the library: plan creation and validation, kernel selection, launch.
+// Host code only; the kernels live in gemm_kernels.hip.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/gemm.h"
+#include "gemm_internal.h"
+
+using tge::GemmParams;
+using tge::KernelEntry;
+
+struct gemm_plan {
+    int64_t M, N, K, lda, ldb, ldc;
+    int op_a, op_b, ab, cd, epi;
+    const KernelEntry *kernel;
+    int tiles_m, tiles_n, group_m;
+    unsigned grid;
+    char desc[192];
+};
+
+namespace {
+
+const char *dtype_name(int t) {
+    switch (t) {
+    case GEMM_F32: return "f32";
+    case GEMM_F16: return "f16";
+    case GEMM_BF16: return "bf16";
+    case GEMM_I8: return "i8";
+    case GEMM_I32: return "i32";
+    }
+    return "?";
+}
+
+int elem_bytes(int t) {
+    switch (t) {
+    case GEMM_F16:
+    case GEMM_BF16: return 2;
+    case GEMM_I8: return 1;
+    default: return 4;
+    }
+}
+
+using Lookup = const KernelEntry *(*)(int, int, int);
+
+Lookup pair_table(int ab, int cd) {
+    if (ab == GEMM_F32 && cd == GEMM_F32) return tge::kernels_f32_f32;
+    if (ab == GEMM_F16 && cd == GEMM_F16) return tge::kernels_f16_f16;
+    if (ab == GEMM_F16 && cd == GEMM_F32) return tge::kernels_f16_f32;
+    if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::kernels_bf16_bf16;
+    if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::kernels_bf16_f32;
+    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::kernels_i8_i32;
+    return nullptr;
+}
+
+// Bytes from the first to one past the last element a rows x cols row-major view touches.
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int eb) {
+    if (rows == 0 || cols == 0) return 0;
+    return ((rows - 1) * ld + cols) * eb;
+}
+
+// Tile choice: the largest tile that still gives at least one tile per compute unit (256 CUs),
+// else the smallest tile.  int8 and fp32 K-slabs are 128 bytes like the 16-bit ones.
+int choose_cfg(int64_t M, int64_t N, int ab) {
+    (void)ab;
+    const int64_t cus = 256;
+    const int sizes[tge::CFG_COUNT] = {256, 128, 64};
+    for (int c = 0; c < tge::CFG_COUNT; ++c) {
+        int64_t t = ((M + sizes[c] - 1) / sizes[c]) * ((N + sizes[c] - 1) / sizes[c]);
+        if (t >= cus) return c;
+    }
+    return tge::CFG_64;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gemm_status_string(gemm_status_t s) {
+    switch (s) {
+    case GEMM_STATUS_SUCCESS: return "GEMM_STATUS_SUCCESS";
+    case GEMM_STATUS_INVALID_VALUE: return "GEMM_STATUS_INVALID_VALUE";
+    case GEMM_STATUS_NOT_SUPPORTED: return "GEMM_STATUS_NOT_SUPPORTED";
+    case GEMM_STATUS_HIP_ERROR: return "GEMM_STATUS_HIP_ERROR";
+    case GEMM_STATUS_ALLOC_FAILED: return "GEMM_STATUS_ALLOC_FAILED";
+    }
+    return "GEMM_STATUS_UNKNOWN";
+}
+
+gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K, gemm_op_t op_a,
+                               gemm_op_t op_b, int64_t lda, int64_t ldb, int64_t ldc,
+                               gemm_dtype_t ab_type, gemm_dtype_t cd_type, gemm_epilogue_t epi) {
+    if (!out) return GEMM_STATUS_INVALID_VALUE;
+    *out = nullptr;
+    if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
+    if ((op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T))
+        return GEMM_STATUS_INVALID_VALUE;
+    if ((int)ab_type < GEMM_F32 || (int)ab_type > GEMM_I32 || (int)cd_type < GEMM_F32 ||
+        (int)cd_type > GEMM_I32)
+        return GEMM_STATUS_INVALID_VALUE;
+    if ((int)epi < GEMM_EPI_NONE || (int)epi > GEMM_EPI_BIAS_RELU) return GEMM_STATUS_INVALID_VALUE;
+    // minimum leading dimensions (stored row length), never below 1
+    int64_t min_lda = op_a == GEMM_OP_N ? K : M;
+    int64_t min_ldb = op_b == GEMM_OP_N ? N : K;
+    if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
+        ldc < (N > 1 ? N : 1))
+        return GEMM_STATUS_INVALID_VALUE;
+    Lookup table = pair_table(ab_type, cd_type);
+    if (!table) return GEMM_STATUS_NOT_SUPPORTED;
+    // 32-bit offsets inside the kernels: every matrix must span less than 2^31 bytes
+    const int64_t lim = (int64_t)1 << 31;
+    int eab = elem_bytes(ab_type), ecd = elem_bytes(cd_type);
+    int64_t sa = op_a == GEMM_OP_N ? span_bytes(M, K, lda, eab) : span_bytes(K, M, lda, eab);
+    int64_t sb = op_b == GEMM_OP_N ? span_bytes(K, N, ldb, eab) : span_bytes(N, K, ldb, eab);
+    int64_t sc = span_bytes(M, N, ldc, ecd);
+    if (sa >= lim || sb >= lim || sc >= lim || lda >= lim || ldb >= lim || ldc >= lim)
+        return GEMM_STATUS_NOT_SUPPORTED;
+
+    int cfg = choose_cfg(M, N, ab_type);
+    // TGE_FORCE_TILE=256|128|64 pins the workgroup tile (tests and tuning sweeps)
+    if (const char *f = getenv("TGE_FORCE_TILE")) {
+        int v = atoi(f);
+        if (v == 256) cfg = tge::CFG_256;
+        else if (v == 128) cfg = tge::CFG_128;
+        else if (v == 64) cfg = tge::CFG_64;
+    }
+    const KernelEntry *k = table(op_a, op_b, cfg);
+    if (!k) return GEMM_STATUS_NOT_SUPPORTED;
+
+    gemm_plan *p = new (std::nothrow) gemm_plan;
+    if (!p) return GEMM_STATUS_ALLOC_FAILED;
+    p->M = M; p->N = N; p->K = K;
+    p->lda = lda; p->ldb = ldb; p->ldc = ldc;
+    p->op_a = op_a; p->op_b = op_b; p->ab = ab_type; p->cd = cd_type; p->epi = epi;
+    p->kernel = k;
+    p->tiles_m = (int)((M + k->bm - 1) / k->bm);
+    p->tiles_n = (int)((N + k->bn - 1) / k->bn);
+    p->group_m = 8;
+    p->grid = (unsigned)((int64_t)p->tiles_m * p->tiles_n);
+    snprintf(p->desc, sizeof(p->desc), "%s %s->%s %c%c tile %dx%dx%d waves %dx%d grid %u",
+             k->name, dtype_name(ab_type), dtype_name(cd_type), op_a ? 'T' : 'N',
+             op_b ? 'T' : 'N', k->bm, k->bn, k->bk, k->waves_m, k->waves_n, p->grid);
+    *out = p;
+    return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_plan_destroy(gemm_plan_t p) {
+    delete p;
+    return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_plan_describe(gemm_plan_t p, char *buf, size_t len) {
+    if (!p || !buf || len == 0) return GEMM_STATUS_INVALID_VALUE;
+    snprintf(buf, len, "%s", p->desc);
+    return GEMM_STATUS_SUCCESS;
+}
+
+gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                       const void *bias, float alpha, float beta, void *stream) {
+    if (!p) return GEMM_STATUS_INVALID_VALUE;
+    if (p->M == 0 || p->N == 0) return GEMM_STATUS_SUCCESS;
+    const bool has_bias = p->epi == GEMM_EPI_BIAS || p->epi == GEMM_EPI_BIAS_RELU;
+    const bool relu = p->epi == GEMM_EPI_RELU || p->epi == GEMM_EPI_BIAS_RELU;
+    if (!D) return GEMM_STATUS_INVALID_VALUE;
+    if (p->K > 0 && (!A || !B)) return GEMM_STATUS_INVALID_VALUE;
+    if (beta != 0.0f && !C) return GEMM_STATUS_INVALID_VALUE;
+    if (has_bias && !bias) return GEMM_STATUS_INVALID_VALUE;
+    if (p->ab == GEMM_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f)))
+        return GEMM_STATUS_NOT_SUPPORTED;
+    if (alpha != alpha || beta != beta) return GEMM_STATUS_INVALID_VALUE;  // NaN scalars
+
+    GemmParams prm;
+    prm.A = A; prm.B = B; prm.C = C; prm.D = D; prm.bias = bias;
+    prm.M = (int)p->M; prm.N = (int)p->N; prm.K = (int)p->K;
+    prm.lda = (int)p->lda; prm.ldb = (int)p->ldb; prm.ldc = (int)p->ldc;
+    prm.alpha = alpha; prm.beta = beta;
+    prm.has_beta = beta != 0.0f;
+    prm.has_bias = has_bias;
+    prm.relu = relu;
+    prm.tiles_m = p->tiles_m; prm.tiles_n = p->tiles_n; prm.group_m = p->group_m;
+    hipError_t e = p->kernel->launch(prm, p->grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;
+}
+
+}  // extern "C"

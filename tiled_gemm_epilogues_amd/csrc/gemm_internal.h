@@ -1,0 +1,43 @@
+// Internal interface between the host plan/run code and the device kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tge {
+
+// Everything a kernel needs for one launch; passed by value as the kernel argument.
+struct GemmParams {
+    const void *A, *B, *C;
+    void *D;
+    const void *bias;
+    int M, N, K;
+    int lda, ldb, ldc;       // elements of each matrix's own type
+    float alpha, beta;
+    int has_beta, has_bias, relu;
+    int tiles_m, tiles_n;    // output tiles along M and N
+    int group_m;             // tile rows per raster group
+};
+
+using LaunchFn = hipError_t (*)(const GemmParams &, unsigned grid, hipStream_t);
+
+// One compiled kernel variant and its tile shape.
+struct KernelEntry {
+    LaunchFn launch;
+    int bm, bn, bk;          // workgroup tile (bk in elements)
+    int waves_m, waves_n;    // wave grid inside the workgroup
+    const char *name;
+};
+
+// Tile configurations, largest first.
+enum TileCfg { CFG_256 = 0, CFG_128 = 1, CFG_64 = 2, CFG_COUNT = 3 };
+
+// Per type-pair lookup, defined by the kernel translation units (one per pair).
+// op_a/op_b: 0 = N, 1 = T.  Returns nullptr for an unknown combination.
+const KernelEntry *kernels_f32_f32(int op_a, int op_b, int cfg);
+const KernelEntry *kernels_f16_f16(int op_a, int op_b, int cfg);
+const KernelEntry *kernels_f16_f32(int op_a, int op_b, int cfg);
+const KernelEntry *kernels_bf16_bf16(int op_a, int op_b, int cfg);
+const KernelEntry *kernels_bf16_f32(int op_a, int op_b, int cfg);
+const KernelEntry *kernels_i8_i32(int op_a, int op_b, int cfg);
+
+}  // namespace tge
