@@ -2,8 +2,8 @@
 the benchmark.  This module only draws and stores numbers; it holds none of the GEMM's
 arithmetic, and neither the HIP path nor the oracle imports it.
 
-Every draw comes from numpy's PCG64 seeded by SeedSequence([workload id, shape index, operand
-id]) with operand ids A=0, B=1, C=2, bias=3.  A logical op(A) (M x K) and op(B) (K x N) are drawn
+Every draw comes from numpy's PCG64 seeded by SeedSequence([*key, operand id]), where key is
+(workload id, shape index[, case]) and the operand ids are A=0, B=1, C=2, bias=3.  A logical op(A) (M x K) and op(B) (K x N) are drawn
 once per shape and then stored in the requested physical layout, so all four N/T layouts of one
 shape hold the same logical problem.  Float values are drawn in float64 and quantised once to
 the storage type with round-to-nearest-even; the raw arrays (uint16 bit patterns for f16 and
@@ -136,8 +136,7 @@ def _store(logical, op, ld, fill):
 
 def make_inputs(p: Problem, pad_fill=0):
     """Raw stored arrays {A, B, C, bias} (C and bias None when unused) for problem p."""
-    cfg, shp = p.key
-    ga, gb, gc, gbias = (rng(cfg, shp, i) for i in range(4))
+    ga, gb, gc, gbias = (rng(*p.key, i) for i in range(4))
     a = quantize(p.ab, draw(ga, p.a_dist, p.M * p.K)).reshape(p.M, p.K)
     b = quantize(p.ab, draw(gb, p.b_dist, p.K * p.N)).reshape(p.K, p.N)
     A = _store(a, p.op_a, p.lda, pad_fill)

@@ -118,3 +118,10 @@ def test_forced_tile(monkeypatch):
     for t in (256, 128, 64):
         monkeypatch.setenv("TGE_FORCE_TILE", str(t))
         assert f"tile {t}x{t}" in tge.Plan(100, 100, 100).describe()
+
+
+def test_single_hip_runtime_in_process():
+    # the library must bind to the HIP runtime torch loaded, never bring a second one
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    assert len(paths) == 1, paths

@@ -20,6 +20,11 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
                       "(python -m tiled_gemm_epilogues_amd.build)")
 
+# torch ships its own HIP runtime (same soname as ROCm's).  Load it first so that libtge.so binds
+# to that one runtime: device memory and streams come from torch, and a second runtime in the
+# process would own neither.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 OP = {"N": 0, "T": 1}

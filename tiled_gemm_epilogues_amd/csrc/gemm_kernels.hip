@@ -84,9 +84,12 @@ struct TF32 {
     // so the 4 instructions together cover 8 distinct k exactly once.
     __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[j]),
-                                                     __builtin_bit_cast(float, b[j]), c, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+            // copy the element out first: bit_cast of a vector-element lvalue reads element 0
+            const uint32_t aj = a[j], bj = b[j];
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, aj),
+                                                     __builtin_bit_cast(float, bj), c, 0, 0, 0);
+        }
         return c;
     }
 };
