@@ -196,3 +196,42 @@ def test_workload_full_size_sampled(name, idx):
 def synth_decode(cd, raw):
     import oracle
     return oracle.decode(cd, raw) if cd != "i32" else raw
+
+
+# ---- the fast 256x256 path (16-bit inputs) ----------------------------------------------------
+
+# shapes that meet the fast kernel's preconditions (16-byte aligned leading dimensions, M and N
+# multiples of 8) with ragged tiles, K tails and one-tile edge cases
+FAST_SHAPES = [(256, 256, 64), (304, 520, 200), (512, 264, 128), (264, 8, 72), (8, 304, 192),
+               (640, 512, 320), (1000, 776, 1000)]
+
+
+@pytest.mark.parametrize("shape", FAST_SHAPES)
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_fast_path_exact(ab, cd, lay, shape, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    M, N, K = shape
+    i = LAYOUTS.index(lay) + 4 * FAST_SHAPES.index(shape)
+    epi = EPIS[i % 4]
+    alpha, beta = SCALARS[i % 4]
+    p = _exact(M, N, K, lay, ab, cd, epi, alpha, beta, key=(109, i))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_fast" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_fast_path_random_and_unaligned_fallback(lay, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    p = synth.Problem(776, 1024, 576, lay[0], lay[1], "f16", "f16", "bias_relu", 1.0, 0.0,
+                      key=(110, LAYOUTS.index(lay)))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_fast" in pl.describe()
+    ref = reference(p, x)
+    check(p, x, D, ref)
+    # a pointer offset by one element forces the general kernel at run time: same result
+    D2, _ = run(p, x, offset=1)
+    check(p, x, D2, ref)

@@ -17,7 +17,8 @@ using tge::KernelEntry;
 struct gemm_plan {
     int64_t M, N, K, lda, ldb, ldc;
     int op_a, op_b, ab, cd, epi;
-    const KernelEntry *kernel;
+    const KernelEntry *kernel;       // general kernel (always valid)
+    const KernelEntry *fast;         // fast kernel when the plan qualifies, else nullptr
     int tiles_m, tiles_n, group_m;
     unsigned grid;
     char desc[192];
@@ -46,6 +47,16 @@ int elem_bytes(int t) {
 }
 
 using Lookup = const KernelEntry *(*)(int, int, int);
+
+using FastLookup = const KernelEntry *(*)(int, int);
+
+FastLookup fast_table(int ab, int cd) {
+    if (ab == GEMM_F16 && cd == GEMM_F16) return tge::fast_f16_f16;
+    if (ab == GEMM_F16 && cd == GEMM_F32) return tge::fast_f16_f32;
+    if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::fast_bf16_bf16;
+    if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::fast_bf16_f32;
+    return nullptr;
+}
 
 Lookup pair_table(int ab, int cd) {
     if (ab == GEMM_F32 && cd == GEMM_F32) return tge::kernels_f32_f32;
@@ -131,19 +142,33 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     const KernelEntry *k = table(op_a, op_b, cfg);
     if (!k) return GEMM_STATUS_NOT_SUPPORTED;
 
+    // fast path: 16-bit inputs, 256x256 tiles worth it, shape/ld preconditions of gemm_fast
+    const KernelEntry *fast = nullptr;
+    FastLookup ft = fast_table(ab_type, cd_type);
+    const char *fk = getenv("TGE_FORCE_KERNEL");  // "fast" or "general" (tests, sweeps)
+    bool want_fast = cfg == tge::CFG_256;
+    if (fk && strcmp(fk, "fast") == 0) want_fast = true;
+    if (fk && strcmp(fk, "general") == 0) want_fast = false;
+    if (ft && want_fast && K >= 64 && (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 &&
+        (op_a == GEMM_OP_N || M % 8 == 0) && (op_b == GEMM_OP_T || N % 8 == 0))
+        fast = ft(op_a, op_b);
+
     gemm_plan *p = new (std::nothrow) gemm_plan;
     if (!p) return GEMM_STATUS_ALLOC_FAILED;
     p->M = M; p->N = N; p->K = K;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
     p->op_a = op_a; p->op_b = op_b; p->ab = ab_type; p->cd = cd_type; p->epi = epi;
     p->kernel = k;
-    p->tiles_m = (int)((M + k->bm - 1) / k->bm);
-    p->tiles_n = (int)((N + k->bn - 1) / k->bn);
+    p->fast = fast;
+    const KernelEntry *shown = fast ? fast : k;
+    p->tiles_m = (int)((M + shown->bm - 1) / shown->bm);
+    p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
     p->grid = (unsigned)((int64_t)p->tiles_m * p->tiles_n);
     snprintf(p->desc, sizeof(p->desc), "%s %s->%s %c%c tile %dx%dx%d waves %dx%d grid %u",
-             k->name, dtype_name(ab_type), dtype_name(cd_type), op_a ? 'T' : 'N',
-             op_b ? 'T' : 'N', k->bm, k->bn, k->bk, k->waves_m, k->waves_n, p->grid);
+             shown->name, dtype_name(ab_type), dtype_name(cd_type), op_a ? 'T' : 'N',
+             op_b ? 'T' : 'N', shown->bm, shown->bn, shown->bk, shown->waves_m, shown->waves_n,
+             p->grid);
     *out = p;
     return GEMM_STATUS_SUCCESS;
 }
@@ -181,8 +206,14 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     prm.has_beta = beta != 0.0f;
     prm.has_bias = has_bias;
     prm.relu = relu;
-    prm.tiles_m = p->tiles_m; prm.tiles_n = p->tiles_n; prm.group_m = p->group_m;
-    hipError_t e = p->kernel->launch(prm, p->grid, static_cast<hipStream_t>(stream));
+    prm.group_m = p->group_m;
+    const KernelEntry *k = p->kernel;
+    // the fast kernel needs 16-byte aligned operand pointers; else the general kernel runs
+    if (p->fast && ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0) k = p->fast;
+    prm.tiles_m = (int)((p->M + k->bm - 1) / k->bm);
+    prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
+    const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n);
+    hipError_t e = k->launch(prm, grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;
 }
 

@@ -1,0 +1,406 @@
+// Fast path for large fp16/bf16 GEMMs on gfx950: 256x256 output tile per workgroup, 4 waves of
+// 128x128 (4x4 MFMA 32x32x16 tiles, accumulators in AGPRs), K walked in slabs of 64.
+//
+// The blocking follows "Flexible Performant GEMM Kernels on GPUs" (section 3: tiles copied up
+// the memory hierarchy, global -> shared -> registers, then matrix-multiply-accumulate) and the
+// software pipelining of "CUTLASS: Fast Linear Algebra in CUDA C++" ("Software Pipelining":
+// loads for the next slab in flight while the current one is multiplied, one barrier per slab),
+// re-done for the hardware:
+//
+//  * global -> LDS with direct-to-LDS 16-byte loads (global_load_lds_dwordx4): no staging
+//    registers and no LDS write instructions.  One wave instruction fills 1 KiB of LDS, lane l
+//    writing bytes [16l, 16l+16); the XOR swizzle is therefore applied on the global side by
+//    choosing which 16-byte chunk each lane fetches.
+//  * layouts are handled at load time without transposing through registers ("Flexible GEMM"
+//    section 5.1 adapts its loaders to the N/T layout the same way): an operand whose contiguous
+//    dimension is K is kept [mn][k] in LDS and read with ds_read_b128; an operand whose
+//    contiguous dimension is M or N is kept [k][mn] and read with the gfx950 transposing LDS
+//    read ds_read_b64_tr_b16, which hands each lane four consecutive-k values of one column.
+//  * swizzles (bank-conflict avoidance, the role padding plays in "Flexible GEMM" section 5.1):
+//    [mn][k] rows of 128 B hold logical 16-byte chunk c at c ^ ((r ^ r>>3) & 7); [k][mn] rows of
+//    512 B hold chunk c at c ^ h(k & 3) with h = {0, 4, 10, 14}.  Both spread every group of
+//    reads over distinct banks for 32- and 64-bank LDS organisations.
+//  * pipeline per slab s (buffers X = s % 2, Y = the other): the fragments of k-slice j+1 are
+//    read while the MFMAs of k-slice j run; after the last read of X the wave waits for its own
+//    loads of slab s+1 and joins the barrier; then it issues the loads of slab s+2 into X and the
+//    first fragment reads of Y while the last k-slice's MFMAs run.
+//  * M/N edges: source rows past the edge are clamped to the last valid row (their products
+//    only reach output rows/columns that the masked epilogue drops); the K tail (K % 64) runs one
+//    guarded register-staged slab with zero fill.
+//  * epilogue: identical to the general kernel (alpha, beta*C, bias[j], ReLU, convert, masked
+//    store from the accumulator registers).
+//
+// Preconditions (checked by the host): 16-bit inputs, A/B base pointers and leading dimensions
+// 16-byte aligned, M (if A is stored transposed) and N (if B is not transposed) multiples of 8,
+// K >= 64.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "gemm_internal.h"
+
+namespace tge {
+namespace {
+
+using namespace dev;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int BM = 256, BN = 256, BKE = 64;          // tile; K slab in elements
+constexpr int NT = 256;                              // 4 waves
+constexpr int KC_BYTES = 256 * 128;                  // one operand slab: 32 KiB either layout
+// LDS map: [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB each, so that every fragment
+// read is (base register) + (stage and k-slice offset as the instruction's 16-bit immediate)
+constexpr int OPND = 2 * KC_BYTES;                   // byte offset of operand B's stages
+
+__device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_mc(int k) {
+    const int q = k & 3;
+    return 4 * q + 2 * (q >> 1);
+}
+__device__ __forceinline__ int off_kc(int r, int c) { return r * 128 + ((c ^ swz_kc(r)) << 4); }
+__device__ __forceinline__ int off_mc(int k, int c) { return k * 512 + ((c ^ swz_mc(k)) << 4); }
+
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One direct-to-LDS 16-byte load per lane: global address sbase + voff (bytes), LDS destination
+// lds + 16 * lane.  Issued as inline assembly so that the compiler does not treat the LDS write
+// as aliasing every later LDS read (it would wait for the load before each read); completion is
+// awaited explicitly with s_waitcnt vmcnt before the barrier that publishes the slab.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
+                 :: "s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)p;
+}
+
+// ---- per-operand direct-load plan -----------------------------------------------------------
+// Each wave issues 8 instructions per operand per slab.  For lane l and instruction i the byte
+// offset from the slab's base address is fixed for the whole kernel.
+
+template <bool KC>
+struct Loader {
+    uint32_t voff[8];
+
+    // row0: first M (or N) index of the tile; ext: M (or N); ld: leading dimension.
+    __device__ __forceinline__ void init(int wave, int lane, int row0, int ext, int ld) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (KC) {
+                const int r = (wave * 8 + i) * 8 + (lane >> 3);   // tile row
+                const int c = (lane & 7) ^ swz_kc(r);             // logical chunk this lane fetches
+                const int gr = min(row0 + r, ext - 1);
+                voff[i] = (uint32_t)(gr * ld + c * 8) * 2u;
+            } else {
+                const int k = (wave * 8 + i) * 2 + (lane >> 5);   // slab row (k)
+                const int c = (lane & 31) ^ swz_mc(k);
+                const int col = min(row0 + c * 8, ext - 8);       // ext % 8 == 0: whole chunks
+                voff[i] = (uint32_t)(k * ld + col) * 2u;
+            }
+        }
+    }
+    // base of the slab whose K starts at element k0
+    __device__ __forceinline__ static const uint16_t *slab_base(const uint16_t *base, int ld, int k0) {
+        return KC ? base + k0 : base + (size_t)k0 * ld;
+    }
+    // instruction i of this wave: LDS block (wave*8 + i) of the operand slab at `dst`
+    __device__ __forceinline__ void issue(const uint16_t *sb, uint32_t dst, int wave, int i) const {
+        dma16(sb, voff[i], dst + (uint32_t)(wave * 8 + i) * 1024u);
+    }
+};
+
+// Guarded staging of a partial slab (k0 .. K-1, zero beyond) into the same LDS layout.
+template <bool KC>
+__device__ void stage_tail(const uint16_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
+                           int tid) {
+    // 2048 chunks of 16 bytes per operand slab, 8 per thread
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) {
+        const int q = tid + NT * i;
+        uint16_t v[8];
+        if constexpr (KC) {
+            const int r = q >> 3, c = q & 7;
+            const int gr = min(row0 + r, ext - 1);
+            const uint16_t *p = base + (size_t)gr * ld + k0 + c * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (k0 + c * 8 + e < K) ? p[e] : (uint16_t)0;
+            __builtin_memcpy(dst + off_kc(r, c), v, 16);
+        } else {
+            const int k = q >> 5, c = q & 31;
+            const int col = min(row0 + c * 8, ext - 8);
+            if (k0 + k < K) {
+                const uint16_t *p = base + (size_t)(k0 + k) * ld + col;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = p[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0;
+            }
+            __builtin_memcpy(dst + off_mc(k, c), v, 16);
+        }
+    }
+}
+
+// ---- fragment reads ---------------------------------------------------------------------------
+// Fragment (sub-tile t, k-slice j): lane l holds 8 consecutive k (k = 16j + 8*(l/32) + 0..7) of
+// tile row (or column) 32t + l%32, as 16 bytes.  A K-contiguous operand needs one ds_read_b128
+// per fragment, an M/N-contiguous one two transposing reads (k 0..3 and 4..7).
+
+template <bool KC>
+struct Frag {
+    static constexpr int NI = KC ? 1 : 2;   // LDS instructions per fragment
+    // byte address (LDS) of this lane's fragment in stage 0: per sub-tile and k-slice for a
+    // K-contiguous operand (the XOR swizzle is not additive), per sub-tile otherwise
+    uint32_t addr[4][KC ? 4 : 1];
+
+    __device__ __forceinline__ void init(int lane, int wrow, uint32_t opbase) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (KC) {
+                const int r = wrow + 32 * t + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    addr[t][j] = opbase + (uint32_t)off_kc(r, 2 * j + (lane >> 5));
+            } else {
+                // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i % 4
+                // of the 8-byte chunks addressed by lanes i/4 + 4e, e = 0..3.  Lane a of the
+                // group therefore addresses k row a/4 and columns 4*(a%4) .. +3.
+                const int q = (lane & 15) >> 2;
+                const int k = 8 * (lane >> 5) + q;
+                const int col = wrow + 32 * t + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                addr[t][0] = opbase + (uint32_t)(k * 512 + (((col >> 3) ^ swz_mc(k)) << 4) + (col & 7) * 2);
+            }
+        }
+    }
+    // instruction h (< NI) of fragment (t, j) of `stage` into dst
+    __device__ __forceinline__ void read(int stage, int t, int j, int h, u32x4 &dst) const {
+        if constexpr (KC) {
+            dst = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)(addr[t][j] + stage * KC_BYTES);
+        } else {
+            // rows 16j + 4h + (0..3): the swizzle depends only on k & 3
+            const uint32_t a = addr[t][0] + stage * KC_BYTES + (16 * j + 4 * h) * 512;
+            s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
+            dst[2 * h] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 0, 1));
+            dst[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 2, 3));
+        }
+    }
+};
+
+template <class TI, class TO, bool AK, bool BK>
+__global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
+    using accv_t = typename TI::accv_t;
+    using acc_t = typename TI::acc_t;
+    using FA = Frag<AK>;
+    using FB = Frag<BK>;
+    // LDS instructions per k-slice, issued in the order the next k-slice's MFMAs consume them:
+    // A0, B0, B1, B2, B3, A1, A2, A3 (each fragment 1 or 2 instructions)
+    constexpr int NRD = 4 * FA::NI + 4 * FB::NI;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * OPND];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tile_m, tile_n;
+    raster(xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+    const uint16_t *A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+
+    Loader<AK> la;
+    Loader<BK> lb;
+    la.init(wave, lane, m0, p.M, p.lda);
+    lb.init(wave, lane, n0, p.N, p.ldb);
+    FA fa;
+    FB fb;
+    const uint32_t lds0 = lds_addr(smem);
+    fa.init(lane, wm * 128, lds0);
+    fb.init(lane, wn * 128, lds0 + OPND);
+
+    accv_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int nfull = p.K / BKE;
+
+    u32x4 af[2][4], bf[2][4];
+
+    // read instruction q (0 .. NRD-1) of k-slice j of `stage` into fragment buffer `buf`
+    auto rd = [&](int stage, int j, int buf, int q) {
+        // fragment order A0, B0, B1, B2, B3, A1, A2, A3
+        int idx = 0;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            const bool isA = f == 0 || f >= 5;
+            const int t = f == 0 ? 0 : (f <= 4 ? f - 1 : f - 4);
+            const int ni = isA ? FA::NI : FB::NI;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h < ni) {
+                    if (idx == q) {
+                        if (isA) fa.read(stage, t, j, h, af[buf][t]);
+                        else fb.read(stage, t, j, h, bf[buf][t]);
+                    }
+                    ++idx;
+                }
+            }
+        }
+    };
+    // MFMA number t (0..15) of a k-slice: A fragment t/4 times B fragment t%4
+    auto mma = [&](int buf, int t) {
+        const int i = t >> 2, j = t & 3;
+        acc[i][j] = TI::mma(bf[buf][j], af[buf][i], acc[i][j]);
+    };
+    // LDS addresses of operand slabs in a stage
+    auto dstA = [&](int st) { return lds0 + (uint32_t)(st * KC_BYTES); };
+    auto dstB = [&](int st) { return lds0 + (uint32_t)(OPND + st * KC_BYTES); };
+    auto issue_slab = [&](int s, int st) {
+        const uint16_t *sa = Loader<AK>::slab_base(A, p.lda, s * BKE);
+        const uint16_t *sb = Loader<BK>::slab_base(B, p.ldb, s * BKE);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) la.issue(sa, dstA(st), wave, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lb.issue(sb, dstB(st), wave, i);
+    };
+
+    if (nfull > 0) {
+        issue_slab(0, 0);
+        if (nfull > 1) {
+            issue_slab(1, 1);
+            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // slab 0 landed, slab 1 may fly
+        } else {
+            wait_vmcnt0();
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NRD; ++q) rd(0, 0, 0, q);
+    }
+
+    // Slab s reads buffer X; slab s+1 lives in Y.  The 16 loads of a slab are spread one per
+    // three MFMA slots over 47 slots: loads 0-4 of slab s+2 go out in k-slice 3 of slab s (after
+    // the barrier has freed X), loads 5-15 of slab s+1 in k-slices 0 and 1 of slab s; k-slice 2
+    // issues none, leaving time for the last ones to land before the barrier.  Bursting all 16
+    // at once fills the vector-memory queue and stalls the wave's in-order issue (MFMAs too).
+    //   dma_next:  issue loads 5-15 of slab s+1 into Y (its loads 0-4 went out in slab s-1)
+    //   dma_next2: issue loads 0-4 of slab s+2 into X
+    //   has_next:  slab s+1 exists (wait for it, read its k-slice 0)
+    auto slab_step = [&](int s, int X, int Y, bool dma_next, bool dma_next2, bool has_next) {
+        const uint16_t *na = Loader<AK>::slab_base(A, p.lda, (s + 1) * BKE);
+        const uint16_t *nb = Loader<BK>::slab_base(B, p.ldb, (s + 1) * BKE);
+        const uint16_t *n2a = Loader<AK>::slab_base(A, p.lda, (s + 2) * BKE);
+        const uint16_t *n2b = Loader<BK>::slab_base(B, p.ldb, (s + 2) * BKE);
+        auto dma = [&](const uint16_t *sa, const uint16_t *sb, int st, int d) {
+            if (d < 8) la.issue(sa, dstA(st), wave, d);
+            else lb.issue(sb, dstB(st), wave, d - 8);
+        };
+        // k-slices 0..2: MFMAs of slice j interleaved with the reads of slice j+1
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                mma(j & 1, t);
+                if (t < NRD) rd(X, j + 1, (j + 1) & 1, t);
+                if (dma_next && j < 2) {
+                    const int q = 15 + 16 * j + t;               // global load slot 15..46
+                    if (q % 3 == 0) dma(na, nb, Y, q / 3);       // loads 5..15
+                }
+                fence();
+            }
+        }
+        // k-slice 3: every read of X has been issued.  Finish them and our loads of slab s+1,
+        // meet at the barrier (after one MFMA, so the matrix core is busy meanwhile), then
+        // start refilling X with slab s+2 and read slice 0 of Y while the remaining MFMAs run.
+        wait_lgkmcnt0();
+        if (has_next) wait_vmcnt0();
+        fence();
+        mma(1, 0);
+        fence();
+        __syncthreads();
+        fence();
+#pragma unroll
+        for (int t = 1; t < 16; ++t) {
+            mma(1, t);
+            if (dma_next2) {
+                const int q = t - 1;                             // global load slot 0..14
+                if (q % 3 == 0) dma(n2a, n2b, X, q / 3);         // loads 0..4
+            }
+            if (has_next) {
+                if (t - 1 < NRD) rd(Y, 0, 0, t - 1);
+                if (t == 15 && NRD == 16) rd(Y, 0, 0, 15);
+            }
+            fence();
+        }
+    };
+
+    // two slabs per trip so the stage of every read and load is a compile-time constant; the
+    // flags are uniform branches (slab 1 was loaded whole by the prologue)
+#pragma unroll 1
+    for (int s = 0; s < nfull; s += 2) {
+        slab_step(s, 0, 1, s >= 1 && s + 1 < nfull, s + 2 < nfull, s + 1 < nfull);
+        if (s + 1 < nfull) slab_step(s + 1, 1, 0, s + 2 < nfull, s + 3 < nfull, s + 2 < nfull);
+    }
+
+    // K tail: one guarded slab through registers (zero fill past K)
+    const int k0 = nfull * BKE;
+    if (k0 < p.K) {
+        __syncthreads();
+        stage_tail<AK>(A, p.lda, m0, p.M, k0, p.K, smem, tid);
+        stage_tail<BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < NRD; ++q) rd(0, j, 0, q);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) mma(0, t);
+        }
+    }
+
+    store_tile<TO, acc_t>(p, m0 + wm * 128, n0 + wn * 128, lane, acc);
+}
+
+template <class TI, class TO, bool AT, bool BT>
+hipError_t launch_fast(const GemmParams &p, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT>), dim3(grid), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+template <class TI, class TO>
+const KernelEntry *lookup_fast(int op_a, int op_b) {
+    static const KernelEntry e[4] = {
+        {launch_fast<TI, TO, false, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast<TI, TO, false, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast<TI, TO, true, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast<TI, TO, true, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
+    };
+    if (op_a < 0 || op_a > 1 || op_b < 0 || op_b > 1) return nullptr;
+    return &e[op_a * 2 + op_b];
+}
+
+}  // namespace
+
+#if defined(TGE_PAIR_F16_F16)
+const KernelEntry *fast_f16_f16(int a, int b) { return lookup_fast<TF16, OF16>(a, b); }
+#elif defined(TGE_PAIR_F16_F32)
+const KernelEntry *fast_f16_f32(int a, int b) { return lookup_fast<TF16, OF32>(a, b); }
+#elif defined(TGE_PAIR_BF16_BF16)
+const KernelEntry *fast_bf16_bf16(int a, int b) { return lookup_fast<TBF16, OBF16>(a, b); }
+#elif defined(TGE_PAIR_BF16_F32)
+const KernelEntry *fast_bf16_f32(int a, int b) { return lookup_fast<TBF16, OF32>(a, b); }
+#else
+#error "define one 16-bit TGE_PAIR_* macro"
+#endif
+
+}  // namespace tge

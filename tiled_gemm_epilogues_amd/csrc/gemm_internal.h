@@ -40,4 +40,12 @@ const KernelEntry *kernels_bf16_bf16(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_bf16_f32(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_i8_i32(int op_a, int op_b, int cfg);
 
+// Fast 256x256 path for 16-bit inputs (gemm_fast.hip).  Preconditions: 16-byte aligned A/B
+// pointers and leading dimensions, K >= 64, M % 8 == 0 when A is stored transposed and
+// N % 8 == 0 when B is not.
+const KernelEntry *fast_f16_f16(int op_a, int op_b);
+const KernelEntry *fast_f16_f32(int op_a, int op_b);
+const KernelEntry *fast_bf16_bf16(int op_a, int op_b);
+const KernelEntry *fast_bf16_f32(int op_a, int op_b);
+
 }  // namespace tge

@@ -31,102 +31,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
+#include "device_common.hpp"
 #include "gemm_internal.h"
 
 namespace tge {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// ---- element types ---------------------------------------------------------------------------
-// Every MFMA step consumes 16 bytes of K per lane for each operand: 8 fp16/bf16, 16 int8, or
-// 4 fp32 (4 chained 32x32x2 instructions).
-
-struct TF16 {
-    static constexpr int E = 2;
-    using acc_t = float;
-    using accv_t = f32x16;
-    __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-};
-struct TBF16 {
-    static constexpr int E = 2;
-    using acc_t = float;
-    using accv_t = f32x16;
-    __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-};
-struct TI8 {
-    static constexpr int E = 1;
-    using acc_t = int;
-    using accv_t = i32x16;
-    __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
-        return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                     __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
-    }
-};
-struct TF32 {
-    static constexpr int E = 4;
-    using acc_t = float;
-    using accv_t = f32x16;
-    // lanes 0-31 and 32-63 each supply 4 consecutive k; instruction j takes element j of both,
-    // so the 4 instructions together cover 8 distinct k exactly once.
-    __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // copy the element out first: bit_cast of a vector-element lvalue reads element 0
-            const uint32_t aj = a[j], bj = b[j];
-            c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, aj),
-                                                     __builtin_bit_cast(float, bj), c, 0, 0, 0);
-        }
-        return c;
-    }
-};
-
-// output element types
-struct OF16 { using T = _Float16; static constexpr int E = 2; };
-struct OBF16 { using T = __bf16; static constexpr int E = 2; };
-struct OF32 { using T = float; static constexpr int E = 4; };
-struct OI32 { using T = int; static constexpr int E = 4; };
+using namespace dev;
 
 // ---- small helpers ---------------------------------------------------------------------------
-
-// 16-byte global load with no alignment requirement (gfx950 serves unaligned dwordx4 loads).
-__device__ __forceinline__ u32x4 ldg16(const uint8_t *p) {
-    u32x4 v;
-    __builtin_memcpy(&v, p, 16);
-    return v;
-}
-
-// Element-wise 16-byte chunk load: elements with index e < nvalid are read, the rest are 0.
-template <int E>
-__device__ __forceinline__ u32x4 ldg16_partial(const uint8_t *p, int nvalid) {
-    uint8_t tmp[16];
-#pragma unroll
-    for (int e = 0; e < 16 / E; ++e) {
-        if (e < nvalid) {
-#pragma unroll
-            for (int b = 0; b < E; ++b) tmp[e * E + b] = p[e * E + b];
-        } else {
-#pragma unroll
-            for (int b = 0; b < E; ++b) tmp[e * E + b] = 0;
-        }
-    }
-    u32x4 v;
-    __builtin_memcpy(&v, tmp, 16);
-    return v;
-}
 
 // Physical 16-byte chunk of logical chunk c in LDS row r (8 chunks of 16 bytes per row).
 // (r ^ r>>3) & 7 differs for 8 consecutive rows (fragment reads walk rows) and for rows
@@ -134,70 +47,6 @@ __device__ __forceinline__ u32x4 ldg16_partial(const uint8_t *p, int nvalid) {
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return (row * 8 + (chunk ^ swz(row))) * 16; }
-
-// Transpose a VE x VE block of E-byte elements held as VE rows of 16 bytes.
-template <int E>
-__device__ __forceinline__ void transpose_block(const u32x4 *in, u32x4 *out);
-
-template <>
-__device__ __forceinline__ void transpose_block<2>(const u32x4 *in, u32x4 *out) {
-    // out[e] word w = (in[2w] half e, in[2w+1] half e)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t lo = in[2 * w][e >> 1], hi = in[2 * w + 1][e >> 1];
-            // v_perm_b32: bytes 0-3 select from the second operand, 4-7 from the first
-            out[e][w] = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
-        }
-}
-
-template <>
-__device__ __forceinline__ void transpose_block<4>(const u32x4 *in, u32x4 *out) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) out[e][r] = in[r][e];
-}
-
-template <>
-__device__ __forceinline__ void transpose_block<1>(const u32x4 *in, u32x4 *out) {
-    // out[e] byte r = in[r] byte e.  First gather 4 rows' byte e into one word with two
-    // permutes per word.
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int wsel = e >> 2, bsel = e & 3;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t x0 = in[4 * w + 0][wsel], x1 = in[4 * w + 1][wsel];
-            uint32_t x2 = in[4 * w + 2][wsel], x3 = in[4 * w + 3][wsel];
-            // pick byte bsel of x0 (low) and x1 (next), then of x2, x3
-            uint32_t s01 = __builtin_amdgcn_perm(x1, x0, (uint32_t)(bsel | ((bsel + 4) << 8)) | 0x0c0c0000u);
-            uint32_t s23 = __builtin_amdgcn_perm(x3, x2, (uint32_t)(bsel | ((bsel + 4) << 8)) | 0x0c0c0000u);
-            out[e][w] = (s01 & 0xffffu) | (s23 << 16);
-        }
-    }
-}
-
-// XCD-aware re-mapping: the hardware hands workgroup w to XCD w % 8.  Give each XCD a
-// contiguous range of logical tile ids so the tiles resident on one XCD share its L2.
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-    constexpr int NX = 8;
-    int q = nwg / NX, r = nwg % NX;
-    int x = wg % NX, i = wg / NX;
-    return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-}
-
-// Grouped raster: consecutive ids walk down group_m tile rows, then move one tile column.
-__device__ __forceinline__ void raster(int id, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
-    int per_group = group_m * tiles_n;
-    int g = id / per_group;
-    int first = g * group_m;
-    int gm = min(tiles_m - first, group_m);
-    int in = id - g * per_group;
-    tm = first + in % gm;
-    tn = in / gm;
-}
 
 // ---- operand staging -------------------------------------------------------------------------
 // Side view of one operand: rows are the M (for A) or N (for B) index, columns the K index.
@@ -287,83 +136,6 @@ struct Stager<E, BMN, NT, false> {
     }
 };
 
-// ---- epilogue --------------------------------------------------------------------------------
-
-template <class O>
-__device__ __forceinline__ float cd_to_f32(typename O::T v) { return (float)v; }
-
-template <class O, class Acc>
-__device__ __forceinline__ void epilogue4(const GemmParams &p, int m, int n, const Acc v[4]) {
-    using T = typename O::T;
-    const int N = p.N;
-    const int64_t row = (int64_t)m * p.ldc;
-    T out[4];
-    if constexpr (std::is_same<Acc, int>::value) {
-        // integer path: alpha == 1, beta in {0, 1}
-        int t[4];
-        const int *bias = static_cast<const int *>(p.bias);
-        const T *C = static_cast<const T *>(p.C);
-        if (n + 3 < N) {
-            int cv[4] = {0, 0, 0, 0}, bv[4] = {0, 0, 0, 0};
-            if (p.has_beta) __builtin_memcpy(cv, C + row + n, 16);
-            if (p.has_bias) __builtin_memcpy(bv, bias + n, 16);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                t[e] = v[e] + cv[e] + bv[e];
-                if (p.relu) t[e] = max(t[e], 0);
-                out[e] = t[e];
-            }
-            __builtin_memcpy(static_cast<T *>(p.D) + row + n, out, sizeof(out));
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (n + e >= N) break;
-                int x = v[e];
-                if (p.has_beta) x += C[row + n + e];
-                if (p.has_bias) x += bias[n + e];
-                if (p.relu) x = max(x, 0);
-                static_cast<T *>(p.D)[row + n + e] = x;
-            }
-        }
-    } else {
-        const float *bias = static_cast<const float *>(p.bias);
-        const T *C = static_cast<const T *>(p.C);
-        if (n + 3 < N) {
-            float t[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t[e] = p.alpha * v[e];
-            if (p.has_beta) {
-                T cv[4];
-                __builtin_memcpy(cv, C + row + n, sizeof(cv));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] += p.beta * cd_to_f32<O>(cv[e]);
-            }
-            if (p.has_bias) {
-                float bv[4];
-                __builtin_memcpy(bv, bias + n, 16);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] += bv[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (p.relu) t[e] = t[e] > 0.0f ? t[e] : 0.0f;
-                out[e] = (T)t[e];
-            }
-            __builtin_memcpy(static_cast<T *>(p.D) + row + n, out, sizeof(out));
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (n + e >= N) break;
-                float x = p.alpha * v[e];
-                if (p.has_beta) x += p.beta * cd_to_f32<O>(C[row + n + e]);
-                if (p.has_bias) x += bias[n + e];
-                if (p.relu) x = x > 0.0f ? x : 0.0f;
-                static_cast<T *>(p.D)[row + n + e] = (T)x;
-            }
-        }
-    }
-}
-
 // ---- the kernel ------------------------------------------------------------------------------
 
 template <int BM, int BN, int WGM, int WGN, class TI, class TO, bool AT, bool BT>
@@ -452,21 +224,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
         __syncthreads();
     }
 
-    // epilogue: lane holds D[m][n .. n+3] for 4 column groups per MFMA tile
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * WTM + 32 * i + (lane & 31);
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + 32 * j + 8 * g + 4 * khalf;
-                acc_t v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                              acc[i][j][4 * g + 3]};
-                epilogue4<TO, acc_t>(p, m, n, v);
-            }
-    }
+    store_tile<TO, acc_t>(p, m0 + wm * WTM, n0 + wn * WTN, lane, acc);
 }
 
 template <int BM, int BN, int WGM, int WGN, class TI, class TO, bool AT, bool BT>
