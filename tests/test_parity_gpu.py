@@ -235,3 +235,34 @@ def test_fast_path_random_and_unaligned_fallback(lay, monkeypatch):
     # a pointer offset by one element forces the general kernel at run time: same result
     D2, _ = run(p, x, offset=1)
     check(p, x, D2, ref)
+
+
+# ---- the memory-bound path for M <= 64 (16-bit inputs, A not transposed) ----------------------
+
+SKINNY_SHAPES = [(1, 16, 32), (5, 40, 64), (16, 520, 320), (17, 64, 96), (33, 200, 1024),
+                 (48, 24, 160), (64, 4096, 128), (16, 4096, 4096)]
+
+
+@pytest.mark.parametrize("shape", SKINNY_SHAPES)
+@pytest.mark.parametrize("lb", ["N", "T"])
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_skinny_path_exact(ab, cd, lb, shape, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    M, N, K = shape
+    i = SKINNY_SHAPES.index(shape) * 2 + (lb == "T")
+    p = _exact(M, N, K, "N" + lb, ab, cd, EPIS[i % 4], *SCALARS[i % 4], key=(111, i))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_skinny" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
+def test_skinny_ineligible_shapes_fall_back(monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    # K not a multiple of 32, and A transposed: the general kernel runs, same results
+    for j, (lay, K) in enumerate([("NN", 100), ("TN", 64)]):
+        p = _exact(16, 128, K, lay, "f16", "f16", "bias_relu", 1.0, 0.0, key=(112, j))
+        x = synth.make_inputs(p)
+        D, pl = run(p, x)
+        assert "gemm_skinny" not in pl.describe()
+        check(p, x, D, reference(p, x), exact=True)

@@ -18,7 +18,8 @@ struct gemm_plan {
     int64_t M, N, K, lda, ldb, ldc;
     int op_a, op_b, ab, cd, epi;
     const KernelEntry *kernel;       // general kernel (always valid)
-    const KernelEntry *fast;         // fast kernel when the plan qualifies, else nullptr
+    const KernelEntry *fast;         // fast or skinny kernel when the plan qualifies, else nullptr
+    bool fast_is_skinny;             // grid of `fast` is one workgroup per 16 columns
     int tiles_m, tiles_n, group_m;
     unsigned grid;
     char desc[192];
@@ -55,6 +56,16 @@ FastLookup fast_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F32) return tge::fast_f16_f32;
     if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::fast_bf16_bf16;
     if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::fast_bf16_f32;
+    return nullptr;
+}
+
+using SkinnyLookup = const KernelEntry *(*)(int, int);
+
+SkinnyLookup skinny_table(int ab, int cd) {
+    if (ab == GEMM_F16 && cd == GEMM_F16) return tge::skinny_f16_f16;
+    if (ab == GEMM_F16 && cd == GEMM_F32) return tge::skinny_f16_f32;
+    if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::skinny_bf16_bf16;
+    if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::skinny_bf16_f32;
     return nullptr;
 }
 
@@ -153,6 +164,19 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
         (op_a == GEMM_OP_N || M % 8 == 0) && (op_b == GEMM_OP_T || N % 8 == 0))
         fast = ft(op_a, op_b);
 
+    // skinny path: M <= 64, memory bound; preferred over both tiled kernels when it applies
+    bool skinny = false;
+    SkinnyLookup st = skinny_table(ab_type, cd_type);
+    bool want_skinny = M <= 64;
+    if (fk && strcmp(fk, "general") == 0) want_skinny = false;
+    if (fk && strcmp(fk, "fast") == 0) want_skinny = false;
+    if (fk && strcmp(fk, "skinny") == 0) want_skinny = true;
+    if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % 32 == 0 &&
+        (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && (op_b == GEMM_OP_T || N % 8 == 0)) {
+        fast = st(op_b, (int)((M + 15) / 16));
+        skinny = fast != nullptr;
+    }
+
     gemm_plan *p = new (std::nothrow) gemm_plan;
     if (!p) return GEMM_STATUS_ALLOC_FAILED;
     p->M = M; p->N = N; p->K = K;
@@ -160,8 +184,9 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     p->op_a = op_a; p->op_b = op_b; p->ab = ab_type; p->cd = cd_type; p->epi = epi;
     p->kernel = k;
     p->fast = fast;
+    p->fast_is_skinny = skinny;
     const KernelEntry *shown = fast ? fast : k;
-    p->tiles_m = (int)((M + shown->bm - 1) / shown->bm);
+    p->tiles_m = skinny ? 1 : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
     p->grid = (unsigned)((int64_t)p->tiles_m * p->tiles_n);
@@ -210,7 +235,8 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     const KernelEntry *k = p->kernel;
     // the fast kernel needs 16-byte aligned operand pointers; else the general kernel runs
     if (p->fast && ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0) k = p->fast;
-    prm.tiles_m = (int)((p->M + k->bm - 1) / k->bm);
+    const bool sk = k == p->fast && p->fast_is_skinny;
+    prm.tiles_m = sk ? 1 : (int)((p->M + k->bm - 1) / k->bm);
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
     const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n);
     hipError_t e = k->launch(prm, grid, static_cast<hipStream_t>(stream));

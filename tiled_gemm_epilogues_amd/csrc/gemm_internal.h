@@ -48,4 +48,12 @@ const KernelEntry *fast_f16_f32(int op_a, int op_b);
 const KernelEntry *fast_bf16_bf16(int op_a, int op_b);
 const KernelEntry *fast_bf16_f32(int op_a, int op_b);
 
+// Memory-bound path for M <= 64 (gemm_skinny.hip); mt = ceil(M / 16).  Preconditions: 16-bit
+// inputs, op_a == N, K % 32 == 0, 16-byte aligned A/B pointers and leading dimensions,
+// N % 8 == 0 when B is not transposed.  One workgroup per 16 columns: grid = ceil(N / 16).
+const KernelEntry *skinny_f16_f16(int op_b, int mt);
+const KernelEntry *skinny_f16_f32(int op_b, int mt);
+const KernelEntry *skinny_bf16_bf16(int op_b, int mt);
+const KernelEntry *skinny_bf16_f32(int op_b, int mt);
+
 }  // namespace tge
