@@ -266,3 +266,22 @@ def test_skinny_ineligible_shapes_fall_back(monkeypatch):
         D, pl = run(p, x)
         assert "gemm_skinny" not in pl.describe()
         check(p, x, D, reference(p, x), exact=True)
+
+
+# int8 through the fast path: K >= 128 and leading dimensions / M,N multiples of 16
+FAST_SHAPES_I8 = [(256, 256, 128), (304, 528, 208), (512, 272, 256), (272, 16, 144),
+                  (16, 304, 384), (640, 512, 640), (1008, 784, 1008)]
+
+
+@pytest.mark.parametrize("shape", FAST_SHAPES_I8)
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_fast_path_int8_exact(lay, shape, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    M, N, K = shape
+    i = LAYOUTS.index(lay) + 4 * FAST_SHAPES_I8.index(shape)
+    epi = ["none", "relu", "bias", "bias_relu"][i % 4]
+    p = _exact(M, N, K, lay, "i8", "i32", epi, 1.0, 1.0 if i % 3 == 0 else 0.0, key=(113, i))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_fast" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)

@@ -15,7 +15,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtge.so")
 
 PAIRS = ["F32_F32", "F16_F16", "F16_F32", "BF16_BF16", "BF16_F32", "I8_I32"]
-FAST_PAIRS = ["F16_F16", "F16_F32", "BF16_BF16", "BF16_F32"]
+FAST_PAIRS = ["F16_F16", "F16_F32", "BF16_BF16", "BF16_F32", "I8_I32"]
+SKINNY_PAIRS = ["F16_F16", "F16_F32", "BF16_BF16", "BF16_F32"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -46,6 +47,7 @@ def build(verbose=False, jobs=None):
         obj = os.path.join(BUILD, f"gemm_fast_{pair.lower()}.o")
         steps.append([HIPCC, *FLAGS, f"-DTGE_PAIR_{pair}", "-c",
                       os.path.join(CSRC, "gemm_fast.hip"), "-o", obj])
+    for pair in SKINNY_PAIRS:
         obj = os.path.join(BUILD, f"gemm_skinny_{pair.lower()}.o")
         steps.append([HIPCC, *FLAGS, f"-DTGE_PAIR_{pair}", "-c",
                       os.path.join(CSRC, "gemm_skinny.hip"), "-o", obj])

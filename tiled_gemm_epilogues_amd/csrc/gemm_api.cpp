@@ -56,6 +56,7 @@ FastLookup fast_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F32) return tge::fast_f16_f32;
     if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::fast_bf16_bf16;
     if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::fast_bf16_f32;
+    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::fast_i8_i32;
     return nullptr;
 }
 
@@ -160,8 +161,9 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     bool want_fast = cfg == tge::CFG_256;
     if (fk && strcmp(fk, "fast") == 0) want_fast = true;
     if (fk && strcmp(fk, "general") == 0) want_fast = false;
-    if (ft && want_fast && K >= 64 && (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 &&
-        (op_a == GEMM_OP_N || M % 8 == 0) && (op_b == GEMM_OP_T || N % 8 == 0))
+    const int ve = 16 / eab;   // elements per 16-byte chunk
+    if (ft && want_fast && K >= 128 / eab && (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 &&
+        (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0))
         fast = ft(op_a, op_b);
 
     // skinny path: M <= 64, memory bound; preferred over both tiled kernels when it applies

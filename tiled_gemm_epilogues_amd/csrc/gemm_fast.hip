@@ -48,21 +48,38 @@ using namespace dev;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-constexpr int BM = 256, BN = 256, BKE = 64;          // tile; K slab in elements
+constexpr int BM = 256, BN = 256;                    // output tile
+constexpr int SLAB_BYTES = 128;                      // K bytes per slab: 64 fp16/bf16 or 128 int8
 constexpr int NT = 256;                              // 4 waves
-constexpr int KC_BYTES = 256 * 128;                  // one operand slab: 32 KiB either layout
+constexpr int KC_BYTES = 256 * SLAB_BYTES;           // one operand slab: 32 KiB either layout
 // LDS map: [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB each, so that every fragment
 // read is (base register) + (stage and k-slice offset as the instruction's 16-bit immediate)
 constexpr int OPND = 2 * KC_BYTES;                   // byte offset of operand B's stages
 
+// [mn][k] layout (K-contiguous operands): 256 rows of 128 B, 16-byte chunk c of row r at
+// c ^ swz_kc(r); identical in bytes for 8- and 16-bit elements.
 __device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int swz_mc(int k) {
-    const int q = k & 3;
-    return 4 * q + 2 * (q >> 1);
-}
 __device__ __forceinline__ int off_kc(int r, int c) { return r * 128 + ((c ^ swz_kc(r)) << 4); }
-__device__ __forceinline__ int off_mc(int k, int c) { return k * 512 + ((c ^ swz_mc(k)) << 4); }
+
+// [k][mn] layout (M/N-contiguous operands): 64 rows of 512 B (16-bit) or 128 rows of 256 B
+// (8-bit).  The transposing reads touch, per group of lanes served together, 4 (16-bit) or 8
+// (8-bit) consecutive rows at 2 adjacent 16-byte chunks; the swizzle gives those accesses
+// distinct banks for 32- and 64-bank LDS.
+template <int E>
+__device__ __forceinline__ int swz_mc(int k) {
+    if constexpr (E == 2) {
+        const int q = k & 3;
+        return 4 * q + 2 * (q >> 1);
+    } else {
+        const int q = k & 7;
+        return 2 * q + (q >> 2);
+    }
+}
+template <int E>
+__device__ __forceinline__ int off_mc(int k, int c) { return k * 256 * E + ((c ^ swz_mc<E>(k)) << 4); }
 
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -82,78 +99,86 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
 }
 
 // ---- per-operand direct-load plan -----------------------------------------------------------
-// Each wave issues 8 instructions per operand per slab.  For lane l and instruction i the byte
-// offset from the slab's base address is fixed for the whole kernel.
+// Each wave issues 8 instructions (1 KiB each) per operand per slab.  For lane l and instruction
+// i the byte offset from the slab's base address is fixed for the whole kernel.
 
-template <bool KC>
+template <int E, bool KC>
 struct Loader {
+    static constexpr int VE = 16 / E;    // elements per 16-byte chunk
     uint32_t voff[8];
 
     // row0: first M (or N) index of the tile; ext: M (or N); ld: leading dimension.
     __device__ __forceinline__ void init(int wave, int lane, int row0, int ext, int ld) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            const int blk = wave * 8 + i;                          // 1 KiB block of the slab
             if constexpr (KC) {
-                const int r = (wave * 8 + i) * 8 + (lane >> 3);   // tile row
-                const int c = (lane & 7) ^ swz_kc(r);             // logical chunk this lane fetches
+                const int r = blk * 8 + (lane >> 3);               // tile row (8 rows of 128 B)
+                const int c = (lane & 7) ^ swz_kc(r);              // logical chunk this lane fetches
                 const int gr = min(row0 + r, ext - 1);
-                voff[i] = (uint32_t)(gr * ld + c * 8) * 2u;
+                voff[i] = (uint32_t)(gr * ld + c * VE) * (uint32_t)E;
             } else {
-                const int k = (wave * 8 + i) * 2 + (lane >> 5);   // slab row (k)
-                const int c = (lane & 31) ^ swz_mc(k);
-                const int col = min(row0 + c * 8, ext - 8);       // ext % 8 == 0: whole chunks
-                voff[i] = (uint32_t)(k * ld + col) * 2u;
+                constexpr int CPR = 16 * E;                        // chunks per [k] row
+                const int k = blk * (64 / CPR) + lane / CPR;       // slab row (k)
+                const int c = (lane % CPR) ^ swz_mc<E>(k);
+                const int col = min(row0 + c * VE, ext - VE);      // ext % VE == 0: whole chunks
+                voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
             }
         }
     }
     // base of the slab whose K starts at element k0
-    __device__ __forceinline__ static const uint16_t *slab_base(const uint16_t *base, int ld, int k0) {
-        return KC ? base + k0 : base + (size_t)k0 * ld;
+    __device__ __forceinline__ static const uint8_t *slab_base(const uint8_t *base, int ld, int k0) {
+        return KC ? base + (size_t)k0 * E : base + (size_t)k0 * ld * E;
     }
     // instruction i of this wave: LDS block (wave*8 + i) of the operand slab at `dst`
-    __device__ __forceinline__ void issue(const uint16_t *sb, uint32_t dst, int wave, int i) const {
+    __device__ __forceinline__ void issue(const uint8_t *sb, uint32_t dst, int wave, int i) const {
         dma16(sb, voff[i], dst + (uint32_t)(wave * 8 + i) * 1024u);
     }
 };
 
 // Guarded staging of a partial slab (k0 .. K-1, zero beyond) into the same LDS layout.
-template <bool KC>
-__device__ void stage_tail(const uint16_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
+template <int E, bool KC>
+__device__ void stage_tail(const uint8_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
                            int tid) {
+    constexpr int VE = 16 / E;
     // 2048 chunks of 16 bytes per operand slab, 8 per thread
 #pragma unroll 1
     for (int i = 0; i < 8; ++i) {
         const int q = tid + NT * i;
-        uint16_t v[8];
+        uint8_t v[16];
         if constexpr (KC) {
             const int r = q >> 3, c = q & 7;
             const int gr = min(row0 + r, ext - 1);
-            const uint16_t *p = base + (size_t)gr * ld + k0 + c * 8;
+            const uint8_t *p = base + ((size_t)gr * ld + k0 + c * VE) * E;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (k0 + c * 8 + e < K) ? p[e] : (uint16_t)0;
+            for (int e = 0; e < VE; ++e)
+#pragma unroll
+                for (int b = 0; b < E; ++b) v[e * E + b] = (k0 + c * VE + e < K) ? p[e * E + b] : (uint8_t)0;
             __builtin_memcpy(dst + off_kc(r, c), v, 16);
         } else {
-            const int k = q >> 5, c = q & 31;
-            const int col = min(row0 + c * 8, ext - 8);
+            constexpr int CPR = 16 * E;
+            const int k = q / CPR, c = q % CPR;
+            const int col = min(row0 + c * VE, ext - VE);
             if (k0 + k < K) {
-                const uint16_t *p = base + (size_t)(k0 + k) * ld + col;
+                const uint8_t *p = base + ((size_t)(k0 + k) * ld + col) * E;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = p[e];
+                for (int e = 0; e < 16; ++e) v[e] = p[e];
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = 0;
+                for (int e = 0; e < 16; ++e) v[e] = 0;
             }
-            __builtin_memcpy(dst + off_mc(k, c), v, 16);
+            __builtin_memcpy(dst + off_mc<E>(k, c), v, 16);
         }
     }
 }
 
 // ---- fragment reads ---------------------------------------------------------------------------
-// Fragment (sub-tile t, k-slice j): lane l holds 8 consecutive k (k = 16j + 8*(l/32) + 0..7) of
-// tile row (or column) 32t + l%32, as 16 bytes.  A K-contiguous operand needs one ds_read_b128
-// per fragment, an M/N-contiguous one two transposing reads (k 0..3 and 4..7).
+// Fragment (sub-tile t, k-slice j): lane l holds 16 bytes of consecutive k (8 fp16/bf16 or 16
+// int8 values, k = j*KS + (l/32)*KS/2 + ..., KS = 32 bytes of K per k-slice) of tile row (or
+// column) 32t + l%32.  A K-contiguous operand needs one ds_read_b128 per fragment, an
+// M/N-contiguous one two transposing reads.
 
-template <bool KC>
+template <int E, bool KC>
 struct Frag {
     static constexpr int NI = KC ? 1 : 2;   // LDS instructions per fragment
     // byte address (LDS) of this lane's fragment in stage 0: per sub-tile and k-slice for a
@@ -168,14 +193,22 @@ struct Frag {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     addr[t][j] = opbase + (uint32_t)off_kc(r, 2 * j + (lane >> 5));
-            } else {
+            } else if constexpr (E == 2) {
                 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i % 4
                 // of the 8-byte chunks addressed by lanes i/4 + 4e, e = 0..3.  Lane a of the
                 // group therefore addresses k row a/4 and columns 4*(a%4) .. +3.
                 const int q = (lane & 15) >> 2;
                 const int k = 8 * (lane >> 5) + q;
                 const int col = wrow + 32 * t + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-                addr[t][0] = opbase + (uint32_t)(k * 512 + (((col >> 3) ^ swz_mc(k)) << 4) + (col & 7) * 2);
+                addr[t][0] = opbase + (uint32_t)(k * 512 + (((col >> 3) ^ swz_mc<2>(k)) << 4) + (col & 7) * 2);
+            } else {
+                // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
+                // the 8-byte chunks addressed by lanes i/8 + 2e, e = 0..7.  Lane a of the group
+                // therefore addresses k row a/2 and columns 8*(a%2) .. +7.
+                const int a = lane & 15;
+                const int k = 16 * (lane >> 5) + (a >> 1);
+                const int col = wrow + 32 * t + 16 * ((lane >> 4) & 1) + 8 * (a & 1);
+                addr[t][0] = opbase + (uint32_t)(k * 256 + (((col >> 4) ^ swz_mc<1>(k)) << 4) + (col & 15));
             }
         }
     }
@@ -183,12 +216,18 @@ struct Frag {
     __device__ __forceinline__ void read(int stage, int t, int j, int h, u32x4 &dst) const {
         if constexpr (KC) {
             dst = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)(addr[t][j] + stage * KC_BYTES);
-        } else {
+        } else if constexpr (E == 2) {
             // rows 16j + 4h + (0..3): the swizzle depends only on k & 3
             const uint32_t a = addr[t][0] + stage * KC_BYTES + (16 * j + 4 * h) * 512;
             s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
             dst[2 * h] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 0, 1));
             dst[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 2, 3));
+        } else {
+            // rows 32j + 8h + (0..7): the swizzle depends only on k & 7
+            const uint32_t a = addr[t][0] + stage * KC_BYTES + (32 * j + 8 * h) * 256;
+            i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)a);
+            dst[2 * h] = (uint32_t)v[0];
+            dst[2 * h + 1] = (uint32_t)v[1];
         }
     }
 };
@@ -197,8 +236,10 @@ template <class TI, class TO, bool AK, bool BK>
 __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     using accv_t = typename TI::accv_t;
     using acc_t = typename TI::acc_t;
-    using FA = Frag<AK>;
-    using FB = Frag<BK>;
+    constexpr int E = TI::E;
+    constexpr int BKE = SLAB_BYTES / E;       // K elements per slab
+    using FA = Frag<E, AK>;
+    using FB = Frag<E, BK>;
     // LDS instructions per k-slice, issued in the order the next k-slice's MFMAs consume them:
     // A0, B0, B1, B2, B3, A1, A2, A3 (each fragment 1 or 2 instructions)
     constexpr int NRD = 4 * FA::NI + 4 * FB::NI;
@@ -212,11 +253,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     raster(xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-    const uint16_t *A = static_cast<const uint16_t *>(p.A);
-    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+    const uint8_t *A = static_cast<const uint8_t *>(p.A);
+    const uint8_t *B = static_cast<const uint8_t *>(p.B);
 
-    Loader<AK> la;
-    Loader<BK> lb;
+    Loader<E, AK> la;
+    Loader<E, BK> lb;
     la.init(wave, lane, m0, p.M, p.lda);
     lb.init(wave, lane, n0, p.N, p.ldb);
     FA fa;
@@ -267,8 +308,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     auto dstA = [&](int st) { return lds0 + (uint32_t)(st * KC_BYTES); };
     auto dstB = [&](int st) { return lds0 + (uint32_t)(OPND + st * KC_BYTES); };
     auto issue_slab = [&](int s, int st) {
-        const uint16_t *sa = Loader<AK>::slab_base(A, p.lda, s * BKE);
-        const uint16_t *sb = Loader<BK>::slab_base(B, p.ldb, s * BKE);
+        const uint8_t *sa = Loader<E, AK>::slab_base(A, p.lda, s * BKE);
+        const uint8_t *sb = Loader<E, BK>::slab_base(B, p.ldb, s * BKE);
 #pragma unroll
         for (int i = 0; i < 8; ++i) la.issue(sa, dstA(st), wave, i);
 #pragma unroll
@@ -297,11 +338,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     //   dma_next2: issue loads 0-4 of slab s+2 into X
     //   has_next:  slab s+1 exists (wait for it, read its k-slice 0)
     auto slab_step = [&](int s, int X, int Y, bool dma_next, bool dma_next2, bool has_next) {
-        const uint16_t *na = Loader<AK>::slab_base(A, p.lda, (s + 1) * BKE);
-        const uint16_t *nb = Loader<BK>::slab_base(B, p.ldb, (s + 1) * BKE);
-        const uint16_t *n2a = Loader<AK>::slab_base(A, p.lda, (s + 2) * BKE);
-        const uint16_t *n2b = Loader<BK>::slab_base(B, p.ldb, (s + 2) * BKE);
-        auto dma = [&](const uint16_t *sa, const uint16_t *sb, int st, int d) {
+        const uint8_t *na = Loader<E, AK>::slab_base(A, p.lda, (s + 1) * BKE);
+        const uint8_t *nb = Loader<E, BK>::slab_base(B, p.ldb, (s + 1) * BKE);
+        const uint8_t *n2a = Loader<E, AK>::slab_base(A, p.lda, (s + 2) * BKE);
+        const uint8_t *n2b = Loader<E, BK>::slab_base(B, p.ldb, (s + 2) * BKE);
+        auto dma = [&](const uint8_t *sa, const uint8_t *sb, int st, int d) {
             if (d < 8) la.issue(sa, dstA(st), wave, d);
             else lb.issue(sb, dstB(st), wave, d - 8);
         };
@@ -356,8 +397,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     const int k0 = nfull * BKE;
     if (k0 < p.K) {
         __syncthreads();
-        stage_tail<AK>(A, p.lda, m0, p.M, k0, p.K, smem, tid);
-        stage_tail<BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid);
+        stage_tail<E, AK>(A, p.lda, m0, p.M, k0, p.K, smem, tid);
+        stage_tail<E, BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -379,6 +420,7 @@ hipError_t launch_fast(const GemmParams &p, unsigned grid, hipStream_t s) {
 
 template <class TI, class TO>
 const KernelEntry *lookup_fast(int op_a, int op_b) {
+    constexpr int BKE = SLAB_BYTES / TI::E;
     static const KernelEntry e[4] = {
         {launch_fast<TI, TO, false, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
         {launch_fast<TI, TO, false, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
@@ -399,8 +441,10 @@ const KernelEntry *fast_f16_f32(int a, int b) { return lookup_fast<TF16, OF32>(a
 const KernelEntry *fast_bf16_bf16(int a, int b) { return lookup_fast<TBF16, OBF16>(a, b); }
 #elif defined(TGE_PAIR_BF16_F32)
 const KernelEntry *fast_bf16_f32(int a, int b) { return lookup_fast<TBF16, OF32>(a, b); }
+#elif defined(TGE_PAIR_I8_I32)
+const KernelEntry *fast_i8_i32(int a, int b) { return lookup_fast<TI8, OI32>(a, b); }
 #else
-#error "define one 16-bit TGE_PAIR_* macro"
+#error "define one TGE_PAIR_* macro with a 16- or 8-bit input type"
 #endif
 
 }  // namespace tge

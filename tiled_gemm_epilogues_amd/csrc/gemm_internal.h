@@ -40,13 +40,14 @@ const KernelEntry *kernels_bf16_bf16(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_bf16_f32(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_i8_i32(int op_a, int op_b, int cfg);
 
-// Fast 256x256 path for 16-bit inputs (gemm_fast.hip).  Preconditions: 16-byte aligned A/B
-// pointers and leading dimensions, K >= 64, M % 8 == 0 when A is stored transposed and
-// N % 8 == 0 when B is not.
+// Fast 256x256 path for 16- and 8-bit inputs (gemm_fast.hip).  Preconditions: 16-byte aligned
+// A/B pointers and leading dimensions, K >= one slab (64 elements, 128 for int8), and M (when A
+// is stored transposed) and N (when B is not) multiples of 16 / element size.
 const KernelEntry *fast_f16_f16(int op_a, int op_b);
 const KernelEntry *fast_f16_f32(int op_a, int op_b);
 const KernelEntry *fast_bf16_bf16(int op_a, int op_b);
 const KernelEntry *fast_bf16_f32(int op_a, int op_b);
+const KernelEntry *fast_i8_i32(int op_a, int op_b);
 
 // Memory-bound path for M <= 64 (gemm_skinny.hip); mt = ceil(M / 16).  Preconditions: 16-bit
 // inputs, op_a == N, K % 32 == 0, 16-byte aligned A/B pointers and leading dimensions,
