@@ -8,8 +8,15 @@ from HIP events recorded on the launch stream) and the CPU oracle timed on a bou
 of the same workload on this host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME[:IDX]] [--no-cpu]
+  python bench.py --calibrate-copy     (plain 1 GiB device copies, for scaling HBM counters)
+
+roofline.traffic is the measured HBM traffic per launch (FETCH_SIZE + WRITE_SIZE from rocprofv3,
+each scaled by what the same counter reads for a plain copy of known size), taken from the
+summary profiles/traffic_<workload>.json when that summary was measured on the current kernel
+sources (it records their hash); otherwise null.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -41,6 +48,40 @@ def host_threads():
     return max(1, n)
 
 
+def kernel_source_hash():
+    """Hash of the HIP sources the timed kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_gemm_epilogues_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from a committed counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def calibrate_copy():
+    """Plain device-to-device copies of 1 GiB (the reference for scaling FETCH/WRITE_SIZE)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+
+
 def pick_workload(spec):
     import synth
     name, _, idx = spec.partition(":")
@@ -57,6 +98,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain 1 GiB copies (reference for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -72,6 +115,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     p = pick_workload(args.workload)
     log(f"[bench] workload {p.label()}")
@@ -132,33 +178,34 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4), "traffic": None}
-
-    # parity of the timed output on a row band and a sample of points (not timed)
-    import oracle
-    Dh = D.view(torch.int16).cpu().numpy().view(np.uint16) if p.cd in ("f16", "bf16") \
-        else D.cpu().numpy()
-    Dh = Dh.reshape(p.M, p.ldc)
+    roof["traffic"] = measured_traffic(args.workload.replace(":", "_"))
 
     cpu = None
     parity = None
     if not args.no_cpu:
+        # the CPU-baseline leg: the oracle timed on a row sample, which also checks those rows
+        # of the timed output (not timed)
+        import oracle
+        Dh = D.view(torch.int16).cpu().numpy().view(np.uint16) if p.cd in ("f16", "bf16") \
+            else D.cpu().numpy()
+        Dh = Dh.reshape(p.M, p.ldc)
         threads = host_threads()
-        # pilot on 32 rows, then size the sample for about --cpu-seconds of oracle work
-        r_pilot = min(32, p.M)
-        t0 = time.perf_counter()
-        oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab, C=x["C"],
-                    ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha, beta=p.beta, relu=p.relu,
-                    rows=(0, r_pilot), threads=threads)
-        pilot = time.perf_counter() - t0
-        rows = r_pilot
-        if pilot < args.cpu_seconds:
-            rows = int(r_pilot * args.cpu_seconds / max(pilot, 1e-3)) // 32 * 32
-            rows = max(r_pilot, min(p.M, rows))
-        t0 = time.perf_counter()
-        ref = oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab,
-                          C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
-                          beta=p.beta, relu=p.relu, rows=(0, rows), threads=threads)
-        t_cpu = time.perf_counter() - t0
+        # two pilots separate the fixed cost (decoding B) from the per-row cost; the sample is
+        # then sized for about --cpu-seconds of oracle work
+        def oracle_rows(r):
+            t0 = time.perf_counter()
+            out = oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab,
+                              C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
+                              beta=p.beta, relu=p.relu, rows=(0, r), threads=threads)
+            return time.perf_counter() - t0, out
+        r1, r2 = min(32, p.M), min(96, p.M)
+        t1, _ = oracle_rows(r1)
+        t2, _ = oracle_rows(r2) if r2 > r1 else (t1, None)
+        per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
+        fixed = max(t1 - r1 * per_row, 0.0)
+        rows = int((args.cpu_seconds - fixed) / per_row) // 32 * 32
+        rows = max(r1, min(p.M, rows))
+        t_cpu, ref = oracle_rows(rows)
         sample_flops = 2.0 * rows * p.N * p.K
         cpu = {"value": round(sample_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
