@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gemm_internal.h"
 
@@ -232,6 +234,100 @@ struct Frag {
     }
 };
 
+// ---- epilogue through LDS -------------------------------------------------------------------
+// One wave's 128x128 sub-tile, 32 rows at a time: values are computed in the accumulator layout
+// (alpha, beta*C, bias[j], ReLU, convert; lane l holds row 32i + l%32, columns 32j + 8g +
+// 4(l/32) + e), written row-major into the wave's private staging buffer (16-byte chunk c of
+// staged row r at c ^ (r % chunks-per-row)) and read back as 16-byte row pieces, so every store
+// instruction writes whole 128-byte lines of D instead of 16-byte pieces of 32 rows.
+template <class O>
+__device__ __forceinline__ constexpr int stg_bytes() { return 32 * 128 * (int)sizeof(typename O::T); }
+
+template <class O, class Acc, class AccV>
+__device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase, int nbase, int lane,
+                                                  AccV (&acc)[4][4], uint8_t *stg) {
+    using T = typename O::T;
+    constexpr bool INT = std::is_same<Acc, int>::value;
+    using Bt = typename std::conditional<INT, int, float>::type;
+    constexpr int ES = sizeof(T);
+    constexpr int RB = 128 * ES;           // staged row bytes
+    constexpr int CPR = RB / 16;           // 16-byte chunks per row
+    constexpr int VE = 16 / ES;            // elements per chunk
+    const int hi = lane >> 5, rl = lane & 31;
+    const int N = p.N;
+    const bool full_n = nbase + 128 <= N;
+    const Bt *bias = static_cast<const Bt *>(p.bias);
+    const T *C = static_cast<const T *>(p.C);
+    T *D = static_cast<T *>(p.D);
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = mbase + 32 * i + rl;
+        const bool mrow = m < p.M;
+        const int64_t row = (int64_t)min(m, p.M - 1) * p.ldc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = nbase + 32 * j + 8 * g + 4 * hi;
+                Bt bv[4] = {0, 0, 0, 0};
+                T cv[4] = {(T)0, (T)0, (T)0, (T)0};
+                if (full_n) {
+                    if (p.has_bias) __builtin_memcpy(bv, bias + n, sizeof(bv));
+                    if (p.has_beta && mrow) __builtin_memcpy(cv, C + row + n, sizeof(cv));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (p.has_bias && n + e < N) bv[e] = bias[n + e];
+                        if (p.has_beta && mrow && n + e < N) cv[e] = C[row + n + e];
+                    }
+                }
+                T out[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (INT) {
+                        int t = acc[i][j][4 * g + e] + bv[e];
+                        if (p.has_beta) t += (int)cv[e];
+                        if (p.relu) t = t > 0 ? t : 0;
+                        out[e] = (T)t;
+                    } else {
+                        float t = p.alpha * acc[i][j][4 * g + e];
+                        if (p.has_beta) t += p.beta * (float)cv[e];
+                        t += bv[e];
+                        if (p.relu) t = t > 0.0f ? t : 0.0f;
+                        out[e] = (T)t;
+                    }
+                }
+                const int byte = (32 * j + 8 * g + 4 * hi) * ES;
+                const int c = byte >> 4;
+                __builtin_memcpy(stg + rl * RB + ((c ^ (rl % CPR)) << 4) + (byte & 15), out, 4 * ES);
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // read back: 32 rows x CPR chunks, 16 bytes per lane per round
+#pragma unroll
+        for (int q = 0; q < 32 * CPR / 64; ++q) {
+            const int idx = q * 64 + lane;
+            const int rr = idx / CPR, c = idx % CPR;
+            u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rr * RB + ((c ^ (rr % CPR)) << 4));
+            const int mg = mbase + 32 * i + rr;
+            const int ng = nbase + c * VE;
+            if (mg < p.M) {
+                T *dst = D + (int64_t)mg * p.ldc + ng;
+                if (ng + VE <= N) {
+                    __builtin_memcpy(dst, &v, 16);
+                } else {
+                    T tv[VE];
+                    __builtin_memcpy(tv, &v, 16);
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        if (ng + e < N) dst[e] = tv[e];
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+
 template <class TI, class TO, bool AK, bool BK>
 __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     using accv_t = typename TI::accv_t;
@@ -243,39 +339,39 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     // LDS instructions per k-slice, issued in the order the next k-slice's MFMAs consume them:
     // A0, B0, B1, B2, B3, A1, A2, A3 (each fragment 1 or 2 instructions)
     constexpr int NRD = 4 * FA::NI + 4 * FB::NI;
+    // two pipeline stages of both operands; after the main loop the stage-1 halves of A and B
+    // (never used by the K tail) hold the four waves' epilogue staging buffers
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * OPND];
+    constexpr int STG = stg_bytes<TO>();
+    static_assert(2 * STG <= KC_BYTES, "two staging buffers fit in one operand stage");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    int tile_m, tile_n;
-    raster(xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
-    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);   // this workgroup's raster id
 
     const uint8_t *A = static_cast<const uint8_t *>(p.A);
     const uint8_t *B = static_cast<const uint8_t *>(p.B);
+    const uint32_t lds0 = lds_addr(smem);
+    uint8_t *const stg = smem + (wave < 2 ? 0 : OPND) + KC_BYTES + (wave & 1) * STG;
 
-    Loader<E, AK> la;
-    Loader<E, BK> lb;
-    la.init(wave, lane, m0, p.M, p.lda);
-    lb.init(wave, lane, n0, p.N, p.ldb);
     FA fa;
     FB fb;
-    const uint32_t lds0 = lds_addr(smem);
-    fa.init(lane, wm * 128, lds0);
-    fb.init(lane, wn * 128, lds0 + OPND);
-
-    accv_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    Loader<E, AK> la;
+    Loader<E, BK> lb;
+    int m0 = 0, n0 = 0;
+    auto set_tile = [&](int id) {
+        int tm, tn;
+        raster(id, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+        la.init(wave, lane, m0, p.M, p.lda);
+        lb.init(wave, lane, n0, p.N, p.ldb);
+    };
 
     const int nfull = p.K / BKE;
-
+    accv_t acc[4][4];
     u32x4 af[2][4], bf[2][4];
 
     // read instruction q (0 .. NRD-1) of k-slice j of `stage` into fragment buffer `buf`
@@ -315,21 +411,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) lb.issue(sb, dstB(st), wave, i);
     };
+    auto prologue = [&]() {
+        if (nfull > 0) issue_slab(0, 0);
+        if (nfull > 1) issue_slab(1, 1);
+    };
 
-    if (nfull > 0) {
-        issue_slab(0, 0);
-        if (nfull > 1) {
-            issue_slab(1, 1);
-            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // slab 0 landed, slab 1 may fly
-        } else {
-            wait_vmcnt0();
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < NRD; ++q) rd(0, 0, 0, q);
-    }
-
-    // Slab s reads buffer X; slab s+1 lives in Y.  The 16 loads of a slab are spread one per
+    // Slab s reads stage X; slab s+1 lives in Y.  The 16 loads of a slab are spread one per
     // three MFMA slots over 47 slots: loads 0-4 of slab s+2 go out in k-slice 3 of slab s (after
     // the barrier has freed X), loads 5-15 of slab s+1 in k-slices 0 and 1 of slab s; k-slice 2
     // issues none, leaving time for the last ones to land before the barrier.  Bursting all 16
@@ -385,6 +472,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         }
     };
 
+    set_tile(lid);
+    fa.init(lane, wm * 128, lds0);
+    fb.init(lane, wn * 128, lds0 + OPND);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    if (nfull > 0) {
+        prologue();
+        // slab 0 landed, slab 1 may still fly
+        if (nfull > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else wait_vmcnt0();
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NRD; ++q) rd(0, 0, 0, q);
+    }
+
     // two slabs per trip so the stage of every read and load is a compile-time constant; the
     // flags are uniform branches (slab 1 was loaded whole by the prologue)
 #pragma unroll 1
@@ -393,7 +500,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         if (s + 1 < nfull) slab_step(s + 1, 1, 0, s + 2 < nfull, s + 3 < nfull, s + 2 < nfull);
     }
 
-    // K tail: one guarded slab through registers (zero fill past K)
+    // K tail: one guarded slab through registers (zero fill past K), in stage 0
     const int k0 = nfull * BKE;
     if (k0 < p.K) {
         __syncthreads();
@@ -401,7 +508,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         stage_tail<E, BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid);
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j) {   // the 4 k-slices of the slab
 #pragma unroll
             for (int q = 0; q < NRD; ++q) rd(0, j, 0, q);
 #pragma unroll
@@ -409,7 +516,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         }
     }
 
-    store_tile<TO, acc_t>(p, m0 + wm * 128, n0 + wn * 128, lane, acc);
+    // every wave's reads of the stage-1 buffers ended before the last slab's barrier
+    store_tile_staged<TO, acc_t>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
 }
 
 template <class TI, class TO, bool AT, bool BT>
