@@ -23,16 +23,20 @@
 //  * pipeline per slab s (buffers X = s % 2, Y = the other): the fragments of k-slice j+1 are
 //    read while the MFMAs of k-slice j run; after the last read of X the wave waits for its own
 //    loads of slab s+1 and joins the barrier; then it issues the loads of slab s+2 into X and the
-//    first fragment reads of Y while the last k-slice's MFMAs run.
+//    first fragment reads of Y while the last k-slice's MFMAs run.  The loop body holds two slabs
+//    so that every stage index is a compile-time constant; the trips between the first and the
+//    last ones carry no branches.
 //  * M/N edges: source rows past the edge are clamped to the last valid row (their products
-//    only reach output rows/columns that the masked epilogue drops); the K tail (K % 64) runs one
-//    guarded register-staged slab with zero fill.
-//  * epilogue: identical to the general kernel (alpha, beta*C, bias[j], ReLU, convert, masked
-//    store from the accumulator registers).
+//    only reach output rows/columns that the masked epilogue drops); the K tail (K % slab) runs
+//    one guarded register-staged slab with zero fill.
+//  * epilogue (the epilogue building block of "Flexible GEMM" section 4, fused as in the bias and
+//    ReLU functor of "CUTLASS", "Fusing Element-wise Operations"): alpha, beta*C, bias[j], ReLU
+//    and the conversion run on the accumulators; the result goes through a per-wave LDS staging
+//    buffer so that D is written in whole 128-byte lines.
 //
-// Preconditions (checked by the host): 16-bit inputs, A/B base pointers and leading dimensions
-// 16-byte aligned, M (if A is stored transposed) and N (if B is not transposed) multiples of 8,
-// K >= 64.
+// Preconditions (checked by the host): 16- or 8-bit inputs, A/B base pointers and leading
+// dimensions 16-byte aligned, M (if A is stored transposed) and N (if B is not transposed)
+// multiples of 16 bytes' worth of elements, K of at least one slab.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -60,6 +64,8 @@ constexpr int KC_BYTES = 256 * SLAB_BYTES;           // one operand slab: 32 KiB
 // LDS map: [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB each, so that every fragment
 // read is (base register) + (stage and k-slice offset as the instruction's 16-bit immediate)
 constexpr int OPND = 2 * KC_BYTES;                   // byte offset of operand B's stages
+// a slab's 16 direct loads go out one per DMA_STRIDE MFMA slots (see slab_step)
+constexpr int DMA_STRIDE = 2;
 
 // [mn][k] layout (K-contiguous operands): 256 rows of 128 B, 16-byte chunk c of row r at
 // c ^ swz_kc(r); identical in bytes for 8- and 16-bit elements.
@@ -140,7 +146,7 @@ struct Loader {
 
 // Guarded staging of a partial slab (k0 .. K-1, zero beyond) into the same LDS layout.
 template <int E, bool KC>
-__device__ void stage_tail(const uint8_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
+__device__ __forceinline__ void stage_tail(const uint8_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
                            int tid) {
     constexpr int VE = 16 / E;
     // 2048 chunks of 16 bytes per operand slab, 8 per thread
@@ -240,10 +246,15 @@ struct Frag {
 // 4(l/32) + e), written row-major into the wave's private staging buffer (16-byte chunk c of
 // staged row r at c ^ (r % chunks-per-row)) and read back as 16-byte row pieces, so every store
 // instruction writes whole 128-byte lines of D instead of 16-byte pieces of 32 rows.
+//
+// Vector-memory operations complete in issue order, so a load issued after a store can only be
+// awaited together with that store.  Every load is therefore issued before the stores it would
+// otherwise wait behind: the bias once before the first block, the C values of block i+1 before
+// the stores of block i.
 template <class O>
 __device__ __forceinline__ constexpr int stg_bytes() { return 32 * 128 * (int)sizeof(typename O::T); }
 
-template <class O, class Acc, class AccV>
+template <class O, class Acc, bool BETA, class AccV>
 __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase, int nbase, int lane,
                                                   AccV (&acc)[4][4], uint8_t *stg) {
     using T = typename O::T;
@@ -254,46 +265,70 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
     constexpr int VE = 16 / ES;            // elements per chunk
     const int hi = lane >> 5, rl = lane & 31;
-    const int N = p.N;
+    const int M = p.M, N = p.N;
     const bool full_n = nbase + 128 <= N;
+    const bool full = full_n && mbase + 128 <= M;
     const Bt *bias = static_cast<const Bt *>(p.bias);
     const T *C = static_cast<const T *>(p.C);
     T *D = static_cast<T *>(p.D);
 
+    // bias of this lane's 64 columns, shared by the four row blocks
+    Bt bv[4][4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = nbase + 32 * j + 8 * g + 4 * hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[j][g][e] = 0;
+            if (p.has_bias) {
+                if (full_n) {
+                    __builtin_memcpy(bv[j][g], bias + n, sizeof(bv[j][g]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) bv[j][g][e] = bias[n + e];
+                }
+            }
+        }
+    // C values of row block i for this lane
+    T cv[4][4][4];
+    auto load_c = [&](int i) {
         const int m = mbase + 32 * i + rl;
-        const bool mrow = m < p.M;
-        const int64_t row = (int64_t)min(m, p.M - 1) * p.ldc;
+        const int64_t row = (int64_t)min(m, M - 1) * p.ldc;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = nbase + 32 * j + 8 * g + 4 * hi;
-                Bt bv[4] = {0, 0, 0, 0};
-                T cv[4] = {(T)0, (T)0, (T)0, (T)0};
                 if (full_n) {
-                    if (p.has_bias) __builtin_memcpy(bv, bias + n, sizeof(bv));
-                    if (p.has_beta && mrow) __builtin_memcpy(cv, C + row + n, sizeof(cv));
+                    __builtin_memcpy(cv[j][g], C + row + n, sizeof(cv[j][g]));
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (p.has_bias && n + e < N) bv[e] = bias[n + e];
-                        if (p.has_beta && mrow && n + e < N) cv[e] = C[row + n + e];
-                    }
+                    for (int e = 0; e < 4; ++e) cv[j][g][e] = n + e < N ? C[row + n + e] : (T)0;
                 }
+            }
+    };
+    if constexpr (BETA) load_c(0);
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
                 T out[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (INT) {
-                        int t = acc[i][j][4 * g + e] + bv[e];
-                        if (p.has_beta) t += (int)cv[e];
+                        int t = acc[i][j][4 * g + e] + bv[j][g][e];
+                        if constexpr (BETA) t += (int)cv[j][g][e];
                         if (p.relu) t = t > 0 ? t : 0;
                         out[e] = (T)t;
                     } else {
                         float t = p.alpha * acc[i][j][4 * g + e];
-                        if (p.has_beta) t += p.beta * (float)cv[e];
-                        t += bv[e];
+                        if constexpr (BETA) t += p.beta * (float)cv[j][g][e];
+                        t += bv[j][g][e];
                         if (p.relu) t = t > 0.0f ? t : 0.0f;
                         out[e] = (T)t;
                     }
@@ -302,6 +337,9 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
                 const int c = byte >> 4;
                 __builtin_memcpy(stg + rl * RB + ((c ^ (rl % CPR)) << 4) + (byte & 15), out, 4 * ES);
             }
+        if constexpr (BETA) {
+            if (i < 3) load_c(i + 1);
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // read back: 32 rows x CPR chunks, 16 bytes per lane per round
 #pragma unroll
@@ -311,8 +349,10 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
             u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rr * RB + ((c ^ (rr % CPR)) << 4));
             const int mg = mbase + 32 * i + rr;
             const int ng = nbase + c * VE;
-            if (mg < p.M) {
-                T *dst = D + (int64_t)mg * p.ldc + ng;
+            T *dst = D + (int64_t)mg * p.ldc + ng;
+            if (full) {
+                __builtin_memcpy(dst, &v, 16);
+            } else if (mg < M) {
                 if (ng + VE <= N) {
                     __builtin_memcpy(dst, &v, 16);
                 } else {
@@ -440,9 +480,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
             for (int t = 0; t < 16; ++t) {
                 mma(j & 1, t);
                 if (t < NRD) rd(X, j + 1, (j + 1) & 1, t);
-                if (dma_next && j < 2) {
-                    const int q = 15 + 16 * j + t;               // global load slot 15..46
-                    if (q % 3 == 0) dma(na, nb, Y, q / 3);       // loads 5..15
+                if (dma_next) {
+                    const int q = 15 + 16 * j + t;               // load slot 15..62
+                    if (q % DMA_STRIDE == 0 && q / DMA_STRIDE < 16) dma(na, nb, Y, q / DMA_STRIDE);
                 }
                 fence();
             }
@@ -461,8 +501,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         for (int t = 1; t < 16; ++t) {
             mma(1, t);
             if (dma_next2) {
-                const int q = t - 1;                             // global load slot 0..14
-                if (q % 3 == 0) dma(n2a, n2b, X, q / 3);         // loads 0..4
+                const int q = t - 1;                             // load slot 0..14
+                if (q % DMA_STRIDE == 0) dma(n2a, n2b, X, q / DMA_STRIDE);
             }
             if (has_next) {
                 if (t - 1 < NRD) rd(Y, 0, 0, t - 1);
@@ -492,13 +532,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         for (int q = 0; q < NRD; ++q) rd(0, 0, 0, q);
     }
 
-    // two slabs per trip so the stage of every read and load is a compile-time constant; the
-    // flags are uniform branches (slab 1 was loaded whole by the prologue)
-#pragma unroll 1
-    for (int s = 0; s < nfull; s += 2) {
-        slab_step(s, 0, 1, s >= 1 && s + 1 < nfull, s + 2 < nfull, s + 1 < nfull);
-        if (s + 1 < nfull) slab_step(s + 1, 1, 0, s + 2 < nfull, s + 3 < nfull, s + 2 < nfull);
+    // two slabs per trip so the stage of every read and load is a compile-time constant.  The
+    // first trip and the last ones take the flags as uniform branches (slab 1 was loaded whole by
+    // the prologue); the trips in between have every flag set and no branches.
+    auto trip = [&](int s) {
+        [[clang::always_inline]] slab_step(s, 0, 1, s >= 1 && s + 1 < nfull, s + 2 < nfull, s + 1 < nfull);
+        if (s + 1 < nfull)
+            [[clang::always_inline]] slab_step(s + 1, 1, 0, s + 2 < nfull, s + 3 < nfull, s + 2 < nfull);
+    };
+    int s = 0;
+    if (nfull > 0) {
+        [[clang::always_inline]] trip(0);
+        s = 2;
     }
+#pragma unroll 1
+    for (; s + 3 < nfull; s += 2) {
+        [[clang::always_inline]] slab_step(s, 0, 1, true, true, true);
+        [[clang::always_inline]] slab_step(s + 1, 1, 0, true, true, true);
+    }
+#pragma unroll 1
+    for (; s < nfull; s += 2) [[clang::always_inline]] trip(s);
 
     // K tail: one guarded slab through registers (zero fill past K), in stage 0
     const int k0 = nfull * BKE;
@@ -517,7 +570,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     }
 
     // every wave's reads of the stage-1 buffers ended before the last slab's barrier
-    store_tile_staged<TO, acc_t>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
+    if (p.has_beta) store_tile_staged<TO, acc_t, true>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
+    else store_tile_staged<TO, acc_t, false>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
 }
 
 template <class TI, class TO, bool AT, bool BT>
