@@ -254,7 +254,7 @@ struct Frag {
 template <class O>
 __device__ __forceinline__ constexpr int stg_bytes() { return 32 * 128 * (int)sizeof(typename O::T); }
 
-template <class O, class Acc, bool BETA, class AccV>
+template <class O, class Acc, bool BETA, bool FULL, class AccV>
 __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase, int nbase, int lane,
                                                   AccV (&acc)[4][4], uint8_t *stg) {
     using T = typename O::T;
@@ -264,10 +264,10 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
     constexpr int RB = 128 * ES;           // staged row bytes
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
     constexpr int VE = 16 / ES;            // elements per chunk
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef T t2 __attribute__((ext_vector_type(2)));
     const int hi = lane >> 5, rl = lane & 31;
     const int M = p.M, N = p.N;
-    const bool full_n = nbase + 128 <= N;
-    const bool full = full_n && mbase + 128 <= M;
     const Bt *bias = static_cast<const Bt *>(p.bias);
     const T *C = static_cast<const T *>(p.C);
     T *D = static_cast<T *>(p.D);
@@ -282,7 +282,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
 #pragma unroll
             for (int e = 0; e < 4; ++e) bv[j][g][e] = 0;
             if (p.has_bias) {
-                if (full_n) {
+                if constexpr (FULL) {
                     __builtin_memcpy(bv[j][g], bias + n, sizeof(bv[j][g]));
                 } else {
 #pragma unroll
@@ -295,13 +295,13 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
     T cv[4][4][4];
     auto load_c = [&](int i) {
         const int m = mbase + 32 * i + rl;
-        const int64_t row = (int64_t)min(m, M - 1) * p.ldc;
+        const int64_t row = (int64_t)(FULL ? m : min(m, M - 1)) * p.ldc;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = nbase + 32 * j + 8 * g + 4 * hi;
-                if (full_n) {
+                if constexpr (FULL) {
                     __builtin_memcpy(cv[j][g], C + row + n, sizeof(cv[j][g]));
                 } else {
 #pragma unroll
@@ -318,19 +318,30 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 T out[4];
+                if constexpr (INT) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (INT) {
+                    for (int e = 0; e < 4; ++e) {
                         int t = acc[i][j][4 * g + e] + bv[j][g][e];
                         if constexpr (BETA) t += (int)cv[j][g][e];
-                        if (p.relu) t = t > 0 ? t : 0;
+                        if (p.relu) t = max(t, 0);
                         out[e] = (T)t;
+                    }
+                } else {
+                    float t[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        t[e] = __builtin_fmaf(p.alpha, acc[i][j][4 * g + e], bv[j][g][e]);
+                        if constexpr (BETA) t[e] = __builtin_fmaf(p.beta, (float)cv[j][g][e], t[e]);
+                        if (p.relu) t[e] = __builtin_fmaxf(t[e], 0.0f);
+                    }
+                    if constexpr (ES == 2) {
+                        // two-at-a-time conversion (round to nearest even)
+                        const t2 lo = __builtin_convertvector((f32x2){t[0], t[1]}, t2);
+                        const t2 hi2 = __builtin_convertvector((f32x2){t[2], t[3]}, t2);
+                        out[0] = lo[0]; out[1] = lo[1]; out[2] = hi2[0]; out[3] = hi2[1];
                     } else {
-                        float t = p.alpha * acc[i][j][4 * g + e];
-                        if constexpr (BETA) t += p.beta * (float)cv[j][g][e];
-                        t += bv[j][g][e];
-                        if (p.relu) t = t > 0.0f ? t : 0.0f;
-                        out[e] = (T)t;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = (T)t[e];
                     }
                 }
                 const int byte = (32 * j + 8 * g + 4 * hi) * ES;
@@ -340,8 +351,8 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
         if constexpr (BETA) {
             if (i < 3) load_c(i + 1);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // read back: 32 rows x CPR chunks, 16 bytes per lane per round
+        // read back (the wave's LDS operations execute in order): 32 rows x CPR chunks, 16 bytes
+        // per lane per round
 #pragma unroll
         for (int q = 0; q < 32 * CPR / 64; ++q) {
             const int idx = q * 64 + lane;
@@ -350,7 +361,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
             const int mg = mbase + 32 * i + rr;
             const int ng = nbase + c * VE;
             T *dst = D + (int64_t)mg * p.ldc + ng;
-            if (full) {
+            if constexpr (FULL) {
                 __builtin_memcpy(dst, &v, 16);
             } else if (mg < M) {
                 if (ng + VE <= N) {
@@ -364,7 +375,20 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
                 }
             }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+
+template <class O, class Acc, class AccV>
+__device__ __forceinline__ void epilogue(const GemmParams &p, int mbase, int nbase, int lane,
+                                         AccV (&acc)[4][4], uint8_t *stg) {
+    // interior wave tiles (the common case) take a path with no edge checks
+    const bool full = mbase + 128 <= p.M && nbase + 128 <= p.N;
+    if (full) {
+        if (p.has_beta) store_tile_staged<O, Acc, true, true>(p, mbase, nbase, lane, acc, stg);
+        else store_tile_staged<O, Acc, false, true>(p, mbase, nbase, lane, acc, stg);
+    } else {
+        if (p.has_beta) store_tile_staged<O, Acc, true, false>(p, mbase, nbase, lane, acc, stg);
+        else store_tile_staged<O, Acc, false, false>(p, mbase, nbase, lane, acc, stg);
     }
 }
 
@@ -570,8 +594,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     }
 
     // every wave's reads of the stage-1 buffers ended before the last slab's barrier
-    if (p.has_beta) store_tile_staged<TO, acc_t, true>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
-    else store_tile_staged<TO, acc_t, false>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
+    epilogue<TO, acc_t>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
 }
 
 template <class TI, class TO, bool AT, bool BT>
