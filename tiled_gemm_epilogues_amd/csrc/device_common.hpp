@@ -15,6 +15,7 @@ namespace dev {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -27,8 +28,14 @@ struct TF16 {
     static constexpr int E = 2;
     using acc_t = float;
     using accv_t = f32x16;
+    using accv16_t = f32x4;
     __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    // 16x16 output, K = 32 per step (8 values per lane and operand, as above)
+    __device__ static accv16_t mma16(u32x4 a, u32x4 b, accv16_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
 };
@@ -36,8 +43,13 @@ struct TBF16 {
     static constexpr int E = 2;
     using acc_t = float;
     using accv_t = f32x16;
+    using accv16_t = f32x4;
     __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static accv16_t mma16(u32x4 a, u32x4 b, accv16_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
 };
@@ -45,8 +57,14 @@ struct TI8 {
     static constexpr int E = 1;
     using acc_t = int;
     using accv_t = i32x16;
+    using accv16_t = i32x4;
     __device__ static accv_t mma(u32x4 a, u32x4 b, accv_t c) {
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                     __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    }
+    // 16x16 output, K = 64 per step (16 values per lane and operand)
+    __device__ static accv16_t mma16(u32x4 a, u32x4 b, accv16_t c) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
                                                      __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
     }
 };

@@ -1,5 +1,6 @@
-// Fast path for large fp16/bf16 GEMMs on gfx950: 256x256 output tile per workgroup, 4 waves of
-// 128x128 (4x4 MFMA 32x32x16 tiles, accumulators in AGPRs), K walked in slabs of 64.
+// Fast path for large fp16/bf16/int8 GEMMs on gfx950: 256x256 output tile per workgroup, 4 waves
+// of 128x128 (8x8 MFMA 16x16 tiles, or 4x4 32x32 tiles; 256 accumulators per lane in AGPRs), K
+// walked in slabs of 128 bytes (64 fp16/bf16, 128 int8).
 //
 // The blocking follows "Flexible Performant GEMM Kernels on GPUs" (section 3: tiles copied up
 // the memory hierarchy, global -> shared -> registers, then matrix-multiply-accumulate) and the
@@ -64,8 +65,6 @@ constexpr int KC_BYTES = 256 * SLAB_BYTES;           // one operand slab: 32 KiB
 // LDS map: [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB each, so that every fragment
 // read is (base register) + (stage and k-slice offset as the instruction's 16-bit immediate)
 constexpr int OPND = 2 * KC_BYTES;                   // byte offset of operand B's stages
-// a slab's 16 direct loads go out one per DMA_STRIDE MFMA slots (see slab_step)
-constexpr int DMA_STRIDE = 2;
 
 // [mn][k] layout (K-contiguous operands): 256 rows of 128 B, 16-byte chunk c of row r at
 // c ^ swz_kc(r); identical in bytes for 8- and 16-bit elements.
@@ -181,41 +180,55 @@ __device__ __forceinline__ void stage_tail(const uint8_t *base, int ld, int row0
 }
 
 // ---- fragment reads ---------------------------------------------------------------------------
-// Fragment (sub-tile t, k-slice j): lane l holds 16 bytes of consecutive k (8 fp16/bf16 or 16
-// int8 values, k = j*KS + (l/32)*KS/2 + ..., KS = 32 bytes of K per k-slice) of tile row (or
-// column) 32t + l%32.  A K-contiguous operand needs one ds_read_b128 per fragment, an
-// M/N-contiguous one two transposing reads.
+// MF = 32 (MFMA 32x32, k-slice of 32 bytes of K): fragment (sub-tile t, k-slice j) gives lane l
+// 16 bytes of consecutive k (k = j*KS + (l/32)*KS/2 + ..., KS = 32 bytes) of tile row (or
+// column) 32t + l%32.  MF = 16 (MFMA 16x16, k-slice of 64 bytes): lane l gets 16 bytes of
+// consecutive k (k = j*KS + (l/16)*KS/4 + ..., KS = 64 bytes) of row 16t + l%16.  A K-contiguous
+// operand needs one ds_read_b128 per fragment, an M/N-contiguous one two transposing reads.
 
-template <int E, bool KC>
+template <int MF>
+struct Shape {
+    static constexpr int NF = MF == 32 ? 4 : 8;     // fragments per operand and k-slice
+    static constexpr int NS = MF == 32 ? 4 : 2;     // k-slices per slab
+    static constexpr int NMS = NF * NF;             // MFMAs per k-slice
+    static constexpr int KSB = SLAB_BYTES / NS;     // bytes of K per k-slice
+};
+
+template <int E, bool KC, int MF>
 struct Frag {
+    using S = Shape<MF>;
+    static constexpr int NF = S::NF;
     static constexpr int NI = KC ? 1 : 2;   // LDS instructions per fragment
     // byte address (LDS) of this lane's fragment in stage 0: per sub-tile and k-slice for a
     // K-contiguous operand (the XOR swizzle is not additive), per sub-tile otherwise
-    uint32_t addr[4][KC ? 4 : 1];
+    uint32_t addr[NF][KC ? S::NS : 1];
 
     __device__ __forceinline__ void init(int lane, int wrow, uint32_t opbase) {
+        constexpr int LR = MF;                       // lanes per row group
+        const int lr = lane & (LR - 1), lg = lane / LR;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NF; ++t) {
             if constexpr (KC) {
-                const int r = wrow + 32 * t + (lane & 31);
+                const int r = wrow + MF * t + lr;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    addr[t][j] = opbase + (uint32_t)off_kc(r, 2 * j + (lane >> 5));
+                for (int j = 0; j < S::NS; ++j)
+                    addr[t][j] = opbase + (uint32_t)off_kc(r, (S::KSB / 16) * j + lg);
             } else if constexpr (E == 2) {
                 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i % 4
                 // of the 8-byte chunks addressed by lanes i/4 + 4e, e = 0..3.  Lane a of the
-                // group therefore addresses k row a/4 and columns 4*(a%4) .. +3.
+                // group therefore addresses k row a/4 and columns 4*(a%4) .. +3; lane group g
+                // (of 64/MF... groups of 16) covers k 8g.. (MF 16) or 8(l/32).. (MF 32).
                 const int q = (lane & 15) >> 2;
-                const int k = 8 * (lane >> 5) + q;
-                const int col = wrow + 32 * t + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                const int k = 8 * lg + q;
+                const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
                 addr[t][0] = opbase + (uint32_t)(k * 512 + (((col >> 3) ^ swz_mc<2>(k)) << 4) + (col & 7) * 2);
             } else {
                 // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
                 // the 8-byte chunks addressed by lanes i/8 + 2e, e = 0..7.  Lane a of the group
                 // therefore addresses k row a/2 and columns 8*(a%2) .. +7.
                 const int a = lane & 15;
-                const int k = 16 * (lane >> 5) + (a >> 1);
-                const int col = wrow + 32 * t + 16 * ((lane >> 4) & 1) + 8 * (a & 1);
+                const int k = 16 * lg + (a >> 1);
+                const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 8 * (a & 1);
                 addr[t][0] = opbase + (uint32_t)(k * 256 + (((col >> 4) ^ swz_mc<1>(k)) << 4) + (col & 15));
             }
         }
@@ -225,14 +238,14 @@ struct Frag {
         if constexpr (KC) {
             dst = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)(addr[t][j] + stage * KC_BYTES);
         } else if constexpr (E == 2) {
-            // rows 16j + 4h + (0..3): the swizzle depends only on k & 3
-            const uint32_t a = addr[t][0] + stage * KC_BYTES + (16 * j + 4 * h) * 512;
+            // k rows j*KS/2 + 4h + (0..3) past the lane's base: the swizzle depends only on k & 3
+            const uint32_t a = addr[t][0] + stage * KC_BYTES + ((S::KSB / 2) * j + 4 * h) * 512;
             s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
             dst[2 * h] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 0, 1));
             dst[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 2, 3));
         } else {
-            // rows 32j + 8h + (0..7): the swizzle depends only on k & 7
-            const uint32_t a = addr[t][0] + stage * KC_BYTES + (32 * j + 8 * h) * 256;
+            // k rows j*KS + 8h + (0..7) past the lane's base: the swizzle depends only on k & 7
+            const uint32_t a = addr[t][0] + stage * KC_BYTES + (S::KSB * j + 8 * h) * 256;
             i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)a);
             dst[2 * h] = (uint32_t)v[0];
             dst[2 * h + 1] = (uint32_t)v[1];
@@ -241,11 +254,15 @@ struct Frag {
 };
 
 // ---- epilogue through LDS -------------------------------------------------------------------
-// One wave's 128x128 sub-tile, 32 rows at a time: values are computed in the accumulator layout
-// (alpha, beta*C, bias[j], ReLU, convert; lane l holds row 32i + l%32, columns 32j + 8g +
-// 4(l/32) + e), written row-major into the wave's private staging buffer (16-byte chunk c of
-// staged row r at c ^ (r % chunks-per-row)) and read back as 16-byte row pieces, so every store
-// instruction writes whole 128-byte lines of D instead of 16-byte pieces of 32 rows.
+// One wave's 128x128 sub-tile, in four blocks of 32 rows: values are computed in the
+// accumulator layout (alpha, beta*C, bias[j], ReLU, convert), written row-major into the wave's
+// private staging buffer (16-byte chunk c of staged row r at c ^ (r % chunks-per-row)) and read
+// back as 16-byte row pieces, so every store instruction writes whole 128-byte lines of D
+// instead of 16-byte pieces of 32 rows.
+//
+// In both MFMA shapes a lane holds, per block, 16 groups of 4 consecutive columns of one row:
+//   MF 32: group q = 4j + g of block b is acc[b][j][4g..4g+3], row l%32, columns 32j + 8g + 4(l/32)
+//   MF 16: group q = 8i + j of block b is acc[2b+i][j][0..3], row 16i + l%16, columns 16j + 4(l/16)
 //
 // Vector-memory operations complete in issue order, so a load issued after a store can only be
 // awaited together with that store.  Every load is therefore issued before the stores it would
@@ -254,10 +271,21 @@ struct Frag {
 template <class O>
 __device__ __forceinline__ constexpr int stg_bytes() { return 32 * 128 * (int)sizeof(typename O::T); }
 
-template <class O, class Acc, bool BETA, bool FULL, class AccV>
+template <int MF>
+struct EpiMap {
+    static constexpr int NBG = MF == 32 ? 16 : 8;   // distinct column groups per lane
+    __device__ static int row(int q, int lane) { return MF == 32 ? (lane & 31) : 16 * (q >> 3) + (lane & 15); }
+    __device__ static int col(int q, int lane) {
+        return MF == 32 ? 32 * (q >> 2) + 8 * (q & 3) + 4 * (lane >> 5) : 16 * (q & 7) + 4 * (lane >> 4);
+    }
+    __device__ static int bgroup(int q) { return MF == 32 ? q : (q & 7); }
+};
+
+template <class O, class Acc, int MF, bool BETA, bool FULL, class AccV, int NF>
 __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase, int nbase, int lane,
-                                                  AccV (&acc)[4][4], uint8_t *stg) {
+                                                  AccV (&acc)[NF][NF], uint8_t *stg) {
     using T = typename O::T;
+    using Map = EpiMap<MF>;
     constexpr bool INT = std::is_same<Acc, int>::value;
     using Bt = typename std::conditional<INT, int, float>::type;
     constexpr int ES = sizeof(T);
@@ -266,90 +294,90 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
     constexpr int VE = 16 / ES;            // elements per chunk
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef T t2 __attribute__((ext_vector_type(2)));
-    const int hi = lane >> 5, rl = lane & 31;
     const int M = p.M, N = p.N;
     const Bt *bias = static_cast<const Bt *>(p.bias);
     const T *C = static_cast<const T *>(p.C);
     T *D = static_cast<T *>(p.D);
+    // accumulator value e of group q in block b
+    auto accv = [&](int b, int q, int e) -> Acc {
+        if constexpr (MF == 32) return acc[b][q >> 2][4 * (q & 3) + e];
+        else return acc[2 * b + (q >> 3)][q & 7][e];
+    };
 
-    // bias of this lane's 64 columns, shared by the four row blocks
-    Bt bv[4][4][4];
+    // bias of this lane's columns, shared by the four row blocks
+    Bt bv[Map::NBG][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int q = 0; q < Map::NBG; ++q) {
+        const int n = nbase + Map::col(q, lane);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = nbase + 32 * j + 8 * g + 4 * hi;
+        for (int e = 0; e < 4; ++e) bv[q][e] = 0;
+        if (p.has_bias) {
+            if constexpr (FULL) {
+                __builtin_memcpy(bv[q], bias + n, sizeof(bv[q]));
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bv[j][g][e] = 0;
-            if (p.has_bias) {
-                if constexpr (FULL) {
-                    __builtin_memcpy(bv[j][g], bias + n, sizeof(bv[j][g]));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) bv[j][g][e] = bias[n + e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) bv[q][e] = bias[n + e];
             }
         }
-    // C values of row block i for this lane
-    T cv[4][4][4];
-    auto load_c = [&](int i) {
-        const int m = mbase + 32 * i + rl;
-        const int64_t row = (int64_t)(FULL ? m : min(m, M - 1)) * p.ldc;
+    }
+    // C values of row block b for this lane
+    T cv[16][4];
+    auto load_c = [&](int b) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int q = 0; q < 16; ++q) {
+            const int m = mbase + 32 * b + Map::row(q, lane);
+            const int64_t row = (int64_t)(FULL ? m : min(m, M - 1)) * p.ldc;
+            const int n = nbase + Map::col(q, lane);
+            if constexpr (FULL) {
+                __builtin_memcpy(cv[q], C + row + n, sizeof(cv[q]));
+            } else {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = nbase + 32 * j + 8 * g + 4 * hi;
-                if constexpr (FULL) {
-                    __builtin_memcpy(cv[j][g], C + row + n, sizeof(cv[j][g]));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cv[j][g][e] = n + e < N ? C[row + n + e] : (T)0;
-                }
+                for (int e = 0; e < 4; ++e) cv[q][e] = n + e < N ? C[row + n + e] : (T)0;
             }
+        }
     };
     if constexpr (BETA) load_c(0);
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int b = 0; b < 4; ++b) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int q = 0; q < 16; ++q) {
+            const Bt *bq = bv[Map::bgroup(q)];
+            T out[4];
+            if constexpr (INT) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                T out[4];
-                if constexpr (INT) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        int t = acc[i][j][4 * g + e] + bv[j][g][e];
-                        if constexpr (BETA) t += (int)cv[j][g][e];
-                        if (p.relu) t = max(t, 0);
-                        out[e] = (T)t;
-                    }
-                } else {
-                    float t[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t[e] = __builtin_fmaf(p.alpha, acc[i][j][4 * g + e], bv[j][g][e]);
-                        if constexpr (BETA) t[e] = __builtin_fmaf(p.beta, (float)cv[j][g][e], t[e]);
-                        if (p.relu) t[e] = __builtin_fmaxf(t[e], 0.0f);
-                    }
-                    if constexpr (ES == 2) {
-                        // two-at-a-time conversion (round to nearest even)
-                        const t2 lo = __builtin_convertvector((f32x2){t[0], t[1]}, t2);
-                        const t2 hi2 = __builtin_convertvector((f32x2){t[2], t[3]}, t2);
-                        out[0] = lo[0]; out[1] = lo[1]; out[2] = hi2[0]; out[3] = hi2[1];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) out[e] = (T)t[e];
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    int t = accv(b, q, e) + bq[e];
+                    if constexpr (BETA) t += (int)cv[q][e];
+                    if (p.relu) t = max(t, 0);
+                    out[e] = (T)t;
                 }
-                const int byte = (32 * j + 8 * g + 4 * hi) * ES;
-                const int c = byte >> 4;
-                __builtin_memcpy(stg + rl * RB + ((c ^ (rl % CPR)) << 4) + (byte & 15), out, 4 * ES);
+            } else {
+                float t[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    t[e] = __builtin_fmaf(p.alpha, accv(b, q, e), bq[e]);
+                    if constexpr (BETA) t[e] = __builtin_fmaf(p.beta, (float)cv[q][e], t[e]);
+                    if (p.relu) t[e] = __builtin_fmaxf(t[e], 0.0f);
+                }
+                if constexpr (ES == 2) {
+                    // two-at-a-time conversion (round to nearest even)
+                    const t2 lo = __builtin_convertvector((f32x2){t[0], t[1]}, t2);
+                    const t2 hi2 = __builtin_convertvector((f32x2){t[2], t[3]}, t2);
+                    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi2[0]; out[3] = hi2[1];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = (T)t[e];
+                }
             }
+            const int rl = Map::row(q, lane);
+            const int byte = Map::col(q, lane) * ES;
+            const int c = byte >> 4;
+            __builtin_memcpy(stg + rl * RB + ((c ^ (rl % CPR)) << 4) + (byte & 15), out, 4 * ES);
+        }
         if constexpr (BETA) {
-            if (i < 3) load_c(i + 1);
+            if (b < 3) load_c(b + 1);
         }
         // read back (the wave's LDS operations execute in order): 32 rows x CPR chunks, 16 bytes
         // per lane per round
@@ -358,7 +386,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
             const int idx = q * 64 + lane;
             const int rr = idx / CPR, c = idx % CPR;
             u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rr * RB + ((c ^ (rr % CPR)) << 4));
-            const int mg = mbase + 32 * i + rr;
+            const int mg = mbase + 32 * b + rr;
             const int ng = nbase + c * VE;
             T *dst = D + (int64_t)mg * p.ldc + ng;
             if constexpr (FULL) {
@@ -378,31 +406,46 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
     }
 }
 
-template <class O, class Acc, class AccV>
+template <class O, class Acc, int MF, class AccV, int NF>
 __device__ __forceinline__ void epilogue(const GemmParams &p, int mbase, int nbase, int lane,
-                                         AccV (&acc)[4][4], uint8_t *stg) {
+                                         AccV (&acc)[NF][NF], uint8_t *stg) {
     // interior wave tiles (the common case) take a path with no edge checks
     const bool full = mbase + 128 <= p.M && nbase + 128 <= p.N;
     if (full) {
-        if (p.has_beta) store_tile_staged<O, Acc, true, true>(p, mbase, nbase, lane, acc, stg);
-        else store_tile_staged<O, Acc, false, true>(p, mbase, nbase, lane, acc, stg);
+        if (p.has_beta) store_tile_staged<O, Acc, MF, true, true>(p, mbase, nbase, lane, acc, stg);
+        else store_tile_staged<O, Acc, MF, false, true>(p, mbase, nbase, lane, acc, stg);
     } else {
-        if (p.has_beta) store_tile_staged<O, Acc, true, false>(p, mbase, nbase, lane, acc, stg);
-        else store_tile_staged<O, Acc, false, false>(p, mbase, nbase, lane, acc, stg);
+        if (p.has_beta) store_tile_staged<O, Acc, MF, true, false>(p, mbase, nbase, lane, acc, stg);
+        else store_tile_staged<O, Acc, MF, false, false>(p, mbase, nbase, lane, acc, stg);
     }
 }
 
-template <class TI, class TO, bool AK, bool BK>
+// Per-shape schedule: BAR_AT MFMAs of a slab's last k-slice run before its barrier; the slab's 16
+// direct loads go out one per DS MFMA slots (N3 of them after the barrier, in the last k-slice
+// of the previous slab, the rest from the start of the slab).
+template <int MF>
+struct Sched {
+    static constexpr int BAR_AT = MF == 32 ? 4 : 8;
+    static constexpr int DS = MF == 32 ? 2 : 4;
+    static constexpr int REM = Shape<MF>::NMS - BAR_AT;   // MFMA slots after the barrier
+    static constexpr int N3 = (REM + DS - 1) / DS;       // loads of slab s+2 in them
+    static_assert(N3 <= 16, "loads after the barrier");
+};
+
+template <class TI, class TO, bool AK, bool BK, int MF>
 __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
-    using accv_t = typename TI::accv_t;
     using acc_t = typename TI::acc_t;
+    using accv_t = typename std::conditional<MF == 32, typename TI::accv_t, typename TI::accv16_t>::type;
+    using SH = Shape<MF>;
+    using SC = Sched<MF>;
+    constexpr int NF = SH::NF, NS = SH::NS, NMS = SH::NMS;
     constexpr int E = TI::E;
     constexpr int BKE = SLAB_BYTES / E;       // K elements per slab
-    using FA = Frag<E, AK>;
-    using FB = Frag<E, BK>;
+    using FA = Frag<E, AK, MF>;
+    using FB = Frag<E, BK, MF>;
     // LDS instructions per k-slice, issued in the order the next k-slice's MFMAs consume them:
-    // A0, B0, B1, B2, B3, A1, A2, A3 (each fragment 1 or 2 instructions)
-    constexpr int NRD = 4 * FA::NI + 4 * FB::NI;
+    // A0, B0 .. B(NF-1), A1 .. A(NF-1) (each fragment 1 or 2 instructions)
+    constexpr int NRD = NF * FA::NI + NF * FB::NI;
     // two pipeline stages of both operands; after the main loop the stage-1 halves of A and B
     // (never used by the K tail) hold the four waves' epilogue staging buffers
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * OPND];
@@ -435,34 +478,38 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     };
 
     const int nfull = p.K / BKE;
-    accv_t acc[4][4];
-    u32x4 af[2][4], bf[2][4];
+    accv_t acc[NF][NF];
+    u32x4 af[2][NF], bf[2][NF];
 
-    // read instruction q (0 .. NRD-1) of k-slice j of `stage` into fragment buffer `buf`
+    // read instruction q (0 .. NRD-1) of k-slice j of `stage` into fragment buffer `buf`, in
+    // the fragment order A0, B0 .. B(NF-1), A1 .. A(NF-1)
     auto rd = [&](int stage, int j, int buf, int q) {
-        // fragment order A0, B0, B1, B2, B3, A1, A2, A3
-        int idx = 0;
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            const bool isA = f == 0 || f >= 5;
-            const int t = f == 0 ? 0 : (f <= 4 ? f - 1 : f - 4);
-            const int ni = isA ? FA::NI : FB::NI;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if (h < ni) {
-                    if (idx == q) {
-                        if (isA) fa.read(stage, t, j, h, af[buf][t]);
-                        else fb.read(stage, t, j, h, bf[buf][t]);
-                    }
-                    ++idx;
-                }
-            }
+        if (q < FA::NI) {
+            fa.read(stage, 0, j, q, af[buf][0]);
+        } else if (q < FA::NI + NF * FB::NI) {
+            const int r = q - FA::NI;
+            fb.read(stage, r / FB::NI, j, r % FB::NI, bf[buf][r / FB::NI]);
+        } else {
+            const int r = q - FA::NI - NF * FB::NI;
+            fa.read(stage, 1 + r / FA::NI, j, r % FA::NI, af[buf][1 + r / FA::NI]);
         }
     };
-    // MFMA number t (0..15) of a k-slice: A fragment t/4 times B fragment t%4
+    // reads issued with MFMA slot t of a k-slice (slots 0 .. NMS-1 spread NRD reads)
+    auto rd_slot = [&](int stage, int j, int buf, int t, int slots) {
+        if constexpr (MF == 32) {
+            if (slots == NMS) {
+                if (t < NRD) rd(stage, j, buf, t);
+                return;
+            }
+        }
+#pragma unroll
+        for (int q = (t * NRD) / slots; q < ((t + 1) * NRD) / slots; ++q) rd(stage, j, buf, q);
+    };
+    // MFMA number t (0 .. NMS-1) of a k-slice: A fragment t/NF times B fragment t%NF
     auto mma = [&](int buf, int t) {
-        const int i = t >> 2, j = t & 3;
-        acc[i][j] = TI::mma(bf[buf][j], af[buf][i], acc[i][j]);
+        const int i = t / NF, j = t % NF;
+        if constexpr (MF == 32) acc[i][j] = TI::mma(bf[buf][j], af[buf][i], acc[i][j]);
+        else acc[i][j] = TI::mma16(bf[buf][j], af[buf][i], acc[i][j]);
     };
     // LDS addresses of operand slabs in a stage
     auto dstA = [&](int st) { return lds0 + (uint32_t)(st * KC_BYTES); };
@@ -480,13 +527,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         if (nfull > 1) issue_slab(1, 1);
     };
 
-    // Slab s reads stage X; slab s+1 lives in Y.  The 16 loads of a slab are spread one per
-    // three MFMA slots over 47 slots: loads 0-4 of slab s+2 go out in k-slice 3 of slab s (after
-    // the barrier has freed X), loads 5-15 of slab s+1 in k-slices 0 and 1 of slab s; k-slice 2
-    // issues none, leaving time for the last ones to land before the barrier.  Bursting all 16
-    // at once fills the vector-memory queue and stalls the wave's in-order issue (MFMAs too).
-    //   dma_next:  issue loads 5-15 of slab s+1 into Y (its loads 0-4 went out in slab s-1)
-    //   dma_next2: issue loads 0-4 of slab s+2 into X
+    // Slab s reads stage X; slab s+1 lives in Y.  The 16 loads of a slab are spread one per DS
+    // MFMA slots: the first N3 go out in the last k-slice of slab s-2 (after its barrier freed
+    // the stage), the rest from the start of slab s-1.  Bursting all 16 at once fills the
+    // vector-memory queue and stalls the wave's in-order issue (MFMAs too).
+    //   dma_next:  issue loads N3..15 of slab s+1 into Y (its first loads went out in slab s-1)
+    //   dma_next2: issue loads 0..N3-1 of slab s+2 into X
     //   has_next:  slab s+1 exists (wait for it, read its k-slice 0)
     auto slab_step = [&](int s, int X, int Y, bool dma_next, bool dma_next2, bool has_next) {
         const uint8_t *na = Loader<E, AK>::slab_base(A, p.lda, (s + 1) * BKE);
@@ -497,41 +543,41 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
             if (d < 8) la.issue(sa, dstA(st), wave, d);
             else lb.issue(sb, dstB(st), wave, d - 8);
         };
-        // k-slices 0..2: MFMAs of slice j interleaved with the reads of slice j+1
+        // k-slices 0 .. NS-2: MFMAs of slice j interleaved with the reads of slice j+1
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+        for (int j = 0; j < NS - 1; ++j) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < NMS; ++t) {
                 mma(j & 1, t);
-                if (t < NRD) rd(X, j + 1, (j + 1) & 1, t);
+                rd_slot(X, j + 1, (j + 1) & 1, t, NMS);
                 if (dma_next) {
-                    const int q = 15 + 16 * j + t;               // load slot 15..62
-                    if (q % DMA_STRIDE == 0 && q / DMA_STRIDE < 16) dma(na, nb, Y, q / DMA_STRIDE);
+                    const int q = NMS * j + t;                   // load slot in the slab
+                    if (q % SC::DS == 0 && SC::N3 + q / SC::DS < 16) dma(na, nb, Y, SC::N3 + q / SC::DS);
                 }
                 fence();
             }
         }
-        // k-slice 3: every read of X has been issued.  Finish them and our loads of slab s+1,
-        // meet at the barrier (after one MFMA, so the matrix core is busy meanwhile), then
-        // start refilling X with slab s+2 and read slice 0 of Y while the remaining MFMAs run.
+        // last k-slice: every read of X has been issued.  The first BAR_AT MFMAs run while those
+        // reads land; then the wave finishes them and its loads of slab s+1 and meets the others
+        // at the barrier; then it starts refilling X with slab s+2 and reads slice 0 of Y while
+        // the remaining MFMAs run.
+        constexpr int LB = (NS - 1) & 1;                         // fragment buffer of the slice
+#pragma unroll
+        for (int t = 0; t < SC::BAR_AT; ++t) {
+            mma(LB, t);
+            fence();
+        }
         wait_lgkmcnt0();
         if (has_next) wait_vmcnt0();
-        fence();
-        mma(1, 0);
         fence();
         __syncthreads();
         fence();
 #pragma unroll
-        for (int t = 1; t < 16; ++t) {
-            mma(1, t);
-            if (dma_next2) {
-                const int q = t - 1;                             // load slot 0..14
-                if (q % DMA_STRIDE == 0) dma(n2a, n2b, X, q / DMA_STRIDE);
-            }
-            if (has_next) {
-                if (t - 1 < NRD) rd(Y, 0, 0, t - 1);
-                if (t == 15 && NRD == 16) rd(Y, 0, 0, 15);
-            }
+        for (int t = SC::BAR_AT; t < NMS; ++t) {
+            mma(LB, t);
+            const int u = t - SC::BAR_AT;                        // slot after the barrier
+            if (dma_next2 && u % SC::DS == 0) dma(n2a, n2b, X, u / SC::DS);
+            if (has_next) rd_slot(Y, 0, 0, u, SC::REM);
             fence();
         }
     };
@@ -540,11 +586,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     fa.init(lane, wm * 128, lds0);
     fb.init(lane, wn * 128, lds0 + OPND);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NF; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+            for (int r = 0; r < (MF == 32 ? 16 : 4); ++r) acc[i][j][r] = 0;
 
     if (nfull > 0) {
         prologue();
@@ -585,21 +631,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         stage_tail<E, BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid);
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {   // the 4 k-slices of the slab
+        for (int j = 0; j < NS; ++j) {   // the k-slices of the slab
 #pragma unroll
             for (int q = 0; q < NRD; ++q) rd(0, j, 0, q);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) mma(0, t);
+            for (int t = 0; t < NMS; ++t) mma(0, t);
         }
     }
 
     // every wave's reads of the stage-1 buffers ended before the last slab's barrier
-    epilogue<TO, acc_t>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
+    epilogue<TO, acc_t, MF>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
 }
+
+// MFMA shape of the fast path.  Both shapes give the same results (fp32/int32 accumulation of
+// the same products); the 16x16 one (K = 32 fp16/bf16 or 64 int8 per instruction) moves half
+// as much accumulator data per multiply-add, which on this power-limited part keeps the clock
+// higher: ~10% more throughput at 8192^3 than the 32x32 shape.
+constexpr int FAST_MF = 16;
 
 template <class TI, class TO, bool AT, bool BT>
 hipError_t launch_fast(const GemmParams &p, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT>), dim3(grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, FAST_MF>), dim3(grid), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
