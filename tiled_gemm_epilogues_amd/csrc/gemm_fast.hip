@@ -184,7 +184,9 @@ __device__ __forceinline__ void stage_tail(const uint8_t *base, int ld, int row0
 // 16 bytes of consecutive k (k = j*KS + (l/32)*KS/2 + ..., KS = 32 bytes) of tile row (or
 // column) 32t + l%32.  MF = 16 (MFMA 16x16, k-slice of 64 bytes): lane l gets 16 bytes of
 // consecutive k (k = j*KS + (l/16)*KS/4 + ..., KS = 64 bytes) of row 16t + l%16.  A K-contiguous
-// operand needs one ds_read_b128 per fragment, an M/N-contiguous one two transposing reads.
+// operand needs one ds_read_b128 per fragment, an M/N-contiguous one two transposing reads,
+// issued together and assembled as one vector (assembling the halves in separate steps makes
+// the register allocator shuffle accumulators).
 
 template <int MF>
 struct Shape {
@@ -198,7 +200,6 @@ template <int E, bool KC, int MF>
 struct Frag {
     using S = Shape<MF>;
     static constexpr int NF = S::NF;
-    static constexpr int NI = KC ? 1 : 2;   // LDS instructions per fragment
     // byte address (LDS) of this lane's fragment in stage 0: per sub-tile and k-slice for a
     // K-contiguous operand (the XOR swizzle is not additive), per sub-tile otherwise
     uint32_t addr[NF][KC ? S::NS : 1];
@@ -233,22 +234,24 @@ struct Frag {
             }
         }
     }
-    // instruction h (< NI) of fragment (t, j) of `stage` into dst
-    __device__ __forceinline__ void read(int stage, int t, int j, int h, u32x4 &dst) const {
+    // fragment (t, j) of `stage` into dst
+    __device__ __forceinline__ void read(int stage, int t, int j, u32x4 &dst) const {
         if constexpr (KC) {
             dst = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)(addr[t][j] + stage * KC_BYTES);
         } else if constexpr (E == 2) {
-            // k rows j*KS/2 + 4h + (0..3) past the lane's base: the swizzle depends only on k & 3
-            const uint32_t a = addr[t][0] + stage * KC_BYTES + ((S::KSB / 2) * j + 4 * h) * 512;
-            s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
-            dst[2 * h] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 0, 1));
-            dst[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v, v, 2, 3));
+            // k rows j*KS/2 + (0..3) and + (4..7) past the lane's base: the swizzle depends only
+            // on k & 3
+            const uint32_t a = addr[t][0] + stage * KC_BYTES + ((S::KSB / 2) * j) * 512;
+            s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
+            s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(a + 4 * 512));
+            dst = __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-            // k rows j*KS + 8h + (0..7) past the lane's base: the swizzle depends only on k & 7
-            const uint32_t a = addr[t][0] + stage * KC_BYTES + (S::KSB * j + 8 * h) * 256;
-            i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)a);
-            dst[2 * h] = (uint32_t)v[0];
-            dst[2 * h + 1] = (uint32_t)v[1];
+            // k rows j*KS + (0..7) and + (8..15) past the lane's base: the swizzle depends only
+            // on k & 7
+            const uint32_t a = addr[t][0] + stage * KC_BYTES + (S::KSB * j) * 256;
+            i32x2 v0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)a);
+            i32x2 v1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)(a + 8 * 256));
+            dst = __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3));
         }
     }
 };
@@ -443,9 +446,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     constexpr int BKE = SLAB_BYTES / E;       // K elements per slab
     using FA = Frag<E, AK, MF>;
     using FB = Frag<E, BK, MF>;
-    // LDS instructions per k-slice, issued in the order the next k-slice's MFMAs consume them:
-    // A0, B0 .. B(NF-1), A1 .. A(NF-1) (each fragment 1 or 2 instructions)
-    constexpr int NRD = NF * FA::NI + NF * FB::NI;
+    // fragment reads per k-slice, issued in the order the next k-slice's MFMAs consume them:
+    // A0, B0 .. B(NF-1), A1 .. A(NF-1)
+    constexpr int NRD = 2 * NF;
     // two pipeline stages of both operands; after the main loop the stage-1 halves of A and B
     // (never used by the K tail) hold the four waves' epilogue staging buffers
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * OPND];
@@ -481,18 +484,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     accv_t acc[NF][NF];
     u32x4 af[2][NF], bf[2][NF];
 
-    // read instruction q (0 .. NRD-1) of k-slice j of `stage` into fragment buffer `buf`, in
-    // the fragment order A0, B0 .. B(NF-1), A1 .. A(NF-1)
+    // fragment read q (0 .. NRD-1) of k-slice j of `stage` into fragment buffer `buf`, in the
+    // order A0, B0 .. B(NF-1), A1 .. A(NF-1)
     auto rd = [&](int stage, int j, int buf, int q) {
-        if (q < FA::NI) {
-            fa.read(stage, 0, j, q, af[buf][0]);
-        } else if (q < FA::NI + NF * FB::NI) {
-            const int r = q - FA::NI;
-            fb.read(stage, r / FB::NI, j, r % FB::NI, bf[buf][r / FB::NI]);
-        } else {
-            const int r = q - FA::NI - NF * FB::NI;
-            fa.read(stage, 1 + r / FA::NI, j, r % FA::NI, af[buf][1 + r / FA::NI]);
-        }
+        if (q == 0) fa.read(stage, 0, j, af[buf][0]);
+        else if (q <= NF) fb.read(stage, q - 1, j, bf[buf][q - 1]);
+        else fa.read(stage, q - NF, j, af[buf][q - NF]);
     };
     // reads issued with MFMA slot t of a k-slice (slots 0 .. NMS-1 spread NRD reads)
     auto rd_slot = [&](int stage, int j, int buf, int t, int slots) {
