@@ -643,12 +643,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
 // MFMA shape of the fast path.  Both shapes give the same results (fp32/int32 accumulation of
 // the same products); the 16x16 one (K = 32 fp16/bf16 or 64 int8 per instruction) moves half
 // as much accumulator data per multiply-add, which on this power-limited part keeps the clock
-// higher: ~10% more throughput at 8192^3 than the 32x32 shape.
-constexpr int FAST_MF = 16;
+// higher: ~10% more throughput at 8192^3 than the 32x32 shape.  With both operands M/N-
+// contiguous (A transposed, B not) the 16x16 schedule needs more registers than the allocator
+// finds without shuffling accumulators, so that layout keeps the 32x32 shape.
+template <bool AT, bool BT>
+constexpr int fast_mf() { return (AT && !BT) ? 32 : 16; }
 
 template <class TI, class TO, bool AT, bool BT>
 hipError_t launch_fast(const GemmParams &p, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, FAST_MF>), dim3(grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, fast_mf<AT, BT>()>), dim3(grid), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
