@@ -138,10 +138,13 @@ def main():
     B = dev(p.ab, x["B"])
     C = dev(p.cd, x["C"]) if x["C"] is not None else None
     bias = dev(p.bias_dt, x["bias"]) if x["bias"] is not None else None
-    D = torch.empty(p.M * p.ldc, dtype={"f16": torch.float16, "bf16": torch.bfloat16,
-                                        "f32": torch.float32, "i32": torch.int32}[p.cd],
+    D = torch.empty(max(p.batch - 1, 0) * p.stride_c + p.M * p.ldc,
+                    dtype={"f16": torch.float16, "bf16": torch.bfloat16,
+                           "f32": torch.float32, "i32": torch.int32}[p.cd],
                     device="cuda:0")
-    plan = Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    plan = Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
+                batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
+                stride_bias=p.stride_bias)
     log(f"[bench] kernel: {plan.describe()}")
 
     stream = torch.cuda.current_stream()
@@ -186,8 +189,10 @@ def main():
         # the CPU-baseline leg: the oracle timed on a row sample, which also checks those rows
         # of the timed output (not timed)
         import oracle
-        Dh = D.view(torch.int16).cpu().numpy().view(np.uint16) if p.cd in ("f16", "bf16") \
-            else D.cpu().numpy()
+        # product 0 of a batch (the sample is taken from it)
+        D0 = D[: p.M * p.ldc]
+        Dh = D0.view(torch.int16).cpu().numpy().view(np.uint16) if p.cd in ("f16", "bf16") \
+            else D0.cpu().numpy()
         Dh = Dh.reshape(p.M, p.ldc)
         threads = host_threads()
         # two pilots separate the fixed cost (decoding B) from the per-row cost; the sample is
@@ -209,7 +214,8 @@ def main():
         sample_flops = 2.0 * rows * p.N * p.K
         cpu = {"value": round(sample_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
-               "sample": f"output rows 0..{rows - 1} of {p.M} (all {p.N} columns, full K={p.K}): "
+               "sample": f"output rows 0..{rows - 1} of {p.M}{' of product 0' if p.batch != 1 else ''} "
+                         f"(all {p.N} columns, full K={p.K}): "
                          f"{sample_flops:.3e} flop in {t_cpu:.1f}s, fp64/int64 accumulation"}
         log(f"[bench] cpu oracle: {cpu['sample']}")
         got = oracle.decode(p.cd, Dh[:rows, : p.N]) if p.cd != "i32" else Dh[:rows, : p.N].astype(np.int64)
@@ -235,7 +241,8 @@ def main():
         "vs_baseline": None,
         "dtype": p.ab,
         "data": "synthetic",
-        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "layout": p.op_a + p.op_b,
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+                   "layout": p.op_a + p.op_b,
                    "ab": p.ab, "cd": p.cd, "epilogue": p.epi, "alpha": p.alpha, "beta": p.beta,
                    "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4)},
         "roofline": roof,

@@ -95,6 +95,28 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
                                gemm_dtype_t ab_type, gemm_dtype_t cd_type, gemm_epilogue_t epi);
 
 /*
+ * Strided-batched plan: `batch` independent products of the same shape in one launch,
+ *   D_b = act(alpha*op(A_b)*op(B_b) + beta*C_b + bias_b),  b = 0 .. batch-1,
+ * where X_b starts stride_x elements (of X's own type) after X_{b-1}: A_b = A + b*stride_a,
+ * B_b = B + b*stride_b, C_b = C + b*stride_c and D_b = D + b*stride_c (C and D share the
+ * stride, as they share ldc), bias_b = bias + b*stride_bias.  This is the simplest of the
+ * logical-index-to-offset mappings that "Flexible Performant GEMM Kernels on GPUs" (section 4)
+ * builds with its layout component for batched and tensor-contraction operands.
+ *   batch          number of products, >= 0 (0 is a valid empty launch).
+ *   stride_a, stride_b, stride_bias   >= 0; 0 shares the operand between all products.
+ *   stride_c       0 when batch <= 1, else at least the span of one D ((M-1)*ldc + N), so
+ *                  that products never write the same element.
+ * The other arguments and the errors are those of gemm_plan_create, plus INVALID_VALUE for a
+ * negative batch or stride or an overlapping stride_c, and NOT_SUPPORTED when the launch would
+ * need 2^31 workgroups or more.  gemm_run then takes the pointers of product 0.
+ */
+gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, int64_t K,
+                                       gemm_op_t op_a, gemm_op_t op_b, int64_t lda, int64_t ldb,
+                                       int64_t ldc, gemm_dtype_t ab_type, gemm_dtype_t cd_type,
+                                       gemm_epilogue_t epi, int64_t batch, int64_t stride_a,
+                                       int64_t stride_b, int64_t stride_c, int64_t stride_bias);
+
+/*
  * Enqueues D = act(alpha*op(A)*op(B) + beta*C + bias) on `stream` (a hipStream_t; NULL is the
  * null stream of the current device).  All pointers are device pointers on the current device.
  *   A, B     operands (may be NULL only if the product is empty: M, N or K == 0).
@@ -103,10 +125,11 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
  *   D        output, required when M > 0 and N > 0.
  *   bias     N elements (fp32, or int32 for int8 inputs); required when the plan's epilogue
  *            includes a bias, ignored otherwise.
+ * For a batched plan every pointer is that of product 0 (see gemm_plan_create_batched).
  *   alpha, beta  scalars applied in fp32 (int8 plans require alpha == 1 and beta in {0, 1}).
  * Returns INVALID_VALUE for a NULL plan or a missing required pointer, NOT_SUPPORTED for int8
- * scalars outside the rule above, HIP_ERROR when the launch fails.  M == 0 or N == 0 returns
- * SUCCESS without launching.
+ * scalars outside the rule above, HIP_ERROR when the launch fails.  M == 0, N == 0 or a batch
+ * of 0 returns SUCCESS without launching.
  */
 gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream);

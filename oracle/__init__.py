@@ -173,6 +173,28 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
     return out.reshape(mr, N)
 
 
+def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
+                 bias_dt=None, alpha=1.0, beta=0.0, relu=False, batch=1, stride_a=0, stride_b=0,
+                 stride_c=0, stride_bias=0, threads=None):
+    """Exact results (batch x M x N) of a strided batch: product b uses the stored operands
+    starting b * stride elements after those of product 0 (C and D share stride_c; a zero
+    stride shares the operand).  The logical-index-to-offset mapping of a batched operand is
+    the layout idea of "Flexible Performant GEMM Kernels on GPUs", section 4; each product is
+    the plain definition above."""
+    integer = is_int(ab)
+    out = np.empty((batch, M, N), np.int64 if integer else np.float64)
+    Ar, Br = _raw(ab, A), _raw(ab, B)
+    Cr = _raw(cd, C) if (C is not None and beta != 0) else None
+    bias_dt = bias_dt or ("i32" if integer else "f32")
+    br = _raw(bias_dt, bias) if bias is not None else None
+    for b in range(batch):
+        out[b] = gemm(M, N, K, op_a, op_b, Ar[b * stride_a:], lda, Br[b * stride_b:], ldb, ab,
+                      C=Cr[b * stride_c:] if Cr is not None else None, ldc=ldc, cd=cd,
+                      bias=br[b * stride_bias:] if br is not None else None, bias_dt=bias_dt,
+                      alpha=alpha, beta=beta, relu=relu, threads=threads)
+    return out
+
+
 def points(ii, jj, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=0, cd="f32", bias=None,
            bias_dt=None, alpha=1.0, beta=0.0, relu=False):
     """Exact result at the output points (ii[p], jj[p]), straight from the raw stored operands

@@ -10,7 +10,7 @@ the storage type with round-to-nearest-even; the raw arrays (uint16 bit patterns
 bf16) are exactly what both the GPU and the oracle receive.  Leading dimensions are tight
 unless a padded ld is asked for.
 """
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 import math
 
 import numpy as np
@@ -75,6 +75,13 @@ class Problem:
     bias_dist: tuple = ("uniform", -0.5, 0.5)
     key: tuple = (0, 0)
     name: str = ""
+    # strided batch: `batch` products, operand x of product b starting stride_x elements after
+    # that of product b-1; -1 -> one stored matrix further (tight), 0 -> shared by all products
+    batch: int = 1
+    stride_a: int = -1
+    stride_b: int = -1
+    stride_c: int = -1
+    stride_bias: int = -1
 
     def __post_init__(self):
         if not self.lda:
@@ -83,6 +90,17 @@ class Problem:
             self.ldb = max(1, self.N if self.op_b == "N" else self.K)
         if not self.ldc:
             self.ldc = max(1, self.N)
+        if self.batch <= 1:
+            self.stride_a = self.stride_b = self.stride_c = self.stride_bias = 0
+        else:
+            if self.stride_a < 0:
+                self.stride_a = self.a_shape()[0] * self.lda
+            if self.stride_b < 0:
+                self.stride_b = self.b_shape()[0] * self.ldb
+            if self.stride_c < 0:
+                self.stride_c = self.M * self.ldc
+            if self.stride_bias < 0:
+                self.stride_bias = self.N if self.has_bias else 0
 
     @property
     def bias_dt(self):
@@ -98,7 +116,7 @@ class Problem:
 
     @property
     def flops(self):
-        return 2.0 * self.M * self.N * self.K
+        return 2.0 * self.M * self.N * self.K * max(self.batch, 0)
 
     def a_shape(self):   # stored 2-D shape (rows, ld)
         return (self.M, self.lda) if self.op_a == "N" else (self.K, self.lda)
@@ -107,17 +125,22 @@ class Problem:
         return (self.K, self.ldb) if self.op_b == "N" else (self.N, self.ldb)
 
     def algorithmic_bytes(self):
-        """Compulsory HBM traffic: op(A), op(B) read once, C if beta != 0, bias, D written once."""
+        """Compulsory HBM traffic: op(A), op(B) read once, C if beta != 0, bias, D written once
+        (per product; an operand shared by a batch is counted once)."""
         eb, ec = ELEM_BYTES[self.ab], ELEM_BYTES[self.cd]
-        b = (self.M * self.K + self.K * self.N) * eb + self.M * self.N * ec
+        nb = max(self.batch, 0)
+        per = lambda stride: nb if (nb <= 1 or stride != 0) else 1
+        b = (self.M * self.K * per(self.stride_a) + self.K * self.N * per(self.stride_b)) * eb
+        b += self.M * self.N * ec * nb
         if self.beta != 0:
-            b += self.M * self.N * ec
+            b += self.M * self.N * ec * nb
         if self.has_bias:
-            b += self.N * 4
+            b += self.N * 4 * per(self.stride_bias)
         return b
 
     def label(self):
-        return (f"{self.name or 'gemm'}:{self.M}x{self.N}x{self.K}:{self.op_a}{self.op_b}:"
+        bt = f":batch{self.batch}" if self.batch != 1 else ""
+        return (f"{self.name or 'gemm'}:{self.M}x{self.N}x{self.K}{bt}:{self.op_a}{self.op_b}:"
                 f"{self.ab}->{self.cd}:{self.epi}:a{self.alpha:g}b{self.beta:g}")
 
 
@@ -135,7 +158,11 @@ def _store(logical, op, ld, fill):
 
 
 def make_inputs(p: Problem, pad_fill=0):
-    """Raw stored arrays {A, B, C, bias} (C and bias None when unused) for problem p."""
+    """Raw stored arrays {A, B, C, bias} (C and bias None when unused) for problem p.  For a
+    batch, flat arrays holding product b at b * stride (product b drawn with key (*key, 1000+b);
+    a shared operand is product 0's; gaps hold pad_fill)."""
+    if p.batch != 1:
+        return _make_batched_inputs(p, pad_fill)
     ga, gb, gc, gbias = (rng(*p.key, i) for i in range(4))
     a = quantize(p.ab, draw(ga, p.a_dist, p.M * p.K)).reshape(p.M, p.K)
     b = quantize(p.ab, draw(gb, p.b_dist, p.K * p.N)).reshape(p.K, p.N)
@@ -147,6 +174,25 @@ def make_inputs(p: Problem, pad_fill=0):
         C = _store(c, "N", p.ldc, pad_fill)
     bias = quantize(p.bias_dt, draw(gbias, p.bias_dist, p.N)) if p.has_bias else None
     return {"A": A, "B": B, "C": C, "bias": bias}
+
+
+def _make_batched_inputs(p: Problem, pad_fill=0):
+    out = {"A": None, "B": None, "C": None, "bias": None}
+    strides = {"A": p.stride_a, "B": p.stride_b, "C": p.stride_c, "bias": p.stride_bias}
+    dtypes = {"A": p.ab, "B": p.ab, "C": p.cd, "bias": p.bias_dt}
+    for b in range(max(p.batch, 0)):
+        one = make_inputs(replace(p, batch=1, key=(*p.key, 1000 + b)), pad_fill)
+        for name, arr in one.items():
+            if arr is None:
+                continue
+            flat = arr.reshape(-1)
+            st = strides[name]
+            if out[name] is None:
+                n = flat.size + (st * (p.batch - 1) if st > 0 else 0)
+                out[name] = np.full(n, pad_fill, dtype=RAW_NP[dtypes[name]])
+            if st > 0 or b == 0:
+                out[name][b * st: b * st + flat.size] = flat
+    return out
 
 
 # ---- the workloads ---------------------------------------------------------------------------
@@ -199,25 +245,36 @@ def fc_layers(layouts=("NN",)):
     return out
 
 
+def batched_fp16():
+    """A strided batch of 16 independent fp16 2048^3 products (NN, bias per product, ReLU ->
+    fp16), A,B ~ N(0,1)/sqrt(K), bias ~ U[-0.5,0.5]: the batched operand layout of "Flexible
+    Performant GEMM Kernels on GPUs", section 4, at a size where one launch fills the chip
+    (16 x 64 tiles of 256x256)."""
+    K = 2048
+    s = 1.0 / math.sqrt(K)
+    return [Problem(2048, 2048, K, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                    a_dist=("normal", s), b_dist=("normal", s), key=(6, 0), name="batched_fp16",
+                    batch=16)]
+
+
 WORKLOADS = {
     "sgemm_256": sgemm_256,
     "fp16_8192_bias_relu": fp16_8192_bias_relu,
     "bf16_layout_sweep": bf16_layout_sweep,
     "int8_4096_bias": int8_4096_bias,
     "fc_layers": fc_layers,
+    "batched_fp16": batched_fp16,
 }
 
 
-def exact_integer_problem(M, N, K, op_a, op_b, ab, cd, epi, alpha, beta, key, ld_pad=0):
+def exact_integer_problem(M, N, K, op_a, op_b, ab, cd, epi, alpha, beta, key, ld_pad=0, **batch):
     """Inputs whose every partial sum is an integer of magnitude <= 16*K + small, so fp32
     accumulation (any order) and the fp32 epilogue are exact whenever 16*K < 2^24 and alpha,
     beta are small powers of two: A,B integers in [-4,4], C integers in [-8,8], bias integers in
     [-8,8]."""
     p = Problem(M, N, K, op_a, op_b, ab, cd, epi, alpha, beta,
                 a_dist=("int", -4, 4), b_dist=("int", -4, 4), c_dist=("int", -8, 8),
-                bias_dist=("int", -8, 8), key=key, name="exact_int")
+                bias_dist=("int", -8, 8), key=key, name="exact_int", **batch)
     if ld_pad:
-        p.lda += ld_pad
-        p.ldb += ld_pad
-        p.ldc += ld_pad
+        p = replace(p, lda=p.lda + ld_pad, ldb=p.ldb + ld_pad, ldc=p.ldc + ld_pad)
     return p

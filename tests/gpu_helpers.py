@@ -109,3 +109,28 @@ def check_points(p, x, Draw, n=2000, seed=0):
     err = float(np.max(np.abs(got - ref)) / den)
     assert err <= TOL, f"normalised error {err:.3e} > {TOL}"
     return err
+
+
+def run_batched(p, x, offset=0):
+    """Run the strided-batched problem p (flat inputs x) through a batched plan; returns the raw
+    flat D storage (initialised with a sentinel, gaps between products included)."""
+    A = to_dev(p.ab, x["A"], offset)
+    B = to_dev(p.ab, x["B"], offset)
+    nD = max(p.batch - 1, 0) * p.stride_c + p.M * p.ldc
+    D = to_dev(p.cd, np.full(nD, sentinel(p.cd), dtype=synth.RAW_NP[p.cd]), offset)
+    C = to_dev(p.cd, x["C"], offset) if x["C"] is not None else None
+    bias = to_dev(p.bias_dt, x["bias"], offset) if x["bias"] is not None else None
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
+                  batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
+                  stride_bias=p.stride_bias)
+    pl.run(A, B, C, D, bias, p.alpha, p.beta)
+    torch.cuda.synchronize()
+    return to_host(p.cd, D).reshape(-1), pl
+
+
+def reference_batched(p, x):
+    return oracle.gemm_batched(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab,
+                               C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
+                               beta=p.beta, relu=p.relu, batch=p.batch, stride_a=p.stride_a,
+                               stride_b=p.stride_b, stride_c=p.stride_c,
+                               stride_bias=p.stride_bias)

@@ -277,3 +277,56 @@ def test_exact_integer_inputs_are_integers():
     ref = oracle.gemm(p.M, p.N, p.K, "N", "T", x["A"], p.lda, x["B"], p.ldb, "bf16", C=x["C"],
                       ldc=p.ldc, cd="bf16", bias=x["bias"], alpha=2.0, beta=-1.0, relu=True)
     assert np.array_equal(ref, np.round(ref))
+
+
+# ---- strided batch ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+def test_batched_against_numpy_strided_views(lay):
+    """Each product of a strided batch is the plain product of the operands at b * stride:
+    checked against numpy's batched matmul on as_strided views of the same flat buffers
+    (int8 values, exact in int64), with padded strides, a shared (stride 0) operand and
+    per-product bias."""
+    g = np.random.default_rng(31)
+    for (M, N, K, batch) in [(3, 5, 4, 3), (1, 7, 2, 4), (6, 1, 5, 2), (4, 4, 4, 1)]:
+        lda = (K if lay[0] == "N" else M) + 2
+        ldb = (N if lay[1] == "N" else K) + 1
+        ldc = N + 3
+        sa = ((M if lay[0] == "N" else K) * lda) + 5
+        sb_shared = 0                                  # B shared by every product
+        sc = M * ldc + 2
+        sbias = N + 1
+        A = g.integers(-3, 4, sa * batch + 8).astype(np.int8)
+        B = g.integers(-3, 4, (K if lay[1] == "N" else N) * ldb + 8).astype(np.int8)
+        C = g.integers(-5, 6, sc * batch + 8).astype(np.int32)
+        bias = g.integers(-9, 10, sbias * batch + 4).astype(np.int32)
+        got = oracle.gemm_batched(M, N, K, lay[0], lay[1], A, lda, B, ldb, "i8", C=C, ldc=ldc,
+                                  cd="i32", bias=bias, alpha=1, beta=1, relu=True, batch=batch,
+                                  stride_a=sa, stride_b=sb_shared, stride_c=sc,
+                                  stride_bias=sbias)
+        st = np.lib.stride_tricks.as_strided
+        A64, B64, C64, b64 = (x.astype(np.int64) for x in (A, B, C, bias))
+        e = 8
+        if lay[0] == "N":
+            Av = st(A64, (batch, M, K), (sa * e, lda * e, e))
+        else:
+            Av = st(A64, (batch, K, M), (sa * e, lda * e, e)).transpose(0, 2, 1)
+        if lay[1] == "N":
+            Bv = st(B64, (batch, K, N), (0, ldb * e, e))
+        else:
+            Bv = st(B64, (batch, N, K), (0, ldb * e, e)).transpose(0, 2, 1)
+        Cv = st(C64, (batch, M, N), (sc * e, ldc * e, e))
+        bv = st(b64, (batch, 1, N), (sbias * e, 0, e))
+        ref = np.maximum(np.matmul(Av, Bv) + Cv + bv, 0)
+        assert np.array_equal(got, ref)
+
+
+def test_batched_of_one_and_zero_strides_repeat_the_product():
+    g = np.random.default_rng(32)
+    M, N, K = 5, 6, 7
+    A = g.integers(-4, 5, M * K).astype(np.int8)
+    B = g.integers(-4, 5, K * N).astype(np.int8)
+    one = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "i8")
+    rep = oracle.gemm_batched(M, N, K, "N", "N", A, K, B, N, "i8", batch=3, stride_c=M * N)
+    for b in range(3):
+        assert np.array_equal(rep[b], one)

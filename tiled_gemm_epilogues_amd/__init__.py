@@ -4,8 +4,9 @@
 
 Argument marshalling only: every step of the computation runs in the HIP kernels behind the C
 ABI (include/gemm.h).  The low-level functions carry the C names (gemm_plan_create, gemm_run,
-gemm_plan_destroy, gemm_status_string, gemm_plan_describe); `Plan` wraps them for torch
-tensors, whose device memory and streams are the only things taken from PyTorch.
+gemm_plan_create_batched, gemm_plan_destroy, gemm_status_string, gemm_plan_describe); `Plan`
+wraps them for torch tensors, whose device memory and streams are the only things taken from
+PyTorch.
 
 There is no fallback: importing this package fails if the HIP library has not been built
 (python -m tiled_gemm_epilogues_amd.build, or __graft_entry__.build()).
@@ -36,6 +37,9 @@ _i64, _vp, _ci, _f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_flo
 _lib.gemm_plan_create.argtypes = [ctypes.POINTER(_vp), _i64, _i64, _i64, _ci, _ci, _i64, _i64, _i64,
                                   _ci, _ci, _ci]
 _lib.gemm_plan_create.restype = _ci
+_lib.gemm_plan_create_batched.argtypes = [ctypes.POINTER(_vp), _i64, _i64, _i64, _ci, _ci, _i64, _i64,
+                                          _i64, _ci, _ci, _ci, _i64, _i64, _i64, _i64, _i64]
+_lib.gemm_plan_create_batched.restype = _ci
 _lib.gemm_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _vp]
 _lib.gemm_run.restype = _ci
 _lib.gemm_plan_destroy.argtypes = [_vp]
@@ -45,8 +49,8 @@ _lib.gemm_status_string.restype = ctypes.c_char_p
 _lib.gemm_plan_describe.argtypes = [_vp, ctypes.c_char_p, ctypes.c_size_t]
 _lib.gemm_plan_describe.restype = _ci
 
-EXPORTED = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_status_string",
-            "gemm_plan_describe")
+EXPORTED = ("gemm_plan_create", "gemm_plan_create_batched", "gemm_run", "gemm_plan_destroy",
+            "gemm_status_string", "gemm_plan_describe")
 
 
 class GemmError(RuntimeError):
@@ -65,6 +69,17 @@ def gemm_plan_create(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epilo
     st = _lib.gemm_plan_create(ctypes.byref(h), M, N, K, _enum(OP, op_a), _enum(OP, op_b), lda, ldb,
                                ldc, _enum(DTYPE, ab_type), _enum(DTYPE, cd_type),
                                _enum(EPILOGUE, epilogue))
+    return st, h.value
+
+
+def gemm_plan_create_batched(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epilogue, batch,
+                             stride_a, stride_b, stride_c, stride_bias):
+    """Returns (status, handle) of a strided-batched plan (strides in elements)."""
+    h = _vp()
+    st = _lib.gemm_plan_create_batched(ctypes.byref(h), M, N, K, _enum(OP, op_a), _enum(OP, op_b),
+                                       lda, ldb, ldc, _enum(DTYPE, ab_type), _enum(DTYPE, cd_type),
+                                       _enum(EPILOGUE, epilogue), batch, stride_a, stride_b,
+                                       stride_c, stride_bias)
     return st, h.value
 
 
@@ -108,16 +123,25 @@ def _ptr(t, want, what):
 
 
 class Plan:
-    """A plan for one problem description (see include/gemm.h for the storage rules)."""
+    """A plan for one problem description (see include/gemm.h for the storage rules).  With
+    batch != 1 it is a strided-batched plan (gemm_plan_create_batched; strides in elements)."""
 
     def __init__(self, M, N, K, op_a="N", op_b="N", lda=None, ldb=None, ldc=None, ab="f16",
-                 cd="f16", epilogue="none"):
+                 cd="f16", epilogue="none", batch=1, stride_a=0, stride_b=0, stride_c=0,
+                 stride_bias=0):
         self.M, self.N, self.K = M, N, K
         self.op_a, self.op_b, self.ab, self.cd, self.epilogue = op_a, op_b, ab, cd, epilogue
         self.lda = lda if lda is not None else max(1, K if op_a == "N" else M)
         self.ldb = ldb if ldb is not None else max(1, N if op_b == "N" else K)
         self.ldc = ldc if ldc is not None else max(1, N)
-        st, h = gemm_plan_create(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd, epilogue)
+        self.batch = batch
+        if batch == 1 and not (stride_a or stride_b or stride_c or stride_bias):
+            st, h = gemm_plan_create(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd,
+                                     epilogue)
+        else:
+            st, h = gemm_plan_create_batched(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab,
+                                             cd, epilogue, batch, stride_a, stride_b, stride_c,
+                                             stride_bias)
         if st != STATUS_SUCCESS:
             raise GemmError(st, "gemm_plan_create")
         self._h = h

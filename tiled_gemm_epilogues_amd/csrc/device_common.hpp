@@ -173,6 +173,22 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// Strided batch: workgroup id -> (product b, id inside the product, `per` ids per product); the
+// operand pointers of `p` are moved to product b.  Consecutive ids share a product, so the
+// XCD-contiguous id ranges of xcd_remap keep each product on few XCDs.
+template <int EAB, int ECD>
+__device__ __forceinline__ int select_batch(GemmParams &p, int id, int per) {
+    const int b = __builtin_amdgcn_readfirstlane(id / per);   // uniform: keeps pointers scalar
+    if (b > 0) {
+        p.A = static_cast<const uint8_t *>(p.A) + b * p.stride_a * EAB;
+        p.B = static_cast<const uint8_t *>(p.B) + b * p.stride_b * EAB;
+        if (p.C) p.C = static_cast<const uint8_t *>(p.C) + b * p.stride_c * ECD;
+        p.D = static_cast<uint8_t *>(p.D) + b * p.stride_c * ECD;
+        if (p.bias) p.bias = static_cast<const uint8_t *>(p.bias) + b * p.stride_bias * 4;
+    }
+    return __builtin_amdgcn_readfirstlane(id - b * per);
+}
+
 // Grouped raster: consecutive ids walk down group_m tile rows, then move one tile column.
 __device__ __forceinline__ void raster(int id, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
     int per_group = group_m * tiles_n;

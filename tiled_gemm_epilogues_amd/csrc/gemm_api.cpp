@@ -16,6 +16,7 @@ using tge::KernelEntry;
 
 struct gemm_plan {
     int64_t M, N, K, lda, ldb, ldc;
+    int64_t batch, stride_a, stride_b, stride_c, stride_bias;
     int op_a, op_b, ab, cd, epi;
     const KernelEntry *kernel;       // general kernel (always valid)
     const KernelEntry *fast;         // fast or skinny kernel when the plan qualifies, else nullptr
@@ -117,9 +118,20 @@ const char *gemm_status_string(gemm_status_t s) {
 gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K, gemm_op_t op_a,
                                gemm_op_t op_b, int64_t lda, int64_t ldb, int64_t ldc,
                                gemm_dtype_t ab_type, gemm_dtype_t cd_type, gemm_epilogue_t epi) {
+    return gemm_plan_create_batched(out, M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epi,
+                                    1, 0, 0, 0, 0);
+}
+
+gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, int64_t K,
+                                       gemm_op_t op_a, gemm_op_t op_b, int64_t lda, int64_t ldb,
+                                       int64_t ldc, gemm_dtype_t ab_type, gemm_dtype_t cd_type,
+                                       gemm_epilogue_t epi, int64_t batch, int64_t stride_a,
+                                       int64_t stride_b, int64_t stride_c, int64_t stride_bias) {
     if (!out) return GEMM_STATUS_INVALID_VALUE;
     *out = nullptr;
     if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
+    if (batch < 0 || stride_a < 0 || stride_b < 0 || stride_c < 0 || stride_bias < 0)
+        return GEMM_STATUS_INVALID_VALUE;
     if ((op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T))
         return GEMM_STATUS_INVALID_VALUE;
     if ((int)ab_type < GEMM_F32 || (int)ab_type > GEMM_I32 || (int)cd_type < GEMM_F32 ||
@@ -142,6 +154,14 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     int64_t sc = span_bytes(M, N, ldc, ecd);
     if (sa >= lim || sb >= lim || sc >= lim || lda >= lim || ldb >= lim || ldc >= lim)
         return GEMM_STATUS_NOT_SUPPORTED;
+    // products of a batch never write the same element of D
+    if (batch > 1 && M > 0 && N > 0 && stride_c < (M - 1) * ldc + N) return GEMM_STATUS_INVALID_VALUE;
+    if (batch <= 1) stride_a = stride_b = stride_c = stride_bias = 0;
+    // the byte offset of the last product must fit in 63 bits
+    const int64_t big = (int64_t)1 << 62;
+    if (batch > 1 && (stride_a > big / batch / 4 || stride_b > big / batch / 4 ||
+                      stride_c > big / batch / 4 || stride_bias > big / batch / 4))
+        return GEMM_STATUS_NOT_SUPPORTED;
 
     int cfg = choose_cfg(M, N, ab_type);
     // TGE_FORCE_TILE=256|128|64 pins the workgroup tile (tests and tuning sweeps)
@@ -162,8 +182,10 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     if (fk && strcmp(fk, "fast") == 0) want_fast = true;
     if (fk && strcmp(fk, "general") == 0) want_fast = false;
     const int ve = 16 / eab;   // elements per 16-byte chunk
+    // every product of a batch keeps the 16-byte alignment of product 0
+    const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0;
     if (ft && want_fast && K >= 128 / eab && (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 &&
-        (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0))
+        strides16 && (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0))
         fast = ft(op_a, op_b);
 
     // skinny path: M <= 64, memory bound; preferred over both tiled kernels when it applies
@@ -174,7 +196,7 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     if (fk && strcmp(fk, "fast") == 0) want_skinny = false;
     if (fk && strcmp(fk, "skinny") == 0) want_skinny = true;
     if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % 32 == 0 &&
-        (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && (op_b == GEMM_OP_T || N % 8 == 0)) {
+        (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && strides16 && (op_b == GEMM_OP_T || N % 8 == 0)) {
         fast = st(op_b, (int)((M + 15) / 16));
         skinny = fast != nullptr;
     }
@@ -182,6 +204,8 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     gemm_plan *p = new (std::nothrow) gemm_plan;
     if (!p) return GEMM_STATUS_ALLOC_FAILED;
     p->M = M; p->N = N; p->K = K;
+    p->batch = batch;
+    p->stride_a = stride_a; p->stride_b = stride_b; p->stride_c = stride_c; p->stride_bias = stride_bias;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
     p->op_a = op_a; p->op_b = op_b; p->ab = ab_type; p->cd = cd_type; p->epi = epi;
     p->kernel = k;
@@ -191,11 +215,18 @@ gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K
     p->tiles_m = skinny ? 1 : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
-    p->grid = (unsigned)((int64_t)p->tiles_m * p->tiles_n);
-    snprintf(p->desc, sizeof(p->desc), "%s %s->%s %c%c tile %dx%dx%d waves %dx%d grid %u",
+    const int64_t grid = (int64_t)p->tiles_m * p->tiles_n * batch;
+    if (grid >= ((int64_t)1 << 31)) {
+        delete p;
+        return GEMM_STATUS_NOT_SUPPORTED;
+    }
+    p->grid = (unsigned)grid;
+    char bdesc[48] = "";
+    if (batch != 1) snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
+    snprintf(p->desc, sizeof(p->desc), "%s %s->%s %c%c tile %dx%dx%d waves %dx%d grid %u%s",
              shown->name, dtype_name(ab_type), dtype_name(cd_type), op_a ? 'T' : 'N',
              op_b ? 'T' : 'N', shown->bm, shown->bn, shown->bk, shown->waves_m, shown->waves_n,
-             p->grid);
+             p->grid, bdesc);
     *out = p;
     return GEMM_STATUS_SUCCESS;
 }
@@ -214,7 +245,7 @@ gemm_status_t gemm_plan_describe(gemm_plan_t p, char *buf, size_t len) {
 gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream) {
     if (!p) return GEMM_STATUS_INVALID_VALUE;
-    if (p->M == 0 || p->N == 0) return GEMM_STATUS_SUCCESS;
+    if (p->M == 0 || p->N == 0 || p->batch == 0) return GEMM_STATUS_SUCCESS;
     const bool has_bias = p->epi == GEMM_EPI_BIAS || p->epi == GEMM_EPI_BIAS_RELU;
     const bool relu = p->epi == GEMM_EPI_RELU || p->epi == GEMM_EPI_BIAS_RELU;
     if (!D) return GEMM_STATUS_INVALID_VALUE;
@@ -234,13 +265,16 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     prm.has_bias = has_bias;
     prm.relu = relu;
     prm.group_m = p->group_m;
+    prm.batch = (int)p->batch;
+    prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
+    prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
     const KernelEntry *k = p->kernel;
     // the fast kernel needs 16-byte aligned operand pointers; else the general kernel runs
     if (p->fast && ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0) k = p->fast;
     const bool sk = k == p->fast && p->fast_is_skinny;
     prm.tiles_m = sk ? 1 : (int)((p->M + k->bm - 1) / k->bm);
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
-    const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n);
+    const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * p->batch);
     hipError_t e = k->launch(prm, grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;
 }

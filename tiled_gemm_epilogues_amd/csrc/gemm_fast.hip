@@ -459,7 +459,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);   // this workgroup's raster id
+    // this workgroup's product and raster id inside it
+    const int lid = select_batch<TI::E, (int)sizeof(typename TO::T)>(p, xcd_remap(blockIdx.x, gridDim.x),
+                                                                    p.tiles_m * p.tiles_n);
 
     const uint8_t *A = static_cast<const uint8_t *>(p.A);
     const uint8_t *B = static_cast<const uint8_t *>(p.B);

@@ -14,8 +14,13 @@ struct GemmParams {
     int lda, ldb, ldc;       // elements of each matrix's own type
     float alpha, beta;
     int has_beta, has_bias, relu;
-    int tiles_m, tiles_n;    // output tiles along M and N
+    int tiles_m, tiles_n;    // output tiles along M and N (of one product)
     int group_m;             // tile rows per raster group
+    // strided batch: the launch computes `batch` independent products; product b reads and
+    // writes the operands moved by b * stride (in elements of each operand's own type; C and D
+    // share stride_c; a zero stride shares that operand between products)
+    int batch;
+    int64_t stride_a, stride_b, stride_c, stride_bias;
 };
 
 using LaunchFn = hipError_t (*)(const GemmParams &, unsigned grid, hipStream_t);

@@ -156,7 +156,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
     const int wm = wave / WGN, wn = wave % WGN;
 
     int tile_m, tile_n;
-    raster(xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
+    const int tid_in = select_batch<TI::E, (int)sizeof(typename TO::T)>(
+        p, xcd_remap(blockIdx.x, gridDim.x), p.tiles_m * p.tiles_n);
+    raster(tid_in, p.tiles_m, p.tiles_n, p.group_m, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int m_valid = p.M - m0, n_valid = p.N - n0;
     const bool mn_interior = m_valid >= BM && n_valid >= BN;

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // consecutive column blocks share 128-byte lines of a non-transposed B: keep them on one
     // XCD (one L2) with the same re-mapping the tiled kernels use
-    const int n0 = xcd_remap(blockIdx.x, gridDim.x) * NB;
+    const int n0 = select_batch<2, (int)sizeof(typename TO::T)>(p, xcd_remap(blockIdx.x, gridDim.x), p.tiles_n) * NB;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
