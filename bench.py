@@ -144,7 +144,8 @@ def main():
                     device="cuda:0")
     plan = Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                 batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
-                stride_bias=p.stride_bias)
+                stride_bias=p.stride_bias, transform_a=p.transform_a, transform_b=p.transform_b,
+                transform_c=p.transform_c)
     log(f"[bench] kernel: {plan.describe()}")
 
     stream = torch.cuda.current_stream()
@@ -201,7 +202,9 @@ def main():
             t0 = time.perf_counter()
             out = oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab,
                               C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
-                              beta=p.beta, relu=p.relu, rows=(0, r), threads=threads)
+                              beta=p.beta, relu=p.relu, rows=(0, r), threads=threads,
+                              transform_a=p.transform_a, transform_b=p.transform_b,
+                              transform_c=p.transform_c)
             return time.perf_counter() - t0, out
         r1, r2 = min(32, p.M), min(96, p.M)
         t1, _ = oracle_rows(r1)
@@ -242,6 +245,7 @@ def main():
         "dtype": p.ab,
         "data": "synthetic",
         "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+                   "transforms": [p.transform_a, p.transform_b, p.transform_c],
                    "layout": p.op_a + p.op_b,
                    "ab": p.ab, "cd": p.cd, "epilogue": p.epi, "alpha": p.alpha, "beta": p.beta,
                    "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4)},

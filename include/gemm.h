@@ -73,7 +73,35 @@ typedef enum {
     GEMM_STATUS_ALLOC_FAILED = 4   /* host memory for the plan could not be allocated */
 } gemm_status_t;
 
+/*
+ * Element-wise transforms applied to operand values as they are loaded, before they enter the
+ * product or the epilogue: the "transform" component of "Flexible Performant GEMM Kernels on
+ * GPUs" (section 4), which applies a function to every element after a load, e.g. an
+ * activation, and the "bias + ReLU on C & D" variant of that paper's section 5.3 (Table 2).
+ *   GEMM_TRANSFORM_RELU replaces every element whose sign bit is set by +0, i.e. max(x, 0) for
+ *   every non-NaN x (-0 becomes +0; a NaN keeps its value unless its sign bit is set).
+ */
+typedef enum { GEMM_TRANSFORM_NONE = 0, GEMM_TRANSFORM_RELU = 1 } gemm_transform_t;
+
 typedef struct gemm_plan *gemm_plan_t;
+
+/*
+ * Full problem description for gemm_plan_create_desc.  The first twelve fields are the
+ * arguments of gemm_plan_create; batch and the strides are those of gemm_plan_create_batched
+ * (batch 1 and zero strides for a single product); transform_a / transform_b act on op(A) and
+ * op(B) (zero-padding past the edges is unaffected), transform_c on C before it is scaled by
+ * beta.  Plain data: the library keeps no pointer to it.
+ */
+typedef struct {
+    int64_t M, N, K;
+    gemm_op_t op_a, op_b;
+    int64_t lda, ldb, ldc;
+    gemm_dtype_t ab_type, cd_type;
+    gemm_epilogue_t epilogue;
+    int64_t batch;
+    int64_t stride_a, stride_b, stride_c, stride_bias;
+    gemm_transform_t transform_a, transform_b, transform_c;
+} gemm_desc_t;
 
 /*
  * Builds a plan for one problem description.  Host-only: makes no HIP call.
@@ -115,6 +143,15 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
                                        int64_t ldc, gemm_dtype_t ab_type, gemm_dtype_t cd_type,
                                        gemm_epilogue_t epi, int64_t batch, int64_t stride_a,
                                        int64_t stride_b, int64_t stride_c, int64_t stride_bias);
+
+/*
+ * Builds a plan from a full description (see gemm_desc_t): every option of gemm_plan_create
+ * and gemm_plan_create_batched plus the load transforms,
+ *   D_b = act(alpha * tA(op(A_b)) * tB(op(B_b)) + beta * tC(C_b) + bias_b).
+ * Returns the errors of gemm_plan_create_batched, plus INVALID_VALUE for desc == NULL or a
+ * transform out of range.
+ */
+gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
 
 /*
  * Enqueues D = act(alpha*op(A)*op(B) + beta*C + bias) on `stream` (a hipStream_t; NULL is the

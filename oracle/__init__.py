@@ -127,13 +127,26 @@ def _span(op, rows, cols, ld):
     return (cols - 1) * ld + rows if op == "T" else (rows - 1) * ld + cols
 
 
+def zero_negative(x):
+    """The load transform ReLU on decoded values: every element whose sign bit is set becomes
+    +0, i.e. max(x, 0) for every non-NaN x ("Flexible Performant GEMM Kernels on GPUs",
+    section 4: a transform applies a function such as an activation to every element after it
+    is loaded; the ReLU itself is max(0, x), as in "CUTLASS: Fast Linear Algebra in CUDA C++",
+    "Fusing Element-wise Operations").  Reading where the pages are silent: -0 -> +0, and a NaN
+    is kept unless its sign bit is set."""
+    x = np.asarray(x)
+    return np.where(np.signbit(x), x.dtype.type(0), x)
+
+
 def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
-         bias_dt=None, alpha=1.0, beta=0.0, relu=False, order="tiled", rows=None, threads=None):
-    """Exact (unrounded) result rows x N of act(alpha*op(A)op(B) + beta*C + bias).
+         bias_dt=None, alpha=1.0, beta=0.0, relu=False, order="tiled", rows=None, threads=None,
+         transform_a="none", transform_b="none", transform_c="none"):
+    """Exact (unrounded) result rows x N of act(alpha*tA(op(A)) tB(op(B)) + beta*tC(C) + bias).
 
     ab: input dtype; cd: C/D dtype; bias_dt: bias dtype (default f32, i32 for i8 inputs).
-    rows: optional (r0, r1) to compute only those output rows.  Returns float64, or int64
-    when the inputs are int8."""
+    rows: optional (r0, r1) to compute only those output rows.  transform_*: "none" or "relu"
+    (zero_negative) on the loaded op(A), op(B) and C.  Returns float64, or int64 when the
+    inputs are int8."""
     integer = is_int(ab)
     r0, r1 = (0, M) if rows is None else rows
     mr = r1 - r0
@@ -148,6 +161,10 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
     Bd = decode(ab, Br[: _span(op_b, K, N, ldb)])
     Aop = _dense_op(op_a, mr, K, Ad, lda, integer)
     Bop = _dense_op(op_b, K, N, Bd, ldb, integer)
+    if transform_a == "relu":
+        Aop = np.ascontiguousarray(zero_negative(Aop))
+    if transform_b == "relu":
+        Bop = np.ascontiguousarray(zero_negative(Bop))
     acc = np.zeros(mr * N, np.int64 if integer else np.float64)
     if mr and N and K:
         f = lib().oracle_matmul_i64 if integer else lib().oracle_matmul_f64
@@ -158,6 +175,8 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
         Cd = np.empty(mr * N, np.int64 if integer else np.float64)
         for i in range(mr):
             Cd[i * N:(i + 1) * N] = decode(cd, Cr[(r0 + i) * ldc:(r0 + i) * ldc + N])
+        if transform_c == "relu":
+            Cd = np.ascontiguousarray(zero_negative(Cd))
     bd = None
     if bias is not None:
         bias_dt = bias_dt or ("i32" if integer else "f32")
@@ -175,7 +194,8 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
 
 def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
                  bias_dt=None, alpha=1.0, beta=0.0, relu=False, batch=1, stride_a=0, stride_b=0,
-                 stride_c=0, stride_bias=0, threads=None):
+                 stride_c=0, stride_bias=0, threads=None, transform_a="none", transform_b="none",
+                 transform_c="none"):
     """Exact results (batch x M x N) of a strided batch: product b uses the stored operands
     starting b * stride elements after those of product 0 (C and D share stride_c; a zero
     stride shares the operand).  The logical-index-to-offset mapping of a batched operand is
@@ -191,7 +211,8 @@ def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=N
         out[b] = gemm(M, N, K, op_a, op_b, Ar[b * stride_a:], lda, Br[b * stride_b:], ldb, ab,
                       C=Cr[b * stride_c:] if Cr is not None else None, ldc=ldc, cd=cd,
                       bias=br[b * stride_bias:] if br is not None else None, bias_dt=bias_dt,
-                      alpha=alpha, beta=beta, relu=relu, threads=threads)
+                      alpha=alpha, beta=beta, relu=relu, threads=threads,
+                      transform_a=transform_a, transform_b=transform_b, transform_c=transform_c)
     return out
 
 

@@ -77,6 +77,10 @@ class Problem:
     name: str = ""
     # strided batch: `batch` products, operand x of product b starting stride_x elements after
     # that of product b-1; -1 -> one stored matrix further (tight), 0 -> shared by all products
+    # load transforms on op(A), op(B), C: "none" or "relu"
+    transform_a: str = "none"
+    transform_b: str = "none"
+    transform_c: str = "none"
     batch: int = 1
     stride_a: int = -1
     stride_b: int = -1
@@ -257,6 +261,18 @@ def batched_fp16():
                     batch=16)]
 
 
+def fp16_8192_transforms():
+    """The headline shape with the load transforms of "Flexible Performant GEMM Kernels on
+    GPUs" section 5.3 (Table 2, bias + ReLU on C and D) plus a ReLU on A as it is loaded (an
+    activation fused into the next layer's GEMM): fp16 8192^3 NN, D = ReLU(relu(A) B +
+    relu(C) + bias), A,B ~ N(0,1)/sqrt(K), C ~ U[-1,1] fp16, bias ~ U[-0.5,0.5]."""
+    K = 8192
+    s = 1.0 / math.sqrt(K)
+    return [Problem(8192, 8192, K, "N", "N", "f16", "f16", "bias_relu", 1.0, 1.0,
+                    a_dist=("normal", s), b_dist=("normal", s), key=(7, 0),
+                    name="fp16_8192_transforms", transform_a="relu", transform_c="relu")]
+
+
 WORKLOADS = {
     "sgemm_256": sgemm_256,
     "fp16_8192_bias_relu": fp16_8192_bias_relu,
@@ -264,6 +280,7 @@ WORKLOADS = {
     "int8_4096_bias": int8_4096_bias,
     "fc_layers": fc_layers,
     "batched_fp16": batched_fp16,
+    "fp16_8192_transforms": fp16_8192_transforms,
 }
 
 

@@ -51,7 +51,9 @@ def run(p, x, offset=0, d_rows_extra=0, c_is_d=False, stream=None, plan=None):
     D = to_dev(p.cd, Dinit, offset)
     C = D if c_is_d else (to_dev(p.cd, x["C"], offset) if x["C"] is not None else None)
     bias = to_dev(p.bias_dt, x["bias"], offset) if x["bias"] is not None else None
-    pl = plan or tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    pl = plan or tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
+                          transform_a=p.transform_a, transform_b=p.transform_b,
+                          transform_c=p.transform_c)
     pl.run(A, B, C, D, bias, p.alpha, p.beta, stream=stream)
     torch.cuda.synchronize()
     return to_host(p.cd, D).reshape(rows, p.ldc), pl
@@ -60,7 +62,8 @@ def run(p, x, offset=0, d_rows_extra=0, c_is_d=False, stream=None, plan=None):
 def reference(p, x, rows=None, threads=None):
     return oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab, C=x["C"],
                        ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha, beta=p.beta, relu=p.relu,
-                       rows=rows, threads=threads)
+                       rows=rows, threads=threads, transform_a=p.transform_a,
+                       transform_b=p.transform_b, transform_c=p.transform_c)
 
 
 def normaliser(p, x):
@@ -122,7 +125,8 @@ def run_batched(p, x, offset=0):
     bias = to_dev(p.bias_dt, x["bias"], offset) if x["bias"] is not None else None
     pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                   batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
-                  stride_bias=p.stride_bias)
+                  stride_bias=p.stride_bias, transform_a=p.transform_a,
+                  transform_b=p.transform_b, transform_c=p.transform_c)
     pl.run(A, B, C, D, bias, p.alpha, p.beta)
     torch.cuda.synchronize()
     return to_host(p.cd, D).reshape(-1), pl
@@ -133,4 +137,5 @@ def reference_batched(p, x):
                                C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
                                beta=p.beta, relu=p.relu, batch=p.batch, stride_a=p.stride_a,
                                stride_b=p.stride_b, stride_c=p.stride_c,
-                               stride_bias=p.stride_bias)
+                               stride_bias=p.stride_bias, transform_a=p.transform_a,
+                               transform_b=p.transform_b, transform_c=p.transform_c)

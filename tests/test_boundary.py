@@ -125,3 +125,67 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     paths = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     assert len(paths) == 1, paths
+
+
+# ---- strided batch and the full description ---------------------------------------------------
+
+def _create_batched(**kw):
+    a = dict(M=64, N=64, K=64, op_a="N", op_b="N", lda=64, ldb=64, ldc=64, ab_type="f16",
+             cd_type="f16", epilogue="none", batch=4, stride_a=64 * 64, stride_b=64 * 64,
+             stride_c=64 * 64, stride_bias=0)
+    a.update(kw)
+    return tge.gemm_plan_create_batched(**a)
+
+
+@pytest.mark.parametrize("kw", [dict(batch=-1), dict(stride_a=-1), dict(stride_b=-2),
+                                dict(stride_c=-1), dict(stride_bias=-1),
+                                dict(stride_c=64 * 63 + 63), dict(stride_c=0)])
+def test_batched_invalid_values(kw):
+    st, h = _create_batched(**kw)
+    assert st == tge.STATUS_INVALID_VALUE and h is None
+
+
+def test_batched_valid_and_described():
+    st, h = _create_batched(stride_c=64 * 63 + 64, stride_a=0)
+    assert st == tge.STATUS_SUCCESS
+    assert "batch 4" in tge.gemm_plan_describe(h)[1]
+    tge.gemm_plan_destroy(h)
+    # batch 1 ignores the strides, batch 0 is a valid empty launch
+    for b in (0, 1):
+        st, h = _create_batched(batch=b, stride_c=0)
+        assert st == tge.STATUS_SUCCESS
+        tge.gemm_plan_destroy(h)
+
+
+def test_batched_grid_limit():
+    st, _ = _create_batched(M=4096, N=4096, K=64, lda=64, ldb=4096, ldc=4096, batch=1 << 24,
+                            stride_a=0, stride_b=0, stride_c=4096 * 4096)
+    assert st == tge.STATUS_NOT_SUPPORTED
+
+
+def test_batch_zero_run_returns_without_launch():
+    p = tge.Plan(64, 64, 64, batch=0, stride_c=64 * 64)
+    assert tge.gemm_run(p.handle, None, None, None, 1, None, 1.0, 0.0, None) == tge.STATUS_SUCCESS
+
+
+def test_desc_validation_and_transforms_described():
+    st, h = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, "f16", "f16", "none",
+                                      transform_a="relu", transform_c="relu")
+    assert st == tge.STATUS_SUCCESS and "relu-in AC" in tge.gemm_plan_describe(h)[1]
+    tge.gemm_plan_destroy(h)
+    for bad in (dict(transform_a=2), dict(transform_b=-1), dict(transform_c=7)):
+        st, h = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, "f16", "f16", "none",
+                                          **bad)
+        assert st == tge.STATUS_INVALID_VALUE and h is None
+    lib = ctypes.CDLL(tge.LIB_PATH)
+    lib.gemm_plan_create_desc.restype = ctypes.c_int
+    out = ctypes.c_void_p()
+    assert lib.gemm_plan_create_desc(ctypes.byref(out), None) == tge.STATUS_INVALID_VALUE
+    assert out.value is None
+
+
+def test_desc_matches_the_plain_create():
+    a = tge.gemm_plan_create_desc(300, 200, 100, "T", "N", 300, 200, 200, "bf16", "f32", "bias")
+    b = tge.gemm_plan_create(300, 200, 100, "T", "N", 300, 200, 200, "bf16", "f32", "bias")
+    assert a[0] == b[0] == tge.STATUS_SUCCESS
+    assert tge.gemm_plan_describe(a[1])[1] == tge.gemm_plan_describe(b[1])[1]

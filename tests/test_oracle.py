@@ -330,3 +330,33 @@ def test_batched_of_one_and_zero_strides_repeat_the_product():
     rep = oracle.gemm_batched(M, N, K, "N", "N", A, K, B, N, "i8", batch=3, stride_c=M * N)
     for b in range(3):
         assert np.array_equal(rep[b], one)
+
+
+# ---- load transforms ---------------------------------------------------------------------------
+
+def test_zero_negative_rule():
+    """max(x, 0) for non-NaN x, read as: sign bit set -> +0 (so -0 -> +0, -NaN -> 0, +NaN kept)."""
+    x = np.array([-2.5, -0.0, 0.0, 1.5, -np.inf, np.inf, np.nan, -np.nan])
+    y = oracle.zero_negative(x)
+    assert list(y[:6]) == [0.0, 0.0, 0.0, 1.5, 0.0, np.inf]
+    assert not np.signbit(y[:2]).any()
+    assert np.isnan(y[6]) and y[7] == 0.0 and not np.signbit(y[7])
+    assert list(oracle.zero_negative(np.array([-128, -1, 0, 1, 127], np.int64))) == [0, 0, 0, 1, 127]
+
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+def test_transforms_against_numpy(lay):
+    """tA, tB on the operands and tC on C against numpy with np.maximum(., 0) applied to the
+    logical matrices (int8 values, exact in int64)."""
+    g = np.random.default_rng(33)
+    for (M, N, K) in [(4, 5, 6), (1, 3, 7), (9, 2, 4)]:
+        X, Y, A, lda, B, ldb = _random_problem(g, M, N, K, lay[0], lay[1], True, pad=2)
+        C = g.integers(-50, 50, M * N).astype(np.int32)
+        for ta, tb, tc in [("relu", "none", "none"), ("none", "relu", "relu"), ("relu", "relu", "relu")]:
+            got = oracle.gemm(M, N, K, lay[0], lay[1], A, lda, B, ldb, "i8", C=C, ldc=N, cd="i32",
+                              alpha=1, beta=1, transform_a=ta, transform_b=tb, transform_c=tc)
+            Xt = np.maximum(X.astype(np.int64), 0) if ta == "relu" else X.astype(np.int64)
+            Yt = np.maximum(Y.astype(np.int64), 0) if tb == "relu" else Y.astype(np.int64)
+            Ct = C.astype(np.int64).reshape(M, N)
+            Ct = np.maximum(Ct, 0) if tc == "relu" else Ct
+            assert np.array_equal(got, Xt @ Yt + Ct)

@@ -4,9 +4,9 @@
 
 Argument marshalling only: every step of the computation runs in the HIP kernels behind the C
 ABI (include/gemm.h).  The low-level functions carry the C names (gemm_plan_create, gemm_run,
-gemm_plan_create_batched, gemm_plan_destroy, gemm_status_string, gemm_plan_describe); `Plan`
-wraps them for torch tensors, whose device memory and streams are the only things taken from
-PyTorch.
+gemm_plan_create_batched, gemm_plan_create_desc, gemm_plan_destroy, gemm_status_string,
+gemm_plan_describe); `Plan` wraps them for torch tensors, whose device memory and streams are the
+only things taken from PyTorch.
 
 There is no fallback: importing this package fails if the HIP library has not been built
 (python -m tiled_gemm_epilogues_amd.build, or __graft_entry__.build()).
@@ -31,6 +31,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OP = {"N": 0, "T": 1}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4}
 EPILOGUE = {"none": 0, "relu": 1, "bias": 2, "bias_relu": 3}
+TRANSFORM = {"none": 0, "relu": 1}
 STATUS_SUCCESS, STATUS_INVALID_VALUE, STATUS_NOT_SUPPORTED, STATUS_HIP_ERROR, STATUS_ALLOC_FAILED = range(5)
 
 _i64, _vp, _ci, _f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -40,6 +41,19 @@ _lib.gemm_plan_create.restype = _ci
 _lib.gemm_plan_create_batched.argtypes = [ctypes.POINTER(_vp), _i64, _i64, _i64, _ci, _ci, _i64, _i64,
                                           _i64, _ci, _ci, _ci, _i64, _i64, _i64, _i64, _i64]
 _lib.gemm_plan_create_batched.restype = _ci
+
+
+class GemmDesc(ctypes.Structure):
+    """gemm_desc_t of include/gemm.h (field order and types as declared there)."""
+    _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("op_a", _ci), ("op_b", _ci),
+                ("lda", _i64), ("ldb", _i64), ("ldc", _i64), ("ab_type", _ci), ("cd_type", _ci),
+                ("epilogue", _ci), ("batch", _i64), ("stride_a", _i64), ("stride_b", _i64),
+                ("stride_c", _i64), ("stride_bias", _i64), ("transform_a", _ci),
+                ("transform_b", _ci), ("transform_c", _ci)]
+
+
+_lib.gemm_plan_create_desc.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(GemmDesc)]
+_lib.gemm_plan_create_desc.restype = _ci
 _lib.gemm_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _vp]
 _lib.gemm_run.restype = _ci
 _lib.gemm_plan_destroy.argtypes = [_vp]
@@ -49,8 +63,8 @@ _lib.gemm_status_string.restype = ctypes.c_char_p
 _lib.gemm_plan_describe.argtypes = [_vp, ctypes.c_char_p, ctypes.c_size_t]
 _lib.gemm_plan_describe.restype = _ci
 
-EXPORTED = ("gemm_plan_create", "gemm_plan_create_batched", "gemm_run", "gemm_plan_destroy",
-            "gemm_status_string", "gemm_plan_describe")
+EXPORTED = ("gemm_plan_create", "gemm_plan_create_batched", "gemm_plan_create_desc", "gemm_run",
+            "gemm_plan_destroy", "gemm_status_string", "gemm_plan_describe")
 
 
 class GemmError(RuntimeError):
@@ -80,6 +94,19 @@ def gemm_plan_create_batched(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_typ
                                        lda, ldb, ldc, _enum(DTYPE, ab_type), _enum(DTYPE, cd_type),
                                        _enum(EPILOGUE, epilogue), batch, stride_a, stride_b,
                                        stride_c, stride_bias)
+    return st, h.value
+
+
+def gemm_plan_create_desc(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epilogue,
+                          batch=1, stride_a=0, stride_b=0, stride_c=0, stride_bias=0,
+                          transform_a="none", transform_b="none", transform_c="none"):
+    """Returns (status, handle) of a plan built from a full gemm_desc_t."""
+    d = GemmDesc(M, N, K, _enum(OP, op_a), _enum(OP, op_b), lda, ldb, ldc, _enum(DTYPE, ab_type),
+                 _enum(DTYPE, cd_type), _enum(EPILOGUE, epilogue), batch, stride_a, stride_b,
+                 stride_c, stride_bias, _enum(TRANSFORM, transform_a),
+                 _enum(TRANSFORM, transform_b), _enum(TRANSFORM, transform_c))
+    h = _vp()
+    st = _lib.gemm_plan_create_desc(ctypes.byref(h), ctypes.byref(d))
     return st, h.value
 
 
@@ -124,18 +151,24 @@ def _ptr(t, want, what):
 
 class Plan:
     """A plan for one problem description (see include/gemm.h for the storage rules).  With
-    batch != 1 it is a strided-batched plan (gemm_plan_create_batched; strides in elements)."""
+    batch != 1 it is a strided-batched plan (gemm_plan_create_batched; strides in elements);
+    with a transform it is built from a full description (gemm_plan_create_desc)."""
 
     def __init__(self, M, N, K, op_a="N", op_b="N", lda=None, ldb=None, ldc=None, ab="f16",
                  cd="f16", epilogue="none", batch=1, stride_a=0, stride_b=0, stride_c=0,
-                 stride_bias=0):
+                 stride_bias=0, transform_a="none", transform_b="none", transform_c="none"):
         self.M, self.N, self.K = M, N, K
         self.op_a, self.op_b, self.ab, self.cd, self.epilogue = op_a, op_b, ab, cd, epilogue
         self.lda = lda if lda is not None else max(1, K if op_a == "N" else M)
         self.ldb = ldb if ldb is not None else max(1, N if op_b == "N" else K)
         self.ldc = ldc if ldc is not None else max(1, N)
         self.batch = batch
-        if batch == 1 and not (stride_a or stride_b or stride_c or stride_bias):
+        xf = (transform_a, transform_b, transform_c)
+        if any(_enum(TRANSFORM, t) for t in xf):
+            st, h = gemm_plan_create_desc(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd,
+                                          epilogue, batch, stride_a, stride_b, stride_c,
+                                          stride_bias, *xf)
+        elif batch == 1 and not (stride_a or stride_b or stride_c or stride_bias):
             st, h = gemm_plan_create(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd,
                                      epilogue)
         else:

@@ -173,6 +173,46 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// Load transform GEMM_TRANSFORM_RELU on a 16-byte chunk of E-byte elements: every element whose
+// sign bit is set becomes +0 (max(x, 0) for every non-NaN x; the same rule for fp16, bf16 and
+// int8 as 16- or 8-bit two's-complement sign tests, and for fp32 / int32 as 32-bit ones).
+// Branch-free with the enable `on` (uniform 0/1), so it can sit inside a software pipeline.
+template <int E>
+__device__ __forceinline__ u32x4 zero_negative(u32x4 v, int on) {
+    if constexpr (E == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (on && (int)v[i] < 0) ? 0u : v[i];
+    } else if constexpr (E == 2) {
+        typedef short s2 __attribute__((ext_vector_type(2)));
+        const short fl = on ? (short)0 : (short)-32768;   // max(x, -32768) leaves x unchanged
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = v[i];   // bit_cast of a vector-element lvalue would read element 0
+            const s2 h = __builtin_bit_cast(s2, w);
+            v[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(h, (s2){fl, fl}));
+        }
+    } else {
+        // sign bits m (0x80 per negative byte) -> whole-byte masks m | (m - m/128); no byte
+        // borrows from its neighbour because each byte of m is >= the same byte of m >> 7
+        const uint32_t sel = on ? 0x80808080u : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t m = v[i] & sel;
+            v[i] &= ~(m | (m - (m >> 7)));
+        }
+    }
+    return v;
+}
+
+// A C element as the epilogue uses it: in the accumulation type, with the load transform
+// (relu_in: sign bit set -> +0) applied.
+template <class T>
+__device__ __forceinline__ float c_in_f(T c, int relu_in) {
+    const float f = (float)c;
+    return (relu_in && __builtin_bit_cast(int, f) < 0) ? 0.0f : f;
+}
+__device__ __forceinline__ int c_in_i(int c, int relu_in) { return (relu_in && c < 0) ? 0 : c; }
+
 // Strided batch: workgroup id -> (product b, id inside the product, `per` ids per product); the
 // operand pointers of `p` are moved to product b.  Consecutive ids share a product, so the
 // XCD-contiguous id ranges of xcd_remap keep each product on few XCDs.
@@ -265,12 +305,12 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int mbase, int n
                     if constexpr (INT) {
                         // integer path: alpha == 1, beta in {0, 1}
                         int t = acc[i][j][4 * g + e] + bv[j][g][e];
-                        if (p.has_beta) t += (int)cv[j][g][e];
+                        if (p.has_beta) t += c_in_i((int)cv[j][g][e], p.xform_c);
                         if (p.relu) t = t > 0 ? t : 0;
                         out[e] = (T)t;
                     } else {
                         float t = p.alpha * acc[i][j][4 * g + e];
-                        if (p.has_beta) t += p.beta * (float)cv[j][g][e];
+                        if (p.has_beta) t += p.beta * c_in_f(cv[j][g][e], p.xform_c);
                         t += bv[j][g][e];
                         if (p.relu) t = t > 0.0f ? t : 0.0f;
                         out[e] = (T)t;

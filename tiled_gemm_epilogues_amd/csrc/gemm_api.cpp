@@ -17,6 +17,7 @@ using tge::KernelEntry;
 struct gemm_plan {
     int64_t M, N, K, lda, ldb, ldc;
     int64_t batch, stride_a, stride_b, stride_c, stride_bias;
+    int xform_a, xform_b, xform_c;
     int op_a, op_b, ab, cd, epi;
     const KernelEntry *kernel;       // general kernel (always valid)
     const KernelEntry *fast;         // fast or skinny kernel when the plan qualifies, else nullptr
@@ -127,8 +128,31 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
                                        int64_t ldc, gemm_dtype_t ab_type, gemm_dtype_t cd_type,
                                        gemm_epilogue_t epi, int64_t batch, int64_t stride_a,
                                        int64_t stride_b, int64_t stride_c, int64_t stride_bias) {
+    gemm_desc_t d;
+    d.M = M; d.N = N; d.K = K;
+    d.op_a = op_a; d.op_b = op_b;
+    d.lda = lda; d.ldb = ldb; d.ldc = ldc;
+    d.ab_type = ab_type; d.cd_type = cd_type; d.epilogue = epi;
+    d.batch = batch;
+    d.stride_a = stride_a; d.stride_b = stride_b; d.stride_c = stride_c; d.stride_bias = stride_bias;
+    d.transform_a = d.transform_b = d.transform_c = GEMM_TRANSFORM_NONE;
+    return gemm_plan_create_desc(out, &d);
+}
+
+gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (!out) return GEMM_STATUS_INVALID_VALUE;
     *out = nullptr;
+    if (!desc) return GEMM_STATUS_INVALID_VALUE;
+    const int64_t M = desc->M, N = desc->N, K = desc->K;
+    const gemm_op_t op_a = desc->op_a, op_b = desc->op_b;
+    const int64_t lda = desc->lda, ldb = desc->ldb, ldc = desc->ldc;
+    const gemm_dtype_t ab_type = desc->ab_type, cd_type = desc->cd_type;
+    const gemm_epilogue_t epi = desc->epilogue;
+    const int64_t batch = desc->batch;
+    int64_t stride_a = desc->stride_a, stride_b = desc->stride_b, stride_c = desc->stride_c,
+            stride_bias = desc->stride_bias;
+    for (gemm_transform_t t : {desc->transform_a, desc->transform_b, desc->transform_c})
+        if ((int)t != GEMM_TRANSFORM_NONE && (int)t != GEMM_TRANSFORM_RELU) return GEMM_STATUS_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
     if (batch < 0 || stride_a < 0 || stride_b < 0 || stride_c < 0 || stride_bias < 0)
         return GEMM_STATUS_INVALID_VALUE;
@@ -205,6 +229,7 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
     if (!p) return GEMM_STATUS_ALLOC_FAILED;
     p->M = M; p->N = N; p->K = K;
     p->batch = batch;
+    p->xform_a = desc->transform_a; p->xform_b = desc->transform_b; p->xform_c = desc->transform_c;
     p->stride_a = stride_a; p->stride_b = stride_b; p->stride_c = stride_c; p->stride_bias = stride_bias;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
     p->op_a = op_a; p->op_b = op_b; p->ab = ab_type; p->cd = cd_type; p->epi = epi;
@@ -221,8 +246,12 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
         return GEMM_STATUS_NOT_SUPPORTED;
     }
     p->grid = (unsigned)grid;
-    char bdesc[48] = "";
-    if (batch != 1) snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
+    char bdesc[64] = "";
+    int bl = 0;
+    if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
+    if (desc->transform_a || desc->transform_b || desc->transform_c)
+        snprintf(bdesc + bl, sizeof(bdesc) - bl, " relu-in %s%s%s", desc->transform_a ? "A" : "",
+                 desc->transform_b ? "B" : "", desc->transform_c ? "C" : "");
     snprintf(p->desc, sizeof(p->desc), "%s %s->%s %c%c tile %dx%dx%d waves %dx%d grid %u%s",
              shown->name, dtype_name(ab_type), dtype_name(cd_type), op_a ? 'T' : 'N',
              op_b ? 'T' : 'N', shown->bm, shown->bn, shown->bk, shown->waves_m, shown->waves_n,
@@ -266,6 +295,7 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     prm.relu = relu;
     prm.group_m = p->group_m;
     prm.batch = (int)p->batch;
+    prm.xform_a = p->xform_a; prm.xform_b = p->xform_b; prm.xform_c = p->xform_c;
     prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
     prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
     const KernelEntry *k = p->kernel;

@@ -352,7 +352,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     int t = accv(b, q, e) + bq[e];
-                    if constexpr (BETA) t += (int)cv[q][e];
+                    if constexpr (BETA) t += c_in_i((int)cv[q][e], p.xform_c);
                     if (p.relu) t = max(t, 0);
                     out[e] = (T)t;
                 }
@@ -361,7 +361,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     t[e] = __builtin_fmaf(p.alpha, accv(b, q, e), bq[e]);
-                    if constexpr (BETA) t[e] = __builtin_fmaf(p.beta, (float)cv[q][e], t[e]);
+                    if constexpr (BETA) t[e] = __builtin_fmaf(p.beta, c_in_f(cv[q][e], p.xform_c), t[e]);
                     if (p.relu) t[e] = __builtin_fmaxf(t[e], 0.0f);
                 }
                 if constexpr (ES == 2) {
@@ -435,7 +435,9 @@ struct Sched {
     static_assert(N3 <= 16, "loads after the barrier");
 };
 
-template <class TI, class TO, bool AK, bool BK, int MF>
+// XF: the launch has a load transform on op(A) or op(B), applied to every fragment after its LDS
+// read (the direct loads put raw operand bytes in LDS)
+template <class TI, class TO, bool AK, bool BK, int MF, bool XF>
 __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     using acc_t = typename TI::acc_t;
     using accv_t = typename std::conditional<MF == 32, typename TI::accv_t, typename TI::accv16_t>::type;
@@ -492,6 +494,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         if (q == 0) fa.read(stage, 0, j, af[buf][0]);
         else if (q <= NF) fb.read(stage, q - 1, j, bf[buf][q - 1]);
         else fa.read(stage, q - NF, j, af[buf][q - NF]);
+        if constexpr (XF) {
+            // load transform on the fragment just read (a disabled one is a no-op)
+            if (q == 0) af[buf][0] = zero_negative<E>(af[buf][0], p.xform_a);
+            else if (q <= NF) bf[buf][q - 1] = zero_negative<E>(bf[buf][q - 1], p.xform_b);
+            else af[buf][q - NF] = zero_negative<E>(af[buf][q - NF], p.xform_a);
+        }
     };
     // reads issued with MFMA slot t of a k-slice (slots 0 .. NMS-1 spread NRD reads)
     auto rd_slot = [&](int stage, int j, int buf, int t, int slots) {
@@ -507,6 +515,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     // MFMA number t (0 .. NMS-1) of a k-slice: A fragment t/NF times B fragment t%NF
     auto mma = [&](int buf, int t) {
         const int i = t / NF, j = t % NF;
+
         if constexpr (MF == 32) acc[i][j] = TI::mma(bf[buf][j], af[buf][i], acc[i][j]);
         else acc[i][j] = TI::mma16(bf[buf][j], af[buf][i], acc[i][j]);
     };
@@ -653,7 +662,13 @@ constexpr int fast_mf() { return (AT && !BT) ? 32 : 16; }
 
 template <class TI, class TO, bool AT, bool BT>
 hipError_t launch_fast(const GemmParams &p, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, fast_mf<AT, BT>()>), dim3(grid), dim3(NT), 0, s, p);
+    // load transforms on op(A)/op(B) run on the fragments; with the 16x16 schedule the extra
+    // VALU work on fragment registers makes the allocator shuffle accumulators, the 32x32 one
+    // stays clean
+    if (p.xform_a || p.xform_b)
+        hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, 32, true>), dim3(grid), dim3(NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, fast_mf<AT, BT>(), false>), dim3(grid), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

@@ -21,6 +21,8 @@ struct GemmParams {
     // share stride_c; a zero stride shares that operand between products)
     int batch;
     int64_t stride_a, stride_b, stride_c, stride_bias;
+    // load transforms (1: zero every element whose sign bit is set) on op(A), op(B) and C
+    int xform_a, xform_b, xform_c;
 };
 
 using LaunchFn = hipError_t (*)(const GemmParams &, unsigned grid, hipStream_t);

@@ -80,11 +80,12 @@ struct Stager<E, BMN, NT, true> {
             }
         }
     }
-    __device__ __forceinline__ void store(uint8_t *lds, int tid) const {
+    // xf: the load transform (sign bit set -> +0) on the staged values
+    __device__ __forceinline__ void store(uint8_t *lds, int tid, int xf) const {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             int q = tid + NT * i, row = q >> 3, c = q & 7;
-            *reinterpret_cast<u32x4 *>(lds + lds_off(row, c)) = r[i];
+            *reinterpret_cast<u32x4 *>(lds + lds_off(row, c)) = zero_negative<E>(r[i], xf);
         }
     }
 };
@@ -121,14 +122,16 @@ struct Stager<E, BMN, NT, false> {
             }
         }
     }
-    __device__ __forceinline__ void store(uint8_t *lds, int tid) const {
+    __device__ __forceinline__ void store(uint8_t *lds, int tid, int xf) const {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             int b = tid + NT * i;
             if (NBLK % NT != 0 && b >= NBLK) break;
             int mc = b % NCH, kg = b / NCH;
-            u32x4 t[VE];
-            transpose_block<E>(r[i], t);
+            u32x4 t[VE], x[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) x[e] = zero_negative<E>(r[i][e], xf);
+            transpose_block<E>(x, t);
 #pragma unroll
             for (int e = 0; e < VE; ++e)
                 *reinterpret_cast<u32x4 *>(lds + lds_off(mc * VE + e, kg)) = t[e];
@@ -182,8 +185,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
         bool interior = mn_interior && BK <= p.K;
         sa.load(A, p.lda, m0, m_valid, 0, p.K, interior, tid);
         sb.load(B, p.ldb, n0, n_valid, 0, p.K, interior, tid);
-        sa.store(smem, tid);
-        sb.store(smem + BM * 128, tid);
+        sa.store(smem, tid, p.xform_a);
+        sb.store(smem + BM * 128, tid, p.xform_b);
     }
     __syncthreads();
 
@@ -220,8 +223,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
         }
         if (more) {
             uint8_t *nxt = smem + (cur ^ 1) * STAGE;
-            sa.store(nxt, tid);
-            sb.store(nxt + BM * 128, tid);
+            sa.store(nxt, tid, p.xform_a);
+            sb.store(nxt + BM * 128, tid, p.xform_b);
         }
         __syncthreads();
     }

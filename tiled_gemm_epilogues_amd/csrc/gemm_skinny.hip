@@ -173,6 +173,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
             af[t] = *(const lds_u32x4 *)(uintptr_t)(lds_addr(sl) + 1024u * (1 + t) + offA);
+        // load transforms (no-ops when disabled)
+        bf = zero_negative<2>(bf, p.xform_b);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) af[t] = zero_negative<2>(af[t], p.xform_a);
         // the slot is refilled below: its reads must have returned first
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
             if (m >= p.M) continue;
             const int64_t idx = (int64_t)m * p.ldc + n;
             float x = p.alpha * acc[t][r];
-            if (p.has_beta) x += p.beta * (float)C[idx];
+            if (p.has_beta) x += p.beta * c_in_f(C[idx], p.xform_c);
             x += bv;
             if (p.relu) x = x > 0.0f ? x : 0.0f;
             D[idx] = (T)x;
