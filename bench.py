@@ -145,7 +145,7 @@ def main():
     plan = Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                 batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
                 stride_bias=p.stride_bias, transform_a=p.transform_a, transform_b=p.transform_b,
-                transform_c=p.transform_c)
+                transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b)
     log(f"[bench] kernel: {plan.describe()}")
 
     stream = torch.cuda.current_stream()
@@ -204,7 +204,7 @@ def main():
                               C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
                               beta=p.beta, relu=p.relu, rows=(0, r), threads=threads,
                               transform_a=p.transform_a, transform_b=p.transform_b,
-                              transform_c=p.transform_c)
+                              transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b)
             return time.perf_counter() - t0, out
         r1, r2 = min(32, p.M), min(96, p.M)
         t1, _ = oracle_rows(r1)
@@ -214,7 +214,7 @@ def main():
         rows = int((args.cpu_seconds - fixed) / per_row) // 32 * 32
         rows = max(r1, min(p.M, rows))
         t_cpu, ref = oracle_rows(rows)
-        sample_flops = 2.0 * rows * p.N * p.K
+        sample_flops = p.flops * rows / p.M / max(p.batch, 1)
         cpu = {"value": round(sample_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
                "sample": f"output rows 0..{rows - 1} of {p.M}{' of product 0' if p.batch != 1 else ''} "
@@ -222,8 +222,10 @@ def main():
                          f"{sample_flops:.3e} flop in {t_cpu:.1f}s, fp64/int64 accumulation"}
         log(f"[bench] cpu oracle: {cpu['sample']}")
         got = oracle.decode(p.cd, Dh[:rows, : p.N]) if p.cd != "i32" else Dh[:rows, : p.N].astype(np.int64)
-        maxa = oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda)
-        maxb = oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb)
+        maxa = (float(np.abs(oracle.decode(p.ab, x["A"])).max()) if p.kind_a == "diagonal"
+                else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda))
+        maxb = (float(np.abs(oracle.decode(p.ab, x["B"])).max()) if p.kind_b == "diagonal"
+                else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb))
         den = p.K * maxa * maxb
         err = float(np.max(np.abs(got - ref)) / den) if den else float(np.max(np.abs(got - ref)))
         parity = {"rows_checked": rows, "max_normalised_error": err, "tolerance": 2e-3,
@@ -246,6 +248,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
                    "transforms": [p.transform_a, p.transform_b, p.transform_c],
+                   "kinds": [p.kind_a, p.kind_b],
                    "layout": p.op_a + p.op_b,
                    "ab": p.ab, "cd": p.cd, "epilogue": p.epi, "alpha": p.alpha, "beta": p.beta,
                    "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4)},

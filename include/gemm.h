@@ -83,6 +83,15 @@ typedef enum {
  */
 typedef enum { GEMM_TRANSFORM_NONE = 0, GEMM_TRANSFORM_RELU = 1 } gemm_transform_t;
 
+/*
+ * Kind of an operand.  GEMM_OPERAND_DIAGONAL: the operand is a square diagonal matrix given by
+ * the vector of its diagonal elements (ab_type; a diagonal A is M x M with K == M, a diagonal B
+ * is N x N with K == N); its op and leading dimension are ignored.  Off-diagonal elements are
+ * never loaded and K steps that meet no diagonal element are skipped: the diagonal layout and
+ * the skip predicate of "Flexible Performant GEMM Kernels on GPUs", section 5.2 (Table 1).
+ */
+typedef enum { GEMM_OPERAND_DENSE = 0, GEMM_OPERAND_DIAGONAL = 1 } gemm_operand_t;
+
 typedef struct gemm_plan *gemm_plan_t;
 
 /*
@@ -90,7 +99,8 @@ typedef struct gemm_plan *gemm_plan_t;
  * arguments of gemm_plan_create; batch and the strides are those of gemm_plan_create_batched
  * (batch 1 and zero strides for a single product); transform_a / transform_b act on op(A) and
  * op(B) (zero-padding past the edges is unaffected), transform_c on C before it is scaled by
- * beta.  Plain data: the library keeps no pointer to it.
+ * beta; kind_a / kind_b make an operand diagonal (see gemm_operand_t; a diagonal operand's
+ * stride_a / stride_b moves its vector).  Plain data: the library keeps no pointer to it.
  */
 typedef struct {
     int64_t M, N, K;
@@ -101,6 +111,7 @@ typedef struct {
     int64_t batch;
     int64_t stride_a, stride_b, stride_c, stride_bias;
     gemm_transform_t transform_a, transform_b, transform_c;
+    gemm_operand_t kind_a, kind_b;
 } gemm_desc_t;
 
 /*
@@ -148,8 +159,9 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
  * Builds a plan from a full description (see gemm_desc_t): every option of gemm_plan_create
  * and gemm_plan_create_batched plus the load transforms,
  *   D_b = act(alpha * tA(op(A_b)) * tB(op(B_b)) + beta * tC(C_b) + bias_b).
- * Returns the errors of gemm_plan_create_batched, plus INVALID_VALUE for desc == NULL or a
- * transform out of range.
+ * Returns the errors of gemm_plan_create_batched, plus INVALID_VALUE for desc == NULL, a
+ * transform or operand kind out of range, or a diagonal operand that is not square (K != M for
+ * A, K != N for B).
  */
 gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
 

@@ -140,27 +140,39 @@ def zero_negative(x):
 
 def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
          bias_dt=None, alpha=1.0, beta=0.0, relu=False, order="tiled", rows=None, threads=None,
-         transform_a="none", transform_b="none", transform_c="none"):
+         transform_a="none", transform_b="none", transform_c="none", kind_a="dense",
+         kind_b="dense"):
     """Exact (unrounded) result rows x N of act(alpha*tA(op(A)) tB(op(B)) + beta*tC(C) + bias).
 
     ab: input dtype; cd: C/D dtype; bias_dt: bias dtype (default f32, i32 for i8 inputs).
     rows: optional (r0, r1) to compute only those output rows.  transform_*: "none" or "relu"
-    (zero_negative) on the loaded op(A), op(B) and C.  Returns float64, or int64 when the
-    inputs are int8."""
+    (zero_negative) on the loaded op(A), op(B) and C.  kind_*: "dense" or "diagonal" (the
+    operand is the square diagonal matrix of the vector given, its op and ld ignored:
+    "Flexible Performant GEMM Kernels on GPUs", section 5.2).  Returns float64, or int64 when
+    the inputs are int8."""
     integer = is_int(ab)
     r0, r1 = (0, M) if rows is None else rows
     mr = r1 - r0
     threads = threads or os.cpu_count() or 1
     Ar, Br = _raw(ab, A), _raw(ab, B)
-    # decode only the stored rows that op(A)[r0:r1] touches
-    if op_a == "N":
-        Asub = Ar[r0 * lda: r0 * lda + _span("N", mr, K, lda)]
+    if kind_a == "diagonal":
+        # rows r0..r1 of diag(a): element (i, k) = a[r0 + i] if k == r0 + i else 0
+        assert K == M
+        Aop = np.zeros((mr, K), np.int64 if integer else np.float64)
+        Aop[np.arange(mr), r0 + np.arange(mr)] = decode(ab, Ar[r0:r1])
+        Aop = Aop.reshape(-1)
     else:
-        Asub = Ar[r0: r0 + _span("T", mr, K, lda)]
-    Ad = decode(ab, Asub)
-    Bd = decode(ab, Br[: _span(op_b, K, N, ldb)])
-    Aop = _dense_op(op_a, mr, K, Ad, lda, integer)
-    Bop = _dense_op(op_b, K, N, Bd, ldb, integer)
+        # decode only the stored rows that op(A)[r0:r1] touches
+        if op_a == "N":
+            Asub = Ar[r0 * lda: r0 * lda + _span("N", mr, K, lda)]
+        else:
+            Asub = Ar[r0: r0 + _span("T", mr, K, lda)]
+        Aop = _dense_op(op_a, mr, K, decode(ab, Asub), lda, integer)
+    if kind_b == "diagonal":
+        assert K == N
+        Bop = np.diag(decode(ab, Br[:N])).astype(np.int64 if integer else np.float64).reshape(-1)
+    else:
+        Bop = _dense_op(op_b, K, N, decode(ab, Br[: _span(op_b, K, N, ldb)]), ldb, integer)
     if transform_a == "relu":
         Aop = np.ascontiguousarray(zero_negative(Aop))
     if transform_b == "relu":
@@ -195,7 +207,7 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
 def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
                  bias_dt=None, alpha=1.0, beta=0.0, relu=False, batch=1, stride_a=0, stride_b=0,
                  stride_c=0, stride_bias=0, threads=None, transform_a="none", transform_b="none",
-                 transform_c="none"):
+                 transform_c="none", kind_a="dense", kind_b="dense"):
     """Exact results (batch x M x N) of a strided batch: product b uses the stored operands
     starting b * stride elements after those of product 0 (C and D share stride_c; a zero
     stride shares the operand).  The logical-index-to-offset mapping of a batched operand is
@@ -212,7 +224,8 @@ def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=N
                       C=Cr[b * stride_c:] if Cr is not None else None, ldc=ldc, cd=cd,
                       bias=br[b * stride_bias:] if br is not None else None, bias_dt=bias_dt,
                       alpha=alpha, beta=beta, relu=relu, threads=threads,
-                      transform_a=transform_a, transform_b=transform_b, transform_c=transform_c)
+                      transform_a=transform_a, transform_b=transform_b, transform_c=transform_c,
+                      kind_a=kind_a, kind_b=kind_b)
     return out
 
 

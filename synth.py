@@ -81,6 +81,9 @@ class Problem:
     transform_a: str = "none"
     transform_b: str = "none"
     transform_c: str = "none"
+    # "dense" or "diagonal" (the operand is the vector of a square diagonal matrix's elements)
+    kind_a: str = "dense"
+    kind_b: str = "dense"
     batch: int = 1
     stride_a: int = -1
     stride_b: int = -1
@@ -94,13 +97,17 @@ class Problem:
             self.ldb = max(1, self.N if self.op_b == "N" else self.K)
         if not self.ldc:
             self.ldc = max(1, self.N)
+        if self.kind_a == "diagonal":
+            self.lda = 1
+        if self.kind_b == "diagonal":
+            self.ldb = 1
         if self.batch <= 1:
             self.stride_a = self.stride_b = self.stride_c = self.stride_bias = 0
         else:
             if self.stride_a < 0:
-                self.stride_a = self.a_shape()[0] * self.lda
+                self.stride_a = self.M if self.kind_a == "diagonal" else self.a_shape()[0] * self.lda
             if self.stride_b < 0:
-                self.stride_b = self.b_shape()[0] * self.ldb
+                self.stride_b = self.N if self.kind_b == "diagonal" else self.b_shape()[0] * self.ldb
             if self.stride_c < 0:
                 self.stride_c = self.M * self.ldc
             if self.stride_bias < 0:
@@ -120,7 +127,14 @@ class Problem:
 
     @property
     def flops(self):
-        return 2.0 * self.M * self.N * self.K * max(self.batch, 0)
+        """2 x the multiply-adds the product needs: M*N*K, or for a diagonal operand only the
+        non-zero terms (one per output element; with both diagonal, one per diagonal element)."""
+        nb = max(self.batch, 0)
+        if self.kind_a == "diagonal" and self.kind_b == "diagonal":
+            return 2.0 * min(self.M, self.N) * nb
+        if self.kind_a == "diagonal" or self.kind_b == "diagonal":
+            return 2.0 * self.M * self.N * nb
+        return 2.0 * self.M * self.N * self.K * nb
 
     def a_shape(self):   # stored 2-D shape (rows, ld)
         return (self.M, self.lda) if self.op_a == "N" else (self.K, self.lda)
@@ -134,7 +148,9 @@ class Problem:
         eb, ec = ELEM_BYTES[self.ab], ELEM_BYTES[self.cd]
         nb = max(self.batch, 0)
         per = lambda stride: nb if (nb <= 1 or stride != 0) else 1
-        b = (self.M * self.K * per(self.stride_a) + self.K * self.N * per(self.stride_b)) * eb
+        na = self.M if self.kind_a == "diagonal" else self.M * self.K
+        nbb = self.N if self.kind_b == "diagonal" else self.K * self.N
+        b = (na * per(self.stride_a) + nbb * per(self.stride_b)) * eb
         b += self.M * self.N * ec * nb
         if self.beta != 0:
             b += self.M * self.N * ec * nb
@@ -168,10 +184,16 @@ def make_inputs(p: Problem, pad_fill=0):
     if p.batch != 1:
         return _make_batched_inputs(p, pad_fill)
     ga, gb, gc, gbias = (rng(*p.key, i) for i in range(4))
-    a = quantize(p.ab, draw(ga, p.a_dist, p.M * p.K)).reshape(p.M, p.K)
-    b = quantize(p.ab, draw(gb, p.b_dist, p.K * p.N)).reshape(p.K, p.N)
-    A = _store(a, p.op_a, p.lda, pad_fill)
-    B = _store(b, p.op_b, p.ldb, pad_fill)
+    if p.kind_a == "diagonal":
+        A = quantize(p.ab, draw(ga, p.a_dist, p.M))
+    else:
+        a = quantize(p.ab, draw(ga, p.a_dist, p.M * p.K)).reshape(p.M, p.K)
+        A = _store(a, p.op_a, p.lda, pad_fill)
+    if p.kind_b == "diagonal":
+        B = quantize(p.ab, draw(gb, p.b_dist, p.N))
+    else:
+        b = quantize(p.ab, draw(gb, p.b_dist, p.K * p.N)).reshape(p.K, p.N)
+        B = _store(b, p.op_b, p.ldb, pad_fill)
     C = None
     if p.beta != 0:
         c = quantize(p.cd, draw(gc, p.c_dist, p.M * p.N)).reshape(p.M, p.N)
@@ -273,6 +295,14 @@ def fp16_8192_transforms():
                     name="fp16_8192_transforms", transform_a="relu", transform_c="relu")]
 
 
+def diag_fp16():
+    """A diagonal-operand product at the headline size: D = diag(a) B + bias, ReLU, fp16
+    8192 x 8192 (K = M = 8192), a ~ U[-1,1], B ~ N(0,1), bias ~ U[-0.5,0.5].  Memory-bound:
+    read B, write D ("Flexible Performant GEMM Kernels on GPUs", section 5.2, Table 1)."""
+    return [Problem(8192, 8192, 8192, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                    b_dist=("normal", 1.0), key=(8, 0), name="diag_fp16", kind_a="diagonal")]
+
+
 WORKLOADS = {
     "sgemm_256": sgemm_256,
     "fp16_8192_bias_relu": fp16_8192_bias_relu,
@@ -281,6 +311,7 @@ WORKLOADS = {
     "fc_layers": fc_layers,
     "batched_fp16": batched_fp16,
     "fp16_8192_transforms": fp16_8192_transforms,
+    "diag_fp16": diag_fp16,
 }
 
 

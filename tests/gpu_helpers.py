@@ -53,7 +53,7 @@ def run(p, x, offset=0, d_rows_extra=0, c_is_d=False, stream=None, plan=None):
     bias = to_dev(p.bias_dt, x["bias"], offset) if x["bias"] is not None else None
     pl = plan or tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                           transform_a=p.transform_a, transform_b=p.transform_b,
-                          transform_c=p.transform_c)
+                          transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b)
     pl.run(A, B, C, D, bias, p.alpha, p.beta, stream=stream)
     torch.cuda.synchronize()
     return to_host(p.cd, D).reshape(rows, p.ldc), pl
@@ -63,12 +63,15 @@ def reference(p, x, rows=None, threads=None):
     return oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab, C=x["C"],
                        ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha, beta=p.beta, relu=p.relu,
                        rows=rows, threads=threads, transform_a=p.transform_a,
-                       transform_b=p.transform_b, transform_c=p.transform_c)
+                       transform_b=p.transform_b, transform_c=p.transform_c, kind_a=p.kind_a,
+                       kind_b=p.kind_b)
 
 
 def normaliser(p, x):
-    ma = oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda)
-    mb = oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb)
+    ma = (float(np.abs(oracle.decode(p.ab, x["A"])).max()) if p.kind_a == "diagonal"
+          else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda))
+    mb = (float(np.abs(oracle.decode(p.ab, x["B"])).max()) if p.kind_b == "diagonal"
+          else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb))
     return p.K * ma * mb
 
 
@@ -126,7 +129,8 @@ def run_batched(p, x, offset=0):
     pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                   batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
                   stride_bias=p.stride_bias, transform_a=p.transform_a,
-                  transform_b=p.transform_b, transform_c=p.transform_c)
+                  transform_b=p.transform_b, transform_c=p.transform_c, kind_a=p.kind_a,
+                  kind_b=p.kind_b)
     pl.run(A, B, C, D, bias, p.alpha, p.beta)
     torch.cuda.synchronize()
     return to_host(p.cd, D).reshape(-1), pl
@@ -138,4 +142,5 @@ def reference_batched(p, x):
                                beta=p.beta, relu=p.relu, batch=p.batch, stride_a=p.stride_a,
                                stride_b=p.stride_b, stride_c=p.stride_c,
                                stride_bias=p.stride_bias, transform_a=p.transform_a,
-                               transform_b=p.transform_b, transform_c=p.transform_c)
+                               transform_b=p.transform_b, transform_c=p.transform_c,
+                               kind_a=p.kind_a, kind_b=p.kind_b)

@@ -360,3 +360,30 @@ def test_transforms_against_numpy(lay):
             Ct = C.astype(np.int64).reshape(M, N)
             Ct = np.maximum(Ct, 0) if tc == "relu" else Ct
             assert np.array_equal(got, Xt @ Yt + Ct)
+
+
+# ---- diagonal operands ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("which", ["A", "B", "AB"])
+def test_diagonal_operands_against_numpy(which):
+    """A diagonal operand given by its vector equals the dense product with numpy's np.diag of
+    that vector (int8 values, exact), for row subsets too."""
+    g = np.random.default_rng(34)
+    for (M, N) in [(5, 7), (6, 6), (9, 3)]:
+        if which == "AB":
+            N = M
+        K = M if "A" in which else N
+        avec = g.integers(-5, 6, M).astype(np.int8)
+        bvec = g.integers(-5, 6, N).astype(np.int8)
+        X = g.integers(-5, 6, (M, K)).astype(np.int8)
+        Y = g.integers(-5, 6, (K, N)).astype(np.int8)
+        Aref = np.diag(avec.astype(np.int64)) if "A" in which else X.astype(np.int64)
+        Bref = np.diag(bvec.astype(np.int64)) if "B" in which else Y.astype(np.int64)
+        A = avec if "A" in which else X
+        B = bvec if "B" in which else Y
+        kw = dict(kind_a="diagonal" if "A" in which else "dense",
+                  kind_b="diagonal" if "B" in which else "dense")
+        got = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "i8", **kw)
+        assert np.array_equal(got, Aref @ Bref)
+        part = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "i8", rows=(1, M - 1), **kw)
+        assert np.array_equal(part, (Aref @ Bref)[1:M - 1])

@@ -5,7 +5,8 @@
 * random inputs within the normalised tolerance on every pair and layout;
 * edge cases: K = 0, single rows/columns, beta = 0 with NaN in C, in-place C == D, padded and
   odd leading dimensions, unaligned pointers, guard bands, determinism;
-* the five workloads at full size on sampled outputs, plus properties that hold everywhere.
+* the workloads at full size on sampled outputs (every product of a batch in full), plus
+  properties that hold everywhere.
 """
 import os
 
@@ -14,7 +15,8 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import check, check_points, normaliser, reference, run
+from gpu_helpers import (check, check_points, normaliser, reference, reference_batched, run,
+                         run_batched)
 
 pytestmark = pytest.mark.gpu
 
@@ -169,7 +171,7 @@ def test_nn_equals_tt_of_transposed_problem():
     np.testing.assert_allclose(DT, D.T, rtol=0, atol=1e-5)
 
 
-# ---- the five workloads at full size -----------------------------------------------------------
+# ---- the workloads at full size -----------------------------------------------------------
 
 FULL = [(name, i) for name, fn in synth.WORKLOADS.items() for i in range(len(fn()))]
 
@@ -178,12 +180,24 @@ FULL = [(name, i) for name, fn in synth.WORKLOADS.items() for i in range(len(fn(
 def test_workload_full_size_sampled(name, idx):
     p = synth.WORKLOADS[name]()[idx]
     x = synth.make_inputs(p)
+    if p.batch != 1:
+        # every product of the batch, in full
+        Df, pl = run_batched(p, x)
+        print(f"{p.label()} -> {pl.describe()}", flush=True)
+        ref = reference_batched(p, x)
+        for b in range(p.batch):
+            Db = Df[b * p.stride_c: b * p.stride_c + p.M * p.ldc].reshape(p.M, p.ldc)
+            check(p, x, Db, ref[b])
+        return
     D, pl = run(p, x)
     print(f"{p.label()} -> {pl.describe()}", flush=True)
+    plain = (p.kind_a, p.kind_b) == ("dense", "dense") and \
+        (p.transform_a, p.transform_b, p.transform_c) == ("none", "none", "none")
     if p.M * p.N * p.K <= 256 ** 3:
         check(p, x, D, reference(p, x))
     else:
-        check_points(p, x, D)
+        if plain:   # per-point references read the raw dense operands
+            check_points(p, x, D)
         # a whole row band through the oracle as well (first and last rows)
         for r0 in (0, p.M - 2):
             ref = reference(p, x, rows=(r0, r0 + 2))

@@ -32,6 +32,7 @@ OP = {"N": 0, "T": 1}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4}
 EPILOGUE = {"none": 0, "relu": 1, "bias": 2, "bias_relu": 3}
 TRANSFORM = {"none": 0, "relu": 1}
+KIND = {"dense": 0, "diagonal": 1}
 STATUS_SUCCESS, STATUS_INVALID_VALUE, STATUS_NOT_SUPPORTED, STATUS_HIP_ERROR, STATUS_ALLOC_FAILED = range(5)
 
 _i64, _vp, _ci, _f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -49,7 +50,7 @@ class GemmDesc(ctypes.Structure):
                 ("lda", _i64), ("ldb", _i64), ("ldc", _i64), ("ab_type", _ci), ("cd_type", _ci),
                 ("epilogue", _ci), ("batch", _i64), ("stride_a", _i64), ("stride_b", _i64),
                 ("stride_c", _i64), ("stride_bias", _i64), ("transform_a", _ci),
-                ("transform_b", _ci), ("transform_c", _ci)]
+                ("transform_b", _ci), ("transform_c", _ci), ("kind_a", _ci), ("kind_b", _ci)]
 
 
 _lib.gemm_plan_create_desc.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(GemmDesc)]
@@ -99,12 +100,14 @@ def gemm_plan_create_batched(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_typ
 
 def gemm_plan_create_desc(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epilogue,
                           batch=1, stride_a=0, stride_b=0, stride_c=0, stride_bias=0,
-                          transform_a="none", transform_b="none", transform_c="none"):
+                          transform_a="none", transform_b="none", transform_c="none",
+                          kind_a="dense", kind_b="dense"):
     """Returns (status, handle) of a plan built from a full gemm_desc_t."""
     d = GemmDesc(M, N, K, _enum(OP, op_a), _enum(OP, op_b), lda, ldb, ldc, _enum(DTYPE, ab_type),
                  _enum(DTYPE, cd_type), _enum(EPILOGUE, epilogue), batch, stride_a, stride_b,
                  stride_c, stride_bias, _enum(TRANSFORM, transform_a),
-                 _enum(TRANSFORM, transform_b), _enum(TRANSFORM, transform_c))
+                 _enum(TRANSFORM, transform_b), _enum(TRANSFORM, transform_c),
+                 _enum(KIND, kind_a), _enum(KIND, kind_b))
     h = _vp()
     st = _lib.gemm_plan_create_desc(ctypes.byref(h), ctypes.byref(d))
     return st, h.value
@@ -152,11 +155,13 @@ def _ptr(t, want, what):
 class Plan:
     """A plan for one problem description (see include/gemm.h for the storage rules).  With
     batch != 1 it is a strided-batched plan (gemm_plan_create_batched; strides in elements);
-    with a transform it is built from a full description (gemm_plan_create_desc)."""
+    with a transform or a diagonal operand it is built from a full description
+    (gemm_plan_create_desc)."""
 
     def __init__(self, M, N, K, op_a="N", op_b="N", lda=None, ldb=None, ldc=None, ab="f16",
                  cd="f16", epilogue="none", batch=1, stride_a=0, stride_b=0, stride_c=0,
-                 stride_bias=0, transform_a="none", transform_b="none", transform_c="none"):
+                 stride_bias=0, transform_a="none", transform_b="none", transform_c="none",
+                 kind_a="dense", kind_b="dense"):
         self.M, self.N, self.K = M, N, K
         self.op_a, self.op_b, self.ab, self.cd, self.epilogue = op_a, op_b, ab, cd, epilogue
         self.lda = lda if lda is not None else max(1, K if op_a == "N" else M)
@@ -164,10 +169,10 @@ class Plan:
         self.ldc = ldc if ldc is not None else max(1, N)
         self.batch = batch
         xf = (transform_a, transform_b, transform_c)
-        if any(_enum(TRANSFORM, t) for t in xf):
+        if any(_enum(TRANSFORM, t) for t in xf) or _enum(KIND, kind_a) or _enum(KIND, kind_b):
             st, h = gemm_plan_create_desc(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd,
                                           epilogue, batch, stride_a, stride_b, stride_c,
-                                          stride_bias, *xf)
+                                          stride_bias, *xf, kind_a=kind_a, kind_b=kind_b)
         elif batch == 1 and not (stride_a or stride_b or stride_c or stride_bias):
             st, h = gemm_plan_create(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd,
                                      epilogue)

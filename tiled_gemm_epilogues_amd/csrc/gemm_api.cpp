@@ -72,6 +72,16 @@ SkinnyLookup skinny_table(int ab, int cd) {
     return nullptr;
 }
 
+Lookup diag_table(int ab, int cd) {
+    if (ab == GEMM_F32 && cd == GEMM_F32) return tge::kernels_diag_f32_f32;
+    if (ab == GEMM_F16 && cd == GEMM_F16) return tge::kernels_diag_f16_f16;
+    if (ab == GEMM_F16 && cd == GEMM_F32) return tge::kernels_diag_f16_f32;
+    if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::kernels_diag_bf16_bf16;
+    if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::kernels_diag_bf16_f32;
+    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::kernels_diag_i8_i32;
+    return nullptr;
+}
+
 Lookup pair_table(int ab, int cd) {
     if (ab == GEMM_F32 && cd == GEMM_F32) return tge::kernels_f32_f32;
     if (ab == GEMM_F16 && cd == GEMM_F16) return tge::kernels_f16_f16;
@@ -88,14 +98,15 @@ int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int eb) {
     return ((rows - 1) * ld + cols) * eb;
 }
 
-// Tile choice: the largest tile that still gives at least one tile per compute unit (256 CUs),
-// else the smallest tile.  int8 and fp32 K-slabs are 128 bytes like the 16-bit ones.
-int choose_cfg(int64_t M, int64_t N, int ab) {
-    (void)ab;
+// Tile choice: the largest tile that still gives at least one tile per compute unit (256 CUs,
+// counting every product of a batch), else the smallest tile.  int8 and fp32 K-slabs are 128
+// bytes like the 16-bit ones.
+int choose_cfg(int64_t M, int64_t N, int64_t batch) {
     const int64_t cus = 256;
     const int sizes[tge::CFG_COUNT] = {256, 128, 64};
     for (int c = 0; c < tge::CFG_COUNT; ++c) {
-        int64_t t = ((M + sizes[c] - 1) / sizes[c]) * ((N + sizes[c] - 1) / sizes[c]);
+        int64_t t = ((M + sizes[c] - 1) / sizes[c]) * ((N + sizes[c] - 1) / sizes[c]) *
+                    (batch > 1 ? batch : 1);
         if (t >= cus) return c;
     }
     return tge::CFG_64;
@@ -136,6 +147,7 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
     d.batch = batch;
     d.stride_a = stride_a; d.stride_b = stride_b; d.stride_c = stride_c; d.stride_bias = stride_bias;
     d.transform_a = d.transform_b = d.transform_c = GEMM_TRANSFORM_NONE;
+    d.kind_a = d.kind_b = GEMM_OPERAND_DENSE;
     return gemm_plan_create_desc(out, &d);
 }
 
@@ -153,6 +165,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
             stride_bias = desc->stride_bias;
     for (gemm_transform_t t : {desc->transform_a, desc->transform_b, desc->transform_c})
         if ((int)t != GEMM_TRANSFORM_NONE && (int)t != GEMM_TRANSFORM_RELU) return GEMM_STATUS_INVALID_VALUE;
+    for (gemm_operand_t k : {desc->kind_a, desc->kind_b})
+        if ((int)k != GEMM_OPERAND_DENSE && (int)k != GEMM_OPERAND_DIAGONAL) return GEMM_STATUS_INVALID_VALUE;
+    const bool diag_a = desc->kind_a == GEMM_OPERAND_DIAGONAL;
+    const bool diag_b = desc->kind_b == GEMM_OPERAND_DIAGONAL;
+    if ((diag_a && K != M) || (diag_b && K != N)) return GEMM_STATUS_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return GEMM_STATUS_INVALID_VALUE;
     if (batch < 0 || stride_a < 0 || stride_b < 0 || stride_c < 0 || stride_bias < 0)
         return GEMM_STATUS_INVALID_VALUE;
@@ -165,7 +182,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // minimum leading dimensions (stored row length), never below 1
     int64_t min_lda = op_a == GEMM_OP_N ? K : M;
     int64_t min_ldb = op_b == GEMM_OP_N ? N : K;
-    if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
+    // a diagonal operand has no leading dimension (its vector is contiguous)
+    if ((!diag_a && lda < (min_lda > 1 ? min_lda : 1)) || (!diag_b && ldb < (min_ldb > 1 ? min_ldb : 1)) ||
         ldc < (N > 1 ? N : 1))
         return GEMM_STATUS_INVALID_VALUE;
     Lookup table = pair_table(ab_type, cd_type);
@@ -173,8 +191,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // 32-bit offsets inside the kernels: every matrix must span less than 2^31 bytes
     const int64_t lim = (int64_t)1 << 31;
     int eab = elem_bytes(ab_type), ecd = elem_bytes(cd_type);
-    int64_t sa = op_a == GEMM_OP_N ? span_bytes(M, K, lda, eab) : span_bytes(K, M, lda, eab);
-    int64_t sb = op_b == GEMM_OP_N ? span_bytes(K, N, ldb, eab) : span_bytes(N, K, ldb, eab);
+    int64_t sa = diag_a ? K * eab : op_a == GEMM_OP_N ? span_bytes(M, K, lda, eab) : span_bytes(K, M, lda, eab);
+    int64_t sb = diag_b ? K * eab : op_b == GEMM_OP_N ? span_bytes(K, N, ldb, eab) : span_bytes(N, K, ldb, eab);
     int64_t sc = span_bytes(M, N, ldc, ecd);
     if (sa >= lim || sb >= lim || sc >= lim || lda >= lim || ldb >= lim || ldc >= lim)
         return GEMM_STATUS_NOT_SUPPORTED;
@@ -187,7 +205,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
                       stride_c > big / batch / 4 || stride_bias > big / batch / 4))
         return GEMM_STATUS_NOT_SUPPORTED;
 
-    int cfg = choose_cfg(M, N, ab_type);
+    int cfg = (diag_a || diag_b) ? tge::CFG_128 : choose_cfg(M, N, batch);
     // TGE_FORCE_TILE=256|128|64 pins the workgroup tile (tests and tuning sweeps)
     if (const char *f = getenv("TGE_FORCE_TILE")) {
         int v = atoi(f);
@@ -196,6 +214,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         else if (v == 64) cfg = tge::CFG_64;
     }
     const KernelEntry *k = table(op_a, op_b, cfg);
+    if (diag_a || diag_b) k = diag_table(ab_type, cd_type)(op_a, op_b, (diag_a ? 1 : 0) | (diag_b ? 2 : 0));
     if (!k) return GEMM_STATUS_NOT_SUPPORTED;
 
     // fast path: 16-bit inputs, 256x256 tiles worth it, shape/ld preconditions of gemm_fast
@@ -207,7 +226,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (fk && strcmp(fk, "general") == 0) want_fast = false;
     const int ve = 16 / eab;   // elements per 16-byte chunk
     // every product of a batch keeps the 16-byte alignment of product 0
-    const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0;
+    const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0 && !diag_a && !diag_b;
     if (ft && want_fast && K >= 128 / eab && (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 &&
         strides16 && (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0))
         fast = ft(op_a, op_b);
@@ -249,6 +268,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     char bdesc[64] = "";
     int bl = 0;
     if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
+    if (diag_a || diag_b)
+        bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " diag %s%s", diag_a ? "A" : "", diag_b ? "B" : "");
     if (desc->transform_a || desc->transform_b || desc->transform_c)
         snprintf(bdesc + bl, sizeof(bdesc) - bl, " relu-in %s%s%s", desc->transform_a ? "A" : "",
                  desc->transform_b ? "B" : "", desc->transform_c ? "C" : "");

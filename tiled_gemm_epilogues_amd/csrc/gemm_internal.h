@@ -47,6 +47,14 @@ const KernelEntry *kernels_bf16_bf16(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_bf16_f32(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_i8_i32(int op_a, int op_b, int cfg);
 
+// General kernel with diagonal operands (dg: bit 0 = A diagonal, bit 1 = B diagonal), 128x128.
+const KernelEntry *kernels_diag_f32_f32(int op_a, int op_b, int dg);
+const KernelEntry *kernels_diag_f16_f16(int op_a, int op_b, int dg);
+const KernelEntry *kernels_diag_f16_f32(int op_a, int op_b, int dg);
+const KernelEntry *kernels_diag_bf16_bf16(int op_a, int op_b, int dg);
+const KernelEntry *kernels_diag_bf16_f32(int op_a, int op_b, int dg);
+const KernelEntry *kernels_diag_i8_i32(int op_a, int op_b, int dg);
+
 // Fast 256x256 path for 16- and 8-bit inputs (gemm_fast.hip).  Preconditions: 16-byte aligned
 // A/B pointers and leading dimensions, K >= one slab (64 elements, 128 for int8), and M (when A
 // is stored transposed) and N (when B is not) multiples of 16 / element size.
