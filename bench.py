@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s (and % of MFMA peak) fp16->fp32 GEMM 8192^3 with bias+ReLU epilogue"
 # MI355X published dense peaks (TFLOP/s, TOP/s for int8) and HBM bandwidth (GB/s)
-PEAK = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f32": 157.3}
+PEAK = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f32": 157.3,
+        "cf16": 2516.6, "df16": 2516.6}   # complex / dual: fp16 parts on the fp16 MFMA
 HBM_GBS = 8000.0
 
 
@@ -127,6 +128,8 @@ def main():
 
     def dev(dtype, raw):
         flat = np.ascontiguousarray(raw).reshape(-1)
+        if flat.dtype == np.uint16 and dtype not in ("f16", "bf16"):
+            return torch.from_numpy(flat.view(np.int16)).to("cuda:0")   # fp16 parts of pairs
         if dtype in ("f16", "bf16"):
             t = torch.from_numpy(flat.view(np.int16)).view(
                 {"f16": torch.float16, "bf16": torch.bfloat16}[dtype])
@@ -138,9 +141,10 @@ def main():
     B = dev(p.ab, x["B"])
     C = dev(p.cd, x["C"]) if x["C"] is not None else None
     bias = dev(p.bias_dt, x["bias"]) if x["bias"] is not None else None
-    D = torch.empty(max(p.batch - 1, 0) * p.stride_c + p.M * p.ldc,
+    pair = p.cd in synth.PART          # complex / dual output: interleaved parts
+    D = torch.empty((max(p.batch - 1, 0) * p.stride_c + p.M * p.ldc) * (2 if pair else 1),
                     dtype={"f16": torch.float16, "bf16": torch.bfloat16,
-                           "f32": torch.float32, "i32": torch.int32}[p.cd],
+                           "f32": torch.float32, "i32": torch.int32}[synth.PART.get(p.cd, p.cd)],
                     device="cuda:0")
     plan = Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                 batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
@@ -191,15 +195,21 @@ def main():
         # of the timed output (not timed)
         import oracle
         # product 0 of a batch (the sample is taken from it)
-        D0 = D[: p.M * p.ldc]
-        Dh = D0.view(torch.int16).cpu().numpy().view(np.uint16) if p.cd in ("f16", "bf16") \
+        part = synth.PART.get(p.cd, p.cd)
+        D0 = D[: p.M * p.ldc * (2 if pair else 1)]
+        Dh = D0.view(torch.int16).cpu().numpy().view(np.uint16) if part in ("f16", "bf16") \
             else D0.cpu().numpy()
-        Dh = Dh.reshape(p.M, p.ldc)
+        Dh = Dh.reshape((p.M, p.ldc, 2) if pair else (p.M, p.ldc))
         threads = host_threads()
         # two pilots separate the fixed cost (decoding B) from the per-row cost; the sample is
         # then sized for about --cpu-seconds of oracle work
         def oracle_rows(r):
             t0 = time.perf_counter()
+            if pair:
+                out = oracle.gemm_pair(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb,
+                                       p.ab, C=x["C"], ldc=p.ldc, cd=p.cd, alpha=p.alpha,
+                                       beta=p.beta, rows=(0, r), threads=threads)
+                return time.perf_counter() - t0, out
             out = oracle.gemm(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab,
                               C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
                               beta=p.beta, relu=p.relu, rows=(0, r), threads=threads,
@@ -221,11 +231,15 @@ def main():
                          f"(all {p.N} columns, full K={p.K}): "
                          f"{sample_flops:.3e} flop in {t_cpu:.1f}s, fp64/int64 accumulation"}
         log(f"[bench] cpu oracle: {cpu['sample']}")
-        got = oracle.decode(p.cd, Dh[:rows, : p.N]) if p.cd != "i32" else Dh[:rows, : p.N].astype(np.int64)
-        maxa = (float(np.abs(oracle.decode(p.ab, x["A"])).max()) if p.kind_a == "diagonal"
-                else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda))
-        maxb = (float(np.abs(oracle.decode(p.ab, x["B"])).max()) if p.kind_b == "diagonal"
-                else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb))
+        got = oracle.decode(part, Dh[:rows, : p.N]) if p.cd != "i32" else Dh[:rows, : p.N].astype(np.int64)
+        if pair:   # the parts of every stored number (ld padding included) bound |op(X)|
+            maxa = float(np.abs(oracle.decode(synth.PART[p.ab], x["A"])).max())
+            maxb = float(np.abs(oracle.decode(synth.PART[p.ab], x["B"])).max())
+        else:
+            maxa = (float(np.abs(oracle.decode(p.ab, x["A"])).max()) if p.kind_a == "diagonal"
+                    else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda))
+            maxb = (float(np.abs(oracle.decode(p.ab, x["B"])).max()) if p.kind_b == "diagonal"
+                    else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb))
         den = p.K * maxa * maxb
         err = float(np.max(np.abs(got - ref)) / den) if den else float(np.max(np.abs(got - ref)))
         parity = {"rows_checked": rows, "max_normalised_error": err, "tolerance": 2e-3,

@@ -25,7 +25,9 @@
  *
  * Supported type combinations (ab_type -> cd_type); bias is fp32 for float inputs and int32
  * for int8 inputs; C has the type of D; accumulation is fp32 (int32 for int8):
- *   F32 -> F32,  F16 -> F16 | F32,  BF16 -> BF16 | F32,  I8 -> I32.
+ *   F32 -> F32,  F16 -> F16 | F32,  BF16 -> BF16 | F32,  I8 -> I32,
+ *   CF16 -> CF32 | CF16,  DF16 -> DF32 | DF16  (epilogue NONE only; alpha and beta are real
+ *   and scale both parts; no transforms or diagonal operands).
  * Conversion to a 16-bit output rounds to nearest even.
  *
  * Ownership: the caller owns every device buffer and keeps it alive until the stream work that
@@ -49,12 +51,22 @@ extern "C" {
 
 typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
 
+/*
+ * Element types.  The complex and dual types are pairs stored interleaved (first part, then
+ * second part of each number, 2 x 16 or 2 x 32 bits): complex x = re + im*i with i^2 = -1, dual
+ * x = re + eps*d with eps^2 = 0 ("Flexible Performant GEMM Kernels on GPUs", section 5.4).  A
+ * leading dimension or stride of such a matrix counts numbers, not parts.
+ */
 typedef enum {
     GEMM_F32 = 0,
     GEMM_F16 = 1,
     GEMM_BF16 = 2,
     GEMM_I8 = 3,
-    GEMM_I32 = 4
+    GEMM_I32 = 4,
+    GEMM_CF16 = 5,   /* complex, fp16 parts */
+    GEMM_CF32 = 6,   /* complex, fp32 parts */
+    GEMM_DF16 = 7,   /* dual, fp16 parts */
+    GEMM_DF32 = 8    /* dual, fp32 parts */
 } gemm_dtype_t;
 
 /* bias: bias[j] added to every row; relu: max(0, .) applied last. */

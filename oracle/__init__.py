@@ -16,7 +16,8 @@ Readings where the pages are silent (all matrices row-major, op T = the stored a
 transpose, beta == 0 means C is not read, RNE to the output type) are stated in oracle.c.
 
 Raw operand formats (the exact bits a kernel receives): f32 -> numpy float32, f16 and bf16 ->
-numpy uint16 bit patterns, i8 -> int8, i32 -> int32.  Matrices are flat or 2-D C-contiguous
+numpy uint16 bit patterns, i8 -> int8, i32 -> int32; complex / dual numbers (cf16, df16, cf32,
+df32) -> interleaved pairs of their part type.  Matrices are flat or 2-D C-contiguous
 arrays with an explicit leading dimension.
 """
 import ctypes
@@ -202,6 +203,40 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
         lib().oracle_epilogue_f64(mr, N, _ptr(acc), float(alpha), _ptr(Cd), float(beta),
                                   _ptr(bd), 1 if relu else 0, _ptr(out))
     return out.reshape(mr, N)
+
+
+PART = {"cf16": "f16", "df16": "f16", "cf32": "f32", "df32": "f32"}
+
+
+def gemm_pair(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, alpha=1.0,
+              beta=0.0, rows=None, threads=None):
+    """Exact result (rows x N x 2: first and second parts) of D = alpha*op(A)op(B) + beta*C on
+    complex ("cf16") or dual ("df16") numbers stored interleaved (two parts per number, ld in
+    numbers), with real alpha and beta.  "Flexible Performant GEMM Kernels on GPUs", section 5.4:
+    the product of a tile is four real products of the parts, combined as
+      complex: re = Are*Bre - Aim*Bim,  im = Are*Bim + Aim*Bre   (i^2 = -1)
+      dual:    re = Are*Bre,            im = Are*Bim + Aim*Bre   (eps^2 = 0)
+    each real product being the plain definition above (fp64, ascending k)."""
+    part = PART[ab]
+    Ar = _raw(part, A).reshape(-1, 2)
+    Br = _raw(part, B).reshape(-1, 2)
+    prod = {}
+    for (x, y) in [(0, 0), (1, 1), (0, 1), (1, 0)]:
+        if ab.startswith("d") and (x, y) == (1, 1):
+            continue
+        prod[(x, y)] = gemm(M, N, K, op_a, op_b, np.ascontiguousarray(Ar[:, x]), lda,
+                            np.ascontiguousarray(Br[:, y]), ldb, part, rows=rows, threads=threads)
+    re = prod[(0, 0)] - prod[(1, 1)] if ab.startswith("c") else prod[(0, 0)]
+    im = prod[(0, 1)] + prod[(1, 0)]
+    out = np.stack([re, im], axis=-1) * float(alpha)
+    if beta != 0:
+        r0, r1 = (0, M) if rows is None else rows
+        Cr = _raw(PART[cd], C).reshape(-1, 2)
+        Cd = np.empty((r1 - r0, N, 2))
+        for i in range(r1 - r0):
+            Cd[i] = decode(PART[cd], Cr[(r0 + i) * ldc:(r0 + i) * ldc + N])
+        out = out + float(beta) * Cd
+    return out
 
 
 def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,

@@ -15,8 +15,12 @@ import math
 
 import numpy as np
 
-RAW_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "i32": np.int32}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4}
+RAW_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "i32": np.int32,
+          "cf16": np.uint16, "df16": np.uint16, "cf32": np.float32, "df32": np.float32}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "cf16": 4, "df16": 4, "cf32": 8,
+              "df32": 8}
+# complex / dual types: numbers of two parts of this real type, stored interleaved
+PART = {"cf16": "f16", "df16": "f16", "cf32": "f32", "df32": "f32"}
 
 
 def rng(*key):
@@ -127,9 +131,12 @@ class Problem:
 
     @property
     def flops(self):
-        """2 x the multiply-adds the product needs: M*N*K, or for a diagonal operand only the
-        non-zero terms (one per output element; with both diagonal, one per diagonal element)."""
+        """2 x the real multiply-adds the product needs: M*N*K, or for a diagonal operand only
+        the non-zero terms (one per output element; with both diagonal, one per diagonal
+        element); x4 for complex numbers (four real products), x3 for dual numbers."""
         nb = max(self.batch, 0)
+        if self.ab in ("cf16", "df16"):
+            return (4.0 if self.ab == "cf16" else 3.0) * 2.0 * self.M * self.N * self.K * nb
         if self.kind_a == "diagonal" and self.kind_b == "diagonal":
             return 2.0 * min(self.M, self.N) * nb
         if self.kind_a == "diagonal" or self.kind_b == "diagonal":
@@ -180,9 +187,13 @@ def _store(logical, op, ld, fill):
 def make_inputs(p: Problem, pad_fill=0):
     """Raw stored arrays {A, B, C, bias} (C and bias None when unused) for problem p.  For a
     batch, flat arrays holding product b at b * stride (product b drawn with key (*key, 1000+b);
-    a shared operand is product 0's; gaps hold pad_fill)."""
+    a shared operand is product 0's; gaps hold pad_fill).  Complex and dual numbers: both parts
+    drawn from the operand's distribution (first parts, then second parts), stored interleaved
+    as (rows, ld, 2) raw arrays of the part type."""
     if p.batch != 1:
         return _make_batched_inputs(p, pad_fill)
+    if p.ab in PART:
+        return _make_pair_inputs(p, pad_fill)
     ga, gb, gc, gbias = (rng(*p.key, i) for i in range(4))
     if p.kind_a == "diagonal":
         A = quantize(p.ab, draw(ga, p.a_dist, p.M))
@@ -202,9 +213,37 @@ def make_inputs(p: Problem, pad_fill=0):
     return {"A": A, "B": B, "C": C, "bias": bias}
 
 
+def _make_pair_inputs(p: Problem, pad_fill=0):
+    ga, gb, gc = (rng(*p.key, i) for i in range(3))
+    pa, pc = PART[p.ab], PART[p.cd]
+
+    def pair(g, dist, rows, cols, part):
+        re = quantize(part, draw(g, dist, rows * cols)).reshape(rows, cols)
+        im = quantize(part, draw(g, dist, rows * cols)).reshape(rows, cols)
+        return np.stack([re, im], axis=-1)
+
+    def store(logical, op, ld):
+        rows, cols = logical.shape[:2]
+        if op == "N":
+            out = np.full((rows, ld, 2), pad_fill, dtype=logical.dtype)
+            out[:, :cols] = logical
+        else:
+            out = np.full((cols, ld, 2), pad_fill, dtype=logical.dtype)
+            out[:, :rows] = logical.transpose(1, 0, 2)
+        return out
+
+    A = store(pair(ga, p.a_dist, p.M, p.K, pa), p.op_a, p.lda)
+    B = store(pair(gb, p.b_dist, p.K, p.N, pa), p.op_b, p.ldb)
+    C = store(pair(gc, p.c_dist, p.M, p.N, pc), "N", p.ldc) if p.beta != 0 else None
+    return {"A": A, "B": B, "C": C, "bias": None}
+
+
 def _make_batched_inputs(p: Problem, pad_fill=0):
     out = {"A": None, "B": None, "C": None, "bias": None}
-    strides = {"A": p.stride_a, "B": p.stride_b, "C": p.stride_c, "bias": p.stride_bias}
+    # strides count numbers: raw (part) elements per number for complex / dual types
+    fa, fc = (2 if p.ab in PART else 1), (2 if p.cd in PART else 1)
+    strides = {"A": p.stride_a * fa, "B": p.stride_b * fa, "C": p.stride_c * fc,
+               "bias": p.stride_bias}
     dtypes = {"A": p.ab, "B": p.ab, "C": p.cd, "bias": p.bias_dt}
     for b in range(max(p.batch, 0)):
         one = make_inputs(replace(p, batch=1, key=(*p.key, 1000 + b)), pad_fill)
@@ -303,6 +342,15 @@ def diag_fp16():
                     b_dist=("normal", 1.0), key=(8, 0), name="diag_fp16", kind_a="diagonal")]
 
 
+def complex_fp16():
+    """Complex and dual numbers with fp16 parts, fp32 accumulation and output, 4096^3 NN, parts
+    ~ U[-1,1] ("Flexible Performant GEMM Kernels on GPUs", section 5.4, Figure 12)."""
+    return [Problem(4096, 4096, 4096, "N", "N", "cf16", "cf32", "none", 1.0, 0.0, key=(9, 0),
+                    name="complex_fp16"),
+            Problem(4096, 4096, 4096, "N", "N", "df16", "df32", "none", 1.0, 0.0, key=(9, 1),
+                    name="complex_fp16")]
+
+
 WORKLOADS = {
     "sgemm_256": sgemm_256,
     "fp16_8192_bias_relu": fp16_8192_bias_relu,
@@ -312,6 +360,7 @@ WORKLOADS = {
     "batched_fp16": batched_fp16,
     "fp16_8192_transforms": fp16_8192_transforms,
     "diag_fp16": diag_fp16,
+    "complex_fp16": complex_fp16,
 }
 
 

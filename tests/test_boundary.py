@@ -41,7 +41,7 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw", [dict(M=-1), dict(N=-1), dict(K=-1), dict(lda=63), dict(ldb=63),
                                 dict(ldc=63), dict(op_a="T", lda=63), dict(op_b="T", ldb=63),
-                                dict(op_a=2), dict(ab_type=7), dict(cd_type=-1), dict(epilogue=4),
+                                dict(op_a=2), dict(ab_type=9), dict(cd_type=-1), dict(epilogue=4),
                                 dict(M=0, N=0, K=0, lda=0, ldb=0, ldc=0)])
 def test_invalid_values(kw):
     st, h = _create(**kw)
@@ -49,7 +49,8 @@ def test_invalid_values(kw):
 
 
 @pytest.mark.parametrize("ab,cd", [("f16", "bf16"), ("bf16", "f16"), ("i8", "f32"), ("f32", "f16"),
-                                   ("i32", "i32"), ("i8", "i8"), ("f16", "i32")])
+                                   ("i32", "i32"), ("i8", "i8"), ("f16", "i32"), ("cf16", "df32"),
+                                   ("cf32", "cf32"), ("df16", "f32"), ("f16", "cf32")])
 def test_unsupported_pairs(ab, cd):
     st, h = _create(ab_type=ab, cd_type=cd)
     assert st == tge.STATUS_NOT_SUPPORTED and h is None
@@ -189,3 +190,20 @@ def test_desc_matches_the_plain_create():
     b = tge.gemm_plan_create(300, 200, 100, "T", "N", 300, 200, 200, "bf16", "f32", "bias")
     assert a[0] == b[0] == tge.STATUS_SUCCESS
     assert tge.gemm_plan_describe(a[1])[1] == tge.gemm_plan_describe(b[1])[1]
+
+
+@pytest.mark.parametrize("ab,cd", [("cf16", "cf32"), ("cf16", "cf16"), ("df16", "df32"),
+                                   ("df16", "df16")])
+def test_complex_dual_plans(ab, cd):
+    st, h = _create(ab_type=ab, cd_type=cd, op_b="T")
+    assert st == tge.STATUS_SUCCESS
+    d = tge.gemm_plan_describe(h)[1]
+    assert ("gemm_dual" if ab.startswith("d") else "gemm_complex") in d and f"{ab}->{cd} NT" in d
+    tge.gemm_plan_destroy(h)
+    # only the plain product: no bias / ReLU epilogue, transforms or diagonal operands
+    for epi in ("relu", "bias", "bias_relu"):
+        assert _create(ab_type=ab, cd_type=cd, epilogue=epi)[0] == tge.STATUS_NOT_SUPPORTED
+    assert tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, ab, cd, "none",
+                                     transform_a="relu")[0] == tge.STATUS_NOT_SUPPORTED
+    assert tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, ab, cd, "none",
+                                     kind_a="diagonal")[0] == tge.STATUS_NOT_SUPPORTED

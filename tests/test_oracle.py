@@ -387,3 +387,55 @@ def test_diagonal_operands_against_numpy(which):
         assert np.array_equal(got, Aref @ Bref)
         part = oracle.gemm(M, N, K, "N", "N", A, K, B, N, "i8", rows=(1, M - 1), **kw)
         assert np.array_equal(part, (Aref @ Bref)[1:M - 1])
+
+
+# ---- complex and dual numbers -------------------------------------------------------------------
+
+def _pairs(g, rows, cols, lo=-4, hi=4):
+    re = g.integers(lo, hi + 1, (rows, cols)).astype(np.float64)
+    im = g.integers(lo, hi + 1, (rows, cols)).astype(np.float64)
+    return re, im
+
+
+def _store_pairs(re, im, op, pad):
+    if op == "T":
+        re, im = re.T, im.T
+    rows, cols = re.shape
+    out = np.zeros((rows, cols + pad, 2), np.uint16)
+    out[:, :cols, 0] = oracle.round_to("f16", re)
+    out[:, :cols, 1] = oracle.round_to("f16", im)
+    return out, cols + pad
+
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+def test_complex_against_numpy(lay):
+    """Complex numbers against numpy's complex128 matmul (integer parts: exact)."""
+    g = np.random.default_rng(35)
+    for (M, N, K) in [(3, 4, 5), (1, 6, 2), (7, 1, 3)]:
+        ar, ai = _pairs(g, M, K)
+        br, bi = _pairs(g, K, N)
+        cr, ci = _pairs(g, M, N)
+        A, lda = _store_pairs(ar, ai, lay[0], 2)
+        B, ldb = _store_pairs(br, bi, lay[1], 1)
+        C = np.stack([cr, ci], axis=-1).astype(np.float32)
+        got = oracle.gemm_pair(M, N, K, lay[0], lay[1], A, lda, B, ldb, "cf16", C=C, ldc=N,
+                               cd="cf32", alpha=2.0, beta=-1.0)
+        ref = 2.0 * ((ar + 1j * ai) @ (br + 1j * bi)) - (cr + 1j * ci)
+        assert np.array_equal(got[..., 0], ref.real) and np.array_equal(got[..., 1], ref.imag)
+
+
+def test_dual_numbers_carry_the_derivative():
+    """Dual numbers X + eps X': the second part of the product is d/dt (X + tX')(Y + tY') at 0 =
+    X'Y + XY' (numpy real matmuls), the first part XY."""
+    g = np.random.default_rng(36)
+    M, N, K = 5, 6, 7
+    xr, xd = _pairs(g, M, K)
+    yr, yd = _pairs(g, K, N)
+    A, lda = _store_pairs(xr, xd, "N", 0)
+    B, ldb = _store_pairs(yr, yd, "N", 0)
+    got = oracle.gemm_pair(M, N, K, "N", "N", A, lda, B, ldb, "df16")
+    assert np.array_equal(got[..., 0], xr @ yr)
+    assert np.array_equal(got[..., 1], xd @ yr + xr @ yd)
+    # and differs from the complex product exactly by the dropped -Xd*Yd term
+    c = oracle.gemm_pair(M, N, K, "N", "N", A, lda, B, ldb, "cf16")
+    assert np.array_equal(c[..., 0], got[..., 0] - xd @ yd)

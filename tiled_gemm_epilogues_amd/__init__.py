@@ -29,7 +29,8 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 OP = {"N": 0, "T": 1}
-DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4}
+DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "cf16": 5, "cf32": 6, "df16": 7,
+         "df32": 8}
 EPILOGUE = {"none": 0, "relu": 1, "bias": 2, "bias_relu": 3}
 TRANSFORM = {"none": 0, "relu": 1}
 KIND = {"dense": 0, "diagonal": 1}
@@ -135,9 +136,11 @@ def _enum(table, v):
 # ---- torch-facing wrapper ---------------------------------------------------------------------
 
 def _torch_dtype(name):
+    """torch dtype of a real element type; None for the complex and dual types, whose storage
+    (interleaved parts) is passed as is."""
     import torch
     return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
-            "i32": torch.int32}[name]
+            "i32": torch.int32}.get(name)
 
 
 def _ptr(t, want, what):
@@ -147,7 +150,7 @@ def _ptr(t, want, what):
         return t
     if not t.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
-    if want is not None and t.dtype != _torch_dtype(want):
+    if want is not None and _torch_dtype(want) is not None and t.dtype != _torch_dtype(want):
         raise TypeError(f"{what} must be {want}, got {t.dtype}")
     return t.data_ptr()
 

@@ -36,6 +36,10 @@ const char *dtype_name(int t) {
     case GEMM_BF16: return "bf16";
     case GEMM_I8: return "i8";
     case GEMM_I32: return "i32";
+    case GEMM_CF16: return "cf16";
+    case GEMM_CF32: return "cf32";
+    case GEMM_DF16: return "df16";
+    case GEMM_DF32: return "df32";
     }
     return "?";
 }
@@ -45,6 +49,10 @@ int elem_bytes(int t) {
     case GEMM_F16:
     case GEMM_BF16: return 2;
     case GEMM_I8: return 1;
+    case GEMM_CF16:
+    case GEMM_DF16: return 4;
+    case GEMM_CF32:
+    case GEMM_DF32: return 8;
     default: return 4;
     }
 }
@@ -69,6 +77,16 @@ SkinnyLookup skinny_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F32) return tge::skinny_f16_f32;
     if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::skinny_bf16_bf16;
     if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::skinny_bf16_f32;
+    return nullptr;
+}
+
+using ComplexLookup = const KernelEntry *(*)(int, int);
+
+ComplexLookup complex_table(int ab, int cd) {
+    if (ab == GEMM_CF16 && cd == GEMM_CF32) return tge::complex_cf16_cf32;
+    if (ab == GEMM_CF16 && cd == GEMM_CF16) return tge::complex_cf16_cf16;
+    if (ab == GEMM_DF16 && cd == GEMM_DF32) return tge::complex_df16_df32;
+    if (ab == GEMM_DF16 && cd == GEMM_DF16) return tge::complex_df16_df16;
     return nullptr;
 }
 
@@ -175,8 +193,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         return GEMM_STATUS_INVALID_VALUE;
     if ((op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T))
         return GEMM_STATUS_INVALID_VALUE;
-    if ((int)ab_type < GEMM_F32 || (int)ab_type > GEMM_I32 || (int)cd_type < GEMM_F32 ||
-        (int)cd_type > GEMM_I32)
+    if ((int)ab_type < GEMM_F32 || (int)ab_type > GEMM_DF32 || (int)cd_type < GEMM_F32 ||
+        (int)cd_type > GEMM_DF32)
         return GEMM_STATUS_INVALID_VALUE;
     if ((int)epi < GEMM_EPI_NONE || (int)epi > GEMM_EPI_BIAS_RELU) return GEMM_STATUS_INVALID_VALUE;
     // minimum leading dimensions (stored row length), never below 1
@@ -187,7 +205,12 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         ldc < (N > 1 ? N : 1))
         return GEMM_STATUS_INVALID_VALUE;
     Lookup table = pair_table(ab_type, cd_type);
-    if (!table) return GEMM_STATUS_NOT_SUPPORTED;
+    ComplexLookup ctable = complex_table(ab_type, cd_type);
+    if (!table && !ctable) return GEMM_STATUS_NOT_SUPPORTED;
+    // complex and dual numbers: the plain product with real alpha/beta only
+    if (ctable && (epi != GEMM_EPI_NONE || desc->transform_a || desc->transform_b || desc->transform_c ||
+                   diag_a || diag_b))
+        return GEMM_STATUS_NOT_SUPPORTED;
     // 32-bit offsets inside the kernels: every matrix must span less than 2^31 bytes
     const int64_t lim = (int64_t)1 << 31;
     int eab = elem_bytes(ab_type), ecd = elem_bytes(cd_type);
@@ -205,7 +228,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
                       stride_c > big / batch / 4 || stride_bias > big / batch / 4))
         return GEMM_STATUS_NOT_SUPPORTED;
 
-    int cfg = (diag_a || diag_b) ? tge::CFG_128 : choose_cfg(M, N, batch);
+    int cfg = (diag_a || diag_b || ctable) ? tge::CFG_128 : choose_cfg(M, N, batch);
     // TGE_FORCE_TILE=256|128|64 pins the workgroup tile (tests and tuning sweeps)
     if (const char *f = getenv("TGE_FORCE_TILE")) {
         int v = atoi(f);
@@ -213,7 +236,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         else if (v == 128) cfg = tge::CFG_128;
         else if (v == 64) cfg = tge::CFG_64;
     }
-    const KernelEntry *k = table(op_a, op_b, cfg);
+    const KernelEntry *k = ctable ? ctable(op_a, op_b) : table(op_a, op_b, cfg);
     if (diag_a || diag_b) k = diag_table(ab_type, cd_type)(op_a, op_b, (diag_a ? 1 : 0) | (diag_b ? 2 : 0));
     if (!k) return GEMM_STATUS_NOT_SUPPORTED;
 

@@ -64,6 +64,12 @@ const KernelEntry *fast_bf16_bf16(int op_a, int op_b);
 const KernelEntry *fast_bf16_f32(int op_a, int op_b);
 const KernelEntry *fast_i8_i32(int op_a, int op_b);
 
+// Complex and dual GEMM (gemm_complex.hip): fp16 parts, fp32 accumulation, 128x128 tile.
+const KernelEntry *complex_cf16_cf32(int op_a, int op_b);
+const KernelEntry *complex_cf16_cf16(int op_a, int op_b);
+const KernelEntry *complex_df16_df32(int op_a, int op_b);
+const KernelEntry *complex_df16_df16(int op_a, int op_b);
+
 // Memory-bound path for M <= 64 (gemm_skinny.hip); mt = ceil(M / 16).  Preconditions: 16-bit
 // inputs, op_a == N, K % 32 == 0, 16-byte aligned A/B pointers and leading dimensions,
 // N % 8 == 0 when B is not transposed.  One workgroup per 16 columns: grid = ceil(N / 16).
