@@ -244,7 +244,13 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const KernelEntry *fast = nullptr;
     FastLookup ft = fast_table(ab_type, cd_type);
     const char *fk = getenv("TGE_FORCE_KERNEL");  // "fast" or "general" (tests, sweeps)
-    bool want_fast = cfg == tge::CFG_256;
+    // the fast kernel does ~3x the work per CU-round of the general 128x128 kernel: take it
+    // when its rounds of 256x256 tiles cost less than 3x as many rounds of 128x128 tiles
+    const int64_t nb = batch > 1 ? batch : 1;
+    const int64_t r256 = (((M + 255) / 256) * ((N + 255) / 256) * nb + 255) / 256;
+    const int64_t r128 = (((M + 127) / 128) * ((N + 127) / 128) * nb + 255) / 256;
+    bool want_fast = cfg == tge::CFG_256 || (cfg == tge::CFG_128 && 4 * r256 <= 3 * r128);
+    if (getenv("TGE_FORCE_TILE")) want_fast = cfg == tge::CFG_256;
     if (fk && strcmp(fk, "fast") == 0) want_fast = true;
     if (fk && strcmp(fk, "general") == 0) want_fast = false;
     const int ve = 16 / eab;   // elements per 16-byte chunk
