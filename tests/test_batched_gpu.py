@@ -73,14 +73,15 @@ def test_batched_exact(case, monkeypatch):
     _check_exact(p, D, reference_batched(p, x))
 
 
-def test_batched_unaligned_stride_takes_the_general_kernel(monkeypatch):
-    # a stride that moves product 1 off 16-byte alignment: the fast kernel is not eligible
+def test_batched_unaligned_stride_takes_the_register_staged_kernel(monkeypatch):
+    # a stride that moves product 1 off 16-byte alignment: the direct loads are not eligible,
+    # the register-staged fast kernel runs
     monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
     p = synth.exact_integer_problem(256, 264, 128, "N", "N", "f16", "f16", "bias", 1.0, 0.0,
                                     key=(121, 0), batch=2, stride_a=256 * 128 + 3)
     x = synth.make_inputs(p)
     D, pl = run_batched(p, x)
-    assert "gemm_fast" not in pl.describe()
+    assert "gemm_fast_256x256_rs" in pl.describe(), pl.describe()
     _check_exact(p, D, reference_batched(p, x))
 
 

@@ -248,7 +248,8 @@ def test_fast_path_random_and_unaligned_fallback(lay, monkeypatch):
     assert "gemm_fast" in pl.describe()
     ref = reference(p, x)
     check(p, x, D, ref)
-    # a pointer offset by one element forces the general kernel at run time: same result
+    # a pointer offset by one element takes the register-staged fast kernel at run time: same
+    # result
     D2, _ = run(p, x, offset=1)
     check(p, x, D2, ref)
 
@@ -300,4 +301,77 @@ def test_fast_path_int8_exact(lay, shape, monkeypatch):
     x = synth.make_inputs(p)
     D, pl = run(p, x)
     assert "gemm_fast" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
+# ---- the register-staged fast path: layouts the direct loads cannot take ----------------------
+# (M, N, K, leading-dimension padding): odd leading dimensions, M/N off the 16-byte grid with the
+# tile crossing the edge, an M/N-contiguous extent of exactly one chunk, K tails
+RS_SHAPES = [(300, 261, 200, 1), (257, 9, 136, 3), (9, 263, 72, 0), (520, 515, 333, 5),
+             (264, 264, 64, 1), (16, 16, 128, 7)]
+VE = {"f16": 8, "bf16": 8, "i8": 16}
+
+
+def _direct_ok(p, pad):
+    e = {"f16": 2, "bf16": 2, "i8": 1}[p.ab]
+    return ((p.lda * e) % 16 == 0 and (p.ldb * e) % 16 == 0 and
+            (p.op_a == "N" or p.M % VE[p.ab] == 0) and (p.op_b == "T" or p.N % VE[p.ab] == 0))
+
+
+@pytest.mark.parametrize("shape", RS_SHAPES)
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"),
+                                   ("bf16", "f32"), ("i8", "i32")])
+def test_fast_register_staged_exact(ab, cd, lay, shape, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    M, N, K, pad = shape
+    if ab == "i8":
+        K *= 2                              # one int8 slab is 128 deep
+        if M < VE[ab] or N < VE[ab]:
+            M, N = max(M, 16), max(N, 16)
+    i = LAYOUTS.index(lay) + 4 * RS_SHAPES.index(shape)
+    p = _exact(M, N, K, lay, ab, cd, EPIS[i % 4], *SCALARS[(i // 4) % 4], key=(114, i),
+               ld_pad=pad)
+    x = synth.make_inputs(p)
+    print(p.label(), flush=True)
+    D, pl = run(p, x)
+    want = "gemm_fast_256x256 " if _direct_ok(p, pad) else "gemm_fast_256x256_rs"
+    assert want in pl.describe() + " ", pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+    # unaligned operand pointers: the register-staged kernel at run time, same result
+    D2, _ = run(p, x, offset=1)
+    check(p, x, D2, reference(p, x), exact=True)
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_fast_register_staged_random(lay, monkeypatch):
+    # random data, bf16 -> f32 with bias + ReLU, odd leading dimensions over several tiles
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    p = synth.Problem(777, 1031, 611, lay[0], lay[1], "bf16", "f32", "bias_relu", 1.0, 0.5,
+                      key=(115, LAYOUTS.index(lay)))
+    p.lda += 1; p.ldb += 3; p.ldc += 1
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_fast_256x256_rs" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x))
+
+
+def test_fast_register_staged_with_transforms(monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    p = synth.exact_integer_problem(300, 261, 200, "T", "N", "f16", "f32", "bias", 1.0, 1.0,
+                                    key=(116, 0), ld_pad=1, transform_a="relu",
+                                    transform_b="relu", transform_c="relu")
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_fast_256x256_rs" in pl.describe() and "relu-in ABC" in pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
+def test_fast_extent_below_one_chunk_takes_the_general_kernel(monkeypatch):
+    # N = 5 with B not transposed: no in-bounds 16-byte chunk exists, the general kernel runs
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    p = _exact(300, 5, 128, "NN", "f16", "f16", "bias", 1.0, 0.0, key=(117, 0))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_fast" not in pl.describe(), pl.describe()
     check(p, x, D, reference(p, x), exact=True)

@@ -22,6 +22,7 @@ struct gemm_plan {
     const KernelEntry *kernel;       // general kernel (always valid)
     const KernelEntry *fast;         // fast or skinny kernel when the plan qualifies, else nullptr
     bool fast_is_skinny;             // grid of `fast` is one workgroup per 16 columns
+    const KernelEntry *fast_rs;      // register-staged fast kernel: any alignment, else nullptr
     int tiles_m, tiles_n, group_m;
     unsigned grid;
     char desc[192];
@@ -59,7 +60,7 @@ int elem_bytes(int t) {
 
 using Lookup = const KernelEntry *(*)(int, int, int);
 
-using FastLookup = const KernelEntry *(*)(int, int);
+using FastLookup = const KernelEntry *(*)(int, int, int);
 
 FastLookup fast_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F16) return tge::fast_f16_f16;
@@ -258,7 +259,13 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0 && !diag_a && !diag_b;
     if (ft && want_fast && K >= 128 / eab && (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 &&
         strides16 && (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0))
-        fast = ft(op_a, op_b);
+        fast = ft(op_a, op_b, 0);
+    // the register-staged variant takes every layout the direct loads cannot (odd leading
+    // dimensions or strides, unaligned pointers, M/N-contiguous extents off the 16-byte grid)
+    const KernelEntry *fast_rs = nullptr;
+    if (ft && want_fast && K >= 128 / eab && !diag_a && !diag_b && (op_a == GEMM_OP_N || M >= ve) &&
+        (op_b == GEMM_OP_T || N >= ve))
+        fast_rs = ft(op_a, op_b, 1);
 
     // skinny path: M <= 64, memory bound; preferred over both tiled kernels when it applies
     bool skinny = false;
@@ -284,7 +291,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->kernel = k;
     p->fast = fast;
     p->fast_is_skinny = skinny;
-    const KernelEntry *shown = fast ? fast : k;
+    p->fast_rs = fast_rs;
+    const KernelEntry *shown = fast ? fast : fast_rs ? fast_rs : k;
     p->tiles_m = skinny ? 1 : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
@@ -349,8 +357,10 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
     prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
     const KernelEntry *k = p->kernel;
-    // the fast kernel needs 16-byte aligned operand pointers; else the general kernel runs
+    // the direct-load fast kernel needs 16-byte aligned operand pointers; else the
+    // register-staged one runs when the plan has it, else the general kernel
     if (p->fast && ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0) k = p->fast;
+    else if (p->fast_rs) k = p->fast_rs;
     const bool sk = k == p->fast && p->fast_is_skinny;
     prm.tiles_m = sk ? 1 : (int)((p->M + k->bm - 1) / k->bm);
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);

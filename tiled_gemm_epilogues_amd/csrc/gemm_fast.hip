@@ -109,7 +109,16 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
 // Each wave issues 8 instructions (1 KiB each) per operand per slab.  For lane l and instruction
 // i the byte offset from the slab's base address is fixed for the whole kernel.
 
-template <int E, bool KC>
+// RS: register-staged variant for operands the direct loads cannot take (a pointer or leading
+// dimension off 16-byte alignment, or an M/N-contiguous extent that is not a whole number of
+// chunks): the same chunk of the same slab goes global -> registers (unaligned 16-byte loads are
+// legal) -> LDS, so the LDS image is identical.  An M/N-contiguous chunk that starts inside the
+// row and crosses its end reads on into the next stored row (at most 15 bytes, inside the
+// matrix as long as a next row exists: the last row of K always goes through the guarded tail);
+// a chunk that starts past the end reads the row's last element onwards.  Those extra elements
+// only reach output rows or columns past the edge, which are never stored.  Needs an extent of
+// at least one chunk.
+template <int E, bool KC, bool RS = false>
 struct Loader {
     static constexpr int VE = 16 / E;    // elements per 16-byte chunk
     uint32_t voff[8];
@@ -128,8 +137,13 @@ struct Loader {
                 constexpr int CPR = 16 * E;                        // chunks per [k] row
                 const int k = blk * (64 / CPR) + lane / CPR;       // slab row (k)
                 const int c = (lane % CPR) ^ swz_mc<E>(k);
-                const int col = min(row0 + c * VE, ext - VE);      // ext % VE == 0: whole chunks
-                voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
+                if constexpr (RS) {
+                    const int col = min(row0 + c * VE, ext - 1);   // starts inside the row
+                    voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
+                } else {
+                    const int col = min(row0 + c * VE, ext - VE);  // ext % VE == 0: whole chunks
+                    voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
+                }
             }
         }
     }
@@ -141,41 +155,49 @@ struct Loader {
     __device__ __forceinline__ void issue(const uint8_t *sb, uint32_t dst, int wave, int i) const {
         dma16(sb, voff[i], dst + (uint32_t)(wave * 8 + i) * 1024u);
     }
+    // RS: chunk i of this lane from the slab at sb, into registers (raw; nothing may touch the
+    // registers before put, so the load has a slab's time to land)
+    __device__ __forceinline__ u32x4 fetch(const uint8_t *sb, int i) const { return ldg16(sb + voff[i]); }
+    // RS: chunk i fetched into v, with the load transform applied (xf), to its LDS place in the
+    // slab (the one a direct load would fill)
+    __device__ __forceinline__ static void put(uint8_t *slab, int wave, int i, int lane, u32x4 v, int xf) {
+        v = zero_negative<E>(v, xf);
+        *reinterpret_cast<u32x4 *>(slab + (wave * 8 + i) * 1024 + 16 * lane) = v;
+    }
 };
 
-// Guarded staging of a partial slab (k0 .. K-1, zero beyond) into the same LDS layout.
+// Guarded staging of a partial slab (k0 .. K-1, zero beyond) into the same LDS layout, with the
+// load transform xf applied (register-staged kernels; the others transform their fragments).
 template <int E, bool KC>
 __device__ __forceinline__ void stage_tail(const uint8_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
-                           int tid) {
+                                           int tid, int xf) {
     constexpr int VE = 16 / E;
-    // 2048 chunks of 16 bytes per operand slab, 8 per thread
-#pragma unroll 1
+    // 2048 chunks of 16 bytes per operand slab, 8 per thread (unrolled: the loads go out together)
+#pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int q = tid + NT * i;
-        uint8_t v[16];
+        const uint8_t *p;
+        int nval;          // leading elements of the chunk inside the operand (0 .. VE)
+        uint32_t off;      // LDS byte offset of the chunk
         if constexpr (KC) {
             const int r = q >> 3, c = q & 7;
-            const int gr = min(row0 + r, ext - 1);
-            const uint8_t *p = base + ((size_t)gr * ld + k0 + c * VE) * E;
-#pragma unroll
-            for (int e = 0; e < VE; ++e)
-#pragma unroll
-                for (int b = 0; b < E; ++b) v[e * E + b] = (k0 + c * VE + e < K) ? p[e * E + b] : (uint8_t)0;
-            __builtin_memcpy(dst + off_kc(r, c), v, 16);
+            p = base + ((size_t)min(row0 + r, ext - 1) * ld + k0 + c * VE) * E;
+            nval = K - (k0 + c * VE);
+            off = off_kc(r, c);
         } else {
             constexpr int CPR = 16 * E;
             const int k = q / CPR, c = q % CPR;
-            const int col = min(row0 + c * VE, ext - VE);
-            if (k0 + k < K) {
-                const uint8_t *p = base + ((size_t)(k0 + k) * ld + col) * E;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) v[e] = p[e];
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) v[e] = 0;
-            }
-            __builtin_memcpy(dst + off_mc<E>(k, c), v, 16);
+            const int col = row0 + c * VE;
+            p = base + ((size_t)(k0 + k) * ld + col) * E;
+            // elements past the M/N edge are zero (their products are never stored)
+            nval = k0 + k < K ? ext - col : 0;
+            off = off_mc<E>(k, c);
         }
+        u32x4 v = {0, 0, 0, 0};
+        if (nval >= VE) v = ldg16(p);
+        else if (nval > 0) v = ldg16_partial<E>(p, nval);
+        v = zero_negative<E>(v, xf);
+        __builtin_memcpy(dst + off, &v, 16);
     }
 }
 
@@ -436,8 +458,10 @@ struct Sched {
 };
 
 // XF: the launch has a load transform on op(A) or op(B), applied to every fragment after its LDS
-// read (the direct loads put raw operand bytes in LDS)
-template <class TI, class TO, bool AK, bool BK, int MF, bool XF>
+// read (the direct loads put raw operand bytes in LDS).  RS: operands go through registers
+// (global -> VGPR -> LDS, same LDS image) for layouts the direct loads cannot take; the load
+// transforms are then applied once per element on the way to LDS (XF stays off).
+template <class TI, class TO, bool AK, bool BK, int MF, bool XF, bool RS = false>
 __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     using acc_t = typename TI::acc_t;
     using accv_t = typename std::conditional<MF == 32, typename TI::accv_t, typename TI::accv16_t>::type;
@@ -472,8 +496,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
 
     FA fa;
     FB fb;
-    Loader<E, AK> la;
-    Loader<E, BK> lb;
+    Loader<E, AK, RS> la;
+    Loader<E, BK, RS> lb;
+    // RS: one slab of this wave's chunks in flight between global memory and LDS
+    u32x4 ra[RS ? 8 : 1], rb[RS ? 8 : 1];
     int m0 = 0, n0 = 0;
     auto set_tile = [&](int id) {
         int tm, tn;
@@ -484,7 +510,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         lb.init(wave, lane, n0, p.N, p.ldb);
     };
 
-    const int nfull = p.K / BKE;
+    // full slabs through the pipeline; a register-staged M/N-contiguous operand leaves the slab
+    // holding the last row of K to the guarded tail
+    const int nfull = (RS && (!AK || !BK)) ? (p.K - 1) / BKE : p.K / BKE;
     accv_t acc[NF][NF];
     u32x4 af[2][NF], bf[2][NF];
 
@@ -534,6 +562,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         if (nfull > 0) issue_slab(0, 0);
         if (nfull > 1) issue_slab(1, 1);
     };
+    // RS: chunk d (0-7 A, 8-15 B) of slab s into registers; register chunk d into stage st
+    auto rs_fetch = [&](int s, int d) {
+        if (d < 8) ra[d] = la.fetch(Loader<E, AK, RS>::slab_base(A, p.lda, s * BKE), d);
+        else rb[d - 8] = lb.fetch(Loader<E, BK, RS>::slab_base(B, p.ldb, s * BKE), d - 8);
+    };
+    auto rs_put = [&](int st, int d) {
+        if (d < 8) la.put(smem + st * KC_BYTES, wave, d, lane, ra[d], p.xform_a);
+        else lb.put(smem + OPND + st * KC_BYTES, wave, d - 8, lane, rb[d - 8], p.xform_b);
+    };
 
     // Slab s reads stage X; slab s+1 lives in Y.  The 16 loads of a slab are spread one per DS
     // MFMA slots: the first N3 go out in the last k-slice of slab s-2 (after its barrier freed
@@ -542,11 +579,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     //   dma_next:  issue loads N3..15 of slab s+1 into Y (its first loads went out in slab s-1)
     //   dma_next2: issue loads 0..N3-1 of slab s+2 into X
     //   has_next:  slab s+1 exists (wait for it, read its k-slice 0)
+    //   RS: in the first k-slices, chunk by chunk, the registers (slab s+1) go to Y and are
+    //   refilled with slab s+2 (has_next, dma_next2); the barrier then waits for LDS only
     auto slab_step = [&](int s, int X, int Y, bool dma_next, bool dma_next2, bool has_next) {
-        const uint8_t *na = Loader<E, AK>::slab_base(A, p.lda, (s + 1) * BKE);
-        const uint8_t *nb = Loader<E, BK>::slab_base(B, p.ldb, (s + 1) * BKE);
-        const uint8_t *n2a = Loader<E, AK>::slab_base(A, p.lda, (s + 2) * BKE);
-        const uint8_t *n2b = Loader<E, BK>::slab_base(B, p.ldb, (s + 2) * BKE);
+        const uint8_t *na = Loader<E, AK, RS>::slab_base(A, p.lda, (s + 1) * BKE);
+        const uint8_t *nb = Loader<E, BK, RS>::slab_base(B, p.ldb, (s + 1) * BKE);
+        const uint8_t *n2a = Loader<E, AK, RS>::slab_base(A, p.lda, (s + 2) * BKE);
+        const uint8_t *n2b = Loader<E, BK, RS>::slab_base(B, p.ldb, (s + 2) * BKE);
         auto dma = [&](const uint8_t *sa, const uint8_t *sb, int st, int d) {
             if (d < 8) la.issue(sa, dstA(st), wave, d);
             else lb.issue(sb, dstB(st), wave, d - 8);
@@ -558,8 +597,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
             for (int t = 0; t < NMS; ++t) {
                 mma(j & 1, t);
                 rd_slot(X, j + 1, (j + 1) & 1, t, NMS);
-                if (dma_next) {
-                    const int q = NMS * j + t;                   // load slot in the slab
+                const int q = NMS * j + t;                       // load slot in the slab
+                if constexpr (RS) {
+                    if (q % 2 == 0 && q / 2 < 16) {
+                        if (has_next) rs_put(Y, q / 2);
+                        if (dma_next2) rs_fetch(s + 2, q / 2);
+                    }
+                } else if (dma_next) {
                     if (q % SC::DS == 0 && SC::N3 + q / SC::DS < 16) dma(na, nb, Y, SC::N3 + q / SC::DS);
                 }
                 fence();
@@ -576,7 +620,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
             fence();
         }
         wait_lgkmcnt0();
-        if (has_next) wait_vmcnt0();
+        if (has_next && !RS) wait_vmcnt0();
         fence();
         __syncthreads();
         fence();
@@ -584,7 +628,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         for (int t = SC::BAR_AT; t < NMS; ++t) {
             mma(LB, t);
             const int u = t - SC::BAR_AT;                        // slot after the barrier
-            if (dma_next2 && u % SC::DS == 0) dma(n2a, n2b, X, u / SC::DS);
+            if (!RS && dma_next2 && u % SC::DS == 0) dma(n2a, n2b, X, u / SC::DS);
             if (has_next) rd_slot(Y, 0, 0, u, SC::REM);
             fence();
         }
@@ -601,10 +645,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
             for (int r = 0; r < (MF == 32 ? 16 : 4); ++r) acc[i][j][r] = 0;
 
     if (nfull > 0) {
-        prologue();
-        // slab 0 landed, slab 1 may still fly
-        if (nfull > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else wait_vmcnt0();
+        if constexpr (RS) {
+            // slab 0 to stage 0 through the registers; slab 1 stays in them
+#pragma unroll
+            for (int d = 0; d < 16; ++d) rs_fetch(0, d);
+#pragma unroll
+            for (int d = 0; d < 16; ++d) rs_put(0, d);
+            if (nfull > 1)
+#pragma unroll
+                for (int d = 0; d < 16; ++d) rs_fetch(1, d);
+        } else {
+            prologue();
+            // slab 0 landed, slab 1 may still fly
+            if (nfull > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            else wait_vmcnt0();
+        }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < NRD; ++q) rd(0, 0, 0, q);
@@ -635,8 +690,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     const int k0 = nfull * BKE;
     if (k0 < p.K) {
         __syncthreads();
-        stage_tail<E, AK>(A, p.lda, m0, p.M, k0, p.K, smem, tid);
-        stage_tail<E, BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid);
+        stage_tail<E, AK>(A, p.lda, m0, p.M, k0, p.K, smem, tid, RS ? p.xform_a : 0);
+        stage_tail<E, BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid, RS ? p.xform_b : 0);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NS; ++j) {   // the k-slices of the slab
@@ -672,31 +727,44 @@ hipError_t launch_fast(const GemmParams &p, unsigned grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Register-staged launch: every operand pointer, leading dimension and extent.  Always with the
+// 32x32 shape (its register budget leaves room for the staging registers); the load transforms
+// run in the staging step.
+template <class TI, class TO, bool AT, bool BT>
+hipError_t launch_fast_rs(const GemmParams &p, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, 32, false, true>), dim3(grid), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
 template <class TI, class TO>
-const KernelEntry *lookup_fast(int op_a, int op_b) {
+const KernelEntry *lookup_fast(int op_a, int op_b, int rs) {
     constexpr int BKE = SLAB_BYTES / TI::E;
-    static const KernelEntry e[4] = {
+    static const KernelEntry e[8] = {
         {launch_fast<TI, TO, false, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
         {launch_fast<TI, TO, false, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
         {launch_fast<TI, TO, true, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
         {launch_fast<TI, TO, true, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast_rs<TI, TO, false, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
+        {launch_fast_rs<TI, TO, false, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
+        {launch_fast_rs<TI, TO, true, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
+        {launch_fast_rs<TI, TO, true, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
     };
     if (op_a < 0 || op_a > 1 || op_b < 0 || op_b > 1) return nullptr;
-    return &e[op_a * 2 + op_b];
+    return &e[(rs ? 4 : 0) + op_a * 2 + op_b];
 }
 
 }  // namespace
 
 #if defined(TGE_PAIR_F16_F16)
-const KernelEntry *fast_f16_f16(int a, int b) { return lookup_fast<TF16, OF16>(a, b); }
+const KernelEntry *fast_f16_f16(int a, int b, int rs) { return lookup_fast<TF16, OF16>(a, b, rs); }
 #elif defined(TGE_PAIR_F16_F32)
-const KernelEntry *fast_f16_f32(int a, int b) { return lookup_fast<TF16, OF32>(a, b); }
+const KernelEntry *fast_f16_f32(int a, int b, int rs) { return lookup_fast<TF16, OF32>(a, b, rs); }
 #elif defined(TGE_PAIR_BF16_BF16)
-const KernelEntry *fast_bf16_bf16(int a, int b) { return lookup_fast<TBF16, OBF16>(a, b); }
+const KernelEntry *fast_bf16_bf16(int a, int b, int rs) { return lookup_fast<TBF16, OBF16>(a, b, rs); }
 #elif defined(TGE_PAIR_BF16_F32)
-const KernelEntry *fast_bf16_f32(int a, int b) { return lookup_fast<TBF16, OF32>(a, b); }
+const KernelEntry *fast_bf16_f32(int a, int b, int rs) { return lookup_fast<TBF16, OF32>(a, b, rs); }
 #elif defined(TGE_PAIR_I8_I32)
-const KernelEntry *fast_i8_i32(int a, int b) { return lookup_fast<TI8, OI32>(a, b); }
+const KernelEntry *fast_i8_i32(int a, int b, int rs) { return lookup_fast<TI8, OI32>(a, b, rs); }
 #else
 #error "define one TGE_PAIR_* macro with a 16- or 8-bit input type"
 #endif

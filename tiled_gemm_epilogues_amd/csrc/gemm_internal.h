@@ -55,14 +55,15 @@ const KernelEntry *kernels_diag_bf16_bf16(int op_a, int op_b, int dg);
 const KernelEntry *kernels_diag_bf16_f32(int op_a, int op_b, int dg);
 const KernelEntry *kernels_diag_i8_i32(int op_a, int op_b, int dg);
 
-// Fast 256x256 path for 16- and 8-bit inputs (gemm_fast.hip).  Preconditions: 16-byte aligned
-// A/B pointers and leading dimensions, K >= one slab (64 elements, 128 for int8), and M (when A
-// is stored transposed) and N (when B is not) multiples of 16 / element size.
-const KernelEntry *fast_f16_f16(int op_a, int op_b);
-const KernelEntry *fast_f16_f32(int op_a, int op_b);
-const KernelEntry *fast_bf16_bf16(int op_a, int op_b);
-const KernelEntry *fast_bf16_f32(int op_a, int op_b);
-const KernelEntry *fast_i8_i32(int op_a, int op_b);
+// Fast 256x256 path for 16- and 8-bit inputs (gemm_fast.hip); K >= one slab (64 elements, 128
+// for int8).  rs = 0: direct-to-LDS loads; needs 16-byte aligned A/B pointers, leading dimensions
+// and batch strides, and M (when A is stored transposed) and N (when B is not) multiples of
+// 16 / element size.  rs = 1: register-staged loads, no alignment or extent preconditions.
+const KernelEntry *fast_f16_f16(int op_a, int op_b, int rs);
+const KernelEntry *fast_f16_f32(int op_a, int op_b, int rs);
+const KernelEntry *fast_bf16_bf16(int op_a, int op_b, int rs);
+const KernelEntry *fast_bf16_f32(int op_a, int op_b, int rs);
+const KernelEntry *fast_i8_i32(int op_a, int op_b, int rs);
 
 // Complex and dual GEMM (gemm_complex.hip): fp16 parts, fp32 accumulation, 128x128 tile.
 const KernelEntry *complex_cf16_cf32(int op_a, int op_b);
