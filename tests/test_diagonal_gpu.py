@@ -1,7 +1,8 @@
 """GPU parity of diagonal operands (gemm_operand_t GEMM_OPERAND_DIAGONAL: the operand is the
-vector of a square diagonal matrix; only K steps that meet the diagonal run) against the oracle,
-bit-exact on exact-integer inputs: diagonal A, B or both, every type pair, ragged edges, the
-dense operand in both layouts, with C, bias, transforms and a batch."""
+vector of a square diagonal matrix; each output element takes its one product) against the
+oracle, bit-exact on exact-integer inputs: diagonal A, B or both, every type pair, ragged edges,
+the dense operand in both layouts (row and transposed streaming kernels), with C, bias,
+transforms and a batch."""
 import numpy as np
 import pytest
 import torch
@@ -79,3 +80,35 @@ def test_diagonal_full_size_random():
     D, pl = run(p, x)
     for r0, r1 in [(0, 96), (4000, 4064), (8128, 8192)]:
         check(p, x, D, reference(p, x, rows=(r0, r1)), rows=slice(r0, r1))
+
+
+# odd leading dimensions and operand pointers one element off alignment, tiny and one-tile
+# shapes, through both streaming kernels
+EDGE = [("A", 333, 517, "N", 3), ("A", 333, 517, "T", 1), ("B", 517, 333, "N", 5),
+        ("B", 517, 333, "T", 7), ("AB", 65, 65, "N", 1), ("A", 1, 1, "N", 0), ("B", 1, 9, "T", 0),
+        ("A", 64, 64, "T", 0)]
+
+
+@pytest.mark.parametrize("ab,cd", [("f16", "f32"), ("bf16", "bf16"), ("i8", "i32"), ("f32", "f32")])
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_diagonal_odd_layouts_and_unaligned(case, ab, cd):
+    which, M, N, op, pad = EDGE[case]
+    p = _problem(which, M, N, op, ab, cd, (143, case))
+    p.lda += pad; p.ldb += pad; p.ldc += pad
+    x = synth.make_inputs(p)
+    ref = reference(p, x)
+    for off in (0, 1):
+        D, pl = run(p, x, offset=off)
+        assert ("gemm_diag_cols" in pl.describe()) == (op == "T" and which != "AB"), pl.describe()
+        check(p, x, D, ref, exact=True)
+
+
+def test_diagonal_batched_transposed_dense():
+    p = _problem("A", 200, 136, "T", "f16", "f16", (144, 0), batch=2)
+    x = synth.make_inputs(p)
+    D, pl = run_batched(p, x)
+    assert "gemm_diag_cols" in pl.describe() and "batch 2" in pl.describe()
+    ref = reference_batched(p, x)
+    for b in range(p.batch):
+        Db = D[b * p.stride_c: b * p.stride_c + p.M * p.ldc].reshape(p.M, p.ldc)[:, : p.N]
+        assert np.array_equal(oracle.decode("f16", Db), oracle.decode("f16", oracle.round_to("f16", ref[b])))

@@ -51,8 +51,9 @@ def build(verbose=False, jobs=None):
         obj = os.path.join(BUILD, f"gemm_skinny_{pair.lower()}.o")
         steps.append([HIPCC, *FLAGS, f"-DTGE_PAIR_{pair}", "-c",
                       os.path.join(CSRC, "gemm_skinny.hip"), "-o", obj])
-    steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "gemm_complex.hip"), "-o",
-                  os.path.join(BUILD, "gemm_complex.o")])
+    for name in ("gemm_complex", "gemm_diag"):
+        steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, name + ".hip"), "-o",
+                      os.path.join(BUILD, name + ".o")])
     api_obj = os.path.join(BUILD, "gemm_api.o")
     steps.append([HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "gemm_api.cpp"), "-o", api_obj])
     with cf.ThreadPoolExecutor(jobs) as ex:

@@ -92,12 +92,12 @@ ComplexLookup complex_table(int ab, int cd) {
 }
 
 Lookup diag_table(int ab, int cd) {
-    if (ab == GEMM_F32 && cd == GEMM_F32) return tge::kernels_diag_f32_f32;
-    if (ab == GEMM_F16 && cd == GEMM_F16) return tge::kernels_diag_f16_f16;
-    if (ab == GEMM_F16 && cd == GEMM_F32) return tge::kernels_diag_f16_f32;
-    if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::kernels_diag_bf16_bf16;
-    if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::kernels_diag_bf16_f32;
-    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::kernels_diag_i8_i32;
+    if (ab == GEMM_F32 && cd == GEMM_F32) return tge::diag_f32_f32;
+    if (ab == GEMM_F16 && cd == GEMM_F16) return tge::diag_f16_f16;
+    if (ab == GEMM_F16 && cd == GEMM_F32) return tge::diag_f16_f32;
+    if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::diag_bf16_bf16;
+    if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::diag_bf16_f32;
+    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::diag_i8_i32;
     return nullptr;
 }
 

@@ -47,13 +47,14 @@ const KernelEntry *kernels_bf16_bf16(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_bf16_f32(int op_a, int op_b, int cfg);
 const KernelEntry *kernels_i8_i32(int op_a, int op_b, int cfg);
 
-// General kernel with diagonal operands (dg: bit 0 = A diagonal, bit 1 = B diagonal), 128x128.
-const KernelEntry *kernels_diag_f32_f32(int op_a, int op_b, int dg);
-const KernelEntry *kernels_diag_f16_f16(int op_a, int op_b, int dg);
-const KernelEntry *kernels_diag_f16_f32(int op_a, int op_b, int dg);
-const KernelEntry *kernels_diag_bf16_bf16(int op_a, int op_b, int dg);
-const KernelEntry *kernels_diag_bf16_f32(int op_a, int op_b, int dg);
-const KernelEntry *kernels_diag_i8_i32(int op_a, int op_b, int dg);
+// Products with a diagonal operand (gemm_diag.hip), streamed: dg bit 0 = A diagonal, bit 1 =
+// B diagonal; the op of the dense operand picks the kernel.  No alignment preconditions.
+const KernelEntry *diag_f32_f32(int op_a, int op_b, int dg);
+const KernelEntry *diag_f16_f16(int op_a, int op_b, int dg);
+const KernelEntry *diag_f16_f32(int op_a, int op_b, int dg);
+const KernelEntry *diag_bf16_bf16(int op_a, int op_b, int dg);
+const KernelEntry *diag_bf16_f32(int op_a, int op_b, int dg);
+const KernelEntry *diag_i8_i32(int op_a, int op_b, int dg);
 
 // Fast 256x256 path for 16- and 8-bit inputs (gemm_fast.hip); K >= one slab (64 elements, 128
 // for int8).  rs = 0: direct-to-LDS loads; needs 16-byte aligned A/B pointers, leading dimensions

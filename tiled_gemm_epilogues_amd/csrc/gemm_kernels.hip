@@ -139,47 +139,9 @@ struct Stager<E, BMN, NT, false> {
     }
 };
 
-// Diagonal operand ("Flexible Performant GEMM Kernels on GPUs", section 5.2: a layout that
-// returns 0 off the diagonal without a memory access and loads the diagonal from the vector of
-// its elements).  Element (row, k) of the operand is vec[row] when row == k, else 0; the chunk
-// written to LDS has the K-contiguous form of Stager<..., true>, whatever the stored layout
-// (a diagonal matrix is its own transpose).
-template <int E, int BMN, int NT>
-struct StagerDiag {
-    static constexpr int VE = 16 / E;
-    static constexpr int CH = BMN * 8 / NT;
-    u32x4 r[CH];
-
-    // n_diag: length of the diagonal (the operand's row count, equal to K)
-    __device__ __forceinline__ void load(const uint8_t *vec, int row0, int n_diag, int k0,
-                                         int tid) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            int q = tid + NT * i, row = q >> 3, c = q & 7;
-            const int g = row0 + row;                      // global row index = its diagonal k
-            const int d = g - (k0 + c * VE);               // position of k == g in this chunk
-            uint8_t v[16] = {0};
-            if (d >= 0 && d < VE && g < n_diag) {
-#pragma unroll
-                for (int b = 0; b < E; ++b) v[d * E + b] = vec[(int64_t)g * E + b];
-            }
-            __builtin_memcpy(&r[i], v, 16);
-        }
-    }
-    __device__ __forceinline__ void store(uint8_t *lds, int tid, int xf) const {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            int q = tid + NT * i, row = q >> 3, c = q & 7;
-            *reinterpret_cast<u32x4 *>(lds + lds_off(row, c)) = zero_negative<E>(r[i], xf);
-        }
-    }
-};
-
 // ---- the kernel ------------------------------------------------------------------------------
 
-// DG: bit 0 = A is diagonal, bit 1 = B is diagonal.  Only the K slabs that can hold a diagonal
-// element of this tile run (the pages' skip predicate for off-diagonal iterations).
-template <int BM, int BN, int WGM, int WGN, class TI, class TO, bool AT, bool BT, int DG>
+template <int BM, int BN, int WGM, int WGN, class TI, class TO, bool AT, bool BT>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
     constexpr int NT = WGM * WGN * 64;
     constexpr int E = TI::E;
@@ -207,14 +169,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
     const uint8_t *A = static_cast<const uint8_t *>(p.A);
     const uint8_t *B = static_cast<const uint8_t *>(p.B);
 
-    typename std::conditional<(DG & 1) != 0, StagerDiag<E, BM, NT>, Stager<E, BM, NT, !AT>>::type sa;
-    typename std::conditional<(DG & 2) != 0, StagerDiag<E, BN, NT>, Stager<E, BN, NT, BT>>::type sb;
+    Stager<E, BM, NT, !AT> sa;
+    Stager<E, BN, NT, BT> sb;
     // load slab at K offset k0 into the stagers
     auto load = [&](int k0, bool interior) {
-        if constexpr ((DG & 1) != 0) sa.load(A, m0, p.K, k0, tid);
-        else sa.load(A, p.lda, m0, m_valid, k0, p.K, interior, tid);
-        if constexpr ((DG & 2) != 0) sb.load(B, n0, p.K, k0, tid);
-        else sb.load(B, p.ldb, n0, n_valid, k0, p.K, interior, tid);
+        sa.load(A, p.lda, m0, m_valid, k0, p.K, interior, tid);
+        sb.load(B, p.ldb, n0, n_valid, k0, p.K, interior, tid);
     };
 
     accv_t acc[TM][TN];
@@ -225,15 +185,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // K slabs [kt0, kt0 + nk): all of K, or those that meet the diagonal rows of this tile
-    int klo = 0, khi = p.K;
-    if constexpr ((DG & 1) != 0) { klo = max(klo, m0); khi = min(khi, m0 + BM); }
-    if constexpr ((DG & 2) != 0) { klo = max(klo, n0); khi = min(khi, n0 + BN); }
-    const int kt0 = klo / BK;
-    const int nk = khi > klo ? (khi + BK - 1) / BK - kt0 : 0;
+    const int nk = (p.K + BK - 1) / BK;   // K slabs
     if (nk > 0) {
-        const int k0 = kt0 * BK;
-        load(k0, mn_interior && k0 + BK <= p.K);
+        load(0, mn_interior && BK <= p.K);
         sa.store(smem, tid, p.xform_a);
         sb.store(smem + BM * 128, tid, p.xform_b);
     }
@@ -248,7 +202,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nk;
         if (more) {
-            const int k0 = (kt0 + kt + 1) * BK;
+            const int k0 = (kt + 1) * BK;
             load(k0, mn_interior && k0 + BK <= p.K);
         }
         const uint8_t *la = smem + cur * STAGE;
@@ -279,9 +233,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_mfma(GemmParams p) {
     store_tile<TO, acc_t>(p, m0 + wm * WTM, n0 + wn * WTN, lane, acc);
 }
 
-template <int BM, int BN, int WGM, int WGN, class TI, class TO, bool AT, bool BT, int DG = 0>
+template <int BM, int BN, int WGM, int WGN, class TI, class TO, bool AT, bool BT>
 hipError_t launch(const GemmParams &p, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_mfma<BM, BN, WGM, WGN, TI, TO, AT, BT, DG>), dim3(grid),
+    hipLaunchKernelGGL((gemm_mfma<BM, BN, WGM, WGN, TI, TO, AT, BT>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, s, p);
     return hipGetLastError();
 }
@@ -302,25 +256,6 @@ struct Table {
     }
 };
 
-// Diagonal operands run on the 128x128 tile only (the problem is memory-bound: the skip
-// predicate leaves one tile-deep band of K per tile).  The stored layout of a diagonal operand
-// does not matter; that of a dense one does.
-template <class TI, class TO>
-const KernelEntry *lookup_diag(int op_a, int op_b, int dg) {
-    constexpr int BKE = 128 / TI::E;
-    static const KernelEntry e[5] = {
-        {launch<128, 128, 2, 2, TI, TO, false, false, 1>, 128, 128, BKE, 2, 2, "gemm_mfma_128x128_diag"},
-        {launch<128, 128, 2, 2, TI, TO, false, true, 1>, 128, 128, BKE, 2, 2, "gemm_mfma_128x128_diag"},
-        {launch<128, 128, 2, 2, TI, TO, false, false, 2>, 128, 128, BKE, 2, 2, "gemm_mfma_128x128_diag"},
-        {launch<128, 128, 2, 2, TI, TO, true, false, 2>, 128, 128, BKE, 2, 2, "gemm_mfma_128x128_diag"},
-        {launch<128, 128, 2, 2, TI, TO, false, false, 3>, 128, 128, BKE, 2, 2, "gemm_mfma_128x128_diag"},
-    };
-    if (dg == 1) return &e[op_b ? 1 : 0];
-    if (dg == 2) return &e[op_a ? 3 : 2];
-    if (dg == 3) return &e[4];
-    return nullptr;
-}
-
 template <class TI, class TO>
 const KernelEntry *lookup(int op_a, int op_b, int cfg) {
     if (op_a == 0 && op_b == 0) return Table<TI, TO, false, false>::get(cfg);
@@ -334,22 +269,16 @@ const KernelEntry *lookup(int op_a, int op_b, int cfg) {
 
 #if defined(TGE_PAIR_F32_F32)
 const KernelEntry *kernels_f32_f32(int a, int b, int c) { return lookup<TF32, OF32>(a, b, c); }
-const KernelEntry *kernels_diag_f32_f32(int a, int b, int dg) { return lookup_diag<TF32, OF32>(a, b, dg); }
 #elif defined(TGE_PAIR_F16_F16)
 const KernelEntry *kernels_f16_f16(int a, int b, int c) { return lookup<TF16, OF16>(a, b, c); }
-const KernelEntry *kernels_diag_f16_f16(int a, int b, int dg) { return lookup_diag<TF16, OF16>(a, b, dg); }
 #elif defined(TGE_PAIR_F16_F32)
 const KernelEntry *kernels_f16_f32(int a, int b, int c) { return lookup<TF16, OF32>(a, b, c); }
-const KernelEntry *kernels_diag_f16_f32(int a, int b, int dg) { return lookup_diag<TF16, OF32>(a, b, dg); }
 #elif defined(TGE_PAIR_BF16_BF16)
 const KernelEntry *kernels_bf16_bf16(int a, int b, int c) { return lookup<TBF16, OBF16>(a, b, c); }
-const KernelEntry *kernels_diag_bf16_bf16(int a, int b, int dg) { return lookup_diag<TBF16, OBF16>(a, b, dg); }
 #elif defined(TGE_PAIR_BF16_F32)
 const KernelEntry *kernels_bf16_f32(int a, int b, int c) { return lookup<TBF16, OF32>(a, b, c); }
-const KernelEntry *kernels_diag_bf16_f32(int a, int b, int dg) { return lookup_diag<TBF16, OF32>(a, b, dg); }
 #elif defined(TGE_PAIR_I8_I32)
 const KernelEntry *kernels_i8_i32(int a, int b, int c) { return lookup<TI8, OI32>(a, b, c); }
-const KernelEntry *kernels_diag_i8_i32(int a, int b, int dg) { return lookup_diag<TI8, OI32>(a, b, dg); }
 #else
 #error "define one TGE_PAIR_* macro"
 #endif
