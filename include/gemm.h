@@ -31,9 +31,13 @@
  * Conversion to a 16-bit output rounds to nearest even.
  *
  * Ownership: the caller owns every device buffer and keeps it alive until the stream work that
- * uses it has finished.  A plan is a small immutable host object: it holds no device memory and
- * no workspace, may be shared between host threads and streams, and must be destroyed with
- * gemm_plan_destroy.
+ * uses it has finished.  A plan is a small host object, destroyed with gemm_plan_destroy.  Most
+ * plans hold no device memory and may be shared between host threads and streams.  A plan for
+ * a short product (M <= 64) that splits K over workgroups ("ksplit S" in its description) owns
+ * a split-K workspace (S * M * N floats per product of the batch) on the device of its first
+ * gemm_run, allocated by that call and freed by gemm_plan_destroy: its runs must not overlap in
+ * time (use one plan per concurrent stream), and its first run must not be captured into a
+ * graph (later runs may be).  Such a run enqueues two kernels.
  *
  * Errors: every function returns a status; nothing throws across this boundary.  gemm_run is
  * asynchronous: it validates, enqueues one kernel on `stream` and returns; faults during
@@ -189,13 +193,15 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
  * For a batched plan every pointer is that of product 0 (see gemm_plan_create_batched).
  *   alpha, beta  scalars applied in fp32 (int8 plans require alpha == 1 and beta in {0, 1}).
  * Returns INVALID_VALUE for a NULL plan or a missing required pointer, NOT_SUPPORTED for int8
- * scalars outside the rule above, HIP_ERROR when the launch fails.  M == 0, N == 0 or a batch
- * of 0 returns SUCCESS without launching.
+ * scalars outside the rule above or for the first run of a split-K plan during stream capture,
+ * ALLOC_FAILED when that first run cannot allocate its workspace, HIP_ERROR when the launch
+ * fails.  M == 0, N == 0 or a batch of 0 returns SUCCESS without launching.
  */
 gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream);
 
-/* Frees a plan.  NULL is a no-op.  Always returns SUCCESS. */
+/* Frees a plan and its workspace, if any (waiting for the device work that may use it).  NULL is
+ * a no-op.  Always returns SUCCESS. */
 gemm_status_t gemm_plan_destroy(gemm_plan_t plan);
 
 /* Static, human-readable name of a status code (never NULL). */

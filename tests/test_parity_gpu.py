@@ -256,8 +256,11 @@ def test_fast_path_random_and_unaligned_fallback(lay, monkeypatch):
 
 # ---- the memory-bound path for M <= 64 (16-bit inputs, A not transposed) ----------------------
 
+# (K split over workgroups, with the split-K workspace, for (33, 200, 1024), (16, 4096, 4096),
+# (16, 1000, 2048), (7, 4104, 8192) and (64, 8192, 1024))
 SKINNY_SHAPES = [(1, 16, 32), (5, 40, 64), (16, 520, 320), (17, 64, 96), (33, 200, 1024),
-                 (48, 24, 160), (64, 4096, 128), (16, 4096, 4096)]
+                 (48, 24, 160), (64, 4096, 128), (16, 4096, 4096), (16, 1000, 2048),
+                 (7, 4104, 8192), (64, 8192, 1024)]
 
 
 @pytest.mark.parametrize("shape", SKINNY_SHAPES)
@@ -272,6 +275,52 @@ def test_skinny_path_exact(ab, cd, lb, shape, monkeypatch):
     D, pl = run(p, x)
     assert "gemm_skinny" in pl.describe(), pl.describe()
     check(p, x, D, reference(p, x), exact=True)
+
+
+def test_skinny_split_k_repeatable_and_graph_safe(monkeypatch):
+    # the split-K counters reset themselves: repeated runs, a second plan of the same shape,
+    # and graph replays after a first eager run give the same bits
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    p = _exact(16, 1000, 2048, "NN", "f16", "f32", "bias_relu", 2.0, -1.0, key=(118, 0))
+    x = synth.make_inputs(p)
+    D0, pl = run(p, x)
+    assert "gemm_skinny" in pl.describe() and "ksplit" in pl.describe(), pl.describe()
+    check(p, x, D0, reference(p, x), exact=True)
+    for _ in range(3):
+        D1, _ = run(p, x, plan=pl)
+        assert np.array_equal(D0, D1)
+    # graph capture of later runs (the first run allocated the workspace outside the capture)
+    from gpu_helpers import to_dev, to_host
+    A, B = to_dev(p.ab, x["A"]), to_dev(p.ab, x["B"])
+    C, bias = to_dev(p.cd, x["C"]), to_dev(p.bias_dt, x["bias"])
+    D = torch.zeros(p.M * p.ldc, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        pl.run(A, B, C, D, bias, p.alpha, p.beta)   # eager, on the capture stream
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(2):
+                pl.run(A, B, C, D, bias, p.alpha, p.beta)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        D.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(p.cd, D).reshape(p.M, p.ldc), D0)
+
+
+def test_skinny_split_k_batched(monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    p = synth.exact_integer_problem(16, 520, 2048, "N", "T", "bf16", "bf16", "bias", 1.0, 1.0,
+                                    key=(119, 0), batch=3, stride_bias=520)
+    x = synth.make_inputs(p)
+    D, pl = run_batched(p, x)
+    assert "gemm_skinny" in pl.describe() and "ksplit" in pl.describe(), pl.describe()
+    ref = reference_batched(p, x)
+    import oracle
+    for b in range(p.batch):
+        Db = D[b * p.stride_c: b * p.stride_c + p.M * p.ldc].reshape(p.M, p.ldc)[:, : p.N]
+        assert np.array_equal(oracle.decode(p.cd, Db), oracle.decode(p.cd, oracle.round_to(p.cd, ref[b])))
 
 
 def test_skinny_ineligible_shapes_fall_back(monkeypatch):

@@ -21,7 +21,10 @@ struct gemm_plan {
     int op_a, op_b, ab, cd, epi;
     const KernelEntry *kernel;       // general kernel (always valid)
     const KernelEntry *fast;         // fast or skinny kernel when the plan qualifies, else nullptr
-    bool fast_is_skinny;             // grid of `fast` is one workgroup per 16 columns
+    bool fast_is_skinny;             // `fast` is the skinny kernel (grid: k splits x 64-column blocks)
+    int ksplit;                      // skinny kernel: k splits S over workgroups
+    int ws_dev;                      // device of the skinny split-K workspace (-1: none yet)
+    float *ws;                       // skinny split-K partial sums: batch * S * M * N floats
     const KernelEntry *fast_rs;      // register-staged fast kernel: any alignment, else nullptr
     int tiles_m, tiles_n, group_m;
     unsigned grid;
@@ -132,6 +135,28 @@ int choose_cfg(int64_t M, int64_t N, int64_t batch) {
 }
 
 }  // namespace
+
+// The split-K workspace of a skinny plan on the current device, allocated by the first run there
+// (not while the stream is being captured into a graph).  Every run overwrites what it reads.
+static gemm_status_t skinny_workspace(gemm_plan *p, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+    if (p->ws && p->ws_dev == dev) return GEMM_STATUS_SUCCESS;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+    if (cs != hipStreamCaptureStatusNone) return GEMM_STATUS_NOT_SUPPORTED;
+    if (p->ws) (void)hipFree(p->ws);
+    p->ws = nullptr;
+    p->ws_dev = -1;
+    const int64_t nb = p->batch > 1 ? p->batch : 1;
+    const size_t wsb = (size_t)nb * p->ksplit * p->M * p->N * sizeof(float);
+    if (hipMalloc(&p->ws, wsb) != hipSuccess) {
+        p->ws = nullptr;
+        return GEMM_STATUS_ALLOC_FAILED;
+    }
+    p->ws_dev = dev;
+    return GEMM_STATUS_SUCCESS;
+}
 
 extern "C" {
 
@@ -292,8 +317,21 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->fast = fast;
     p->fast_is_skinny = skinny;
     p->fast_rs = fast_rs;
+    p->ksplit = 1;
+    p->ws_dev = -1;
+    p->ws = nullptr;
+    if (skinny) {
+        // split K over workgroups until there is about one workgroup per CU, keeping at least
+        // eight 32-deep chunks per wave
+        const int64_t blocks = ((N + 63) / 64) * (batch > 1 ? batch : 1);
+        int64_t sp = (256 + blocks - 1) / blocks;
+        const int64_t most = K / 32 / 32;
+        if (sp > most) sp = most;
+        if (sp > 64) sp = 64;
+        p->ksplit = sp > 1 ? (int)sp : 1;
+    }
     const KernelEntry *shown = fast ? fast : fast_rs ? fast_rs : k;
-    p->tiles_m = skinny ? 1 : (int)((M + shown->bm - 1) / shown->bm);
+    p->tiles_m = skinny ? p->ksplit : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
     const int64_t grid = (int64_t)p->tiles_m * p->tiles_n * batch;
@@ -305,6 +343,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     char bdesc[64] = "";
     int bl = 0;
     if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
+    if (p->ksplit > 1) bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " ksplit %d", p->ksplit);
     if (diag_a || diag_b)
         bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " diag %s%s", diag_a ? "A" : "", diag_b ? "B" : "");
     if (desc->transform_a || desc->transform_b || desc->transform_c)
@@ -319,6 +358,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
 }
 
 gemm_status_t gemm_plan_destroy(gemm_plan_t p) {
+    if (p && p->ws) (void)hipFree(p->ws);
     delete p;
     return GEMM_STATUS_SUCCESS;
 }
@@ -362,8 +402,14 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     if (p->fast && ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0) k = p->fast;
     else if (p->fast_rs) k = p->fast_rs;
     const bool sk = k == p->fast && p->fast_is_skinny;
-    prm.tiles_m = sk ? 1 : (int)((p->M + k->bm - 1) / k->bm);
+    prm.tiles_m = sk ? p->ksplit : (int)((p->M + k->bm - 1) / k->bm);
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
+    prm.ws = nullptr;
+    if (sk && p->ksplit > 1) {
+        const gemm_status_t st = skinny_workspace(p, static_cast<hipStream_t>(stream));
+        if (st != GEMM_STATUS_SUCCESS) return st;
+        prm.ws = p->ws;
+    }
     const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * p->batch);
     hipError_t e = k->launch(prm, grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;

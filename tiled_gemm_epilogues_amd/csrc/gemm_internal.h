@@ -23,6 +23,8 @@ struct GemmParams {
     int64_t stride_a, stride_b, stride_c, stride_bias;
     // load transforms (1: zero every element whose sign bit is set) on op(A), op(B) and C
     int xform_a, xform_b, xform_c;
+    // split-K workspace of the skinny kernel (partial sums of every k split); unused elsewhere
+    float *ws;
 };
 
 using LaunchFn = hipError_t (*)(const GemmParams &, unsigned grid, hipStream_t);
@@ -74,7 +76,10 @@ const KernelEntry *complex_df16_df16(int op_a, int op_b);
 
 // Memory-bound path for M <= 64 (gemm_skinny.hip); mt = ceil(M / 16).  Preconditions: 16-bit
 // inputs, op_a == N, K % 32 == 0, 16-byte aligned A/B pointers and leading dimensions,
-// N % 8 == 0 when B is not transposed.  One workgroup per 16 columns: grid = ceil(N / 16).
+// N % 8 == 0 when B is not transposed.  One workgroup per 64 columns and k split: the launch
+// sets tiles_m = S (k splits), tiles_n = ceil(N / 64), grid = S * tiles_n * batch, and with
+// S > 1 passes the workspace ws (batch * S * M * N floats); the entry then enqueues a second,
+// finishing kernel.
 const KernelEntry *skinny_f16_f16(int op_b, int mt);
 const KernelEntry *skinny_f16_f32(int op_b, int mt);
 const KernelEntry *skinny_bf16_bf16(int op_b, int mt);

@@ -4,20 +4,24 @@
 // "CUTLASS: Fast Linear Algebra in CUDA C++" ("CUTLASS GEMM Strategies") specialises its tiling
 // for tall and narrow shapes the same way; the shape here is the transposed case.
 //
-//  * one workgroup per 16 output columns (N / 16 workgroups, 256 for N = 4096), K split evenly
-//    over its 4 waves; neighbouring column blocks are placed on the same XCD so that the 128-byte
-//    lines they share are fetched into one L2;
-//  * each wave streams its own K range through a private ring of 16 LDS slots with direct-to-LDS
+//  * one workgroup (one per CU: its LDS is the whole ring) per 64 output columns and k split:
+//    a row of a non-transposed B is read as whole 128-byte lines; K is split S ways over
+//    workgroups when the column blocks alone are too few to fill the chip (S chosen by the
+//    plan), and over the 4 waves of a workgroup;
+//  * each wave streams its K range through a private ring of LDS slots with direct-to-LDS
 //    loads (no barriers inside the loop: a wave only waits for its own loads): per 32-wide k
-//    chunk, 1 KiB of B (32 k x 16 columns) and 1 KiB of A per 16 rows;
+//    chunk, 4 KiB of B (32 k x 64 columns) and 1 KiB of A per 16 rows;
 //  * fragments: A (K-contiguous) and a transposed B with ds_read_b128, a non-transposed B with
 //    the transposing read ds_read_b64_tr_b16; MFMA 16x16x32 with fp32 accumulation;
-//  * the four waves' partial sums are added through LDS and the first wave applies the fused
-//    epilogue (alpha, beta*C, bias[j], ReLU, convert) and stores.
+//  * the four waves' partial sums are added through LDS; then either the fused epilogue
+//    (alpha, beta*C, bias[j], ReLU, convert) and the store, or, with S > 1, the workgroup's
+//    sums go to a workspace and a second small kernel adds the S splits in split order and
+//    applies the epilogue (the kernel boundary orders the two; no device-wide fences, which
+//    cost more than the whole product here).
 //
 // Preconditions (checked by the host): 16-bit inputs, op(A) = A (not transposed), M <= 64,
 // K % 32 == 0, A/B pointers and leading dimensions 16-byte aligned, N % 8 == 0 when B is not
-// transposed.
+// transposed; with S > 1 a workspace of S * M * N floats per product of the batch.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,9 +40,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int NT = 256;
-constexpr int NB = 16;         // output columns per workgroup
-constexpr int KCH = 32;        // k per chunk
-constexpr int RING = 16;       // LDS slots per wave
+constexpr int NB = 64;         // output columns per workgroup: whole 128-byte lines of a row of B
+constexpr int KCH = 32;        // k per chunk (one MFMA step)
+constexpr int BCH = 4;         // 1 KiB load instructions per chunk of B (64 columns x 32 k)
 
 template <class TI>
 __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c);
@@ -61,8 +65,6 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
                  :: "s"(sbase), "v"(voff), "s"(lds) : "memory", "m0");
 }
 
-constexpr int min_c(int a, int b) { return a < b ? a : b; }
-
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
@@ -80,45 +82,55 @@ __device__ __forceinline__ void wait_vm_atmost(int n) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// MT: 16-row tiles of A (M <= 16 * MT); BT: B is stored transposed (N x K)
+// MT: 16-row tiles of A (M <= 16 * MT); BT: B is stored transposed (N x K).
+// Grid: (k split, column block) pairs of every product: p.tiles_m holds the number of k splits
+// S, p.tiles_n the number of 64-column blocks.
 template <class TI, class TO, int MT, bool BT>
 __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
-    constexpr int SLOT = (1 + MT) * 1024;   // B chunk, then MT A chunks
-    constexpr int DPC = 1 + MT;              // load instructions per chunk
-    // ring depth: at most RING, within 40 KiB of LDS per wave, and few enough loads in flight
-    // for the 6-bit vmcnt to count
-    constexpr int DEPTH = min_c(min_c(RING, 40 / DPC), 63 / DPC);
-    constexpr int STEADY = (DEPTH - 1) * DPC;  // loads allowed in flight when waiting for one chunk
-    static_assert(4 * DEPTH * SLOT <= 160 * 1024 && 3 * MT * 1024 <= 4 * DEPTH * SLOT, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * DEPTH * SLOT];
+    constexpr int DPC = BCH + MT;                       // load instructions per chunk
+    constexpr int SLOT = DPC * 1024;                    // B chunk, then MT A chunks
+    // ring depth per wave: as deep as the CU's 160 KiB of LDS allows
+    constexpr int DEPTH = MT == 1 ? 8 : MT == 2 ? 6 : 5;
+    constexpr int STEADY = (DEPTH - 1) * DPC;           // loads in flight when waiting for one chunk
+    constexpr int RING_BYTES = 4 * DEPTH * SLOT;
+    static_assert(RING_BYTES <= 160 * 1024 && STEADY <= 63, "LDS budget, vmcnt range");
+    static_assert(4 * MT * 4 * 64 * 16 <= RING_BYTES, "reduction area");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[RING_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // consecutive column blocks share 128-byte lines of a non-transposed B: keep them on one
-    // XCD (one L2) with the same re-mapping the tiled kernels use
-    const int n0 = select_batch<2, (int)sizeof(typename TO::T)>(p, xcd_remap(blockIdx.x, gridDim.x), p.tiles_n) * NB;
+    const int per = p.tiles_m * p.tiles_n;
+    const int prod = blockIdx.x / per;                  // product of the batch
+    const int lid = select_batch<2, (int)sizeof(typename TO::T)>(p, blockIdx.x, per);
+    const int S = p.tiles_m;
+    const int split = lid / p.tiles_n, cb = lid - split * p.tiles_n;
+    const int n0 = cb * NB;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
-    // K range of this wave, in chunks
+    // chunks [c0, c1) of this wave: the split's share of K, divided over the four waves
     const int nch_all = p.K / KCH;
-    const int per = (nch_all + 3) / 4;
-    const int c0 = min(wave * per, nch_all), c1 = min(c0 + per, nch_all);
+    const int s0 = (int)((int64_t)nch_all * split / S), s1 = (int)((int64_t)nch_all * (split + 1) / S);
+    const int c0 = s0 + (s1 - s0) * wave / 4, c1 = s0 + (s1 - s0) * (wave + 1) / 4;
     const int nch = c1 - c0;
 
     uint8_t *ring = smem + wave * DEPTH * SLOT;
     const uint32_t lring = lds_addr(ring);
 
     // per-lane load offsets (bytes) inside one chunk, relative to the chunk's base pointer
-    uint32_t voffB, voffA[MT];
-    if constexpr (BT) {
-        // B stored N x K: 16 rows (n) of 64 B; lane -> row lane/4, 16 B piece lane%4
-        const int n = min(n0 + (lane >> 2), p.N - 1);
-        voffB = (uint32_t)(n * p.ldb + (lane & 3) * 8) * 2u;
-    } else {
-        // B stored K x N: 32 rows (k) of 32 B; lane -> row lane/2, columns 8*(lane%2) .. +7
-        const int col = min(n0 + 8 * (lane & 1), p.N - 8);
-        voffB = (uint32_t)((lane >> 1) * p.ldb + col) * 2u;
+    uint32_t voffB[BCH], voffA[MT];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+        if constexpr (BT) {
+            // B stored N x K: 64 rows (n) of 64 B; instruction i -> rows 16i + lane/4, piece lane%4
+            const int n = min(n0 + 16 * i + (lane >> 2), p.N - 1);
+            voffB[i] = (uint32_t)(n * p.ldb + (lane & 3) * 8) * 2u;
+        } else {
+            // B stored K x N: 32 rows (k) of 128 B (whole lines); instruction i -> rows 8i + lane/8,
+            // columns 8*(lane%8) .. +7 (columns past N read the last 8 valid ones: never stored)
+            const int col = min(n0 + 8 * (lane & 7), p.N - 8);
+            voffB[i] = (uint32_t)((8 * i + (lane >> 3)) * p.ldb + col) * 2u;
+        }
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -127,29 +139,31 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         voffA[t] = (uint32_t)(m * p.lda + (lane & 3) * 8) * 2u;
     }
     auto issue = [&](int c, int slot) {
-        const int k0 = (c0 + c) * KCH;
+        const int k0 = c * KCH;
         const uint16_t *bb = BT ? B + k0 : B + (size_t)k0 * p.ldb;
         const uint32_t dst = lring + (uint32_t)(slot * SLOT);
-        dma16(bb, voffB, dst);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) dma16(A + k0, voffA[t], dst + 1024u * (1 + t));
+        for (int i = 0; i < BCH; ++i) dma16(bb, voffB[i], dst + 1024u * i);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) dma16(A + k0, voffA[t], dst + 1024u * (BCH + t));
     };
 
-    // fragment read offsets inside a slot
-    // A chunk (16 rows x 64 B, row r at 64 r): lane l needs row l%16, k 8*(l/16) .. +7
+    // fragment read offsets inside a slot.  A chunk (16 rows x 64 B, row r at 64 r): lane l
+    // needs row l%16, k 8*(l/16) .. +7.  B, transposed layout: rows n at 64 B, column group g
+    // (16 columns) at 1024 g, same lane map as A.  B, K x N layout: rows k of 128 B, read with
+    // the transposing read: lane a of each 16-lane group addresses row a/4 (+ 8*(l/16) + 4h) and
+    // columns 16g + 4*(a%4) .. +3.
     const uint32_t offA = (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16);
-    // B: transposed layout = same shape as A (rows n); otherwise rows k of 32 B read with the
-    // transposing read: lane a of each 16-lane group addresses row a/4 (+ 8*(l/16) + 4h) and
-    // columns 4*(a%4) .. +3
-    const uint32_t offB = BT ? offA
-                             : (uint32_t)((8 * (lane >> 4) + ((lane & 15) >> 2)) * 32 + (lane & 3) * 8);
+    const uint32_t offB = BT ? offA : (uint32_t)((8 * (lane >> 4) + ((lane & 15) >> 2)) * 128 + (lane & 3) * 8);
 
-    f32x4 acc[MT];
+    f32x4 acc[MT][4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int npro = min(DEPTH, nch);
-    for (int c = 0; c < npro; ++c) issue(c, c);
+    for (int c = 0; c < npro; ++c) issue(c0 + c, c);
 
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
@@ -157,54 +171,74 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         // loads of later chunks still allowed in flight
         if (nch - 1 - c >= DEPTH - 1) wait_vm<STEADY>();
         else wait_vm_atmost((nch - 1 - c) * DPC);
-        const uint8_t *sl = ring + slot * SLOT;
-        u32x4 bf;
-        if constexpr (BT) {
-            bf = *(const lds_u32x4 *)(uintptr_t)(lds_addr(sl) + offB);
-        } else {
-            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(lds_addr(sl) + offB));
-            s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(lds_addr(sl) + offB + 4 * 32));
-            bf[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
-            bf[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
-            bf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
-            bf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+        const uint32_t sl = lring + (uint32_t)(slot * SLOT);
+        u32x4 bf[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if constexpr (BT) {
+                bf[g] = *(const lds_u32x4 *)(uintptr_t)(sl + 1024u * g + offB);
+            } else {
+                const uint32_t a = sl + offB + 32u * g;
+                s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
+                s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(a + 4 * 128));
+                bf[g][0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+                bf[g][1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+                bf[g][2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+                bf[g][3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+            }
         }
         u32x4 af[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-            af[t] = *(const lds_u32x4 *)(uintptr_t)(lds_addr(sl) + 1024u * (1 + t) + offA);
+        for (int t = 0; t < MT; ++t) af[t] = *(const lds_u32x4 *)(uintptr_t)(sl + 1024u * (BCH + t) + offA);
         // load transforms (no-ops when disabled)
-        bf = zero_negative<2>(bf, p.xform_b);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bf[g] = zero_negative<2>(bf[g], p.xform_b);
 #pragma unroll
         for (int t = 0; t < MT; ++t) af[t] = zero_negative<2>(af[t], p.xform_a);
         // the slot is refilled below: its reads must have returned first
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = mma16<TI>(af[t], bf, acc[t]);
-        if (c + DEPTH < nch) issue(c + DEPTH, slot);
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) acc[t][g] = mma16<TI>(af[t], bf[g], acc[t][g]);
+        if (c + DEPTH < nch) issue(c0 + c + DEPTH, slot);
     }
 
-    // add the four waves' partial sums: waves 1..3 park theirs in LDS
+    // add the four waves' partial sums (every wave has waited for all of its loads): all park
+    // theirs in LDS, then wave w adds up column group w in wave order
     __syncthreads();
-    float *part = reinterpret_cast<float *>(smem);   // [wave 1..3][MT][64 lanes][4]
-    if (wave > 0) {
+    f32x4 *part = reinterpret_cast<f32x4 *>(smem);    // [wave][MT][group][64 lanes]
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) part[((wave * MT + t) * 4 + g) * 64 + lane] = acc[t][g];
+    __syncthreads();
+    f32x4 sum[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        sum[t] = part[((0 * MT + t) * 4 + wave) * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sum[t] += part[((w * MT + t) * 4 + wave) * 64 + lane];
+    }
+
+    // lane holds rows 16t + 4*(lane/16) + r of column n
+    const int n = n0 + 16 * wave + (lane & 15);
+    if (S > 1) {
+        // split K: this split's sums to the workspace, for the finishing kernel
+        if (n >= p.N) return;
+        float *ws = p.ws + ((int64_t)prod * S + split) * p.M * p.N;
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[(((wave - 1) * MT + t) * 64 + lane) * 4 + r] = acc[t][r];
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * t + 4 * (lane >> 4) + r;
+                if (m < p.M) ws[(int64_t)m * p.N + n] = sum[t][r];
+            }
+        return;
     }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[t][r] += part[((w * MT + t) * 64 + lane) * 4 + r];
 
-    // epilogue: lane holds D[16t + 4*(lane/16) + r][n0 + lane%16]
+    // epilogue
     using T = typename TO::T;
-    const int n = n0 + (lane & 15);
     if (n >= p.N) return;
     const float bv = p.has_bias ? static_cast<const float *>(p.bias)[n] : 0.0f;
     const T *C = static_cast<const T *>(p.C);
@@ -216,7 +250,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
             const int m = 16 * t + 4 * (lane >> 4) + r;
             if (m >= p.M) continue;
             const int64_t idx = (int64_t)m * p.ldc + n;
-            float x = p.alpha * acc[t][r];
+            float x = p.alpha * sum[t][r];
             if (p.has_beta) x += p.beta * c_in_f(C[idx], p.xform_c);
             x += bv;
             if (p.relu) x = x > 0.0f ? x : 0.0f;
@@ -224,9 +258,37 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         }
 }
 
+// Split K, second step: D[m][n] = epilogue(sum of the S splits' partial sums, in split order).
+// One thread per output element; workgroup = 256 consecutive columns of one row of a product.
+template <class TO>
+__global__ __launch_bounds__(NT) void skinny_finish(GemmParams p) {
+    using T = typename TO::T;
+    const int tiles = (p.N + NT - 1) / NT;
+    const int per = tiles * p.M;
+    const int prod = blockIdx.x / per;
+    const int lid = select_batch<2, (int)sizeof(T)>(p, blockIdx.x, per);
+    const int m = lid / tiles;
+    const int n = (lid - m * tiles) * NT + (int)threadIdx.x;
+    if (n >= p.N) return;
+    const int S = p.tiles_m;
+    const float *ws = p.ws + (int64_t)prod * S * p.M * p.N + (int64_t)m * p.N + n;
+    float v = 0.0f;
+    for (int q = 0; q < S; ++q) v += ws[(int64_t)q * p.M * p.N];
+    const int64_t idx = (int64_t)m * p.ldc + n;
+    float x = p.alpha * v;
+    if (p.has_beta) x += p.beta * c_in_f(static_cast<const T *>(p.C)[idx], p.xform_c);
+    if (p.has_bias) x += static_cast<const float *>(p.bias)[n];
+    if (p.relu) x = x > 0.0f ? x : 0.0f;
+    static_cast<T *>(p.D)[idx] = (T)x;
+}
+
 template <class TI, class TO, int MT, bool BT>
 hipError_t launch_skinny(const GemmParams &p, unsigned grid, hipStream_t s) {
     hipLaunchKernelGGL((gemm_skinny<TI, TO, MT, BT>), dim3(grid), dim3(NT), 0, s, p);
+    if (p.tiles_m > 1) {
+        const unsigned g2 = (unsigned)((int64_t)((p.N + NT - 1) / NT) * p.M * p.batch);
+        hipLaunchKernelGGL((skinny_finish<TO>), dim3(g2), dim3(NT), 0, s, p);
+    }
     return hipGetLastError();
 }
 
