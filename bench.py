@@ -8,7 +8,12 @@ from HIP events recorded on the launch stream) and the CPU oracle timed on a bou
 of the same workload on this host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME[:IDX]] [--no-cpu]
+                  [--no-graph]
   python bench.py --calibrate-copy     (plain 1 GiB device copies, for scaling HBM counters)
+
+The K timed launches are captured once into a HIP graph and replayed, so that a short kernel
+is timed without the host's per-call overhead (every launch still runs the full product);
+--no-graph times K eager calls instead.
 
 roofline.traffic is the measured HBM traffic per launch (FETCH_SIZE + WRITE_SIZE from rocprofv3,
 each scaled by what the same counter reads for a plain copy of known size), taken from the
@@ -97,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="fp16_8192_bias_relu")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time K eager launches instead of one graph of K launches")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -152,19 +159,33 @@ def main():
                 transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b)
     log(f"[bench] kernel: {plan.describe()}")
 
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        plan.run(A, B, C, D, bias, p.alpha, p.beta)
+    # every launch goes to one non-default stream (the graph is captured and replayed there)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            plan.run(A, B, C, D, bias, p.alpha, p.beta)
     torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(args.steps):
+                plan.run(A, B, C, D, bias, p.alpha, p.beta)
+        torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        plan.run(A, B, C, D, bias, p.alpha, p.beta)
-    ev1.record(stream)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for _ in range(args.steps):
+                plan.run(A, B, C, D, bias, p.alpha, p.beta)
+        ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_events = ev0.elapsed_time(ev1) / max(1, args.steps)
@@ -265,7 +286,8 @@ def main():
                    "kinds": [p.kind_a, p.kind_b],
                    "layout": p.op_a + p.op_b,
                    "ab": p.ab, "cd": p.cd, "epilogue": p.epi, "alpha": p.alpha, "beta": p.beta,
-                   "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4)},
+                   "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4),
+                   "launch": "eager" if graph is None else f"one HIP graph of {args.steps} launches"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,
