@@ -72,21 +72,33 @@ __device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int off_kc(int r, int c) { return r * 128 + ((c ^ swz_kc(r)) << 4); }
 
 // [k][mn] layout (M/N-contiguous operands): 64 rows of 512 B (16-bit) or 128 rows of 256 B
-// (8-bit).  The transposing reads touch, per group of lanes served together, 4 (16-bit) or 8
-// (8-bit) consecutive rows at 2 adjacent 16-byte chunks; the swizzle gives those accesses
-// distinct banks for 32- and 64-bank LDS.
-template <int E>
+// (8-bit).  A transposing read (8 bytes per lane) is served 32 lanes at a time; the 16 lanes of
+// one k group touch 4 (16-bit) or 8 (8-bit) consecutive rows at 2 adjacent 16-byte chunks, and
+// the swizzle gives those accesses distinct banks.  With the 16x16 MFMA shape the two k groups
+// served together (lanes 0-15 and 16-31) lie 16 (16-bit) or 32 (8-bit) rows apart: one more
+// row bit of the swizzle moves the second group to the other half of the banks (the 32x32
+// shape keeps the k groups of a pass in one row block, and adds whole k-slices to a base
+// address, which must not change the swizzle).
+template <int E, int MF>
 __device__ __forceinline__ int swz_mc(int k) {
     if constexpr (E == 2) {
         const int q = k & 3;
-        return 4 * q + 2 * (q >> 1);
+        return (4 * q + 2 * (q >> 1)) ^ (MF == 16 ? ((k >> 4) & 1) << 1 : 0);
     } else {
         const int q = k & 7;
-        return 2 * q + (q >> 2);
+        return (2 * q + (q >> 2)) ^ (MF == 16 ? (k >> 5) & 1 : 0);
     }
 }
-template <int E>
-__device__ __forceinline__ int off_mc(int k, int c) { return k * 256 * E + ((c ^ swz_mc<E>(k)) << 4); }
+template <int E, int MF>
+__device__ __forceinline__ int off_mc(int k, int c) { return k * 256 * E + ((c ^ swz_mc<E, MF>(k)) << 4); }
+
+// k group of the 16 lanes l/16 = g of a 16x16 MFMA fragment.  A 16-byte read (ds_read_b128)
+// is served as lanes l and l+32 together, so the groups g and g+2 must read chunks of opposite
+// parity (a bank-disjoint pair under the [mn][k] swizzle): group g takes the k range
+// 8*grp(g) .. +7 of the k-slice (16 for 8-bit), the same for both operands, which only
+// relabels the products' summation order.  The 32x32 shape keeps the natural order.
+template <int MF>
+__device__ __forceinline__ int kgrp(int g) { return MF == 16 ? ((g & 1) << 1) | (g >> 1) : g; }
 
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -118,7 +130,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
 // a chunk that starts past the end reads the row's last element onwards.  Those extra elements
 // only reach output rows or columns past the edge, which are never stored.  Needs an extent of
 // at least one chunk.
-template <int E, bool KC, bool RS = false>
+template <int E, bool KC, int MF, bool RS = false>
 struct Loader {
     static constexpr int VE = 16 / E;    // elements per 16-byte chunk
     uint32_t voff[8];
@@ -136,7 +148,7 @@ struct Loader {
             } else {
                 constexpr int CPR = 16 * E;                        // chunks per [k] row
                 const int k = blk * (64 / CPR) + lane / CPR;       // slab row (k)
-                const int c = (lane % CPR) ^ swz_mc<E>(k);
+                const int c = (lane % CPR) ^ swz_mc<E, MF>(k);
                 if constexpr (RS) {
                     const int col = min(row0 + c * VE, ext - 1);   // starts inside the row
                     voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
@@ -168,7 +180,7 @@ struct Loader {
 
 // Guarded staging of a partial slab (k0 .. K-1, zero beyond) into the same LDS layout, with the
 // load transform xf applied (register-staged kernels; the others transform their fragments).
-template <int E, bool KC>
+template <int E, bool KC, int MF>
 __device__ __forceinline__ void stage_tail(const uint8_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
                                            int tid, int xf) {
     constexpr int VE = 16 / E;
@@ -191,7 +203,7 @@ __device__ __forceinline__ void stage_tail(const uint8_t *base, int ld, int row0
             p = base + ((size_t)(k0 + k) * ld + col) * E;
             // elements past the M/N edge are zero (their products are never stored)
             nval = k0 + k < K ? ext - col : 0;
-            off = off_mc<E>(k, c);
+            off = off_mc<E, MF>(k, c);
         }
         u32x4 v = {0, 0, 0, 0};
         if (nval >= VE) v = ldg16(p);
@@ -235,24 +247,24 @@ struct Frag {
                 const int r = wrow + MF * t + lr;
 #pragma unroll
                 for (int j = 0; j < S::NS; ++j)
-                    addr[t][j] = opbase + (uint32_t)off_kc(r, (S::KSB / 16) * j + lg);
+                    addr[t][j] = opbase + (uint32_t)off_kc(r, (S::KSB / 16) * j + kgrp<MF>(lg));
             } else if constexpr (E == 2) {
                 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i % 4
                 // of the 8-byte chunks addressed by lanes i/4 + 4e, e = 0..3.  Lane a of the
                 // group therefore addresses k row a/4 and columns 4*(a%4) .. +3; lane group g
-                // (of 64/MF... groups of 16) covers k 8g.. (MF 16) or 8(l/32).. (MF 32).
+                // (of 64/MF... groups of 16) covers k 8 kgrp(g).. (MF 16) or 8(l/32).. (MF 32).
                 const int q = (lane & 15) >> 2;
-                const int k = 8 * lg + q;
+                const int k = 8 * kgrp<MF>(lg) + q;
                 const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
-                addr[t][0] = opbase + (uint32_t)(k * 512 + (((col >> 3) ^ swz_mc<2>(k)) << 4) + (col & 7) * 2);
+                addr[t][0] = opbase + (uint32_t)(k * 512 + (((col >> 3) ^ swz_mc<2, MF>(k)) << 4) + (col & 7) * 2);
             } else {
                 // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
                 // the 8-byte chunks addressed by lanes i/8 + 2e, e = 0..7.  Lane a of the group
                 // therefore addresses k row a/2 and columns 8*(a%2) .. +7.
                 const int a = lane & 15;
-                const int k = 16 * lg + (a >> 1);
+                const int k = 16 * kgrp<MF>(lg) + (a >> 1);
                 const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 8 * (a & 1);
-                addr[t][0] = opbase + (uint32_t)(k * 256 + (((col >> 4) ^ swz_mc<1>(k)) << 4) + (col & 15));
+                addr[t][0] = opbase + (uint32_t)(k * 256 + (((col >> 4) ^ swz_mc<1, MF>(k)) << 4) + (col & 15));
             }
         }
     }
@@ -261,15 +273,15 @@ struct Frag {
         if constexpr (KC) {
             dst = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)(addr[t][j] + stage * KC_BYTES);
         } else if constexpr (E == 2) {
-            // k rows j*KS/2 + (0..3) and + (4..7) past the lane's base: the swizzle depends only
-            // on k & 3
+            // k rows j*KS/2 + (0..3) and + (4..7) past the lane's base: the swizzle depends on
+            // k & 3 and (16x16 shape) k bit 4, which these offsets leave unchanged
             const uint32_t a = addr[t][0] + stage * KC_BYTES + ((S::KSB / 2) * j) * 512;
             s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
             s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(a + 4 * 512));
             dst = __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-            // k rows j*KS + (0..7) and + (8..15) past the lane's base: the swizzle depends only
-            // on k & 7
+            // k rows j*KS + (0..7) and + (8..15) past the lane's base: the swizzle depends on
+            // k & 7 and (16x16 shape) k bit 5, which these offsets leave unchanged
             const uint32_t a = addr[t][0] + stage * KC_BYTES + (S::KSB * j) * 256;
             i32x2 v0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)a);
             i32x2 v1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)(a + 8 * 256));
@@ -496,8 +508,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
 
     FA fa;
     FB fb;
-    Loader<E, AK, RS> la;
-    Loader<E, BK, RS> lb;
+    Loader<E, AK, MF, RS> la;
+    Loader<E, BK, MF, RS> lb;
     // RS: one slab of this wave's chunks in flight between global memory and LDS
     u32x4 ra[RS ? 8 : 1], rb[RS ? 8 : 1];
     int m0 = 0, n0 = 0;
@@ -551,8 +563,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     auto dstA = [&](int st) { return lds0 + (uint32_t)(st * KC_BYTES); };
     auto dstB = [&](int st) { return lds0 + (uint32_t)(OPND + st * KC_BYTES); };
     auto issue_slab = [&](int s, int st) {
-        const uint8_t *sa = Loader<E, AK>::slab_base(A, p.lda, s * BKE);
-        const uint8_t *sb = Loader<E, BK>::slab_base(B, p.ldb, s * BKE);
+        const uint8_t *sa = Loader<E, AK, MF>::slab_base(A, p.lda, s * BKE);
+        const uint8_t *sb = Loader<E, BK, MF>::slab_base(B, p.ldb, s * BKE);
 #pragma unroll
         for (int i = 0; i < 8; ++i) la.issue(sa, dstA(st), wave, i);
 #pragma unroll
@@ -564,8 +576,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     };
     // RS: chunk d (0-7 A, 8-15 B) of slab s into registers; register chunk d into stage st
     auto rs_fetch = [&](int s, int d) {
-        if (d < 8) ra[d] = la.fetch(Loader<E, AK, RS>::slab_base(A, p.lda, s * BKE), d);
-        else rb[d - 8] = lb.fetch(Loader<E, BK, RS>::slab_base(B, p.ldb, s * BKE), d - 8);
+        if (d < 8) ra[d] = la.fetch(Loader<E, AK, MF, RS>::slab_base(A, p.lda, s * BKE), d);
+        else rb[d - 8] = lb.fetch(Loader<E, BK, MF, RS>::slab_base(B, p.ldb, s * BKE), d - 8);
     };
     auto rs_put = [&](int st, int d) {
         if (d < 8) la.put(smem + st * KC_BYTES, wave, d, lane, ra[d], p.xform_a);
@@ -582,10 +594,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     //   RS: in the first k-slices, chunk by chunk, the registers (slab s+1) go to Y and are
     //   refilled with slab s+2 (has_next, dma_next2); the barrier then waits for LDS only
     auto slab_step = [&](int s, int X, int Y, bool dma_next, bool dma_next2, bool has_next) {
-        const uint8_t *na = Loader<E, AK, RS>::slab_base(A, p.lda, (s + 1) * BKE);
-        const uint8_t *nb = Loader<E, BK, RS>::slab_base(B, p.ldb, (s + 1) * BKE);
-        const uint8_t *n2a = Loader<E, AK, RS>::slab_base(A, p.lda, (s + 2) * BKE);
-        const uint8_t *n2b = Loader<E, BK, RS>::slab_base(B, p.ldb, (s + 2) * BKE);
+        const uint8_t *na = Loader<E, AK, MF, RS>::slab_base(A, p.lda, (s + 1) * BKE);
+        const uint8_t *nb = Loader<E, BK, MF, RS>::slab_base(B, p.ldb, (s + 1) * BKE);
+        const uint8_t *n2a = Loader<E, AK, MF, RS>::slab_base(A, p.lda, (s + 2) * BKE);
+        const uint8_t *n2b = Loader<E, BK, MF, RS>::slab_base(B, p.ldb, (s + 2) * BKE);
         auto dma = [&](const uint8_t *sa, const uint8_t *sb, int st, int d) {
             if (d < 8) la.issue(sa, dstA(st), wave, d);
             else lb.issue(sb, dstB(st), wave, d - 8);
@@ -690,8 +702,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     const int k0 = nfull * BKE;
     if (k0 < p.K) {
         __syncthreads();
-        stage_tail<E, AK>(A, p.lda, m0, p.M, k0, p.K, smem, tid, RS ? p.xform_a : 0);
-        stage_tail<E, BK>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid, RS ? p.xform_b : 0);
+        stage_tail<E, AK, MF>(A, p.lda, m0, p.M, k0, p.K, smem, tid, RS ? p.xform_a : 0);
+        stage_tail<E, BK, MF>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid, RS ? p.xform_b : 0);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NS; ++j) {   // the k-slices of the slab
