@@ -11,7 +11,9 @@
 //  * global -> LDS with direct-to-LDS 16-byte loads (global_load_lds_dwordx4): no staging
 //    registers and no LDS write instructions.  One wave instruction fills 1 KiB of LDS, lane l
 //    writing bytes [16l, 16l+16); the XOR swizzle is therefore applied on the global side by
-//    choosing which 16-byte chunk each lane fetches.
+//    choosing which 16-byte chunk each lane fetches.  Layouts the direct loads cannot take
+//    (unaligned pointers, leading dimensions or strides; M/N extents off the 16-byte grid) run
+//    a register-staged variant that moves the same chunks through registers to the same places.
 //  * layouts are handled at load time without transposing through registers ("Flexible GEMM"
 //    section 5.1 adapts its loaders to the N/T layout the same way): an operand whose contiguous
 //    dimension is K is kept [mn][k] in LDS and read with ds_read_b128; an operand whose
@@ -19,8 +21,9 @@
 //    read ds_read_b64_tr_b16, which hands each lane four consecutive-k values of one column.
 //  * swizzles (bank-conflict avoidance, the role padding plays in "Flexible GEMM" section 5.1):
 //    [mn][k] rows of 128 B hold logical 16-byte chunk c at c ^ ((r ^ r>>3) & 7); [k][mn] rows of
-//    512 B hold chunk c at c ^ h(k & 3) with h = {0, 4, 10, 14}.  Both spread every group of
-//    reads over distinct banks for 32- and 64-bank LDS organisations.
+//    512 B hold chunk c at c ^ h(k & 3) with h = {0, 4, 10, 14} (16x16 shape: also ^ 2 in rows
+//    16-31 of each 32).  With the k-group order of kgrp() they give every group of lanes the LDS
+//    serves together distinct banks (the LDS bank-conflict counter reads ~0 in the loop).
 //  * pipeline per slab s (buffers X = s % 2, Y = the other): the fragments of k-slice j+1 are
 //    read while the MFMAs of k-slice j run; after the last read of X the wave waits for its own
 //    loads of slab s+1 and joins the barrier; then it issues the loads of slab s+2 into X and the
@@ -30,14 +33,18 @@
 //  * M/N edges: source rows past the edge are clamped to the last valid row (their products
 //    only reach output rows/columns that the masked epilogue drops); the K tail (K % slab) runs
 //    one guarded register-staged slab with zero fill.
+//  * MFMA shape: 16x16x32 (16x16x64 int8) for NN, NT and TT; 32x32 for TN, for the load
+//    transforms and for the register-staged variant, whose extra live registers the 16x16
+//    schedule cannot hold without shuffling accumulators.
 //  * epilogue (the epilogue building block of "Flexible GEMM" section 4, fused as in the bias and
 //    ReLU functor of "CUTLASS", "Fusing Element-wise Operations"): alpha, beta*C, bias[j], ReLU
 //    and the conversion run on the accumulators; the result goes through a per-wave LDS staging
 //    buffer so that D is written in whole 128-byte lines.
 //
-// Preconditions (checked by the host): 16- or 8-bit inputs, A/B base pointers and leading
-// dimensions 16-byte aligned, M (if A is stored transposed) and N (if B is not transposed)
-// multiples of 16 bytes' worth of elements, K of at least one slab.
+// Preconditions (checked by the host): 16- or 8-bit inputs and K of at least one slab; for the
+// direct loads also A/B base pointers, leading dimensions and batch strides 16-byte aligned and
+// M (if A is stored transposed) and N (if B is not transposed) multiples of 16 bytes' worth of
+// elements; for the register-staged variant an M/N-contiguous extent of at least one chunk.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
