@@ -54,13 +54,36 @@ def host_threads():
     return max(1, n)
 
 
+def _code_only(text):
+    """C++ source without comments and blank space: edits to comments keep the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources the timed kernels are built from."""
+    """Hash of the code (comments and spacing left out) of the HIP sources the timed kernels are
+    built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_gemm_epilogues_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
