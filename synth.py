@@ -300,13 +300,20 @@ def int8_4096_bias():
 
 def fc_layers(layouts=("NN",)):
     """Fully-connected shapes, fp16 in / fp32 acc / fp16 out with bias+ReLU: activations A ~
-    N(0,1), weights B ~ N(0,1/K), bias fp32 ~ U[-0.5,0.5]."""
+    N(0,1), weights B ~ N(0,1/K), bias fp32 ~ U[-0.5,0.5].  The three shapes NN, then the
+    memory-bound one again with the weights stored N x K (B transposed, the layout of a linear
+    layer's weight matrix)."""
     out = []
-    for si, (M, N, K) in enumerate([(16, 4096, 4096), (8192, 16384, 4096), (8192, 4096, 16384)]):
+    shapes = [(16, 4096, 4096), (8192, 16384, 4096), (8192, 4096, 16384)]
+    for si, (M, N, K) in enumerate(shapes):
         for lay in layouts:
             out.append(Problem(M, N, K, lay[0], lay[1], "f16", "f16", "bias_relu", 1.0, 0.0,
                                a_dist=("normal", 1.0), b_dist=("normal", 1.0 / math.sqrt(K)),
                                key=(5, si), name="fc_layers"))
+    M, N, K = shapes[0]
+    out.append(Problem(M, N, K, "N", "T", "f16", "f16", "bias_relu", 1.0, 0.0,
+                       a_dist=("normal", 1.0), b_dist=("normal", 1.0 / math.sqrt(K)),
+                       key=(5, 0), name="fc_layers"))
     return out
 
 
