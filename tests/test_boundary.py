@@ -207,3 +207,44 @@ def test_complex_dual_plans(ab, cd):
                                      transform_a="relu")[0] == tge.STATUS_NOT_SUPPORTED
     assert tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, ab, cd, "none",
                                      kind_a="diagonal")[0] == tge.STATUS_NOT_SUPPORTED
+
+
+# ---- kernel choice (host logic: the plan's description names the kernel it will launch) -----
+
+@pytest.mark.parametrize("shape,lay,ab,cd,want", [
+    # aligned large product: the direct-load fast kernel
+    ((8192, 8192, 8192), "NN", "f16", "f16", "gemm_fast_256x256 "),
+    # odd leading dimensions (4095 x 3073 x 2047 stored tightly): the register-staged variant
+    ((4095, 3073, 2047), "NN", "bf16", "f32", "gemm_fast_256x256_rs"),
+    ((4095, 3073, 2047), "TT", "bf16", "f32", "gemm_fast_256x256_rs"),
+    # aligned ld but N off the 16-byte grid with B not transposed: register-staged
+    ((4096, 4100, 4096), "NN", "f16", "f16", "gemm_fast_256x256_rs"),
+    # the same with B transposed (K-contiguous): the direct loads take it
+    ((4096, 4100, 4096), "NT", "f16", "f16", "gemm_fast_256x256 "),
+    # fp32 has no fast path; a short product takes the skinny kernel with K split 4 ways
+    ((8192, 8192, 8192), "NN", "f32", "f32", "gemm_mfma_256x256"),
+    ((16, 4096, 4096), "NN", "f16", "f16", "gemm_skinny_m16"),
+])
+def test_kernel_choice(shape, lay, ab, cd, want):
+    M, N, K = shape
+    p = tge.Plan(M, N, K, lay[0], lay[1], ab=ab, cd=cd)
+    assert want in p.describe() + " ", p.describe()
+
+
+def test_skinny_split_k_described():
+    # 64 column blocks fill a quarter of the chip: K is split 4 ways (8 chunks per wave); short K
+    # is not split
+    assert "ksplit 4" in tge.Plan(16, 4096, 4096, "N", "N").describe()
+    assert "ksplit" not in tge.Plan(16, 4096, 512, "N", "N").describe()
+    assert "ksplit" not in tge.Plan(16, 16384, 4096, "N", "N").describe()
+
+
+def test_diagonal_kernels_described():
+    d = tge.Plan(4096, 4096, 4096, "N", "N", kind_a="diagonal").describe()
+    assert "gemm_diag_rows" in d and "diag A" in d, d
+    d = tge.Plan(4096, 4096, 4096, "N", "T", kind_a="diagonal").describe()
+    assert "gemm_diag_cols" in d, d
+    d = tge.Plan(4096, 4096, 4096, "T", "N", kind_b="diagonal").describe()
+    assert "gemm_diag_cols" in d and "diag B" in d, d
+    d = tge.Plan(512, 512, 512, "N", "N", kind_a="diagonal", kind_b="diagonal").describe()
+    assert "gemm_diag_rows" in d and "diag AB" in d, d
