@@ -74,6 +74,19 @@ def test_transforms_skinny_exact(lb, xf, monkeypatch):
     check(p, x, D, reference(p, x), exact=True)
 
 
+@pytest.mark.parametrize("lb", ["N", "T"])
+def test_transforms_skinny_split_k_exact(lb, monkeypatch):
+    # K long enough that the skinny plan splits it over workgroups: the operand transforms run
+    # in the splitting kernel, the C transform in the finishing one
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    p = _problem(33, 200, 4096, "N" + lb, "f16", "f32", "bias_relu", 1.0, -0.5,
+                 (133, lb == "T"), ("relu", "relu", "relu"))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_skinny" in pl.describe() and "ksplit" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
 def test_transforms_random_within_tolerance(monkeypatch):
     monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
     p = synth.Problem(1000, 776, 1000, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.5,
