@@ -424,3 +424,17 @@ def test_fast_extent_below_one_chunk_takes_the_general_kernel(monkeypatch):
     D, pl = run(p, x)
     assert "gemm_fast" not in pl.describe(), pl.describe()
     check(p, x, D, reference(p, x), exact=True)
+
+
+def test_fast_streaming_stores_unaligned_d(monkeypatch):
+    # more than one round of 256x256 tiles (17 x 17 = 289 workgroups): interior tiles write D with
+    # non-temporal stores; an odd ldc makes those stores unaligned.  C read in place as well.
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    for j, (cd, pad) in enumerate([("f16", 1), ("f32", 3), ("f16", 0)]):
+        p = _exact(4200, 4200, 128, "NN", "f16", cd, "bias_relu", 2.0, -1.0, key=(122, j))
+        p.ldc += pad
+        x = synth.make_inputs(p)
+        print(p.label(), "ldc", p.ldc, flush=True)
+        D, pl = run(p, x)
+        assert "gemm_fast_256x256 " in pl.describe() + " " and "grid 289" in pl.describe(), pl.describe()
+        check(p, x, D, reference(p, x), exact=True)
