@@ -8,6 +8,7 @@ import torch
 
 import oracle
 import synth
+from dataclasses import replace
 from gpu_helpers import reference_batched, run_batched, sentinel
 
 pytestmark = pytest.mark.gpu
@@ -73,15 +74,36 @@ def test_batched_exact(case, monkeypatch):
     _check_exact(p, D, reference_batched(p, x))
 
 
-def test_batched_unaligned_stride_takes_the_register_staged_kernel(monkeypatch):
-    # a stride that moves product 1 off 16-byte alignment: the direct loads are not eligible,
-    # the register-staged fast kernel runs
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+@pytest.mark.parametrize("mode", ["fast", "staged"])
+def test_batched_unaligned_stride(mode, monkeypatch):
+    # a stride that moves product 1 off 16-byte alignment: the direct loads cannot read A in
+    # place; A is copied per product into aligned rows (fast) or the register-staged kernel runs
+    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
     p = synth.exact_integer_problem(256, 264, 128, "N", "N", "f16", "f16", "bias", 1.0, 0.0,
                                     key=(121, 0), batch=2, stride_a=256 * 128 + 3)
     x = synth.make_inputs(p)
     D, pl = run_batched(p, x)
-    assert "gemm_fast_256x256_rs" in pl.describe(), pl.describe()
+    if mode == "staged":
+        assert "gemm_fast_256x256_rs" in pl.describe(), pl.describe()
+    else:
+        assert "gemm_fast_256x256 " in pl.describe() and "repack A " in pl.describe() + " ", pl.describe()
+    _check_exact(p, D, reference_batched(p, x))
+
+
+@pytest.mark.parametrize("lay", ["NN", "TN", "NT", "TT"])
+def test_batched_repack_shared_and_strided(lay, monkeypatch):
+    # odd leading dimensions and strides, B shared by every product (stride 0, one copy) and
+    # a per-product bias; bf16 -> f32 with beta over three products
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    M, N, K = 300, 261, 200
+    ra = (M if lay[0] == "N" else K)
+    p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], "bf16", "f32", "bias_relu", 1.0, 1.0,
+                                    key=(123, ["NN", "TN", "NT", "TT"].index(lay)), ld_pad=1,
+                                    batch=3, stride_b=0, stride_bias=N)
+    p = replace(p, stride_a=ra * p.lda + 5, stride_c=M * p.ldc + 3)
+    x = synth.make_inputs(p)
+    D, pl = run_batched(p, x)
+    assert "gemm_fast_256x256 " in pl.describe() and "repack AB" in pl.describe(), pl.describe()
     _check_exact(p, D, reference_batched(p, x))
 
 

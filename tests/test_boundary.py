@@ -211,24 +211,49 @@ def test_complex_dual_plans(ab, cd):
 
 # ---- kernel choice (host logic: the plan's description names the kernel it will launch) -----
 
-@pytest.mark.parametrize("shape,lay,ab,cd,want", [
+@pytest.mark.parametrize("shape,lay,ab,cd,want,extra", [
     # aligned large product: the direct-load fast kernel
-    ((8192, 8192, 8192), "NN", "f16", "f16", "gemm_fast_256x256 "),
-    # odd leading dimensions (4095 x 3073 x 2047 stored tightly): the register-staged variant
-    ((4095, 3073, 2047), "NN", "bf16", "f32", "gemm_fast_256x256_rs"),
-    ((4095, 3073, 2047), "TT", "bf16", "f32", "gemm_fast_256x256_rs"),
-    # aligned ld but N off the 16-byte grid with B not transposed: register-staged
-    ((4096, 4100, 4096), "NN", "f16", "f16", "gemm_fast_256x256_rs"),
+    ((8192, 8192, 8192), "NN", "f16", "f16", "gemm_fast_256x256 ", None),
+    # odd leading dimensions (4095 x 3073 x 2047 stored tightly): both operands are copied
+    # into aligned rows, then the direct-load kernel runs on the copies
+    ((4095, 3073, 2047), "NN", "bf16", "f32", "gemm_fast_256x256 ", " repack AB"),
+    ((4095, 3073, 2047), "TT", "bf16", "f32", "gemm_fast_256x256 ", " repack AB"),
+    # aligned ld but N off the 16-byte grid with B not transposed: B is copied (rows padded)
+    ((4096, 4100, 4096), "NN", "f16", "f16", "gemm_fast_256x256 ", " repack B"),
     # the same with B transposed (K-contiguous): the direct loads take it
-    ((4096, 4100, 4096), "NT", "f16", "f16", "gemm_fast_256x256 "),
+    ((4096, 4100, 4096), "NT", "f16", "f16", "gemm_fast_256x256 ", None),
     # fp32 has no fast path; a short product takes the skinny kernel with K split 4 ways
-    ((8192, 8192, 8192), "NN", "f32", "f32", "gemm_mfma_256x256"),
-    ((16, 4096, 4096), "NN", "f16", "f16", "gemm_skinny_m16"),
+    ((8192, 8192, 8192), "NN", "f32", "f32", "gemm_mfma_256x256", None),
+    ((16, 4096, 4096), "NN", "f16", "f16", "gemm_skinny_m16", None),
 ])
-def test_kernel_choice(shape, lay, ab, cd, want):
+def test_kernel_choice(shape, lay, ab, cd, want, extra):
     M, N, K = shape
     p = tge.Plan(M, N, K, lay[0], lay[1], ab=ab, cd=cd)
     assert want in p.describe() + " ", p.describe()
+    assert (extra in p.describe()) if extra else ("repack" not in p.describe()), p.describe()
+
+
+@pytest.mark.parametrize("shape,lay", [((4095, 3073, 2047), "NN"), ((4095, 3073, 2047), "TN"),
+                                       ((4096, 4100, 4096), "NN")])
+def test_kernel_choice_register_staged(shape, lay, monkeypatch):
+    # TGE_FORCE_KERNEL=staged: the register-staged variant reads such operands in place
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "staged")
+    M, N, K = shape
+    d = tge.Plan(M, N, K, lay[0], lay[1], ab="bf16", cd="f32").describe()
+    assert "gemm_fast_256x256_rs" in d and "repack" not in d, d
+
+
+def test_repack_only_what_the_direct_loads_cannot_read():
+    # only the operand off the grid is copied: B with an odd ld; A with an M extent off the grid
+    # when stored transposed; a K-contiguous operand's K tail needs no copy
+    assert tge.Plan(4096, 4096, 4096, "N", "N", 4096, 4097, 4096).describe().endswith("repack B")
+    assert tge.Plan(4100, 4096, 4096, "T", "N").describe().endswith("repack A")
+    d = tge.Plan(4096, 4096, 4100, "N", "T", 4104, 4104, 4096).describe()
+    assert "gemm_fast_256x256 " in d and "repack" not in d, d
+    # a strided batch whose A stride breaks alignment copies A per product
+    d = tge.Plan(2048, 2048, 2048, "N", "N", batch=4, stride_a=2048 * 2048 + 1,
+                 stride_b=2048 * 2048, stride_c=2048 * 2048).describe()
+    assert "repack A" in d and "batch 4" in d, d
 
 
 def test_skinny_split_k_described():

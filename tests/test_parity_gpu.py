@@ -248,8 +248,8 @@ def test_fast_path_random_and_unaligned_fallback(lay, monkeypatch):
     assert "gemm_fast" in pl.describe()
     ref = reference(p, x)
     check(p, x, D, ref)
-    # a pointer offset by one element takes the register-staged fast kernel at run time: same
-    # result
+    # a pointer offset by one element: the operands are copied to aligned rows at run time and
+    # the same kernel runs on the copies; same result
     D2, _ = run(p, x, offset=1)
     check(p, x, D2, ref)
 
@@ -353,9 +353,11 @@ def test_fast_path_int8_exact(lay, shape, monkeypatch):
     check(p, x, D, reference(p, x), exact=True)
 
 
-# ---- the register-staged fast path: layouts the direct loads cannot take ----------------------
+# ---- layouts the direct loads cannot take: repacked copies, or the register-staged variant -----
 # (M, N, K, leading-dimension padding): odd leading dimensions, M/N off the 16-byte grid with the
-# tile crossing the edge, an M/N-contiguous extent of exactly one chunk, K tails
+# tile crossing the edge, an M/N-contiguous extent of exactly one chunk, K tails.  Mode "fast"
+# copies such operands into aligned, zero-padded rows and runs the direct-load kernel on the
+# copies; mode "staged" runs the register-staged variant on the operands in place.
 RS_SHAPES = [(300, 261, 200, 1), (257, 9, 136, 3), (9, 263, 72, 0), (520, 515, 333, 5),
              (264, 264, 64, 1), (16, 16, 128, 7)]
 VE = {"f16": 8, "bf16": 8, "i8": 16}
@@ -367,12 +369,13 @@ def _direct_ok(p, pad):
             (p.op_a == "N" or p.M % VE[p.ab] == 0) and (p.op_b == "T" or p.N % VE[p.ab] == 0))
 
 
+@pytest.mark.parametrize("mode", ["fast", "staged"])
 @pytest.mark.parametrize("shape", RS_SHAPES)
 @pytest.mark.parametrize("lay", LAYOUTS)
 @pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"),
                                    ("bf16", "f32"), ("i8", "i32")])
-def test_fast_register_staged_exact(ab, cd, lay, shape, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+def test_fast_unaligned_layouts_exact(ab, cd, lay, shape, mode, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
     M, N, K, pad = shape
     if ab == "i8":
         K *= 2                              # one int8 slab is 128 deep
@@ -384,46 +387,104 @@ def test_fast_register_staged_exact(ab, cd, lay, shape, monkeypatch):
     x = synth.make_inputs(p)
     print(p.label(), flush=True)
     D, pl = run(p, x)
-    want = "gemm_fast_256x256 " if _direct_ok(p, pad) else "gemm_fast_256x256_rs"
+    if _direct_ok(p, pad):
+        want = "gemm_fast_256x256 "
+    elif mode == "fast":
+        want = "gemm_fast_256x256 "
+        assert " repack " in pl.describe(), pl.describe()
+    else:
+        want = "gemm_fast_256x256_rs"
     assert want in pl.describe() + " ", pl.describe()
     check(p, x, D, reference(p, x), exact=True)
-    # unaligned operand pointers: the register-staged kernel at run time, same result
+    # unaligned operand pointers: copied (fast) or register-staged at run time, same result
     D2, _ = run(p, x, offset=1)
     check(p, x, D2, reference(p, x), exact=True)
 
 
+@pytest.mark.parametrize("mode", ["fast", "staged"])
 @pytest.mark.parametrize("lay", LAYOUTS)
-def test_fast_register_staged_random(lay, monkeypatch):
+def test_fast_unaligned_layouts_random(lay, mode, monkeypatch):
     # random data, bf16 -> f32 with bias + ReLU, odd leading dimensions over several tiles
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
     p = synth.Problem(777, 1031, 611, lay[0], lay[1], "bf16", "f32", "bias_relu", 1.0, 0.5,
                       key=(115, LAYOUTS.index(lay)))
     p.lda += 1; p.ldb += 3; p.ldc += 1
     x = synth.make_inputs(p)
     D, pl = run(p, x)
-    assert "gemm_fast_256x256_rs" in pl.describe(), pl.describe()
+    want = "gemm_fast_256x256_rs" if mode == "staged" else "gemm_fast_256x256 "
+    assert want in pl.describe(), pl.describe()
+    assert (" repack AB" in pl.describe()) == (mode == "fast"), pl.describe()
     check(p, x, D, reference(p, x))
 
 
-def test_fast_register_staged_with_transforms(monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+@pytest.mark.parametrize("mode", ["fast", "staged"])
+def test_fast_unaligned_layouts_with_transforms(mode, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
     p = synth.exact_integer_problem(300, 261, 200, "T", "N", "f16", "f32", "bias", 1.0, 1.0,
                                     key=(116, 0), ld_pad=1, transform_a="relu",
                                     transform_b="relu", transform_c="relu")
     x = synth.make_inputs(p)
     D, pl = run(p, x)
-    assert "gemm_fast_256x256_rs" in pl.describe() and "relu-in ABC" in pl.describe()
+    want = "gemm_fast_256x256_rs" if mode == "staged" else "gemm_fast_256x256 "
+    assert want in pl.describe() and "relu-in ABC" in pl.describe(), pl.describe()
     check(p, x, D, reference(p, x), exact=True)
 
 
-def test_fast_extent_below_one_chunk_takes_the_general_kernel(monkeypatch):
-    # N = 5 with B not transposed: no in-bounds 16-byte chunk exists, the general kernel runs
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+@pytest.mark.parametrize("mode", ["fast", "staged"])
+def test_fast_extent_below_one_chunk(mode, monkeypatch):
+    # N = 5 with B not transposed: no in-bounds 16-byte chunk exists in place.  Copied, B's rows
+    # are padded to one whole chunk and the direct-load kernel runs; the register-staged variant
+    # cannot take it and the general kernel runs
+    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
     p = _exact(300, 5, 128, "NN", "f16", "f16", "bias", 1.0, 0.0, key=(117, 0))
     x = synth.make_inputs(p)
     D, pl = run(p, x)
-    assert "gemm_fast" not in pl.describe(), pl.describe()
+    if mode == "fast":
+        assert "gemm_fast_256x256 " in pl.describe() and "repack B" in pl.describe(), pl.describe()
+    else:
+        assert "gemm_fast" not in pl.describe(), pl.describe()
     check(p, x, D, reference(p, x), exact=True)
+
+
+def test_repack_graph_capture(monkeypatch):
+    # a first run inside a capture cannot allocate the copy workspace: it runs the
+    # register-staged kernel; after an eager run (which allocates it) captured runs copy the
+    # operands; every replay, with eager work between, gives the eager result bit for bit
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    p = _exact(520, 515, 333, "TN", "f16", "f32", "bias_relu", 2.0, -1.0, key=(122, 0), ld_pad=1)
+    x = synth.make_inputs(p)
+    ref = reference(p, x)
+    from gpu_helpers import to_dev, to_host
+    A, B = to_dev(p.ab, x["A"]), to_dev(p.ab, x["B"])
+    C, bias = to_dev(p.cd, x["C"]), to_dev(p.bias_dt, x["bias"])
+    import tiled_gemm_epilogues_amd as tge
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    assert "repack AB" in pl.describe(), pl.describe()
+    D = torch.zeros(p.M * p.ldc, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(s):
+        g0 = torch.cuda.CUDAGraph()                       # no workspace yet: register-staged
+        with torch.cuda.graph(g0, stream=s):
+            pl.run(A, B, C, D, bias, p.alpha, p.beta)
+        graphs.append(g0)
+        pl.run(A, B, C, D, bias, p.alpha, p.beta)          # eager: allocates the copies
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=s):
+            for _ in range(2):
+                pl.run(A, B, C, D, bias, p.alpha, p.beta)
+        graphs.append(g1)
+    torch.cuda.synchronize()
+    D0 = to_host(p.cd, D).reshape(p.M, p.ldc).copy()
+    check(p, x, D0, ref, exact=True)
+    for _ in range(3):
+        for g in graphs:
+            D.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(p.cd, D).reshape(p.M, p.ldc), D0)
+            pl.run(A, B, C, D, bias, p.alpha, p.beta)      # eager work between replays
+            torch.cuda.synchronize()
 
 
 def test_fast_streaming_stores_unaligned_d(monkeypatch):

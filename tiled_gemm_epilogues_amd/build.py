@@ -51,7 +51,7 @@ def build(verbose=False, jobs=None):
         obj = os.path.join(BUILD, f"gemm_skinny_{pair.lower()}.o")
         steps.append([HIPCC, *FLAGS, f"-DTGE_PAIR_{pair}", "-c",
                       os.path.join(CSRC, "gemm_skinny.hip"), "-o", obj])
-    for name in ("gemm_complex", "gemm_diag"):
+    for name in ("gemm_complex", "gemm_diag", "gemm_repack"):
         steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, name + ".hip"), "-o",
                       os.path.join(BUILD, name + ".o")])
     api_obj = os.path.join(BUILD, "gemm_api.o")

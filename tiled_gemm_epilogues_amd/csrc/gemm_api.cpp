@@ -26,6 +26,13 @@ struct gemm_plan {
     int ws_dev;                      // device of the skinny split-K workspace (-1: none yet)
     float *ws;                       // skinny split-K partial sums: batch * S * M * N floats
     const KernelEntry *fast_rs;      // register-staged fast kernel: any alignment, else nullptr
+    // direct-load fast kernel on aligned copies of the operands it cannot read in place
+    const KernelEntry *fast_pk;      // nullptr: no repacking for this plan
+    int pk_need;                     // bit 0 / bit 1: A / B always copied (ld, stride or extent)
+    int64_t pk_ld_a, pk_ld_b;        // leading dimensions of the copies (whole 16-byte chunks)
+    int64_t pk_off_b, pk_bytes;      // byte offset of B's copy in the workspace, total size
+    int pk_dev;                      // device of the copy workspace (-1: none yet)
+    void *pk_ws;
     int tiles_m, tiles_n, group_m;
     unsigned grid;
     char desc[192];
@@ -158,6 +165,27 @@ static gemm_status_t skinny_workspace(gemm_plan *p, hipStream_t stream) {
     return GEMM_STATUS_SUCCESS;
 }
 
+// The copy workspace of a repacking plan on the current device, allocated by the first run there
+// that needs it (not while the stream is being captured into a graph).
+static gemm_status_t repack_workspace(gemm_plan *p, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+    if (p->pk_ws && p->pk_dev == dev) return GEMM_STATUS_SUCCESS;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+    if (cs != hipStreamCaptureStatusNone) return GEMM_STATUS_NOT_SUPPORTED;
+    if (p->pk_ws) (void)hipFree(p->pk_ws);
+    p->pk_ws = nullptr;
+    p->pk_dev = -1;
+    if (hipMalloc(&p->pk_ws, (size_t)p->pk_bytes) != hipSuccess) {
+        p->pk_ws = nullptr;
+        (void)hipGetLastError();
+        return GEMM_STATUS_ALLOC_FAILED;
+    }
+    p->pk_dev = dev;
+    return GEMM_STATUS_SUCCESS;
+}
+
 extern "C" {
 
 const char *gemm_status_string(gemm_status_t s) {
@@ -269,7 +297,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // fast path: 16-bit inputs, 256x256 tiles worth it, shape/ld preconditions of gemm_fast
     const KernelEntry *fast = nullptr;
     FastLookup ft = fast_table(ab_type, cd_type);
-    const char *fk = getenv("TGE_FORCE_KERNEL");  // "fast" or "general" (tests, sweeps)
+    // "fast", "staged" (the fast kernel, register-staged for operands the direct loads cannot
+    // read in place instead of repacking them), "general" or "skinny" (tests, sweeps)
+    const char *fk = getenv("TGE_FORCE_KERNEL");
+    const bool staged = fk && strcmp(fk, "staged") == 0;
     // the fast kernel does ~3x the work per CU-round of the general 128x128 kernel: take it
     // when its rounds of 256x256 tiles cost less than 3x as many rounds of 128x128 tiles
     const int64_t nb = batch > 1 ? batch : 1;
@@ -277,7 +308,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const int64_t r128 = (((M + 127) / 128) * ((N + 127) / 128) * nb + 255) / 256;
     bool want_fast = cfg == tge::CFG_256 || (cfg == tge::CFG_128 && 4 * r256 <= 3 * r128);
     if (getenv("TGE_FORCE_TILE")) want_fast = cfg == tge::CFG_256;
-    if (fk && strcmp(fk, "fast") == 0) want_fast = true;
+    if ((fk && strcmp(fk, "fast") == 0) || staged) want_fast = true;
     if (fk && strcmp(fk, "general") == 0) want_fast = false;
     const int ve = 16 / eab;   // elements per 16-byte chunk
     // every product of a batch keeps the 16-byte alignment of product 0
@@ -292,12 +323,46 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         (op_b == GEMM_OP_T || N >= ve))
         fast_rs = ft(op_a, op_b, 1);
 
+    // repacking: operands the direct loads cannot read in place are copied into aligned rows
+    // padded to whole 16-byte chunks, then the direct-load kernel runs on the copies
+    // (TGE_FORCE_KERNEL=staged keeps the register-staged variant for such operands)
+    const KernelEntry *fast_pk = nullptr;
+    int pk_need = 0;
+    int64_t pk_ld_a = 0, pk_ld_b = 0, pk_off_b = 0, pk_bytes = 0;
+    if (ft && want_fast && K >= 128 / eab && !diag_a && !diag_b && !staged) {
+        const int64_t rows_a = op_a == GEMM_OP_N ? M : K, len_a = op_a == GEMM_OP_N ? K : M;
+        const int64_t rows_b = op_b == GEMM_OP_N ? K : N, len_b = op_b == GEMM_OP_N ? N : K;
+        pk_ld_a = (len_a + ve - 1) / ve * ve;
+        pk_ld_b = (len_b + ve - 1) / ve * ve;
+        // a batch stride of 0 shares the operand between products: one copy
+        const int64_t na = batch > 1 && stride_a ? batch : 1, nbb = batch > 1 && stride_b ? batch : 1;
+        const int64_t one_a = rows_a * pk_ld_a * eab, one_b = rows_b * pk_ld_b * eab;
+        // an M/N-contiguous operand (A transposed, B not) must also be whole chunks wide
+        const bool need_a = (lda * eab) % 16 != 0 || (stride_a * eab) % 16 != 0 ||
+                            (op_a == GEMM_OP_T && M % ve != 0);
+        const bool need_b = (ldb * eab) % 16 != 0 || (stride_b * eab) % 16 != 0 ||
+                            (op_b == GEMM_OP_N && N % ve != 0);
+        pk_need = (need_a ? 1 : 0) | (need_b ? 2 : 0);
+        // the copies obey the 32-bit offset limit of the kernels; the copy grid (workgroups of
+        // 4 rows x 1 KiB) fits 31 bits
+        auto blocks = [&](int64_t rows, int64_t ld, int64_t n) {
+            return ((ld * eab + 1023) / 1024) * ((rows + 3) / 4) * n;
+        };
+        if (one_a < lim && one_b < lim && blocks(rows_a, pk_ld_a, na) + blocks(rows_b, pk_ld_b, nbb) < lim) {
+            pk_off_b = (na * one_a + 255) / 256 * 256;
+            pk_bytes = pk_off_b + nbb * one_b;
+            fast_pk = ft(op_a, op_b, 0);
+        } else {
+            pk_need = 0;
+        }
+    }
+
     // skinny path: M <= 64, memory bound; preferred over both tiled kernels when it applies
     bool skinny = false;
     SkinnyLookup st = skinny_table(ab_type, cd_type);
     bool want_skinny = M <= 64;
     if (fk && strcmp(fk, "general") == 0) want_skinny = false;
-    if (fk && strcmp(fk, "fast") == 0) want_skinny = false;
+    if ((fk && strcmp(fk, "fast") == 0) || staged) want_skinny = false;
     if (fk && strcmp(fk, "skinny") == 0) want_skinny = true;
     if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % 32 == 0 &&
         (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && strides16 && (op_b == GEMM_OP_T || N % 8 == 0)) {
@@ -317,6 +382,12 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->fast = fast;
     p->fast_is_skinny = skinny;
     p->fast_rs = fast_rs;
+    p->fast_pk = fast_pk;
+    p->pk_need = pk_need;
+    p->pk_ld_a = pk_ld_a; p->pk_ld_b = pk_ld_b;
+    p->pk_off_b = pk_off_b; p->pk_bytes = pk_bytes;
+    p->pk_dev = -1;
+    p->pk_ws = nullptr;
     p->ksplit = 1;
     p->ws_dev = -1;
     p->ws = nullptr;
@@ -330,7 +401,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if (sp > 64) sp = 64;
         p->ksplit = sp > 1 ? (int)sp : 1;
     }
-    const KernelEntry *shown = fast ? fast : fast_rs ? fast_rs : k;
+    // a plan that always copies an operand shows the direct kernel on the copies
+    const bool shows_pk = !fast && fast_pk && pk_need;
+    const KernelEntry *shown = fast ? fast : shows_pk ? fast_pk : fast_rs ? fast_rs : k;
     p->tiles_m = skinny ? p->ksplit : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
@@ -344,6 +417,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     int bl = 0;
     if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
     if (p->ksplit > 1) bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " ksplit %d", p->ksplit);
+    if (shows_pk)
+        bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " repack %s%s", pk_need & 1 ? "A" : "",
+                       pk_need & 2 ? "B" : "");
     if (diag_a || diag_b)
         bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " diag %s%s", diag_a ? "A" : "", diag_b ? "B" : "");
     if (desc->transform_a || desc->transform_b || desc->transform_c)
@@ -359,6 +435,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
 
 gemm_status_t gemm_plan_destroy(gemm_plan_t p) {
     if (p && p->ws) (void)hipFree(p->ws);
+    if (p && p->pk_ws) (void)hipFree(p->pk_ws);
     delete p;
     return GEMM_STATUS_SUCCESS;
 }
@@ -397,10 +474,38 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
     prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
     const KernelEntry *k = p->kernel;
-    // the direct-load fast kernel needs 16-byte aligned operand pointers; else the
-    // register-staged one runs when the plan has it, else the general kernel
-    if (p->fast && ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0) k = p->fast;
-    else if (p->fast_rs) k = p->fast_rs;
+    // the direct-load fast kernel needs 16-byte aligned operand pointers; an operand it cannot
+    // read in place is copied first when the plan repacks (and its workspace exists or can be
+    // allocated now); else the register-staged kernel runs when the plan has it, else the
+    // general kernel
+    const int need = (p->pk_need | (((uintptr_t)A % 16) ? 1 : 0) | (((uintptr_t)B % 16) ? 2 : 0)) &
+                     (p->K > 0 ? 3 : 0);
+    if (p->fast && !need) k = p->fast;
+    else if (p->fast_pk && need && repack_workspace(p, static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
+        const int eab = elem_bytes(p->ab);
+        const bool sh_a = p->batch > 1 && p->stride_a, sh_b = p->batch > 1 && p->stride_b;
+        tge::RepackJob ja = {}, jb = {};
+        uint8_t *ws = static_cast<uint8_t *>(p->pk_ws);
+        if (need & 1) {
+            const int64_t rows = p->op_a == GEMM_OP_N ? p->M : p->K, len = p->op_a == GEMM_OP_N ? p->K : p->M;
+            ja = {static_cast<const uint8_t *>(A), ws, rows, len * eab, p->lda * eab, p->pk_ld_a * eab,
+                  p->stride_a * eab, rows * p->pk_ld_a * eab, sh_a ? p->batch : 1};
+            prm.A = ws;
+            prm.lda = (int)p->pk_ld_a;
+            prm.stride_a = sh_a ? rows * p->pk_ld_a : 0;
+        }
+        if (need & 2) {
+            const int64_t rows = p->op_b == GEMM_OP_N ? p->K : p->N, len = p->op_b == GEMM_OP_N ? p->N : p->K;
+            jb = {static_cast<const uint8_t *>(B), ws + p->pk_off_b, rows, len * eab, p->ldb * eab,
+                  p->pk_ld_b * eab, p->stride_b * eab, rows * p->pk_ld_b * eab, sh_b ? p->batch : 1};
+            prm.B = ws + p->pk_off_b;
+            prm.ldb = (int)p->pk_ld_b;
+            prm.stride_b = sh_b ? rows * p->pk_ld_b : 0;
+        }
+        if (tge::repack_launch(ja, jb, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return GEMM_STATUS_HIP_ERROR;
+        k = p->fast_pk;
+    } else if (p->fast_rs) k = p->fast_rs;
     const bool sk = k == p->fast && p->fast_is_skinny;
     prm.tiles_m = sk ? p->ksplit : (int)((p->M + k->bm - 1) / k->bm);
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);

@@ -160,7 +160,9 @@ struct Loader {
                     const int col = min(row0 + c * VE, ext - 1);   // starts inside the row
                     voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
                 } else {
-                    const int col = min(row0 + c * VE, ext - VE);  // ext % VE == 0: whole chunks
+                    // the last chunk starts at the last multiple of VE below ext: whole chunks
+                    // when ext % VE == 0, else it runs into the zero padding of a repacked row
+                    const int col = min(row0 + c * VE, (ext - 1) / VE * VE);
                     voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
                 }
             }
