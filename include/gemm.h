@@ -38,10 +38,18 @@
  * gemm_run, allocated by that call and freed by gemm_plan_destroy: its runs must not overlap in
  * time (use one plan per concurrent stream), and its first run must not be captured into a
  * graph (later runs may be).  Such a run enqueues two kernels.
+ * A large 16- or 8-bit plan whose operand rows are off the 16-byte grid (an odd leading
+ * dimension or batch stride, an unaligned pointer at run time, or an M/N-contiguous row length
+ * that is not a multiple of 16 bytes; "repack A/B/AB" in its description when the plan itself
+ * fixes it) first copies those operands into aligned, zero-padded rows of a workspace it owns
+ * (about the size of the copied operands), then runs the direct-load kernel on the copies: two
+ * kernels per run.  The workspace is allocated by the first run that needs it on a device (not
+ * while the stream is captured: such a run reads the operands in place with a slower kernel,
+ * same results) and freed by gemm_plan_destroy; runs of one such plan must not overlap in time.
  *
  * Errors: every function returns a status; nothing throws across this boundary.  gemm_run is
- * asynchronous: it validates, enqueues one kernel on `stream` and returns; faults during
- * execution surface at the caller's next synchronisation.
+ * asynchronous: it validates, enqueues its kernels (one, or two as above) on `stream` and
+ * returns; faults during execution surface at the caller's next synchronisation.
  */
 #ifndef TGE_GEMM_H
 #define TGE_GEMM_H
@@ -194,8 +202,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
  *   alpha, beta  scalars applied in fp32 (int8 plans require alpha == 1 and beta in {0, 1}).
  * Returns INVALID_VALUE for a NULL plan or a missing required pointer, NOT_SUPPORTED for int8
  * scalars outside the rule above or for the first run of a split-K plan during stream capture,
- * ALLOC_FAILED when that first run cannot allocate its workspace, HIP_ERROR when the launch
- * fails.  M == 0, N == 0 or a batch of 0 returns SUCCESS without launching.
+ * ALLOC_FAILED when that first run cannot allocate its workspace (a repacking plan that cannot
+ * allocate its copies reads the operands in place instead), HIP_ERROR when a launch fails.  M == 0, N == 0 or a batch of 0 returns SUCCESS without launching.
  */
 gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream);

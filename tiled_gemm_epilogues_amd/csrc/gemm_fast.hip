@@ -11,9 +11,11 @@
 //  * global -> LDS with direct-to-LDS 16-byte loads (global_load_lds_dwordx4): no staging
 //    registers and no LDS write instructions.  One wave instruction fills 1 KiB of LDS, lane l
 //    writing bytes [16l, 16l+16); the XOR swizzle is therefore applied on the global side by
-//    choosing which 16-byte chunk each lane fetches.  Layouts the direct loads cannot take
-//    (unaligned pointers, leading dimensions or strides; M/N extents off the 16-byte grid) run
-//    a register-staged variant that moves the same chunks through registers to the same places.
+//    choosing which 16-byte chunk each lane fetches.  Operands the direct loads cannot take
+//    (unaligned pointers, leading dimensions or strides; M/N extents off the 16-byte grid) are
+//    copied into aligned, zero-padded rows first (gemm_repack.hip), or, when no copy workspace
+//    exists, read by a register-staged variant that moves the same chunks through registers to
+//    the same places.
 //  * layouts are handled at load time without transposing through registers ("Flexible GEMM"
 //    section 5.1 adapts its loaders to the N/T layout the same way): an operand whose contiguous
 //    dimension is K is kept [mn][k] in LDS and read with ds_read_b128; an operand whose
@@ -44,7 +46,8 @@
 // Preconditions (checked by the host): 16- or 8-bit inputs and K of at least one slab; for the
 // direct loads also A/B base pointers, leading dimensions and batch strides 16-byte aligned and
 // M (if A is stored transposed) and N (if B is not transposed) multiples of 16 bytes' worth of
-// elements; for the register-staged variant an M/N-contiguous extent of at least one chunk.
+// elements, or stored rows zero-padded to whole chunks (the copies); for the register-staged
+// variant an M/N-contiguous extent of at least one chunk.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
