@@ -46,6 +46,10 @@
  * kernels per run.  The workspace is allocated by the first run that needs it on a device (not
  * while the stream is captured: such a run reads the operands in place with a slower kernel,
  * same results) and freed by gemm_plan_destroy; runs of one such plan must not overlap in time.
+ * Likewise a complex or dual plan large enough for the real fast kernel ("as real 2x2 blocks"
+ * in its description) owns a workspace for op(B) rewritten as real 2 x 2 blocks (twice B's
+ * bytes) and, when A is transposed, A split into parts; its runs enqueue the rewrite and then
+ * the real product, and a run without that workspace uses the complex kernel.
  *
  * Errors: every function returns a status; nothing throws across this boundary.  gemm_run is
  * asynchronous: it validates, enqueues its kernels (one, or two as above) on `stream` and

@@ -33,9 +33,15 @@ struct gemm_plan {
     int64_t pk_off_b, pk_bytes;      // byte offset of B's copy in the workspace, total size
     int pk_dev;                      // device of the copy workspace (-1: none yet)
     void *pk_ws;
+    // complex / dual numbers as a real fp16 product M x 2N x 2K on rewritten operands
+    gemm_plan *cx;                   // that real plan; nullptr: the complex kernel runs
+    int64_t cx_ld_a, cx_ld_b;        // rewritten A (A transposed only) and B: leading dimensions
+    int64_t cx_off_b, cx_bytes;      // byte offset of B's rewrite in the workspace, total size
+    int cx_dev;
+    void *cx_ws;
     int tiles_m, tiles_n, group_m;
     unsigned grid;
-    char desc[192];
+    char desc[256];
 };
 
 namespace {
@@ -165,25 +171,30 @@ static gemm_status_t skinny_workspace(gemm_plan *p, hipStream_t stream) {
     return GEMM_STATUS_SUCCESS;
 }
 
-// The copy workspace of a repacking plan on the current device, allocated by the first run there
-// that needs it (not while the stream is being captured into a graph).
-static gemm_status_t repack_workspace(gemm_plan *p, hipStream_t stream) {
+// A plan-owned workspace on the current device, allocated by the first run there that needs it
+// (not while the stream is being captured into a graph).
+static gemm_status_t lazy_workspace(void **ws, int *ws_dev, size_t bytes, hipStream_t stream) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
-    if (p->pk_ws && p->pk_dev == dev) return GEMM_STATUS_SUCCESS;
+    if (*ws && *ws_dev == dev) return GEMM_STATUS_SUCCESS;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
     if (cs != hipStreamCaptureStatusNone) return GEMM_STATUS_NOT_SUPPORTED;
-    if (p->pk_ws) (void)hipFree(p->pk_ws);
-    p->pk_ws = nullptr;
-    p->pk_dev = -1;
-    if (hipMalloc(&p->pk_ws, (size_t)p->pk_bytes) != hipSuccess) {
-        p->pk_ws = nullptr;
+    if (*ws) (void)hipFree(*ws);
+    *ws = nullptr;
+    *ws_dev = -1;
+    if (hipMalloc(ws, bytes) != hipSuccess) {
+        *ws = nullptr;
         (void)hipGetLastError();
         return GEMM_STATUS_ALLOC_FAILED;
     }
-    p->pk_dev = dev;
+    *ws_dev = dev;
     return GEMM_STATUS_SUCCESS;
+}
+
+// The copy workspace of a repacking plan.
+static gemm_status_t repack_workspace(gemm_plan *p, hipStream_t stream) {
+    return lazy_workspace(&p->pk_ws, &p->pk_dev, (size_t)p->pk_bytes, stream);
 }
 
 extern "C" {
@@ -370,8 +381,52 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         skinny = fast != nullptr;
     }
 
+    // complex and dual numbers where the real fast kernels apply: the product as a real fp16
+    // GEMM M x 2N x 2K.  op(A) read as M x 2K reals is A itself when not transposed (parts
+    // interleaved along K), else A's rows split into parts; every number of op(B) becomes a
+    // 2 x 2 block (PairJob).  Elsewhere the complex kernel runs.
+    gemm_plan *cx = nullptr;
+    int64_t cx_ld_a = 0, cx_ld_b = 0, cx_off_b = 0, cx_bytes = 0;
+    if (ctable && M > 0 && N > 0 && K > 0 && !(fk && strcmp(fk, "general") == 0)) {
+        gemm_desc_t r = *desc;
+        r.N = 2 * N;
+        r.K = 2 * K;
+        cx_ld_a = op_a == GEMM_OP_N ? 2 * lda : (M + 7) / 8 * 8;
+        cx_ld_b = op_b == GEMM_OP_N ? (2 * N + 7) / 8 * 8 : (2 * K + 7) / 8 * 8;
+        const int64_t rows_b = op_b == GEMM_OP_N ? 2 * K : 2 * N;
+        const int64_t na = batch > 1 && stride_a ? batch : 1, nbb = batch > 1 && stride_b ? batch : 1;
+        r.lda = cx_ld_a;
+        r.ldb = cx_ld_b;
+        r.ldc = 2 * ldc;
+        r.ab_type = GEMM_F16;
+        r.cd_type = (cd_type == GEMM_CF32 || cd_type == GEMM_DF32) ? GEMM_F32 : GEMM_F16;
+        r.stride_a = op_a == GEMM_OP_N ? 2 * stride_a : (na > 1 ? 2 * K * cx_ld_a : 0);
+        r.stride_b = nbb > 1 ? rows_b * cx_ld_b : 0;
+        r.stride_c = 2 * stride_c;
+        r.stride_bias = 0;
+        auto pblocks = [](int64_t pitch, int gb, int64_t rows, int64_t n) {
+            return ((pitch / gb + 63) / 64) * ((rows + 3) / 4) * n;
+        };
+        const int64_t blocks = (op_a == GEMM_OP_T ? pblocks(cx_ld_a * 2, 8, K, na) : 0) +
+                               pblocks(cx_ld_b * 2, 16, op_b == GEMM_OP_N ? K : N, nbb);
+        gemm_plan *rp = nullptr;
+        if (blocks < lim && gemm_plan_create_desc(&rp, &r) == GEMM_STATUS_SUCCESS) {
+            if ((rp->fast && !rp->fast_is_skinny) || rp->fast_pk || rp->fast_rs) {
+                cx = rp;
+                const int64_t bytes_a = op_a == GEMM_OP_T ? na * 2 * K * cx_ld_a * 2 : 0;
+                cx_off_b = (bytes_a + 255) / 256 * 256;
+                cx_bytes = cx_off_b + nbb * rows_b * cx_ld_b * 2;
+            } else {
+                gemm_plan_destroy(rp);
+            }
+        }
+    }
+
     gemm_plan *p = new (std::nothrow) gemm_plan;
-    if (!p) return GEMM_STATUS_ALLOC_FAILED;
+    if (!p) {
+        if (cx) gemm_plan_destroy(cx);
+        return GEMM_STATUS_ALLOC_FAILED;
+    }
     p->M = M; p->N = N; p->K = K;
     p->batch = batch;
     p->xform_a = desc->transform_a; p->xform_b = desc->transform_b; p->xform_c = desc->transform_c;
@@ -388,6 +443,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->pk_off_b = pk_off_b; p->pk_bytes = pk_bytes;
     p->pk_dev = -1;
     p->pk_ws = nullptr;
+    p->cx = cx;
+    p->cx_ld_a = cx_ld_a; p->cx_ld_b = cx_ld_b;
+    p->cx_off_b = cx_off_b; p->cx_bytes = cx_bytes;
+    p->cx_dev = -1;
+    p->cx_ws = nullptr;
     p->ksplit = 1;
     p->ws_dev = -1;
     p->ws = nullptr;
@@ -409,6 +469,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->group_m = 8;
     const int64_t grid = (int64_t)p->tiles_m * p->tiles_n * batch;
     if (grid >= ((int64_t)1 << 31)) {
+        if (cx) gemm_plan_destroy(cx);
         delete p;
         return GEMM_STATUS_NOT_SUPPORTED;
     }
@@ -429,6 +490,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
              shown->name, dtype_name(ab_type), dtype_name(cd_type), op_a ? 'T' : 'N',
              op_b ? 'T' : 'N', shown->bm, shown->bn, shown->bk, shown->waves_m, shown->waves_n,
              p->grid, bdesc);
+    if (cx)
+        snprintf(p->desc, sizeof(p->desc), "%s->%s %c%c as real 2x2 blocks: %s", dtype_name(ab_type),
+                 dtype_name(cd_type), op_a ? 'T' : 'N', op_b ? 'T' : 'N', cx->desc);
     *out = p;
     return GEMM_STATUS_SUCCESS;
 }
@@ -436,6 +500,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
 gemm_status_t gemm_plan_destroy(gemm_plan_t p) {
     if (p && p->ws) (void)hipFree(p->ws);
     if (p && p->pk_ws) (void)hipFree(p->pk_ws);
+    if (p && p->cx_ws) (void)hipFree(p->cx_ws);
+    if (p && p->cx) gemm_plan_destroy(p->cx);
     delete p;
     return GEMM_STATUS_SUCCESS;
 }
@@ -459,6 +525,32 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     if (p->ab == GEMM_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f)))
         return GEMM_STATUS_NOT_SUPPORTED;
     if (alpha != alpha || beta != beta) return GEMM_STATUS_INVALID_VALUE;  // NaN scalars
+
+    // complex / dual product as a real one: rewrite B (and a transposed A) into the plan's
+    // workspace, then run the real plan; without a workspace (first run inside a capture, or
+    // no memory) the complex kernel below runs instead
+    if (p->cx && lazy_workspace(&p->cx_ws, &p->cx_dev, (size_t)p->cx_bytes,
+                                static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
+        const bool dual = p->ab == GEMM_DF16;
+        uint8_t *ws = static_cast<uint8_t *>(p->cx_ws);
+        const int64_t na = p->batch > 1 && p->stride_a ? p->batch : 1;
+        const int64_t nbb = p->batch > 1 && p->stride_b ? p->batch : 1;
+        tge::PairJob ja = {}, jb = {};
+        const void *Ar = A;
+        if (p->op_a == GEMM_OP_T) {
+            ja = {static_cast<const uint8_t *>(A), ws, p->K, p->M, p->lda * 4, p->cx_ld_a * 2,
+                  p->stride_a * 4, 2 * p->K * p->cx_ld_a * 2, na, tge::PAIR_PARTS, dual};
+            Ar = ws;
+        }
+        const bool bn = p->op_b == GEMM_OP_N;
+        const int64_t rows_b = bn ? p->K : p->N;
+        jb = {static_cast<const uint8_t *>(B), ws + p->cx_off_b, rows_b, bn ? p->N : p->K, p->ldb * 4,
+              p->cx_ld_b * 2, p->stride_b * 4, 2 * rows_b * p->cx_ld_b * 2, nbb,
+              bn ? tge::PAIR_BLOCK_N : tge::PAIR_BLOCK_T, dual};
+        if (tge::pair_launch(ja, jb, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return GEMM_STATUS_HIP_ERROR;
+        return gemm_run(p->cx, Ar, ws + p->cx_off_b, C, D, nullptr, alpha, beta, stream);
+    }
 
     GemmParams prm;
     prm.A = A; prm.B = B; prm.C = C; prm.D = D; prm.bias = bias;

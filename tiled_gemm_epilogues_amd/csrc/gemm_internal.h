@@ -82,6 +82,27 @@ struct RepackJob {
 int64_t repack_blocks(const RepackJob &j);
 hipError_t repack_launch(const RepackJob &a, const RepackJob &b, hipStream_t stream);
 
+// Complex / dual operands with fp16 parts rewritten as real fp16 matrices for the real kernels
+// (gemm_repack.hip).  Source row r of product b holds `numbers` numbers (4 bytes each: real
+// part low, other part high) at src + b * src_stride + r * src_pitch; it becomes destination
+// rows 2r and 2r+1 at dst + b * dst_stride + (2r + h) * dst_pitch (bytes; dst_pitch a multiple
+// of 16, zero-padded past the data):
+//   PAIR_PARTS    row 2r: the real parts, row 2r+1: the other parts (numbers fp16 values each)
+//   PAIR_BLOCK_N  row 2r: (re, im) pairs as stored, row 2r+1: (-im, re) pairs, dual (0, re)
+//   PAIR_BLOCK_T  row 2r: (re, -im) pairs, dual (re, 0), row 2r+1: (im, re) pairs
+// A complex product is then a real one: with op(A) read as M x 2K reals (parts interleaved
+// along K) and each number b of op(B) replaced by the 2 x 2 block [re im; -im re] (dual:
+// [re im; 0 re]), D read as M x 2N reals is op(A) times the 2K x 2N block matrix.
+enum PairMode { PAIR_PARTS = 0, PAIR_BLOCK_N = 1, PAIR_BLOCK_T = 2 };
+struct PairJob {
+    const uint8_t *src;
+    uint8_t *dst;
+    int64_t rows, numbers, src_pitch, dst_pitch, src_stride, dst_stride, batch;
+    int mode, dual;
+};
+int64_t pair_blocks(const PairJob &j);
+hipError_t pair_launch(const PairJob &a, const PairJob &b, hipStream_t stream);
+
 // Complex and dual GEMM (gemm_complex.hip): fp16 parts, fp32 accumulation, 128x128 tile.
 const KernelEntry *complex_cf16_cf32(int op_a, int op_b);
 const KernelEntry *complex_cf16_cf16(int op_a, int op_b);

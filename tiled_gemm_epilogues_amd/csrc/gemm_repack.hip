@@ -9,6 +9,12 @@
 // loads ("Ragged" in the Julia GemmKernels design, "Layout modularity"); on gfx950 one
 // streaming copy costs less than narrow or register-staged loads inside the pipelined loop.
 //
+// Complex and dual numbers (fp16 parts) on large shapes are rewritten here as real matrices so
+// that the real fast kernel computes their product (pair_rows): "Flexible Performant GEMM
+// Kernels on GPUs" (section 5.4) builds these GEMMs from four real products of the parts; the
+// same four products are the 2 x 2 real block [re im; -im re] that replaces each number of
+// op(B) (dual numbers: [re im; 0 re]), with op(A) read as reals whose parts alternate along K.
+//
 // The copy is byte-exact (any element type): row r of product b goes from
 // src + b * src_stride + r * src_pitch (row_bytes bytes) to dst + b * dst_stride + r * dst_pitch,
 // followed by zeros up to dst_pitch.  One wave copies 64 consecutive chunks (1 KiB) of one row;
@@ -24,6 +30,8 @@ namespace tge {
 namespace {
 
 using namespace dev;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int RP_ROWS = 4;     // rows per workgroup (one wave each)
 constexpr int RP_CHUNKS = 64;  // 16-byte chunks per wave
@@ -60,9 +68,86 @@ uint32_t job_blocks(const RepackJob &j) {
     return (uint32_t)(cblk * rblk * j.batch);
 }
 
+// ---- complex and dual operands as real matrices -----------------------------------------------
+// A number is one dword: real part in the low half, imaginary (or dual) part in the high half.
+// A thread takes 4 consecutive numbers of a source row (a 16-byte load; numbers past the row
+// read as 0) and writes its share of the two destination rows 2r and 2r+1.
+
+constexpr uint32_t SIGN_LO = 0x8000u, SIGN_HI = 0x80000000u;
+
+__device__ __forceinline__ void pair_block(const PairJob &j, uint32_t blk, int wave, int lane) {
+    const int gb = j.mode == PAIR_PARTS ? 8 : 16;                 // destination bytes per group
+    const uint32_t cblk = (uint32_t)((j.dst_pitch / gb + RP_CHUNKS - 1) / RP_CHUNKS);
+    const uint32_t rblk = (uint32_t)((j.rows + RP_ROWS - 1) / RP_ROWS);
+    const uint32_t prod = blk / (cblk * rblk);
+    const uint32_t rem = blk - prod * cblk * rblk;
+    const uint32_t rb = rem / cblk, cb = rem - rb * cblk;
+    const int64_t r = (int64_t)rb * RP_ROWS + wave;
+    const int64_t g = (int64_t)cb * RP_CHUNKS + lane;              // group of 4 numbers
+    if (r >= j.rows || g * gb >= j.dst_pitch) return;
+    const uint8_t *s = j.src + (int64_t)prod * j.src_stride + r * j.src_pitch + g * 16;
+    const int64_t left = j.numbers - 4 * g;
+    u32x4 v = {0, 0, 0, 0};
+    if (left >= 4) v = ldg16(s);
+    else if (left > 0) v = ldg16_partial<4>(s, (int)left);
+    uint8_t *d0 = j.dst + (int64_t)prod * j.dst_stride + 2 * r * j.dst_pitch + g * gb;
+    uint8_t *d1 = d0 + j.dst_pitch;
+    if (j.mode == PAIR_PARTS) {
+        // row 2r: the four real parts; row 2r+1: the four other parts
+        u32x2 re, im;
+        re[0] = (v[0] & 0xFFFFu) | (v[1] << 16);
+        re[1] = (v[2] & 0xFFFFu) | (v[3] << 16);
+        im[0] = (v[0] >> 16) | (v[1] & 0xFFFF0000u);
+        im[1] = (v[2] >> 16) | (v[3] & 0xFFFF0000u);
+        *reinterpret_cast<u32x2 *>(d0) = re;
+        *reinterpret_cast<u32x2 *>(d1) = im;
+        return;
+    }
+    u32x4 w0, w1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = v[i];
+        const uint32_t swapped = (x >> 16) | (x << 16);            // (im, re)
+        if (j.mode == PAIR_BLOCK_N) {
+            // row 2k: (re, im) as stored; row 2k+1: (-im, re), dual (0, re)
+            w0[i] = x;
+            w1[i] = j.dual ? (x << 16) : (swapped ^ SIGN_LO);
+        } else {
+            // row 2n: (re, -im), dual (re, 0); row 2n+1: (im, re)
+            w0[i] = j.dual ? (x & 0xFFFFu) : (x ^ SIGN_HI);
+            w1[i] = swapped;
+        }
+    }
+    *reinterpret_cast<u32x4 *>(d0) = w0;
+    *reinterpret_cast<u32x4 *>(d1) = w1;
+}
+
+__global__ __launch_bounds__(RP_ROWS * 64) void pair_rows(PairJob a, PairJob b, uint32_t blocks_a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (blockIdx.x < blocks_a) pair_block(a, blockIdx.x, wave, lane);
+    else pair_block(b, blockIdx.x - blocks_a, wave, lane);
+}
+
+uint32_t pair_job_blocks(const PairJob &j) {
+    if (j.rows <= 0 || j.batch <= 0) return 0;
+    const int gb = j.mode == PAIR_PARTS ? 8 : 16;
+    const int64_t cblk = (j.dst_pitch / gb + RP_CHUNKS - 1) / RP_CHUNKS;
+    const int64_t rblk = (j.rows + RP_ROWS - 1) / RP_ROWS;
+    return (uint32_t)(cblk * rblk * j.batch);
+}
+
 }  // namespace
 
 int64_t repack_blocks(const RepackJob &j) { return job_blocks(j); }
+
+int64_t pair_blocks(const PairJob &j) { return pair_job_blocks(j); }
+
+hipError_t pair_launch(const PairJob &a, const PairJob &b, hipStream_t stream) {
+    const uint32_t na = pair_job_blocks(a), nb = pair_job_blocks(b);
+    if (na + nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(pair_rows, dim3(na + nb), dim3(RP_ROWS * 64), 0, stream, a, b, na);
+    return hipGetLastError();
+}
 
 hipError_t repack_launch(const RepackJob &a, const RepackJob &b, hipStream_t stream) {
     const uint32_t na = job_blocks(a), nb = job_blocks(b);
