@@ -30,6 +30,7 @@ struct gemm_plan {
     const KernelEntry *fast_pk;      // nullptr: no repacking for this plan
     int pk_need;                     // bit 0 / bit 1: A / B always copied (ld, stride or extent)
     int64_t pk_ld_a, pk_ld_b;        // leading dimensions of the copies (whole 16-byte chunks)
+    int64_t pk_kpad;                 // K rounded up to whole slabs: the copies are zero there
     int64_t pk_off_b, pk_bytes;      // byte offset of B's copy in the workspace, total size
     int pk_dev;                      // device of the copy workspace (-1: none yet)
     void *pk_ws;
@@ -339,10 +340,14 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // (TGE_FORCE_KERNEL=staged keeps the register-staged variant for such operands)
     const KernelEntry *fast_pk = nullptr;
     int pk_need = 0;
-    int64_t pk_ld_a = 0, pk_ld_b = 0, pk_off_b = 0, pk_bytes = 0;
+    int64_t pk_ld_a = 0, pk_ld_b = 0, pk_off_b = 0, pk_bytes = 0, pk_kpad = 0;
     if (ft && want_fast && K >= 128 / eab && !diag_a && !diag_b && !staged) {
-        const int64_t rows_a = op_a == GEMM_OP_N ? M : K, len_a = op_a == GEMM_OP_N ? K : M;
-        const int64_t rows_b = op_b == GEMM_OP_N ? K : N, len_b = op_b == GEMM_OP_N ? N : K;
+        // the copies hold K rounded up to whole slabs, zero past K: when both operands are
+        // copied the kernel runs on that K and needs no guarded tail slab
+        const int64_t slab = 128 / eab;
+        pk_kpad = (K + slab - 1) / slab * slab;
+        const int64_t rows_a = op_a == GEMM_OP_N ? M : pk_kpad, len_a = op_a == GEMM_OP_N ? pk_kpad : M;
+        const int64_t rows_b = op_b == GEMM_OP_N ? pk_kpad : N, len_b = op_b == GEMM_OP_N ? N : pk_kpad;
         pk_ld_a = (len_a + ve - 1) / ve * ve;
         pk_ld_b = (len_b + ve - 1) / ve * ve;
         // a batch stride of 0 shares the operand between products: one copy
@@ -440,6 +445,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->fast_pk = fast_pk;
     p->pk_need = pk_need;
     p->pk_ld_a = pk_ld_a; p->pk_ld_b = pk_ld_b;
+    p->pk_kpad = pk_kpad;
     p->pk_off_b = pk_off_b; p->pk_bytes = pk_bytes;
     p->pk_dev = -1;
     p->pk_ws = nullptr;
@@ -578,24 +584,32 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
         const bool sh_a = p->batch > 1 && p->stride_a, sh_b = p->batch > 1 && p->stride_b;
         tge::RepackJob ja = {}, jb = {};
         uint8_t *ws = static_cast<uint8_t *>(p->pk_ws);
+        // stored rows of the copies: K-major operands get pk_kpad rows, the extra ones zero
         if (need & 1) {
-            const int64_t rows = p->op_a == GEMM_OP_N ? p->M : p->K, len = p->op_a == GEMM_OP_N ? p->K : p->M;
-            ja = {static_cast<const uint8_t *>(A), ws, rows, len * eab, p->lda * eab, p->pk_ld_a * eab,
-                  p->stride_a * eab, rows * p->pk_ld_a * eab, sh_a ? p->batch : 1};
+            const bool an = p->op_a == GEMM_OP_N;
+            const int64_t rows = an ? p->M : p->K, rows_out = an ? p->M : p->pk_kpad;
+            const int64_t len = an ? p->K : p->M;
+            ja = {static_cast<const uint8_t *>(A), ws, rows, rows_out, len * eab, p->lda * eab,
+                  p->pk_ld_a * eab, p->stride_a * eab, rows_out * p->pk_ld_a * eab, sh_a ? p->batch : 1};
             prm.A = ws;
             prm.lda = (int)p->pk_ld_a;
-            prm.stride_a = sh_a ? rows * p->pk_ld_a : 0;
+            prm.stride_a = sh_a ? rows_out * p->pk_ld_a : 0;
         }
         if (need & 2) {
-            const int64_t rows = p->op_b == GEMM_OP_N ? p->K : p->N, len = p->op_b == GEMM_OP_N ? p->N : p->K;
-            jb = {static_cast<const uint8_t *>(B), ws + p->pk_off_b, rows, len * eab, p->ldb * eab,
-                  p->pk_ld_b * eab, p->stride_b * eab, rows * p->pk_ld_b * eab, sh_b ? p->batch : 1};
+            const bool bn = p->op_b == GEMM_OP_N;
+            const int64_t rows = bn ? p->K : p->N, rows_out = bn ? p->pk_kpad : p->N;
+            const int64_t len = bn ? p->N : p->K;
+            jb = {static_cast<const uint8_t *>(B), ws + p->pk_off_b, rows, rows_out, len * eab,
+                  p->ldb * eab, p->pk_ld_b * eab, p->stride_b * eab, rows_out * p->pk_ld_b * eab,
+                  sh_b ? p->batch : 1};
             prm.B = ws + p->pk_off_b;
             prm.ldb = (int)p->pk_ld_b;
-            prm.stride_b = sh_b ? rows * p->pk_ld_b : 0;
+            prm.stride_b = sh_b ? rows_out * p->pk_ld_b : 0;
         }
         if (tge::repack_launch(ja, jb, static_cast<hipStream_t>(stream)) != hipSuccess)
             return GEMM_STATUS_HIP_ERROR;
+        // both operands from the copies: the products past K are 0 * 0, no tail slab
+        if (need == 3) prm.K = (int)p->pk_kpad;
         k = p->fast_pk;
     } else if (p->fast_rs) k = p->fast_rs;
     const bool sk = k == p->fast && p->fast_is_skinny;

@@ -69,15 +69,16 @@ const KernelEntry *fast_bf16_f32(int op_a, int op_b, int rs);
 const KernelEntry *fast_i8_i32(int op_a, int op_b, int rs);
 
 // Byte-exact copy of an operand into rows that are 16-byte aligned and zero-padded to whole
-// 16-byte chunks (gemm_repack.hip), for operands the direct loads cannot take: row r of product
-// b goes from src + b * src_stride + r * src_pitch (row_bytes bytes) to
-// dst + b * dst_stride + r * dst_pitch (all in bytes; dst, dst_pitch and dst_stride multiples of
-// 16, dst_pitch >= row_bytes).  repack_launch copies a and b (rows == 0: no job) in one launch;
-// the caller keeps the total of repack_blocks below 2^31.
+// 16-byte chunks (gemm_repack.hip), for operands the direct loads cannot take: row r < rows of
+// product b goes from src + b * src_stride + r * src_pitch (row_bytes bytes) to
+// dst + b * dst_stride + r * dst_pitch, rows rows .. rows_out - 1 are written as zeros (all in
+// bytes; dst, dst_pitch and dst_stride multiples of 16, dst_pitch >= row_bytes, rows_out >=
+// rows).  repack_launch copies a and b (rows_out == 0: no job) in one launch; the caller keeps
+// the total of repack_blocks below 2^31.
 struct RepackJob {
     const uint8_t *src;
     uint8_t *dst;
-    int64_t rows, row_bytes, src_pitch, dst_pitch, src_stride, dst_stride, batch;
+    int64_t rows, rows_out, row_bytes, src_pitch, dst_pitch, src_stride, dst_stride, batch;
 };
 int64_t repack_blocks(const RepackJob &j);
 hipError_t repack_launch(const RepackJob &a, const RepackJob &b, hipStream_t stream);

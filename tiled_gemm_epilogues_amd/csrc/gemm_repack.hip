@@ -17,7 +17,8 @@
 //
 // The copy is byte-exact (any element type): row r of product b goes from
 // src + b * src_stride + r * src_pitch (row_bytes bytes) to dst + b * dst_stride + r * dst_pitch,
-// followed by zeros up to dst_pitch.  One wave copies 64 consecutive chunks (1 KiB) of one row;
+// followed by zeros up to dst_pitch; rows past the source's (K rounded up to whole slabs, for
+// an operand stored K-major) are zeros.  One wave copies 64 consecutive chunks (1 KiB) of one row;
 // a workgroup covers 4 rows.
 
 #include <hip/hip_runtime.h>
@@ -39,15 +40,16 @@ constexpr int RP_CHUNKS = 64;  // 16-byte chunks per wave
 __device__ __forceinline__ void repack_block(const RepackJob &j, uint32_t blk, int wave, int lane) {
     // workgroup blk -> (product, block of 4 rows, block of 64 chunks); uniform divisions
     const uint32_t cblk = (uint32_t)((j.dst_pitch / 16 + RP_CHUNKS - 1) / RP_CHUNKS);
-    const uint32_t rblk = (uint32_t)((j.rows + RP_ROWS - 1) / RP_ROWS);
+    const uint32_t rblk = (uint32_t)((j.rows_out + RP_ROWS - 1) / RP_ROWS);
     const uint32_t prod = blk / (cblk * rblk);
     const uint32_t rem = blk - prod * cblk * rblk;
     const uint32_t rb = rem / cblk, cb = rem - rb * cblk;
     const int64_t r = (int64_t)rb * RP_ROWS + wave;
     const int64_t c = (int64_t)cb * RP_CHUNKS + lane;
-    if (r >= j.rows || c * 16 >= j.dst_pitch) return;
+    if (r >= j.rows_out || c * 16 >= j.dst_pitch) return;
     const uint8_t *s = j.src + (int64_t)prod * j.src_stride + r * j.src_pitch + c * 16;
-    const int64_t left = j.row_bytes - c * 16;   // bytes of the source row from this chunk on
+    // bytes of the source row from this chunk on (none in the zero rows past `rows`)
+    const int64_t left = r < j.rows ? j.row_bytes - c * 16 : 0;
     u32x4 v = {0, 0, 0, 0};
     if (left >= 16) v = ldg16(s);
     else if (left > 0) v = ldg16_partial<1>(s, (int)left);
@@ -62,9 +64,9 @@ __global__ __launch_bounds__(RP_ROWS * 64) void repack_rows(RepackJob a, RepackJ
 }
 
 uint32_t job_blocks(const RepackJob &j) {
-    if (j.rows <= 0 || j.batch <= 0) return 0;
+    if (j.rows_out <= 0 || j.batch <= 0) return 0;
     const int64_t cblk = (j.dst_pitch / 16 + RP_CHUNKS - 1) / RP_CHUNKS;
-    const int64_t rblk = (j.rows + RP_ROWS - 1) / RP_ROWS;
+    const int64_t rblk = (j.rows_out + RP_ROWS - 1) / RP_ROWS;
     return (uint32_t)(cblk * rblk * j.batch);
 }
 
