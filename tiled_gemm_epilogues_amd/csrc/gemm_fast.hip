@@ -192,38 +192,46 @@ struct Loader {
 
 // Guarded staging of a partial slab (k0 .. K-1, zero beyond) into the same LDS layout, with the
 // load transform xf applied (register-staged kernels; the others transform their fragments).
+// fetch() issues all of this thread's loads (8 chunks of 16 bytes; both operands' fetches go
+// out before the barrier that frees the stage), put() writes them to LDS.
 template <int E, bool KC, int MF>
-__device__ __forceinline__ void stage_tail(const uint8_t *base, int ld, int row0, int ext, int k0, int K, uint8_t *dst,
-                                           int tid, int xf) {
-    constexpr int VE = 16 / E;
-    // 2048 chunks of 16 bytes per operand slab, 8 per thread (unrolled: the loads go out together)
+struct TailStage {
+    static constexpr int VE = 16 / E;
+    static constexpr int CPR = 16 * E;   // chunks per [k] row of an M/N-contiguous slab
+    u32x4 v[8];
+
+    __device__ __forceinline__ void fetch(const uint8_t *base, int ld, int row0, int ext, int k0, int K, int tid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = tid + NT * i;
-        const uint8_t *p;
-        int nval;          // leading elements of the chunk inside the operand (0 .. VE)
-        uint32_t off;      // LDS byte offset of the chunk
-        if constexpr (KC) {
-            const int r = q >> 3, c = q & 7;
-            p = base + ((size_t)min(row0 + r, ext - 1) * ld + k0 + c * VE) * E;
-            nval = K - (k0 + c * VE);
-            off = off_kc(r, c);
-        } else {
-            constexpr int CPR = 16 * E;
-            const int k = q / CPR, c = q % CPR;
-            const int col = row0 + c * VE;
-            p = base + ((size_t)(k0 + k) * ld + col) * E;
-            // elements past the M/N edge are zero (their products are never stored)
-            nval = k0 + k < K ? ext - col : 0;
-            off = off_mc<E, MF>(k, c);
+        for (int i = 0; i < 8; ++i) {
+            const int q = tid + NT * i;
+            const uint8_t *p;
+            int nval;          // leading elements of the chunk inside the operand (0 .. VE)
+            if constexpr (KC) {
+                const int r = q >> 3, c = q & 7;
+                p = base + ((size_t)min(row0 + r, ext - 1) * ld + k0 + c * VE) * E;
+                nval = K - (k0 + c * VE);
+            } else {
+                const int k = q / CPR, c = q % CPR;
+                const int col = row0 + c * VE;
+                p = base + ((size_t)(k0 + k) * ld + col) * E;
+                // elements past the M/N edge are zero (their products are never stored)
+                nval = k0 + k < K ? ext - col : 0;
+            }
+            v[i] = u32x4{0, 0, 0, 0};
+            if (nval >= VE) v[i] = ldg16(p);
+            else if (nval > 0) v[i] = ldg16_partial<E>(p, nval);
         }
-        u32x4 v = {0, 0, 0, 0};
-        if (nval >= VE) v = ldg16(p);
-        else if (nval > 0) v = ldg16_partial<E>(p, nval);
-        v = zero_negative<E>(v, xf);
-        __builtin_memcpy(dst + off, &v, 16);
     }
-}
+    __device__ __forceinline__ void put(uint8_t *dst, int tid, int xf) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = tid + NT * i;
+            const uint32_t off = KC ? off_kc(q >> 3, q & 7) : off_mc<E, MF>(q / CPR, q % CPR);
+            const u32x4 w = zero_negative<E>(v[i], xf);
+            __builtin_memcpy(dst + off, &w, 16);
+        }
+    }
+};
 
 // ---- fragment reads ---------------------------------------------------------------------------
 // MF = 32 (MFMA 32x32, k-slice of 32 bytes of K): fragment (sub-tile t, k-slice j) gives lane l
@@ -723,9 +731,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     // K tail: one guarded slab through registers (zero fill past K), in stage 0
     const int k0 = nfull * BKE;
     if (k0 < p.K) {
+        TailStage<E, AK, MF> ta;
+        TailStage<E, BK, MF> tb;
+        ta.fetch(A, p.lda, m0, p.M, k0, p.K, tid);
+        tb.fetch(B, p.ldb, n0, p.N, k0, p.K, tid);
         __syncthreads();
-        stage_tail<E, AK, MF>(A, p.lda, m0, p.M, k0, p.K, smem, tid, RS ? p.xform_a : 0);
-        stage_tail<E, BK, MF>(B, p.ldb, n0, p.N, k0, p.K, smem + OPND, tid, RS ? p.xform_b : 0);
+        ta.put(smem, tid, RS ? p.xform_a : 0);
+        tb.put(smem + OPND, tid, RS ? p.xform_b : 0);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NS; ++j) {   // the k-slices of the slab
