@@ -1,7 +1,9 @@
 """GPU parity of the load transforms (gemm_plan_create_desc: ReLU on op(A), op(B) and C as they
 are loaded) against the oracle: bit-exact on exact-integer inputs (which hold negatives, so
 every transform changes the result) through the fast, general and skinny kernels, in every
-layout, alone and together with a strided batch."""
+layout, alone and together with a strided batch.  The fast path is covered both ways: the
+operand transforms applied by the aligned copy before the kernel ("fast"), and fused into the
+kernel's loads ("staged": no copies)."""
 import numpy as np
 import pytest
 import torch
@@ -41,6 +43,9 @@ CASES = [
     ("fast", 304, 520, 200, "f16", "f16", "bias_relu", 1.0, 1.0),
     ("fast", 512, 264, 128, "bf16", "f32", "bias", 2.0, -1.0),
     ("fast", 304, 528, 208, "i8", "i32", "bias", 1.0, 1.0),
+    ("staged", 304, 520, 200, "f16", "f16", "bias_relu", 1.0, 1.0),
+    ("staged", 512, 264, 128, "bf16", "f32", "bias", 2.0, -1.0),
+    ("staged", 304, 528, 208, "i8", "i32", "bias", 1.0, 1.0),
     ("general", 200, 136, 150, "f32", "f32", "relu", 0.5, 0.5),
     ("general", 130, 70, 90, "bf16", "bf16", "bias", -1.0, 1.0),
     ("general", 96, 80, 300, "i8", "i32", "bias_relu", 1.0, 1.0),
@@ -57,9 +62,15 @@ def test_transforms_exact(case, lay, xf, monkeypatch):
     p = _problem(M, N, K, lay, ab, cd, epi, alpha, beta, (130, i), XFORMS[xf])
     x = synth.make_inputs(p)
     D, pl = run(p, x)
-    assert ("gemm_fast" in pl.describe()) == (kern == "fast"), pl.describe()
+    assert ("gemm_fast" in pl.describe()) == (kern != "general"), pl.describe()
     assert "relu-in" in pl.describe()
+    # the copy applies the operand transforms (aligned operands are copied only for them)
+    copies = kern == "fast" and "relu" in XFORMS[xf][:2]
+    assert (" repack " in pl.describe()) == copies, pl.describe()
     check(p, x, D, reference(p, x), exact=True)
+    # a pointer one element off: copied (and transformed) at run time, or register-staged
+    D2, _ = run(p, x, offset=1)
+    check(p, x, D2, reference(p, x), exact=True)
 
 
 @pytest.mark.parametrize("xf", range(len(XFORMS)))

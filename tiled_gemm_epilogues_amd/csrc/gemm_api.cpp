@@ -467,8 +467,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if (sp > 64) sp = 64;
         p->ksplit = sp > 1 ? (int)sp : 1;
     }
-    // a plan that always copies an operand shows the direct kernel on the copies
-    const bool shows_pk = !fast && fast_pk && pk_need;
+    // a plan that always copies an operand (off the 16-byte grid, or carrying a load transform
+    // that the copy applies) shows the direct kernel on the copies
+    const int pk_shown = fast_pk ? (pk_need | (desc->transform_a ? 1 : 0) | (desc->transform_b ? 2 : 0)) : 0;
+    const bool shows_pk = pk_shown != 0;
     const KernelEntry *shown = fast ? fast : shows_pk ? fast_pk : fast_rs ? fast_rs : k;
     p->tiles_m = skinny ? p->ksplit : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
@@ -485,8 +487,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
     if (p->ksplit > 1) bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " ksplit %d", p->ksplit);
     if (shows_pk)
-        bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " repack %s%s", pk_need & 1 ? "A" : "",
-                       pk_need & 2 ? "B" : "");
+        bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " repack %s%s", pk_shown & 1 ? "A" : "",
+                       pk_shown & 2 ? "B" : "");
     if (diag_a || diag_b)
         bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " diag %s%s", diag_a ? "A" : "", diag_b ? "B" : "");
     if (desc->transform_a || desc->transform_b || desc->transform_c)
@@ -576,8 +578,12 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     // read in place is copied first when the plan repacks (and its workspace exists or can be
     // allocated now); else the register-staged kernel runs when the plan has it, else the
     // general kernel
-    const int need = (p->pk_need | (((uintptr_t)A % 16) ? 1 : 0) | (((uintptr_t)B % 16) ? 2 : 0)) &
-                     (p->K > 0 ? 3 : 0);
+    // operands the direct loads cannot read in place, and operands whose load transform the
+    // copy applies (so that the kernel runs its untransformed 16x16 schedule)
+    const int kk = p->K > 0 ? 3 : 0;
+    const int unaligned = (p->pk_need | (((uintptr_t)A % 16) ? 1 : 0) | (((uintptr_t)B % 16) ? 2 : 0)) & kk;
+    const int xf = ((p->xform_a ? 1 : 0) | (p->xform_b ? 2 : 0)) & kk;
+    const int need = unaligned | (p->fast_pk ? xf : 0);
     if (p->fast && !need) k = p->fast;
     else if (p->fast_pk && need && repack_workspace(p, static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
         const int eab = elem_bytes(p->ab);
@@ -590,7 +596,9 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
             const int64_t rows = an ? p->M : p->K, rows_out = an ? p->M : p->pk_kpad;
             const int64_t len = an ? p->K : p->M;
             ja = {static_cast<const uint8_t *>(A), ws, rows, rows_out, len * eab, p->lda * eab,
-                  p->pk_ld_a * eab, p->stride_a * eab, rows_out * p->pk_ld_a * eab, sh_a ? p->batch : 1};
+                  p->pk_ld_a * eab, p->stride_a * eab, rows_out * p->pk_ld_a * eab, sh_a ? p->batch : 1,
+                  p->xform_a ? eab : 0};
+            prm.xform_a = 0;
             prm.A = ws;
             prm.lda = (int)p->pk_ld_a;
             prm.stride_a = sh_a ? rows_out * p->pk_ld_a : 0;
@@ -601,7 +609,8 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
             const int64_t len = bn ? p->N : p->K;
             jb = {static_cast<const uint8_t *>(B), ws + p->pk_off_b, rows, rows_out, len * eab,
                   p->ldb * eab, p->pk_ld_b * eab, p->stride_b * eab, rows_out * p->pk_ld_b * eab,
-                  sh_b ? p->batch : 1};
+                  sh_b ? p->batch : 1, p->xform_b ? eab : 0};
+            prm.xform_b = 0;
             prm.B = ws + p->pk_off_b;
             prm.ldb = (int)p->pk_ld_b;
             prm.stride_b = sh_b ? rows_out * p->pk_ld_b : 0;
@@ -611,7 +620,11 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
         // both operands from the copies: the products past K are 0 * 0, no tail slab
         if (need == 3) prm.K = (int)p->pk_kpad;
         k = p->fast_pk;
-    } else if (p->fast_rs) k = p->fast_rs;
+    } else if (p->fast && !unaligned) {
+        k = p->fast;              // no workspace: the direct loads with the transforms fused
+    } else if (p->fast_rs) {
+        k = p->fast_rs;
+    }
     const bool sk = k == p->fast && p->fast_is_skinny;
     prm.tiles_m = sk ? p->ksplit : (int)((p->M + k->bm - 1) / k->bm);
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);

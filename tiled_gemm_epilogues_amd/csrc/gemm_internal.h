@@ -75,10 +75,13 @@ const KernelEntry *fast_i8_i32(int op_a, int op_b, int rs);
 // bytes; dst, dst_pitch and dst_stride multiples of 16, dst_pitch >= row_bytes, rows_out >=
 // rows).  repack_launch copies a and b (rows_out == 0: no job) in one launch; the caller keeps
 // the total of repack_blocks below 2^31.
+// With xf_elem = 1 or 2 the copy also applies the load transform GEMM_TRANSFORM_RELU to
+// elements of that many bytes (every element whose sign bit is set becomes +0).
 struct RepackJob {
     const uint8_t *src;
     uint8_t *dst;
     int64_t rows, rows_out, row_bytes, src_pitch, dst_pitch, src_stride, dst_stride, batch;
+    int xf_elem;
 };
 int64_t repack_blocks(const RepackJob &j);
 hipError_t repack_launch(const RepackJob &a, const RepackJob &b, hipStream_t stream);

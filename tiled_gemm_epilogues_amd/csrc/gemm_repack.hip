@@ -15,7 +15,12 @@
 // same four products are the 2 x 2 real block [re im; -im re] that replaces each number of
 // op(B) (dual numbers: [re im; 0 re]), with op(A) read as reals whose parts alternate along K.
 //
-// The copy is byte-exact (any element type): row r of product b goes from
+// A plan with a load transform (ReLU as loaded) on op(A) or op(B) copies that operand too and
+// applies the transform in the copy: the fast kernel's 16x16 MFMA schedule has no registers to
+// spare for transforming fragments, and one streaming pass costs less than the 32x32 schedule
+// that can.
+//
+// The copy is byte-exact (any element type) unless it carries the transform: row r of product b goes from
 // src + b * src_stride + r * src_pitch (row_bytes bytes) to dst + b * dst_stride + r * dst_pitch,
 // followed by zeros up to dst_pitch; rows past the source's (K rounded up to whole slabs, for
 // an operand stored K-major) are zeros.  One wave copies 64 consecutive chunks (1 KiB) of one row;
@@ -53,6 +58,9 @@ __device__ __forceinline__ void repack_block(const RepackJob &j, uint32_t blk, i
     u32x4 v = {0, 0, 0, 0};
     if (left >= 16) v = ldg16(s);
     else if (left > 0) v = ldg16_partial<1>(s, (int)left);
+    // the load transform, when the copy carries it (branch-free on the uniform xf_elem)
+    v = zero_negative<2>(v, j.xf_elem == 2);
+    v = zero_negative<1>(v, j.xf_elem == 1);
     *reinterpret_cast<u32x4 *>(j.dst + (int64_t)prod * j.dst_stride + r * j.dst_pitch + c * 16) = v;
 }
 
