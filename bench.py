@@ -20,7 +20,9 @@ the 256 MB infinity cache; the cache-hot figure of one reused set is reported be
 roofline.traffic is the measured HBM traffic per launch (FETCH_SIZE + WRITE_SIZE from rocprofv3,
 each scaled by what the same counter reads for a plain copy of known size), taken from the
 summary profiles/traffic_<workload>.json when that summary was measured on the current kernel
-sources (it records their hash); otherwise null.
+sources (it records their hash); otherwise null.  clocks holds rocm-smi's core and memory clock
+readings just before the warm-up and right after the timed launches (the clock the kernel ran at
+on average comes from the counters in profiles/).
 """
 import argparse
 import hashlib
@@ -123,6 +125,30 @@ def cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+def gpu_clocks():
+    """Current GPU core (sclk) and memory (mclk) clocks in MHz from rocm-smi, run as a child
+    process (None when it is not available)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        cards = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    out = {}
+    for card, fields in cards.items():
+        if not isinstance(fields, dict):
+            continue
+        clk = {}
+        for key, val in fields.items():
+            for name in ("sclk", "mclk"):
+                if key.startswith(name) and "speed" in key:
+                    digits = "".join(ch for ch in str(val) if ch.isdigit())
+                    clk[name + "_MHz"] = int(digits) if digits else None
+        out[card] = clk
+    return out or None
 
 
 def pick_workload(spec):
@@ -236,7 +262,11 @@ def main():
         return ev0.elapsed_time(ev1) / max(1, args.steps), wall * 1e3 / max(1, args.steps)
 
     base = (A, B, C, D, bias)
+    clocks = {"before": gpu_clocks()}
     ms_hot, ms_wall = time_launches([base])
+    # right after the timed launches (the clock reading comes from sysfs a moment later)
+    clocks["after"] = gpu_clocks()
+    log(f"[bench] clocks before / after the timed launches: {clocks}")
     log(f"[bench] {args.steps} steps: {ms_hot:.4f} ms/launch (events), {ms_wall:.4f} ms/step (wall)")
     ms_events, hot = ms_hot, None
     if hbm_bound:
@@ -344,6 +374,7 @@ def main():
                    "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4),
                    "launch": "eager" if graph is None else f"one HIP graph of {args.steps} launches"},
         "roofline": roof,
+        "clocks": clocks,
         "cpu_baseline": cpu,
         "parity": parity,
     }
