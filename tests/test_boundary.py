@@ -273,3 +273,16 @@ def test_diagonal_kernels_described():
     assert "gemm_diag_cols" in d and "diag B" in d, d
     d = tge.Plan(512, 512, 512, "N", "N", kind_a="diagonal", kind_b="diagonal").describe()
     assert "gemm_diag_rows" in d and "diag AB" in d, d
+
+
+def test_transform_copies_only_for_the_fast_kernel():
+    # the fast path copies an operand to apply its load transform; a skinny plan applies it in
+    # its own kernel (also when a batch makes the fast kernel eligible too)
+    d = tge.Plan(8192, 8192, 8192, "N", "N", transform_a="relu", transform_c="relu").describe()
+    assert "gemm_fast_256x256 " in d and "repack A " in d and "relu-in AC" in d, d
+    d = tge.Plan(64, 4096, 4096, "N", "N", batch=64, stride_a=64 * 4096, stride_b=0,
+                 stride_c=64 * 4096, transform_a="relu").describe()
+    assert "gemm_skinny" in d and "repack" not in d, d
+    # only C transformed: nothing to copy
+    d = tge.Plan(8192, 8192, 8192, "N", "N", transform_c="relu").describe()
+    assert "repack" not in d, d

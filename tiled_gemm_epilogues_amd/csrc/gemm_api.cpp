@@ -469,7 +469,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     }
     // a plan that always copies an operand (off the 16-byte grid, or carrying a load transform
     // that the copy applies) shows the direct kernel on the copies
-    const int pk_shown = fast_pk ? (pk_need | (desc->transform_a ? 1 : 0) | (desc->transform_b ? 2 : 0)) : 0;
+    // (a skinny plan applies its transforms in its own kernel)
+    const int pk_shown = fast_pk && !skinny ? (pk_need | (desc->transform_a ? 1 : 0) | (desc->transform_b ? 2 : 0)) : 0;
     const bool shows_pk = pk_shown != 0;
     const KernelEntry *shown = fast ? fast : shows_pk ? fast_pk : fast_rs ? fast_rs : k;
     p->tiles_m = skinny ? p->ksplit : (int)((M + shown->bm - 1) / shown->bm);
@@ -574,16 +575,16 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
     prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
     const KernelEntry *k = p->kernel;
-    // the direct-load fast kernel needs 16-byte aligned operand pointers; an operand it cannot
-    // read in place is copied first when the plan repacks (and its workspace exists or can be
-    // allocated now); else the register-staged kernel runs when the plan has it, else the
-    // general kernel
-    // operands the direct loads cannot read in place, and operands whose load transform the
-    // copy applies (so that the kernel runs its untransformed 16x16 schedule)
+    // Kernel choice per run.  The direct-load fast kernel reads an operand in place when its
+    // rows are on the 16-byte grid (pointer included) and it carries no load transform.  Other
+    // operands are copied first (aligned rows, the transform applied by the copy) when the plan
+    // repacks and its workspace exists or can be allocated now.  Otherwise the fast kernel
+    // with fused transforms (aligned operands), the register-staged variant, or the general
+    // kernel runs.
     const int kk = p->K > 0 ? 3 : 0;
     const int unaligned = (p->pk_need | (((uintptr_t)A % 16) ? 1 : 0) | (((uintptr_t)B % 16) ? 2 : 0)) & kk;
     const int xf = ((p->xform_a ? 1 : 0) | (p->xform_b ? 2 : 0)) & kk;
-    const int need = unaligned | (p->fast_pk ? xf : 0);
+    const int need = unaligned | (p->fast_pk && !p->fast_is_skinny ? xf : 0);
     if (p->fast && !need) k = p->fast;
     else if (p->fast_pk && need && repack_workspace(p, static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
         const int eab = elem_bytes(p->ab);
