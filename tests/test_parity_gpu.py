@@ -499,3 +499,35 @@ def test_fast_streaming_stores_unaligned_d(monkeypatch):
         D, pl = run(p, x)
         assert "gemm_fast_256x256 " in pl.describe() + " " and "grid 289" in pl.describe(), pl.describe()
         check(p, x, D, reference(p, x), exact=True)
+
+
+# ---- randomized shapes through the fast path ----------------------------------------------------
+# Seeded draws of shape, layout, type pair, leading-dimension padding per operand, pointer offset
+# and route (aligned copies, or register-staged in place): exact-integer inputs, so every case
+# must match the oracle bit for bit.
+RANDOM_CASES = 48
+
+
+@pytest.mark.parametrize("case", range(RANDOM_CASES))
+def test_fast_random_shapes_exact(case, monkeypatch):
+    from dataclasses import replace
+    rng = np.random.default_rng(np.random.SeedSequence([124, case]))
+    pairs = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("i8", "i32")]
+    ab, cd = pairs[case % len(pairs)]
+    lay = LAYOUTS[int(rng.integers(4))]
+    mode = "fast" if case % 3 else "staged"
+    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
+    kmin = 128 if ab == "i8" else 64
+    M, N = (int(v) for v in rng.integers(16, 700, size=2))
+    K = int(rng.integers(kmin, 700))
+    epi = EPIS[int(rng.integers(4))]
+    alpha, beta = SCALARS[int(rng.integers(4))]
+    p = _exact(M, N, K, lay, ab, cd, epi, alpha, beta, key=(125, case))
+    pa, pb, pc = (int(v) for v in rng.integers(0, 10, size=3))
+    p = replace(p, lda=p.lda + pa, ldb=p.ldb + pb, ldc=p.ldc + pc)
+    offset = int(rng.integers(2))
+    x = synth.make_inputs(p)
+    print(p.label(), "lda", p.lda, "ldb", p.ldb, "ldc", p.ldc, "offset", offset, mode, flush=True)
+    D, pl = run(p, x, offset=offset)
+    assert "gemm_fast" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
