@@ -49,7 +49,9 @@
  * Likewise a complex or dual plan large enough for the real fast kernel ("as real 2x2 blocks"
  * in its description) owns a workspace for op(B) rewritten as real 2 x 2 blocks (twice B's
  * bytes) and, when A is transposed, A split into parts; its runs enqueue the rewrite and then
- * the real product, and a run without that workspace uses the complex kernel.
+ * the real product, and a run without that workspace uses the complex kernel.  A graph that
+ * captured runs of a plan holding a workspace reads and writes that workspace when replayed:
+ * destroy such a plan only after the graphs that captured it.
  *
  * Errors: every function returns a status; nothing throws across this boundary.  gemm_run is
  * asynchronous: it validates, enqueues its kernels (one, or two as above) on `stream` and
