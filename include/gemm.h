@@ -40,10 +40,11 @@
  * graph (later runs may be).  Such a run enqueues two kernels.
  * A large 16- or 8-bit plan whose operand rows are off the 16-byte grid (an odd leading
  * dimension or batch stride, an unaligned pointer at run time, or an M/N-contiguous row length
- * that is not a multiple of 16 bytes; "repack A/B/AB" in its description when the plan itself
- * fixes it) first copies those operands into aligned, zero-padded rows of a workspace it owns
- * (about the size of the copied operands), then runs the direct-load kernel on the copies: two
- * kernels per run.  The workspace is allocated by the first run that needs it on a device (not
+ * that is not a multiple of 16 bytes), or with a load transform on op(A) or op(B), first copies
+ * those operands into aligned, zero-padded rows of a workspace it owns (about the size of the
+ * copied operands; the copy applies the transform), then runs the direct-load kernel on the
+ * copies: two kernels per run ("repack A/B/AB" in the description when the plan itself calls
+ * for the copy).  The workspace is allocated by the first run that needs it on a device (not
  * while the stream is captured: such a run reads the operands in place with a slower kernel,
  * same results) and freed by gemm_plan_destroy; runs of one such plan must not overlap in time.
  * Likewise a complex or dual plan large enough for the real fast kernel ("as real 2x2 blocks"
