@@ -264,6 +264,18 @@ def test_skinny_split_k_described():
     assert "ksplit" not in tge.Plan(16, 16384, 4096, "N", "N").describe()
 
 
+def test_skinny_narrow_blocks_described():
+    # B transposed, M <= 16: 16-column blocks when they make one round of 192-256 workgroups
+    # (no k split); otherwise the 64-column blocks, split over K when they are too few
+    d = tge.Plan(16, 4096, 4096, "N", "T").describe()
+    assert "gemm_skinny_m16_n16" in d and "ksplit" not in d, d
+    d = tge.Plan(16, 4096, 4096, "N", "N").describe()
+    assert "gemm_skinny_m16 " in d and "ksplit 4" in d, d
+    for shape in [(32, 4096, 4096), (7, 4104, 8192), (16, 1000, 2048)]:
+        d = tge.Plan(*shape, "N", "T").describe()
+        assert "_n16" not in d, d
+
+
 def test_diagonal_kernels_described():
     d = tge.Plan(4096, 4096, 4096, "N", "N", kind_a="diagonal").describe()
     assert "gemm_diag_rows" in d and "diag A" in d, d

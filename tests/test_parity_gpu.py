@@ -258,9 +258,11 @@ def test_fast_path_random_and_unaligned_fallback(lay, monkeypatch):
 
 # (K split over workgroups, with the split-K workspace, for (33, 200, 1024), (16, 4096, 4096),
 # (16, 1000, 2048), (7, 4104, 8192) and (64, 8192, 1024))
+# (with B transposed, (16, 4096, 4096), (5, 3072, 1024) and (16, 4000, 2048) take the
+# 16-column variant: one round of 192-256 workgroups, no k split; the last has a partial block)
 SKINNY_SHAPES = [(1, 16, 32), (5, 40, 64), (16, 520, 320), (17, 64, 96), (33, 200, 1024),
                  (48, 24, 160), (64, 4096, 128), (16, 4096, 4096), (16, 1000, 2048),
-                 (7, 4104, 8192), (64, 8192, 1024)]
+                 (7, 4104, 8192), (64, 8192, 1024), (5, 3072, 1024), (16, 4000, 2048)]
 
 
 @pytest.mark.parametrize("shape", SKINNY_SHAPES)

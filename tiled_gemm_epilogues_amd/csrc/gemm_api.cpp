@@ -88,7 +88,7 @@ FastLookup fast_table(int ab, int cd) {
     return nullptr;
 }
 
-using SkinnyLookup = const KernelEntry *(*)(int, int);
+using SkinnyLookup = const KernelEntry *(*)(int, int, int);
 
 SkinnyLookup skinny_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F16) return tge::skinny_f16_f16;
@@ -382,7 +382,15 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (fk && strcmp(fk, "skinny") == 0) want_skinny = true;
     if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % 32 == 0 &&
         (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && strides16 && (op_b == GEMM_OP_T || N % 8 == 0)) {
-        fast = st(op_b, (int)((M + 15) / 16));
+        // B transposed, M <= 16: 16-column blocks when they make one round of 192 to 256
+        // workgroups and the 64-column ones would need a k split (no partial sums, no second
+        // kernel).  Each narrow block reads as many bytes of A as of B, so larger M, or a
+        // second round, measured slower than the split.
+        const int64_t nbk = batch > 1 ? batch : 1;
+        const int64_t nblk = ((N + 15) / 16) * nbk;
+        const bool narrow = op_b == GEMM_OP_T && M <= 16 && ((N + 63) / 64) * nbk < 256 &&
+                            nblk >= 192 && nblk <= 256;
+        fast = st(op_b, (int)((M + 15) / 16), narrow ? 1 : 0);
         skinny = fast != nullptr;
     }
 
@@ -457,7 +465,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->ksplit = 1;
     p->ws_dev = -1;
     p->ws = nullptr;
-    if (skinny) {
+    if (skinny && fast->bn == 64) {
         // split K over workgroups until there is about one workgroup per CU, keeping at least
         // eight 32-deep chunks per wave
         const int64_t blocks = ((N + 63) / 64) * (batch > 1 ? batch : 1);

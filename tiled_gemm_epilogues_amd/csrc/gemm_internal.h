@@ -115,13 +115,13 @@ const KernelEntry *complex_df16_df16(int op_a, int op_b);
 
 // Memory-bound path for M <= 64 (gemm_skinny.hip); mt = ceil(M / 16).  Preconditions: 16-bit
 // inputs, op_a == N, K % 32 == 0, 16-byte aligned A/B pointers and leading dimensions,
-// N % 8 == 0 when B is not transposed.  One workgroup per 64 columns and k split: the launch
-// sets tiles_m = S (k splits), tiles_n = ceil(N / 64), grid = S * tiles_n * batch, and with
-// S > 1 passes the workspace ws (batch * S * M * N floats); the entry then enqueues a second,
-// finishing kernel.
-const KernelEntry *skinny_f16_f16(int op_b, int mt);
-const KernelEntry *skinny_f16_f32(int op_b, int mt);
-const KernelEntry *skinny_bf16_bf16(int op_b, int mt);
-const KernelEntry *skinny_bf16_f32(int op_b, int mt);
+// N % 8 == 0 when B is not transposed.  One workgroup per bn (64) columns and k split: the
+// launch sets tiles_m = S (k splits), tiles_n = ceil(N / bn), grid = S * tiles_n * batch, and
+// with S > 1 passes the workspace ws (batch * S * M * N floats); the entry then enqueues a
+// second, finishing kernel.  narrow = 1 (B transposed only): 16 columns per workgroup, S = 1.
+const KernelEntry *skinny_f16_f16(int op_b, int mt, int narrow);
+const KernelEntry *skinny_f16_f32(int op_b, int mt, int narrow);
+const KernelEntry *skinny_bf16_bf16(int op_b, int mt, int narrow);
+const KernelEntry *skinny_bf16_f32(int op_b, int mt, int narrow);
 
 }  // namespace tge

@@ -7,7 +7,9 @@
 //  * one workgroup (one per CU: its LDS is the whole ring) per 64 output columns and k split:
 //    a row of a non-transposed B is read as whole 128-byte lines; K is split S ways over
 //    workgroups when the column blocks alone are too few to fill the chip (S chosen by the
-//    plan), and over the 4 waves of a workgroup;
+//    plan), and over the 4 waves of a workgroup.  A transposed B (rows along K) can be read
+//    16 output columns per workgroup instead, each of its rows still in whole lines: with
+//    enough such blocks to fill the chip the plan takes that narrow variant and no k split;
 //  * each wave streams its K range through a private ring of LDS slots with direct-to-LDS
 //    loads (no barriers inside the loop: a wave only waits for its own loads): per 32-wide k
 //    chunk, 4 KiB of B (32 k x 64 columns) and 1 KiB of A per 16 rows;
@@ -41,8 +43,8 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int NT = 256;
 constexpr int NB = 64;         // output columns per workgroup: whole 128-byte lines of a row of B
+constexpr int NB_NARROW = 16;  // output columns per workgroup of the narrow variant (B transposed)
 constexpr int KCH = 32;        // k per chunk (one MFMA step)
-constexpr int BCH = 4;         // 1 KiB load instructions per chunk of B (64 columns x 32 k)
 
 template <class TI>
 __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c);
@@ -82,19 +84,24 @@ __device__ __forceinline__ void wait_vm_atmost(int n) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// MT: 16-row tiles of A (M <= 16 * MT); BT: B is stored transposed (N x K).
+// MT: 16-row tiles of A (M <= 16 * MT); BT: B is stored transposed (N x K); CB: output
+// columns per workgroup (64, or 16 with B transposed).
 // Grid: (k split, column block) pairs of every product: p.tiles_m holds the number of k splits
-// S, p.tiles_n the number of 64-column blocks.
-template <class TI, class TO, int MT, bool BT>
+// S, p.tiles_n the number of CB-column blocks.
+template <class TI, class TO, int MT, bool BT, int CB>
 __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
+    static_assert(CB == NB || (CB == NB_NARROW && BT), "narrow blocks need rows of B along K");
+    constexpr int G = CB / 16;                          // 16-column groups (MFMA N tiles)
+    constexpr int BCH = G;                              // 1 KiB loads per chunk of B (CB x 32 k)
     constexpr int DPC = BCH + MT;                       // load instructions per chunk
     constexpr int SLOT = DPC * 1024;                    // B chunk, then MT A chunks
-    // ring depth per wave: as deep as the CU's 160 KiB of LDS allows
-    constexpr int DEPTH = MT == 1 ? 8 : MT == 2 ? 6 : 5;
+    // ring depth per wave: as deep as the CU's 160 KiB of LDS and the vmcnt range allow
+    constexpr int DEPTH = CB == NB ? (MT == 1 ? 8 : MT == 2 ? 6 : 5)
+                                   : (MT == 1 ? 16 : MT == 2 ? 12 : MT == 3 ? 9 : 7);
     constexpr int STEADY = (DEPTH - 1) * DPC;           // loads in flight when waiting for one chunk
     constexpr int RING_BYTES = 4 * DEPTH * SLOT;
     static_assert(RING_BYTES <= 160 * 1024 && STEADY <= 63, "LDS budget, vmcnt range");
-    static_assert(4 * MT * 4 * 64 * 16 <= RING_BYTES, "reduction area");
+    static_assert(4 * MT * G * 64 * 16 <= RING_BYTES, "reduction area");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[RING_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     const int lid = select_batch<2, (int)sizeof(typename TO::T)>(p, blockIdx.x, per);
     const int S = p.tiles_m;
     const int split = lid / p.tiles_n, cb = lid - split * p.tiles_n;
-    const int n0 = cb * NB;
+    const int n0 = cb * CB;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
 
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
         if constexpr (BT) {
-            // B stored N x K: 64 rows (n) of 64 B; instruction i -> rows 16i + lane/4, piece lane%4
+            // B stored N x K: CB rows (n) of 64 B; instruction i -> rows 16i + lane/4, piece lane%4
             const int n = min(n0 + 16 * i + (lane >> 2), p.N - 1);
             voffB[i] = (uint32_t)(n * p.ldb + (lane & 3) * 8) * 2u;
         } else {
@@ -156,11 +163,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     const uint32_t offA = (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16);
     const uint32_t offB = BT ? offA : (uint32_t)((8 * (lane >> 4) + ((lane & 15) >> 2)) * 128 + (lane & 3) * 8);
 
-    f32x4 acc[MT][4];
+    f32x4 acc[MT][G];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < G; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int npro = min(DEPTH, nch);
     for (int c = 0; c < npro; ++c) issue(c0 + c, c);
@@ -172,9 +179,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         if (nch - 1 - c >= DEPTH - 1) wait_vm<STEADY>();
         else wait_vm_atmost((nch - 1 - c) * DPC);
         const uint32_t sl = lring + (uint32_t)(slot * SLOT);
-        u32x4 bf[4];
+        u32x4 bf[G];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < G; ++g) {
             if constexpr (BT) {
                 bf[g] = *(const lds_u32x4 *)(uintptr_t)(sl + 1024u * g + offB);
             } else {
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         for (int t = 0; t < MT; ++t) af[t] = *(const lds_u32x4 *)(uintptr_t)(sl + 1024u * (BCH + t) + offA);
         // load transforms (no-ops when disabled)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) bf[g] = zero_negative<2>(bf[g], p.xform_b);
+        for (int g = 0; g < G; ++g) bf[g] = zero_negative<2>(bf[g], p.xform_b);
 #pragma unroll
         for (int t = 0; t < MT; ++t) af[t] = zero_negative<2>(af[t], p.xform_a);
         // the slot is refilled below: its reads must have returned first
@@ -200,25 +207,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) acc[t][g] = mma16<TI>(af[t], bf[g], acc[t][g]);
+            for (int g = 0; g < G; ++g) acc[t][g] = mma16<TI>(af[t], bf[g], acc[t][g]);
         if (c + DEPTH < nch) issue(c0 + c + DEPTH, slot);
     }
 
     // add the four waves' partial sums (every wave has waited for all of its loads): all park
-    // theirs in LDS, then wave w adds up column group w in wave order
+    // theirs in LDS, then wave w adds up column group w in wave order (the narrow variant has
+    // one group: wave 0 adds it, the others are done)
     __syncthreads();
     f32x4 *part = reinterpret_cast<f32x4 *>(smem);    // [wave][MT][group][64 lanes]
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) part[((wave * MT + t) * 4 + g) * 64 + lane] = acc[t][g];
+        for (int g = 0; g < G; ++g) part[((wave * MT + t) * G + g) * 64 + lane] = acc[t][g];
     __syncthreads();
+    if (wave >= G) return;
     f32x4 sum[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        sum[t] = part[((0 * MT + t) * 4 + wave) * 64 + lane];
+        sum[t] = part[((0 * MT + t) * G + wave) * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) sum[t] += part[((w * MT + t) * 4 + wave) * 64 + lane];
+        for (int w = 1; w < 4; ++w) sum[t] += part[((w * MT + t) * G + wave) * 64 + lane];
     }
 
     // lane holds rows 16t + 4*(lane/16) + r of column n
@@ -282,9 +291,9 @@ __global__ __launch_bounds__(NT) void skinny_finish(GemmParams p) {
     static_cast<T *>(p.D)[idx] = (T)x;
 }
 
-template <class TI, class TO, int MT, bool BT>
+template <class TI, class TO, int MT, bool BT, int CB = NB>
 hipError_t launch_skinny(const GemmParams &p, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_skinny<TI, TO, MT, BT>), dim3(grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((gemm_skinny<TI, TO, MT, BT, CB>), dim3(grid), dim3(NT), 0, s, p);
     if (p.tiles_m > 1) {
         const unsigned g2 = (unsigned)((int64_t)((p.N + NT - 1) / NT) * p.M * p.batch);
         hipLaunchKernelGGL((skinny_finish<TO>), dim3(g2), dim3(NT), 0, s, p);
@@ -292,8 +301,15 @@ hipError_t launch_skinny(const GemmParams &p, unsigned grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// narrow = 1: the 16-column variant (B transposed only)
 template <class TI, class TO>
-const KernelEntry *lookup_skinny(int op_b, int mt) {
+const KernelEntry *lookup_skinny(int op_b, int mt, int narrow) {
+    static const KernelEntry nar[4] = {
+        {launch_skinny<TI, TO, 1, true, NB_NARROW>, 16, NB_NARROW, KCH, 1, 4, "gemm_skinny_m16_n16"},
+        {launch_skinny<TI, TO, 2, true, NB_NARROW>, 32, NB_NARROW, KCH, 1, 4, "gemm_skinny_m32_n16"},
+        {launch_skinny<TI, TO, 3, true, NB_NARROW>, 48, NB_NARROW, KCH, 1, 4, "gemm_skinny_m48_n16"},
+        {launch_skinny<TI, TO, 4, true, NB_NARROW>, 64, NB_NARROW, KCH, 1, 4, "gemm_skinny_m64_n16"}};
+    if (narrow) return (op_b == 1 && mt >= 1 && mt <= 4) ? &nar[mt - 1] : nullptr;
     static const KernelEntry e[2][4] = {
         {{launch_skinny<TI, TO, 1, false>, 16, NB, KCH, 1, 4, "gemm_skinny_m16"},
          {launch_skinny<TI, TO, 2, false>, 32, NB, KCH, 1, 4, "gemm_skinny_m32"},
@@ -311,13 +327,13 @@ const KernelEntry *lookup_skinny(int op_b, int mt) {
 }  // namespace
 
 #if defined(TGE_PAIR_F16_F16)
-const KernelEntry *skinny_f16_f16(int b, int mt) { return lookup_skinny<TF16, OF16>(b, mt); }
+const KernelEntry *skinny_f16_f16(int b, int mt, int nw) { return lookup_skinny<TF16, OF16>(b, mt, nw); }
 #elif defined(TGE_PAIR_F16_F32)
-const KernelEntry *skinny_f16_f32(int b, int mt) { return lookup_skinny<TF16, OF32>(b, mt); }
+const KernelEntry *skinny_f16_f32(int b, int mt, int nw) { return lookup_skinny<TF16, OF32>(b, mt, nw); }
 #elif defined(TGE_PAIR_BF16_BF16)
-const KernelEntry *skinny_bf16_bf16(int b, int mt) { return lookup_skinny<TBF16, OBF16>(b, mt); }
+const KernelEntry *skinny_bf16_bf16(int b, int mt, int nw) { return lookup_skinny<TBF16, OBF16>(b, mt, nw); }
 #elif defined(TGE_PAIR_BF16_F32)
-const KernelEntry *skinny_bf16_f32(int b, int mt) { return lookup_skinny<TBF16, OF32>(b, mt); }
+const KernelEntry *skinny_bf16_f32(int b, int mt, int nw) { return lookup_skinny<TBF16, OF32>(b, mt, nw); }
 #else
 #error "define one 16-bit TGE_PAIR_* macro"
 #endif
