@@ -325,6 +325,21 @@ def test_skinny_split_k_batched(monkeypatch):
         assert np.array_equal(oracle.decode(p.cd, Db), oracle.decode(p.cd, oracle.round_to(p.cd, ref[b])))
 
 
+def test_skinny_narrow_blocks_batched(monkeypatch):
+    # three products of 64 sixteen-column blocks each: one round of 192 narrow workgroups
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    p = synth.exact_integer_problem(13, 1024, 1024, "N", "T", "f16", "f32", "bias_relu", 2.0, -1.0,
+                                    key=(126, 0), batch=3, stride_bias=1024)
+    x = synth.make_inputs(p)
+    D, pl = run_batched(p, x)
+    assert "gemm_skinny_m16_n16" in pl.describe() and "batch 3" in pl.describe(), pl.describe()
+    ref = reference_batched(p, x)
+    import oracle
+    for b in range(p.batch):
+        Db = D[b * p.stride_c: b * p.stride_c + p.M * p.ldc].reshape(p.M, p.ldc)[:, : p.N]
+        assert np.array_equal(oracle.decode(p.cd, Db), oracle.decode(p.cd, oracle.round_to(p.cd, ref[b])))
+
+
 def test_skinny_ineligible_shapes_fall_back(monkeypatch):
     monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
     # K not a multiple of 32, and A transposed: the general kernel runs, same results
