@@ -20,11 +20,11 @@
 // spare for transforming fragments, and one streaming pass costs less than the 32x32 schedule
 // that can.
 //
-// The copy is byte-exact (any element type) unless it carries the transform: row r of product b goes from
-// src + b * src_stride + r * src_pitch (row_bytes bytes) to dst + b * dst_stride + r * dst_pitch,
-// followed by zeros up to dst_pitch; rows past the source's (K rounded up to whole slabs, for
-// an operand stored K-major) are zeros.  One wave copies 64 consecutive chunks (1 KiB) of one row;
-// a workgroup covers 4 rows.
+// The copy is byte-exact (any element type) unless it carries the transform: row r of product
+// b goes from src + b * src_stride + r * src_pitch (row_bytes bytes) to
+// dst + b * dst_stride + r * dst_pitch, followed by zeros up to dst_pitch; rows past the
+// source's (K rounded up to whole slabs, for an operand stored K-major) are zeros.  One wave
+// copies 64 consecutive chunks (1 KiB) of one row; a workgroup covers 4 rows.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -64,7 +64,7 @@ __device__ __forceinline__ void repack_block(const RepackJob &j, uint32_t blk, i
     *reinterpret_cast<u32x4 *>(j.dst + (int64_t)prod * j.dst_stride + r * j.dst_pitch + c * 16) = v;
 }
 
-// Grid: blocks_a workgroups for job a, then those of job b (none when b.rows == 0).
+// Grid: blocks_a workgroups for job a, then those of job b (none when b.rows_out == 0).
 __global__ __launch_bounds__(RP_ROWS * 64) void repack_rows(RepackJob a, RepackJob b, uint32_t blocks_a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (blockIdx.x < blocks_a) repack_block(a, blockIdx.x, wave, lane);
