@@ -298,3 +298,20 @@ def test_transform_copies_only_for_the_fast_kernel():
     # only C transformed: nothing to copy
     d = tge.Plan(8192, 8192, 8192, "N", "N", transform_c="relu").describe()
     assert "repack" not in d, d
+
+
+def test_fast_k_split_described(monkeypatch):
+    # few 256x256 tiles and K >= 4096: K cut into chunks of at least 16 slabs, tiles x S >= 128
+    d = tge.Plan(2048, 2048, 8192, "N", "N").describe()
+    assert "gemm_fast_256x256 " in d and "ksplit 4" in d, d
+    d = tge.Plan(1024, 1024, 8192, "N", "T", ab="bf16", cd="f32").describe()
+    assert "gemm_fast_256x256 " in d and "ksplit 8" in d, d
+    # 2048^3 (K = 2048) stays on the general kernel; enough tiles: no split
+    assert "ksplit" not in tge.Plan(2048, 2048, 2048, "N", "N").describe()
+    assert "ksplit" not in tge.Plan(8192, 8192, 8192, "N", "N").describe()
+    # no split with load transforms on A/B, int8, a batch, or unaligned leading dimensions
+    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", transform_a="relu").describe()
+    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", ab="i8", cd="i32").describe()
+    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "nosplit")
+    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N").describe()

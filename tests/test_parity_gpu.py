@@ -9,6 +9,7 @@
   properties that hold everywhere.
 """
 import os
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -527,7 +528,6 @@ RANDOM_CASES = 48
 
 @pytest.mark.parametrize("case", range(RANDOM_CASES))
 def test_fast_random_shapes_exact(case, monkeypatch):
-    from dataclasses import replace
     rng = np.random.default_rng(np.random.SeedSequence([124, case]))
     pairs = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("i8", "i32")]
     ab, cd = pairs[case % len(pairs)]
@@ -548,3 +548,85 @@ def test_fast_random_shapes_exact(case, monkeypatch):
     D, pl = run(p, x, offset=offset)
     assert "gemm_fast" in pl.describe(), pl.describe()
     check(p, x, D, reference(p, x), exact=True)
+
+
+# ---- the fast kernel's K split (chunks of K as a batch into fp32 partial sums, then the
+# finishing kernel) -------------------------------------------------------------------------------
+# TGE_FORCE_KERNEL=split makes small shapes split (any S >= 2); the plan's own rule splits only
+# large-K products with few tiles.  Exact-integer inputs: partial sums and their total are exact.
+SPLIT_SHAPES = [(300, 264, 1024), (520, 300, 640), (256, 256, 128), (17, 600, 2048),
+                (600, 9, 512), (777, 513, 1280)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_fast_k_split_exact(ab, cd, lay, shape, monkeypatch):
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "split")
+    M, N, K = shape
+    i = LAYOUTS.index(lay) + 4 * SPLIT_SHAPES.index(shape)
+    p = _exact(M, N, K, lay, ab, cd, EPIS[i % 4], *SCALARS[(i // 4) % 4], key=(127, i))
+    if i % 3 == 0:
+        p = replace(p, transform_c="relu")          # the C transform runs in the finishing step
+    x = synth.make_inputs(p)
+    print(p.label(), flush=True)
+    D, pl = run(p, x)
+    ve = 8
+    aligned = ((lay[0] == "N" or M % ve == 0) and (lay[1] == "T" or N % ve == 0))
+    if aligned:
+        assert "gemm_fast_256x256 " in pl.describe() and " ksplit " in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+    # an unaligned pointer: the operands are copied and the product runs whole, same result
+    D2, _ = run(p, x, offset=1)
+    check(p, x, D2, reference(p, x), exact=True)
+
+
+def test_fast_k_split_graph_capture(monkeypatch):
+    # no workspace yet inside the first capture: that run is not split; after an eager run the
+    # captured runs split; every replay gives the eager result bit for bit
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "split")
+    p = _exact(520, 300, 640, "NT", "bf16", "f32", "bias_relu", 2.0, -1.0, key=(128, 0))
+    x = synth.make_inputs(p)
+    ref = reference(p, x)
+    from gpu_helpers import to_dev, to_host
+    A, B = to_dev(p.ab, x["A"]), to_dev(p.ab, x["B"])
+    C, bias = to_dev(p.cd, x["C"]), to_dev(p.bias_dt, x["bias"])
+    import tiled_gemm_epilogues_amd as tge
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    assert " ksplit " in pl.describe(), pl.describe()
+    D = torch.zeros(p.M * p.ldc, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(s):
+        g0 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g0, stream=s):
+            pl.run(A, B, C, D, bias, p.alpha, p.beta)
+        graphs.append(g0)
+        pl.run(A, B, C, D, bias, p.alpha, p.beta)
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=s):
+            pl.run(A, B, C, D, bias, p.alpha, p.beta)
+        graphs.append(g1)
+    torch.cuda.synchronize()
+    D0 = to_host(p.cd, D).reshape(p.M, p.ldc).copy()
+    check(p, x, D0, ref, exact=True)
+    for _ in range(3):
+        for g in graphs:
+            D.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(p.cd, D).reshape(p.M, p.ldc), D0)
+            pl.run(A, B, C, D, bias, p.alpha, p.beta)
+            torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("lay", ["NN", "TT"])
+def test_fast_k_split_full_size_points(lay):
+    # the plan's own choice at 2048 x 2048 x 8192 (64 tiles, K split 4), random fp16 inputs,
+    # bias + ReLU: sampled outputs against the oracle's per-point reference
+    p = synth.Problem(2048, 2048, 8192, lay[0], lay[1], "f16", "f16", "bias_relu", 1.0, 0.0,
+                      key=(129, lay == "TT"))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert "gemm_fast_256x256 " in pl.describe() and "ksplit 4" in pl.describe(), pl.describe()
+    check_points(p, x, D)

@@ -124,4 +124,12 @@ const KernelEntry *skinny_f16_f32(int op_b, int mt, int narrow);
 const KernelEntry *skinny_bf16_bf16(int op_b, int mt, int narrow);
 const KernelEntry *skinny_bf16_f32(int op_b, int mt, int narrow);
 
+// The finishing step alone: D = epilogue(sum over the p.tiles_m splits of ws, in split order),
+// ws laid out [product][split][M][N] floats; p otherwise as for the product (C, bias, ldc,
+// alpha, beta, ReLU, the C transform).  Used by the fast kernel's K split too.
+hipError_t finish_f16_f16(const GemmParams &p, hipStream_t s);
+hipError_t finish_f16_f32(const GemmParams &p, hipStream_t s);
+hipError_t finish_bf16_bf16(const GemmParams &p, hipStream_t s);
+hipError_t finish_bf16_f32(const GemmParams &p, hipStream_t s);
+
 }  // namespace tge

@@ -301,6 +301,14 @@ hipError_t launch_skinny(const GemmParams &p, unsigned grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The finishing kernel on its own (the fast kernel's K split writes the same workspace layout).
+template <class TO>
+hipError_t launch_finish(const GemmParams &p, hipStream_t s) {
+    const unsigned g = (unsigned)((int64_t)((p.N + NT - 1) / NT) * p.M * p.batch);
+    hipLaunchKernelGGL((skinny_finish<TO>), dim3(g), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
 // narrow = 1: the 16-column variant (B transposed only)
 template <class TI, class TO>
 const KernelEntry *lookup_skinny(int op_b, int mt, int narrow) {
@@ -328,12 +336,16 @@ const KernelEntry *lookup_skinny(int op_b, int mt, int narrow) {
 
 #if defined(TGE_PAIR_F16_F16)
 const KernelEntry *skinny_f16_f16(int b, int mt, int nw) { return lookup_skinny<TF16, OF16>(b, mt, nw); }
+hipError_t finish_f16_f16(const GemmParams &p, hipStream_t s) { return launch_finish<OF16>(p, s); }
 #elif defined(TGE_PAIR_F16_F32)
 const KernelEntry *skinny_f16_f32(int b, int mt, int nw) { return lookup_skinny<TF16, OF32>(b, mt, nw); }
+hipError_t finish_f16_f32(const GemmParams &p, hipStream_t s) { return launch_finish<OF32>(p, s); }
 #elif defined(TGE_PAIR_BF16_BF16)
 const KernelEntry *skinny_bf16_bf16(int b, int mt, int nw) { return lookup_skinny<TBF16, OBF16>(b, mt, nw); }
+hipError_t finish_bf16_bf16(const GemmParams &p, hipStream_t s) { return launch_finish<OBF16>(p, s); }
 #elif defined(TGE_PAIR_BF16_F32)
 const KernelEntry *skinny_bf16_f32(int b, int mt, int nw) { return lookup_skinny<TBF16, OF32>(b, mt, nw); }
+hipError_t finish_bf16_f32(const GemmParams &p, hipStream_t s) { return launch_finish<OF32>(p, s); }
 #else
 #error "define one 16-bit TGE_PAIR_* macro"
 #endif
