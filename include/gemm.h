@@ -33,11 +33,12 @@
  * Ownership: the caller owns every device buffer and keeps it alive until the stream work that
  * uses it has finished.  A plan is a small host object, destroyed with gemm_plan_destroy.  Most
  * plans hold no device memory and may be shared between host threads and streams.  A plan for
- * a short product (M <= 64) that splits K over workgroups ("ksplit S" in its description) owns
- * a split-K workspace (S * M * N floats per product of the batch) on the device of its first
- * gemm_run, allocated by that call and freed by gemm_plan_destroy: its runs must not overlap in
- * time (use one plan per concurrent stream), and its first run must not be captured into a
- * graph (later runs may be).  Such a run enqueues two kernels.
+ * plan that splits K over workgroups ("ksplit S" in its description: a short product, M <= 64,
+ * or a 16-bit product with few output tiles and K >= 4096) owns a split-K workspace (S * M * N
+ * floats per product of the batch) on the device of its first gemm_run, allocated by that call
+ * and freed by gemm_plan_destroy: its runs must not overlap in time (use one plan per concurrent
+ * stream).  A short product's first run must not be captured into a graph (later runs may be);
+ * the other kind's first run inside a capture runs unsplit.  Such a run enqueues two kernels.
  * A large 16- or 8-bit plan whose operand rows are off the 16-byte grid (an odd leading
  * dimension or batch stride, an unaligned pointer at run time, or an M/N-contiguous row length
  * that is not a multiple of 16 bytes), or with a load transform on op(A) or op(B), first copies
