@@ -209,9 +209,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
  * For a batched plan every pointer is that of product 0 (see gemm_plan_create_batched).
  *   alpha, beta  scalars applied in fp32 (int8 plans require alpha == 1 and beta in {0, 1}).
  * Returns INVALID_VALUE for a NULL plan or a missing required pointer, NOT_SUPPORTED for int8
- * scalars outside the rule above or for the first run of a split-K plan during stream capture,
- * ALLOC_FAILED when that first run cannot allocate its workspace (a repacking plan that cannot
- * allocate its copies reads the operands in place instead), HIP_ERROR when a launch fails.  M == 0, N == 0 or a batch of 0 returns SUCCESS without launching.
+ * scalars outside the rule above or for the first run of a short (M <= 64) split-K plan during
+ * stream capture, ALLOC_FAILED when that first run cannot allocate its workspace (the plans
+ * that copy or rewrite operands, or split K for the fast kernel, run without their workspace
+ * instead), HIP_ERROR when a launch fails.  M == 0, N == 0 or a batch of 0 returns SUCCESS
+ * without launching.
  */
 gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream);
