@@ -323,8 +323,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // fast path: 16-bit inputs, 256x256 tiles worth it, shape/ld preconditions of gemm_fast
     const KernelEntry *fast = nullptr;
     FastLookup ft = fast_table(ab_type, cd_type);
-    // "fast", "staged" (the fast kernel, register-staged for operands the direct loads cannot
-    // read in place instead of repacking them), "general" or "skinny" (tests, sweeps)
+    // TGE_FORCE_KERNEL (tests, sweeps): "fast", "staged" (the fast kernel, register-staged for
+    // operands the direct loads cannot read in place instead of copying them), "general",
+    // "skinny", "split" / "nosplit" (the fast kernel's K split forced / never)
     const char *fk = getenv("TGE_FORCE_KERNEL");
     const bool staged = fk && strcmp(fk, "staged") == 0;
     // the fast kernel does ~3x the work per CU-round of the general 128x128 kernel: take it
@@ -354,8 +355,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         const int64_t min_chunk = force_split ? 1 : 16;
         if (sp > slabs / min_chunk) sp = slabs / min_chunk;
         while (sp > 1 && slabs % sp) --sp;
-        if (sp >= 2 && (force_split || (tiles * sp >= 128 && K >= 4096)) && fast_table(ab_type, GEMM_F32) &&
-            finish_table(ab_type, cd_type))
+        const bool worth = force_split || (tiles * sp >= 128 && K >= 4096);
+        if (sp >= 2 && worth && fast_table(ab_type, GEMM_F32) && finish_table(ab_type, cd_type))
             split_s = (int)sp;
     }
     if (split_s) want_fast = true;
