@@ -311,7 +311,10 @@ def test_fast_k_split_described(monkeypatch):
     assert "ksplit" not in tge.Plan(8192, 8192, 8192, "N", "N").describe()
     # no split with load transforms on A/B, int8, a batch, or unaligned leading dimensions
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", transform_a="relu").describe()
-    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", ab="i8", cd="i32").describe()
+    # int8: 64 slabs of 128 from K = 8192
+    d = tge.Plan(2048, 2048, 8192, "N", "N", ab="i8", cd="i32").describe()
+    assert "gemm_fast_256x256 " in d and "ksplit 4" in d, d
+    assert "ksplit" not in tge.Plan(2048, 2048, 4096, "N", "N", ab="i8", cd="i32").describe()
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
     monkeypatch.setenv("TGE_FORCE_KERNEL", "nosplit")
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N").describe()

@@ -581,6 +581,25 @@ def test_fast_k_split_exact(ab, cd, lay, shape, monkeypatch):
     check(p, x, D2, reference(p, x), exact=True)
 
 
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_fast_k_split_int8_exact(lay, shape, monkeypatch):
+    # int8 -> int32: int32 partial sums, the integer finishing kernel (bias, beta in {0, 1},
+    # ReLU); K doubled so that every chunk is a whole int8 slab of 128
+    monkeypatch.setenv("TGE_FORCE_KERNEL", "split")
+    M, N, K = shape
+    K *= 2
+    i = LAYOUTS.index(lay) + 4 * SPLIT_SHAPES.index(shape)
+    p = _exact(M, N, K, lay, "i8", "i32", EPIS[i % 4], 1.0, 1.0 if i % 2 else 0.0, key=(130, i))
+    x = synth.make_inputs(p)
+    print(p.label(), flush=True)
+    D, pl = run(p, x)
+    aligned = ((lay[0] == "N" or M % 16 == 0) and (lay[1] == "T" or N % 16 == 0))
+    if aligned:
+        assert "gemm_fast_256x256 " in pl.describe() and " ksplit " in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
 def test_fast_k_split_graph_capture(monkeypatch):
     # no workspace yet inside the first capture: that run is not split; after an eager run the
     # captured runs split; every replay gives the eager result bit for bit

@@ -101,6 +101,7 @@ FinishFn finish_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F32) return tge::finish_f16_f32;
     if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::finish_bf16_bf16;
     if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::finish_bf16_f32;
+    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::finish_i8_i32;
     return nullptr;
 }
 
@@ -336,27 +337,31 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     bool want_fast = cfg == tge::CFG_256 || (cfg == tge::CFG_128 && 4 * r256 <= 3 * r128);
     if (getenv("TGE_FORCE_TILE")) want_fast = cfg == tge::CFG_256;
     if ((fk && strcmp(fk, "fast") == 0) || staged) want_fast = true;
-    // K split of the fast kernel: few 256x256 tiles and a long K (4096 or more).  K is cut
-    // into S equal chunks of whole slabs (at least 16 each) so that tiles x S workgroups fill
-    // the chip (at least 128); the chunks' fp32 partial sums go to a workspace and the
-    // finishing kernel adds them in chunk order and applies the epilogue.  16-bit inputs, one
-    // product, no load transforms.  Such a plan takes the fast kernel even where the general
-    // one would otherwise run: measured 1.1-2.9x faster for K >= 4096, slower at 2048^3
+    // K split of the fast kernel: few 256x256 tiles and a long K (64 slabs or more: K >= 4096
+    // for 16-bit inputs, 8192 for int8).  K is cut into S equal chunks of whole slabs (at least
+    // 16 each) so that tiles x S workgroups fill the chip (at least 128); the chunks' partial
+    // sums (fp32, int32 for int8) go to a workspace and the finishing kernel adds them in chunk
+    // order and applies the epilogue.  One product, no load transforms.  Such a plan takes the
+    // fast kernel even where the general one would otherwise run: measured 1.1-2.9x faster
+    // from 64 slabs, slower at 2048^3 (32 slabs)
     // (TGE_FORCE_KERNEL=split: any S >= 2, chunks of one slab or more; =nosplit: never).
     int split_s = 0;
     const bool force_split = fk && strcmp(fk, "split") == 0;
-    if ((ab_type == GEMM_F16 || ab_type == GEMM_BF16) && batch <= 1 && !ctable && !diag_a &&
-        !diag_b && !desc->transform_a && !desc->transform_b && K % 64 == 0 && !staged &&
+    const int64_t slab_k = 128 / elem_bytes(ab_type);   // K elements per slab of the fast kernel
+    const int part_cd = ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32;
+    if ((ab_type == GEMM_F16 || ab_type == GEMM_BF16 || ab_type == GEMM_I8) && batch <= 1 &&
+        !ctable && !diag_a && !diag_b && !desc->transform_a && !desc->transform_b &&
+        K % slab_k == 0 && !staged &&
         !(fk && (strcmp(fk, "nosplit") == 0 || strcmp(fk, "general") == 0 ||
                  strcmp(fk, "skinny") == 0))) {
         const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-        const int64_t slabs = K / 64;
+        const int64_t slabs = K / slab_k;
         int64_t sp = tiles > 0 ? 256 / tiles : 0;
         const int64_t min_chunk = force_split ? 1 : 16;
         if (sp > slabs / min_chunk) sp = slabs / min_chunk;
         while (sp > 1 && slabs % sp) --sp;
-        const bool worth = force_split || (tiles * sp >= 128 && K >= 4096);
-        if (sp >= 2 && worth && fast_table(ab_type, GEMM_F32) && finish_table(ab_type, cd_type))
+        const bool worth = force_split || (tiles * sp >= 128 && slabs >= 64);
+        if (sp >= 2 && worth && fast_table(ab_type, part_cd) && finish_table(ab_type, cd_type))
             split_s = (int)sp;
     }
     if (split_s) want_fast = true;
@@ -518,7 +523,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->fast_part = nullptr;
     p->finish = nullptr;
     if (split_s && fast && !skinny) {
-        p->fast_part = fast_table(ab_type, GEMM_F32)(op_a, op_b, 0);
+        p->fast_part = fast_table(ab_type, ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32)(op_a, op_b, 0);
         p->finish = finish_table(ab_type, cd_type);
         p->ksplit = split_s;
     }

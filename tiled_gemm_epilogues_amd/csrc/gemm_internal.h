@@ -131,5 +131,7 @@ hipError_t finish_f16_f16(const GemmParams &p, hipStream_t s);
 hipError_t finish_f16_f32(const GemmParams &p, hipStream_t s);
 hipError_t finish_bf16_bf16(const GemmParams &p, hipStream_t s);
 hipError_t finish_bf16_f32(const GemmParams &p, hipStream_t s);
+// int8 -> int32 (gemm_repack.hip): int32 partial sums in ws, one product (batch 1)
+hipError_t finish_i8_i32(const GemmParams &p, hipStream_t s);
 
 }  // namespace tge

@@ -146,7 +146,33 @@ uint32_t pair_job_blocks(const PairJob &j) {
     return (uint32_t)(cblk * rblk * j.batch);
 }
 
+// ---- the K split's finishing step for int8 products ---------------------------------------------
+// D[m][n] = ReLU?(sum of the S int32 partial sums [split][M][N] in ws, in split order,
+// + beta * C (beta 0 or 1) + bias[n]); int32 arithmetic wraps exactly as the unsplit sum does.
+__global__ __launch_bounds__(256) void finish_int(GemmParams p) {
+    const int tiles = (p.N + 255) / 256;
+    const int m = blockIdx.x / tiles;
+    const int n = (blockIdx.x - m * tiles) * 256 + (int)threadIdx.x;
+    if (m >= p.M || n >= p.N) return;
+    const int S = p.tiles_m;
+    const int *ws = reinterpret_cast<const int *>(p.ws) + (int64_t)m * p.N + n;
+    uint32_t v = 0;
+    for (int q = 0; q < S; ++q) v += (uint32_t)ws[(int64_t)q * p.M * p.N];
+    const int64_t idx = (int64_t)m * p.ldc + n;
+    if (p.has_beta) v += (uint32_t)c_in_i(static_cast<const int *>(p.C)[idx], p.xform_c);
+    if (p.has_bias) v += (uint32_t)static_cast<const int *>(p.bias)[n];
+    int x = (int)v;
+    if (p.relu) x = x > 0 ? x : 0;
+    static_cast<int *>(p.D)[idx] = x;
+}
+
 }  // namespace
+
+hipError_t finish_i8_i32(const GemmParams &p, hipStream_t s) {
+    const unsigned g = (unsigned)((int64_t)((p.N + 255) / 256) * p.M);
+    hipLaunchKernelGGL(finish_int, dim3(g), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
 
 int64_t repack_blocks(const RepackJob &j) { return job_blocks(j); }
 
