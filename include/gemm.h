@@ -34,7 +34,7 @@
  * uses it has finished.  A plan is a small host object, destroyed with gemm_plan_destroy.  Most
  * plans hold no device memory and may be shared between host threads and streams.  A plan for
  * plan that splits K over workgroups ("ksplit S" in its description: a short product, M <= 64,
- * or a 16-bit product with few output tiles and K >= 4096) owns a split-K workspace (S * M * N
+ * or a product with few output tiles and a long K) owns a split-K workspace (S * M * N
  * floats per product of the batch) on the device of its first gemm_run, allocated by that call
  * and freed by gemm_plan_destroy: its runs must not overlap in time (use one plan per concurrent
  * stream).  A short product's first run must not be captured into a graph (later runs may be);
