@@ -309,12 +309,14 @@ def test_fast_k_split_described(monkeypatch):
     # 2048^3 (K = 2048) stays on the general kernel; enough tiles: no split
     assert "ksplit" not in tge.Plan(2048, 2048, 2048, "N", "N").describe()
     assert "ksplit" not in tge.Plan(8192, 8192, 8192, "N", "N").describe()
-    # no split with load transforms on A/B, int8, a batch, or unaligned leading dimensions
+    # no split with load transforms on A/B
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", transform_a="relu").describe()
     # int8: 64 slabs of 128 from K = 8192
     d = tge.Plan(2048, 2048, 8192, "N", "N", ab="i8", cd="i32").describe()
     assert "gemm_fast_256x256 " in d and "ksplit 4" in d, d
     assert "ksplit" not in tge.Plan(2048, 2048, 4096, "N", "N", ab="i8", cd="i32").describe()
-    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
+    # an operand off the 16-byte grid is copied first, then split as well
+    d = tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
+    assert "ksplit 4" in d and "repack A" in d, d
     monkeypatch.setenv("TGE_FORCE_KERNEL", "nosplit")
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N").describe()

@@ -519,10 +519,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if (sp > 64) sp = 64;
         p->ksplit = sp > 1 ? (int)sp : 1;
     }
-    // the fast kernel's K split (above) applies when the operands can be read in place
+    // the fast kernel's K split (above): on the operands in place or on their aligned copies
     p->fast_part = nullptr;
     p->finish = nullptr;
-    if (split_s && fast && !skinny) {
+    if (split_s && (fast || fast_pk) && !skinny) {
         p->fast_part = fast_table(ab_type, ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32)(op_a, op_b, 0);
         p->finish = finish_table(ab_type, cd_type);
         p->ksplit = split_s;
@@ -691,15 +691,16 @@ gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
     prm.ws = nullptr;
     // fast kernel with K split (needs its workspace; a first run inside a capture runs whole)
-    if (k == p->fast && !sk && p->fast_part &&
+    if ((k == p->fast || k == p->fast_pk) && !sk && p->fast_part &&
         skinny_workspace(p, static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
         const int S = p->ksplit;
         const int kc = (int)(p->K / S);                  // K of one chunk (whole slabs)
         GemmParams part = prm;
         part.K = kc;
         part.batch = S;
-        part.stride_a = p->op_a == GEMM_OP_N ? kc : (int64_t)kc * p->lda;
-        part.stride_b = p->op_b == GEMM_OP_N ? (int64_t)kc * p->ldb : kc;
+        // chunk offsets in the operands the kernel reads (the copies, when copied)
+        part.stride_a = p->op_a == GEMM_OP_N ? kc : (int64_t)kc * prm.lda;
+        part.stride_b = p->op_b == GEMM_OP_N ? (int64_t)kc * prm.ldb : kc;
         part.C = nullptr;
         part.D = p->ws;
         part.bias = nullptr;
