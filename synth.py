@@ -278,6 +278,16 @@ def fp16_8192_bias_relu():
                     name="fp16_8192_bias_relu")]
 
 
+def fp16_long_k():
+    """Few output tiles and a long K (the fast kernel's K split): fp16 2048 x 2048 x 8192 NN,
+    A,B ~ N(0,1)/sqrt(K), D = ReLU(acc + bias[N]) -> fp16, bias fp32 ~ U[-0.5,0.5]."""
+    K = 8192
+    s = 1.0 / math.sqrt(K)
+    return [Problem(2048, 2048, K, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                    a_dist=("normal", s), b_dist=("normal", s), key=(11, 0),
+                    name="fp16_long_k")]
+
+
 def bf16_layout_sweep():
     """bf16 in, fp32 C/D, alpha=1.5, beta=-0.5, A,B,C ~ U[-1,1], NN/NT/TN/TT on the ragged
     shapes 4095x3073x2047 and 5000^3."""
@@ -361,6 +371,7 @@ def complex_fp16():
 WORKLOADS = {
     "sgemm_256": sgemm_256,
     "fp16_8192_bias_relu": fp16_8192_bias_relu,
+    "fp16_long_k": fp16_long_k,
     "bf16_layout_sweep": bf16_layout_sweep,
     "int8_4096_bias": int8_4096_bias,
     "fc_layers": fc_layers,

@@ -149,27 +149,49 @@ uint32_t pair_job_blocks(const PairJob &j) {
 // ---- the K split's finishing step for int8 products ---------------------------------------------
 // D[m][n] = ReLU?(sum of the S int32 partial sums [split][M][N] in ws, in split order,
 // + beta * C (beta 0 or 1) + bias[n]); int32 arithmetic wraps exactly as the unsplit sum does.
+// One thread per 4 consecutive columns (16-byte loads of the partial sums when N % 4 == 0, the
+// split loop unrolled so that several loads are in flight).
 __global__ __launch_bounds__(256) void finish_int(GemmParams p) {
-    const int tiles = (p.N + 255) / 256;
+    constexpr int CPT = 4, SPAN = 256 * CPT;
+    const int tiles = (p.N + SPAN - 1) / SPAN;
     const int m = blockIdx.x / tiles;
-    const int n = (blockIdx.x - m * tiles) * 256 + (int)threadIdx.x;
-    if (m >= p.M || n >= p.N) return;
+    const int n0 = (blockIdx.x - m * tiles) * SPAN + (int)threadIdx.x * CPT;
+    if (m >= p.M || n0 >= p.N) return;
     const int S = p.tiles_m;
-    const int *ws = reinterpret_cast<const int *>(p.ws) + (int64_t)m * p.N + n;
-    uint32_t v = 0;
-    for (int q = 0; q < S; ++q) v += (uint32_t)ws[(int64_t)q * p.M * p.N];
-    const int64_t idx = (int64_t)m * p.ldc + n;
-    if (p.has_beta) v += (uint32_t)c_in_i(static_cast<const int *>(p.C)[idx], p.xform_c);
-    if (p.has_bias) v += (uint32_t)static_cast<const int *>(p.bias)[n];
-    int x = (int)v;
-    if (p.relu) x = x > 0 ? x : 0;
-    static_cast<int *>(p.D)[idx] = x;
+    const int64_t plane = (int64_t)p.M * p.N;
+    const uint32_t *ws = reinterpret_cast<const uint32_t *>(p.ws) + (int64_t)m * p.N + n0;
+    uint32_t v[CPT] = {0, 0, 0, 0};
+    if (p.N % CPT == 0) {
+#pragma unroll 4
+        for (int q = 0; q < S; ++q) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(ws + q * plane);
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) v[e] += w[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e)
+            if (n0 + e < p.N)
+                for (int q = 0; q < S; ++q) v[e] += ws[q * plane + e];
+    }
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+        const int n = n0 + e;
+        if (n >= p.N) break;
+        const int64_t idx = (int64_t)m * p.ldc + n;
+        uint32_t t = v[e];
+        if (p.has_beta) t += (uint32_t)c_in_i(static_cast<const int *>(p.C)[idx], p.xform_c);
+        if (p.has_bias) t += (uint32_t)static_cast<const int *>(p.bias)[n];
+        int x = (int)t;
+        if (p.relu) x = x > 0 ? x : 0;
+        static_cast<int *>(p.D)[idx] = x;
+    }
 }
 
 }  // namespace
 
 hipError_t finish_i8_i32(const GemmParams &p, hipStream_t s) {
-    const unsigned g = (unsigned)((int64_t)((p.N + 255) / 256) * p.M);
+    const unsigned g = (unsigned)((int64_t)((p.N + 1023) / 1024) * p.M);
     hipLaunchKernelGGL(finish_int, dim3(g), dim3(256), 0, s, p);
     return hipGetLastError();
 }

@@ -268,46 +268,76 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
 }
 
 // Split K, second step: D[m][n] = epilogue(sum of the S splits' partial sums, in split order).
-// One thread per output element; workgroup = 256 consecutive columns of one row of a product.
-template <class TO>
+// One thread per FCOLS consecutive output columns (FCOLS = 4: 16-byte loads of the partial sums
+// when N is a multiple of 4, for large outputs; 1 for small ones, which then get more
+// workgroups); the split loop is unrolled so that several loads are in flight; workgroup =
+// 256 * FCOLS consecutive columns of one row of a product.
+template <class TO, int FCOLS>
 __global__ __launch_bounds__(NT) void skinny_finish(GemmParams p) {
     using T = typename TO::T;
-    const int tiles = (p.N + NT - 1) / NT;
+    constexpr int SPAN = NT * FCOLS;
+    const int tiles = (p.N + SPAN - 1) / SPAN;
     const int per = tiles * p.M;
     const int prod = blockIdx.x / per;
     const int lid = select_batch<2, (int)sizeof(T)>(p, blockIdx.x, per);
     const int m = lid / tiles;
-    const int n = (lid - m * tiles) * NT + (int)threadIdx.x;
-    if (n >= p.N) return;
+    const int n0 = (lid - m * tiles) * SPAN + (int)threadIdx.x * FCOLS;
+    if (n0 >= p.N) return;
     const int S = p.tiles_m;
-    const float *ws = p.ws + (int64_t)prod * S * p.M * p.N + (int64_t)m * p.N + n;
-    float v = 0.0f;
-    for (int q = 0; q < S; ++q) v += ws[(int64_t)q * p.M * p.N];
-    const int64_t idx = (int64_t)m * p.ldc + n;
-    float x = p.alpha * v;
-    if (p.has_beta) x += p.beta * c_in_f(static_cast<const T *>(p.C)[idx], p.xform_c);
-    if (p.has_bias) x += static_cast<const float *>(p.bias)[n];
-    if (p.relu) x = x > 0.0f ? x : 0.0f;
-    static_cast<T *>(p.D)[idx] = (T)x;
+    const int64_t plane = (int64_t)p.M * p.N;
+    const float *ws = p.ws + (int64_t)prod * S * plane + (int64_t)m * p.N + n0;
+    float v[FCOLS];
+#pragma unroll
+    for (int e = 0; e < FCOLS; ++e) v[e] = 0.0f;
+    if (FCOLS == 1) {
+#pragma unroll 4
+        for (int q = 0; q < S; ++q) v[0] += ws[q * plane];
+    } else if (p.N % FCOLS == 0) {
+        // whole, 16-byte aligned groups (the workspace rows are N floats)
+#pragma unroll 4
+        for (int q = 0; q < S; ++q) {
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(ws + q * plane);
+#pragma unroll
+            for (int e = 0; e < FCOLS; ++e) v[e] += w[e & 3];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < FCOLS; ++e)
+            if (n0 + e < p.N)
+                for (int q = 0; q < S; ++q) v[e] += ws[q * plane + e];
+    }
+#pragma unroll
+    for (int e = 0; e < FCOLS; ++e) {
+        const int n = n0 + e;
+        if (n >= p.N) break;
+        const int64_t idx = (int64_t)m * p.ldc + n;
+        float x = p.alpha * v[e];
+        if (p.has_beta) x += p.beta * c_in_f(static_cast<const T *>(p.C)[idx], p.xform_c);
+        if (p.has_bias) x += static_cast<const float *>(p.bias)[n];
+        if (p.relu) x = x > 0.0f ? x : 0.0f;
+        static_cast<T *>(p.D)[idx] = (T)x;
+    }
+}
+
+// The finishing kernel (also used on its own by the fast kernel's K split, which writes the same
+// workspace layout): 4 columns per thread from 2^20 output elements per product, else 1.
+template <class TO>
+hipError_t launch_finish(const GemmParams &p, hipStream_t s) {
+    const bool wide = (int64_t)p.M * p.N >= ((int64_t)1 << 20);
+    const int span = NT * (wide ? 4 : 1);
+    const unsigned g = (unsigned)((int64_t)((p.N + span - 1) / span) * p.M * p.batch);
+    if (wide) hipLaunchKernelGGL((skinny_finish<TO, 4>), dim3(g), dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((skinny_finish<TO, 1>), dim3(g), dim3(NT), 0, s, p);
+    return hipGetLastError();
 }
 
 template <class TI, class TO, int MT, bool BT, int CB = NB>
 hipError_t launch_skinny(const GemmParams &p, unsigned grid, hipStream_t s) {
     hipLaunchKernelGGL((gemm_skinny<TI, TO, MT, BT, CB>), dim3(grid), dim3(NT), 0, s, p);
-    if (p.tiles_m > 1) {
-        const unsigned g2 = (unsigned)((int64_t)((p.N + NT - 1) / NT) * p.M * p.batch);
-        hipLaunchKernelGGL((skinny_finish<TO>), dim3(g2), dim3(NT), 0, s, p);
-    }
+    if (p.tiles_m > 1) return launch_finish<TO>(p, s);
     return hipGetLastError();
 }
 
-// The finishing kernel on its own (the fast kernel's K split writes the same workspace layout).
-template <class TO>
-hipError_t launch_finish(const GemmParams &p, hipStream_t s) {
-    const unsigned g = (unsigned)((int64_t)((p.N + NT - 1) / NT) * p.M * p.batch);
-    hipLaunchKernelGGL((skinny_finish<TO>), dim3(g), dim3(NT), 0, s, p);
-    return hipGetLastError();
-}
 
 // narrow = 1: the 16-column variant (B transposed only)
 template <class TI, class TO>
