@@ -600,6 +600,24 @@ def test_fast_k_split_int8_exact(lay, shape, monkeypatch):
     check(p, x, D, reference(p, x), exact=True)
 
 
+@pytest.mark.parametrize("shape", [(16, 4096, 4096), (5, 1000, 2048), (64, 520, 1024),
+                                   (33, 4096, 8192)])
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_fast_k_split_short_int8_exact(lay, shape):
+    # the plan's own choice for short int8 products: the fast kernel with K split into chunks
+    # of 2 slabs or more, int32 partial sums, the integer finishing kernel; bias, beta = 1, ReLU
+    M, N, K = shape
+    i = LAYOUTS.index(lay) + 4 * [(16, 4096, 4096), (5, 1000, 2048), (64, 520, 1024),
+                                  (33, 4096, 8192)].index(shape)
+    p = _exact(M, N, K, lay, "i8", "i32", EPIS[i % 4], 1.0, 1.0 if i % 2 else 0.0, key=(131, i))
+    x = synth.make_inputs(p)
+    print(p.label(), flush=True)
+    D, pl = run(p, x)
+    assert "gemm_fast_256x256 " in pl.describe() or "repack" in pl.describe() or \
+        "gemm_mfma" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
 def test_fast_k_split_graph_capture(monkeypatch):
     # no workspace yet inside the first capture: that run is not split; after an eager run the
     # captured runs split; every replay gives the eager result bit for bit
