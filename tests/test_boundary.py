@@ -320,6 +320,10 @@ def test_fast_k_split_described(monkeypatch):
     assert "gemm_fast_256x256 " in d and "ksplit 16" in d, d
     d = tge.Plan(64, 8192, 4096, "N", "T", ab="i8", cd="i32").describe()
     assert "gemm_fast_256x256 " in d and "ksplit 8" in d, d
+    # ... and short 16-bit products with A transposed (the skinny kernel needs A not transposed)
+    d = tge.Plan(16, 4096, 4096, "T", "N").describe()
+    assert "gemm_fast_256x256 " in d and "ksplit 16" in d, d
+    assert "gemm_skinny" in tge.Plan(16, 4096, 4096, "N", "N").describe()
     # an operand off the 16-byte grid is copied first, then split as well
     d = tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
     assert "ksplit 4" in d and "repack A" in d, d

@@ -618,6 +618,22 @@ def test_fast_k_split_short_int8_exact(lay, shape):
     check(p, x, D, reference(p, x), exact=True)
 
 
+@pytest.mark.parametrize("shape", [(16, 4096, 4096), (5, 1000, 2048), (64, 520, 1024)])
+@pytest.mark.parametrize("lb", ["N", "T"])
+@pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("bf16", "f32")])
+def test_fast_k_split_short_transposed_a_exact(ab, cd, lb, shape):
+    # short 16-bit products with A transposed (no skinny kernel): the plan's K split into chunks
+    # of 2 slabs or more
+    M, N, K = shape
+    i = (lb == "T") + 2 * [(16, 4096, 4096), (5, 1000, 2048), (64, 520, 1024)].index(shape)
+    p = _exact(M, N, K, "T" + lb, ab, cd, EPIS[i % 4], *SCALARS[i % 4], key=(132, i))
+    x = synth.make_inputs(p)
+    print(p.label(), flush=True)
+    D, pl = run(p, x)
+    assert "gemm_fast_256x256 " in pl.describe() and " ksplit " in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x), exact=True)
+
+
 def test_fast_k_split_graph_capture(monkeypatch):
     # no workspace yet inside the first capture: that run is not split; after an eager run the
     # captured runs split; every replay gives the eager result bit for bit

@@ -343,9 +343,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // sums (fp32, int32 for int8) go to a workspace and the finishing kernel adds them in chunk
     // order and applies the epilogue.  One product, no load transforms.  Such a plan takes the
     // fast kernel even where the general one would otherwise run: measured 1.1-2.9x faster
-    // from 64 slabs, slower at 2048^3 (32 slabs).  Short int8 products (M <= 64, which have no
-    // skinny kernel) split down to chunks of 2 slabs: their partial sums are small, and the
-    // split measured 3-6x faster than the general kernel (16 x 4096 x 4096: 97 -> 17 us)
+    // from 64 slabs, slower at 2048^3 (32 slabs).  Short products the skinny kernel cannot take
+    // (M <= 64 with int8 inputs, or with A transposed) split down to chunks of 2 slabs: their
+    // partial sums are small, and the split measured 1.1-6x faster than the general kernel
+    // (int8 16 x 4096 x 4096: 97 -> 17 us; fp16 TN: 135 -> 28 us)
     // (TGE_FORCE_KERNEL=split: any S >= 2, chunks of one slab or more; =nosplit: never).
     int split_s = 0;
     const bool force_split = fk && strcmp(fk, "split") == 0;
@@ -359,7 +360,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t slabs = K / slab_k;
         int64_t sp = tiles > 0 ? 256 / tiles : 0;
-        const bool short_i8 = ab_type == GEMM_I8 && M <= 64;
+        const bool short_i8 = M <= 64 && (ab_type == GEMM_I8 || op_a == GEMM_OP_T);
         const int64_t min_chunk = force_split ? 1 : short_i8 ? 2 : 16;
         if (sp > slabs / min_chunk) sp = slabs / min_chunk;
         while (sp > 1 && slabs % sp) --sp;
