@@ -439,3 +439,51 @@ def test_dual_numbers_carry_the_derivative():
     # and differs from the complex product exactly by the dropped -Xd*Yd term
     c = oracle.gemm_pair(M, N, K, "N", "N", A, lda, B, ldb, "cf16")
     assert np.array_equal(c[..., 0], got[..., 0] - xd @ yd)
+
+
+# ---- the tolerance normaliser ------------------------------------------------------------------
+
+def check_max_abs_op_pins(mod):
+    """max |op(X)| over the elements op(X) uses, on hand-built stored arrays whose padding and
+    trailing storage hold larger values that must be left out (the tolerance's denominator,
+    K * max|op(A)| * max|op(B)|, is defined over op(A) and op(B) only)."""
+    h = lambda v: np.asarray(v, np.float16).view(np.uint16)
+    # op N, 2 x 3 stored with ld 5: padding columns hold 99; max |.| = 7
+    xn = h([[1, -7, 2, 99, 99], [3, 0.5, -4, 99, 99]])
+    assert mod.max_abs_op("f16", xn, "N", 2, 3, 5) == 7.0
+    # op T: op(X) is 3 x 2, stored 2 x 3 with ld 4 (column 3 is padding, -70 there); max = 9
+    xt = h([[1, 2, -9, 50], [0.25, 6, 3, -70]])
+    assert mod.max_abs_op("f16", xt, "T", 3, 2, 4) == 9.0
+    # the same storage read as op N 2 x 3 (ld 4) has the same elements
+    assert mod.max_abs_op("f16", xt, "N", 2, 3, 4) == 9.0
+    # storage past the last used element (a larger array, another product) is not part of it
+    tail = np.concatenate([h([[0.5, -1.5, 1]]).reshape(-1), h([-64.0])])
+    assert mod.max_abs_op("f16", tail, "N", 1, 3, 3) == 1.5
+    # the largest element sits in the last used position of the last stored row
+    xl = h([[1, 2, 0, 100], [3, -11, 0, 100]])
+    assert mod.max_abs_op("f16", xl, "T", 2, 2, 4) == 11.0
+    # int8, bf16, fp32 decode by value; empty operands give 0
+    assert mod.max_abs_op("i8", np.array([[-128, 5], [3, 127]], np.int8), "N", 2, 2, 2) == 128.0
+    bf = (np.array([[-2.5, 1.0], [0.75, 300.0]], np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert mod.max_abs_op("bf16", bf, "N", 2, 1, 2) == 2.5
+    assert mod.max_abs_op("f32", np.array([1.0, -3.0, 8.0], np.float32), "T", 2, 1, 3) == 3.0
+    assert mod.max_abs_op("f16", xn, "N", 0, 3, 5) == 0.0
+
+
+def test_max_abs_op_pins():
+    check_max_abs_op_pins(oracle)
+
+
+def test_max_abs_op_matches_a_dense_view():
+    # random stored arrays with padded ld: the maximum over the numpy view op(X)
+    g = np.random.default_rng(5)
+    for op in ("N", "T"):
+        rows, cols, pad = 37, 23, 6
+        srows, slen = (rows, cols) if op == "N" else (cols, rows)
+        ld = slen + pad
+        vals = g.uniform(-1, 1, (srows, ld))
+        vals[:, slen:] = 1e4                      # padding larger than every used value
+        x = vals.astype(np.float16)
+        view = x[:, :slen] if op == "N" else x[:, :slen].T
+        want = float(np.abs(view.astype(np.float64)).max())
+        assert oracle.max_abs_op("f16", x.view(np.uint16), op, rows, cols, ld) == want

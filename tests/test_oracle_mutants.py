@@ -47,3 +47,39 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle.py")], env=env, cwd=ROOT,
                        capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"planted mistake {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+# planted mistakes in the Python side of the oracle (the tolerance normaliser)
+PY_MUTANTS = {
+    "t_rows_cols_swapped": ("    else:\n        idx_ok = (np.arange(d.size) % ld) < rows",
+                            "    else:\n        idx_ok = (np.arange(d.size) % ld) < cols"),
+    "padding_included": ("    if op == \"N\":\n        idx_ok = (np.arange(d.size) % ld) < cols",
+                         "    if op == \"N\":\n        idx_ok = (np.arange(d.size) % ld) < ld"),
+    "span_one_short": ("d = decode(dtype, _raw(dtype, X)[: _span(op, rows, cols, ld)])",
+                       "d = decode(dtype, _raw(dtype, X)[: _span(op, rows, cols, ld) - 1])"),
+    "whole_storage": ("d = decode(dtype, _raw(dtype, X)[: _span(op, rows, cols, ld)])",
+                      "d = decode(dtype, _raw(dtype, X))"),
+    "sign_kept": ("return float(np.max(np.abs(d[idx_ok]))) if idx_ok.any() else 0.0",
+                  "return float(np.max(d[idx_ok])) if idx_ok.any() else 0.0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_normaliser_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
+    import importlib.util
+
+    import oracle
+    from test_oracle import check_max_abs_op_pins
+
+    old, new = PY_MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert old in src, f"mutation anchor for {name} not found"
+    path = tmp_path / "oracle_mut.py"
+    path.write_text(src.replace(old, new))
+    # the mutated module uses the same C library as the real one
+    monkeypatch.setenv("ORACLE_LIB", oracle._LIB_PATH)
+    spec = importlib.util.spec_from_file_location("oracle_mut", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with pytest.raises(AssertionError):
+        check_max_abs_op_pins(mod)
