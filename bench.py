@@ -20,9 +20,15 @@ the 256 MB infinity cache; the cache-hot figure of one reused set is reported be
 roofline.traffic is the measured HBM traffic per launch (FETCH_SIZE + WRITE_SIZE from rocprofv3,
 each scaled by what the same counter reads for a plain copy of known size), taken from the
 summary profiles/traffic_<workload>.json when that summary was measured on the current kernel
-sources (it records their hash); otherwise null.  clocks holds rocm-smi's core and memory clock
-readings just before the warm-up and right after the timed launches (the clock the kernel ran at
-on average comes from the counters in profiles/).
+sources (it records their hash); otherwise null.  clocks holds the driver's current core and
+memory clock levels (sysfs) just before the warm-up and right after the timed launches.
+
+Timing protocol: W untimed warm-up launches, then blocks of exactly K launches (one HIP graph of
+K launches, replayed), each bracketed by device synchronisations and timed with HIP events on
+the launch stream; blocks repeat until the last five agree within a coefficient of variation of
+2 % (at most 30 blocks), and the reported time per launch is the median of those five blocks
+("Flexible Performant GEMM Kernels on GPUs", section 5: samples are taken until the spread of
+the timings is small).  Every block runs the full product on the same resident inputs.
 """
 import argparse
 import hashlib
@@ -128,26 +134,25 @@ def cpu_model():
 
 
 def gpu_clocks():
-    """Current GPU core (sclk) and memory (mclk) clocks in MHz from rocm-smi, run as a child
-    process (None when it is not available)."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        cards = json.loads(r.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
+    """Current GPU core (sclk) and memory (mclk) clocks in MHz, read in-process from the amdgpu
+    driver's sysfs tables (the level marked '*' in pp_dpm_sclk / pp_dpm_mclk); None where the
+    files are absent.  No child process: this runs after the GPU has been initialised."""
+    import glob
     out = {}
-    for card, fields in cards.items():
-        if not isinstance(fields, dict):
-            continue
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
         clk = {}
-        for key, val in fields.items():
-            for name in ("sclk", "mclk"):
-                if key.startswith(name) and "speed" in key:
-                    digits = "".join(ch for ch in str(val) if ch.isdigit())
+        for name in ("sclk", "mclk"):
+            try:
+                with open(os.path.join(dev, f"pp_dpm_{name}")) as fh:
+                    lines = fh.read().splitlines()
+            except OSError:
+                continue
+            for line in lines:
+                if line.rstrip().endswith("*"):
+                    digits = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
                     clk[name + "_MHz"] = int(digits) if digits else None
-        out[card] = clk
+        if clk:
+            out[os.path.basename(os.path.dirname(dev))] = clk
     return out or None
 
 
@@ -161,12 +166,14 @@ def pick_workload(spec):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="fp16_8192_bias_relu")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--no-graph", action="store_true",
                     help="time K eager launches instead of one graph of K launches")
+    ap.add_argument("--max-blocks", type=int, default=30,
+                    help="most timed blocks of --steps launches (fewer once they agree)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -233,7 +240,8 @@ def main():
     stream.wait_stream(torch.cuda.current_stream())
 
     def time_launches(sets):
-        """ms per launch over args.steps launches cycling through the operand sets."""
+        """(median ms per launch, wall ms per launch, blocks) over blocks of args.steps launches
+        cycling through the operand sets."""
         with torch.cuda.stream(stream):
             for i in range(args.warmup):
                 plan.run(*sets[i % len(sets)], p.alpha, p.beta)
@@ -247,27 +255,42 @@ def main():
             torch.cuda.synchronize()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            if graph is not None:
-                graph.replay()
-            else:
-                for i in range(args.steps):
-                    plan.run(*sets[i % len(sets)], p.alpha, p.beta)
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        return ev0.elapsed_time(ev1) / max(1, args.steps), wall * 1e3 / max(1, args.steps)
+        times, walls = [], []
+        window = 5
+        while True:
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            with torch.cuda.stream(stream):
+                ev0.record(stream)
+                if graph is not None:
+                    graph.replay()
+                else:
+                    for i in range(args.steps):
+                        plan.run(*sets[i % len(sets)], p.alpha, p.beta)
+                ev1.record(stream)
+            torch.cuda.synchronize()
+            walls.append((time.perf_counter() - w0) * 1e3 / max(1, args.steps))
+            times.append(ev0.elapsed_time(ev1) / max(1, args.steps))
+            last = np.array(times[-window:])
+            cv = float(last.std() / last.mean()) if len(last) == window else 1.0
+            if cv < 0.02 or len(times) >= args.max_blocks:
+                break
+        log(f"[bench] blocks of {args.steps} launches (ms/launch): "
+            + " ".join(f"{t:.4f}" for t in times) + f"; last {len(last)}: CV {cv:.4f}")
+        blocks = {"launches_per_block": args.steps, "blocks": len(times),
+                  "window": len(last), "cv": round(cv, 5),
+                  "median_of_window_ms": round(float(np.median(last)), 5),
+                  "first_block_ms": round(times[0], 5)}
+        return float(np.median(last)), float(np.median(walls[-window:])), blocks
 
     base = (A, B, C, D, bias)
     clocks = {"before": gpu_clocks()}
-    ms_hot, ms_wall = time_launches([base])
+    ms_hot, ms_wall, blocks = time_launches([base])
     # right after the timed launches (the clock reading comes from sysfs a moment later)
     clocks["after"] = gpu_clocks()
     log(f"[bench] clocks before / after the timed launches: {clocks}")
-    log(f"[bench] {args.steps} steps: {ms_hot:.4f} ms/launch (events), {ms_wall:.4f} ms/step (wall)")
+    log(f"[bench] {args.steps} steps per block: {ms_hot:.4f} ms/launch (events, median), "
+        f"{ms_wall:.4f} ms/step (wall)")
     ms_events, hot = ms_hot, None
     if hbm_bound:
         # a working set this small stays in the 256 MB infinity cache when one set of operands
@@ -276,7 +299,7 @@ def main():
         nsets = max(16 if bytes_alg < 64e6 else 2, int(np.ceil(512e6 / bytes_alg)))
         clone = lambda t: None if t is None else t.clone()
         sets = [base] + [tuple(clone(t) for t in base) for _ in range(nsets - 1)]
-        ms_events, ms_wall = time_launches(sets)
+        ms_events, ms_wall, blocks = time_launches(sets)
         log(f"[bench] {nsets} rotating operand sets: {ms_events:.4f} ms/launch (events)")
         hot = {"ms_per_step": round(ms_hot, 5), "operand_sets": 1,
                "achieved_GBps": round(bytes_alg / (ms_hot * 1e-3) / 1e9, 1)}
@@ -372,8 +395,11 @@ def main():
                    "layout": p.op_a + p.op_b,
                    "ab": p.ab, "cd": p.cd, "epilogue": p.epi, "alpha": p.alpha, "beta": p.beta,
                    "kernel": plan.describe(), "frac_of_peak": round(tflops / peak, 4),
-                   "launch": "eager" if graph is None else f"one HIP graph of {args.steps} launches"},
+                   "launch": "eager" if graph is None else
+                   f"blocks of one HIP graph of {args.steps} launches, median of the last "
+                   f"{blocks['window']}"},
         "roofline": roof,
+        "timing": blocks,
         "clocks": clocks,
         "cpu_baseline": cpu,
         "parity": parity,

@@ -32,13 +32,14 @@
  *
  * Ownership: the caller owns every device buffer and keeps it alive until the stream work that
  * uses it has finished.  A plan is a small host object, destroyed with gemm_plan_destroy.  Most
- * plans hold no device memory and may be shared between host threads and streams.  A plan for
- * plan that splits K over workgroups ("ksplit S" in its description: a short product, M <= 64,
- * or a product with few output tiles and a long K) owns a split-K workspace (S * M * N
- * floats per product of the batch) on the device of its first gemm_run, allocated by that call
- * and freed by gemm_plan_destroy: its runs must not overlap in time (use one plan per concurrent
- * stream).  A short product's first run must not be captured into a graph (later runs may be);
- * the other kind's first run inside a capture runs unsplit.  Such a run enqueues two kernels.
+ * plans hold no device memory and may be shared between host threads and streams.  A plan that
+ * splits K over workgroups ("ksplit S" in its description: a short product, M <= 64, or a
+ * product with few output tiles and a long K) owns a split-K workspace (S * M * N floats per
+ * product of the batch) on the device of its first gemm_run, allocated by that call and freed
+ * by gemm_plan_destroy: its runs must not overlap in time (use one plan per concurrent stream).
+ * The first run of a skinny split-K plan ("gemm_skinny... ksplit S") must not be captured into a
+ * graph (later runs may be); the first run of a fast-kernel split-K plan inside a capture runs
+ * unsplit.  A split run enqueues the partial products and a finishing kernel.
  * A large 16- or 8-bit plan whose operand rows are off the 16-byte grid (an odd leading
  * dimension or batch stride, an unaligned pointer at run time, or an M/N-contiguous row length
  * that is not a multiple of 16 bytes), or with a load transform on op(A) or op(B), first copies
@@ -56,8 +57,9 @@
  * destroy such a plan only after the graphs that captured it.
  *
  * Errors: every function returns a status; nothing throws across this boundary.  gemm_run is
- * asynchronous: it validates, enqueues its kernels (one, or two as above) on `stream` and
- * returns; faults during execution surface at the caller's next synchronisation.
+ * asynchronous: it validates, enqueues its kernels on `stream` and returns (one kernel; or,
+ * as above, a copy or rewrite pass, the product, and a finishing kernel when K is split: up to
+ * three); faults during execution surface at the caller's next synchronisation.
  */
 #ifndef TGE_GEMM_H
 #define TGE_GEMM_H
@@ -102,7 +104,9 @@ typedef enum {
     GEMM_STATUS_INVALID_VALUE = 1, /* a bad argument: negative size, ld too small, NULL pointer */
     GEMM_STATUS_NOT_SUPPORTED = 2, /* a valid request this library does not implement */
     GEMM_STATUS_HIP_ERROR = 3,     /* the HIP runtime reported an error at launch */
-    GEMM_STATUS_ALLOC_FAILED = 4   /* host memory for the plan could not be allocated */
+    GEMM_STATUS_ALLOC_FAILED = 4   /* memory could not be allocated: host memory for a plan
+                                      (plan creation), or device memory for a plan's split-K
+                                      workspace (gemm_run) */
 } gemm_status_t;
 
 /*
@@ -124,6 +128,30 @@ typedef enum { GEMM_TRANSFORM_NONE = 0, GEMM_TRANSFORM_RELU = 1 } gemm_transform
  */
 typedef enum { GEMM_OPERAND_DENSE = 0, GEMM_OPERAND_DIAGONAL = 1 } gemm_operand_t;
 
+/*
+ * Kernel choice of a plan.  GEMM_ALGO_AUTO lets the plan choose from the shape, types and
+ * layouts (the rule is described by gemm_plan_describe's text); the others pin a route, for
+ * comparisons and tests, and fall back to the general kernel where the pinned route's
+ * preconditions do not hold:
+ *   FAST         the 256x256 fast kernel (16- and 8-bit inputs), with its K split when the
+ *                plan's rule asks for one;
+ *   FAST_STAGED  the fast kernel, reading operands that are off the 16-byte grid in place
+ *                through registers instead of copying them first;
+ *   GENERAL      the general tiled kernel, never the fast, skinny or split routes;
+ *   SKINNY       the memory-bound kernel for M <= 64 wherever its preconditions hold;
+ *   SPLIT        the fast kernel with K split into any number >= 2 of whole-slab chunks;
+ *   NOSPLIT      the plan's own choice without a K split.
+ */
+typedef enum {
+    GEMM_ALGO_AUTO = 0,
+    GEMM_ALGO_FAST = 1,
+    GEMM_ALGO_FAST_STAGED = 2,
+    GEMM_ALGO_GENERAL = 3,
+    GEMM_ALGO_SKINNY = 4,
+    GEMM_ALGO_SPLIT = 5,
+    GEMM_ALGO_NOSPLIT = 6
+} gemm_algo_t;
+
 typedef struct gemm_plan *gemm_plan_t;
 
 /*
@@ -132,7 +160,10 @@ typedef struct gemm_plan *gemm_plan_t;
  * (batch 1 and zero strides for a single product); transform_a / transform_b act on op(A) and
  * op(B) (zero-padding past the edges is unaffected), transform_c on C before it is scaled by
  * beta; kind_a / kind_b make an operand diagonal (see gemm_operand_t; a diagonal operand's
- * stride_a / stride_b moves its vector).  Plain data: the library keeps no pointer to it.
+ * stride_a / stride_b moves its vector); algo pins the kernel route (see gemm_algo_t;
+ * GEMM_ALGO_AUTO for the plan's own choice) and tile the workgroup tile of the general kernel
+ * (256, 128 or 64; 0 for the plan's own choice; 256 also selects the fast kernel where it
+ * applies).  Plain data: the library keeps no pointer to it.
  */
 typedef struct {
     int64_t M, N, K;
@@ -144,6 +175,8 @@ typedef struct {
     int64_t stride_a, stride_b, stride_c, stride_bias;
     gemm_transform_t transform_a, transform_b, transform_c;
     gemm_operand_t kind_a, kind_b;
+    gemm_algo_t algo;
+    int32_t tile;
 } gemm_desc_t;
 
 /*
@@ -157,9 +190,8 @@ typedef struct {
  *   epi            epilogue kind.
  * Returns INVALID_VALUE for negative sizes, leading dimensions below the minimum, an enum out of
  * range or out == NULL; NOT_SUPPORTED for a type pair outside the table or when a matrix spans
- * 2^31 bytes or more.
- * The workgroup tile is chosen from the shape; the environment variable TGE_FORCE_TILE=256, 128
- * or 64, read at plan creation, pins it (for tests and tuning sweeps).
+ * 2^31 bytes or more.  The kernel and workgroup tile are chosen from the shape (see
+ * gemm_plan_create_desc to pin them).
  */
 gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K, gemm_op_t op_a,
                                gemm_op_t op_b, int64_t lda, int64_t ldb, int64_t ldc,
@@ -192,8 +224,8 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
  * and gemm_plan_create_batched plus the load transforms,
  *   D_b = act(alpha * tA(op(A_b)) * tB(op(B_b)) + beta * tC(C_b) + bias_b).
  * Returns the errors of gemm_plan_create_batched, plus INVALID_VALUE for desc == NULL, a
- * transform or operand kind out of range, or a diagonal operand that is not square (K != M for
- * A, K != N for B).
+ * transform, operand kind or algorithm out of range, a tile other than 0, 256, 128 or 64, or a
+ * diagonal operand that is not square (K != M for A, K != N for B).
  */
 gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
 
@@ -208,12 +240,12 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
  *            includes a bias, ignored otherwise.
  * For a batched plan every pointer is that of product 0 (see gemm_plan_create_batched).
  *   alpha, beta  scalars applied in fp32 (int8 plans require alpha == 1 and beta in {0, 1}).
- * Returns INVALID_VALUE for a NULL plan or a missing required pointer, NOT_SUPPORTED for int8
- * scalars outside the rule above or for the first run of a short (M <= 64) split-K plan during
- * stream capture, ALLOC_FAILED when that first run cannot allocate its workspace (the plans
- * that copy or rewrite operands, or split K for the fast kernel, run without their workspace
- * instead), HIP_ERROR when a launch fails.  M == 0, N == 0 or a batch of 0 returns SUCCESS
- * without launching.
+ * Returns INVALID_VALUE for a NULL plan, a missing required pointer or a NaN scalar,
+ * NOT_SUPPORTED for int8 scalars outside the rule above or for the first run of a skinny split-K
+ * plan during stream capture, ALLOC_FAILED when that first run cannot allocate its workspace
+ * (the plans that copy or rewrite operands, or split K for the fast kernel, run without their
+ * workspace instead), HIP_ERROR when a launch fails.  M == 0, N == 0 or a batch of 0 returns
+ * SUCCESS without launching.
  */
 gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream);

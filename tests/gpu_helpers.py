@@ -9,6 +9,8 @@ import tiled_gemm_epilogues_amd as tge
 
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
             "i32": torch.int32}
+# kernel route pinned by a test (gemm_algo_t name, tile); the plans built here take it
+FORCE = {"algo": "auto", "tile": 0}
 TOL = 2e-3          # max|D-ref| / (K * max|op(A)| * max|op(B)|) for float outputs
 DEV = "cuda:0"
 
@@ -53,7 +55,8 @@ def run(p, x, offset=0, d_rows_extra=0, c_is_d=False, stream=None, plan=None):
     bias = to_dev(p.bias_dt, x["bias"], offset) if x["bias"] is not None else None
     pl = plan or tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                           transform_a=p.transform_a, transform_b=p.transform_b,
-                          transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b)
+                          transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b,
+                          algo=FORCE["algo"], tile=FORCE["tile"])
     pl.run(A, B, C, D, bias, p.alpha, p.beta, stream=stream)
     torch.cuda.synchronize()
     return to_host(p.cd, D).reshape(rows, p.ldc), pl
@@ -130,7 +133,7 @@ def run_batched(p, x, offset=0):
                   batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
                   stride_bias=p.stride_bias, transform_a=p.transform_a,
                   transform_b=p.transform_b, transform_c=p.transform_c, kind_a=p.kind_a,
-                  kind_b=p.kind_b)
+                  kind_b=p.kind_b, algo=FORCE["algo"], tile=FORCE["tile"])
     pl.run(A, B, C, D, bias, p.alpha, p.beta)
     torch.cuda.synchronize()
     return to_host(p.cd, D).reshape(-1), pl

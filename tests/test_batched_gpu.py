@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from dataclasses import replace
-from gpu_helpers import reference_batched, run_batched, sentinel
+from gpu_helpers import FORCE, reference_batched, run_batched, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,7 @@ CASES = [
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_batched_exact(case, monkeypatch):
     kern, M, N, K, lay, ab, cd, epi, alpha, beta, batch, strides = CASES[case]
-    monkeypatch.setenv("TGE_FORCE_KERNEL", kern)
+    monkeypatch.setitem(FORCE, "algo", kern)
     if ab == "i8":
         p = synth.Problem(M, N, K, lay[0], lay[1], "i8", "i32", epi, 1.0, beta,
                           a_dist=("int", -128, 127), b_dist=("int", -128, 127),
@@ -78,7 +78,7 @@ def test_batched_exact(case, monkeypatch):
 def test_batched_unaligned_stride(mode, monkeypatch):
     # a stride that moves product 1 off 16-byte alignment: the direct loads cannot read A in
     # place; A is copied per product into aligned rows (fast) or the register-staged kernel runs
-    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
+    monkeypatch.setitem(FORCE, "algo", mode)
     p = synth.exact_integer_problem(256, 264, 128, "N", "N", "f16", "f16", "bias", 1.0, 0.0,
                                     key=(121, 0), batch=2, stride_a=256 * 128 + 3)
     x = synth.make_inputs(p)
@@ -94,7 +94,7 @@ def test_batched_unaligned_stride(mode, monkeypatch):
 def test_batched_repack_shared_and_strided(lay, monkeypatch):
     # odd leading dimensions and strides, B shared by every product (stride 0, one copy) and
     # a per-product bias; bf16 -> f32 with beta over three products
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     M, N, K = 300, 261, 200
     ra = (M if lay[0] == "N" else K)
     p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], "bf16", "f32", "bias_relu", 1.0, 1.0,

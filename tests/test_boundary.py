@@ -115,10 +115,23 @@ def test_destroy_null_is_noop():
     assert tge.gemm_plan_destroy(None) == tge.STATUS_SUCCESS
 
 
-def test_forced_tile(monkeypatch):
+def test_forced_tile():
     for t in (256, 128, 64):
-        monkeypatch.setenv("TGE_FORCE_TILE", str(t))
-        assert f"tile {t}x{t}" in tge.Plan(100, 100, 100).describe()
+        assert f"tile {t}x{t}" in tge.Plan(100, 100, 100, tile=t).describe()
+
+
+def test_plans_ignore_the_environment(monkeypatch):
+    # the kernel choice comes from the description only: no environment variable steers it
+    base = tge.Plan(8192, 8192, 8192).describe()
+    for var in ("TGE_FORCE_KERNEL", "TGE_FORCE_TILE"):
+        monkeypatch.setenv(var, "general" if var.endswith("KERNEL") else "64")
+    assert tge.Plan(8192, 8192, 8192).describe() == base
+
+
+@pytest.mark.parametrize("kw", [dict(algo=7), dict(algo=-1), dict(tile=32), dict(tile=-256)])
+def test_invalid_algo_or_tile(kw):
+    st, h = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, "f16", "f16", "none", **kw)
+    assert st == tge.STATUS_INVALID_VALUE and h is None
 
 
 def test_single_hip_runtime_in_process():
@@ -235,11 +248,10 @@ def test_kernel_choice(shape, lay, ab, cd, want, extra):
 
 @pytest.mark.parametrize("shape,lay", [((4095, 3073, 2047), "NN"), ((4095, 3073, 2047), "TN"),
                                        ((4096, 4100, 4096), "NN")])
-def test_kernel_choice_register_staged(shape, lay, monkeypatch):
-    # TGE_FORCE_KERNEL=staged: the register-staged variant reads such operands in place
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "staged")
+def test_kernel_choice_register_staged(shape, lay):
+    # algorithm "staged": the register-staged variant reads such operands in place
     M, N, K = shape
-    d = tge.Plan(M, N, K, lay[0], lay[1], ab="bf16", cd="f32").describe()
+    d = tge.Plan(M, N, K, lay[0], lay[1], ab="bf16", cd="f32", algo="staged").describe()
     assert "gemm_fast_256x256_rs" in d and "repack" not in d, d
 
 
@@ -300,7 +312,7 @@ def test_transform_copies_only_for_the_fast_kernel():
     assert "repack" not in d, d
 
 
-def test_fast_k_split_described(monkeypatch):
+def test_fast_k_split_described():
     # few 256x256 tiles and K >= 4096: K cut into chunks of at least 16 slabs, tiles x S >= 128
     d = tge.Plan(2048, 2048, 8192, "N", "N").describe()
     assert "gemm_fast_256x256 " in d and "ksplit 4" in d, d
@@ -327,5 +339,4 @@ def test_fast_k_split_described(monkeypatch):
     # an operand off the 16-byte grid is copied first, then split as well
     d = tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
     assert "ksplit 4" in d and "repack A" in d, d
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "nosplit")
-    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N").describe()
+    assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", algo="nosplit").describe()

@@ -2,7 +2,7 @@
 four-real-product definition: bit-exact on integer parts in every layout, with ragged edges, K
 tails, beta, both output types and a batch.  Both routes are covered: the complex kernel
 (interleaved in global memory, split in LDS) and, where the real fast kernels apply, the real
-product on 2 x 2 blocks (TGE_FORCE_KERNEL=fast makes small shapes take it)."""
+product on 2 x 2 blocks (the algorithm "fast" makes small shapes take it)."""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +10,7 @@ import torch
 import oracle
 import synth
 import tiled_gemm_epilogues_amd as tge
+from gpu_helpers import FORCE
 
 pytestmark = pytest.mark.gpu
 LAYOUTS = ["NN", "NT", "TN", "TT"]
@@ -34,7 +35,8 @@ def _run(p, x):
     D = torch.full((nD,), float("nan"), dtype=torch.float16 if part == "f16" else torch.float32,
                    device="cuda")
     pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, "none",
-                  batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c)
+                  batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
+                  algo=FORCE["algo"])
     C = _dev(x["C"]) if x["C"] is not None else None
     pl.run(_dev(x["A"]), _dev(x["B"]), C, D, None, p.alpha, p.beta)
     torch.cuda.synchronize()
@@ -67,7 +69,7 @@ def _route_ok(pl, ab, mode, K):
 @pytest.mark.parametrize("types", range(len(TYPES)))
 def test_complex_dual_exact(types, lay, shape, mode, monkeypatch):
     if mode == "fast":
-        monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+        monkeypatch.setitem(FORCE, "algo", "fast")
     ab, cd = TYPES[types]
     M, N, K = SHAPES[shape]
     i = types * 100 + LAYOUTS.index(lay) * 10 + shape
@@ -87,7 +89,7 @@ def test_complex_dual_exact(types, lay, shape, mode, monkeypatch):
 @pytest.mark.parametrize("mode", ["auto", "fast"])
 def test_complex_batched(mode, monkeypatch):
     if mode == "fast":
-        monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+        monkeypatch.setitem(FORCE, "algo", "fast")
     p = synth.Problem(200, 136, 96, "N", "T", "cf16", "cf32", "none", 1.0, 0.0,
                       a_dist=("int", -4, 4), b_dist=("int", -4, 4), key=(151, 0), batch=3,
                       stride_b=0)
@@ -120,7 +122,7 @@ def test_complex_random_full_size_rows():
 def test_complex_as_real_blocks_batched_strided(lay, monkeypatch):
     # dual numbers through the real product: per-product A (odd stride), shared B, beta, fp16
     # output, odd leading dimensions
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     M, N, K = 130, 72, 90
     ra = M if lay[0] == "N" else K
     p = synth.Problem(M, N, K, lay[0], lay[1], "df16", "df16", "none", 2.0, -1.0,
@@ -144,11 +146,12 @@ def test_complex_as_real_blocks_graph_capture(monkeypatch):
     # a first run inside a capture has no workspace for the rewritten operands: the complex
     # kernel runs; after an eager run, captured runs take the real product; every replay, with
     # eager work between, gives the exact result
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     p = synth.Problem(200, 136, 96, "T", "N", "cf16", "cf32", "none", 1.0, 0.0,
                       a_dist=("int", -4, 4), b_dist=("int", -4, 4), key=(153, 0))
     x = synth.make_inputs(p)
-    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, "none")
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, "none",
+                  algo=FORCE["algo"])
     assert "as real 2x2 blocks" in pl.describe(), pl.describe()
     ref = oracle.gemm_pair(p.M, p.N, p.K, "T", "N", x["A"], p.lda, x["B"], p.ldb, "cf16")
     A, B = _dev(x["A"]), _dev(x["B"])

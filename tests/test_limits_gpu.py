@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import check, reference, reference_batched, run, run_batched
+from gpu_helpers import FORCE, check, reference, reference_batched, run, run_batched
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ CASES = [("fast", "NN", 8), ("fast", "TN", 1), ("staged", "TN", 1), ("general", 
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_operand_spans_just_below_2_gib(case, monkeypatch):
     kern, lay, mult = CASES[case]
-    monkeypatch.setenv("TGE_FORCE_KERNEL", kern)
+    monkeypatch.setitem(FORCE, "algo", kern)
     M, N, K = 300, 264, 200
     p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], "f16", "f32", "bias_relu", 1.0, 1.0,
                                     key=(140, case))
@@ -66,7 +66,7 @@ def test_operand_spans_just_below_2_gib(case, monkeypatch):
 
 def test_batch_offsets_beyond_4_gib(monkeypatch):
     # product 1 of A starts 4 GiB + 16 bytes after product 0; B is shared
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     M, N, K = 264, 256, 192
     p = synth.exact_integer_problem(M, N, K, "N", "N", "f16", "f16", "bias", 1.0, 1.0,
                                     key=(141, 0), batch=2, stride_a=(1 << 31) + 8, stride_b=0,

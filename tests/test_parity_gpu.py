@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import (check, check_points, normaliser, reference, reference_batched, run,
+from gpu_helpers import (FORCE, check, check_points, normaliser, reference, reference_batched, run,
                          run_batched)
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,7 @@ SCALARS = [(1.0, 0.0), (2.0, -1.0), (-0.5, 0.5), (1.0, 1.0)]
 @pytest.mark.parametrize("lay", LAYOUTS)
 @pytest.mark.parametrize("ab,cd", PAIRS)
 def test_exact_integer_all_tiles(ab, cd, lay, tile, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_TILE", str(tile))
+    monkeypatch.setitem(FORCE, "tile", tile)
     i = PAIRS.index((ab, cd)) * 4 + LAYOUTS.index(lay)
     M, N, K = 2 * tile + 7, tile + 33, 2 * BK[ab] + 5
     epi = EPIS[i % 4]
@@ -179,35 +179,68 @@ FULL = [(name, i) for name, fn in synth.WORKLOADS.items() for i, q in enumerate(
         if q.ab not in synth.PART]
 
 
+def _host_threads():
+    """The host cores this process may use (the CPU share of the box), for the oracle."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap)) if cap and cap.isdigit() else n)
+
+
 @pytest.mark.parametrize("name,idx", FULL)
-def test_workload_full_size_sampled(name, idx):
+def test_workload_full_output(name, idx):
+    """Every output element of every workload at its full size against the oracle (int8 bit for
+    bit, floats within the normalised tolerance), in the launch configuration the bench times."""
     p = synth.WORKLOADS[name]()[idx]
     x = synth.make_inputs(p)
+    threads = _host_threads()
     if p.batch != 1:
-        # every product of the batch, in full
         Df, pl = run_batched(p, x)
         print(f"{p.label()} -> {pl.describe()}", flush=True)
         ref = reference_batched(p, x)
+        errs = []
         for b in range(p.batch):
             Db = Df[b * p.stride_c: b * p.stride_c + p.M * p.ldc].reshape(p.M, p.ldc)
-            check(p, x, Db, ref[b])
+            errs.append(check(p, x, Db, ref[b]))
+        print(f"[full] {p.label()}: products {p.batch} x rows {p.M} checked, max normalised "
+              f"error {max(errs):.3e}", flush=True)
         return
     D, pl = run(p, x)
     print(f"{p.label()} -> {pl.describe()}", flush=True)
-    plain = (p.kind_a, p.kind_b) == ("dense", "dense") and \
-        (p.transform_a, p.transform_b, p.transform_c) == ("none", "none", "none")
-    if p.M * p.N * p.K <= 256 ** 3:
-        check(p, x, D, reference(p, x))
-    else:
-        if plain:   # per-point references read the raw dense operands
-            check_points(p, x, D)
-        # a whole row band through the oracle as well (first and last rows)
-        for r0 in (0, p.M - 2):
-            ref = reference(p, x, rows=(r0, r0 + 2))
-            check(p, x, D, ref, rows=slice(r0, r0 + 2))
+    ref = reference(p, x, threads=threads)
+    err = check(p, x, D, ref)
+    print(f"[full] {p.label()}: rows {p.M} of {p.M} checked, "
+          f"{'bit-exact' if p.cd == 'i32' else f'max normalised error {err:.3e}'}", flush=True)
     Dv = D[:, : p.N]
     if p.relu:
         assert (synth_decode(p.cd, Dv) >= 0).all()
+
+
+# Exact-integer inputs at full size: every fp32 partial sum is exact, so D must equal RNE(ref)
+# on every element.  Unlike the normalised tolerance, this sees a dropped or repeated K slab, a
+# misplaced tile or a stale round anywhere in the multi-round grids, the partial last round and
+# the streaming-store epilogue that only the full-size launches exercise.
+EXACT_FULL = [((8192, 8192, 8192), "NN", "f16", "f16", "bias_relu", 1.0, 0.0),
+              ((5000, 5000, 5000), "TN", "bf16", "f32", "none", 2.0, -1.0),
+              ((5000, 5000, 5000), "NT", "bf16", "f32", "bias", 0.5, 1.0),
+              ((4095, 3073, 2047), "TT", "bf16", "bf16", "relu", 1.0, -0.5),
+              ((8192, 4096, 16384), "NN", "f16", "f16", "bias_relu", 1.0, 0.0),
+              ((8192, 16384, 4096), "NT", "f16", "f16", "bias_relu", 1.0, 0.0)]
+
+
+@pytest.mark.parametrize("case", range(len(EXACT_FULL)))
+def test_exact_integer_full_size(case):
+    (M, N, K), lay, ab, cd, epi, alpha, beta = EXACT_FULL[case]
+    p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta,
+                                    key=(120, case))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    print(f"{p.label()} -> {pl.describe()}", flush=True)
+    assert "gemm_fast_256x256" in pl.describe(), pl.describe()
+    check(p, x, D, reference(p, x, threads=_host_threads()), exact=True)
+    print(f"[full] {p.label()}: rows {M} of {M} bit-exact", flush=True)
 
 
 def synth_decode(cd, raw):
@@ -227,7 +260,7 @@ FAST_SHAPES = [(256, 256, 64), (304, 520, 200), (512, 264, 128), (264, 8, 72), (
 @pytest.mark.parametrize("lay", LAYOUTS)
 @pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 def test_fast_path_exact(ab, cd, lay, shape, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     M, N, K = shape
     i = LAYOUTS.index(lay) + 4 * FAST_SHAPES.index(shape)
     epi = EPIS[i % 4]
@@ -241,7 +274,7 @@ def test_fast_path_exact(ab, cd, lay, shape, monkeypatch):
 
 @pytest.mark.parametrize("lay", LAYOUTS)
 def test_fast_path_random_and_unaligned_fallback(lay, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     p = synth.Problem(776, 1024, 576, lay[0], lay[1], "f16", "f16", "bias_relu", 1.0, 0.0,
                       key=(110, LAYOUTS.index(lay)))
     x = synth.make_inputs(p)
@@ -270,7 +303,7 @@ SKINNY_SHAPES = [(1, 16, 32), (5, 40, 64), (16, 520, 320), (17, 64, 96), (33, 20
 @pytest.mark.parametrize("lb", ["N", "T"])
 @pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 def test_skinny_path_exact(ab, cd, lb, shape, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    monkeypatch.setitem(FORCE, "algo", "skinny")
     M, N, K = shape
     i = SKINNY_SHAPES.index(shape) * 2 + (lb == "T")
     p = _exact(M, N, K, "N" + lb, ab, cd, EPIS[i % 4], *SCALARS[i % 4], key=(111, i))
@@ -283,7 +316,7 @@ def test_skinny_path_exact(ab, cd, lb, shape, monkeypatch):
 def test_skinny_split_k_repeatable_and_graph_safe(monkeypatch):
     # the split-K counters reset themselves: repeated runs, a second plan of the same shape,
     # and graph replays after a first eager run give the same bits
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    monkeypatch.setitem(FORCE, "algo", "skinny")
     p = _exact(16, 1000, 2048, "NN", "f16", "f32", "bias_relu", 2.0, -1.0, key=(118, 0))
     x = synth.make_inputs(p)
     D0, pl = run(p, x)
@@ -313,7 +346,7 @@ def test_skinny_split_k_repeatable_and_graph_safe(monkeypatch):
 
 
 def test_skinny_split_k_batched(monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    monkeypatch.setitem(FORCE, "algo", "skinny")
     p = synth.exact_integer_problem(16, 520, 2048, "N", "T", "bf16", "bf16", "bias", 1.0, 1.0,
                                     key=(119, 0), batch=3, stride_bias=520)
     x = synth.make_inputs(p)
@@ -328,7 +361,7 @@ def test_skinny_split_k_batched(monkeypatch):
 
 def test_skinny_narrow_blocks_batched(monkeypatch):
     # three products of 64 sixteen-column blocks each: one round of 192 narrow workgroups
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    monkeypatch.setitem(FORCE, "algo", "skinny")
     p = synth.exact_integer_problem(13, 1024, 1024, "N", "T", "f16", "f32", "bias_relu", 2.0, -1.0,
                                     key=(126, 0), batch=3, stride_bias=1024)
     x = synth.make_inputs(p)
@@ -342,7 +375,7 @@ def test_skinny_narrow_blocks_batched(monkeypatch):
 
 
 def test_skinny_ineligible_shapes_fall_back(monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    monkeypatch.setitem(FORCE, "algo", "skinny")
     # K not a multiple of 32, and A transposed: the general kernel runs, same results
     for j, (lay, K) in enumerate([("NN", 100), ("TN", 64)]):
         p = _exact(16, 128, K, lay, "f16", "f16", "bias_relu", 1.0, 0.0, key=(112, j))
@@ -360,7 +393,7 @@ FAST_SHAPES_I8 = [(256, 256, 128), (304, 528, 208), (512, 272, 256), (272, 16, 1
 @pytest.mark.parametrize("shape", FAST_SHAPES_I8)
 @pytest.mark.parametrize("lay", LAYOUTS)
 def test_fast_path_int8_exact(lay, shape, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     M, N, K = shape
     i = LAYOUTS.index(lay) + 4 * FAST_SHAPES_I8.index(shape)
     epi = ["none", "relu", "bias", "bias_relu"][i % 4]
@@ -393,7 +426,7 @@ def _direct_ok(p, pad):
 @pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"),
                                    ("bf16", "f32"), ("i8", "i32")])
 def test_fast_unaligned_layouts_exact(ab, cd, lay, shape, mode, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
+    monkeypatch.setitem(FORCE, "algo", mode)
     M, N, K, pad = shape
     if ab == "i8":
         K *= 2                              # one int8 slab is 128 deep
@@ -423,7 +456,7 @@ def test_fast_unaligned_layouts_exact(ab, cd, lay, shape, mode, monkeypatch):
 @pytest.mark.parametrize("lay", LAYOUTS)
 def test_fast_unaligned_layouts_random(lay, mode, monkeypatch):
     # random data, bf16 -> f32 with bias + ReLU, odd leading dimensions over several tiles
-    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
+    monkeypatch.setitem(FORCE, "algo", mode)
     p = synth.Problem(777, 1031, 611, lay[0], lay[1], "bf16", "f32", "bias_relu", 1.0, 0.5,
                       key=(115, LAYOUTS.index(lay)))
     p.lda += 1; p.ldb += 3; p.ldc += 1
@@ -437,7 +470,7 @@ def test_fast_unaligned_layouts_random(lay, mode, monkeypatch):
 
 @pytest.mark.parametrize("mode", ["fast", "staged"])
 def test_fast_unaligned_layouts_with_transforms(mode, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
+    monkeypatch.setitem(FORCE, "algo", mode)
     p = synth.exact_integer_problem(300, 261, 200, "T", "N", "f16", "f32", "bias", 1.0, 1.0,
                                     key=(116, 0), ld_pad=1, transform_a="relu",
                                     transform_b="relu", transform_c="relu")
@@ -453,7 +486,7 @@ def test_fast_extent_below_one_chunk(mode, monkeypatch):
     # N = 5 with B not transposed: no in-bounds 16-byte chunk exists in place.  Copied, B's rows
     # are padded to one whole chunk and the direct-load kernel runs; the register-staged variant
     # cannot take it and the general kernel runs
-    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
+    monkeypatch.setitem(FORCE, "algo", mode)
     p = _exact(300, 5, 128, "NN", "f16", "f16", "bias", 1.0, 0.0, key=(117, 0))
     x = synth.make_inputs(p)
     D, pl = run(p, x)
@@ -468,7 +501,7 @@ def test_repack_graph_capture(monkeypatch):
     # a first run inside a capture cannot allocate the copy workspace: it runs the
     # register-staged kernel; after an eager run (which allocates it) captured runs copy the
     # operands; every replay, with eager work between, gives the eager result bit for bit
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     p = _exact(520, 515, 333, "TN", "f16", "f32", "bias_relu", 2.0, -1.0, key=(122, 0), ld_pad=1)
     x = synth.make_inputs(p)
     ref = reference(p, x)
@@ -476,7 +509,8 @@ def test_repack_graph_capture(monkeypatch):
     A, B = to_dev(p.ab, x["A"]), to_dev(p.ab, x["B"])
     C, bias = to_dev(p.cd, x["C"]), to_dev(p.bias_dt, x["bias"])
     import tiled_gemm_epilogues_amd as tge
-    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
+                  algo=FORCE["algo"], tile=FORCE["tile"])
     assert "repack AB" in pl.describe(), pl.describe()
     D = torch.zeros(p.M * p.ldc, dtype=torch.float32, device="cuda")
     s = torch.cuda.Stream()
@@ -508,7 +542,7 @@ def test_repack_graph_capture(monkeypatch):
 def test_fast_streaming_stores_unaligned_d(monkeypatch):
     # more than one round of 256x256 tiles (17 x 17 = 289 workgroups): interior tiles write D with
     # non-temporal stores; an odd ldc makes those stores unaligned.  C read in place as well.
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     for j, (cd, pad) in enumerate([("f16", 1), ("f32", 3), ("f16", 0)]):
         p = _exact(4200, 4200, 128, "NN", "f16", cd, "bias_relu", 2.0, -1.0, key=(122, j))
         p.ldc += pad
@@ -533,7 +567,7 @@ def test_fast_random_shapes_exact(case, monkeypatch):
     ab, cd = pairs[case % len(pairs)]
     lay = LAYOUTS[int(rng.integers(4))]
     mode = "fast" if case % 3 else "staged"
-    monkeypatch.setenv("TGE_FORCE_KERNEL", mode)
+    monkeypatch.setitem(FORCE, "algo", mode)
     kmin = 128 if ab == "i8" else 64
     M, N = (int(v) for v in rng.integers(16, 700, size=2))
     K = int(rng.integers(kmin, 700))
@@ -552,7 +586,7 @@ def test_fast_random_shapes_exact(case, monkeypatch):
 
 # ---- the fast kernel's K split (chunks of K as a batch into fp32 partial sums, then the
 # finishing kernel) -------------------------------------------------------------------------------
-# TGE_FORCE_KERNEL=split makes small shapes split (any S >= 2); the plan's own rule splits only
+# the algorithm "split" makes small shapes split (any S >= 2); the plan's own rule splits only
 # large-K products with few tiles.  Exact-integer inputs: partial sums and their total are exact.
 SPLIT_SHAPES = [(300, 264, 1024), (520, 300, 640), (256, 256, 128), (17, 600, 2048),
                 (600, 9, 512), (777, 513, 1280)]
@@ -562,7 +596,7 @@ SPLIT_SHAPES = [(300, 264, 1024), (520, 300, 640), (256, 256, 128), (17, 600, 20
 @pytest.mark.parametrize("lay", LAYOUTS)
 @pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 def test_fast_k_split_exact(ab, cd, lay, shape, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "split")
+    monkeypatch.setitem(FORCE, "algo", "split")
     M, N, K = shape
     i = LAYOUTS.index(lay) + 4 * SPLIT_SHAPES.index(shape)
     p = _exact(M, N, K, lay, ab, cd, EPIS[i % 4], *SCALARS[(i // 4) % 4], key=(127, i))
@@ -586,7 +620,7 @@ def test_fast_k_split_exact(ab, cd, lay, shape, monkeypatch):
 def test_fast_k_split_int8_exact(lay, shape, monkeypatch):
     # int8 -> int32: int32 partial sums, the integer finishing kernel (bias, beta in {0, 1},
     # ReLU); K doubled so that every chunk is a whole int8 slab of 128
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "split")
+    monkeypatch.setitem(FORCE, "algo", "split")
     M, N, K = shape
     K *= 2
     i = LAYOUTS.index(lay) + 4 * SPLIT_SHAPES.index(shape)
@@ -613,8 +647,8 @@ def test_fast_k_split_short_int8_exact(lay, shape):
     x = synth.make_inputs(p)
     print(p.label(), flush=True)
     D, pl = run(p, x)
-    assert "gemm_fast_256x256 " in pl.describe() or "repack" in pl.describe() or \
-        "gemm_mfma" in pl.describe(), pl.describe()
+    assert "gemm_fast_256x256 " in pl.describe() and " ksplit " in pl.describe() + " ", \
+        pl.describe()
     check(p, x, D, reference(p, x), exact=True)
 
 
@@ -637,7 +671,7 @@ def test_fast_k_split_short_transposed_a_exact(ab, cd, lb, shape):
 def test_fast_k_split_graph_capture(monkeypatch):
     # no workspace yet inside the first capture: that run is not split; after an eager run the
     # captured runs split; every replay gives the eager result bit for bit
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "split")
+    monkeypatch.setitem(FORCE, "algo", "split")
     p = _exact(520, 300, 640, "NT", "bf16", "f32", "bias_relu", 2.0, -1.0, key=(128, 0))
     x = synth.make_inputs(p)
     ref = reference(p, x)
@@ -645,7 +679,8 @@ def test_fast_k_split_graph_capture(monkeypatch):
     A, B = to_dev(p.ab, x["A"]), to_dev(p.ab, x["B"])
     C, bias = to_dev(p.cd, x["C"]), to_dev(p.bias_dt, x["bias"])
     import tiled_gemm_epilogues_amd as tge
-    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
+                  algo=FORCE["algo"], tile=FORCE["tile"])
     assert " ksplit " in pl.describe(), pl.describe()
     D = torch.zeros(p.M * p.ldc, dtype=torch.float32, device="cuda")
     s = torch.cuda.Stream()

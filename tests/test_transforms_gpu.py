@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import check, reference, reference_batched, run, run_batched
+from gpu_helpers import FORCE, check, reference, reference_batched, run, run_batched
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,7 @@ CASES = [
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_transforms_exact(case, lay, xf, monkeypatch):
     kern, M, N, K, ab, cd, epi, alpha, beta = CASES[case]
-    monkeypatch.setenv("TGE_FORCE_KERNEL", kern)
+    monkeypatch.setitem(FORCE, "algo", kern)
     i = case * 16 + LAYOUTS.index(lay) * 4 + xf
     p = _problem(M, N, K, lay, ab, cd, epi, alpha, beta, (130, i), XFORMS[xf])
     x = synth.make_inputs(p)
@@ -76,7 +76,7 @@ def test_transforms_exact(case, lay, xf, monkeypatch):
 @pytest.mark.parametrize("xf", range(len(XFORMS)))
 @pytest.mark.parametrize("lb", ["N", "T"])
 def test_transforms_skinny_exact(lb, xf, monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    monkeypatch.setitem(FORCE, "algo", "skinny")
     p = _problem(33, 200, 1024, "N" + lb, "f16", "f32", "bias_relu", 1.0, -0.5,
                  (131, xf * 2 + (lb == "T")), XFORMS[xf])
     x = synth.make_inputs(p)
@@ -89,7 +89,7 @@ def test_transforms_skinny_exact(lb, xf, monkeypatch):
 def test_transforms_skinny_split_k_exact(lb, monkeypatch):
     # K long enough that the skinny plan splits it over workgroups: the operand transforms run
     # in the splitting kernel, the C transform in the finishing one
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "skinny")
+    monkeypatch.setitem(FORCE, "algo", "skinny")
     p = _problem(33, 200, 4096, "N" + lb, "f16", "f32", "bias_relu", 1.0, -0.5,
                  (133, lb == "T"), ("relu", "relu", "relu"))
     x = synth.make_inputs(p)
@@ -99,7 +99,7 @@ def test_transforms_skinny_split_k_exact(lb, monkeypatch):
 
 
 def test_transforms_random_within_tolerance(monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     p = synth.Problem(1000, 776, 1000, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.5,
                       key=(132, 0), transform_a="relu", transform_b="none", transform_c="relu")
     x = synth.make_inputs(p)
@@ -109,7 +109,7 @@ def test_transforms_random_within_tolerance(monkeypatch):
 
 
 def test_transforms_with_a_batch(monkeypatch):
-    monkeypatch.setenv("TGE_FORCE_KERNEL", "fast")
+    monkeypatch.setitem(FORCE, "algo", "fast")
     p = _problem(264, 264, 192, "NN", "f16", "f16", "bias", 1.0, 1.0, (133, 0),
                  ("relu", "relu", "relu"), batch=3, stride_b=0)
     x = synth.make_inputs(p)

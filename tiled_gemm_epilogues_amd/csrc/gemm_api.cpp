@@ -165,28 +165,6 @@ int choose_cfg(int64_t M, int64_t N, int64_t batch) {
 
 }  // namespace
 
-// The split-K workspace of a skinny plan on the current device, allocated by the first run there
-// (not while the stream is being captured into a graph).  Every run overwrites what it reads.
-static gemm_status_t skinny_workspace(gemm_plan *p, hipStream_t stream) {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
-    if (p->ws && p->ws_dev == dev) return GEMM_STATUS_SUCCESS;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
-    if (cs != hipStreamCaptureStatusNone) return GEMM_STATUS_NOT_SUPPORTED;
-    if (p->ws) (void)hipFree(p->ws);
-    p->ws = nullptr;
-    p->ws_dev = -1;
-    const int64_t nb = p->batch > 1 ? p->batch : 1;
-    const size_t wsb = (size_t)nb * p->ksplit * p->M * p->N * sizeof(float);
-    if (hipMalloc(&p->ws, wsb) != hipSuccess) {
-        p->ws = nullptr;
-        return GEMM_STATUS_ALLOC_FAILED;
-    }
-    p->ws_dev = dev;
-    return GEMM_STATUS_SUCCESS;
-}
-
 // A plan-owned workspace on the current device, allocated by the first run there that needs it
 // (not while the stream is being captured into a graph).
 static gemm_status_t lazy_workspace(void **ws, int *ws_dev, size_t bytes, hipStream_t stream) {
@@ -206,6 +184,14 @@ static gemm_status_t lazy_workspace(void **ws, int *ws_dev, size_t bytes, hipStr
     }
     *ws_dev = dev;
     return GEMM_STATUS_SUCCESS;
+}
+
+// The split-K workspace of a skinny plan or of the fast kernel's K split (partial sums of every
+// k split); every run overwrites what it reads.
+static gemm_status_t skinny_workspace(gemm_plan *p, hipStream_t stream) {
+    const int64_t nb = p->batch > 1 ? p->batch : 1;
+    const size_t wsb = (size_t)nb * p->ksplit * p->M * p->N * sizeof(float);
+    return lazy_workspace(reinterpret_cast<void **>(&p->ws), &p->ws_dev, wsb, stream);
 }
 
 // The copy workspace of a repacking plan.
@@ -247,6 +233,8 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
     d.stride_a = stride_a; d.stride_b = stride_b; d.stride_c = stride_c; d.stride_bias = stride_bias;
     d.transform_a = d.transform_b = d.transform_c = GEMM_TRANSFORM_NONE;
     d.kind_a = d.kind_b = GEMM_OPERAND_DENSE;
+    d.algo = GEMM_ALGO_AUTO;
+    d.tile = 0;
     return gemm_plan_create_desc(out, &d);
 }
 
@@ -266,6 +254,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if ((int)t != GEMM_TRANSFORM_NONE && (int)t != GEMM_TRANSFORM_RELU) return GEMM_STATUS_INVALID_VALUE;
     for (gemm_operand_t k : {desc->kind_a, desc->kind_b})
         if ((int)k != GEMM_OPERAND_DENSE && (int)k != GEMM_OPERAND_DIAGONAL) return GEMM_STATUS_INVALID_VALUE;
+    if ((int)desc->algo < GEMM_ALGO_AUTO || (int)desc->algo > GEMM_ALGO_NOSPLIT) return GEMM_STATUS_INVALID_VALUE;
+    if (desc->tile != 0 && desc->tile != 256 && desc->tile != 128 && desc->tile != 64)
+        return GEMM_STATUS_INVALID_VALUE;
     const bool diag_a = desc->kind_a == GEMM_OPERAND_DIAGONAL;
     const bool diag_b = desc->kind_b == GEMM_OPERAND_DIAGONAL;
     if ((diag_a && K != M) || (diag_b && K != N)) return GEMM_STATUS_INVALID_VALUE;
@@ -310,13 +301,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         return GEMM_STATUS_NOT_SUPPORTED;
 
     int cfg = (diag_a || diag_b || ctable) ? tge::CFG_128 : choose_cfg(M, N, batch);
-    // TGE_FORCE_TILE=256|128|64 pins the workgroup tile (tests and tuning sweeps)
-    if (const char *f = getenv("TGE_FORCE_TILE")) {
-        int v = atoi(f);
-        if (v == 256) cfg = tge::CFG_256;
-        else if (v == 128) cfg = tge::CFG_128;
-        else if (v == 64) cfg = tge::CFG_64;
-    }
+    // an explicit tile in the description pins the workgroup tile
+    const int tile = desc->tile;
+    if (tile == 256) cfg = tge::CFG_256;
+    else if (tile == 128) cfg = tge::CFG_128;
+    else if (tile == 64) cfg = tge::CFG_64;
     const KernelEntry *k = ctable ? ctable(op_a, op_b) : table(op_a, op_b, cfg);
     if (diag_a || diag_b) k = diag_table(ab_type, cd_type)(op_a, op_b, (diag_a ? 1 : 0) | (diag_b ? 2 : 0));
     if (!k) return GEMM_STATUS_NOT_SUPPORTED;
@@ -324,19 +313,17 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // fast path: 16-bit inputs, 256x256 tiles worth it, shape/ld preconditions of gemm_fast
     const KernelEntry *fast = nullptr;
     FastLookup ft = fast_table(ab_type, cd_type);
-    // TGE_FORCE_KERNEL (tests, sweeps): "fast", "staged" (the fast kernel, register-staged for
-    // operands the direct loads cannot read in place instead of copying them), "general",
-    // "skinny", "split" / "nosplit" (the fast kernel's K split forced / never)
-    const char *fk = getenv("TGE_FORCE_KERNEL");
-    const bool staged = fk && strcmp(fk, "staged") == 0;
+    // an explicit algorithm in the description (gemm_algo_t) overrides the choices below
+    const int algo = desc->algo;
+    const bool staged = algo == GEMM_ALGO_FAST_STAGED;
     // the fast kernel does ~3x the work per CU-round of the general 128x128 kernel: take it
     // when its rounds of 256x256 tiles cost less than 3x as many rounds of 128x128 tiles
     const int64_t nb = batch > 1 ? batch : 1;
     const int64_t r256 = (((M + 255) / 256) * ((N + 255) / 256) * nb + 255) / 256;
     const int64_t r128 = (((M + 127) / 128) * ((N + 127) / 128) * nb + 255) / 256;
     bool want_fast = cfg == tge::CFG_256 || (cfg == tge::CFG_128 && 4 * r256 <= 3 * r128);
-    if (getenv("TGE_FORCE_TILE")) want_fast = cfg == tge::CFG_256;
-    if ((fk && strcmp(fk, "fast") == 0) || staged) want_fast = true;
+    if (tile) want_fast = cfg == tge::CFG_256;
+    if (algo == GEMM_ALGO_FAST || staged) want_fast = true;
     // K split of the fast kernel: few 256x256 tiles and a long K (64 slabs or more: K >= 4096
     // for 16-bit inputs, 8192 for int8).  K is cut into S equal chunks of whole slabs (at least
     // 16 each) so that tiles x S workgroups fill the chip (at least 128); the chunks' partial
@@ -347,16 +334,15 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // (M <= 64 with int8 inputs, or with A transposed) split down to chunks of 2 slabs: their
     // partial sums are small, and the split measured 1.1-6x faster than the general kernel
     // (int8 16 x 4096 x 4096: 97 -> 17 us; fp16 TN: 135 -> 28 us)
-    // (TGE_FORCE_KERNEL=split: any S >= 2, chunks of one slab or more; =nosplit: never).
+    // (GEMM_ALGO_SPLIT: any S >= 2, chunks of one slab or more; GEMM_ALGO_NOSPLIT: never).
     int split_s = 0;
-    const bool force_split = fk && strcmp(fk, "split") == 0;
+    const bool force_split = algo == GEMM_ALGO_SPLIT;
     const int64_t slab_k = 128 / elem_bytes(ab_type);   // K elements per slab of the fast kernel
     const int part_cd = ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32;
     if ((ab_type == GEMM_F16 || ab_type == GEMM_BF16 || ab_type == GEMM_I8) && batch <= 1 &&
         !ctable && !diag_a && !diag_b && !desc->transform_a && !desc->transform_b &&
         K % slab_k == 0 && !staged &&
-        !(fk && (strcmp(fk, "nosplit") == 0 || strcmp(fk, "general") == 0 ||
-                 strcmp(fk, "skinny") == 0))) {
+        algo != GEMM_ALGO_NOSPLIT && algo != GEMM_ALGO_GENERAL && algo != GEMM_ALGO_SKINNY) {
         const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t slabs = K / slab_k;
         int64_t sp = tiles > 0 ? 256 / tiles : 0;
@@ -369,7 +355,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
             split_s = (int)sp;
     }
     if (split_s) want_fast = true;
-    if (fk && strcmp(fk, "general") == 0) want_fast = false;
+    if (algo == GEMM_ALGO_GENERAL) want_fast = false;
     const int ve = 16 / eab;   // elements per 16-byte chunk
     // every product of a batch keeps the 16-byte alignment of product 0
     const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0 && !diag_a && !diag_b;
@@ -385,7 +371,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
 
     // repacking: operands the direct loads cannot read in place are copied into aligned rows
     // padded to whole 16-byte chunks, then the direct-load kernel runs on the copies
-    // (TGE_FORCE_KERNEL=staged keeps the register-staged variant for such operands)
+    // (GEMM_ALGO_FAST_STAGED keeps the register-staged variant for such operands)
     const KernelEntry *fast_pk = nullptr;
     int pk_need = 0;
     int64_t pk_ld_a = 0, pk_ld_b = 0, pk_off_b = 0, pk_bytes = 0, pk_kpad = 0;
@@ -425,9 +411,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     bool skinny = false;
     SkinnyLookup st = skinny_table(ab_type, cd_type);
     bool want_skinny = M <= 64;
-    if (fk && strcmp(fk, "general") == 0) want_skinny = false;
-    if ((fk && strcmp(fk, "fast") == 0) || staged || force_split) want_skinny = false;
-    if (fk && strcmp(fk, "skinny") == 0) want_skinny = true;
+    if (algo == GEMM_ALGO_GENERAL) want_skinny = false;
+    if (algo == GEMM_ALGO_FAST || staged || force_split) want_skinny = false;
+    if (algo == GEMM_ALGO_SKINNY) want_skinny = true;
     if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % 32 == 0 &&
         (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && strides16 && (op_b == GEMM_OP_T || N % 8 == 0)) {
         // B transposed, M <= 16: 16-column blocks when they make one round of 192 to 256
@@ -448,7 +434,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // 2 x 2 block (PairJob).  Elsewhere the complex kernel runs.
     gemm_plan *cx = nullptr;
     int64_t cx_ld_a = 0, cx_ld_b = 0, cx_off_b = 0, cx_bytes = 0;
-    if (ctable && M > 0 && N > 0 && K > 0 && !(fk && strcmp(fk, "general") == 0)) {
+    if (ctable && M > 0 && N > 0 && K > 0 && algo != GEMM_ALGO_GENERAL) {
         gemm_desc_t r = *desc;
         r.N = 2 * N;
         r.K = 2 * K;
