@@ -139,6 +139,30 @@ def zero_negative(x):
     return np.where(np.signbit(x), x.dtype.type(0), x)
 
 
+# load transforms that convert the stored type to the input type: transform name -> stored type
+CONVERT_FROM = {"from_f32": "f32", "from_i8": "i8"}
+
+
+def convert_to(ab, x):
+    """The type-converting load transform on decoded stored values: each value becomes the
+    nearest `ab` value, ties to even ("Flexible Performant GEMM Kernels on GPUs", section 4: a
+    transform applied to every element after it is loaded may convert its type).  Reading where
+    the pages are silent: round to nearest even, as the output conversion; int8 values convert
+    exactly to fp16 and bf16."""
+    x = np.ascontiguousarray(x, np.float64)
+    return decode(ab, round_to(ab, x))
+
+
+def _operand(ab, transform, raw, span_start, span_len, integer):
+    """Decoded stored elements [span_start, span_start + span_len) of an operand, converted to
+    the input type `ab` when its transform is a type conversion."""
+    st = CONVERT_FROM.get(transform)
+    if st is None:
+        return decode(ab, raw[span_start: span_start + span_len])
+    vals = decode(st, _raw(st, raw)[span_start: span_start + span_len]).astype(np.float64)
+    return convert_to(ab, vals)
+
+
 def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
          bias_dt=None, alpha=1.0, beta=0.0, relu=False, order="tiled", rows=None, threads=None,
          transform_a="none", transform_b="none", transform_c="none", kind_a="dense",
@@ -147,7 +171,9 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
 
     ab: input dtype; cd: C/D dtype; bias_dt: bias dtype (default f32, i32 for i8 inputs).
     rows: optional (r0, r1) to compute only those output rows.  transform_*: "none" or "relu"
-    (zero_negative) on the loaded op(A), op(B) and C.  kind_*: "dense" or "diagonal" (the
+    (zero_negative) on the loaded op(A), op(B) and C; for A and B also "from_f32" / "from_i8"
+    (the operand is stored as fp32 / int8, its array and leading dimension in that type, and
+    every element is converted to `ab` as it is loaded: convert_to).  kind_*: "dense" or "diagonal" (the
     operand is the square diagonal matrix of the vector given, its op and ld ignored:
     "Flexible Performant GEMM Kernels on GPUs", section 5.2).  Returns float64, or int64 when
     the inputs are int8."""
@@ -155,25 +181,28 @@ def gemm(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bia
     r0, r1 = (0, M) if rows is None else rows
     mr = r1 - r0
     threads = threads or os.cpu_count() or 1
-    Ar, Br = _raw(ab, A), _raw(ab, B)
+    Ar = _raw(CONVERT_FROM.get(transform_a, ab), A)
+    Br = _raw(CONVERT_FROM.get(transform_b, ab), B)
     if kind_a == "diagonal":
         # rows r0..r1 of diag(a): element (i, k) = a[r0 + i] if k == r0 + i else 0
         assert K == M
         Aop = np.zeros((mr, K), np.int64 if integer else np.float64)
-        Aop[np.arange(mr), r0 + np.arange(mr)] = decode(ab, Ar[r0:r1])
+        Aop[np.arange(mr), r0 + np.arange(mr)] = _operand(ab, transform_a, Ar, r0, mr, integer)
         Aop = Aop.reshape(-1)
     else:
         # decode only the stored rows that op(A)[r0:r1] touches
         if op_a == "N":
-            Asub = Ar[r0 * lda: r0 * lda + _span("N", mr, K, lda)]
+            Asub = _operand(ab, transform_a, Ar, r0 * lda, _span("N", mr, K, lda), integer)
         else:
-            Asub = Ar[r0: r0 + _span("T", mr, K, lda)]
-        Aop = _dense_op(op_a, mr, K, decode(ab, Asub), lda, integer)
+            Asub = _operand(ab, transform_a, Ar, r0, _span("T", mr, K, lda), integer)
+        Aop = _dense_op(op_a, mr, K, Asub, lda, integer)
     if kind_b == "diagonal":
         assert K == N
-        Bop = np.diag(decode(ab, Br[:N])).astype(np.int64 if integer else np.float64).reshape(-1)
+        Bop = np.diag(_operand(ab, transform_b, Br, 0, N, integer)).astype(
+            np.int64 if integer else np.float64).reshape(-1)
     else:
-        Bop = _dense_op(op_b, K, N, decode(ab, Br[: _span(op_b, K, N, ldb)]), ldb, integer)
+        Bop = _dense_op(op_b, K, N, _operand(ab, transform_b, Br, 0, _span(op_b, K, N, ldb), integer),
+                        ldb, integer)
     if transform_a == "relu":
         Aop = np.ascontiguousarray(zero_negative(Aop))
     if transform_b == "relu":
@@ -250,7 +279,8 @@ def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=N
     the plain definition above."""
     integer = is_int(ab)
     out = np.empty((batch, M, N), np.int64 if integer else np.float64)
-    Ar, Br = _raw(ab, A), _raw(ab, B)
+    Ar = _raw(CONVERT_FROM.get(transform_a, ab), A)
+    Br = _raw(CONVERT_FROM.get(transform_b, ab), B)
     Cr = _raw(cd, C) if (C is not None and beta != 0) else None
     bias_dt = bias_dt or ("i32" if integer else "f32")
     br = _raw(bias_dt, bias) if bias is not None else None
@@ -284,11 +314,16 @@ def points(ii, jj, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=0, cd="f32", b
     return out
 
 
-def max_abs_op(dtype, X, op, rows, cols, ld):
-    """max |op(X)| over the decoded elements op(X) uses (the tolerance's normaliser)."""
+def max_abs_op(dtype, X, op, rows, cols, ld, transform="none"):
+    """max |op(X)| over the decoded elements op(X) uses (the tolerance's normaliser); with a
+    type-converting transform, over the converted values."""
     if rows == 0 or cols == 0:
         return 0.0
-    d = decode(dtype, _raw(dtype, X)[: _span(op, rows, cols, ld)])
+    st = CONVERT_FROM.get(transform)
+    if st is None:
+        d = decode(dtype, _raw(dtype, X)[: _span(op, rows, cols, ld)])
+    else:
+        d = convert_to(dtype, decode(st, _raw(st, X)[: _span(op, rows, cols, ld)]))
     if op == "N":
         idx_ok = (np.arange(d.size) % ld) < cols
     else:

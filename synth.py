@@ -21,6 +21,8 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "cf16": 4, "df16
               "df32": 8}
 # complex / dual types: numbers of two parts of this real type, stored interleaved
 PART = {"cf16": "f16", "df16": "f16", "cf32": "f32", "df32": "f32"}
+# stored element type of an operand whose load transform converts it to the input type
+STORED_BY_TRANSFORM = {"from_f32": "f32", "from_i8": "i8"}
 
 
 def rng(*key):
@@ -118,6 +120,16 @@ class Problem:
                 self.stride_bias = self.N if self.has_bias else 0
 
     @property
+    def a_store(self):
+        """Element type A is stored in: the input type, or the source type of a converting
+        load transform ("from_f32" / "from_i8")."""
+        return STORED_BY_TRANSFORM.get(self.transform_a, self.ab)
+
+    @property
+    def b_store(self):
+        return STORED_BY_TRANSFORM.get(self.transform_b, self.ab)
+
+    @property
     def bias_dt(self):
         return "i32" if self.ab == "i8" else "f32"
 
@@ -152,12 +164,12 @@ class Problem:
     def algorithmic_bytes(self):
         """Compulsory HBM traffic: op(A), op(B) read once, C if beta != 0, bias, D written once
         (per product; an operand shared by a batch is counted once)."""
-        eb, ec = ELEM_BYTES[self.ab], ELEM_BYTES[self.cd]
+        ea, eb, ec = ELEM_BYTES[self.a_store], ELEM_BYTES[self.b_store], ELEM_BYTES[self.cd]
         nb = max(self.batch, 0)
         per = lambda stride: nb if (nb <= 1 or stride != 0) else 1
         na = self.M if self.kind_a == "diagonal" else self.M * self.K
         nbb = self.N if self.kind_b == "diagonal" else self.K * self.N
-        b = (na * per(self.stride_a) + nbb * per(self.stride_b)) * eb
+        b = na * per(self.stride_a) * ea + nbb * per(self.stride_b) * eb
         b += self.M * self.N * ec * nb
         if self.beta != 0:
             b += self.M * self.N * ec * nb
@@ -196,14 +208,14 @@ def make_inputs(p: Problem, pad_fill=0):
         return _make_pair_inputs(p, pad_fill)
     ga, gb, gc, gbias = (rng(*p.key, i) for i in range(4))
     if p.kind_a == "diagonal":
-        A = quantize(p.ab, draw(ga, p.a_dist, p.M))
+        A = quantize(p.a_store, draw(ga, p.a_dist, p.M))
     else:
-        a = quantize(p.ab, draw(ga, p.a_dist, p.M * p.K)).reshape(p.M, p.K)
+        a = quantize(p.a_store, draw(ga, p.a_dist, p.M * p.K)).reshape(p.M, p.K)
         A = _store(a, p.op_a, p.lda, pad_fill)
     if p.kind_b == "diagonal":
-        B = quantize(p.ab, draw(gb, p.b_dist, p.N))
+        B = quantize(p.b_store, draw(gb, p.b_dist, p.N))
     else:
-        b = quantize(p.ab, draw(gb, p.b_dist, p.K * p.N)).reshape(p.K, p.N)
+        b = quantize(p.b_store, draw(gb, p.b_dist, p.K * p.N)).reshape(p.K, p.N)
         B = _store(b, p.op_b, p.ldb, pad_fill)
     C = None
     if p.beta != 0:
@@ -244,7 +256,7 @@ def _make_batched_inputs(p: Problem, pad_fill=0):
     fa, fc = (2 if p.ab in PART else 1), (2 if p.cd in PART else 1)
     strides = {"A": p.stride_a * fa, "B": p.stride_b * fa, "C": p.stride_c * fc,
                "bias": p.stride_bias}
-    dtypes = {"A": p.ab, "B": p.ab, "C": p.cd, "bias": p.bias_dt}
+    dtypes = {"A": p.a_store, "B": p.b_store, "C": p.cd, "bias": p.bias_dt}
     for b in range(max(p.batch, 0)):
         one = make_inputs(replace(p, batch=1, key=(*p.key, 1000 + b)), pad_fill)
         for name, arr in one.items():

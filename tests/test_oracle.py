@@ -487,3 +487,111 @@ def test_max_abs_op_matches_a_dense_view():
         view = x[:, :slen] if op == "N" else x[:, :slen].T
         want = float(np.abs(view.astype(np.float64)).max())
         assert oracle.max_abs_op("f16", x.view(np.uint16), op, rows, cols, ld) == want
+
+
+# ---- type-converting load transforms -------------------------------------------------------------
+
+def check_conversion_pins(mod):
+    """The conversion applied by the type-converting load transforms, and its use in gemm():
+    round to nearest even, checked against numpy's and torch's casts and hand-placed ties, and
+    op(A) I = the converted operand."""
+    _rne_pins(mod)
+    g = np.random.default_rng(45)
+    X32 = g.normal(0, 100, (7, 5)).astype(np.float32)
+    I16 = np.eye(5, dtype=np.float16).view(np.uint16)
+    got = mod.gemm(7, 5, 5, "N", "N", X32, 5, I16, 5, "f16", cd="f32", transform_a="from_f32")
+    assert np.array_equal(got, X32.astype(np.float16).astype(np.float64))
+    # B stored 7 x 5 and transposed: I op(B) = X32^T, converted
+    got = mod.gemm(5, 7, 5, "N", "T", I16, 5, X32, 5, "f16", cd="f32", transform_b="from_f32")
+    assert np.array_equal(got, X32.T.astype(np.float16).astype(np.float64))
+
+
+def test_conversion_pins():
+    check_conversion_pins(oracle)
+
+
+def _rne_pins(mod):
+    # fp32 -> fp16: numpy's float32 -> float16 cast rounds to nearest even; fp32 -> bf16: torch's
+    # float32 -> bfloat16 cast does; both on random values and on hand-placed ties
+    oracle = mod
+    g = np.random.default_rng(41)
+    x = np.concatenate([g.normal(0, 3, 4000), g.uniform(-70000, 70000, 1000)]).astype(np.float32)
+    ties = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -(1 + 2.0 ** -11), 2048 + 1, 2048 + 3,
+                     65504, 65519.99, 65520, 2.0 ** -25, 3 * 2.0 ** -25, 0.0, -0.0], np.float32)
+    x = np.concatenate([x, ties])
+    want16 = x.astype(np.float16).astype(np.float64)
+    got16 = oracle.convert_to("f16", x.astype(np.float64))
+    assert np.array_equal(got16, want16)
+    assert np.array_equal(np.signbit(got16), np.signbit(want16))
+    # the ties themselves, by hand: to the even neighbour
+    assert list(oracle.convert_to("f16", ties[:5].astype(np.float64))) == \
+        [1.0, 1 + 2.0 ** -9, -1.0, 2048.0, 2052.0]
+    assert oracle.convert_to("f16", np.array([65520.0]))[0] == np.inf
+    assert oracle.convert_to("f16", np.array([2.0 ** -25]))[0] == 0.0          # tie to +0
+    assert oracle.convert_to("f16", np.array([3 * 2.0 ** -25]))[0] == 2.0 ** -23
+    xb = x[np.abs(x) < 1e30]
+    wantb = torch.from_numpy(xb).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.convert_to("bf16", xb.astype(np.float64)), wantb)
+    assert list(oracle.convert_to("bf16", np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8]))) == \
+        [1.0, 1 + 2.0 ** -6]
+
+
+def test_int8_converts_exactly():
+    v = np.arange(-128, 128, dtype=np.float64)
+    for ab in ("f16", "bf16"):
+        assert np.array_equal(oracle.convert_to(ab, v), v)
+
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+@pytest.mark.parametrize("ab", ["f16", "bf16"])
+def test_converting_transforms_against_numpy(lay, ab):
+    """A stored as fp32 and B as int8 (and the reverse), converted to the input type as they
+    are loaded, against numpy on the converted logical matrices (integer-valued conversions of
+    small magnitude keep every product and sum exact in fp64)."""
+    g = np.random.default_rng(43)
+    cast = (lambda v: v.astype(np.float16).astype(np.float64)) if ab == "f16" else \
+        (lambda v: torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy())
+    for (M, N, K) in [(4, 5, 6), (1, 3, 7), (9, 2, 4)]:
+        X32 = (g.integers(-64, 64, (M, K)) / 8.0 + g.uniform(-1e-3, 1e-3, (M, K))).astype(np.float32)
+        Y8 = g.integers(-128, 128, (K, N)).astype(np.int8)
+        A = _store_logical(X32, lay[0], 2)
+        B = _store_logical(Y8, lay[1], 3)
+        lda, ldb = A.shape[1], B.shape[1]
+        got = oracle.gemm(M, N, K, lay[0], lay[1], A, lda, B, ldb, ab, cd="f32",
+                          transform_a="from_f32", transform_b="from_i8")
+        want = cast(X32) @ Y8.astype(np.float64)
+        assert np.array_equal(got, want)
+        # the other way round
+        A8 = _store_logical(Y8.T.copy(), lay[0], 1)
+        B32 = _store_logical(X32.T.copy(), lay[1], 0)
+        got = oracle.gemm(N, M, K, lay[0], lay[1], A8, A8.shape[1], B32, B32.shape[1], ab, cd="f32",
+                          transform_a="from_i8", transform_b="from_f32")
+        assert np.array_equal(got, Y8.T.astype(np.float64) @ cast(X32.T.copy()))
+
+
+def test_converting_transform_times_identity_is_the_conversion():
+    # op(A) I = op(A): the result is the converted operand itself, element for element
+    g = np.random.default_rng(44)
+    M, K = 37, 29
+    X32 = g.normal(0, 100, (M, K)).astype(np.float32)
+    I16 = np.eye(K, dtype=np.float16).view(np.uint16)
+    for ab in ("f16", "bf16"):
+        Ib = I16 if ab == "f16" else (np.eye(K, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        got = oracle.gemm(M, K, K, "N", "N", X32, K, Ib, K, ab, cd="f32", transform_a="from_f32")
+        assert np.array_equal(got, oracle.convert_to(ab, X32.astype(np.float64)))
+
+
+def test_max_abs_op_of_a_converted_operand():
+    x = np.array([[1.0, -65519.99, 7.0, 1e6]], np.float32)      # last column is padding
+    assert oracle.max_abs_op("f16", x, "N", 1, 3, 4, transform="from_f32") == 65504.0
+    x8 = np.array([[-128, 5, 127]], np.int8)
+    assert oracle.max_abs_op("bf16", x8, "T", 2, 1, 3, transform="from_i8") == 128.0
+
+
+def _store_logical(X, op, pad):
+    """Row-major storage of logical X (op N) or of its transpose (op T), `pad` extra columns of
+    junk that must never be read."""
+    S = X if op == "N" else X.T
+    out = np.full((S.shape[0], S.shape[1] + pad), 99, dtype=X.dtype)
+    out[:, : S.shape[1]] = S
+    return out

@@ -83,3 +83,34 @@ def test_normaliser_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
     spec.loader.exec_module(mod)
     with pytest.raises(AssertionError):
         check_max_abs_op_pins(mod)
+
+
+# planted mistakes in the type-converting load transform
+CONV_MUTANTS = {
+    "no_rounding": ("    x = np.ascontiguousarray(x, np.float64)\n    return decode(ab, round_to(ab, x))",
+                    "    x = np.ascontiguousarray(x, np.float64)\n    return x"),
+    "rounds_via_f32_truncation": ("    x = np.ascontiguousarray(x, np.float64)\n    return decode(ab, round_to(ab, x))",
+                                  "    x = np.ascontiguousarray(x, np.float64)\n    return decode(ab, round_to(ab, np.trunc(x * 1024) / 1024))"),
+    "conversion_skipped_in_gemm": ("    vals = decode(st, _raw(st, raw)[span_start: span_start + span_len]).astype(np.float64)\n    return convert_to(ab, vals)",
+                                   "    vals = decode(st, _raw(st, raw)[span_start: span_start + span_len]).astype(np.float64)\n    return vals"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conversion_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
+    import importlib.util
+
+    import oracle
+    from test_oracle import check_conversion_pins
+
+    old, new = CONV_MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert old in src, f"mutation anchor for {name} not found"
+    path = tmp_path / "oracle_mut.py"
+    path.write_text(src.replace(old, new))
+    monkeypatch.setenv("ORACLE_LIB", oracle._LIB_PATH)
+    spec = importlib.util.spec_from_file_location("oracle_mut", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with pytest.raises(AssertionError):
+        check_conversion_pins(mod)
