@@ -104,10 +104,15 @@ typedef enum {
     GEMM_STATUS_INVALID_VALUE = 1, /* a bad argument: negative size, ld too small, NULL pointer */
     GEMM_STATUS_NOT_SUPPORTED = 2, /* a valid request this library does not implement */
     GEMM_STATUS_HIP_ERROR = 3,     /* the HIP runtime reported an error at launch */
-    GEMM_STATUS_ALLOC_FAILED = 4   /* memory could not be allocated: host memory for a plan
+    GEMM_STATUS_ALLOC_FAILED = 4,  /* memory could not be allocated: host memory for a plan
                                       (plan creation), or device memory for a plan's split-K
                                       workspace (gemm_run) */
+    GEMM_STATUS_SCRATCH_LIMIT = 5  /* gemm_run_noalloc: the run needs more scratch than
+                                      GEMM_NOALLOC_SCRATCH_BYTES */
 } gemm_status_t;
+
+/* Bytes of device scratch each device holds for gemm_run_noalloc (64 MiB). */
+#define GEMM_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * Element-wise transforms applied to operand values as they are loaded, before they enter the
@@ -249,6 +254,26 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
  */
 gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream);
+
+/*
+ * gemm_run for callers that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.  Same arguments, results and
+ * errors as gemm_run, and the same kernels, but no call allocates or frees memory (no hipMalloc,
+ * no plan-owned workspace is created or used): the split-K partial sums, the aligned operand
+ * copies and the complex/dual operand rewrites that gemm_run keeps in plan-owned workspaces are
+ * placed in a scratch array of GEMM_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on (from the first call there until the process ends).  A run whose route
+ * needs more than that returns GEMM_STATUS_SCRATCH_LIMIT before anything is enqueued.  Nothing
+ * in the scratch needs to start at zero: every run writes the regions it reads.  All calls on a
+ * device share its one array, so calls whose device work overlaps in time (other streams, or
+ * host threads) race on it and give undefined results: serialise them on one stream.  The
+ * plan itself is only read.  The first call on a device that needs scratch looks up the array's
+ * address there (a HIP runtime query, which may load the library's device code on that device):
+ * make that first call outside a stream capture; later calls may be captured.  HIP_ERROR also
+ * covers a failure of that lookup.
+ */
+gemm_status_t gemm_run_noalloc(gemm_plan_t plan, const void *A, const void *B, const void *C,
+                               void *D, const void *bias, float alpha, float beta, void *stream);
 
 /* Frees a plan and its workspace, if any (waiting for the device work that may use it).  NULL is
  * a no-op.  Always returns SUCCESS. */

@@ -27,8 +27,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert tge.gemm_status_string(s).startswith("GEMM_STATUS_")
+    assert tge.gemm_status_string(tge.STATUS_SCRATCH_LIMIT) == "GEMM_STATUS_SCRATCH_LIMIT"
     assert tge.gemm_status_string(99) == "GEMM_STATUS_UNKNOWN"
 
 
@@ -340,3 +341,20 @@ def test_fast_k_split_described():
     d = tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
     assert "ksplit 4" in d and "repack A" in d, d
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", algo="nosplit").describe()
+
+
+def test_noalloc_rejects_runs_beyond_the_scratch_before_any_device_call():
+    # the sizing pass runs on the host only: with fake (never dereferenced) pointers a run whose
+    # aligned copy of A needs 8192 x 8200 x 2 bytes > 64 MiB is rejected before any HIP call
+    assert tge.NOALLOC_SCRATCH_BYTES == 64 << 20
+    st, h = tge.gemm_plan_create(8192, 8192, 8192, "N", "N", 8193, 8192, 8192, "f16", "f16", "none")
+    assert st == tge.STATUS_SUCCESS and "repack A" in tge.gemm_plan_describe(h)[1]
+    fake = 1 << 40
+    assert tge.gemm_run_noalloc(h, fake, fake, None, fake, None, 1.0, 0.0, None) == \
+        tge.STATUS_SCRATCH_LIMIT
+    # argument errors come first, as in gemm_run
+    assert tge.gemm_run_noalloc(h, fake, fake, None, None, None, 1.0, 0.0, None) == \
+        tge.STATUS_INVALID_VALUE
+    assert tge.gemm_run_noalloc(None, fake, fake, None, fake, None, 1.0, 0.0, None) == \
+        tge.STATUS_INVALID_VALUE
+    tge.gemm_plan_destroy(h)

@@ -4,7 +4,7 @@
 
 Argument marshalling only: every step of the computation runs in the HIP kernels behind the C
 ABI (include/gemm.h).  The low-level functions carry the C names (gemm_plan_create, gemm_run,
-gemm_plan_create_batched, gemm_plan_create_desc, gemm_plan_destroy,
+gemm_run_noalloc, gemm_plan_create_batched, gemm_plan_create_desc, gemm_plan_destroy,
 gemm_status_string, gemm_plan_describe); `Plan` wraps them for torch tensors, whose device
 memory and streams are the only things taken from PyTorch.
 
@@ -29,10 +29,12 @@ TRANSFORM = {"none": 0, "relu": 1}
 KIND = {"dense": 0, "diagonal": 1}
 ALGO = {"auto": 0, "fast": 1, "staged": 2, "general": 3, "skinny": 4, "split": 5, "nosplit": 6}
 (STATUS_SUCCESS, STATUS_INVALID_VALUE, STATUS_NOT_SUPPORTED, STATUS_HIP_ERROR,
- STATUS_ALLOC_FAILED) = range(5)
+ STATUS_ALLOC_FAILED, STATUS_SCRATCH_LIMIT) = range(6)
+# device scratch of gemm_run_noalloc (GEMM_NOALLOC_SCRATCH_BYTES in include/gemm.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("gemm_plan_create", "gemm_plan_create_batched", "gemm_plan_create_desc", "gemm_run",
-            "gemm_plan_destroy", "gemm_status_string", "gemm_plan_describe")
+            "gemm_run_noalloc", "gemm_plan_destroy", "gemm_status_string", "gemm_plan_describe")
 
 _i64, _vp, _ci, _f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 
@@ -73,6 +75,8 @@ def lib():
     L.gemm_plan_create_desc.restype = _ci
     L.gemm_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _vp]
     L.gemm_run.restype = _ci
+    L.gemm_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _vp]
+    L.gemm_run_noalloc.restype = _ci
     L.gemm_plan_destroy.argtypes = [_vp]
     L.gemm_plan_destroy.restype = _ci
     L.gemm_status_string.argtypes = [_ci]
@@ -131,6 +135,11 @@ def gemm_plan_create_desc(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, 
 def gemm_run(plan, A, B, C, D, bias, alpha, beta, stream):
     """Raw pointers (ints or None) and a hipStream_t handle (int or None)."""
     return lib().gemm_run(plan, A, B, C, D, bias, alpha, beta, stream)
+
+
+def gemm_run_noalloc(plan, A, B, C, D, bias, alpha, beta, stream):
+    """gemm_run that allocates nothing (the library's per-device scratch); raw pointers."""
+    return lib().gemm_run_noalloc(plan, A, B, C, D, bias, alpha, beta, stream)
 
 
 def gemm_plan_destroy(plan):
@@ -300,6 +309,14 @@ class Plan:
         st = gemm_run(self._h, *args, float(alpha), float(beta), self._stream(stream))
         if st != STATUS_SUCCESS:
             raise GemmError(st, "gemm_run")
+
+    def run_noalloc(self, A, B, C, D, bias=None, alpha=1.0, beta=0.0, stream=None):
+        """run() through gemm_run_noalloc: nothing is allocated; a run that needs more scratch
+        than the library holds raises GemmError (GEMM_STATUS_SCRATCH_LIMIT) before enqueueing."""
+        args = self._args(A, B, C, D, bias, beta)
+        st = gemm_run_noalloc(self._h, *args, float(alpha), float(beta), self._stream(stream))
+        if st != STATUS_SUCCESS:
+            raise GemmError(st, "gemm_run_noalloc")
 
     def close(self):
         if getattr(self, "_h", None):

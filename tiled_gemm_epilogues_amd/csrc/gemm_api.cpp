@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/gemm.h"
@@ -186,17 +187,231 @@ static gemm_status_t lazy_workspace(void **ws, int *ws_dev, size_t bytes, hipStr
     return GEMM_STATUS_SUCCESS;
 }
 
-// The split-K workspace of a skinny plan or of the fast kernel's K split (partial sums of every
-// k split); every run overwrites what it reads.
-static gemm_status_t skinny_workspace(gemm_plan *p, hipStream_t stream) {
-    const int64_t nb = p->batch > 1 ? p->batch : 1;
-    const size_t wsb = (size_t)nb * p->ksplit * p->M * p->N * sizeof(float);
-    return lazy_workspace(reinterpret_cast<void **>(&p->ws), &p->ws_dev, wsb, stream);
+// ---- scratch of gemm_run_noalloc -------------------------------------------------------------
+// One array per device, loaded with the library's code object and held until the process ends.
+// Host code never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];   // device address of `scratch` on each device (nullptr: not yet)
+}  // namespace
+
+// Device address of the scratch array on the current device (resolved on the first call there).
+static gemm_status_t scratch_address(uint8_t **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return GEMM_STATUS_HIP_ERROR;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return GEMM_STATUS_HIP_ERROR;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return GEMM_STATUS_SUCCESS;
 }
 
-// The copy workspace of a repacking plan.
-static gemm_status_t repack_workspace(gemm_plan *p, hipStream_t stream) {
-    return lazy_workspace(&p->pk_ws, &p->pk_dev, (size_t)p->pk_bytes, stream);
+// Scratch of gemm_run_noalloc: a bump allocator over the library's static device array (see
+// below).  dry: a sizing pass that takes regions and skips every launch and memory access.
+struct Scratch {
+    uint8_t *base;
+    size_t cap, used;
+    bool dry;
+};
+
+// `bytes` of workspace for one run: from the scratch when there is one (SCRATCH_LIMIT when it
+// is too small), else the plan-owned buffer *ws allocated on first use (lazy_workspace).
+static gemm_status_t workspace(Scratch *sc, void **ws, int *ws_dev, size_t bytes, hipStream_t stream,
+                               void **out) {
+    if (!sc) {
+        const gemm_status_t st = lazy_workspace(ws, ws_dev, bytes, stream);
+        *out = st == GEMM_STATUS_SUCCESS ? *ws : nullptr;
+        return st;
+    }
+    const size_t off = (sc->used + 255) & ~(size_t)255;
+    if (off > sc->cap || bytes > sc->cap - off) return GEMM_STATUS_SCRATCH_LIMIT;
+    sc->used = off + bytes;
+    // the sizing pass never dereferences or launches with the region
+    *out = sc->dry ? reinterpret_cast<void *>((uintptr_t)0x100 + off) : sc->base + off;
+    return GEMM_STATUS_SUCCESS;
+}
+
+static bool launched(Scratch *sc, hipError_t (*fn)(const GemmParams &, hipStream_t), const GemmParams &prm,
+                     hipStream_t s) {
+    return (sc && sc->dry) || fn(prm, s) == hipSuccess;
+}
+
+// One run of plan p: validation, kernel choice per run, launches.  Workspaces come from the
+// plan (gemm_run: allocated on first use, optional ones skipped when they cannot be had) or
+// from the scratch (gemm_run_noalloc: every region the plan's route needs, or SCRATCH_LIMIT).
+static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                              const void *bias, float alpha, float beta, void *stream, Scratch *sc) {
+    if (!p) return GEMM_STATUS_INVALID_VALUE;
+    if (p->M == 0 || p->N == 0 || p->batch == 0) return GEMM_STATUS_SUCCESS;
+    const bool has_bias = p->epi == GEMM_EPI_BIAS || p->epi == GEMM_EPI_BIAS_RELU;
+    const bool relu = p->epi == GEMM_EPI_RELU || p->epi == GEMM_EPI_BIAS_RELU;
+    if (!D) return GEMM_STATUS_INVALID_VALUE;
+    if (p->K > 0 && (!A || !B)) return GEMM_STATUS_INVALID_VALUE;
+    if (beta != 0.0f && !C) return GEMM_STATUS_INVALID_VALUE;
+    if (has_bias && !bias) return GEMM_STATUS_INVALID_VALUE;
+    if (p->ab == GEMM_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f)))
+        return GEMM_STATUS_NOT_SUPPORTED;
+    if (alpha != alpha || beta != beta) return GEMM_STATUS_INVALID_VALUE;  // NaN scalars
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool dry = sc && sc->dry;
+
+    // complex / dual product as a real one: rewrite B (and a transposed A) into the workspace,
+    // then run the real plan; without a plan-owned workspace (first run inside a capture, or no
+    // memory) the complex kernel below runs instead
+    void *cxw = nullptr;
+    if (p->cx) {
+        const gemm_status_t st = workspace(sc, &p->cx_ws, &p->cx_dev, (size_t)p->cx_bytes, hs, &cxw);
+        if (sc && st != GEMM_STATUS_SUCCESS) return st;
+    }
+    if (p->cx && cxw) {
+        const bool dual = p->ab == GEMM_DF16;
+        uint8_t *ws = static_cast<uint8_t *>(cxw);
+        const int64_t na = p->batch > 1 && p->stride_a ? p->batch : 1;
+        const int64_t nbb = p->batch > 1 && p->stride_b ? p->batch : 1;
+        tge::PairJob ja = {}, jb = {};
+        const void *Ar = A;
+        if (p->op_a == GEMM_OP_T) {
+            ja = {static_cast<const uint8_t *>(A), ws, p->K, p->M, p->lda * 4, p->cx_ld_a * 2,
+                  p->stride_a * 4, 2 * p->K * p->cx_ld_a * 2, na, tge::PAIR_PARTS, dual};
+            Ar = ws;
+        }
+        const bool bn = p->op_b == GEMM_OP_N;
+        const int64_t rows_b = bn ? p->K : p->N;
+        jb = {static_cast<const uint8_t *>(B), ws + p->cx_off_b, rows_b, bn ? p->N : p->K, p->ldb * 4,
+              p->cx_ld_b * 2, p->stride_b * 4, 2 * rows_b * p->cx_ld_b * 2, nbb,
+              bn ? tge::PAIR_BLOCK_N : tge::PAIR_BLOCK_T, dual};
+        if (!dry && tge::pair_launch(ja, jb, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+        return run_impl(p->cx, Ar, ws + p->cx_off_b, C, D, nullptr, alpha, beta, stream, sc);
+    }
+
+    GemmParams prm;
+    prm.A = A; prm.B = B; prm.C = C; prm.D = D; prm.bias = bias;
+    prm.M = (int)p->M; prm.N = (int)p->N; prm.K = (int)p->K;
+    prm.lda = (int)p->lda; prm.ldb = (int)p->ldb; prm.ldc = (int)p->ldc;
+    prm.alpha = alpha; prm.beta = beta;
+    prm.has_beta = beta != 0.0f;
+    prm.has_bias = has_bias;
+    prm.relu = relu;
+    prm.group_m = p->group_m;
+    prm.batch = (int)p->batch;
+    prm.xform_a = p->xform_a; prm.xform_b = p->xform_b; prm.xform_c = p->xform_c;
+    prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
+    prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
+    const KernelEntry *k = p->kernel;
+    // Kernel choice per run.  The direct-load fast kernel reads an operand in place when its
+    // rows are on the 16-byte grid (pointer included) and it carries no load transform.  Other
+    // operands are copied first (aligned rows, the transform applied by the copy) when the plan
+    // repacks and its workspace exists or can be had now.  Otherwise the fast kernel with fused
+    // transforms (aligned operands), the register-staged variant, or the general kernel runs.
+    const int kk = p->K > 0 ? 3 : 0;
+    const int unaligned = (p->pk_need | (((uintptr_t)A % 16) ? 1 : 0) | (((uintptr_t)B % 16) ? 2 : 0)) & kk;
+    const int xf = ((p->xform_a ? 1 : 0) | (p->xform_b ? 2 : 0)) & kk;
+    const int need = unaligned | (p->fast_pk && !p->fast_is_skinny ? xf : 0);
+    void *pkw = nullptr;
+    if (!(p->fast && !need) && p->fast_pk && need) {
+        const gemm_status_t st = workspace(sc, &p->pk_ws, &p->pk_dev, (size_t)p->pk_bytes, hs, &pkw);
+        if (sc && st != GEMM_STATUS_SUCCESS) return st;
+    }
+    if (p->fast && !need) k = p->fast;
+    else if (pkw) {
+        const int eab = elem_bytes(p->ab);
+        const bool sh_a = p->batch > 1 && p->stride_a, sh_b = p->batch > 1 && p->stride_b;
+        tge::RepackJob ja = {}, jb = {};
+        uint8_t *ws = static_cast<uint8_t *>(pkw);
+        // stored rows of the copies: K-major operands get pk_kpad rows, the extra ones zero
+        if (need & 1) {
+            const bool an = p->op_a == GEMM_OP_N;
+            const int64_t rows = an ? p->M : p->K, rows_out = an ? p->M : p->pk_kpad;
+            const int64_t len = an ? p->K : p->M;
+            ja = {static_cast<const uint8_t *>(A), ws, rows, rows_out, len * eab, p->lda * eab,
+                  p->pk_ld_a * eab, p->stride_a * eab, rows_out * p->pk_ld_a * eab, sh_a ? p->batch : 1,
+                  p->xform_a ? eab : 0};
+            prm.xform_a = 0;
+            prm.A = ws;
+            prm.lda = (int)p->pk_ld_a;
+            prm.stride_a = sh_a ? rows_out * p->pk_ld_a : 0;
+        }
+        if (need & 2) {
+            const bool bn = p->op_b == GEMM_OP_N;
+            const int64_t rows = bn ? p->K : p->N, rows_out = bn ? p->pk_kpad : p->N;
+            const int64_t len = bn ? p->N : p->K;
+            jb = {static_cast<const uint8_t *>(B), ws + p->pk_off_b, rows, rows_out, len * eab,
+                  p->ldb * eab, p->pk_ld_b * eab, p->stride_b * eab, rows_out * p->pk_ld_b * eab,
+                  sh_b ? p->batch : 1, p->xform_b ? eab : 0};
+            prm.xform_b = 0;
+            prm.B = ws + p->pk_off_b;
+            prm.ldb = (int)p->pk_ld_b;
+            prm.stride_b = sh_b ? rows_out * p->pk_ld_b : 0;
+        }
+        if (!dry && tge::repack_launch(ja, jb, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+        // both operands from the copies: the products past K are 0 * 0, no tail slab
+        if (need == 3) prm.K = (int)p->pk_kpad;
+        k = p->fast_pk;
+    } else if (p->fast && !unaligned) {
+        k = p->fast;              // no workspace: the direct loads with the transforms fused
+    } else if (p->fast_rs) {
+        k = p->fast_rs;
+    }
+    const bool sk = k == p->fast && p->fast_is_skinny;
+    prm.tiles_m = sk ? p->ksplit : (int)((p->M + k->bm - 1) / k->bm);
+    prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
+    prm.ws = nullptr;
+    // split-K partial sums: batch * S * M * N floats (int32 for int8)
+    const size_t split_bytes = (size_t)(p->batch > 1 ? p->batch : 1) * p->ksplit * p->M * p->N * sizeof(float);
+    // fast kernel with K split (needs its workspace; a first run inside a capture runs whole)
+    void *spw = nullptr;
+    if ((k == p->fast || k == p->fast_pk) && !sk && p->fast_part) {
+        const gemm_status_t st = workspace(sc, reinterpret_cast<void **>(&p->ws), &p->ws_dev, split_bytes, hs, &spw);
+        if (sc && st != GEMM_STATUS_SUCCESS) return st;
+    }
+    if (spw) {
+        const int S = p->ksplit;
+        const int kc = (int)(p->K / S);                  // K of one chunk (whole slabs)
+        GemmParams part = prm;
+        part.K = kc;
+        part.batch = S;
+        // chunk offsets in the operands the kernel reads (the copies, when copied)
+        part.stride_a = p->op_a == GEMM_OP_N ? kc : (int64_t)kc * prm.lda;
+        part.stride_b = p->op_b == GEMM_OP_N ? (int64_t)kc * prm.ldb : kc;
+        part.C = nullptr;
+        part.D = spw;
+        part.bias = nullptr;
+        part.alpha = 1.0f;
+        part.beta = 0.0f;
+        part.has_beta = 0;
+        part.has_bias = 0;
+        part.relu = 0;
+        part.xform_c = 0;
+        part.ldc = (int)p->N;
+        part.stride_c = p->M * p->N;
+        part.stride_bias = 0;
+        const unsigned g1 = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * S);
+        if (!dry && p->fast_part->launch(part, g1, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+        GemmParams fin = prm;
+        fin.tiles_m = S;
+        fin.ws = static_cast<float *>(spw);
+        return launched(sc, p->finish, fin, hs) ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;
+    }
+    if (sk && p->ksplit > 1) {
+        void *w = nullptr;
+        const gemm_status_t st = workspace(sc, reinterpret_cast<void **>(&p->ws), &p->ws_dev, split_bytes, hs, &w);
+        if (st != GEMM_STATUS_SUCCESS) return st;
+        prm.ws = static_cast<float *>(w);
+    }
+    if (dry) return GEMM_STATUS_SUCCESS;
+    const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * p->batch);
+    hipError_t e = k->launch(prm, grid, hs);
+    return e == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;
 }
 
 extern "C" {
@@ -208,6 +423,7 @@ const char *gemm_status_string(gemm_status_t s) {
     case GEMM_STATUS_NOT_SUPPORTED: return "GEMM_STATUS_NOT_SUPPORTED";
     case GEMM_STATUS_HIP_ERROR: return "GEMM_STATUS_HIP_ERROR";
     case GEMM_STATUS_ALLOC_FAILED: return "GEMM_STATUS_ALLOC_FAILED";
+    case GEMM_STATUS_SCRATCH_LIMIT: return "GEMM_STATUS_SCRATCH_LIMIT";
     }
     return "GEMM_STATUS_UNKNOWN";
 }
@@ -573,153 +789,23 @@ gemm_status_t gemm_plan_describe(gemm_plan_t p, char *buf, size_t len) {
 
 gemm_status_t gemm_run(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
                        const void *bias, float alpha, float beta, void *stream) {
-    if (!p) return GEMM_STATUS_INVALID_VALUE;
-    if (p->M == 0 || p->N == 0 || p->batch == 0) return GEMM_STATUS_SUCCESS;
-    const bool has_bias = p->epi == GEMM_EPI_BIAS || p->epi == GEMM_EPI_BIAS_RELU;
-    const bool relu = p->epi == GEMM_EPI_RELU || p->epi == GEMM_EPI_BIAS_RELU;
-    if (!D) return GEMM_STATUS_INVALID_VALUE;
-    if (p->K > 0 && (!A || !B)) return GEMM_STATUS_INVALID_VALUE;
-    if (beta != 0.0f && !C) return GEMM_STATUS_INVALID_VALUE;
-    if (has_bias && !bias) return GEMM_STATUS_INVALID_VALUE;
-    if (p->ab == GEMM_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f)))
-        return GEMM_STATUS_NOT_SUPPORTED;
-    if (alpha != alpha || beta != beta) return GEMM_STATUS_INVALID_VALUE;  // NaN scalars
+    return run_impl(p, A, B, C, D, bias, alpha, beta, stream, nullptr);
+}
 
-    // complex / dual product as a real one: rewrite B (and a transposed A) into the plan's
-    // workspace, then run the real plan; without a workspace (first run inside a capture, or
-    // no memory) the complex kernel below runs instead
-    if (p->cx && lazy_workspace(&p->cx_ws, &p->cx_dev, (size_t)p->cx_bytes,
-                                static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
-        const bool dual = p->ab == GEMM_DF16;
-        uint8_t *ws = static_cast<uint8_t *>(p->cx_ws);
-        const int64_t na = p->batch > 1 && p->stride_a ? p->batch : 1;
-        const int64_t nbb = p->batch > 1 && p->stride_b ? p->batch : 1;
-        tge::PairJob ja = {}, jb = {};
-        const void *Ar = A;
-        if (p->op_a == GEMM_OP_T) {
-            ja = {static_cast<const uint8_t *>(A), ws, p->K, p->M, p->lda * 4, p->cx_ld_a * 2,
-                  p->stride_a * 4, 2 * p->K * p->cx_ld_a * 2, na, tge::PAIR_PARTS, dual};
-            Ar = ws;
-        }
-        const bool bn = p->op_b == GEMM_OP_N;
-        const int64_t rows_b = bn ? p->K : p->N;
-        jb = {static_cast<const uint8_t *>(B), ws + p->cx_off_b, rows_b, bn ? p->N : p->K, p->ldb * 4,
-              p->cx_ld_b * 2, p->stride_b * 4, 2 * rows_b * p->cx_ld_b * 2, nbb,
-              bn ? tge::PAIR_BLOCK_N : tge::PAIR_BLOCK_T, dual};
-        if (tge::pair_launch(ja, jb, static_cast<hipStream_t>(stream)) != hipSuccess)
-            return GEMM_STATUS_HIP_ERROR;
-        return gemm_run(p->cx, Ar, ws + p->cx_off_b, C, D, nullptr, alpha, beta, stream);
+gemm_status_t gemm_run_noalloc(gemm_plan_t p, const void *A, const void *B, const void *C, void *D,
+                               const void *bias, float alpha, float beta, void *stream) {
+    // sizing pass first (no HIP call): a run that needs more scratch than the array holds is
+    // rejected before anything is enqueued
+    Scratch size = {nullptr, (size_t)GEMM_NOALLOC_SCRATCH_BYTES, 0, true};
+    const gemm_status_t st = run_impl(p, A, B, C, D, bias, alpha, beta, stream, &size);
+    if (st != GEMM_STATUS_SUCCESS) return st;
+    // the same route again, launching; a route that takes no region never needs the address
+    Scratch sc = {nullptr, size.used, 0, false};
+    if (size.used > 0) {
+        const gemm_status_t sa = scratch_address(&sc.base);
+        if (sa != GEMM_STATUS_SUCCESS) return sa;
     }
-
-    GemmParams prm;
-    prm.A = A; prm.B = B; prm.C = C; prm.D = D; prm.bias = bias;
-    prm.M = (int)p->M; prm.N = (int)p->N; prm.K = (int)p->K;
-    prm.lda = (int)p->lda; prm.ldb = (int)p->ldb; prm.ldc = (int)p->ldc;
-    prm.alpha = alpha; prm.beta = beta;
-    prm.has_beta = beta != 0.0f;
-    prm.has_bias = has_bias;
-    prm.relu = relu;
-    prm.group_m = p->group_m;
-    prm.batch = (int)p->batch;
-    prm.xform_a = p->xform_a; prm.xform_b = p->xform_b; prm.xform_c = p->xform_c;
-    prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
-    prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
-    const KernelEntry *k = p->kernel;
-    // Kernel choice per run.  The direct-load fast kernel reads an operand in place when its
-    // rows are on the 16-byte grid (pointer included) and it carries no load transform.  Other
-    // operands are copied first (aligned rows, the transform applied by the copy) when the plan
-    // repacks and its workspace exists or can be allocated now.  Otherwise the fast kernel
-    // with fused transforms (aligned operands), the register-staged variant, or the general
-    // kernel runs.
-    const int kk = p->K > 0 ? 3 : 0;
-    const int unaligned = (p->pk_need | (((uintptr_t)A % 16) ? 1 : 0) | (((uintptr_t)B % 16) ? 2 : 0)) & kk;
-    const int xf = ((p->xform_a ? 1 : 0) | (p->xform_b ? 2 : 0)) & kk;
-    const int need = unaligned | (p->fast_pk && !p->fast_is_skinny ? xf : 0);
-    if (p->fast && !need) k = p->fast;
-    else if (p->fast_pk && need && repack_workspace(p, static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
-        const int eab = elem_bytes(p->ab);
-        const bool sh_a = p->batch > 1 && p->stride_a, sh_b = p->batch > 1 && p->stride_b;
-        tge::RepackJob ja = {}, jb = {};
-        uint8_t *ws = static_cast<uint8_t *>(p->pk_ws);
-        // stored rows of the copies: K-major operands get pk_kpad rows, the extra ones zero
-        if (need & 1) {
-            const bool an = p->op_a == GEMM_OP_N;
-            const int64_t rows = an ? p->M : p->K, rows_out = an ? p->M : p->pk_kpad;
-            const int64_t len = an ? p->K : p->M;
-            ja = {static_cast<const uint8_t *>(A), ws, rows, rows_out, len * eab, p->lda * eab,
-                  p->pk_ld_a * eab, p->stride_a * eab, rows_out * p->pk_ld_a * eab, sh_a ? p->batch : 1,
-                  p->xform_a ? eab : 0};
-            prm.xform_a = 0;
-            prm.A = ws;
-            prm.lda = (int)p->pk_ld_a;
-            prm.stride_a = sh_a ? rows_out * p->pk_ld_a : 0;
-        }
-        if (need & 2) {
-            const bool bn = p->op_b == GEMM_OP_N;
-            const int64_t rows = bn ? p->K : p->N, rows_out = bn ? p->pk_kpad : p->N;
-            const int64_t len = bn ? p->N : p->K;
-            jb = {static_cast<const uint8_t *>(B), ws + p->pk_off_b, rows, rows_out, len * eab,
-                  p->ldb * eab, p->pk_ld_b * eab, p->stride_b * eab, rows_out * p->pk_ld_b * eab,
-                  sh_b ? p->batch : 1, p->xform_b ? eab : 0};
-            prm.xform_b = 0;
-            prm.B = ws + p->pk_off_b;
-            prm.ldb = (int)p->pk_ld_b;
-            prm.stride_b = sh_b ? rows_out * p->pk_ld_b : 0;
-        }
-        if (tge::repack_launch(ja, jb, static_cast<hipStream_t>(stream)) != hipSuccess)
-            return GEMM_STATUS_HIP_ERROR;
-        // both operands from the copies: the products past K are 0 * 0, no tail slab
-        if (need == 3) prm.K = (int)p->pk_kpad;
-        k = p->fast_pk;
-    } else if (p->fast && !unaligned) {
-        k = p->fast;              // no workspace: the direct loads with the transforms fused
-    } else if (p->fast_rs) {
-        k = p->fast_rs;
-    }
-    const bool sk = k == p->fast && p->fast_is_skinny;
-    prm.tiles_m = sk ? p->ksplit : (int)((p->M + k->bm - 1) / k->bm);
-    prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
-    prm.ws = nullptr;
-    // fast kernel with K split (needs its workspace; a first run inside a capture runs whole)
-    if ((k == p->fast || k == p->fast_pk) && !sk && p->fast_part &&
-        skinny_workspace(p, static_cast<hipStream_t>(stream)) == GEMM_STATUS_SUCCESS) {
-        const int S = p->ksplit;
-        const int kc = (int)(p->K / S);                  // K of one chunk (whole slabs)
-        GemmParams part = prm;
-        part.K = kc;
-        part.batch = S;
-        // chunk offsets in the operands the kernel reads (the copies, when copied)
-        part.stride_a = p->op_a == GEMM_OP_N ? kc : (int64_t)kc * prm.lda;
-        part.stride_b = p->op_b == GEMM_OP_N ? (int64_t)kc * prm.ldb : kc;
-        part.C = nullptr;
-        part.D = p->ws;
-        part.bias = nullptr;
-        part.alpha = 1.0f;
-        part.beta = 0.0f;
-        part.has_beta = 0;
-        part.has_bias = 0;
-        part.relu = 0;
-        part.xform_c = 0;
-        part.ldc = (int)p->N;
-        part.stride_c = p->M * p->N;
-        part.stride_bias = 0;
-        const unsigned g1 = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * S);
-        if (p->fast_part->launch(part, g1, static_cast<hipStream_t>(stream)) != hipSuccess)
-            return GEMM_STATUS_HIP_ERROR;
-        GemmParams fin = prm;
-        fin.tiles_m = S;
-        fin.ws = p->ws;
-        return p->finish(fin, static_cast<hipStream_t>(stream)) == hipSuccess ? GEMM_STATUS_SUCCESS
-                                                                              : GEMM_STATUS_HIP_ERROR;
-    }
-    if (sk && p->ksplit > 1) {
-        const gemm_status_t st = skinny_workspace(p, static_cast<hipStream_t>(stream));
-        if (st != GEMM_STATUS_SUCCESS) return st;
-        prm.ws = p->ws;
-    }
-    const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * p->batch);
-    hipError_t e = k->launch(prm, grid, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;
+    return run_impl(p, A, B, C, D, bias, alpha, beta, stream, &sc);
 }
 
 }  // extern "C"
