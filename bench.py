@@ -214,8 +214,8 @@ def main():
             t = torch.from_numpy(flat)
         return t.to("cuda:0")
 
-    A = dev(p.ab, x["A"])
-    B = dev(p.ab, x["B"])
+    A = dev(p.a_store, x["A"])
+    B = dev(p.b_store, x["B"])
     C = dev(p.cd, x["C"]) if x["C"] is not None else None
     bias = dev(p.bias_dt, x["bias"]) if x["bias"] is not None else None
     pair = p.cd in synth.PART          # complex / dual output: interleaved parts
@@ -366,9 +366,9 @@ def main():
             maxb = float(np.abs(oracle.decode(synth.PART[p.ab], x["B"])).max())
         else:
             maxa = (float(np.abs(oracle.decode(p.ab, x["A"])).max()) if p.kind_a == "diagonal"
-                    else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda))
+                    else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda, p.transform_a))
             maxb = (float(np.abs(oracle.decode(p.ab, x["B"])).max()) if p.kind_b == "diagonal"
-                    else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb))
+                    else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb, p.transform_b))
         den = p.K * maxa * maxb
         err = float(np.max(np.abs(got - ref)) / den) if den else float(np.max(np.abs(got - ref)))
         parity = {"rows_checked": rows, "max_normalised_error": err, "tolerance": 2e-3,

@@ -121,8 +121,24 @@ typedef enum {
  * activation, and the "bias + ReLU on C & D" variant of that paper's section 5.3 (Table 2).
  *   GEMM_TRANSFORM_RELU replaces every element whose sign bit is set by +0, i.e. max(x, 0) for
  *   every non-NaN x (-0 becomes +0; a NaN keeps its value unless its sign bit is set).
+ * The type conversions of that section ("a type conversion after a load"), for op(A) and op(B)
+ * of a 16-bit plan (ab_type F16 or BF16) with dense operands:
+ *   GEMM_TRANSFORM_FROM_F32  the operand is stored as fp32 (its leading dimension and batch
+ *                            stride count fp32 elements) and every element is rounded to the
+ *                            nearest ab_type value, ties to even, as it is loaded;
+ *   GEMM_TRANSFORM_FROM_I8   the operand is stored as int8 and converted exactly.
+ * A plan with a conversion converts those operands, once per run, into 16-bit rows of a
+ * workspace it owns ("convert A/B from f32/i8" in its description), allocated by its first run
+ * on a device (that run must not be captured into a graph: it returns NOT_SUPPORTED there) and
+ * freed by gemm_plan_destroy; its runs must not overlap in time.  Then the product runs on the
+ * converted rows as the same plan without the conversion would.
  */
-typedef enum { GEMM_TRANSFORM_NONE = 0, GEMM_TRANSFORM_RELU = 1 } gemm_transform_t;
+typedef enum {
+    GEMM_TRANSFORM_NONE = 0,
+    GEMM_TRANSFORM_RELU = 1,
+    GEMM_TRANSFORM_FROM_F32 = 2,
+    GEMM_TRANSFORM_FROM_I8 = 3
+} gemm_transform_t;
 
 /*
  * Kind of an operand.  GEMM_OPERAND_DIAGONAL: the operand is a square diagonal matrix given by
@@ -164,7 +180,7 @@ typedef struct gemm_plan *gemm_plan_t;
  * arguments of gemm_plan_create; batch and the strides are those of gemm_plan_create_batched
  * (batch 1 and zero strides for a single product); transform_a / transform_b act on op(A) and
  * op(B) (zero-padding past the edges is unaffected), transform_c on C before it is scaled by
- * beta; kind_a / kind_b make an operand diagonal (see gemm_operand_t; a diagonal operand's
+ * beta (NONE or RELU: C has the type of D); kind_a / kind_b make an operand diagonal (see gemm_operand_t; a diagonal operand's
  * stride_a / stride_b moves its vector); algo pins the kernel route (see gemm_algo_t;
  * GEMM_ALGO_AUTO for the plan's own choice) and tile the workgroup tile of the general kernel
  * (256, 128 or 64; 0 for the plan's own choice; 256 also selects the fast kernel where it
@@ -229,8 +245,10 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
  * and gemm_plan_create_batched plus the load transforms,
  *   D_b = act(alpha * tA(op(A_b)) * tB(op(B_b)) + beta * tC(C_b) + bias_b).
  * Returns the errors of gemm_plan_create_batched, plus INVALID_VALUE for desc == NULL, a
- * transform, operand kind or algorithm out of range, a tile other than 0, 256, 128 or 64, or a
- * diagonal operand that is not square (K != M for A, K != N for B).
+ * transform, operand kind or algorithm out of range (a conversion on C included), a tile other
+ * than 0, 256, 128 or 64, or a diagonal operand that is not square (K != M for A, K != N for B);
+ * NOT_SUPPORTED for a conversion on a plan whose ab_type is not F16 or BF16, or on a diagonal
+ * or complex operand.  The span limit applies to a converted operand in its stored type.
  */
 gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
 
@@ -247,7 +265,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc);
  *   alpha, beta  scalars applied in fp32 (int8 plans require alpha == 1 and beta in {0, 1}).
  * Returns INVALID_VALUE for a NULL plan, a missing required pointer or a NaN scalar,
  * NOT_SUPPORTED for int8 scalars outside the rule above or for the first run of a skinny split-K
- * plan during stream capture, ALLOC_FAILED when that first run cannot allocate its workspace
+ * plan or of a converting plan (GEMM_TRANSFORM_FROM_*) during stream capture, ALLOC_FAILED when
+ * that first run cannot allocate its workspace
  * (the plans that copy or rewrite operands, or split K for the fast kernel, run without their
  * workspace instead), HIP_ERROR when a launch fails.  M == 0, N == 0 or a batch of 0 returns
  * SUCCESS without launching.

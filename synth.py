@@ -380,6 +380,24 @@ def complex_fp16():
                     name="complex_fp16")]
 
 
+def convert_fp16():
+    """Type-converting load transforms ("Flexible Performant GEMM Kernels on GPUs", section 4: a
+    transform after every load, including a type conversion) at fully-connected and headline
+    sizes: [0] fp16 activations 8192 x 4096 ~ N(0,1)/sqrt(K) times int8 weights 4096 x 16384
+    (integers in [-8, 8]) converted to fp16 as they are loaded, bias+ReLU -> fp16; [1] fp32
+    operands 8192^3 ~ N(0,1)/sqrt(K) rounded to bf16 as they are loaded, bias+ReLU -> bf16."""
+    K = 4096
+    out = [Problem(8192, 16384, K, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                   a_dist=("normal", 1.0 / math.sqrt(K)), b_dist=("int", -8, 8), key=(10, 0),
+                   name="convert_fp16", transform_b="from_i8")]
+    K = 8192
+    s = 1.0 / math.sqrt(K)
+    out.append(Problem(8192, 8192, K, "N", "N", "bf16", "bf16", "bias_relu", 1.0, 0.0,
+                       a_dist=("normal", s), b_dist=("normal", s), key=(10, 1),
+                       name="convert_fp16", transform_a="from_f32", transform_b="from_f32"))
+    return out
+
+
 WORKLOADS = {
     "sgemm_256": sgemm_256,
     "fp16_8192_bias_relu": fp16_8192_bias_relu,
@@ -391,6 +409,7 @@ WORKLOADS = {
     "fp16_8192_transforms": fp16_8192_transforms,
     "diag_fp16": diag_fp16,
     "complex_fp16": complex_fp16,
+    "convert_fp16": convert_fp16,
 }
 
 

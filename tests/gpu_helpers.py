@@ -44,8 +44,8 @@ def sentinel(dtype):
 def run(p, x, offset=0, d_rows_extra=0, c_is_d=False, stream=None, plan=None):
     """Run problem p with inputs x on the GPU; returns the raw D storage (rows M + extra, ldc)
     initialised with a sentinel, so untouched elements are visible."""
-    A = to_dev(p.ab, x["A"], offset)
-    B = to_dev(p.ab, x["B"], offset)
+    A = to_dev(p.a_store, x["A"], offset)
+    B = to_dev(p.b_store, x["B"], offset)
     rows = p.M + d_rows_extra
     Dinit = np.full(rows * p.ldc, sentinel(p.cd), dtype=synth.RAW_NP[p.cd])
     if c_is_d:
@@ -72,9 +72,9 @@ def reference(p, x, rows=None, threads=None):
 
 def normaliser(p, x):
     ma = (float(np.abs(oracle.decode(p.ab, x["A"])).max()) if p.kind_a == "diagonal"
-          else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda))
+          else oracle.max_abs_op(p.ab, x["A"], p.op_a, p.M, p.K, p.lda, p.transform_a))
     mb = (float(np.abs(oracle.decode(p.ab, x["B"])).max()) if p.kind_b == "diagonal"
-          else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb))
+          else oracle.max_abs_op(p.ab, x["B"], p.op_b, p.K, p.N, p.ldb, p.transform_b))
     return p.K * ma * mb
 
 
@@ -123,8 +123,8 @@ def check_points(p, x, Draw, n=2000, seed=0):
 def run_batched(p, x, offset=0):
     """Run the strided-batched problem p (flat inputs x) through a batched plan; returns the raw
     flat D storage (initialised with a sentinel, gaps between products included)."""
-    A = to_dev(p.ab, x["A"], offset)
-    B = to_dev(p.ab, x["B"], offset)
+    A = to_dev(p.a_store, x["A"], offset)
+    B = to_dev(p.b_store, x["B"], offset)
     nD = max(p.batch - 1, 0) * p.stride_c + p.M * p.ldc
     D = to_dev(p.cd, np.full(nD, sentinel(p.cd), dtype=synth.RAW_NP[p.cd]), offset)
     C = to_dev(p.cd, x["C"], offset) if x["C"] is not None else None

@@ -188,7 +188,7 @@ def test_desc_validation_and_transforms_described():
                                       transform_a="relu", transform_c="relu")
     assert st == tge.STATUS_SUCCESS and "relu-in AC" in tge.gemm_plan_describe(h)[1]
     tge.gemm_plan_destroy(h)
-    for bad in (dict(transform_a=2), dict(transform_b=-1), dict(transform_c=7)):
+    for bad in (dict(transform_a=4), dict(transform_b=-1), dict(transform_c=7), dict(transform_c=2)):
         st, h = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, "f16", "f16", "none",
                                           **bad)
         assert st == tge.STATUS_INVALID_VALUE and h is None
@@ -358,3 +358,20 @@ def test_noalloc_rejects_runs_beyond_the_scratch_before_any_device_call():
     assert tge.gemm_run_noalloc(None, fake, fake, None, fake, None, 1.0, 0.0, None) == \
         tge.STATUS_INVALID_VALUE
     tge.gemm_plan_destroy(h)
+
+
+def test_conversion_plans_validate():
+    # conversions need a 16-bit input type and dense operands; none on C
+    ok = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, "f16", "f16", "none",
+                                   transform_a="from_f32")
+    assert ok[0] == tge.STATUS_SUCCESS
+    tge.gemm_plan_destroy(ok[1])
+    for kw, st in [(dict(ab_type="i8", cd_type="i32", transform_b="from_f32"), tge.STATUS_NOT_SUPPORTED),
+                   (dict(transform_c="from_f32"), tge.STATUS_INVALID_VALUE),
+                   (dict(transform_a=4), tge.STATUS_INVALID_VALUE),
+                   (dict(transform_a="from_i8", kind_a="diagonal"), tge.STATUS_NOT_SUPPORTED)]:
+        a = dict(ab_type="f16", cd_type="f16")
+        a.update(kw)
+        ab, cd = a.pop("ab_type"), a.pop("cd_type")
+        got = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, ab, cd, "none", **a)
+        assert got[0] == st and got[1] is None, (kw, got)

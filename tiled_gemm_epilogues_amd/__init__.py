@@ -25,7 +25,9 @@ DTYPE = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "cf16": 5, "cf32": 6,
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "cf16": 4, "cf32": 8, "df16": 4,
               "df32": 8}
 EPILOGUE = {"none": 0, "relu": 1, "bias": 2, "bias_relu": 3}
-TRANSFORM = {"none": 0, "relu": 1}
+TRANSFORM = {"none": 0, "relu": 1, "from_f32": 2, "from_i8": 3}
+# stored element type of an operand whose load transform converts it to the input type
+STORED_BY_TRANSFORM = {"from_f32": "f32", "from_i8": "i8"}
 KIND = {"dense": 0, "diagonal": 1}
 ALGO = {"auto": 0, "fast": 1, "staged": 2, "general": 3, "skinny": 4, "split": 5, "nosplit": 6}
 (STATUS_SUCCESS, STATUS_INVALID_VALUE, STATUS_NOT_SUPPORTED, STATUS_HIP_ERROR,
@@ -192,6 +194,7 @@ class Plan:
         self.stride_a, self.stride_b, self.stride_c = stride_a, stride_b, stride_c
         self.stride_bias = stride_bias
         self.kind_a, self.kind_b = kind_a, kind_b
+        self.transform_a, self.transform_b = transform_a, transform_b
         xf = (transform_a, transform_b, transform_c)
         if (any(_enum(TRANSFORM, t) for t in xf) or _enum(KIND, kind_a) or _enum(KIND, kind_b)
                 or _enum(ALGO, algo) or tile):
@@ -240,9 +243,11 @@ class Plan:
         return {"A": a, "B": b, "C": cd, "D": cd, "bias": bias}
 
     def dtype_of(self, what):
-        """Element type of operand `what` ("A", "B", "C", "D" or "bias")."""
-        if what in ("A", "B"):
-            return self.ab
+        """Stored element type of operand `what` ("A", "B", "C", "D" or "bias")."""
+        if what == "A":
+            return STORED_BY_TRANSFORM.get(self.transform_a, self.ab)
+        if what == "B":
+            return STORED_BY_TRANSFORM.get(self.transform_b, self.ab)
         if what in ("C", "D"):
             return self.cd
         return "i32" if self.ab == "i8" else "f32"

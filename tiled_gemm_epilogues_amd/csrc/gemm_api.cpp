@@ -45,6 +45,16 @@ struct gemm_plan {
     int64_t cx_off_b, cx_bytes;      // byte offset of B's rewrite in the workspace, total size
     int cx_dev;
     void *cx_ws;
+    // operands stored as fp32 or int8 and converted to the 16-bit input type as they are
+    // loaded: a conversion pass into the workspace, then the plan cv on the converted rows
+    gemm_plan *cv;                   // nullptr: no conversion
+    int cv_src_a, cv_src_b;          // -1: not converted, else tge::ConvertSrc
+    int64_t cv_rows_a, cv_rows_b;    // stored rows of one product's operand
+    int64_t cv_len_a, cv_len_b;      // elements per stored row
+    int64_t cv_ld_a, cv_ld_b;        // pitch (elements) of the converted rows
+    int64_t cv_off_b, cv_bytes;      // byte offset of B's converted rows, workspace size
+    int cv_dev;
+    void *cv_ws;
     int tiles_m, tiles_n, group_m;
     unsigned grid;
     char desc[256];
@@ -265,6 +275,36 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool dry = sc && sc->dry;
 
+    // operands stored as fp32 or int8: convert them into 16-bit rows of the workspace, then run
+    // the plan on the converted rows (the conversion needs its workspace: a first run inside a
+    // stream capture returns NOT_SUPPORTED, as a failed allocation returns ALLOC_FAILED)
+    if (p->cv) {
+        if (p->K == 0) return run_impl(p->cv, A, B, C, D, bias, alpha, beta, stream, sc);
+        void *w = nullptr;
+        const gemm_status_t st = workspace(sc, &p->cv_ws, &p->cv_dev, (size_t)p->cv_bytes, hs, &w);
+        if (st != GEMM_STATUS_SUCCESS) return st;
+        uint8_t *ws = static_cast<uint8_t *>(w);
+        const int to_bf16 = p->ab == GEMM_BF16 ? 1 : 0;
+        const auto src_bytes = [](int src) { return src == tge::CONVERT_FROM_F32 ? 4 : 1; };
+        tge::ConvertJob ja = {}, jb = {};
+        if (p->cv_src_a >= 0) {
+            const int sb = src_bytes(p->cv_src_a);
+            const int64_t na = p->batch > 1 && p->stride_a ? p->batch : 1;
+            ja = {static_cast<const uint8_t *>(A), ws, p->cv_rows_a, p->cv_len_a, p->lda * sb,
+                  p->cv_ld_a * 2, p->stride_a * sb, p->cv_rows_a * p->cv_ld_a * 2, na, p->cv_src_a, to_bf16};
+        }
+        if (p->cv_src_b >= 0) {
+            const int sb = src_bytes(p->cv_src_b);
+            const int64_t nbb = p->batch > 1 && p->stride_b ? p->batch : 1;
+            jb = {static_cast<const uint8_t *>(B), ws + p->cv_off_b, p->cv_rows_b, p->cv_len_b,
+                  p->ldb * sb, p->cv_ld_b * 2, p->stride_b * sb, p->cv_rows_b * p->cv_ld_b * 2, nbb,
+                  p->cv_src_b, to_bf16};
+        }
+        if (!dry && tge::convert_launch(ja, jb, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+        return run_impl(p->cv, p->cv_src_a >= 0 ? ws : A, p->cv_src_b >= 0 ? ws + p->cv_off_b : B, C, D,
+                        bias, alpha, beta, stream, sc);
+    }
+
     // complex / dual product as a real one: rewrite B (and a transposed A) into the workspace,
     // then run the real plan; without a plan-owned workspace (first run inside a capture, or no
     // memory) the complex kernel below runs instead
@@ -466,8 +506,15 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const int64_t batch = desc->batch;
     int64_t stride_a = desc->stride_a, stride_b = desc->stride_b, stride_c = desc->stride_c,
             stride_bias = desc->stride_bias;
-    for (gemm_transform_t t : {desc->transform_a, desc->transform_b, desc->transform_c})
-        if ((int)t != GEMM_TRANSFORM_NONE && (int)t != GEMM_TRANSFORM_RELU) return GEMM_STATUS_INVALID_VALUE;
+    for (gemm_transform_t t : {desc->transform_a, desc->transform_b})
+        if ((int)t < GEMM_TRANSFORM_NONE || (int)t > GEMM_TRANSFORM_FROM_I8) return GEMM_STATUS_INVALID_VALUE;
+    // C has the type of D: no conversion on C
+    if ((int)desc->transform_c != GEMM_TRANSFORM_NONE && (int)desc->transform_c != GEMM_TRANSFORM_RELU)
+        return GEMM_STATUS_INVALID_VALUE;
+    const auto converts = [](gemm_transform_t t) {
+        return t == GEMM_TRANSFORM_FROM_F32 || t == GEMM_TRANSFORM_FROM_I8;
+    };
+    const bool cva = converts(desc->transform_a), cvb = converts(desc->transform_b);
     for (gemm_operand_t k : {desc->kind_a, desc->kind_b})
         if ((int)k != GEMM_OPERAND_DENSE && (int)k != GEMM_OPERAND_DIAGONAL) return GEMM_STATUS_INVALID_VALUE;
     if ((int)desc->algo < GEMM_ALGO_AUTO || (int)desc->algo > GEMM_ALGO_NOSPLIT) return GEMM_STATUS_INVALID_VALUE;
@@ -499,11 +546,19 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (ctable && (epi != GEMM_EPI_NONE || desc->transform_a || desc->transform_b || desc->transform_c ||
                    diag_a || diag_b))
         return GEMM_STATUS_NOT_SUPPORTED;
-    // 32-bit offsets inside the kernels: every matrix must span less than 2^31 bytes
+    // type-converting load transforms: 16-bit inputs, dense operands
+    if ((cva || cvb) && ((ab_type != GEMM_F16 && ab_type != GEMM_BF16) || diag_a || diag_b))
+        return GEMM_STATUS_NOT_SUPPORTED;
+    // 32-bit offsets inside the kernels: every matrix must span less than 2^31 bytes (a
+    // converted operand: in its stored type)
     const int64_t lim = (int64_t)1 << 31;
     int eab = elem_bytes(ab_type), ecd = elem_bytes(cd_type);
-    int64_t sa = diag_a ? K * eab : op_a == GEMM_OP_N ? span_bytes(M, K, lda, eab) : span_bytes(K, M, lda, eab);
-    int64_t sb = diag_b ? K * eab : op_b == GEMM_OP_N ? span_bytes(K, N, ldb, eab) : span_bytes(N, K, ldb, eab);
+    const auto stored_bytes = [&](gemm_transform_t t) {
+        return t == GEMM_TRANSFORM_FROM_F32 ? 4 : t == GEMM_TRANSFORM_FROM_I8 ? 1 : eab;
+    };
+    const int esa = stored_bytes(desc->transform_a), esb = stored_bytes(desc->transform_b);
+    int64_t sa = diag_a ? K * esa : op_a == GEMM_OP_N ? span_bytes(M, K, lda, esa) : span_bytes(K, M, lda, esa);
+    int64_t sb = diag_b ? K * esb : op_b == GEMM_OP_N ? span_bytes(K, N, ldb, esb) : span_bytes(N, K, ldb, esb);
     int64_t sc = span_bytes(M, N, ldc, ecd);
     if (sa >= lim || sb >= lim || sc >= lim || lda >= lim || ldb >= lim || ldc >= lim)
         return GEMM_STATUS_NOT_SUPPORTED;
@@ -515,6 +570,66 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (batch > 1 && (stride_a > big / batch / 4 || stride_b > big / batch / 4 ||
                       stride_c > big / batch / 4 || stride_bias > big / batch / 4))
         return GEMM_STATUS_NOT_SUPPORTED;
+
+    if (cva || cvb) {
+        // the product runs as a plan on the converted operands: 16-bit rows, pitch whole
+        // 16-byte chunks, one converted copy per product (one for all when the stride is 0)
+        const int64_t rows_a = op_a == GEMM_OP_N ? M : K, len_a = op_a == GEMM_OP_N ? K : M;
+        const int64_t rows_b = op_b == GEMM_OP_N ? K : N, len_b = op_b == GEMM_OP_N ? N : K;
+        const int64_t ld_a = ((len_a > 1 ? len_a : 1) + 7) / 8 * 8, ld_b = ((len_b > 1 ? len_b : 1) + 7) / 8 * 8;
+        const int64_t na = batch > 1 && stride_a ? batch : 1, nbb = batch > 1 && stride_b ? batch : 1;
+        gemm_desc_t r = *desc;
+        if (cva) {
+            r.transform_a = GEMM_TRANSFORM_NONE;
+            r.lda = ld_a;
+            r.stride_a = na > 1 ? rows_a * ld_a : 0;
+        }
+        if (cvb) {
+            r.transform_b = GEMM_TRANSFORM_NONE;
+            r.ldb = ld_b;
+            r.stride_b = nbb > 1 ? rows_b * ld_b : 0;
+        }
+        const int64_t bytes_a = cva ? na * rows_a * ld_a * 2 : 0;
+        const int64_t off_b = (bytes_a + 255) / 256 * 256;
+        const int64_t bytes = off_b + (cvb ? nbb * rows_b * ld_b * 2 : 0);
+        // the conversion grid (workgroups of 4 rows x 512 elements) fits 31 bits
+        const int64_t blocks = (cva ? (ld_a / 8 + 63) / 64 * ((rows_a + 3) / 4) * na : 0) +
+                               (cvb ? (ld_b / 8 + 63) / 64 * ((rows_b + 3) / 4) * nbb : 0);
+        if (blocks >= lim) return GEMM_STATUS_NOT_SUPPORTED;
+        gemm_plan *inner = nullptr;
+        const gemm_status_t st = gemm_plan_create_desc(&inner, &r);
+        if (st != GEMM_STATUS_SUCCESS) return st;
+        gemm_plan *p = new (std::nothrow) gemm_plan();
+        if (!p) {
+            gemm_plan_destroy(inner);
+            return GEMM_STATUS_ALLOC_FAILED;
+        }
+        p->M = M; p->N = N; p->K = K;
+        p->lda = lda; p->ldb = ldb; p->ldc = ldc;
+        p->batch = batch;
+        p->stride_a = stride_a; p->stride_b = stride_b; p->stride_c = stride_c; p->stride_bias = stride_bias;
+        p->op_a = op_a; p->op_b = op_b; p->ab = ab_type; p->cd = cd_type; p->epi = epi;
+        p->xform_a = desc->transform_a; p->xform_b = desc->transform_b; p->xform_c = desc->transform_c;
+        p->kernel = inner->kernel;
+        p->ws_dev = p->pk_dev = p->cx_dev = p->cv_dev = -1;
+        p->ksplit = 1;
+        p->cv = inner;
+        p->cv_src_a = cva ? (desc->transform_a == GEMM_TRANSFORM_FROM_F32 ? tge::CONVERT_FROM_F32 : tge::CONVERT_FROM_I8) : -1;
+        p->cv_src_b = cvb ? (desc->transform_b == GEMM_TRANSFORM_FROM_F32 ? tge::CONVERT_FROM_F32 : tge::CONVERT_FROM_I8) : -1;
+        p->cv_rows_a = rows_a; p->cv_rows_b = rows_b;
+        p->cv_len_a = len_a; p->cv_len_b = len_b;
+        p->cv_ld_a = ld_a; p->cv_ld_b = ld_b;
+        p->cv_off_b = off_b; p->cv_bytes = bytes;
+        p->grid = inner->grid;
+        const auto src_name = [](int src) { return src == tge::CONVERT_FROM_F32 ? "f32" : "i8"; };
+        char conv[64] = "";
+        int cl = 0;
+        if (cva) cl += snprintf(conv + cl, sizeof(conv) - cl, " convert A from %s", src_name(p->cv_src_a));
+        if (cvb) snprintf(conv + cl, sizeof(conv) - cl, " convert B from %s", src_name(p->cv_src_b));
+        snprintf(p->desc, sizeof(p->desc), "%s%s", inner->desc, conv);
+        *out = p;
+        return GEMM_STATUS_SUCCESS;
+    }
 
     int cfg = (diag_a || diag_b || ctable) ? tge::CFG_128 : choose_cfg(M, N, batch);
     // an explicit tile in the description pins the workgroup tile
@@ -715,6 +830,12 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->ksplit = 1;
     p->ws_dev = -1;
     p->ws = nullptr;
+    p->cv = nullptr;
+    p->cv_src_a = p->cv_src_b = -1;
+    p->cv_rows_a = p->cv_rows_b = p->cv_len_a = p->cv_len_b = p->cv_ld_a = p->cv_ld_b = 0;
+    p->cv_off_b = p->cv_bytes = 0;
+    p->cv_dev = -1;
+    p->cv_ws = nullptr;
     if (skinny && fast->bn == 64) {
         // split K over workgroups until there is about one workgroup per CU, keeping at least
         // eight 32-deep chunks per wave
@@ -777,6 +898,8 @@ gemm_status_t gemm_plan_destroy(gemm_plan_t p) {
     if (p && p->pk_ws) (void)hipFree(p->pk_ws);
     if (p && p->cx_ws) (void)hipFree(p->cx_ws);
     if (p && p->cx) gemm_plan_destroy(p->cx);
+    if (p && p->cv_ws) (void)hipFree(p->cv_ws);
+    if (p && p->cv) gemm_plan_destroy(p->cv);
     delete p;
     return GEMM_STATUS_SUCCESS;
 }

@@ -86,6 +86,23 @@ struct RepackJob {
 int64_t repack_blocks(const RepackJob &j);
 hipError_t repack_launch(const RepackJob &a, const RepackJob &b, hipStream_t stream);
 
+// Type-converting copy (gemm_repack.hip): an operand stored as fp32 (src_type
+// CONVERT_FROM_F32, rounded to nearest even) or int8 (CONVERT_FROM_I8, exact) becomes fp16 (or
+// bf16 with to_bf16) rows.  Row r < rows of product b holds `elems` source elements at
+// src + b * src_stride + r * src_pitch (bytes, any alignment); it is written to
+// dst + b * dst_stride + r * dst_pitch (dst, dst_pitch and dst_stride multiples of 16;
+// dst_pitch >= 2 * elems), zero past the row's elements.  convert_launch converts a and b
+// (rows == 0: no job) in one launch; the caller keeps the total of convert_blocks below 2^31.
+enum ConvertSrc { CONVERT_FROM_F32 = 0, CONVERT_FROM_I8 = 1 };
+struct ConvertJob {
+    const uint8_t *src;
+    uint8_t *dst;
+    int64_t rows, elems, src_pitch, dst_pitch, src_stride, dst_stride, batch;
+    int src_type, to_bf16;
+};
+int64_t convert_blocks(const ConvertJob &j);
+hipError_t convert_launch(const ConvertJob &a, const ConvertJob &b, hipStream_t stream);
+
 // Complex / dual operands with fp16 parts rewritten as real fp16 matrices for the real kernels
 // (gemm_repack.hip).  Source row r of product b holds `numbers` numbers (4 bytes each: real
 // part low, other part high) at src + b * src_stride + r * src_pitch; it becomes destination

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gemm_internal.h"
 
@@ -146,6 +148,98 @@ uint32_t pair_job_blocks(const PairJob &j) {
     return (uint32_t)(cblk * rblk * j.batch);
 }
 
+// ---- type-converting copies ------------------------------------------------------------------
+// An operand stored as fp32 or int8 whose load transform converts it to the 16-bit input type
+// ("Flexible Performant GEMM Kernels on GPUs", section 4: a transform applied to every element
+// after it is loaded, such as a type conversion) is converted here, once per run, into 16-bit
+// rows that are 16-byte aligned and zero-padded to whole chunks; the product then reads the
+// converted rows like any other operand.  fp32 -> fp16 / bf16 rounds to nearest even; int8
+// converts exactly.  A thread writes one 16-byte chunk (8 elements) of a destination row,
+// reading the 8 source elements it holds (32 bytes of fp32 or 8 bytes of int8; elements past the
+// row read as 0); a wave covers 64 consecutive chunks of one row, a workgroup 4 rows.
+
+template <int SRC, bool BF>
+__device__ __forceinline__ void convert_block(const ConvertJob &j, uint32_t blk, int wave, int lane) {
+    constexpr int SB = SRC == CONVERT_FROM_F32 ? 4 : 1;          // source element bytes
+    const uint32_t cblk = (uint32_t)((j.dst_pitch / 16 + RP_CHUNKS - 1) / RP_CHUNKS);
+    const uint32_t rblk = (uint32_t)((j.rows + RP_ROWS - 1) / RP_ROWS);
+    const uint32_t prod = blk / (cblk * rblk);
+    const uint32_t rem = blk - prod * cblk * rblk;
+    const uint32_t rb = rem / cblk, cb = rem - rb * cblk;
+    const int64_t r = (int64_t)rb * RP_ROWS + wave;
+    const int64_t c = (int64_t)cb * RP_CHUNKS + lane;
+    if (r >= j.rows || c * 16 >= j.dst_pitch) return;
+    const uint8_t *s = j.src + (int64_t)prod * j.src_stride + r * j.src_pitch + c * 8 * SB;
+    const int64_t left = j.elems - c * 8;                          // source elements from here
+    float x[8];
+    if constexpr (SRC == CONVERT_FROM_F32) {
+        u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+        if (left >= 8) {
+            lo = ldg16(s);
+            hi = ldg16(s + 16);
+        } else if (left > 0) {
+            lo = ldg16_partial<4>(s, (int)(left < 4 ? left : 4));
+            if (left > 4) hi = ldg16_partial<4>(s + 16, (int)(left - 4));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = __builtin_bit_cast(float, (uint32_t)lo[e]);
+            x[e + 4] = __builtin_bit_cast(float, (uint32_t)hi[e]);
+        }
+    } else {
+        uint8_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (left >= 8) {
+            __builtin_memcpy(b, s, 8);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e < left) b[e] = s[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)b[e];
+    }
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    using T = typename std::conditional<BF, __bf16, _Float16>::type;
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // two-at-a-time conversion, round to nearest even
+        const t2 h = __builtin_convertvector((f32x2){x[2 * e], x[2 * e + 1]}, t2);
+        out[e] = __builtin_bit_cast(uint32_t, h);
+    }
+    *reinterpret_cast<u32x4 *>(j.dst + (int64_t)prod * j.dst_stride + r * j.dst_pitch + c * 16) = out;
+}
+
+uint32_t convert_job_blocks(const ConvertJob &j) {
+    if (j.rows <= 0 || j.batch <= 0) return 0;
+    const int64_t cblk = (j.dst_pitch / 16 + RP_CHUNKS - 1) / RP_CHUNKS;
+    const int64_t rblk = (j.rows + RP_ROWS - 1) / RP_ROWS;
+    return (uint32_t)(cblk * rblk * j.batch);
+}
+
+template <int SRC, bool BF>
+__device__ __forceinline__ void convert_one(const ConvertJob &j, uint32_t blk, int wave, int lane) {
+    convert_block<SRC, BF>(j, blk, wave, lane);
+}
+
+__device__ __forceinline__ void convert_dispatch(const ConvertJob &j, uint32_t blk, int wave, int lane) {
+    // uniform per job
+    if (j.src_type == CONVERT_FROM_F32) {
+        if (j.to_bf16) convert_one<CONVERT_FROM_F32, true>(j, blk, wave, lane);
+        else convert_one<CONVERT_FROM_F32, false>(j, blk, wave, lane);
+    } else {
+        if (j.to_bf16) convert_one<CONVERT_FROM_I8, true>(j, blk, wave, lane);
+        else convert_one<CONVERT_FROM_I8, false>(j, blk, wave, lane);
+    }
+}
+
+__global__ __launch_bounds__(RP_ROWS * 64) void convert_rows(ConvertJob a, ConvertJob b, uint32_t blocks_a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (blockIdx.x < blocks_a) convert_dispatch(a, blockIdx.x, wave, lane);
+    else convert_dispatch(b, blockIdx.x - blocks_a, wave, lane);
+}
+
 // ---- the K split's finishing step for int8 products ---------------------------------------------
 // D[m][n] = ReLU?(sum of the S int32 partial sums [split][M][N] in ws, in split order,
 // + beta * C (beta 0 or 1) + bias[n]); int32 arithmetic wraps exactly as the unsplit sum does.
@@ -204,6 +298,15 @@ hipError_t pair_launch(const PairJob &a, const PairJob &b, hipStream_t stream) {
     const uint32_t na = pair_job_blocks(a), nb = pair_job_blocks(b);
     if (na + nb == 0) return hipSuccess;
     hipLaunchKernelGGL(pair_rows, dim3(na + nb), dim3(RP_ROWS * 64), 0, stream, a, b, na);
+    return hipGetLastError();
+}
+
+int64_t convert_blocks(const ConvertJob &j) { return convert_job_blocks(j); }
+
+hipError_t convert_launch(const ConvertJob &a, const ConvertJob &b, hipStream_t stream) {
+    const uint32_t na = convert_job_blocks(a), nb = convert_job_blocks(b);
+    if (na + nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(convert_rows, dim3(na + nb), dim3(RP_ROWS * 64), 0, stream, a, b, na);
     return hipGetLastError();
 }
 
