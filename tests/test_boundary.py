@@ -21,7 +21,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == set(tge.EXPORTED)
-    lib = ctypes.CDLL(tge.LIB_PATH)
+    lib = tge.lib()
     for n in names:
         assert hasattr(lib, n), n
 
@@ -72,7 +72,7 @@ def test_supported_pairs_and_describe(ab, cd, lay):
 
 
 def test_null_out_pointer():
-    lib = ctypes.CDLL(tge.LIB_PATH)
+    lib = tge.lib()
     lib.gemm_plan_create.restype = ctypes.c_int
     st = lib.gemm_plan_create(None, ctypes.c_int64(1), ctypes.c_int64(1), ctypes.c_int64(1), 0, 0,
                               ctypes.c_int64(1), ctypes.c_int64(1), ctypes.c_int64(1), 1, 1, 0)
@@ -192,7 +192,7 @@ def test_desc_validation_and_transforms_described():
         st, h = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, "f16", "f16", "none",
                                           **bad)
         assert st == tge.STATUS_INVALID_VALUE and h is None
-    lib = ctypes.CDLL(tge.LIB_PATH)
+    lib = tge.lib()
     lib.gemm_plan_create_desc.restype = ctypes.c_int
     out = ctypes.c_void_p()
     assert lib.gemm_plan_create_desc(ctypes.byref(out), None) == tge.STATUS_INVALID_VALUE
@@ -375,3 +375,14 @@ def test_conversion_plans_validate():
         ab, cd = a.pop("ab_type"), a.pop("cd_type")
         got = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, ab, cd, "none", **a)
         assert got[0] == st and got[1] is None, (kw, got)
+
+
+def test_short_products_split_only_from_eight_slabs():
+    # four slabs of K (fp16 K = 256, int8 K = 512) stay on the general kernel, which measured
+    # faster there; eight and more split
+    for shape, ab in [((16, 256, 256), "f16"), ((64, 8192, 256), "f16"), ((64, 8192, 512), "i8")]:
+        d = tge.Plan(*shape, "T", "N", ab=ab, cd="i32" if ab == "i8" else "f16").describe()
+        assert "ksplit" not in d, d
+    for shape, ab in [((32, 1024, 1024), "f16"), ((16, 4096, 1024), "i8"), ((64, 1024, 512), "f16")]:
+        d = tge.Plan(*shape, "T", "N", ab=ab, cd="i32" if ab == "i8" else "f16").describe()
+        assert "gemm_fast_256x256 " in d and " ksplit " in d, d

@@ -664,7 +664,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // from 64 slabs, slower at 2048^3 (32 slabs).  Short products the skinny kernel cannot take
     // (M <= 64 with int8 inputs, or with A transposed) split down to chunks of 2 slabs: their
     // partial sums are small, and the split measured 1.1-6x faster than the general kernel
-    // (int8 16 x 4096 x 4096: 97 -> 17 us; fp16 TN: 135 -> 28 us)
+    // (int8 16 x 4096 x 4096: 97 -> 17 us; fp16 TN: 135 -> 28 us), from 8 slabs of K
     // (GEMM_ALGO_SPLIT: any S >= 2, chunks of one slab or more; GEMM_ALGO_NOSPLIT: never).
     int split_s = 0;
     const bool force_split = algo == GEMM_ALGO_SPLIT;
@@ -681,7 +681,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         const int64_t min_chunk = force_split ? 1 : short_i8 ? 2 : 16;
         if (sp > slabs / min_chunk) sp = slabs / min_chunk;
         while (sp > 1 && slabs % sp) --sp;
-        const bool worth = force_split || short_i8 || (tiles * sp >= 128 && slabs >= 64);
+        // short products split only from 8 slabs of K: with 4 slabs the two chunks and the
+        // finishing kernel measured slower than the general kernel (fp16 64 x 8192 x 256 TN
+        // 21.8 vs 8.3 us, int8 64 x 8192 x 512 NT 16.8 vs 5.8 us); from 8 slabs faster (fp16
+        // 32 x 1024 x 1024 TN 18.2 vs 34.9 us, int8 16 x 4096 x 1024 13.5 vs 26.4 us)
+        const bool worth = force_split || (short_i8 && slabs >= 8) || (tiles * sp >= 128 && slabs >= 64);
         if (sp >= 2 && worth && fast_table(ab_type, part_cd) && finish_table(ab_type, cd_type))
             split_s = (int)sp;
     }
