@@ -10,6 +10,7 @@ of the same workload on this host's cores.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME[:IDX]] [--no-cpu]
                   [--no-graph]
   python bench.py --calibrate-copy     (plain 1 GiB device copies, for scaling HBM counters)
+  python bench.py --calibrate-read     (read-only 1 GiB reductions, the same for FETCH_SIZE)
 
 The K timed launches are captured once into a HIP graph and replayed, so that a short kernel
 is timed without the host's per-call overhead (every launch still runs the full product);
@@ -121,6 +122,18 @@ def calibrate_copy():
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
+def calibrate_read():
+    """Read-only reductions of a 1 GiB buffer (each byte read once, a few bytes written): a second
+    reference for FETCH_SIZE, made of full-line reads like the GEMM kernels' loads."""
+    import torch
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.float16, device="cuda:0")
+    for _ in range(5):
+        x.sum(dtype=torch.float32)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "read", "bytes_read": 2 * n, "launches": 5}))
+
+
 def cpu_model():
     """The host CPU's model name, from /proc/cpuinfo."""
     try:
@@ -178,6 +191,8 @@ def main():
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 1 GiB copies (reference for the HBM byte counters)")
+    ap.add_argument("--calibrate-read", action="store_true",
+                    help="only run read-only reductions of 1 GiB (reference for FETCH_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -195,6 +210,9 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_read:
+        calibrate_read()
         return
 
     p = pick_workload(args.workload)
@@ -272,8 +290,8 @@ def main():
             walls.append((time.perf_counter() - w0) * 1e3 / max(1, args.steps))
             times.append(ev0.elapsed_time(ev1) / max(1, args.steps))
             last = np.array(times[-window:])
-            cv = float(last.std() / last.mean()) if len(last) == window else 1.0
-            if cv < 0.02 or len(times) >= args.max_blocks:
+            cv = float(last.std() / last.mean()) if len(last) >= 2 else 1.0
+            if (len(last) == window and cv < 0.02) or len(times) >= args.max_blocks:
                 break
         log(f"[bench] blocks of {args.steps} launches (ms/launch): "
             + " ".join(f"{t:.4f}" for t in times) + f"; last {len(last)}: CV {cv:.4f}")
