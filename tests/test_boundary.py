@@ -386,3 +386,14 @@ def test_short_products_split_only_from_eight_slabs():
     for shape, ab in [((32, 1024, 1024), "f16"), ((16, 4096, 1024), "i8"), ((64, 1024, 512), "f16")]:
         d = tge.Plan(*shape, "T", "N", ab=ab, cd="i32" if ab == "i8" else "f16").describe()
         assert "gemm_fast_256x256 " in d and " ksplit " in d, d
+
+
+def test_empty_skinny_shapes_plan_and_run_without_launch():
+    # found by the sanitizer build: an empty N (or batch) on a shape the skinny kernel takes
+    # divided by zero while choosing its K split
+    for kw in (dict(N=0, ldb=8, ldc=8), dict(N=4096, batch=0, stride_c=16 * 4096)):
+        a = dict(M=16, K=4096, op_a="N", op_b="N")
+        a.update(kw)
+        p = tge.Plan(**a)
+        assert tge.gemm_run(p.handle, None, None, None, None, None, 1.0, 0.0, None) == \
+            tge.STATUS_SUCCESS

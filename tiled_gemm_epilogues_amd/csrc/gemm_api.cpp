@@ -62,6 +62,19 @@ struct gemm_plan {
 
 namespace {
 
+// The integer held by an enum argument.  Callers across the C ABI may pass any int (C enums are
+// ints); reading an out-of-range value as the C++ enum type is undefined, so arguments are
+// checked through their bits before they are used as enums.
+template <class E>
+int enum_bits(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "C ABI enums are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+template <class E>
+void copy_enum(E &dst, const E &src) { memcpy(&dst, &src, sizeof dst); }
+
 const char *dtype_name(int t) {
     switch (t) {
     case GEMM_F32: return "f32";
@@ -457,7 +470,7 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
 extern "C" {
 
 const char *gemm_status_string(gemm_status_t s) {
-    switch (s) {
+    switch (enum_bits(s)) {
     case GEMM_STATUS_SUCCESS: return "GEMM_STATUS_SUCCESS";
     case GEMM_STATUS_INVALID_VALUE: return "GEMM_STATUS_INVALID_VALUE";
     case GEMM_STATUS_NOT_SUPPORTED: return "GEMM_STATUS_NOT_SUPPORTED";
@@ -468,23 +481,21 @@ const char *gemm_status_string(gemm_status_t s) {
     return "GEMM_STATUS_UNKNOWN";
 }
 
-gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K, gemm_op_t op_a,
-                               gemm_op_t op_b, int64_t lda, int64_t ldb, int64_t ldc,
-                               gemm_dtype_t ab_type, gemm_dtype_t cd_type, gemm_epilogue_t epi) {
-    return gemm_plan_create_batched(out, M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epi,
-                                    1, 0, 0, 0, 0);
-}
-
-gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, int64_t K,
-                                       gemm_op_t op_a, gemm_op_t op_b, int64_t lda, int64_t ldb,
-                                       int64_t ldc, gemm_dtype_t ab_type, gemm_dtype_t cd_type,
-                                       gemm_epilogue_t epi, int64_t batch, int64_t stride_a,
-                                       int64_t stride_b, int64_t stride_c, int64_t stride_bias) {
+// The description of gemm_plan_create(_batched)'s arguments; the enum arguments are taken by
+// reference and copied through their bits (they are checked by gemm_plan_create_desc).
+static gemm_status_t create_from_args(gemm_plan_t *out, int64_t M, int64_t N, int64_t K, const gemm_op_t &op_a,
+                                      const gemm_op_t &op_b, int64_t lda, int64_t ldb, int64_t ldc,
+                                      const gemm_dtype_t &ab_type, const gemm_dtype_t &cd_type,
+                                      const gemm_epilogue_t &epi, int64_t batch, int64_t stride_a,
+                                      int64_t stride_b, int64_t stride_c, int64_t stride_bias) {
     gemm_desc_t d;
     d.M = M; d.N = N; d.K = K;
-    d.op_a = op_a; d.op_b = op_b;
+    copy_enum(d.op_a, op_a);
+    copy_enum(d.op_b, op_b);
     d.lda = lda; d.ldb = ldb; d.ldc = ldc;
-    d.ab_type = ab_type; d.cd_type = cd_type; d.epilogue = epi;
+    copy_enum(d.ab_type, ab_type);
+    copy_enum(d.cd_type, cd_type);
+    copy_enum(d.epilogue, epi);
     d.batch = batch;
     d.stride_a = stride_a; d.stride_b = stride_b; d.stride_c = stride_c; d.stride_bias = stride_bias;
     d.transform_a = d.transform_b = d.transform_c = GEMM_TRANSFORM_NONE;
@@ -494,10 +505,39 @@ gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, i
     return gemm_plan_create_desc(out, &d);
 }
 
+gemm_status_t gemm_plan_create(gemm_plan_t *out, int64_t M, int64_t N, int64_t K, gemm_op_t op_a,
+                               gemm_op_t op_b, int64_t lda, int64_t ldb, int64_t ldc,
+                               gemm_dtype_t ab_type, gemm_dtype_t cd_type, gemm_epilogue_t epi) {
+    return create_from_args(out, M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epi, 1, 0, 0, 0, 0);
+}
+
+gemm_status_t gemm_plan_create_batched(gemm_plan_t *out, int64_t M, int64_t N, int64_t K,
+                                       gemm_op_t op_a, gemm_op_t op_b, int64_t lda, int64_t ldb,
+                                       int64_t ldc, gemm_dtype_t ab_type, gemm_dtype_t cd_type,
+                                       gemm_epilogue_t epi, int64_t batch, int64_t stride_a,
+                                       int64_t stride_b, int64_t stride_c, int64_t stride_bias) {
+    return create_from_args(out, M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epi, batch, stride_a,
+                            stride_b, stride_c, stride_bias);
+}
+
 gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (!out) return GEMM_STATUS_INVALID_VALUE;
     *out = nullptr;
     if (!desc) return GEMM_STATUS_INVALID_VALUE;
+    // every enum field in range (checked through its bits) before it is read as an enum
+    {
+        const auto in = [](int v, int lo, int hi) { return v >= lo && v <= hi; };
+        if (!in(enum_bits(desc->op_a), GEMM_OP_N, GEMM_OP_T) || !in(enum_bits(desc->op_b), GEMM_OP_N, GEMM_OP_T) ||
+            !in(enum_bits(desc->ab_type), GEMM_F32, GEMM_DF32) || !in(enum_bits(desc->cd_type), GEMM_F32, GEMM_DF32) ||
+            !in(enum_bits(desc->epilogue), GEMM_EPI_NONE, GEMM_EPI_BIAS_RELU) ||
+            !in(enum_bits(desc->transform_a), GEMM_TRANSFORM_NONE, GEMM_TRANSFORM_FROM_I8) ||
+            !in(enum_bits(desc->transform_b), GEMM_TRANSFORM_NONE, GEMM_TRANSFORM_FROM_I8) ||
+            !in(enum_bits(desc->transform_c), GEMM_TRANSFORM_NONE, GEMM_TRANSFORM_RELU) ||
+            !in(enum_bits(desc->kind_a), GEMM_OPERAND_DENSE, GEMM_OPERAND_DIAGONAL) ||
+            !in(enum_bits(desc->kind_b), GEMM_OPERAND_DENSE, GEMM_OPERAND_DIAGONAL) ||
+            !in(enum_bits(desc->algo), GEMM_ALGO_AUTO, GEMM_ALGO_NOSPLIT))
+            return GEMM_STATUS_INVALID_VALUE;
+    }
     const int64_t M = desc->M, N = desc->N, K = desc->K;
     const gemm_op_t op_a = desc->op_a, op_b = desc->op_b;
     const int64_t lda = desc->lda, ldb = desc->ldb, ldc = desc->ldc;
@@ -840,7 +880,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->cv_off_b = p->cv_bytes = 0;
     p->cv_dev = -1;
     p->cv_ws = nullptr;
-    if (skinny && fast->bn == 64) {
+    // (an empty problem, N == 0 or a batch of 0, launches nothing and is never split)
+    if (skinny && fast->bn == 64 && N > 0 && batch > 0) {
         // split K over workgroups until there is about one workgroup per CU, keeping at least
         // eight 32-deep chunks per wave
         const int64_t blocks = ((N + 63) / 64) * (batch > 1 ? batch : 1);
