@@ -74,6 +74,11 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+def _raw_store(transform, ab, a):
+    """Flat raw storage of an operand in its stored type (the source type of a conversion)."""
+    return _raw(CONVERT_FROM.get(transform, ab), a)
+
+
 def _raw(dtype, a):
     a = np.ascontiguousarray(a)
     want = RAW_NP[dtype]
@@ -271,12 +276,30 @@ def gemm_pair(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None
 def gemm_batched(M, N, K, op_a, op_b, A, lda, B, ldb, ab, C=None, ldc=None, cd=None, bias=None,
                  bias_dt=None, alpha=1.0, beta=0.0, relu=False, batch=1, stride_a=0, stride_b=0,
                  stride_c=0, stride_bias=0, threads=None, transform_a="none", transform_b="none",
-                 transform_c="none", kind_a="dense", kind_b="dense"):
-    """Exact results (batch x M x N) of a strided batch: product b uses the stored operands
-    starting b * stride elements after those of product 0 (C and D share stride_c; a zero
-    stride shares the operand).  The logical-index-to-offset mapping of a batched operand is
-    the layout idea of "Flexible Performant GEMM Kernels on GPUs", section 4; each product is
-    the plain definition above."""
+                 transform_c="none", kind_a="dense", kind_b="dense", batch2=1, stride2_a=0,
+                 stride2_b=0, stride2_c=0, stride2_bias=0):
+    """Exact results of a strided batch: product b uses the stored operands starting b * stride
+    elements after those of product 0 (C and D share stride_c; a zero stride shares the
+    operand).  With batch2 > 1 the batch has two modes: product (b1, b2), b1 < batch,
+    b2 < batch2, starts b1 * stride + b2 * stride2 elements after product (0, 0), and the
+    result is batch x batch2 x M x N (a zero stride in one mode broadcasts the operand along
+    it).  The logical-index-to-offset mapping of a batched operand is the layout idea of
+    "Flexible Performant GEMM Kernels on GPUs", section 4 (tensor contractions computed as GEMMs
+    whose loads reorganise indices); each product is the plain definition above."""
+    if batch2 != 1:
+        out = [gemm_batched(M, N, K, op_a, op_b, _raw_store(transform_a, ab, A)[b2 * stride2_a:], lda,
+                            _raw_store(transform_b, ab, B)[b2 * stride2_b:], ldb, ab,
+                            C=_raw(cd, C)[b2 * stride2_c:] if (C is not None and beta != 0) else None,
+                            ldc=ldc, cd=cd,
+                            bias=_raw(bias_dt or ("i32" if is_int(ab) else "f32"), bias)[b2 * stride2_bias:]
+                            if bias is not None else None, bias_dt=bias_dt, alpha=alpha, beta=beta,
+                            relu=relu, batch=batch, stride_a=stride_a, stride_b=stride_b,
+                            stride_c=stride_c, stride_bias=stride_bias, threads=threads,
+                            transform_a=transform_a, transform_b=transform_b, transform_c=transform_c,
+                            kind_a=kind_a, kind_b=kind_b)
+               for b2 in range(batch2)]
+        return np.stack(out, axis=1) if batch2 > 0 else np.empty(
+            (batch, 0, M, N), np.int64 if is_int(ab) else np.float64)
     integer = is_int(ab)
     out = np.empty((batch, M, N), np.int64 if integer else np.float64)
     Ar = _raw(CONVERT_FROM.get(transform_a, ab), A)

@@ -95,6 +95,13 @@ class Problem:
     stride_b: int = -1
     stride_c: int = -1
     stride_bias: int = -1
+    # a second batch mode: product (b1, b2), b2 < batch2, at b1 * stride + b2 * stride2 (the
+    # strides of this mode are given explicitly; 0 broadcasts an operand along it)
+    batch2: int = 1
+    stride2_a: int = 0
+    stride2_b: int = 0
+    stride2_c: int = 0
+    stride2_bias: int = 0
 
     def __post_init__(self):
         if not self.lda:
@@ -202,7 +209,7 @@ def make_inputs(p: Problem, pad_fill=0):
     a shared operand is product 0's; gaps hold pad_fill).  Complex and dual numbers: both parts
     drawn from the operand's distribution (first parts, then second parts), stored interleaved
     as (rows, ld, 2) raw arrays of the part type."""
-    if p.batch != 1:
+    if p.batch != 1 or p.batch2 != 1:
         return _make_batched_inputs(p, pad_fill)
     if p.ab in PART:
         return _make_pair_inputs(p, pad_fill)
@@ -251,24 +258,31 @@ def _make_pair_inputs(p: Problem, pad_fill=0):
 
 
 def _make_batched_inputs(p: Problem, pad_fill=0):
+    """Flat arrays holding product (b1, b2) at b1 * stride + b2 * stride2 (one batch mode: b2 = 0);
+    product (b1, b2) is drawn with key (*key, 1000 + b1 * batch2 + b2), an operand shared along a
+    mode (stride 0) is written by the products at index 0 of that mode."""
     out = {"A": None, "B": None, "C": None, "bias": None}
     # strides count numbers: raw (part) elements per number for complex / dual types
     fa, fc = (2 if p.ab in PART else 1), (2 if p.cd in PART else 1)
-    strides = {"A": p.stride_a * fa, "B": p.stride_b * fa, "C": p.stride_c * fc,
-               "bias": p.stride_bias}
+    strides = {"A": (p.stride_a * fa, p.stride2_a * fa), "B": (p.stride_b * fa, p.stride2_b * fa),
+               "C": (p.stride_c * fc, p.stride2_c * fc), "bias": (p.stride_bias, p.stride2_bias)}
     dtypes = {"A": p.a_store, "B": p.b_store, "C": p.cd, "bias": p.bias_dt}
-    for b in range(max(p.batch, 0)):
-        one = make_inputs(replace(p, batch=1, key=(*p.key, 1000 + b)), pad_fill)
-        for name, arr in one.items():
-            if arr is None:
-                continue
-            flat = arr.reshape(-1)
-            st = strides[name]
-            if out[name] is None:
-                n = flat.size + (st * (p.batch - 1) if st > 0 else 0)
-                out[name] = np.full(n, pad_fill, dtype=RAW_NP[dtypes[name]])
-            if st > 0 or b == 0:
-                out[name][b * st: b * st + flat.size] = flat
+    nb1, nb2 = max(p.batch, 0), max(p.batch2, 0)
+    for b1 in range(nb1):
+        for b2 in range(nb2):
+            one = make_inputs(replace(p, batch=1, batch2=1, key=(*p.key, 1000 + b1 * nb2 + b2)),
+                              pad_fill)
+            for name, arr in one.items():
+                if arr is None:
+                    continue
+                flat = arr.reshape(-1)
+                s1, s2 = strides[name]
+                if out[name] is None:
+                    n = flat.size + (s1 * (nb1 - 1) if s1 > 0 else 0) + (s2 * (nb2 - 1) if s2 > 0 else 0)
+                    out[name] = np.full(n, pad_fill, dtype=RAW_NP[dtypes[name]])
+                if (s1 > 0 or b1 == 0) and (s2 > 0 or b2 == 0):
+                    o = b1 * s1 + b2 * s2
+                    out[name][o: o + flat.size] = flat
     return out
 
 

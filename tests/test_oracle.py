@@ -595,3 +595,71 @@ def _store_logical(X, op, pad):
     out = np.full((S.shape[0], S.shape[1] + pad), 99, dtype=X.dtype)
     out[:, : S.shape[1]] = S
     return out
+
+
+# ---- two batch modes -----------------------------------------------------------------------------
+
+def check_two_mode_pins(mod):
+    for lay in ("NN", "NT", "TN", "TT"):
+        _two_mode_case(mod, lay)
+
+
+@pytest.mark.parametrize("lay", ["NN", "NT", "TN", "TT"])
+def test_two_mode_batch_against_numpy_strided_views(lay):
+    """Product (b1, b2) of a two-mode batch uses the operands at b1 * stride + b2 * stride2:
+    checked against numpy's broadcasting matmul on 4-D as_strided views of the same flat buffers
+    (int8, exact in int64).  A varies with b1 only (broadcast along b2), B with b2 only, C, D
+    and the bias with both; padded leading dimensions and strides."""
+    _two_mode_case(oracle, lay)
+
+
+def _two_mode_case(oracle, lay):
+    g = np.random.default_rng(47)
+    st = np.lib.stride_tricks.as_strided
+    e = 8
+    for (M, N, K, b1, b2) in [(3, 5, 4, 2, 3), (1, 6, 3, 3, 2), (4, 2, 5, 1, 4), (2, 3, 2, 3, 1)]:
+        lda = (K if lay[0] == "N" else M) + 1
+        ldb = (N if lay[1] == "N" else K) + 2
+        ldc = N + 1
+        rows_a, rows_b = (M if lay[0] == "N" else K), (K if lay[1] == "N" else N)
+        sa, sa2 = rows_a * lda + 3, 0                  # A: moves with b1, shared along b2
+        sb, sb2 = 0, rows_b * ldb + 1                  # B: shared along b1, moves with b2
+        sc2 = M * ldc + 2
+        sc = b2 * sc2 + 5                              # D blocks laid out b1-major
+        sbias, sbias2 = 1, N + 2
+        A = g.integers(-3, 4, sa * b1 + 8).astype(np.int8)
+        B = g.integers(-3, 4, sb2 * b2 + 8).astype(np.int8)
+        C = g.integers(-5, 6, sc * b1 + 8).astype(np.int32)
+        bias = g.integers(-9, 10, sbias * b1 + sbias2 * b2 + N + 4).astype(np.int32)
+        got = oracle.gemm_batched(M, N, K, lay[0], lay[1], A, lda, B, ldb, "i8", C=C, ldc=ldc,
+                                  cd="i32", bias=bias, alpha=1, beta=1, relu=True, batch=b1,
+                                  stride_a=sa, stride_b=sb, stride_c=sc, stride_bias=sbias,
+                                  batch2=b2, stride2_a=sa2, stride2_b=sb2, stride2_c=sc2,
+                                  stride2_bias=sbias2)
+        A64, B64, C64, bb = (x.astype(np.int64) for x in (A, B, C, bias))
+        if lay[0] == "N":
+            Av = st(A64, (b1, b2, M, K), (sa * e, sa2 * e, lda * e, e))
+        else:
+            Av = st(A64, (b1, b2, K, M), (sa * e, sa2 * e, lda * e, e)).transpose(0, 1, 3, 2)
+        if lay[1] == "N":
+            Bv = st(B64, (b1, b2, K, N), (sb * e, sb2 * e, ldb * e, e))
+        else:
+            Bv = st(B64, (b1, b2, N, K), (sb * e, sb2 * e, ldb * e, e)).transpose(0, 1, 3, 2)
+        Cv = st(C64, (b1, b2, M, N), (sc * e, sc2 * e, ldc * e, e))
+        bv = st(bb, (b1, b2, 1, N), (sbias * e, sbias2 * e, 0, e))
+        ref = np.maximum(np.matmul(Av, Bv) + Cv + bv, 0)
+        assert got.size == b1 * b2 * M * N
+        assert np.array_equal(got.reshape(b1, b2, M, N), ref)
+
+
+def test_two_mode_batch_of_one_mode_is_the_strided_batch():
+    g = np.random.default_rng(48)
+    M, N, K = 5, 4, 3
+    A = g.integers(-3, 4, 4 * M * K).astype(np.int8)
+    B = g.integers(-3, 4, K * N).astype(np.int8)
+    one = oracle.gemm_batched(M, N, K, "N", "N", A, K, B, N, "i8", ldc=N, cd="i32", batch=4,
+                              stride_a=M * K, stride_c=M * N)
+    two = oracle.gemm_batched(M, N, K, "N", "N", A, K, B, N, "i8", ldc=N, cd="i32", batch=2,
+                              stride_a=2 * M * K, stride_c=2 * M * N, batch2=2, stride2_a=M * K,
+                              stride2_c=M * N)
+    assert np.array_equal(two.reshape(4, M, N), one)

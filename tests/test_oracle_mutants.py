@@ -114,3 +114,32 @@ def test_conversion_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
     spec.loader.exec_module(mod)
     with pytest.raises(AssertionError):
         check_conversion_pins(mod)
+
+
+# planted mistakes in the two-mode batch
+BATCH2_MUTANTS = {
+    "a_moves_with_b_stride": ("_raw_store(transform_a, ab, A)[b2 * stride2_a:]",
+                              "_raw_store(transform_a, ab, A)[b2 * stride2_b:]"),
+    "c_second_mode_dropped": ("C=_raw(cd, C)[b2 * stride2_c:]", "C=_raw(cd, C)[0:]"),
+    "modes_swapped_in_result": ("np.stack(out, axis=1)", "np.stack(out, axis=0)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BATCH2_MUTANTS))
+def test_two_mode_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
+    import importlib.util
+
+    import oracle
+    from test_oracle import check_two_mode_pins
+
+    old, new = BATCH2_MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert old in src, f"mutation anchor for {name} not found"
+    path = tmp_path / "oracle_mut.py"
+    path.write_text(src.replace(old, new))
+    monkeypatch.setenv("ORACLE_LIB", oracle._LIB_PATH)
+    spec = importlib.util.spec_from_file_location("oracle_mut", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with pytest.raises(AssertionError):
+        check_two_mode_pins(mod)
