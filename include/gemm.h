@@ -184,7 +184,16 @@ typedef struct gemm_plan *gemm_plan_t;
  * stride_a / stride_b moves its vector); algo pins the kernel route (see gemm_algo_t;
  * GEMM_ALGO_AUTO for the plan's own choice) and tile the workgroup tile of the general kernel
  * (256, 128 or 64; 0 for the plan's own choice; 256 also selects the fast kernel where it
- * applies).  Plain data: the library keeps no pointer to it.
+ * applies); batch2 and the stride2 fields add a second batch mode (0 or 1: none): the launch
+ * computes batch x batch2 products, product (b1, b2) reading and writing every operand moved by
+ * b1 * stride + b2 * stride2 elements (a zero stride broadcasts the operand along that mode),
+ * the index map of a tensor contraction whose batch index has two modes with their own
+ * strides ("Flexible Performant GEMM Kernels on GPUs", section 4: layouts that reorganise
+ * indices as they load).  The D's of all products must be disjoint: the mode with the smaller
+ * C/D stride has a stride of at least one D ((M-1)*ldc + N), the other at least that stride
+ * times the smaller mode's count.  Two-mode plans read their operands in place (no aligned
+ * copies, conversions or complex rewrites: a conversion returns NOT_SUPPORTED).  Plain data:
+ * the library keeps no pointer to it.
  */
 typedef struct {
     int64_t M, N, K;
@@ -198,6 +207,8 @@ typedef struct {
     gemm_operand_t kind_a, kind_b;
     gemm_algo_t algo;
     int32_t tile;
+    int64_t batch2;
+    int64_t stride2_a, stride2_b, stride2_c, stride2_bias;
 } gemm_desc_t;
 
 /*

@@ -125,7 +125,7 @@ def run_batched(p, x, offset=0):
     flat D storage (initialised with a sentinel, gaps between products included)."""
     A = to_dev(p.a_store, x["A"], offset)
     B = to_dev(p.b_store, x["B"], offset)
-    nD = max(p.batch - 1, 0) * p.stride_c + p.M * p.ldc
+    nD = max(p.batch - 1, 0) * p.stride_c + max(p.batch2 - 1, 0) * p.stride2_c + p.M * p.ldc
     D = to_dev(p.cd, np.full(nD, sentinel(p.cd), dtype=synth.RAW_NP[p.cd]), offset)
     C = to_dev(p.cd, x["C"], offset) if x["C"] is not None else None
     bias = to_dev(p.bias_dt, x["bias"], offset) if x["bias"] is not None else None
@@ -133,7 +133,9 @@ def run_batched(p, x, offset=0):
                   batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
                   stride_bias=p.stride_bias, transform_a=p.transform_a,
                   transform_b=p.transform_b, transform_c=p.transform_c, kind_a=p.kind_a,
-                  kind_b=p.kind_b, algo=FORCE["algo"], tile=FORCE["tile"])
+                  kind_b=p.kind_b, algo=FORCE["algo"], tile=FORCE["tile"], batch2=p.batch2,
+                  stride2_a=p.stride2_a, stride2_b=p.stride2_b, stride2_c=p.stride2_c,
+                  stride2_bias=p.stride2_bias)
     pl.run(A, B, C, D, bias, p.alpha, p.beta)
     torch.cuda.synchronize()
     return to_host(p.cd, D).reshape(-1), pl
@@ -146,4 +148,6 @@ def reference_batched(p, x):
                                stride_b=p.stride_b, stride_c=p.stride_c,
                                stride_bias=p.stride_bias, transform_a=p.transform_a,
                                transform_b=p.transform_b, transform_c=p.transform_c,
-                               kind_a=p.kind_a, kind_b=p.kind_b)
+                               kind_a=p.kind_a, kind_b=p.kind_b, batch2=p.batch2,
+                               stride2_a=p.stride2_a, stride2_b=p.stride2_b,
+                               stride2_c=p.stride2_c, stride2_bias=p.stride2_bias)

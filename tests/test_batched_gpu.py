@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from dataclasses import replace
-from gpu_helpers import FORCE, reference_batched, run_batched, sentinel
+from gpu_helpers import FORCE, check, reference_batched, run_batched, sentinel
 
 pytestmark = pytest.mark.gpu
 
@@ -115,3 +115,46 @@ def test_batch_of_zero_launches_nothing():
     pl.run(A, A, None, D)
     torch.cuda.synchronize()
     assert bool((D == 3.0).all())
+
+
+# ---- two batch modes ---------------------------------------------------------------------------
+
+# (M, N, K, layout, ab, cd, algo, kernel expected, batch, batch2, odd stride2 of A)
+TWO_MODE = [(520, 304, 320, "NN", "f16", "f16", "fast", "gemm_fast_256x256 ", 2, 3, False),
+            (304, 264, 200, "TN", "bf16", "f32", "fast", "gemm_fast_256x256 ", 3, 2, False),
+            (264, 520, 384, "NT", "i8", "i32", "fast", "gemm_fast_256x256 ", 2, 2, False),
+            (520, 300, 320, "NN", "f16", "f32", "fast", "gemm_fast_256x256_rs", 2, 2, True),
+            (150, 97, 70, "TT", "f16", "f16", "general", "gemm_mfma", 3, 2, True),
+            (16, 1024, 2048, "NN", "f16", "f16", "auto", "gemm_skinny", 2, 2, False),
+            (100, 60, 33, "NT", "f32", "f32", "auto", "gemm_mfma", 2, 3, False)]
+
+
+@pytest.mark.parametrize("case", range(len(TWO_MODE)))
+def test_two_mode_batch_exact(case, monkeypatch):
+    """Product (b1, b2) at b1 * stride + b2 * stride2: A moves with b1 only (broadcast along b2),
+    B with b2 only, C/D and the bias with both (D blocks b2-major), exact against the oracle on
+    every product."""
+    M, N, K, lay, ab, cd, algo, kern, b1, b2, odd = TWO_MODE[case]
+    monkeypatch.setitem(FORCE, "algo", algo)
+    rows_a = M if lay[0] == "N" else K
+    rows_b = K if lay[1] == "N" else N
+    base = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, "bias_relu",
+                                       1.0 if ab == "i8" else 2.0, 1.0 if ab == "i8" else -1.0,
+                                       key=(160, case))
+    if ab == "i8":
+        base = replace(base, alpha=1.0, beta=1.0)
+    sc = M * base.ldc + 24
+    p = replace(base, batch=b1, stride_a=rows_a * base.lda + (1 if odd else 0), stride_b=0,
+                stride_c=sc, stride_bias=N, batch2=b2, stride2_a=0,
+                stride2_b=rows_b * base.ldb + 16, stride2_c=b1 * sc + 40, stride2_bias=b1 * N)
+    x = synth.make_inputs(p)
+    Df, pl = run_batched(p, x)
+    d = pl.describe()
+    print(f"{p.label()} batch {b1}x{b2} -> {d}", flush=True)
+    assert kern in d and f"batch {b1}x{b2}" in d, d
+    ref = reference_batched(p, x).reshape(b1, b2, M, N)
+    for i in range(b1):
+        for j in range(b2):
+            o = i * p.stride_c + j * p.stride2_c
+            Db = Df[o: o + M * p.ldc].reshape(M, p.ldc)
+            check(p, x, Db, ref[i, j], exact=True)

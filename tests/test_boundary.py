@@ -397,3 +397,34 @@ def test_empty_skinny_shapes_plan_and_run_without_launch():
         p = tge.Plan(**a)
         assert tge.gemm_run(p.handle, None, None, None, None, None, 1.0, 0.0, None) == \
             tge.STATUS_SUCCESS
+
+
+def test_two_mode_batch_validation_and_description():
+    base = dict(M=64, N=64, K=64, op_a="N", op_b="N", lda=64, ldb=64, ldc=64, ab_type="f16",
+                cd_type="f16", epilogue="none", batch=2, stride_a=4096, stride_b=0,
+                stride_c=4096, stride_bias=0)
+    ok = tge.gemm_plan_create_desc(**base, batch2=3, stride2_a=0, stride2_b=4096,
+                                   stride2_c=2 * 4096)
+    assert ok[0] == tge.STATUS_SUCCESS and "batch 2x3" in tge.gemm_plan_describe(ok[1])[1]
+    tge.gemm_plan_destroy(ok[1])
+    # the D blocks of the two modes must nest without overlap; negative values are invalid
+    for kw in (dict(batch2=3, stride2_c=4096), dict(batch2=3, stride2_c=100),
+               dict(batch2=-1), dict(batch2=2, stride2_a=-1)):
+        st, h = tge.gemm_plan_create_desc(**base, **kw)
+        assert st == tge.STATUS_INVALID_VALUE and h is None, kw
+    # batch2 of 0 or 1 is a single mode; a conversion with two modes is not supported
+    for b2 in (0, 1):
+        st, h = tge.gemm_plan_create_desc(**base, batch2=b2, stride2_c=7)
+        assert st == tge.STATUS_SUCCESS and "batch 2 " in tge.gemm_plan_describe(h)[1] + " "
+        tge.gemm_plan_destroy(h)
+    st, h = tge.gemm_plan_create_desc(**base, batch2=2, stride2_c=8192, transform_a="from_f32")
+    assert st == tge.STATUS_NOT_SUPPORTED
+
+
+def test_two_mode_spans_in_the_binding():
+    p = tge.Plan(8, 16, 32, batch=2, stride_a=300, stride_c=200, batch2=3, stride2_a=0,
+                 stride2_b=600, stride2_c=500)
+    sp = p.spans()
+    assert sp["A"][0] == 300 + 7 * 32 + 32
+    assert sp["B"][0] == 31 * 16 + 16 + 2 * 600
+    assert sp["D"][0] == 200 + 2 * 500 + 7 * 16 + 16

@@ -48,7 +48,8 @@ class GemmDesc(ctypes.Structure):
                 ("epilogue", _ci), ("batch", _i64), ("stride_a", _i64), ("stride_b", _i64),
                 ("stride_c", _i64), ("stride_bias", _i64), ("transform_a", _ci),
                 ("transform_b", _ci), ("transform_c", _ci), ("kind_a", _ci), ("kind_b", _ci),
-                ("algo", _ci), ("tile", _ci)]
+                ("algo", _ci), ("tile", _ci), ("batch2", _i64), ("stride2_a", _i64),
+                ("stride2_b", _i64), ("stride2_c", _i64), ("stride2_bias", _i64)]
 
 
 _lib = None
@@ -122,13 +123,15 @@ def gemm_plan_create_batched(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_typ
 def gemm_plan_create_desc(M, N, K, op_a, op_b, lda, ldb, ldc, ab_type, cd_type, epilogue,
                           batch=1, stride_a=0, stride_b=0, stride_c=0, stride_bias=0,
                           transform_a="none", transform_b="none", transform_c="none",
-                          kind_a="dense", kind_b="dense", algo="auto", tile=0):
+                          kind_a="dense", kind_b="dense", algo="auto", tile=0, batch2=1,
+                          stride2_a=0, stride2_b=0, stride2_c=0, stride2_bias=0):
     """Returns (status, handle) of a plan built from a full gemm_desc_t."""
     d = GemmDesc(M, N, K, _enum(OP, op_a), _enum(OP, op_b), lda, ldb, ldc, _enum(DTYPE, ab_type),
                  _enum(DTYPE, cd_type), _enum(EPILOGUE, epilogue), batch, stride_a, stride_b,
                  stride_c, stride_bias, _enum(TRANSFORM, transform_a),
                  _enum(TRANSFORM, transform_b), _enum(TRANSFORM, transform_c),
-                 _enum(KIND, kind_a), _enum(KIND, kind_b), _enum(ALGO, algo), int(tile))
+                 _enum(KIND, kind_a), _enum(KIND, kind_b), _enum(ALGO, algo), int(tile),
+                 batch2, stride2_a, stride2_b, stride2_c, stride2_bias)
     h = _vp()
     st = lib().gemm_plan_create_desc(ctypes.byref(h), ctypes.byref(d))
     return st, h.value
@@ -183,7 +186,8 @@ class Plan:
     def __init__(self, M, N, K, op_a="N", op_b="N", lda=None, ldb=None, ldc=None, ab="f16",
                  cd="f16", epilogue="none", batch=1, stride_a=0, stride_b=0, stride_c=0,
                  stride_bias=0, transform_a="none", transform_b="none", transform_c="none",
-                 kind_a="dense", kind_b="dense", algo="auto", tile=0):
+                 kind_a="dense", kind_b="dense", algo="auto", tile=0, batch2=1, stride2_a=0,
+                 stride2_b=0, stride2_c=0, stride2_bias=0):
         self._h = None
         self.M, self.N, self.K = M, N, K
         self.op_a, self.op_b, self.ab, self.cd, self.epilogue = op_a, op_b, ab, cd, epilogue
@@ -195,13 +199,18 @@ class Plan:
         self.stride_bias = stride_bias
         self.kind_a, self.kind_b = kind_a, kind_b
         self.transform_a, self.transform_b = transform_a, transform_b
+        self.batch2 = batch2
+        self.stride2 = {"A": stride2_a, "B": stride2_b, "C": stride2_c, "D": stride2_c,
+                        "bias": stride2_bias}
         xf = (transform_a, transform_b, transform_c)
         if (any(_enum(TRANSFORM, t) for t in xf) or _enum(KIND, kind_a) or _enum(KIND, kind_b)
-                or _enum(ALGO, algo) or tile):
+                or _enum(ALGO, algo) or tile or batch2 != 1):
             st, h = gemm_plan_create_desc(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd,
                                           epilogue, batch, stride_a, stride_b, stride_c,
                                           stride_bias, *xf, kind_a=kind_a, kind_b=kind_b,
-                                          algo=algo, tile=tile)
+                                          algo=algo, tile=tile, batch2=batch2, stride2_a=stride2_a,
+                                          stride2_b=stride2_b, stride2_c=stride2_c,
+                                          stride2_bias=stride2_bias)
         elif batch == 1 and not (stride_a or stride_b or stride_c or stride_bias):
             st, h = gemm_plan_create(M, N, K, op_a, op_b, self.lda, self.ldb, self.ldc, ab, cd,
                                      epilogue)
@@ -240,7 +249,11 @@ class Plan:
             b = (_span(N, K, self.ldb) + more(self.stride_b) if N and K else 0, self.ldb)
         cd = (_span(M, N, self.ldc) + more(self.stride_c) if M and N else 0, self.ldc)
         bias = (N + more(self.stride_bias) if N else 0, None)
-        return {"A": a, "B": b, "C": cd, "D": cd, "bias": bias}
+        out = {"A": a, "B": b, "C": cd, "D": cd, "bias": bias}
+        if self.batch2 > 1:   # the second batch mode moves every operand by its stride2 too
+            out = {k: (n + (self.batch2 - 1) * self.stride2[k] if n else 0, ld)
+                   for k, (n, ld) in out.items()}
+        return out
 
     def dtype_of(self, what):
         """Stored element type of operand `what` ("A", "B", "C", "D" or "bias")."""

@@ -215,16 +215,22 @@ __device__ __forceinline__ int c_in_i(int c, int relu_in) { return (relu_in && c
 
 // Strided batch: workgroup id -> (product b, id inside the product, `per` ids per product); the
 // operand pointers of `p` are moved to product b.  Consecutive ids share a product, so the
-// XCD-contiguous id ranges of xcd_remap keep each product on few XCDs.
+// XCD-contiguous id ranges of xcd_remap keep each product on few XCDs.  With two batch modes
+// product b is (b1, b2) = (b / batch2, b % batch2), moved by b1 * stride + b2 * stride2: the
+// index map of a tensor contraction whose batch index has two modes with their own strides.
 template <int EAB, int ECD>
 __device__ __forceinline__ int select_batch(GemmParams &p, int id, int per) {
     const int b = __builtin_amdgcn_readfirstlane(id / per);   // uniform: keeps pointers scalar
     if (b > 0) {
-        p.A = static_cast<const uint8_t *>(p.A) + b * p.stride_a * EAB;
-        p.B = static_cast<const uint8_t *>(p.B) + b * p.stride_b * EAB;
-        if (p.C) p.C = static_cast<const uint8_t *>(p.C) + b * p.stride_c * ECD;
-        p.D = static_cast<uint8_t *>(p.D) + b * p.stride_c * ECD;
-        if (p.bias) p.bias = static_cast<const uint8_t *>(p.bias) + b * p.stride_bias * 4;
+        const int b1 = __builtin_amdgcn_readfirstlane(b / p.batch2);
+        const int b2 = b - b1 * p.batch2;
+        const int64_t oa = b1 * p.stride_a + b2 * p.stride2_a, ob = b1 * p.stride_b + b2 * p.stride2_b;
+        const int64_t oc = b1 * p.stride_c + b2 * p.stride2_c, obias = b1 * p.stride_bias + b2 * p.stride2_bias;
+        p.A = static_cast<const uint8_t *>(p.A) + oa * EAB;
+        p.B = static_cast<const uint8_t *>(p.B) + ob * EAB;
+        if (p.C) p.C = static_cast<const uint8_t *>(p.C) + oc * ECD;
+        p.D = static_cast<uint8_t *>(p.D) + oc * ECD;
+        if (p.bias) p.bias = static_cast<const uint8_t *>(p.bias) + obias * 4;
     }
     return __builtin_amdgcn_readfirstlane(id - b * per);
 }

@@ -18,6 +18,8 @@ using tge::KernelEntry;
 struct gemm_plan {
     int64_t M, N, K, lda, ldb, ldc;
     int64_t batch, stride_a, stride_b, stride_c, stride_bias;
+    // a second batch mode (1: none): product (b1, b2) at b1 * stride + b2 * stride2
+    int64_t batch2, stride2_a, stride2_b, stride2_c, stride2_bias;
     int xform_a, xform_b, xform_c;
     int op_a, op_b, ab, cd, epi;
     const KernelEntry *kernel;       // general kernel (always valid)
@@ -356,7 +358,10 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
     prm.has_bias = has_bias;
     prm.relu = relu;
     prm.group_m = p->group_m;
-    prm.batch = (int)p->batch;
+    prm.batch = (int)(p->batch * p->batch2);   // every product of both batch modes
+    prm.batch2 = (int)p->batch2;
+    prm.stride2_a = p->stride2_a; prm.stride2_b = p->stride2_b;
+    prm.stride2_c = p->stride2_c; prm.stride2_bias = p->stride2_bias;
     prm.xform_a = p->xform_a; prm.xform_b = p->xform_b; prm.xform_c = p->xform_c;
     prm.stride_a = p->stride_a; prm.stride_b = p->stride_b;
     prm.stride_c = p->stride_c; prm.stride_bias = p->stride_bias;
@@ -420,7 +425,8 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
     prm.tiles_n = (int)((p->N + k->bn - 1) / k->bn);
     prm.ws = nullptr;
     // split-K partial sums: batch * S * M * N floats (int32 for int8)
-    const size_t split_bytes = (size_t)(p->batch > 1 ? p->batch : 1) * p->ksplit * p->M * p->N * sizeof(float);
+    const size_t split_bytes = (size_t)(p->batch * p->batch2 > 1 ? p->batch * p->batch2 : 1) * p->ksplit * p->M * p->N *
+                               sizeof(float);
     // fast kernel with K split (needs its workspace; a first run inside a capture runs whole)
     void *spw = nullptr;
     if ((k == p->fast || k == p->fast_pk) && !sk && p->fast_part) {
@@ -433,6 +439,8 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
         GemmParams part = prm;
         part.K = kc;
         part.batch = S;
+        part.batch2 = 1;
+        part.stride2_a = part.stride2_b = part.stride2_c = part.stride2_bias = 0;
         // chunk offsets in the operands the kernel reads (the copies, when copied)
         part.stride_a = p->op_a == GEMM_OP_N ? kc : (int64_t)kc * prm.lda;
         part.stride_b = p->op_b == GEMM_OP_N ? (int64_t)kc * prm.ldb : kc;
@@ -462,7 +470,7 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
         prm.ws = static_cast<float *>(w);
     }
     if (dry) return GEMM_STATUS_SUCCESS;
-    const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * p->batch);
+    const unsigned grid = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * p->batch * p->batch2);
     hipError_t e = k->launch(prm, grid, hs);
     return e == hipSuccess ? GEMM_STATUS_SUCCESS : GEMM_STATUS_HIP_ERROR;
 }
@@ -502,6 +510,8 @@ static gemm_status_t create_from_args(gemm_plan_t *out, int64_t M, int64_t N, in
     d.kind_a = d.kind_b = GEMM_OPERAND_DENSE;
     d.algo = GEMM_ALGO_AUTO;
     d.tile = 0;
+    d.batch2 = 1;
+    d.stride2_a = d.stride2_b = d.stride2_c = d.stride2_bias = 0;
     return gemm_plan_create_desc(out, &d);
 }
 
@@ -546,6 +556,16 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const int64_t batch = desc->batch;
     int64_t stride_a = desc->stride_a, stride_b = desc->stride_b, stride_c = desc->stride_c,
             stride_bias = desc->stride_bias;
+    // second batch mode: 0 or 1 means none
+    if (desc->batch2 < 0 || desc->stride2_a < 0 || desc->stride2_b < 0 || desc->stride2_c < 0 ||
+        desc->stride2_bias < 0)
+        return GEMM_STATUS_INVALID_VALUE;
+    const int64_t batch2 = desc->batch2 > 1 ? desc->batch2 : 1;
+    int64_t stride2_a = desc->stride2_a, stride2_b = desc->stride2_b, stride2_c = desc->stride2_c,
+            stride2_bias = desc->stride2_bias;
+    if (batch2 <= 1) stride2_a = stride2_b = stride2_c = stride2_bias = 0;
+    // products of both modes
+    const int64_t nprod = batch * batch2;
     for (gemm_transform_t t : {desc->transform_a, desc->transform_b})
         if ((int)t < GEMM_TRANSFORM_NONE || (int)t > GEMM_TRANSFORM_FROM_I8) return GEMM_STATUS_INVALID_VALUE;
     // C has the type of D: no conversion on C
@@ -602,15 +622,33 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     int64_t sc = span_bytes(M, N, ldc, ecd);
     if (sa >= lim || sb >= lim || sc >= lim || lda >= lim || ldb >= lim || ldc >= lim)
         return GEMM_STATUS_NOT_SUPPORTED;
-    // products of a batch never write the same element of D
-    if (batch > 1 && M > 0 && N > 0 && stride_c < (M - 1) * ldc + N) return GEMM_STATUS_INVALID_VALUE;
+    // products of a batch never write the same element of D: with one mode, consecutive D's at
+    // least one D apart; with two, the modes nest (the smaller stride at least one D, the larger
+    // at least the whole run of the smaller mode)
+    const int64_t dspan = (M > 0 && N > 0) ? (M - 1) * ldc + N : 0;
+    if (batch > 1 && batch2 > 1 && dspan > 0) {
+        const bool in1 = stride_c <= stride2_c;   // mode 1 inner
+        const int64_t si = in1 ? stride_c : stride2_c, ni = in1 ? batch : batch2;
+        const int64_t so = in1 ? stride2_c : stride_c;
+        if (si < dspan || so / ni < si) return GEMM_STATUS_INVALID_VALUE;
+    } else if (batch > 1 && dspan > 0 && stride_c < dspan) {
+        return GEMM_STATUS_INVALID_VALUE;
+    } else if (batch2 > 1 && dspan > 0 && stride2_c < dspan) {
+        return GEMM_STATUS_INVALID_VALUE;
+    }
     if (batch <= 1) stride_a = stride_b = stride_c = stride_bias = 0;
     // the byte offset of the last product must fit in 63 bits
     const int64_t big = (int64_t)1 << 62;
-    if (batch > 1 && (stride_a > big / batch / 4 || stride_b > big / batch / 4 ||
-                      stride_c > big / batch / 4 || stride_bias > big / batch / 4))
+    if (batch > 1 && (stride_a > big / batch / 8 || stride_b > big / batch / 8 ||
+                      stride_c > big / batch / 8 || stride_bias > big / batch / 8))
         return GEMM_STATUS_NOT_SUPPORTED;
+    if (batch2 > 1 && (stride2_a > big / batch2 / 8 || stride2_b > big / batch2 / 8 ||
+                       stride2_c > big / batch2 / 8 || stride2_bias > big / batch2 / 8))
+        return GEMM_STATUS_NOT_SUPPORTED;
+    // the kernels index products with 32-bit ints
+    if (nprod >= ((int64_t)1 << 31)) return GEMM_STATUS_NOT_SUPPORTED;
 
+    if ((cva || cvb) && batch2 > 1) return GEMM_STATUS_NOT_SUPPORTED;
     if (cva || cvb) {
         // the product runs as a plan on the converted operands: 16-bit rows, pitch whole
         // 16-byte chunks, one converted copy per product (one for all when the stride is 0)
@@ -647,6 +685,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         p->M = M; p->N = N; p->K = K;
         p->lda = lda; p->ldb = ldb; p->ldc = ldc;
         p->batch = batch;
+        p->batch2 = 1;
         p->stride_a = stride_a; p->stride_b = stride_b; p->stride_c = stride_c; p->stride_bias = stride_bias;
         p->op_a = op_a; p->op_b = op_b; p->ab = ab_type; p->cd = cd_type; p->epi = epi;
         p->xform_a = desc->transform_a; p->xform_b = desc->transform_b; p->xform_c = desc->transform_c;
@@ -671,7 +710,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         return GEMM_STATUS_SUCCESS;
     }
 
-    int cfg = (diag_a || diag_b || ctable) ? tge::CFG_128 : choose_cfg(M, N, batch);
+    int cfg = (diag_a || diag_b || ctable) ? tge::CFG_128 : choose_cfg(M, N, nprod);
     // an explicit tile in the description pins the workgroup tile
     const int tile = desc->tile;
     if (tile == 256) cfg = tge::CFG_256;
@@ -689,7 +728,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const bool staged = algo == GEMM_ALGO_FAST_STAGED;
     // the fast kernel does ~3x the work per CU-round of the general 128x128 kernel: take it
     // when its rounds of 256x256 tiles cost less than 3x as many rounds of 128x128 tiles
-    const int64_t nb = batch > 1 ? batch : 1;
+    const int64_t nb = nprod > 1 ? nprod : 1;
     const int64_t r256 = (((M + 255) / 256) * ((N + 255) / 256) * nb + 255) / 256;
     const int64_t r128 = (((M + 127) / 128) * ((N + 127) / 128) * nb + 255) / 256;
     bool want_fast = cfg == tge::CFG_256 || (cfg == tge::CFG_128 && 4 * r256 <= 3 * r128);
@@ -710,7 +749,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const bool force_split = algo == GEMM_ALGO_SPLIT;
     const int64_t slab_k = 128 / elem_bytes(ab_type);   // K elements per slab of the fast kernel
     const int part_cd = ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32;
-    if ((ab_type == GEMM_F16 || ab_type == GEMM_BF16 || ab_type == GEMM_I8) && batch <= 1 &&
+    if ((ab_type == GEMM_F16 || ab_type == GEMM_BF16 || ab_type == GEMM_I8) && nprod <= 1 &&
         !ctable && !diag_a && !diag_b && !desc->transform_a && !desc->transform_b &&
         K % slab_k == 0 && !staged &&
         algo != GEMM_ALGO_NOSPLIT && algo != GEMM_ALGO_GENERAL && algo != GEMM_ALGO_SKINNY) {
@@ -733,7 +772,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (algo == GEMM_ALGO_GENERAL) want_fast = false;
     const int ve = 16 / eab;   // elements per 16-byte chunk
     // every product of a batch keeps the 16-byte alignment of product 0
-    const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0 && !diag_a && !diag_b;
+    const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0 &&
+                           (stride2_a * eab) % 16 == 0 && (stride2_b * eab) % 16 == 0 && !diag_a && !diag_b;
     if (ft && want_fast && K >= 128 / eab && (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 &&
         strides16 && (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0))
         fast = ft(op_a, op_b, 0);
@@ -750,7 +790,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const KernelEntry *fast_pk = nullptr;
     int pk_need = 0;
     int64_t pk_ld_a = 0, pk_ld_b = 0, pk_off_b = 0, pk_bytes = 0, pk_kpad = 0;
-    if (ft && want_fast && K >= 128 / eab && !diag_a && !diag_b && !staged) {
+    // (one batch mode only: the copies lay products out along one stride)
+    if (ft && want_fast && K >= 128 / eab && !diag_a && !diag_b && !staged && batch2 <= 1) {
         // the copies hold K rounded up to whole slabs, zero past K: when both operands are
         // copied the kernel runs on that K and needs no guarded tail slab
         const int64_t slab = 128 / eab;
@@ -795,7 +836,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         // workgroups and the 64-column ones would need a k split (no partial sums, no second
         // kernel).  Each narrow block reads as many bytes of A as of B, so larger M, or a
         // second round, measured slower than the split.
-        const int64_t nbk = batch > 1 ? batch : 1;
+        const int64_t nbk = nprod > 1 ? nprod : 1;
         const int64_t nblk = ((N + 15) / 16) * nbk;
         const bool narrow = op_b == GEMM_OP_T && M <= 16 && ((N + 63) / 64) * nbk < 256 &&
                             nblk >= 192 && nblk <= 256;
@@ -809,7 +850,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // 2 x 2 block (PairJob).  Elsewhere the complex kernel runs.
     gemm_plan *cx = nullptr;
     int64_t cx_ld_a = 0, cx_ld_b = 0, cx_off_b = 0, cx_bytes = 0;
-    if (ctable && M > 0 && N > 0 && K > 0 && algo != GEMM_ALGO_GENERAL) {
+    if (ctable && M > 0 && N > 0 && K > 0 && algo != GEMM_ALGO_GENERAL && batch2 <= 1) {
         gemm_desc_t r = *desc;
         r.N = 2 * N;
         r.K = 2 * K;
@@ -851,6 +892,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     }
     p->M = M; p->N = N; p->K = K;
     p->batch = batch;
+    p->batch2 = batch2;
+    p->stride2_a = stride2_a; p->stride2_b = stride2_b; p->stride2_c = stride2_c; p->stride2_bias = stride2_bias;
     p->xform_a = desc->transform_a; p->xform_b = desc->transform_b; p->xform_c = desc->transform_c;
     p->stride_a = stride_a; p->stride_b = stride_b; p->stride_c = stride_c; p->stride_bias = stride_bias;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
@@ -881,10 +924,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->cv_dev = -1;
     p->cv_ws = nullptr;
     // (an empty problem, N == 0 or a batch of 0, launches nothing and is never split)
-    if (skinny && fast->bn == 64 && N > 0 && batch > 0) {
+    if (skinny && fast->bn == 64 && N > 0 && nprod > 0) {
         // split K over workgroups until there is about one workgroup per CU, keeping at least
         // eight 32-deep chunks per wave
-        const int64_t blocks = ((N + 63) / 64) * (batch > 1 ? batch : 1);
+        const int64_t blocks = ((N + 63) / 64) * (nprod > 1 ? nprod : 1);
         int64_t sp = (256 + blocks - 1) / blocks;
         const int64_t most = K / 32 / 32;
         if (sp > most) sp = most;
@@ -908,7 +951,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->tiles_m = skinny ? p->ksplit : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
-    const int64_t grid = (int64_t)p->tiles_m * p->tiles_n * batch;
+    const int64_t grid = (int64_t)p->tiles_m * p->tiles_n * nprod;
     if (grid >= ((int64_t)1 << 31)) {
         if (cx) gemm_plan_destroy(cx);
         delete p;
@@ -917,7 +960,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->grid = (unsigned)grid;
     char bdesc[64] = "";
     int bl = 0;
-    if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
+    if (batch2 > 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lldx%lld", (long long)batch, (long long)batch2);
+    else if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
     if (p->ksplit > 1) bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " ksplit %d", p->ksplit);
     if (shows_pk)
         bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " repack %s%s", pk_shown & 1 ? "A" : "",

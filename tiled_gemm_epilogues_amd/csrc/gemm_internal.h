@@ -18,9 +18,13 @@ struct GemmParams {
     int group_m;             // tile rows per raster group
     // strided batch: the launch computes `batch` independent products; product b reads and
     // writes the operands moved by b * stride (in elements of each operand's own type; C and D
-    // share stride_c; a zero stride shares that operand between products)
+    // share stride_c; a zero stride shares that operand between products).  With a second batch
+    // mode (batch2 > 1) `batch` counts all products and product b = b1 * batch2 + b2 is moved by
+    // b1 * stride + b2 * stride2
     int batch;
     int64_t stride_a, stride_b, stride_c, stride_bias;
+    int batch2;
+    int64_t stride2_a, stride2_b, stride2_c, stride2_bias;
     // load transforms (1: zero every element whose sign bit is set) on op(A), op(B) and C
     int xform_a, xform_b, xform_c;
     // split-K workspace of the skinny kernel (partial sums of every k split); unused elsewhere
