@@ -237,14 +237,17 @@ def main():
     C = dev(p.cd, x["C"]) if x["C"] is not None else None
     bias = dev(p.bias_dt, x["bias"]) if x["bias"] is not None else None
     pair = p.cd in synth.PART          # complex / dual output: interleaved parts
-    D = torch.empty((max(p.batch - 1, 0) * p.stride_c + p.M * p.ldc) * (2 if pair else 1),
+    D = torch.empty((max(p.batch - 1, 0) * p.stride_c + max(p.batch2 - 1, 0) * p.stride2_c +
+                     p.M * p.ldc) * (2 if pair else 1),
                     dtype={"f16": torch.float16, "bf16": torch.bfloat16,
                            "f32": torch.float32, "i32": torch.int32}[synth.PART.get(p.cd, p.cd)],
                     device="cuda:0")
     plan = Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
                 batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b, stride_c=p.stride_c,
                 stride_bias=p.stride_bias, transform_a=p.transform_a, transform_b=p.transform_b,
-                transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b)
+                transform_c=p.transform_c, kind_a=p.kind_a, kind_b=p.kind_b, batch2=p.batch2,
+                stride2_a=p.stride2_a, stride2_b=p.stride2_b, stride2_c=p.stride2_c,
+                stride2_bias=p.stride2_bias)
     log(f"[bench] kernel: {plan.describe()}")
 
     flops = p.flops
@@ -371,10 +374,11 @@ def main():
         rows = int((args.cpu_seconds - fixed) / per_row) // 32 * 32
         rows = max(r1, min(p.M, rows))
         t_cpu, ref = oracle_rows(rows)
-        sample_flops = p.flops * rows / p.M / max(p.batch, 1)
+        sample_flops = p.flops * rows / p.M / max(p.batch * p.batch2, 1)
         cpu = {"value": round(sample_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
-               "sample": f"output rows 0..{rows - 1} of {p.M}{' of product 0' if p.batch != 1 else ''} "
+               "sample": f"output rows 0..{rows - 1} of {p.M}"
+                         f"{' of product 0' if p.batch * p.batch2 != 1 else ''} "
                          f"(all {p.N} columns, full K={p.K}): "
                          f"{sample_flops:.3e} flop in {t_cpu:.1f}s, fp64/int64 accumulation"}
         log(f"[bench] cpu oracle: {cpu['sample']}")
@@ -408,6 +412,7 @@ def main():
         "dtype": p.ab,
         "data": "synthetic",
         "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+                   "batch2": p.batch2,
                    "transforms": [p.transform_a, p.transform_b, p.transform_c],
                    "kinds": [p.kind_a, p.kind_b],
                    "layout": p.op_a + p.op_b,

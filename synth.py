@@ -153,7 +153,7 @@ class Problem:
         """2 x the real multiply-adds the product needs: M*N*K, or for a diagonal operand only
         the non-zero terms (one per output element; with both diagonal, one per diagonal
         element); x4 for complex numbers (four real products), x3 for dual numbers."""
-        nb = max(self.batch, 0)
+        nb = max(self.batch, 0) * max(self.batch2, 0)
         if self.ab in ("cf16", "df16"):
             return (4.0 if self.ab == "cf16" else 3.0) * 2.0 * self.M * self.N * self.K * nb
         if self.kind_a == "diagonal" and self.kind_b == "diagonal":
@@ -172,20 +172,23 @@ class Problem:
         """Compulsory HBM traffic: op(A), op(B) read once, C if beta != 0, bias, D written once
         (per product; an operand shared by a batch is counted once)."""
         ea, eb, ec = ELEM_BYTES[self.a_store], ELEM_BYTES[self.b_store], ELEM_BYTES[self.cd]
-        nb = max(self.batch, 0)
-        per = lambda stride: nb if (nb <= 1 or stride != 0) else 1
+        b1, b2 = max(self.batch, 0), max(self.batch2, 0)
+        nb = b1 * b2
+        # distinct copies of an operand: a zero stride shares it along that batch mode
+        per = lambda s1, s2: (b1 if (b1 <= 1 or s1 != 0) else 1) * (b2 if (b2 <= 1 or s2 != 0) else 1)
         na = self.M if self.kind_a == "diagonal" else self.M * self.K
         nbb = self.N if self.kind_b == "diagonal" else self.K * self.N
-        b = na * per(self.stride_a) * ea + nbb * per(self.stride_b) * eb
+        b = na * per(self.stride_a, self.stride2_a) * ea + nbb * per(self.stride_b, self.stride2_b) * eb
         b += self.M * self.N * ec * nb
         if self.beta != 0:
             b += self.M * self.N * ec * nb
         if self.has_bias:
-            b += self.N * 4 * per(self.stride_bias)
+            b += self.N * 4 * per(self.stride_bias, self.stride2_bias)
         return b
 
     def label(self):
         bt = f":batch{self.batch}" if self.batch != 1 else ""
+        bt += f"x{self.batch2}" if self.batch2 != 1 else ""
         return (f"{self.name or 'gemm'}:{self.M}x{self.N}x{self.K}{bt}:{self.op_a}{self.op_b}:"
                 f"{self.ab}->{self.cd}:{self.epi}:a{self.alpha:g}b{self.beta:g}")
 
@@ -365,6 +368,20 @@ def batched_fp16():
                     batch=16)]
 
 
+def batched2_fp16():
+    """A two-mode batch (the index map of a tensor contraction whose batch index has two modes):
+    D[b1, b2] = ReLU(A[b1] B[b2] + bias[b1, b2]) for b1, b2 < 4, fp16 2048^3 products, A moving
+    with b1 only, B with b2 only (each broadcast along the other mode), D blocks b2-major;
+    A,B ~ N(0,1)/sqrt(K), bias ~ U[-0.5,0.5]."""
+    K = 2048
+    s = 1.0 / math.sqrt(K)
+    n = 2048 * 2048
+    return [Problem(2048, 2048, K, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                    a_dist=("normal", s), b_dist=("normal", s), key=(12, 0), name="batched2_fp16",
+                    batch=4, stride_a=n, stride_b=0, stride_c=n, stride_bias=2048,
+                    batch2=4, stride2_a=0, stride2_b=n, stride2_c=4 * n, stride2_bias=4 * 2048)]
+
+
 def fp16_8192_transforms():
     """The headline shape with the load transforms of "Flexible Performant GEMM Kernels on
     GPUs" section 5.3 (Table 2, bias + ReLU on C and D) plus a ReLU on A as it is loaded (an
@@ -420,6 +437,7 @@ WORKLOADS = {
     "int8_4096_bias": int8_4096_bias,
     "fc_layers": fc_layers,
     "batched_fp16": batched_fp16,
+    "batched2_fp16": batched2_fp16,
     "fp16_8192_transforms": fp16_8192_transforms,
     "diag_fp16": diag_fp16,
     "complex_fp16": complex_fp16,

@@ -142,6 +142,17 @@ def run_batched(p, x, offset=0):
 
 
 def reference_batched(p, x):
+    """Exact results of every product, (batch * batch2) x M x N, product b = b1 * batch2 + b2."""
+    return _reference_batched(p, x).reshape(-1, p.M, p.N)
+
+
+def batch_offset(p, b):
+    """Element offset of product b's C / D (b = b1 * batch2 + b2)."""
+    b1, b2 = divmod(b, max(p.batch2, 1))
+    return b1 * p.stride_c + b2 * p.stride2_c
+
+
+def _reference_batched(p, x):
     return oracle.gemm_batched(p.M, p.N, p.K, p.op_a, p.op_b, x["A"], p.lda, x["B"], p.ldb, p.ab,
                                C=x["C"], ldc=p.ldc, cd=p.cd, bias=x["bias"], alpha=p.alpha,
                                beta=p.beta, relu=p.relu, batch=p.batch, stride_a=p.stride_a,

@@ -152,7 +152,7 @@ def test_two_mode_batch_exact(case, monkeypatch):
     d = pl.describe()
     print(f"{p.label()} batch {b1}x{b2} -> {d}", flush=True)
     assert kern in d and f"batch {b1}x{b2}" in d, d
-    ref = reference_batched(p, x).reshape(b1, b2, M, N)
+    ref = reference_batched(p, x).reshape(b1, b2, M, N)   # product b1 * batch2 + b2
     for i in range(b1):
         for j in range(b2):
             o = i * p.stride_c + j * p.stride2_c

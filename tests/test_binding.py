@@ -90,11 +90,15 @@ def _stored_sizes(p):
     """Elements (numbers for complex / dual types) of the arrays synth.make_inputs stores for p,
     and of the D buffer the tests and the bench allocate."""
     more = lambda stride: stride * (p.batch - 1) if p.batch > 1 and stride > 0 else 0
+    more2 = lambda stride: stride * (p.batch2 - 1) if p.batch2 > 1 and stride > 0 else 0
     a = p.M if p.kind_a == "diagonal" else p.a_shape()[0] * p.lda
     b = p.N if p.kind_b == "diagonal" else p.b_shape()[0] * p.ldb
     c = p.M * p.ldc
-    return {"A": a + more(p.stride_a), "B": b + more(p.stride_b), "C": c + more(p.stride_c),
-            "D": c + max(p.batch - 1, 0) * p.stride_c, "bias": p.N + more(p.stride_bias)}
+    return {"A": a + more(p.stride_a) + more2(p.stride2_a),
+            "B": b + more(p.stride_b) + more2(p.stride2_b),
+            "C": c + more(p.stride_c) + more2(p.stride2_c),
+            "D": c + max(p.batch - 1, 0) * p.stride_c + max(p.batch2 - 1, 0) * p.stride2_c,
+            "bias": p.N + more(p.stride_bias) + more2(p.stride2_bias)}
 
 
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
@@ -106,7 +110,8 @@ def test_synthetic_inputs_fit_their_plans(name):
                         batch=p.batch, stride_a=p.stride_a, stride_b=p.stride_b,
                         stride_c=p.stride_c, stride_bias=p.stride_bias, transform_a=p.transform_a,
                         transform_b=p.transform_b, transform_c=p.transform_c, kind_a=p.kind_a,
-                        kind_b=p.kind_b)
+                        kind_b=p.kind_b, batch2=p.batch2, stride2_a=p.stride2_a,
+                        stride2_b=p.stride2_b, stride2_c=p.stride2_c, stride2_bias=p.stride2_bias)
         sizes = _stored_sizes(p)
         sp = plan.spans()
         for what in ("A", "B", "D"):

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import (FORCE, check, check_points, normaliser, reference, reference_batched, run,
+from gpu_helpers import (FORCE, batch_offset, check, check_points, normaliser, reference, reference_batched, run,
                          run_batched)
 
 pytestmark = pytest.mark.gpu
@@ -196,15 +196,16 @@ def test_workload_full_output(name, idx):
     p = synth.WORKLOADS[name]()[idx]
     x = synth.make_inputs(p)
     threads = _host_threads()
-    if p.batch != 1:
+    if p.batch != 1 or p.batch2 != 1:
         Df, pl = run_batched(p, x)
         print(f"{p.label()} -> {pl.describe()}", flush=True)
         ref = reference_batched(p, x)
         errs = []
-        for b in range(p.batch):
-            Db = Df[b * p.stride_c: b * p.stride_c + p.M * p.ldc].reshape(p.M, p.ldc)
+        for b in range(len(ref)):
+            o = batch_offset(p, b)
+            Db = Df[o: o + p.M * p.ldc].reshape(p.M, p.ldc)
             errs.append(check(p, x, Db, ref[b]))
-        print(f"[full] {p.label()}: products {p.batch} x rows {p.M} checked, max normalised "
+        print(f"[full] {p.label()}: products {len(ref)} x rows {p.M} checked, max normalised "
               f"error {max(errs):.3e}", flush=True)
         return
     D, pl = run(p, x)
