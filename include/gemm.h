@@ -161,7 +161,11 @@ typedef enum { GEMM_OPERAND_DENSE = 0, GEMM_OPERAND_DIAGONAL = 1 } gemm_operand_
  *   GENERAL      the general tiled kernel, never the fast, skinny or split routes;
  *   SKINNY       the memory-bound kernel for M <= 64 wherever its preconditions hold;
  *   SPLIT        the fast kernel with K split into any number >= 2 of whole-slab chunks;
- *   NOSPLIT      the plan's own choice without a K split.
+ *   NOSPLIT      the plan's own choice without a K split;
+ *   FAST_KMAJOR  as FAST, and with A stored transposed and B not, A is first copied transposed
+ *                into K-contiguous rows so that the kernel of the non-transposed layout runs
+ *                (GEMM_ALGO_AUTO makes that copy when the product is wide enough to repay it,
+ *                and always when A has to be copied anyway).
  */
 typedef enum {
     GEMM_ALGO_AUTO = 0,
@@ -170,7 +174,8 @@ typedef enum {
     GEMM_ALGO_GENERAL = 3,
     GEMM_ALGO_SKINNY = 4,
     GEMM_ALGO_SPLIT = 5,
-    GEMM_ALGO_NOSPLIT = 6
+    GEMM_ALGO_NOSPLIT = 6,
+    GEMM_ALGO_FAST_KMAJOR = 7
 } gemm_algo_t;
 
 typedef struct gemm_plan *gemm_plan_t;

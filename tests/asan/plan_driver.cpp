@@ -50,7 +50,7 @@ int main() {
                             d.transform_c = (gemm_transform_t)(v == 5 ? 1 : 0);
                             d.kind_a = (v == 7 && K == M) ? GEMM_OPERAND_DIAGONAL : GEMM_OPERAND_DENSE;
                             d.kind_b = GEMM_OPERAND_DENSE;
-                            d.algo = (gemm_algo_t)(v % 7);
+                            d.algo = (gemm_algo_t)(v % 8);
                             d.tile = v == 6 ? 128 : 0;
                             gemm_plan_t p = nullptr;
                             const gemm_status_t st = gemm_plan_create_desc(&p, &d);

@@ -129,7 +129,7 @@ def test_plans_ignore_the_environment(monkeypatch):
     assert tge.Plan(8192, 8192, 8192).describe() == base
 
 
-@pytest.mark.parametrize("kw", [dict(algo=7), dict(algo=-1), dict(tile=32), dict(tile=-256)])
+@pytest.mark.parametrize("kw", [dict(algo=8), dict(algo=-1), dict(tile=32), dict(tile=-256)])
 def test_invalid_algo_or_tile(kw):
     st, h = tge.gemm_plan_create_desc(64, 64, 64, "N", "N", 64, 64, 64, "f16", "f16", "none", **kw)
     assert st == tge.STATUS_INVALID_VALUE and h is None
@@ -260,13 +260,34 @@ def test_repack_only_what_the_direct_loads_cannot_read():
     # only the operand off the grid is copied: B with an odd ld; A with an M extent off the grid
     # when stored transposed; a K-contiguous operand's K tail needs no copy
     assert tge.Plan(4096, 4096, 4096, "N", "N", 4096, 4097, 4096).describe().endswith("repack B")
-    assert tge.Plan(4100, 4096, 4096, "T", "N").describe().endswith("repack A")
+    assert tge.Plan(4100, 4096, 4096, "T", "N").describe().endswith("repack A (A to K-major)")
     d = tge.Plan(4096, 4096, 4100, "N", "T", 4104, 4104, 4096).describe()
     assert "gemm_fast_256x256 " in d and "repack" not in d, d
     # a strided batch whose A stride breaks alignment copies A per product
     d = tge.Plan(2048, 2048, 2048, "N", "N", batch=4, stride_a=2048 * 2048 + 1,
                  stride_b=2048 * 2048, stride_c=2048 * 2048).describe()
     assert "repack A" in d and "batch 4" in d, d
+
+
+def test_kmajor_copy_of_a_transposed_a():
+    # A stored transposed and B not: A is copied into K-contiguous rows (and the kernel of the
+    # non-transposed layout runs) when N is wide enough to repay the copy, always with the
+    # kmajor algorithm, never with fast; the other layouts never copy for it
+    d = tge.Plan(5000, 5000, 5000, "T", "N", ab="bf16", cd="f32").describe()
+    assert "gemm_fast_256x256 " in d and d.endswith("repack A (A to K-major)"), d
+    d = tge.Plan(5000, 5000, 5000, "T", "N", ab="bf16", cd="f32", algo="fast").describe()
+    assert "gemm_fast_256x256 " in d and "repack" not in d, d
+    for n in (1024, 2048):
+        d = tge.Plan(4096, n, 4096, "T", "N").describe()
+        assert "repack" not in d, d
+    d = tge.Plan(1024, 1024, 1024, "T", "N", algo="kmajor").describe()
+    assert "gemm_fast_256x256 " in d and "(A to K-major)" in d, d
+    for lay in ("NN", "NT", "TT"):
+        d = tge.Plan(4096, 4096, 4096, lay[0], lay[1], algo="kmajor").describe()
+        assert "gemm_fast_256x256 " in d and "repack" not in d, d
+    # an A that has to be copied anyway (M off the 16-byte grid) is copied transposed
+    d = tge.Plan(4100, 1024, 4096, "T", "N", algo="fast").describe()
+    assert d.endswith("repack A (A to K-major)"), d
 
 
 def test_skinny_split_k_described():

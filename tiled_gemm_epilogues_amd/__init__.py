@@ -29,7 +29,8 @@ TRANSFORM = {"none": 0, "relu": 1, "from_f32": 2, "from_i8": 3}
 # stored element type of an operand whose load transform converts it to the input type
 STORED_BY_TRANSFORM = {"from_f32": "f32", "from_i8": "i8"}
 KIND = {"dense": 0, "diagonal": 1}
-ALGO = {"auto": 0, "fast": 1, "staged": 2, "general": 3, "skinny": 4, "split": 5, "nosplit": 6}
+ALGO = {"auto": 0, "fast": 1, "staged": 2, "general": 3, "skinny": 4, "split": 5, "nosplit": 6,
+        "kmajor": 7}
 (STATUS_SUCCESS, STATUS_INVALID_VALUE, STATUS_NOT_SUPPORTED, STATUS_HIP_ERROR,
  STATUS_ALLOC_FAILED, STATUS_SCRATCH_LIMIT) = range(6)
 # device scratch of gemm_run_noalloc (GEMM_NOALLOC_SCRATCH_BYTES in include/gemm.h)

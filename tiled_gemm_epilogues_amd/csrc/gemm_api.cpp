@@ -36,7 +36,13 @@ struct gemm_plan {
     // direct-load fast kernel on aligned copies of the operands it cannot read in place
     const KernelEntry *fast_pk;      // nullptr: no repacking for this plan
     int pk_need;                     // bit 0 / bit 1: A / B always copied (ld, stride or extent)
-    int64_t pk_ld_a, pk_ld_b;        // leading dimensions of the copies (whole 16-byte chunks)
+    int pk_want;                     // bit 0: A copied by choice although readable in place
+    // A stored transposed, B not: A's copies are transposed into K-contiguous rows and the
+    // kernels of the non-transposed layout run on them (the 16x16 schedule)
+    bool pk_tr;
+    const KernelEntry *fast_pk_tr;   // direct-load kernel on a transposed copy of A
+    const KernelEntry *fast_part_tr; // its K-split variant (nullptr: no split)
+    int64_t pk_ld_a, pk_ld_b;        // leading dimensions of the copies (whole 128-byte lines)
     int64_t pk_kpad;                 // K rounded up to whole slabs: the copies are zero there
     int64_t pk_off_b, pk_bytes;      // byte offset of B's copy in the workspace, total size
     int pk_dev;                      // device of the copy workspace (-1: none yet)
@@ -243,6 +249,18 @@ static gemm_status_t scratch_address(uint8_t **out) {
 
 // Scratch of gemm_run_noalloc: a bump allocator over the library's static device array (see
 // below).  dry: a sizing pass that takes regions and skips every launch and memory access.
+// Whether a transposed copy of A (stored transposed, B not) into K-contiguous rows repays its
+// cost when A could be read in place.  The copy moves 2 * M * K elements through HBM; the
+// kernel of the non-transposed layout saves up to ~10 % of the product's time, which grows with
+// N as well, so the copy pays from a wide enough N.  Measured (copy and product, graph-timed):
+// bf16 5000^3 284 -> 252 us, fp16 8192^3 827 -> 758 us, fp16 4096^3 114 -> 112 us, but fp16
+// 4096 x 2048 x 4096 85 -> 87 us and 8192 x 1536 x 8192 171 -> 231 us; int8 4096^3 no change.
+constexpr int64_t KMAJOR_MIN_N_BYTES = 6144;
+static bool kmajor_pays(int64_t M, int64_t N, int64_t K, int eab) {
+    (void)M; (void)K;
+    return N * eab >= KMAJOR_MIN_N_BYTES;
+}
+
 struct Scratch {
     uint8_t *base;
     size_t cap, used;
@@ -374,26 +392,48 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
     const int kk = p->K > 0 ? 3 : 0;
     const int unaligned = (p->pk_need | (((uintptr_t)A % 16) ? 1 : 0) | (((uintptr_t)B % 16) ? 2 : 0)) & kk;
     const int xf = ((p->xform_a ? 1 : 0) | (p->xform_b ? 2 : 0)) & kk;
-    const int need = unaligned | (p->fast_pk && !p->fast_is_skinny ? xf : 0);
+    int need = unaligned | (p->fast_pk && !p->fast_is_skinny ? xf : 0);
+    // A stored transposed (B not) is copied transposed, which reads A element by element: its
+    // pointer must be on the element grid (else that copy cannot be made)
+    const int eab = elem_bytes(p->ab);
+    const bool tr_ok = p->pk_tr && ((uintptr_t)A % eab) == 0;
+    if (p->fast_pk && tr_ok && (p->pk_want & kk & ~need)) {
+        // the copy made by choice, only where its workspace can be had (the scratch: if it fits)
+        bool fits = true;
+        if (sc) {
+            const size_t off = (sc->used + 255) & ~(size_t)255;
+            fits = off <= sc->cap && (size_t)p->pk_bytes <= sc->cap - off;
+        }
+        if (fits) need |= p->pk_want & kk;
+    }
+    const bool a_tr = p->pk_tr && (need & 1);
     void *pkw = nullptr;
-    if (!(p->fast && !need) && p->fast_pk && need) {
+    if (!(p->fast && !need) && p->fast_pk && need && (!a_tr || tr_ok)) {
         const gemm_status_t st = workspace(sc, &p->pk_ws, &p->pk_dev, (size_t)p->pk_bytes, hs, &pkw);
         if (sc && st != GEMM_STATUS_SUCCESS) return st;
     }
     if (p->fast && !need) k = p->fast;
     else if (pkw) {
-        const int eab = elem_bytes(p->ab);
         const bool sh_a = p->batch > 1 && p->stride_a, sh_b = p->batch > 1 && p->stride_b;
         tge::RepackJob ja = {}, jb = {};
         uint8_t *ws = static_cast<uint8_t *>(pkw);
         // stored rows of the copies: K-major operands get pk_kpad rows, the extra ones zero
-        if (need & 1) {
+        if (a_tr) {
+            // K source rows of M elements -> M rows of pk_kpad elements (zero past K)
+            ja = {static_cast<const uint8_t *>(A), ws, p->K, p->pk_kpad, p->M * eab, p->lda * eab,
+                  p->pk_ld_a * eab, p->stride_a * eab, p->M * p->pk_ld_a * eab, sh_a ? p->batch : 1,
+                  p->xform_a ? eab : 0, eab};
+            prm.xform_a = 0;
+            prm.A = ws;
+            prm.lda = (int)p->pk_ld_a;
+            prm.stride_a = sh_a ? p->M * p->pk_ld_a : 0;
+        } else if (need & 1) {
             const bool an = p->op_a == GEMM_OP_N;
             const int64_t rows = an ? p->M : p->K, rows_out = an ? p->M : p->pk_kpad;
             const int64_t len = an ? p->K : p->M;
             ja = {static_cast<const uint8_t *>(A), ws, rows, rows_out, len * eab, p->lda * eab,
                   p->pk_ld_a * eab, p->stride_a * eab, rows_out * p->pk_ld_a * eab, sh_a ? p->batch : 1,
-                  p->xform_a ? eab : 0};
+                  p->xform_a ? eab : 0, 0};
             prm.xform_a = 0;
             prm.A = ws;
             prm.lda = (int)p->pk_ld_a;
@@ -405,7 +445,7 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
             const int64_t len = bn ? p->N : p->K;
             jb = {static_cast<const uint8_t *>(B), ws + p->pk_off_b, rows, rows_out, len * eab,
                   p->ldb * eab, p->pk_ld_b * eab, p->stride_b * eab, rows_out * p->pk_ld_b * eab,
-                  sh_b ? p->batch : 1, p->xform_b ? eab : 0};
+                  sh_b ? p->batch : 1, p->xform_b ? eab : 0, 0};
             prm.xform_b = 0;
             prm.B = ws + p->pk_off_b;
             prm.ldb = (int)p->pk_ld_b;
@@ -414,7 +454,7 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
         if (!dry && tge::repack_launch(ja, jb, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
         // both operands from the copies: the products past K are 0 * 0, no tail slab
         if (need == 3) prm.K = (int)p->pk_kpad;
-        k = p->fast_pk;
+        k = a_tr ? p->fast_pk_tr : p->fast_pk;
     } else if (p->fast && !unaligned) {
         k = p->fast;              // no workspace: the direct loads with the transforms fused
     } else if (p->fast_rs) {
@@ -429,7 +469,8 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
                                sizeof(float);
     // fast kernel with K split (needs its workspace; a first run inside a capture runs whole)
     void *spw = nullptr;
-    if ((k == p->fast || k == p->fast_pk) && !sk && p->fast_part) {
+    const bool k_tr = p->fast_pk_tr && k == p->fast_pk_tr;   // A from its transposed copy
+    if ((k == p->fast || k == p->fast_pk || k_tr) && !sk && p->fast_part) {
         const gemm_status_t st = workspace(sc, reinterpret_cast<void **>(&p->ws), &p->ws_dev, split_bytes, hs, &spw);
         if (sc && st != GEMM_STATUS_SUCCESS) return st;
     }
@@ -442,7 +483,7 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
         part.batch2 = 1;
         part.stride2_a = part.stride2_b = part.stride2_c = part.stride2_bias = 0;
         // chunk offsets in the operands the kernel reads (the copies, when copied)
-        part.stride_a = p->op_a == GEMM_OP_N ? kc : (int64_t)kc * prm.lda;
+        part.stride_a = p->op_a == GEMM_OP_N || k_tr ? kc : (int64_t)kc * prm.lda;
         part.stride_b = p->op_b == GEMM_OP_N ? (int64_t)kc * prm.ldb : kc;
         part.C = nullptr;
         part.D = spw;
@@ -457,7 +498,8 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
         part.stride_c = p->M * p->N;
         part.stride_bias = 0;
         const unsigned g1 = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * S);
-        if (!dry && p->fast_part->launch(part, g1, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+        const KernelEntry *pk = k_tr ? p->fast_part_tr : p->fast_part;
+        if (!dry && pk->launch(part, g1, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
         GemmParams fin = prm;
         fin.tiles_m = S;
         fin.ws = static_cast<float *>(spw);
@@ -545,7 +587,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
             !in(enum_bits(desc->transform_c), GEMM_TRANSFORM_NONE, GEMM_TRANSFORM_RELU) ||
             !in(enum_bits(desc->kind_a), GEMM_OPERAND_DENSE, GEMM_OPERAND_DIAGONAL) ||
             !in(enum_bits(desc->kind_b), GEMM_OPERAND_DENSE, GEMM_OPERAND_DIAGONAL) ||
-            !in(enum_bits(desc->algo), GEMM_ALGO_AUTO, GEMM_ALGO_NOSPLIT))
+            !in(enum_bits(desc->algo), GEMM_ALGO_AUTO, GEMM_ALGO_FAST_KMAJOR))
             return GEMM_STATUS_INVALID_VALUE;
     }
     const int64_t M = desc->M, N = desc->N, K = desc->K;
@@ -577,7 +619,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const bool cva = converts(desc->transform_a), cvb = converts(desc->transform_b);
     for (gemm_operand_t k : {desc->kind_a, desc->kind_b})
         if ((int)k != GEMM_OPERAND_DENSE && (int)k != GEMM_OPERAND_DIAGONAL) return GEMM_STATUS_INVALID_VALUE;
-    if ((int)desc->algo < GEMM_ALGO_AUTO || (int)desc->algo > GEMM_ALGO_NOSPLIT) return GEMM_STATUS_INVALID_VALUE;
+    if ((int)desc->algo < GEMM_ALGO_AUTO || (int)desc->algo > GEMM_ALGO_FAST_KMAJOR) return GEMM_STATUS_INVALID_VALUE;
     if (desc->tile != 0 && desc->tile != 256 && desc->tile != 128 && desc->tile != 64)
         return GEMM_STATUS_INVALID_VALUE;
     const bool diag_a = desc->kind_a == GEMM_OPERAND_DIAGONAL;
@@ -651,10 +693,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if ((cva || cvb) && batch2 > 1) return GEMM_STATUS_NOT_SUPPORTED;
     if (cva || cvb) {
         // the product runs as a plan on the converted operands: 16-bit rows, pitch whole
-        // 16-byte chunks, one converted copy per product (one for all when the stride is 0)
+        // 128-byte lines, one converted copy per product (one for all when the stride is 0)
         const int64_t rows_a = op_a == GEMM_OP_N ? M : K, len_a = op_a == GEMM_OP_N ? K : M;
         const int64_t rows_b = op_b == GEMM_OP_N ? K : N, len_b = op_b == GEMM_OP_N ? N : K;
-        const int64_t ld_a = ((len_a > 1 ? len_a : 1) + 7) / 8 * 8, ld_b = ((len_b > 1 ? len_b : 1) + 7) / 8 * 8;
+        const int64_t ld_a = ((len_a > 1 ? len_a : 1) + 63) / 64 * 64, ld_b = ((len_b > 1 ? len_b : 1) + 63) / 64 * 64;
         const int64_t na = batch > 1 && stride_a ? batch : 1, nbb = batch > 1 && stride_b ? batch : 1;
         gemm_desc_t r = *desc;
         if (cva) {
@@ -733,7 +775,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const int64_t r128 = (((M + 127) / 128) * ((N + 127) / 128) * nb + 255) / 256;
     bool want_fast = cfg == tge::CFG_256 || (cfg == tge::CFG_128 && 4 * r256 <= 3 * r128);
     if (tile) want_fast = cfg == tge::CFG_256;
-    if (algo == GEMM_ALGO_FAST || staged) want_fast = true;
+    if (algo == GEMM_ALGO_FAST || algo == GEMM_ALGO_FAST_KMAJOR || staged) want_fast = true;
     // K split of the fast kernel: few 256x256 tiles and a long K (64 slabs or more: K >= 4096
     // for 16-bit inputs, 8192 for int8).  K is cut into S equal chunks of whole slabs (at least
     // 16 each) so that tiles x S workgroups fill the chip (at least 128); the chunks' partial
@@ -771,6 +813,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (split_s) want_fast = true;
     if (algo == GEMM_ALGO_GENERAL) want_fast = false;
     const int ve = 16 / eab;   // elements per 16-byte chunk
+    // elements per 128-byte line: the pitch of every copy the plan makes.  Rows that start off
+    // a line boundary cost the direct loads a second line per row and slab (~10 % of the loop
+    // time of a 5000-square product), so copies never have them
+    const int vl = 128 / eab;
     // every product of a batch keeps the 16-byte alignment of product 0
     const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0 &&
                            (stride2_a * eab) % 16 == 0 && (stride2_b * eab) % 16 == 0 && !diag_a && !diag_b;
@@ -785,10 +831,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         fast_rs = ft(op_a, op_b, 1);
 
     // repacking: operands the direct loads cannot read in place are copied into aligned rows
-    // padded to whole 16-byte chunks, then the direct-load kernel runs on the copies
+    // padded to whole 128-byte lines, then the direct-load kernel runs on the copies
     // (GEMM_ALGO_FAST_STAGED keeps the register-staged variant for such operands)
-    const KernelEntry *fast_pk = nullptr;
-    int pk_need = 0;
+    const KernelEntry *fast_pk = nullptr, *fast_pk_tr = nullptr;
+    int pk_need = 0, pk_want = 0;
+    bool pk_tr = false;
     int64_t pk_ld_a = 0, pk_ld_b = 0, pk_off_b = 0, pk_bytes = 0, pk_kpad = 0;
     // (one batch mode only: the copies lay products out along one stride)
     if (ft && want_fast && K >= 128 / eab && !diag_a && !diag_b && !staged && batch2 <= 1) {
@@ -796,10 +843,16 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         // copied the kernel runs on that K and needs no guarded tail slab
         const int64_t slab = 128 / eab;
         pk_kpad = (K + slab - 1) / slab * slab;
-        const int64_t rows_a = op_a == GEMM_OP_N ? M : pk_kpad, len_a = op_a == GEMM_OP_N ? pk_kpad : M;
+        // A stored transposed with B not is the one layout whose fast kernel reads both
+        // operands with transposing LDS reads, which leaves the 16x16 schedule short of
+        // registers (it runs the 32x32 one, 10-15 % slower).  A copy of A is then made
+        // transposed, into K-contiguous rows, and the kernel of the non-transposed layout runs
+        pk_tr = op_a == GEMM_OP_T && op_b == GEMM_OP_N && ft(GEMM_OP_N, op_b, 0) != nullptr;
+        const bool an = op_a == GEMM_OP_N || pk_tr;
+        const int64_t rows_a = an ? M : pk_kpad, len_a = an ? pk_kpad : M;
         const int64_t rows_b = op_b == GEMM_OP_N ? pk_kpad : N, len_b = op_b == GEMM_OP_N ? N : pk_kpad;
-        pk_ld_a = (len_a + ve - 1) / ve * ve;
-        pk_ld_b = (len_b + ve - 1) / ve * ve;
+        pk_ld_a = (len_a + vl - 1) / vl * vl;
+        pk_ld_b = (len_b + vl - 1) / vl * vl;
         // a batch stride of 0 shares the operand between products: one copy
         const int64_t na = batch > 1 && stride_a ? batch : 1, nbb = batch > 1 && stride_b ? batch : 1;
         const int64_t one_a = rows_a * pk_ld_a * eab, one_b = rows_b * pk_ld_b * eab;
@@ -809,6 +862,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         const bool need_b = (ldb * eab) % 16 != 0 || (stride_b * eab) % 16 != 0 ||
                             (op_b == GEMM_OP_N && N % ve != 0);
         pk_need = (need_a ? 1 : 0) | (need_b ? 2 : 0);
+        // an A that could be read in place is still copied, transposed, when the product is
+        // large enough to repay the copy (GEMM_ALGO_FAST_KMAJOR: always; GEMM_ALGO_FAST: never)
+        if (pk_tr && !need_a && (algo == GEMM_ALGO_FAST_KMAJOR ||
+                                 (algo == GEMM_ALGO_AUTO && kmajor_pays(M, N, K, eab))))
+            pk_want = 1;
         // the copies obey the 32-bit offset limit of the kernels; the copy grid (workgroups of
         // 4 rows x 1 KiB) fits 31 bits
         auto blocks = [&](int64_t rows, int64_t ld, int64_t n) {
@@ -818,8 +876,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
             pk_off_b = (na * one_a + 255) / 256 * 256;
             pk_bytes = pk_off_b + nbb * one_b;
             fast_pk = ft(op_a, op_b, 0);
+            if (pk_tr) fast_pk_tr = ft(GEMM_OP_N, op_b, 0);
         } else {
-            pk_need = 0;
+            pk_need = pk_want = 0;
+            pk_tr = false;
         }
     }
 
@@ -828,7 +888,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     SkinnyLookup st = skinny_table(ab_type, cd_type);
     bool want_skinny = M <= 64;
     if (algo == GEMM_ALGO_GENERAL) want_skinny = false;
-    if (algo == GEMM_ALGO_FAST || staged || force_split) want_skinny = false;
+    if (algo == GEMM_ALGO_FAST || algo == GEMM_ALGO_FAST_KMAJOR || staged || force_split) want_skinny = false;
     if (algo == GEMM_ALGO_SKINNY) want_skinny = true;
     if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % 32 == 0 &&
         (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && strides16 && (op_b == GEMM_OP_T || N % 8 == 0)) {
@@ -854,8 +914,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         gemm_desc_t r = *desc;
         r.N = 2 * N;
         r.K = 2 * K;
-        cx_ld_a = op_a == GEMM_OP_N ? 2 * lda : (M + 7) / 8 * 8;
-        cx_ld_b = op_b == GEMM_OP_N ? (2 * N + 7) / 8 * 8 : (2 * K + 7) / 8 * 8;
+        cx_ld_a = op_a == GEMM_OP_N ? 2 * lda : (M + 63) / 64 * 64;
+        cx_ld_b = op_b == GEMM_OP_N ? (2 * N + 63) / 64 * 64 : (2 * K + 63) / 64 * 64;
         const int64_t rows_b = op_b == GEMM_OP_N ? 2 * K : 2 * N;
         const int64_t na = batch > 1 && stride_a ? batch : 1, nbb = batch > 1 && stride_b ? batch : 1;
         r.lda = cx_ld_a;
@@ -904,6 +964,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->fast_rs = fast_rs;
     p->fast_pk = fast_pk;
     p->pk_need = pk_need;
+    p->pk_want = pk_want;
+    p->pk_tr = pk_tr;
+    p->fast_pk_tr = fast_pk_tr;
+    p->fast_part_tr = nullptr;
     p->pk_ld_a = pk_ld_a; p->pk_ld_b = pk_ld_b;
     p->pk_kpad = pk_kpad;
     p->pk_off_b = pk_off_b; p->pk_bytes = pk_bytes;
@@ -939,15 +1003,18 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->finish = nullptr;
     if (split_s && (fast || fast_pk) && !skinny) {
         p->fast_part = fast_table(ab_type, ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32)(op_a, op_b, 0);
+        if (pk_tr) p->fast_part_tr = fast_table(ab_type, ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32)(GEMM_OP_N, op_b, 0);
         p->finish = finish_table(ab_type, cd_type);
         p->ksplit = split_s;
     }
     // a plan that always copies an operand (off the 16-byte grid, or carrying a load transform
     // that the copy applies) shows the direct kernel on the copies
     // (a skinny plan applies its transforms in its own kernel)
-    const int pk_shown = fast_pk && !skinny ? (pk_need | (desc->transform_a ? 1 : 0) | (desc->transform_b ? 2 : 0)) : 0;
+    const int pk_shown = fast_pk && !skinny ? (pk_need | pk_want | (desc->transform_a ? 1 : 0) |
+                                               (desc->transform_b ? 2 : 0)) : 0;
     const bool shows_pk = pk_shown != 0;
-    const KernelEntry *shown = fast ? fast : shows_pk ? fast_pk : fast_rs ? fast_rs : k;
+    const bool shows_tr = pk_tr && (pk_shown & 1);
+    const KernelEntry *shown = shows_tr ? fast_pk_tr : fast ? fast : shows_pk ? fast_pk : fast_rs ? fast_rs : k;
     p->tiles_m = skinny ? p->ksplit : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
@@ -964,8 +1031,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     else if (batch != 1) bl = snprintf(bdesc, sizeof(bdesc), " batch %lld", (long long)batch);
     if (p->ksplit > 1) bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " ksplit %d", p->ksplit);
     if (shows_pk)
-        bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " repack %s%s", pk_shown & 1 ? "A" : "",
-                       pk_shown & 2 ? "B" : "");
+        bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " repack %s%s%s", pk_shown & 1 ? "A" : "",
+                       pk_shown & 2 ? "B" : "", shows_tr ? " (A to K-major)" : "");
     if (diag_a || diag_b)
         bl += snprintf(bdesc + bl, sizeof(bdesc) - bl, " diag %s%s", diag_a ? "A" : "", diag_b ? "B" : "");
     if (desc->transform_a || desc->transform_b || desc->transform_c)

@@ -81,11 +81,16 @@ const KernelEntry *fast_i8_i32(int op_a, int op_b, int rs);
 // the total of repack_blocks below 2^31.
 // With xf_elem = 1 or 2 the copy also applies the load transform GEMM_TRANSFORM_RELU to
 // elements of that many bytes (every element whose sign bit is set becomes +0).
+// tr_elem = 1 or 2 makes the copy transposing, for elements of that many bytes: the source's
+// `rows` rows (k) of row_bytes / tr_elem elements (m) become row_bytes / tr_elem destination
+// rows of rows_out elements each (k; zero for k >= rows), row m at dst + b * dst_stride +
+// m * dst_pitch; rows_out * tr_elem a multiple of 128, src_pitch a multiple of tr_elem.
 struct RepackJob {
     const uint8_t *src;
     uint8_t *dst;
     int64_t rows, rows_out, row_bytes, src_pitch, dst_pitch, src_stride, dst_stride, batch;
     int xf_elem;
+    int tr_elem;
 };
 int64_t repack_blocks(const RepackJob &j);
 hipError_t repack_launch(const RepackJob &a, const RepackJob &b, hipStream_t stream);

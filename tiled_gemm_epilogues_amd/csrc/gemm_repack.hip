@@ -66,15 +66,81 @@ __device__ __forceinline__ void repack_block(const RepackJob &j, uint32_t blk, i
     *reinterpret_cast<u32x4 *>(j.dst + (int64_t)prod * j.dst_stride + r * j.dst_pitch + c * 16) = v;
 }
 
+// ---- transposing copies ----------------------------------------------------------------------
+// An operand stored M/N-contiguous (A stored K x M) copied into K-contiguous rows, so that the
+// fast kernel runs the schedule of the other layout.  A workgroup moves one tile of TK source
+// rows (k) x TM elements (m), TK and TM both 128 bytes' worth of elements: the source rows are
+// read across the lanes (consecutive m, any alignment: one element per load), consecutive k are
+// packed into dwords of a row of LDS per m, and each destination row's 128-byte piece leaves as
+// eight 16-byte chunks.  Source rows k >= rows read as zeros, so the copy's K padding is zero.
+constexpr int TR_LINE = 128;                 // bytes of k (destination) and of m (source) per tile
+constexpr int TR_PITCH = TR_LINE + 16;       // LDS row pitch: 16-byte aligned rows, skewed banks
+constexpr int TR_LDS = 128 * TR_PITCH;       // TM <= 128 rows
+
+template <int EB>
+__device__ __forceinline__ void transpose_block(const RepackJob &j, uint32_t blk, int tid, uint8_t *tile) {
+    constexpr int TM = TR_LINE / EB;         // source elements (destination rows) per tile
+    constexpr int PER = 4 / EB;              // k values per dword
+    constexpr int GROUPS = 256 / TM;         // dword columns loaded at once
+    const int64_t M = j.row_bytes / EB;
+    const uint32_t kblk = (uint32_t)(j.rows_out * EB / TR_LINE);
+    const uint32_t mblk = (uint32_t)((M + TM - 1) / TM);
+    const uint32_t prod = blk / (kblk * mblk);
+    const uint32_t rem = blk - prod * kblk * mblk;
+    const uint32_t mb = rem / kblk, kb = rem - mb * kblk;
+    const int64_t m0 = (int64_t)mb * TM, k0 = (int64_t)kb * (TR_LINE / EB);
+    const uint8_t *src = j.src + (int64_t)prod * j.src_stride;
+    {
+        const int mi = tid % TM;
+        const int64_t m = m0 + mi;
+#pragma unroll 4
+        for (int kd = tid / TM; kd < TR_LINE / 4; kd += GROUPS) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int64_t k = k0 + kd * PER + e;
+                if (m < M && k < j.rows) {
+                    const uint8_t *q = src + k * j.src_pitch + m * EB;
+                    const uint32_t x = EB == 2 ? (uint32_t)*reinterpret_cast<const uint16_t *>(q) : (uint32_t)*q;
+                    w |= x << (8 * EB * e);
+                }
+            }
+            *reinterpret_cast<uint32_t *>(tile + mi * TR_PITCH + 4 * kd) = w;
+        }
+    }
+    __syncthreads();
+    uint8_t *dst = j.dst + (int64_t)prod * j.dst_stride + k0 * EB;
+#pragma unroll
+    for (int idx = tid; idx < TM * (TR_LINE / 16); idx += 256) {
+        const int mm = idx / (TR_LINE / 16), c = idx % (TR_LINE / 16);
+        if (m0 + mm >= M) continue;
+        u32x4 v = *reinterpret_cast<const u32x4 *>(tile + mm * TR_PITCH + 16 * c);
+        v = zero_negative<EB>(v, j.xf_elem != 0);
+        *reinterpret_cast<u32x4 *>(dst + (m0 + mm) * j.dst_pitch + 16 * c) = v;
+    }
+}
+
+__device__ __forceinline__ void copy_block(const RepackJob &j, uint32_t blk, int tid, uint8_t *tile) {
+    // uniform per job
+    if (j.tr_elem == 2) transpose_block<2>(j, blk, tid, tile);
+    else if (j.tr_elem == 1) transpose_block<1>(j, blk, tid, tile);
+    else repack_block(j, blk, __builtin_amdgcn_readfirstlane(tid >> 6), tid & 63);
+}
+
 // Grid: blocks_a workgroups for job a, then those of job b (none when b.rows_out == 0).
 __global__ __launch_bounds__(RP_ROWS * 64) void repack_rows(RepackJob a, RepackJob b, uint32_t blocks_a) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (blockIdx.x < blocks_a) repack_block(a, blockIdx.x, wave, lane);
-    else repack_block(b, blockIdx.x - blocks_a, wave, lane);
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TR_LDS];
+    if (blockIdx.x < blocks_a) copy_block(a, blockIdx.x, threadIdx.x, tile);
+    else copy_block(b, blockIdx.x - blocks_a, threadIdx.x, tile);
 }
 
 uint32_t job_blocks(const RepackJob &j) {
     if (j.rows_out <= 0 || j.batch <= 0) return 0;
+    if (j.tr_elem) {
+        const int64_t tm = TR_LINE / j.tr_elem;
+        const int64_t m = j.row_bytes / j.tr_elem;
+        return (uint32_t)((j.rows_out * j.tr_elem / TR_LINE) * ((m + tm - 1) / tm) * j.batch);
+    }
     const int64_t cblk = (j.dst_pitch / 16 + RP_CHUNKS - 1) / RP_CHUNKS;
     const int64_t rblk = (j.rows_out + RP_ROWS - 1) / RP_ROWS;
     return (uint32_t)(cblk * rblk * j.batch);
