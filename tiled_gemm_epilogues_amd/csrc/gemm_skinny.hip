@@ -124,26 +124,34 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     uint8_t *ring = smem + wave * DEPTH * SLOT;
     const uint32_t lring = lds_addr(ring);
 
-    // per-lane load offsets (bytes) inside one chunk, relative to the chunk's base pointer
+    // per-lane load offsets (bytes) inside one chunk, relative to the chunk's base pointer.  A
+    // lane's LDS destination is fixed (16 bytes at 16 * lane of the instruction's KiB), so the
+    // XOR swizzles that keep the fragment reads free of bank conflicts are applied by choosing
+    // which 16-byte piece of its row each lane fetches: a row of 64 B (A, a transposed B) keeps
+    // piece q at q ^ ((row / 4) % 4) of 4; a row of 128 B (B stored K x N) keeps piece q at
+    // q ^ (2 ((row / 2) % 2) + 4 ((row / 8) % 2)) of 8 (row: within the chunk).  Rows that share
+    // banks then hold the pieces one fragment read needs in different banks.
     uint32_t voffB[BCH], voffA[MT];
+    const int sw64 = (lane >> 4) & 3;                   // row lane/4: (row / 4) % 4
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
         if constexpr (BT) {
-            // B stored N x K: CB rows (n) of 64 B; instruction i -> rows 16i + lane/4, piece lane%4
+            // B stored N x K: CB rows (n) of 64 B; instruction i -> rows 16i + lane/4
             const int n = min(n0 + 16 * i + (lane >> 2), p.N - 1);
-            voffB[i] = (uint32_t)(n * p.ldb + (lane & 3) * 8) * 2u;
+            voffB[i] = (uint32_t)(n * p.ldb + ((lane & 3) ^ sw64) * 8) * 2u;
         } else {
             // B stored K x N: 32 rows (k) of 128 B (whole lines); instruction i -> rows 8i + lane/8,
-            // columns 8*(lane%8) .. +7 (columns past N read the last 8 valid ones: never stored)
-            const int col = min(n0 + 8 * (lane & 7), p.N - 8);
+            // 8 columns per piece (columns past N read the last 8 valid ones: never stored)
+            const int sw128 = (((lane >> 4) & 1) << 1) | ((i & 1) << 2);   // row 8i + lane/8
+            const int col = min(n0 + 8 * ((lane & 7) ^ sw128), p.N - 8);
             voffB[i] = (uint32_t)((8 * i + (lane >> 3)) * p.ldb + col) * 2u;
         }
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        // A rows 16t + lane/4 (clamped), 16 B piece lane%4 of the 64 B k chunk
+        // A rows 16t + lane/4 (clamped) of the 64 B k chunk
         const int m = min(16 * t + (lane >> 2), p.M - 1);
-        voffA[t] = (uint32_t)(m * p.lda + (lane & 3) * 8) * 2u;
+        voffA[t] = (uint32_t)(m * p.lda + ((lane & 3) ^ sw64) * 8) * 2u;
     }
     auto issue = [&](int c, int slot) {
         const int k0 = c * KCH;
@@ -156,12 +164,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     };
 
     // fragment read offsets inside a slot.  A chunk (16 rows x 64 B, row r at 64 r): lane l
-    // needs row l%16, k 8*(l/16) .. +7.  B, transposed layout: rows n at 64 B, column group g
-    // (16 columns) at 1024 g, same lane map as A.  B, K x N layout: rows k of 128 B, read with
-    // the transposing read: lane a of each 16-lane group addresses row a/4 (+ 8*(l/16) + 4h) and
-    // columns 16g + 4*(a%4) .. +3.
-    const uint32_t offA = (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16);
-    const uint32_t offB = BT ? offA : (uint32_t)((8 * (lane >> 4) + ((lane & 15) >> 2)) * 128 + (lane & 3) * 8);
+    // needs row l%16, k 8*(l/16) .. +7, i.e. piece l/16 (swizzled).  B, transposed layout: rows n
+    // at 64 B, column group g (16 columns) at 1024 g, same lane map as A.  B, K x N layout: rows
+    // k of 128 B, read with the transposing read: lane a of each 16-lane group addresses row
+    // r = a/4 + 8*(l/16) (+ 4h, which leaves the swizzle unchanged) and columns 16g + 4*(a%4)
+    // .. +3, i.e. 8 bytes of piece 2g + (a%4)/2 (swizzled).
+    const int ra = lane & 15;
+    const uint32_t offA = (uint32_t)(ra * 64 + (((lane >> 4) ^ ((ra >> 2) & 3)) * 16));
+    const int rb = 8 * (lane >> 4) + ((lane & 15) >> 2);
+    const int swb = (((rb >> 1) & 1) << 1) | (((rb >> 3) & 1) << 2);
+    uint32_t offB[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        offB[g] = BT ? offA + 1024u * g
+                     : (uint32_t)(rb * 128 + (((2 * g + ((lane & 3) >> 1)) ^ swb) * 16) + (lane & 1) * 8);
 
     f32x4 acc[MT][G];
 #pragma unroll
@@ -183,9 +199,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if constexpr (BT) {
-                bf[g] = *(const lds_u32x4 *)(uintptr_t)(sl + 1024u * g + offB);
+                bf[g] = *(const lds_u32x4 *)(uintptr_t)(sl + offB[g]);
             } else {
-                const uint32_t a = sl + offB + 32u * g;
+                const uint32_t a = sl + offB[g];
                 s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
                 s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(a + 4 * 128));
                 bf[g][0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
