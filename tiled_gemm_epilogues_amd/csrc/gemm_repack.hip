@@ -93,8 +93,10 @@ __device__ __forceinline__ void transpose_block(const RepackJob &j, uint32_t blk
     {
         const int mi = tid % TM;
         const int64_t m = m0 + mi;
-#pragma unroll 4
-        for (int kd = tid / TM; kd < TR_LINE / 4; kd += GROUPS) {
+        // every load of the tile is issued before the first LDS write waits for one
+#pragma unroll
+        for (int it = 0; it < TR_LINE / 4 / GROUPS; ++it) {
+            const int kd = tid / TM + it * GROUPS;
             uint32_t w = 0;
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
