@@ -296,6 +296,9 @@ def test_skinny_split_k_described():
     assert "ksplit 4" in tge.Plan(16, 4096, 4096, "N", "N").describe()
     assert "ksplit" not in tge.Plan(16, 4096, 512, "N", "N").describe()
     assert "ksplit" not in tge.Plan(16, 16384, 4096, "N", "N").describe()
+    # GEMM_ALGO_NOSPLIT keeps the skinny kernel and drops its split
+    d = tge.Plan(16, 4096, 4096, "N", "N", algo="nosplit").describe()
+    assert "gemm_skinny_m16 " in d and "ksplit" not in d, d
 
 
 def test_skinny_narrow_blocks_described():

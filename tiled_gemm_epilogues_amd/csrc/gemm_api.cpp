@@ -988,7 +988,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->cv_dev = -1;
     p->cv_ws = nullptr;
     // (an empty problem, N == 0 or a batch of 0, launches nothing and is never split)
-    if (skinny && fast->bn == 64 && N > 0 && nprod > 0) {
+    if (skinny && fast->bn == 64 && N > 0 && nprod > 0 && algo != GEMM_ALGO_NOSPLIT) {
         // split K over workgroups until there is about one workgroup per CU, keeping at least
         // eight 32-deep chunks per wave
         const int64_t blocks = ((N + 63) / 64) * (nprod > 1 ? nprod : 1);
