@@ -46,7 +46,10 @@
  * those operands into aligned, zero-padded rows of a workspace it owns (about the size of the
  * copied operands; the copy applies the transform), then runs the direct-load kernel on the
  * copies: two kernels per run ("repack A/B/AB" in the description when the plan itself calls
- * for the copy).  The workspace is allocated by the first run that needs it on a device (not
+ * for the copy).  With A stored transposed and B not, A's copy is made transposed, into
+ * K-contiguous rows ("(A to K-major)"), and it is also made for an A that could be read in
+ * place when the product is wide enough to repay it (see GEMM_ALGO_FAST_KMAJOR).  The
+ * workspace is allocated by the first run that needs it on a device (not
  * while the stream is captured: such a run reads the operands in place with a slower kernel,
  * same results) and freed by gemm_plan_destroy; runs of one such plan must not overlap in time.
  * Likewise a complex or dual plan large enough for the real fast kernel ("as real 2x2 blocks"
@@ -299,7 +302,9 @@ gemm_status_t gemm_run(gemm_plan_t plan, const void *A, const void *B, const voi
  * placed in a scratch array of GEMM_NOALLOC_SCRATCH_BYTES that the library holds on every
  * device it runs on (from the first call there until the process ends).  A run whose route
  * needs more than that returns GEMM_STATUS_SCRATCH_LIMIT before anything is enqueued.  Nothing
- * in the scratch needs to start at zero: every run writes the regions it reads.  All calls on a
+ * in the scratch needs to start at zero: every run writes the regions it reads.  A copy that a
+ * plan makes only by choice (the transposed copy of an A it could read in place) is skipped,
+ * reading A in place, when it does not fit beside the run's other regions.  All calls on a
  * device share its one array, so calls whose device work overlaps in time (other streams, or
  * host threads) race on it and give undefined results: serialise them on one stream.  The
  * plan itself is only read.  The first call on a device that needs scratch looks up the array's

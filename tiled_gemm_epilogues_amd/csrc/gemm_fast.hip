@@ -35,9 +35,10 @@
 //  * M/N edges: source rows past the edge are clamped to the last valid row (their products
 //    only reach output rows/columns that the masked epilogue drops); the K tail (K % slab) runs
 //    one guarded register-staged slab with zero fill.
-//  * MFMA shape: 16x16x32 (16x16x64 int8) for NN, NT and TT; 32x32 for TN, for the load
-//    transforms and for the register-staged variant, whose extra live registers the 16x16
-//    schedule cannot hold without shuffling accumulators.
+//  * MFMA shape: 16x16x32 (16x16x64 int8) for NN, NT and TT; 32x32 for TN read in place, for
+//    the load transforms and for the register-staged variant, whose extra live registers the
+//    16x16 schedule cannot hold without shuffling accumulators (the host copies a TN layout's
+//    A transposed, into K-contiguous rows, when that pays, and runs the NN kernel on it).
 //  * epilogue (the epilogue building block of "Flexible GEMM" section 4, fused as in the bias and
 //    ReLU functor of "CUTLASS", "Fusing Element-wise Operations"): alpha, beta*C, bias[j], ReLU
 //    and the conversion run on the accumulators; the result goes through a per-wave LDS staging
@@ -757,7 +758,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
 // as much accumulator data per multiply-add, which on this power-limited part keeps the clock
 // higher: ~10% more throughput at 8192^3 than the 32x32 shape.  With both operands M/N-
 // contiguous (A transposed, B not) the 16x16 schedule needs more registers than the allocator
-// finds without shuffling accumulators, so that layout keeps the 32x32 shape.
+// finds without shuffling accumulators, so that layout keeps the 32x32 shape when it is read in
+// place.
 template <bool AT, bool BT>
 constexpr int fast_mf() { return (AT && !BT) ? 32 : 16; }
 
