@@ -176,6 +176,65 @@ def pick_workload(spec):
     return probs[int(idx) if idx else 0]
 
 
+def vendor_context(p, A, B, bias, stream, args):
+    """torch.matmul (hipBLASLt on ROCm) on the same operands, for context: the product alone, and
+    the product with the bias add and ReLU as the separate kernels an unfused framework runs.
+    Same block timing as the library's launches (graphs of --steps launches).  Only for one
+    fp16/bf16 -> same-type product of tight row-major operands, not transposed."""
+    import torch
+    if not (p.batch == 1 and p.batch2 == 1 and p.op_a == "N" and p.op_b == "N" and p.ab == p.cd
+            and p.ab in ("f16", "bf16") and p.beta == 0 and p.lda == p.K and p.ldb == p.N
+            and p.ldc == p.N and p.kind_a == p.kind_b == "dense"
+            and (p.transform_a, p.transform_b, p.transform_c) == ("none", "none", "none")):
+        return {"note": "not timed: torch comparison only for dense NN fp16/bf16 products"}
+    tA = A[: p.M * p.K].view(p.M, p.K)
+    tB = B[: p.K * p.N].view(p.K, p.N)
+    out = torch.empty(p.M, p.N, dtype=tA.dtype, device=tA.device)
+    bias_t = bias.to(tA.dtype) if bias is not None else None
+    alpha = p.alpha
+
+    def plain():
+        torch.matmul(tA, tB, out=out)
+
+    def unfused():
+        if bias_t is not None:
+            torch.addmm(bias_t, tA, tB, alpha=alpha, out=out)
+        else:
+            torch.matmul(tA, tB, out=out)
+        if p.relu:
+            torch.relu_(out)
+
+    res = {}
+    for name, fn in (("matmul_ms", plain), ("matmul_bias_relu_ms", unfused)):
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(args.steps):
+                fn()
+        torch.cuda.synchronize()
+        times = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        while True:
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                graph.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / args.steps)
+            last = np.array(times[-5:])
+            if (len(last) == 5 and last.std() / last.mean() < 0.02) or len(times) >= args.max_blocks:
+                break
+        res[name] = round(float(np.median(last)), 5)
+        del graph
+    res["note"] = ("torch " + torch.__version__ + " on the same operands (hipBLASLt); bias and ReLU "
+                   "as separate kernels in the second figure; context only, not a parity reference")
+    log(f"[bench] vendor context: {res}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +248,9 @@ def main():
                     help="most timed blocks of --steps launches (fewer once they agree)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--vendor-context", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on the same operands, plain and with "
+                         "bias and ReLU as separate kernels (context only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 1 GiB copies (reference for the HBM byte counters)")
     ap.add_argument("--calibrate-read", action="store_true",
@@ -327,6 +389,8 @@ def main():
         del sets
     graph = None if args.no_graph else True
 
+    vendor = vendor_context(p, A, B, bias, stream, args) if args.vendor_context else None
+
     tflops = flops / (ms_events * 1e-3) / 1e12
     if hbm_bound:
         gbs = bytes_alg / (ms_events * 1e-3) / 1e9
@@ -427,6 +491,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    if vendor is not None:
+        out["vendor_context"] = vendor
     print(json.dumps(out), flush=True)
 
 
