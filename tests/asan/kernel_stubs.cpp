@@ -34,6 +34,10 @@ const KernelEntry *fast(int a, int b, int rs) {
     if (a < 0 || a > 1 || b < 0 || b > 1) return nullptr;
     return entry(256, 256, 64, rs ? "gemm_fast_256x256_rs" : "gemm_fast_256x256");
 }
+const KernelEntry *fast128(int a, int b) {
+    if (a < 0 || a > 1 || b < 0 || b > 1) return nullptr;
+    return entry(128, 128, 64, "gemm_fast_128x128");
+}
 const KernelEntry *skinny(int b, int mt, int narrow) {
     if (b < 0 || b > 1 || mt < 1 || mt > 4 || (narrow && b != 1)) return nullptr;
     return entry(16 * mt, narrow ? 16 : 64, 32, narrow ? "gemm_skinny_n16" : "gemm_skinny");
@@ -65,6 +69,10 @@ const KernelEntry *fast_f16_f32(int a, int b, int r) { return fast(a, b, r); }
 const KernelEntry *fast_bf16_bf16(int a, int b, int r) { return fast(a, b, r); }
 const KernelEntry *fast_bf16_f32(int a, int b, int r) { return fast(a, b, r); }
 const KernelEntry *fast_i8_i32(int a, int b, int r) { return fast(a, b, r); }
+const KernelEntry *fast128_f16_f16(int a, int b) { return fast128(a, b); }
+const KernelEntry *fast128_f16_f32(int a, int b) { return fast128(a, b); }
+const KernelEntry *fast128_bf16_bf16(int a, int b) { return fast128(a, b); }
+const KernelEntry *fast128_bf16_f32(int a, int b) { return fast128(a, b); }
 const KernelEntry *skinny_f16_f16(int b, int m, int n) { return skinny(b, m, n); }
 const KernelEntry *skinny_f16_f32(int b, int m, int n) { return skinny(b, m, n); }
 const KernelEntry *skinny_bf16_bf16(int b, int m, int n) { return skinny(b, m, n); }

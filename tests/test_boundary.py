@@ -290,6 +290,25 @@ def test_kmajor_copy_of_a_transposed_a():
     assert d.endswith("repack A (A to K-major)"), d
 
 
+def test_fast128_tiles_chosen_for_mid_size_products():
+    # 128x128 tiles of the fast kernel where 256x256 ones would leave half the CUs idle or more
+    # (16-bit inputs read in place, no load transforms); an explicit tile of 128 pins them
+    for (M, N, K) in [(1024, 1024, 1024), (2048, 2048, 2048), (4096, 2048, 2048), (1024, 4096, 1024)]:
+        assert tge.Plan(M, N, K).describe().startswith("gemm_fast_128x128 "), (M, N, K)
+    for (M, N, K) in [(3072, 3072, 3072), (4096, 4096, 4096), (512, 512, 512)]:
+        assert not tge.Plan(M, N, K).describe().startswith("gemm_fast_128x128 "), (M, N, K)
+    assert tge.Plan(2048, 2048, 2048, ab="bf16", cd="f32", op_a="T").describe().startswith("gemm_fast_128x128 ")
+    # not for int8, load transforms, operands off the 16-byte grid, or a long K that splits
+    assert "128x128" in tge.Plan(2048, 2048, 2048, ab="i8", cd="i32").describe()
+    assert not tge.Plan(2048, 2048, 2048, ab="i8", cd="i32").describe().startswith("gemm_fast_128x128 ")
+    assert not tge.Plan(2048, 2048, 2048, transform_a="relu").describe().startswith("gemm_fast_128x128 ")
+    assert not tge.Plan(2048, 2048, 2048, lda=2049).describe().startswith("gemm_fast_128x128 ")
+    assert " ksplit " in tge.Plan(2048, 2048, 8192).describe()
+    d = tge.Plan(3072, 3072, 3072, algo="fast", tile=128).describe()
+    assert d.startswith("gemm_fast_128x128 ") and "grid 576" in d, d
+    assert not tge.Plan(2048, 2048, 2048, algo="general").describe().startswith("gemm_fast")
+
+
 def test_skinny_split_k_described():
     # 64 column blocks fill a quarter of the chip: K is split 4 ways (8 chunks per wave); short K
     # is not split

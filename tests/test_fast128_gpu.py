@@ -1,0 +1,122 @@
+"""GPU parity of the fast kernel's 128x128-tile variant (mid-size 16-bit products, operands read
+in place): every layout and 16-bit type pair on ragged shapes (M and N off the tile, a K tail),
+the epilogue variants, batches of one and two modes, and the plan's own choice of the variant,
+against the oracle through the C ABI.  Exact-integer inputs make every comparison bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import tiled_gemm_epilogues_amd as tge
+from gpu_helpers import (FORCE, batch_offset, check, reference, reference_batched, run, run_batched,
+                         sentinel, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["NN", "NT", "TN", "TT"]
+PAIRS = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture
+def tile128(monkeypatch):
+    monkeypatch.setitem(FORCE, "algo", "fast")
+    monkeypatch.setitem(FORCE, "tile", 128)
+
+
+# (M, N, K, epilogue, alpha, beta, ld_pad): M and N multiples of 8 so that every layout can be
+# read in place; K tails of 8, 0 and 40 elements
+SHAPES = [((296, 264, 200), "bias_relu", 1.0, 0.0, 0),
+          ((1000, 776, 1024), "bias", 2.0, -1.0, 8),
+          ((128, 128, 64), "none", 1.0, 1.0, 0),
+          ((520, 392, 360), "relu", 0.5, 0.5, 16)]
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("pair", range(len(PAIRS)))
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_fast128_exact(shape, pair, lay, tile128):
+    (M, N, K), epi, alpha, beta, pad = SHAPES[shape]
+    ab, cd = PAIRS[pair]
+    p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta,
+                                    key=(170, shape * 16 + pair * 4 + LAYOUTS.index(lay)), ld_pad=pad)
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    d = pl.describe()
+    print(f"{p.label()} -> {d}", flush=True)
+    assert d.startswith("gemm_fast_128x128 "), d
+    check(p, x, D, reference(p, x), exact=True)
+
+
+def test_fast128_random_within_tolerance(tile128):
+    p = synth.Problem(1536, 1536, 1536, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                      a_dist=("normal", 1.0 / np.sqrt(1536)), b_dist=("normal", 1.0 / np.sqrt(1536)),
+                      key=(171, 0))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    assert pl.describe().startswith("gemm_fast_128x128 "), pl.describe()
+    err = check(p, x, D, reference(p, x, threads=16))
+    print(f"normalised error {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("modes", [1, 2])
+def test_fast128_batches(modes, tile128):
+    M, N, K = 264, 392, 256
+    if modes == 1:
+        p = synth.exact_integer_problem(M, N, K, "N", "T", "bf16", "f32", "bias", 1.0, 1.0,
+                                        key=(172, 0), batch=3, stride_a=M * K + 8, stride_b=0,
+                                        stride_c=M * N + 16, stride_bias=N)
+    else:
+        p = synth.exact_integer_problem(M, N, K, "T", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                                        key=(172, 1), batch=2, batch2=3, stride_a=K * M, stride_b=0,
+                                        stride2_a=0, stride2_b=K * N, stride_c=3 * M * N,
+                                        stride2_c=M * N, stride_bias=0, stride2_bias=N)
+    x = synth.make_inputs(p)
+    Df, pl = run_batched(p, x)
+    print(pl.describe(), flush=True)
+    assert pl.describe().startswith("gemm_fast_128x128 "), pl.describe()
+    ref = reference_batched(p, x)
+    for b in range(p.batch * p.batch2):
+        off = batch_offset(p, b)
+        Db = Df[off: off + p.M * p.ldc].reshape(p.M, p.ldc)
+        check(p, x, Db, ref[b], exact=True)
+
+
+def test_fast128_chosen_for_mid_size_products():
+    # the plan's own choice: 128-wide tiles where 256-wide ones would leave most CUs idle
+    for (M, N, K) in [(2048, 2048, 2048), (4096, 2048, 2048), (1536, 1536, 1536)]:
+        p = synth.exact_integer_problem(M, N, K, "N", "N", "f16", "f32", "bias_relu", 1.0, 0.0,
+                                        key=(173, M))
+        x = synth.make_inputs(p)
+        D, pl = run(p, x)
+        print(pl.describe(), flush=True)
+        assert pl.describe().startswith("gemm_fast_128x128 "), pl.describe()
+        check(p, x, D, reference(p, x, threads=16), exact=True)
+
+
+def test_fast128_noalloc_and_unaligned_pointer(tile128):
+    # no workspace: the no-allocation run is the same run; a pointer off 16 bytes at run time
+    # takes the 256-wide kernel on an aligned copy instead, with the same result
+    p = synth.exact_integer_problem(520, 264, 512, "N", "N", "f16", "f32", "bias", 1.0, 0.5,
+                                    key=(174, 0))
+    x = synth.make_inputs(p)
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi,
+                  algo="fast", tile=128)
+    assert pl.describe().startswith("gemm_fast_128x128 "), pl.describe()
+    A, B = to_dev(p.a_store, x["A"]), to_dev(p.b_store, x["B"])
+    C, bias = to_dev(p.cd, x["C"]), to_dev(p.bias_dt, x["bias"])
+    outs = []
+    for runner in (pl.run, pl.run_noalloc, pl.run_noalloc):
+        D = to_dev(p.cd, np.full(p.M * p.ldc, sentinel(p.cd), dtype=synth.RAW_NP[p.cd]))
+        runner(A, B, C, D, bias, p.alpha, p.beta)
+        torch.cuda.synchronize()
+        outs.append(to_host(p.cd, D).reshape(p.M, p.ldc))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    check(p, x, outs[0], reference(p, x), exact=True)
+    D2, _ = run(p, x, offset=1, plan=pl)
+    assert np.array_equal(D2, outs[0])

@@ -124,6 +124,16 @@ FastLookup fast_table(int ab, int cd) {
     return nullptr;
 }
 
+using Fast128Lookup = const KernelEntry *(*)(int, int);
+
+Fast128Lookup fast128_table(int ab, int cd) {
+    if (ab == GEMM_F16 && cd == GEMM_F16) return tge::fast128_f16_f16;
+    if (ab == GEMM_F16 && cd == GEMM_F32) return tge::fast128_f16_f32;
+    if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::fast128_bf16_bf16;
+    if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::fast128_bf16_f32;
+    return nullptr;
+}
+
 using SkinnyLookup = const KernelEntry *(*)(int, int, int);
 
 using FinishFn = hipError_t (*)(const GemmParams &, hipStream_t);
@@ -256,9 +266,23 @@ static gemm_status_t scratch_address(uint8_t **out) {
 // bf16 5000^3 284 -> 252 us, fp16 8192^3 827 -> 758 us, fp16 4096^3 114 -> 112 us, but fp16
 // 4096 x 2048 x 4096 85 -> 87 us and 8192 x 1536 x 8192 171 -> 231 us; int8 4096^3 no change.
 constexpr int64_t KMAJOR_MIN_N_BYTES = 6144;
+constexpr int64_t FAST128_MAX_T256 = 128;
+constexpr int64_t FAST128_MIN_T128 = 64;
 static bool kmajor_pays(int64_t M, int64_t N, int64_t K, int eab) {
     (void)M; (void)K;
     return N * eab >= KMAJOR_MIN_N_BYTES;
+}
+
+// Whether the 128x128 tiles of the fast kernel beat the 256x256 ones and the general kernel:
+// when the 256-wide tiles would leave at least half of the 256 CUs idle, and there are enough
+// 128-wide tiles to spread.  Measured (fp16 NN, graph-timed): 1024^3 general 18.0 us -> 9.9 us,
+// 1536^3 30.4 -> 18.6, 2048^3 fast 256 41.0 -> 25.5, 4096 x 2048 x 2048 42.8 -> 35.0,
+// 1024 x 4096 x 1024 25.0 -> 12.5; but 3072^3 (144 wide tiles) 58.6 -> 74.7.
+static bool fast128_pays(int64_t M, int64_t N, int64_t nprod) {
+    const int64_t nb = nprod > 1 ? nprod : 1;
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * nb;
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128) * nb;
+    return t256 <= FAST128_MAX_T256 && t128 >= FAST128_MIN_T128;
 }
 
 struct Scratch {
@@ -820,9 +844,21 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // every product of a batch keeps the 16-byte alignment of product 0
     const bool strides16 = (stride_a * eab) % 16 == 0 && (stride_b * eab) % 16 == 0 &&
                            (stride2_a * eab) % 16 == 0 && (stride2_b * eab) % 16 == 0 && !diag_a && !diag_b;
-    if (ft && want_fast && K >= 128 / eab && (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 &&
-        strides16 && (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0))
+    const bool direct_ok = K >= 128 / eab && (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 &&
+                           strides16 && (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0);
+    if (ft && want_fast && direct_ok)
         fast = ft(op_a, op_b, 0);
+    // 128x128 tiles of the fast kernel (16-bit inputs, operands read in place, no load
+    // transforms on op(A)/op(B)), for products whose 256x256 tiles would leave most CUs idle;
+    // an explicit tile of 128 with the fast or automatic algorithm pins it
+    const Fast128Lookup f128t = fast128_table(ab_type, cd_type);
+    const KernelEntry *fast128 = nullptr;
+    if (f128t && direct_ok && !desc->transform_a && !desc->transform_b && !diag_a && !diag_b && !ctable &&
+        algo != GEMM_ALGO_GENERAL && !split_s &&
+        ((tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST)) ||
+         (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod))))
+        fast128 = f128t(op_a, op_b);
+    if (fast128) fast = fast128;
     // the register-staged variant takes every layout the direct loads cannot (odd leading
     // dimensions or strides, unaligned pointers, M/N-contiguous extents off the 16-byte grid)
     const KernelEntry *fast_rs = nullptr;
@@ -864,8 +900,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         pk_need = (need_a ? 1 : 0) | (need_b ? 2 : 0);
         // an A that could be read in place is still copied, transposed, when the product is
         // large enough to repay the copy (GEMM_ALGO_FAST_KMAJOR: always; GEMM_ALGO_FAST: never)
+        // (the 128x128 tiles run the 16x16 schedule on this layout in place)
         if (pk_tr && !need_a && (algo == GEMM_ALGO_FAST_KMAJOR ||
-                                 (algo == GEMM_ALGO_AUTO && kmajor_pays(M, N, K, eab))))
+                                 (algo == GEMM_ALGO_AUTO && !fast128 && kmajor_pays(M, N, K, eab))))
             pk_want = 1;
         // the copies obey the 32-bit offset limit of the kernels; the copy grid (workgroups of
         // 4 rows x 1 KiB) fits 31 bits

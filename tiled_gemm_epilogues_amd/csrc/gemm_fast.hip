@@ -69,21 +69,28 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-constexpr int BM = 256, BN = 256;                    // output tile
 constexpr int SLAB_BYTES = 128;                      // K bytes per slab: 64 fp16/bf16 or 128 int8
 constexpr int NT = 256;                              // 4 waves
-constexpr int KC_BYTES = 256 * SLAB_BYTES;           // one operand slab: 32 KiB either layout
-// LDS map: [A stage 0 | A stage 1 | B stage 0 | B stage 1], 32 KiB each, so that every fragment
-// read is (base register) + (stage and k-slice offset as the instruction's 16-bit immediate)
-constexpr int OPND = 2 * KC_BYTES;                   // byte offset of operand B's stages
 
-// [mn][k] layout (K-contiguous operands): 256 rows of 128 B, 16-byte chunk c of row r at
+// Tile geometry: TL x TL output tile (256, or 128 for mid-size products), 4 waves of TL/2 x TL/2.
+// One operand slab is TL * 128 bytes in either layout (32 KiB at TL = 256).  LDS map: [A stage
+// 0 | A stage 1 | B stage 0 | B stage 1], so that every fragment read is (base register) +
+// (stage and k-slice offset as the instruction's 16-bit immediate).
+template <int TL>
+struct Geo {
+    static constexpr int KC = TL * SLAB_BYTES;       // bytes of one operand slab
+    static constexpr int OPND = 2 * KC;              // byte offset of operand B's stages
+    static constexpr int NL = KC / 1024 / 4;         // direct loads per wave, operand and slab
+    static constexpr int WT = TL / 2;                // wave tile
+};
+
+// [mn][k] layout (K-contiguous operands): TL rows of 128 B, 16-byte chunk c of row r at
 // c ^ swz_kc(r); identical in bytes for 8- and 16-bit elements.
 __device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int off_kc(int r, int c) { return r * 128 + ((c ^ swz_kc(r)) << 4); }
 
-// [k][mn] layout (M/N-contiguous operands): 64 rows of 512 B (16-bit) or 128 rows of 256 B
-// (8-bit).  A transposing read (8 bytes per lane) is served 32 lanes at a time; the 16 lanes of
+// [k][mn] layout (M/N-contiguous operands): 64 rows of TL 16-bit elements (512 B at TL = 256, 256 B
+// at TL = 128) or 128 rows of 256 B (8-bit, TL = 256 only).  A transposing read (8 bytes per lane) is served 32 lanes at a time; the 16 lanes of
 // one k group touch 4 (16-bit) or 8 (8-bit) consecutive rows at 2 adjacent 16-byte chunks, and
 // the swizzle gives those accesses distinct banks.  With the 16x16 MFMA shape the two k groups
 // served together (lanes 0-15 and 16-31) lie 16 (16-bit) or 32 (8-bit) rows apart: one more
@@ -100,8 +107,8 @@ __device__ __forceinline__ int swz_mc(int k) {
         return (2 * q + (q >> 2)) ^ (MF == 16 ? (k >> 5) & 1 : 0);
     }
 }
-template <int E, int MF>
-__device__ __forceinline__ int off_mc(int k, int c) { return k * 256 * E + ((c ^ swz_mc<E, MF>(k)) << 4); }
+template <int E, int MF, int TL>
+__device__ __forceinline__ int off_mc(int k, int c) { return k * TL * E + ((c ^ swz_mc<E, MF>(k)) << 4); }
 
 // k group of the 16 lanes l/16 = g of a 16x16 MFMA fragment.  A 16-byte read (ds_read_b128)
 // is served as lanes l and l+32 together, so the groups g and g+2 must read chunks of opposite
@@ -141,23 +148,24 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
 // a chunk that starts past the end reads the row's last element onwards.  Those extra elements
 // only reach output rows or columns past the edge, which are never stored.  Needs an extent of
 // at least one chunk.
-template <int E, bool KC, int MF, bool RS = false>
+template <int E, bool KC, int MF, bool RS = false, int TL = 256>
 struct Loader {
     static constexpr int VE = 16 / E;    // elements per 16-byte chunk
-    uint32_t voff[8];
+    static constexpr int NL = Geo<TL>::NL;
+    uint32_t voff[NL];
 
     // row0: first M (or N) index of the tile; ext: M (or N); ld: leading dimension.
     __device__ __forceinline__ void init(int wave, int lane, int row0, int ext, int ld) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int blk = wave * 8 + i;                          // 1 KiB block of the slab
+        for (int i = 0; i < NL; ++i) {
+            const int blk = wave * NL + i;                         // 1 KiB block of the slab
             if constexpr (KC) {
                 const int r = blk * 8 + (lane >> 3);               // tile row (8 rows of 128 B)
                 const int c = (lane & 7) ^ swz_kc(r);              // logical chunk this lane fetches
                 const int gr = min(row0 + r, ext - 1);
                 voff[i] = (uint32_t)(gr * ld + c * VE) * (uint32_t)E;
             } else {
-                constexpr int CPR = 16 * E;                        // chunks per [k] row
+                constexpr int CPR = TL * E / 16;                   // chunks per [k] row
                 const int k = blk * (64 / CPR) + lane / CPR;       // slab row (k)
                 const int c = (lane % CPR) ^ swz_mc<E, MF>(k);
                 if constexpr (RS) {
@@ -176,9 +184,9 @@ struct Loader {
     __device__ __forceinline__ static const uint8_t *slab_base(const uint8_t *base, int ld, int k0) {
         return KC ? base + (size_t)k0 * E : base + (size_t)k0 * ld * E;
     }
-    // instruction i of this wave: LDS block (wave*8 + i) of the operand slab at `dst`
+    // instruction i of this wave: LDS block (wave*NL + i) of the operand slab at `dst`
     __device__ __forceinline__ void issue(const uint8_t *sb, uint32_t dst, int wave, int i) const {
-        dma16(sb, voff[i], dst + (uint32_t)(wave * 8 + i) * 1024u);
+        dma16(sb, voff[i], dst + (uint32_t)(wave * NL + i) * 1024u);
     }
     // RS: chunk i of this lane from the slab at sb, into registers (raw; nothing may touch the
     // registers before put, so the load has a slab's time to land)
@@ -187,7 +195,7 @@ struct Loader {
     // slab (the one a direct load would fill)
     __device__ __forceinline__ static void put(uint8_t *slab, int wave, int i, int lane, u32x4 v, int xf) {
         v = zero_negative<E>(v, xf);
-        *reinterpret_cast<u32x4 *>(slab + (wave * 8 + i) * 1024 + 16 * lane) = v;
+        *reinterpret_cast<u32x4 *>(slab + (wave * NL + i) * 1024 + 16 * lane) = v;
     }
 };
 
@@ -195,15 +203,16 @@ struct Loader {
 // load transform xf applied (register-staged kernels; the others transform their fragments).
 // fetch() issues all of this thread's loads (8 chunks of 16 bytes; both operands' fetches go
 // out before the barrier that frees the stage), put() writes them to LDS.
-template <int E, bool KC, int MF>
+template <int E, bool KC, int MF, int TL = 256>
 struct TailStage {
     static constexpr int VE = 16 / E;
-    static constexpr int CPR = 16 * E;   // chunks per [k] row of an M/N-contiguous slab
-    u32x4 v[8];
+    static constexpr int CPR = TL * E / 16;   // chunks per [k] row of an M/N-contiguous slab
+    static constexpr int NC = TL * 8 / NT;    // chunks per thread
+    u32x4 v[NC];
 
     __device__ __forceinline__ void fetch(const uint8_t *base, int ld, int row0, int ext, int k0, int K, int tid) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NC; ++i) {
             const int q = tid + NT * i;
             const uint8_t *p;
             int nval;          // leading elements of the chunk inside the operand (0 .. VE)
@@ -225,9 +234,9 @@ struct TailStage {
     }
     __device__ __forceinline__ void put(uint8_t *dst, int tid, int xf) const {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NC; ++i) {
             const int q = tid + NT * i;
-            const uint32_t off = KC ? off_kc(q >> 3, q & 7) : off_mc<E, MF>(q / CPR, q % CPR);
+            const uint32_t off = KC ? off_kc(q >> 3, q & 7) : off_mc<E, MF, TL>(q / CPR, q % CPR);
             const u32x4 w = zero_negative<E>(v[i], xf);
             __builtin_memcpy(dst + off, &w, 16);
         }
@@ -243,17 +252,19 @@ struct TailStage {
 // issued together and assembled as one vector (assembling the halves in separate steps makes
 // the register allocator shuffle accumulators).
 
-template <int MF>
+template <int MF, int TL = 256>
 struct Shape {
-    static constexpr int NF = MF == 32 ? 4 : 8;     // fragments per operand and k-slice
+    static constexpr int NF = TL / 2 / MF;          // fragments per operand and k-slice
     static constexpr int NS = MF == 32 ? 4 : 2;     // k-slices per slab
     static constexpr int NMS = NF * NF;             // MFMAs per k-slice
     static constexpr int KSB = SLAB_BYTES / NS;     // bytes of K per k-slice
 };
 
-template <int E, bool KC, int MF>
+template <int E, bool KC, int MF, int TL = 256>
 struct Frag {
-    using S = Shape<MF>;
+    using S = Shape<MF, TL>;
+    static constexpr int KCB = Geo<TL>::KC;         // bytes of one operand stage
+    static constexpr int ROWB = TL * E;             // bytes of an [k][mn] row
     static constexpr int NF = S::NF;
     // byte address (LDS) of this lane's fragment in stage 0: per sub-tile and k-slice for a
     // K-contiguous operand (the XOR swizzle is not additive), per sub-tile otherwise
@@ -277,7 +288,7 @@ struct Frag {
                 const int q = (lane & 15) >> 2;
                 const int k = 8 * kgrp<MF>(lg) + q;
                 const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
-                addr[t][0] = opbase + (uint32_t)(k * 512 + (((col >> 3) ^ swz_mc<2, MF>(k)) << 4) + (col & 7) * 2);
+                addr[t][0] = opbase + (uint32_t)(k * ROWB + (((col >> 3) ^ swz_mc<2, MF>(k)) << 4) + (col & 7) * 2);
             } else {
                 // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
                 // the 8-byte chunks addressed by lanes i/8 + 2e, e = 0..7.  Lane a of the group
@@ -285,27 +296,27 @@ struct Frag {
                 const int a = lane & 15;
                 const int k = 16 * kgrp<MF>(lg) + (a >> 1);
                 const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 8 * (a & 1);
-                addr[t][0] = opbase + (uint32_t)(k * 256 + (((col >> 4) ^ swz_mc<1, MF>(k)) << 4) + (col & 15));
+                addr[t][0] = opbase + (uint32_t)(k * ROWB + (((col >> 4) ^ swz_mc<1, MF>(k)) << 4) + (col & 15));
             }
         }
     }
     // fragment (t, j) of `stage` into dst
     __device__ __forceinline__ void read(int stage, int t, int j, u32x4 &dst) const {
         if constexpr (KC) {
-            dst = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)(addr[t][j] + stage * KC_BYTES);
+            dst = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)(addr[t][j] + stage * KCB);
         } else if constexpr (E == 2) {
             // k rows j*KS/2 + (0..3) and + (4..7) past the lane's base: the swizzle depends on
             // k & 3 and (16x16 shape) k bit 4, which these offsets leave unchanged
-            const uint32_t a = addr[t][0] + stage * KC_BYTES + ((S::KSB / 2) * j) * 512;
+            const uint32_t a = addr[t][0] + stage * KCB + ((S::KSB / 2) * j) * ROWB;
             s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a);
-            s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(a + 4 * 512));
+            s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(a + 4 * ROWB));
             dst = __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
             // k rows j*KS + (0..7) and + (8..15) past the lane's base: the swizzle depends on
             // k & 7 and (16x16 shape) k bit 5, which these offsets leave unchanged
-            const uint32_t a = addr[t][0] + stage * KC_BYTES + (S::KSB * j) * 256;
+            const uint32_t a = addr[t][0] + stage * KCB + (S::KSB * j) * ROWB;
             i32x2 v0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)a);
-            i32x2 v1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)(a + 8 * 256));
+            i32x2 v1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)(a + 8 * ROWB));
             dst = __builtin_bit_cast(u32x4, __builtin_shufflevector(v0, v1, 0, 1, 2, 3));
         }
     }
@@ -326,28 +337,34 @@ struct Frag {
 // awaited together with that store.  Every load is therefore issued before the stores it would
 // otherwise wait behind: the bias once before the first block, the C values of block i+1 before
 // the stores of block i.
-template <class O>
-__device__ __forceinline__ constexpr int stg_bytes() { return 32 * 128 * (int)sizeof(typename O::T); }
+template <class O, int WT>
+__device__ __forceinline__ constexpr int stg_bytes() { return 32 * WT * (int)sizeof(typename O::T); }
 
-template <int MF>
+// WT: the wave tile (128, or 64 for the 128 x 128 workgroup tile, 16x16 shape only)
+template <int MF, int WT>
 struct EpiMap {
-    static constexpr int NBG = MF == 32 ? 16 : 8;   // distinct column groups per lane
-    __device__ static int row(int q, int lane) { return MF == 32 ? (lane & 31) : 16 * (q >> 3) + (lane & 15); }
+    static_assert(MF == 16 || WT == 128, "the 32x32 shape runs 128-wide wave tiles");
+    static constexpr int NBG = MF == 32 ? 16 : WT / 16;   // distinct column groups per lane
+    static constexpr int QB = MF == 32 ? 16 : 2 * NBG;    // groups of 4 values per 32-row block
+    __device__ static int row(int q, int lane) { return MF == 32 ? (lane & 31) : 16 * (q / NBG) + (lane & 15); }
     __device__ static int col(int q, int lane) {
-        return MF == 32 ? 32 * (q >> 2) + 8 * (q & 3) + 4 * (lane >> 5) : 16 * (q & 7) + 4 * (lane >> 4);
+        return MF == 32 ? 32 * (q >> 2) + 8 * (q & 3) + 4 * (lane >> 5) : 16 * (q % NBG) + 4 * (lane >> 4);
     }
-    __device__ static int bgroup(int q) { return MF == 32 ? q : (q & 7); }
+    __device__ static int bgroup(int q) { return MF == 32 ? q : (q % NBG); }
 };
 
 template <class O, class Acc, int MF, bool BETA, bool FULL, class AccV, int NF>
 __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase, int nbase, int lane,
                                                   AccV (&acc)[NF][NF], uint8_t *stg) {
     using T = typename O::T;
-    using Map = EpiMap<MF>;
+    constexpr int WT = NF * MF;            // wave tile
+    using Map = EpiMap<MF, WT>;
+    constexpr int QB = Map::QB;
+    constexpr int NB = WT / 32;            // 32-row blocks
     constexpr bool INT = std::is_same<Acc, int>::value;
     using Bt = typename std::conditional<INT, int, float>::type;
     constexpr int ES = sizeof(T);
-    constexpr int RB = 128 * ES;           // staged row bytes
+    constexpr int RB = WT * ES;            // staged row bytes
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
     constexpr int VE = 16 / ES;            // elements per chunk
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -360,15 +377,15 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
     // workgroups than CUs), streaming stores keep the L2 and the infinity cache for the A and B
     // panels those rounds read (measured with the 16x16 shape: 3-8 % faster at 8192^3); in a
     // single round, and with the 32x32 shape, the plain stores measured faster
-    const bool stream_d = MF == 16 && (int64_t)p.tiles_m * p.tiles_n * p.batch > 256;
+    const bool stream_d = MF == 16 && (int64_t)p.tiles_m * p.tiles_n * p.batch > (WT == 128 ? 256 : 512);
     typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(1)));
     // accumulator value e of group q in block b
     auto accv = [&](int b, int q, int e) -> Acc {
         if constexpr (MF == 32) return acc[b][q >> 2][4 * (q & 3) + e];
-        else return acc[2 * b + (q >> 3)][q & 7][e];
+        else return acc[2 * b + (q / Map::NBG)][q % Map::NBG][e];
     };
 
-    // bias of this lane's columns, shared by the four row blocks
+    // bias of this lane's columns, shared by the row blocks
     Bt bv[Map::NBG][4];
 #pragma unroll
     for (int q = 0; q < Map::NBG; ++q) {
@@ -386,10 +403,10 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
         }
     }
     // C values of row block b for this lane
-    T cv[16][4];
+    T cv[QB][4];
     auto load_c = [&](int b) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < QB; ++q) {
             const int m = mbase + 32 * b + Map::row(q, lane);
             const int64_t row = (int64_t)(FULL ? m : min(m, M - 1)) * p.ldc;
             const int n = nbase + Map::col(q, lane);
@@ -407,9 +424,9 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
     if constexpr (BETA) load_c(0);
 
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < QB; ++q) {
             const Bt *bq = bv[Map::bgroup(q)];
             T out[4];
             if constexpr (INT) {
@@ -444,7 +461,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, int mbase
             __builtin_memcpy(stg + rl * RB + ((c ^ (rl % CPR)) << 4) + (byte & 15), out, 4 * ES);
         }
         if constexpr (BETA) {
-            if (b < 3) load_c(b + 1);
+            if (b < NB - 1) load_c(b + 1);
         }
         // read back (the wave's LDS operations execute in order): 32 rows x CPR chunks, 16 bytes
         // per lane per round
@@ -478,7 +495,8 @@ template <class O, class Acc, int MF, class AccV, int NF>
 __device__ __forceinline__ void epilogue(const GemmParams &p, int mbase, int nbase, int lane,
                                          AccV (&acc)[NF][NF], uint8_t *stg) {
     // interior wave tiles (the common case) take a path with no edge checks
-    const bool full = mbase + 128 <= p.M && nbase + 128 <= p.N;
+    constexpr int WT = NF * MF;
+    const bool full = mbase + WT <= p.M && nbase + WT <= p.N;
     if (full) {
         if (p.has_beta) store_tile_staged<O, Acc, MF, true, true>(p, mbase, nbase, lane, acc, stg);
         else store_tile_staged<O, Acc, MF, false, true>(p, mbase, nbase, lane, acc, stg);
@@ -491,38 +509,46 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, int mbase, int nba
 // Per-shape schedule: BAR_AT MFMAs of a slab's last k-slice run before its barrier; the slab's 16
 // direct loads go out one per DS MFMA slots (N3 of them after the barrier, in the last k-slice
 // of the previous slab, the rest from the start of the slab).
-template <int MF>
+template <int MF, int TL = 256>
 struct Sched {
+    static constexpr int NLD = 2 * Geo<TL>::NL;          // loads per slab and wave
     static constexpr int BAR_AT = MF == 32 ? 4 : 8;
-    static constexpr int DS = MF == 32 ? 2 : 4;
-    static constexpr int REM = Shape<MF>::NMS - BAR_AT;   // MFMA slots after the barrier
+    static constexpr int DS = MF == 32 || TL == 128 ? 2 : 4;
+    static constexpr int REM = Shape<MF, TL>::NMS - BAR_AT;   // MFMA slots after the barrier
     static constexpr int N3 = (REM + DS - 1) / DS;       // loads of slab s+2 in them
-    static_assert(N3 <= 16, "loads after the barrier");
+    static_assert(N3 <= NLD, "loads after the barrier");
+    // every load of a slab finds a slot: N3 after the barrier, the rest in the first k-slices
+    static_assert(N3 + ((Shape<MF, TL>::NS - 1) * Shape<MF, TL>::NMS + DS - 1) / DS >= NLD, "load slots");
 };
 
 // XF: the launch has a load transform on op(A) or op(B), applied to every fragment after its LDS
 // read (the direct loads put raw operand bytes in LDS).  RS: operands go through registers
 // (global -> VGPR -> LDS, same LDS image) for layouts the direct loads cannot take; the load
-// transforms are then applied once per element on the way to LDS (XF stays off).
-template <class TI, class TO, bool AK, bool BK, int MF, bool XF, bool RS = false>
-__global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
+// transforms are then applied once per element on the way to LDS (XF stays off).  TL: the
+// workgroup tile (256; 128 for mid-size products: two workgroups per CU, 16x16 shape, direct
+// loads, no load transforms).
+template <class TI, class TO, bool AK, bool BK, int MF, bool XF, bool RS = false, int TL = 256>
+__global__ __launch_bounds__(NT, TL == 256 ? 1 : 2) void gemm_fast(GemmParams p) {
+    static_assert(TL == 256 || (TL == 128 && MF == 16 && !XF && !RS && TI::E == 2), "tile variants");
     using acc_t = typename TI::acc_t;
     using accv_t = typename std::conditional<MF == 32, typename TI::accv_t, typename TI::accv16_t>::type;
-    using SH = Shape<MF>;
-    using SC = Sched<MF>;
+    using SH = Shape<MF, TL>;
+    using SC = Sched<MF, TL>;
+    using G = Geo<TL>;
     constexpr int NF = SH::NF, NS = SH::NS, NMS = SH::NMS;
+    constexpr int NL = G::NL;
     constexpr int E = TI::E;
     constexpr int BKE = SLAB_BYTES / E;       // K elements per slab
-    using FA = Frag<E, AK, MF>;
-    using FB = Frag<E, BK, MF>;
+    using FA = Frag<E, AK, MF, TL>;
+    using FB = Frag<E, BK, MF, TL>;
     // fragment reads per k-slice, issued in the order the next k-slice's MFMAs consume them:
     // A0, B0 .. B(NF-1), A1 .. A(NF-1)
     constexpr int NRD = 2 * NF;
     // two pipeline stages of both operands; after the main loop the stage-1 halves of A and B
     // (never used by the K tail) hold the four waves' epilogue staging buffers
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * OPND];
-    constexpr int STG = stg_bytes<TO>();
-    static_assert(2 * STG <= KC_BYTES, "two staging buffers fit in one operand stage");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * G::OPND];
+    constexpr int STG = stg_bytes<TO, G::WT>();
+    static_assert(2 * STG <= G::KC, "two staging buffers fit in one operand stage");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -535,20 +561,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     const uint8_t *A = static_cast<const uint8_t *>(p.A);
     const uint8_t *B = static_cast<const uint8_t *>(p.B);
     const uint32_t lds0 = lds_addr(smem);
-    uint8_t *const stg = smem + (wave < 2 ? 0 : OPND) + KC_BYTES + (wave & 1) * STG;
+    uint8_t *const stg = smem + (wave < 2 ? 0 : G::OPND) + G::KC + (wave & 1) * STG;
 
     FA fa;
     FB fb;
-    Loader<E, AK, MF, RS> la;
-    Loader<E, BK, MF, RS> lb;
+    Loader<E, AK, MF, RS, TL> la;
+    Loader<E, BK, MF, RS, TL> lb;
     // RS: one slab of this wave's chunks in flight between global memory and LDS
-    u32x4 ra[RS ? 8 : 1], rb[RS ? 8 : 1];
+    u32x4 ra[RS ? NL : 1], rb[RS ? NL : 1];
     int m0 = 0, n0 = 0;
     auto set_tile = [&](int id) {
         int tm, tn;
         raster(id, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-        m0 = tm * BM;
-        n0 = tn * BN;
+        m0 = tm * TL;
+        n0 = tn * TL;
         la.init(wave, lane, m0, p.M, p.lda);
         lb.init(wave, lane, n0, p.N, p.ldb);
     };
@@ -591,47 +617,48 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         else acc[i][j] = TI::mma16(bf[buf][j], af[buf][i], acc[i][j]);
     };
     // LDS addresses of operand slabs in a stage
-    auto dstA = [&](int st) { return lds0 + (uint32_t)(st * KC_BYTES); };
-    auto dstB = [&](int st) { return lds0 + (uint32_t)(OPND + st * KC_BYTES); };
+    auto dstA = [&](int st) { return lds0 + (uint32_t)(st * G::KC); };
+    auto dstB = [&](int st) { return lds0 + (uint32_t)(G::OPND + st * G::KC); };
     auto issue_slab = [&](int s, int st) {
-        const uint8_t *sa = Loader<E, AK, MF>::slab_base(A, p.lda, s * BKE);
-        const uint8_t *sb = Loader<E, BK, MF>::slab_base(B, p.ldb, s * BKE);
+        const uint8_t *sa = Loader<E, AK, MF, RS, TL>::slab_base(A, p.lda, s * BKE);
+        const uint8_t *sb = Loader<E, BK, MF, RS, TL>::slab_base(B, p.ldb, s * BKE);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) la.issue(sa, dstA(st), wave, i);
+        for (int i = 0; i < NL; ++i) la.issue(sa, dstA(st), wave, i);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lb.issue(sb, dstB(st), wave, i);
+        for (int i = 0; i < NL; ++i) lb.issue(sb, dstB(st), wave, i);
     };
     auto prologue = [&]() {
         if (nfull > 0) issue_slab(0, 0);
         if (nfull > 1) issue_slab(1, 1);
     };
-    // RS: chunk d (0-7 A, 8-15 B) of slab s into registers; register chunk d into stage st
+    // RS: chunk d (0 .. NL-1 A, NL .. 2NL-1 B) of slab s into registers; register chunk d into
+    // stage st
     auto rs_fetch = [&](int s, int d) {
-        if (d < 8) ra[d] = la.fetch(Loader<E, AK, MF, RS>::slab_base(A, p.lda, s * BKE), d);
-        else rb[d - 8] = lb.fetch(Loader<E, BK, MF, RS>::slab_base(B, p.ldb, s * BKE), d - 8);
+        if (d < NL) ra[d] = la.fetch(Loader<E, AK, MF, RS, TL>::slab_base(A, p.lda, s * BKE), d);
+        else rb[d - NL] = lb.fetch(Loader<E, BK, MF, RS, TL>::slab_base(B, p.ldb, s * BKE), d - NL);
     };
     auto rs_put = [&](int st, int d) {
-        if (d < 8) la.put(smem + st * KC_BYTES, wave, d, lane, ra[d], p.xform_a);
-        else lb.put(smem + OPND + st * KC_BYTES, wave, d - 8, lane, rb[d - 8], p.xform_b);
+        if (d < NL) la.put(smem + st * G::KC, wave, d, lane, ra[d], p.xform_a);
+        else lb.put(smem + G::OPND + st * G::KC, wave, d - NL, lane, rb[d - NL], p.xform_b);
     };
 
-    // Slab s reads stage X; slab s+1 lives in Y.  The 16 loads of a slab are spread one per DS
-    // MFMA slots: the first N3 go out in the last k-slice of slab s-2 (after its barrier freed
-    // the stage), the rest from the start of slab s-1.  Bursting all 16 at once fills the
-    // vector-memory queue and stalls the wave's in-order issue (MFMAs too).
-    //   dma_next:  issue loads N3..15 of slab s+1 into Y (its first loads went out in slab s-1)
+    // Slab s reads stage X; slab s+1 lives in Y.  The NLD (16; 8 at TL = 128) loads of a slab are
+    // spread one per DS MFMA slots: the first N3 go out in the last k-slice of slab s-2 (after
+    // its barrier freed the stage), the rest from the start of slab s-1.  Bursting them all at
+    // once fills the vector-memory queue and stalls the wave's in-order issue (MFMAs too).
+    //   dma_next:  issue loads N3..NLD-1 of slab s+1 into Y (its first loads went out in slab s-1)
     //   dma_next2: issue loads 0..N3-1 of slab s+2 into X
     //   has_next:  slab s+1 exists (wait for it, read its k-slice 0)
     //   RS: in the first k-slices, chunk by chunk, the registers (slab s+1) go to Y and are
     //   refilled with slab s+2 (has_next, dma_next2); the barrier then waits for LDS only
     auto slab_step = [&](int s, int X, int Y, bool dma_next, bool dma_next2, bool has_next) {
-        const uint8_t *na = Loader<E, AK, MF, RS>::slab_base(A, p.lda, (s + 1) * BKE);
-        const uint8_t *nb = Loader<E, BK, MF, RS>::slab_base(B, p.ldb, (s + 1) * BKE);
-        const uint8_t *n2a = Loader<E, AK, MF, RS>::slab_base(A, p.lda, (s + 2) * BKE);
-        const uint8_t *n2b = Loader<E, BK, MF, RS>::slab_base(B, p.ldb, (s + 2) * BKE);
+        const uint8_t *na = Loader<E, AK, MF, RS, TL>::slab_base(A, p.lda, (s + 1) * BKE);
+        const uint8_t *nb = Loader<E, BK, MF, RS, TL>::slab_base(B, p.ldb, (s + 1) * BKE);
+        const uint8_t *n2a = Loader<E, AK, MF, RS, TL>::slab_base(A, p.lda, (s + 2) * BKE);
+        const uint8_t *n2b = Loader<E, BK, MF, RS, TL>::slab_base(B, p.ldb, (s + 2) * BKE);
         auto dma = [&](const uint8_t *sa, const uint8_t *sb, int st, int d) {
-            if (d < 8) la.issue(sa, dstA(st), wave, d);
-            else lb.issue(sb, dstB(st), wave, d - 8);
+            if (d < NL) la.issue(sa, dstA(st), wave, d);
+            else lb.issue(sb, dstB(st), wave, d - NL);
         };
         // k-slices 0 .. NS-2: MFMAs of slice j interleaved with the reads of slice j+1
 #pragma unroll
@@ -642,12 +669,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
                 rd_slot(X, j + 1, (j + 1) & 1, t, NMS);
                 const int q = NMS * j + t;                       // load slot in the slab
                 if constexpr (RS) {
-                    if (q % 2 == 0 && q / 2 < 16) {
+                    if (q % 2 == 0 && q / 2 < SC::NLD) {
                         if (has_next) rs_put(Y, q / 2);
                         if (dma_next2) rs_fetch(s + 2, q / 2);
                     }
                 } else if (dma_next) {
-                    if (q % SC::DS == 0 && SC::N3 + q / SC::DS < 16) dma(na, nb, Y, SC::N3 + q / SC::DS);
+                    if (q % SC::DS == 0 && SC::N3 + q / SC::DS < SC::NLD) dma(na, nb, Y, SC::N3 + q / SC::DS);
                 }
                 fence();
             }
@@ -678,8 +705,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     };
 
     set_tile(lid);
-    fa.init(lane, wm * 128, lds0);
-    fb.init(lane, wn * 128, lds0 + OPND);
+    fa.init(lane, wm * G::WT, lds0);
+    fb.init(lane, wn * G::WT, lds0 + G::OPND);
 #pragma unroll
     for (int i = 0; i < NF; ++i)
 #pragma unroll
@@ -691,17 +718,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
         if constexpr (RS) {
             // slab 0 to stage 0 through the registers; slab 1 stays in them
 #pragma unroll
-            for (int d = 0; d < 16; ++d) rs_fetch(0, d);
+            for (int d = 0; d < 2 * NL; ++d) rs_fetch(0, d);
 #pragma unroll
-            for (int d = 0; d < 16; ++d) rs_put(0, d);
+            for (int d = 0; d < 2 * NL; ++d) rs_put(0, d);
             if (nfull > 1)
 #pragma unroll
-                for (int d = 0; d < 16; ++d) rs_fetch(1, d);
+                for (int d = 0; d < 2 * NL; ++d) rs_fetch(1, d);
         } else {
             prologue();
-            // slab 0 landed, slab 1 may still fly
-            if (nfull > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-            else wait_vmcnt0();
+            // slab 0 landed, slab 1 (its 2 NL loads) may still fly
+            if (nfull > 1) {
+                if constexpr (NL == 8) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            } else {
+                wait_vmcnt0();
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -732,13 +763,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     // K tail: one guarded slab through registers (zero fill past K), in stage 0
     const int k0 = nfull * BKE;
     if (k0 < p.K) {
-        TailStage<E, AK, MF> ta;
-        TailStage<E, BK, MF> tb;
+        TailStage<E, AK, MF, TL> ta;
+        TailStage<E, BK, MF, TL> tb;
         ta.fetch(A, p.lda, m0, p.M, k0, p.K, tid);
         tb.fetch(B, p.ldb, n0, p.N, k0, p.K, tid);
         __syncthreads();
         ta.put(smem, tid, RS ? p.xform_a : 0);
-        tb.put(smem + OPND, tid, RS ? p.xform_b : 0);
+        tb.put(smem + G::OPND, tid, RS ? p.xform_b : 0);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NS; ++j) {   // the k-slices of the slab
@@ -750,7 +781,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast(GemmParams p) {
     }
 
     // every wave's reads of the stage-1 buffers ended before the last slab's barrier
-    epilogue<TO, acc_t, MF>(p, m0 + wm * 128, n0 + wn * 128, lane, acc, stg);
+    epilogue<TO, acc_t, MF>(p, m0 + wm * G::WT, n0 + wn * G::WT, lane, acc, stg);
 }
 
 // MFMA shape of the fast path.  Both shapes give the same results (fp32/int32 accumulation of
@@ -788,29 +819,55 @@ template <class TI, class TO>
 const KernelEntry *lookup_fast(int op_a, int op_b, int rs) {
     constexpr int BKE = SLAB_BYTES / TI::E;
     static const KernelEntry e[8] = {
-        {launch_fast<TI, TO, false, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
-        {launch_fast<TI, TO, false, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
-        {launch_fast<TI, TO, true, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
-        {launch_fast<TI, TO, true, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256"},
-        {launch_fast_rs<TI, TO, false, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
-        {launch_fast_rs<TI, TO, false, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
-        {launch_fast_rs<TI, TO, true, false>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
-        {launch_fast_rs<TI, TO, true, true>, BM, BN, BKE, 2, 2, "gemm_fast_256x256_rs"},
+        {launch_fast<TI, TO, false, false>, 256, 256, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast<TI, TO, false, true>, 256, 256, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast<TI, TO, true, false>, 256, 256, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast<TI, TO, true, true>, 256, 256, BKE, 2, 2, "gemm_fast_256x256"},
+        {launch_fast_rs<TI, TO, false, false>, 256, 256, BKE, 2, 2, "gemm_fast_256x256_rs"},
+        {launch_fast_rs<TI, TO, false, true>, 256, 256, BKE, 2, 2, "gemm_fast_256x256_rs"},
+        {launch_fast_rs<TI, TO, true, false>, 256, 256, BKE, 2, 2, "gemm_fast_256x256_rs"},
+        {launch_fast_rs<TI, TO, true, true>, 256, 256, BKE, 2, 2, "gemm_fast_256x256_rs"},
     };
     if (op_a < 0 || op_a > 1 || op_b < 0 || op_b > 1) return nullptr;
     return &e[(rs ? 4 : 0) + op_a * 2 + op_b];
+}
+
+// 128 x 128 tiles for mid-size products (16-bit inputs, direct loads, no load transforms): 4
+// waves of 64 x 64 and two workgroups per CU, so that a product with a few hundred 128-wide
+// tiles fills the chip that its few dozen 256-wide tiles would leave mostly idle.
+template <class TI, class TO, bool AT, bool BT>
+hipError_t launch_fast128(const GemmParams &p, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_fast<TI, TO, !AT, BT, 16, false, false, 128>), dim3(grid), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+template <class TI, class TO>
+const KernelEntry *lookup_fast128(int op_a, int op_b) {
+    constexpr int BKE = SLAB_BYTES / TI::E;
+    static const KernelEntry e[4] = {
+        {launch_fast128<TI, TO, false, false>, 128, 128, BKE, 2, 2, "gemm_fast_128x128"},
+        {launch_fast128<TI, TO, false, true>, 128, 128, BKE, 2, 2, "gemm_fast_128x128"},
+        {launch_fast128<TI, TO, true, false>, 128, 128, BKE, 2, 2, "gemm_fast_128x128"},
+        {launch_fast128<TI, TO, true, true>, 128, 128, BKE, 2, 2, "gemm_fast_128x128"},
+    };
+    if (op_a < 0 || op_a > 1 || op_b < 0 || op_b > 1) return nullptr;
+    return &e[op_a * 2 + op_b];
 }
 
 }  // namespace
 
 #if defined(TGE_PAIR_F16_F16)
 const KernelEntry *fast_f16_f16(int a, int b, int rs) { return lookup_fast<TF16, OF16>(a, b, rs); }
+const KernelEntry *fast128_f16_f16(int a, int b) { return lookup_fast128<TF16, OF16>(a, b); }
 #elif defined(TGE_PAIR_F16_F32)
 const KernelEntry *fast_f16_f32(int a, int b, int rs) { return lookup_fast<TF16, OF32>(a, b, rs); }
+const KernelEntry *fast128_f16_f32(int a, int b) { return lookup_fast128<TF16, OF32>(a, b); }
 #elif defined(TGE_PAIR_BF16_BF16)
 const KernelEntry *fast_bf16_bf16(int a, int b, int rs) { return lookup_fast<TBF16, OBF16>(a, b, rs); }
+const KernelEntry *fast128_bf16_bf16(int a, int b) { return lookup_fast128<TBF16, OBF16>(a, b); }
 #elif defined(TGE_PAIR_BF16_F32)
 const KernelEntry *fast_bf16_f32(int a, int b, int rs) { return lookup_fast<TBF16, OF32>(a, b, rs); }
+const KernelEntry *fast128_bf16_f32(int a, int b) { return lookup_fast128<TBF16, OF32>(a, b); }
 #elif defined(TGE_PAIR_I8_I32)
 const KernelEntry *fast_i8_i32(int a, int b, int rs) { return lookup_fast<TI8, OI32>(a, b, rs); }
 #else
