@@ -317,6 +317,18 @@ def fp16_long_k():
                     name="fp16_long_k")]
 
 
+def mid_size():
+    """Mid-size products on the 128x128 tiles: fp16 2048^3 NN, A,B ~ N(0,1)/sqrt(K),
+    D = ReLU(acc + bias[N]) -> fp16 (bias fp32 ~ U[-0.5,0.5]); and bf16 -> fp32 2048^3 NN with
+    alpha = 1.5, beta = -0.5, A,B,C ~ U[-1,1]."""
+    K = 2048
+    s = 1.0 / math.sqrt(K)
+    return [Problem(2048, 2048, K, "N", "N", "f16", "f16", "bias_relu", 1.0, 0.0,
+                    a_dist=("normal", s), b_dist=("normal", s), key=(13, 0), name="mid_size"),
+            Problem(2048, 2048, K, "N", "N", "bf16", "f32", "none", 1.5, -0.5, key=(13, 1),
+                    name="mid_size")]
+
+
 def bf16_layout_sweep():
     """bf16 in, fp32 C/D, alpha=1.5, beta=-0.5, A,B,C ~ U[-1,1], NN/NT/TN/TT on the ragged
     shapes 4095x3073x2047 and 5000^3."""
@@ -433,6 +445,7 @@ WORKLOADS = {
     "sgemm_256": sgemm_256,
     "fp16_8192_bias_relu": fp16_8192_bias_relu,
     "fp16_long_k": fp16_long_k,
+    "mid_size": mid_size,
     "bf16_layout_sweep": bf16_layout_sweep,
     "int8_4096_bias": int8_4096_bias,
     "fc_layers": fc_layers,
