@@ -1,6 +1,7 @@
 // Fast path for large fp16/bf16/int8 GEMMs on gfx950: 256x256 output tile per workgroup, 4 waves
 // of 128x128 (8x8 MFMA 16x16 tiles, or 4x4 32x32 tiles; 256 accumulators per lane in AGPRs), K
-// walked in slabs of 128 bytes (64 fp16/bf16, 128 int8).
+// walked in slabs of 128 bytes (64 fp16/bf16, 128 int8).  A 128x128 instance (4 waves of 64x64,
+// two workgroups per CU; 16-bit inputs, direct loads, 16x16 shape) serves mid-size products.
 //
 // The blocking follows "Flexible Performant GEMM Kernels on GPUs" (section 3: tiles copied up
 // the memory hierarchy, global -> shared -> registers, then matrix-multiply-accumulate) and the
