@@ -293,9 +293,10 @@ def test_kmajor_copy_of_a_transposed_a():
 def test_fast128_tiles_chosen_for_mid_size_products():
     # 128x128 tiles of the fast kernel where 256x256 ones would leave half the CUs idle or more
     # (16-bit inputs read in place, no load transforms); an explicit tile of 128 pins them
-    for (M, N, K) in [(1024, 1024, 1024), (2048, 2048, 2048), (4096, 2048, 2048), (1024, 4096, 1024)]:
+    for (M, N, K) in [(1024, 1024, 1024), (2048, 2048, 2048), (4096, 2048, 2048), (1024, 4096, 1024),
+                      (512, 512, 512), (256, 1024, 4096)]:
         assert tge.Plan(M, N, K).describe().startswith("gemm_fast_128x128 "), (M, N, K)
-    for (M, N, K) in [(3072, 3072, 3072), (4096, 4096, 4096), (512, 512, 512)]:
+    for (M, N, K) in [(3072, 3072, 3072), (4096, 4096, 4096), (512, 512, 32)]:
         assert not tge.Plan(M, N, K).describe().startswith("gemm_fast_128x128 "), (M, N, K)
     assert tge.Plan(2048, 2048, 2048, ab="bf16", cd="f32", op_a="T").describe().startswith("gemm_fast_128x128 ")
     # not for int8, load transforms, operands off the 16-byte grid, or a long K that splits

@@ -32,7 +32,8 @@ ROUTES = [((520, 300, 640), "f16", "f16", "from_f32", "none", "fast", "gemm_fast
           ((1000, 776, 384), "bf16", "f32", "none", "from_i8", "fast", "gemm_fast_256x256"),
           ((2048, 2048, 8192), "f16", "f32", "from_i8", "from_f32", "auto", "ksplit"),
           ((16, 4096, 4096), "f16", "f16", "none", "from_f32", "auto", "gemm_skinny"),
-          ((200, 136, 150), "bf16", "bf16", "from_f32", "from_i8", "auto", "gemm_mfma"),
+          ((200, 136, 150), "bf16", "bf16", "from_f32", "from_i8", "auto", "gemm_fast_128x128"),
+          ((200, 136, 150), "bf16", "bf16", "from_f32", "from_i8", "general", "gemm_mfma"),
           ((77, 45, 33), "f16", "f32", "from_i8", "from_i8", "auto", "gemm_mfma")]
 
 

@@ -267,22 +267,22 @@ static gemm_status_t scratch_address(uint8_t **out) {
 // 4096 x 2048 x 4096 85 -> 87 us and 8192 x 1536 x 8192 171 -> 231 us; int8 4096^3 no change.
 constexpr int64_t KMAJOR_MIN_N_BYTES = 6144;
 constexpr int64_t FAST128_MAX_T256 = 128;
-constexpr int64_t FAST128_MIN_T128 = 64;
+constexpr int64_t SHORT_M_MIN_CHUNK = 4;
 static bool kmajor_pays(int64_t M, int64_t N, int64_t K, int eab) {
     (void)M; (void)K;
     return N * eab >= KMAJOR_MIN_N_BYTES;
 }
 
-// Whether the 128x128 tiles of the fast kernel beat the 256x256 ones and the general kernel:
-// when the 256-wide tiles would leave at least half of the 256 CUs idle, and there are enough
-// 128-wide tiles to spread.  Measured (fp16 NN, graph-timed): 1024^3 general 18.0 us -> 9.9 us,
-// 1536^3 30.4 -> 18.6, 2048^3 fast 256 41.0 -> 25.5, 4096 x 2048 x 2048 42.8 -> 35.0,
-// 1024 x 4096 x 1024 25.0 -> 12.5; but 3072^3 (144 wide tiles) 58.6 -> 74.7.
+// Whether the 128x128 tiles of the fast kernel beat the 256x256 ones: when the 256-wide tiles
+// would leave at least half of the 256 CUs idle.  They beat the general kernel at every size
+// measured, down to 16 workgroups.  Measured (fp16 NN, graph-timed): 512^3 general 10.3 us ->
+// 7.0 us, 768^3 13.8 -> 8.4, 256 x 1024 x 4096 56.8 -> 24.9, 1024^3 18.0 -> 9.9, 1536^3
+// 30.4 -> 18.6, 2048^3 fast 256 41.0 -> 25.5, 4096 x 2048 x 2048 42.8 -> 35.0; but 3072^3 (144
+// wide tiles) 58.6 -> 74.7.
 static bool fast128_pays(int64_t M, int64_t N, int64_t nprod) {
     const int64_t nb = nprod > 1 ? nprod : 1;
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * nb;
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128) * nb;
-    return t256 <= FAST128_MAX_T256 && t128 >= FAST128_MIN_T128;
+    return t256 <= FAST128_MAX_T256;
 }
 
 struct Scratch {
@@ -823,7 +823,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         const int64_t slabs = K / slab_k;
         int64_t sp = tiles > 0 ? 256 / tiles : 0;
         const bool short_i8 = M <= 64 && (ab_type == GEMM_I8 || op_a == GEMM_OP_T);
-        const int64_t min_chunk = force_split ? 1 : short_i8 ? 2 : 16;
+        // one row of 256-wide tiles: chunks down to 4 slabs (fp16 96 x 4096 x 4096: general
+        // kernel 77 us, split 16 ways 28 us; 128 x 4096 x 4096 64 -> 29 us; 256 x 4096 x 4096
+        // 128-wide tiles 39 -> 37 us)
+        const bool short_m = M <= 256;
+        const int64_t min_chunk = force_split ? 1 : short_i8 ? 2 : short_m ? SHORT_M_MIN_CHUNK : 16;
         if (sp > slabs / min_chunk) sp = slabs / min_chunk;
         while (sp > 1 && slabs % sp) --sp;
         // short products split only from 8 slabs of K: with 4 slabs the two chunks and the
@@ -971,7 +975,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
                                pblocks(cx_ld_b * 2, 16, op_b == GEMM_OP_N ? K : N, nbb);
         gemm_plan *rp = nullptr;
         if (blocks < lim && gemm_plan_create_desc(&rp, &r) == GEMM_STATUS_SUCCESS) {
-            if ((rp->fast && !rp->fast_is_skinny) || rp->fast_pk || rp->fast_rs) {
+            // (a real product small enough that only the 128-wide tiles would take it keeps
+            // the complex kernel: the rewrite pass would cost more than it saves)
+            if ((rp->fast && !rp->fast_is_skinny && rp->fast->bm == 256) || rp->fast_pk || rp->fast_rs) {
                 cx = rp;
                 const int64_t bytes_a = op_a == GEMM_OP_T ? na * 2 * K * cx_ld_a * 2 : 0;
                 cx_off_b = (bytes_a + 255) / 256 * 256;
