@@ -305,6 +305,13 @@ def test_fast128_tiles_chosen_for_mid_size_products():
     assert not tge.Plan(2048, 2048, 2048, transform_a="relu").describe().startswith("gemm_fast_128x128 ")
     assert not tge.Plan(2048, 2048, 2048, lda=2049).describe().startswith("gemm_fast_128x128 ")
     assert " ksplit " in tge.Plan(2048, 2048, 8192).describe()
+    # short products (64 < M <= 256) from 64 slabs of K split it over the 128-wide tiles
+    for (M, N, K) in [(96, 4096, 4096), (256, 4096, 4096), (128, 8192, 8192)]:
+        d = tge.Plan(M, N, K).describe()
+        assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
+    d = tge.Plan(128, 4096, 2048).describe()
+    assert d.startswith("gemm_fast_128x128 ") and "ksplit" not in d, d
+    assert tge.Plan(64, 4096, 4096).describe().startswith("gemm_skinny")
     d = tge.Plan(3072, 3072, 3072, algo="fast", tile=128).describe()
     assert d.startswith("gemm_fast_128x128 ") and "grid 576" in d, d
     assert not tge.Plan(2048, 2048, 2048, algo="general").describe().startswith("gemm_fast")

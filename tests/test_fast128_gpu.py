@@ -120,3 +120,25 @@ def test_fast128_noalloc_and_unaligned_pointer(tile128):
     check(p, x, outs[0], reference(p, x), exact=True)
     D2, _ = run(p, x, offset=1, plan=pl)
     assert np.array_equal(D2, outs[0])
+
+
+# (M, N, K, layout, ab, cd, epilogue, alpha, beta): short products on the 128-wide tiles with K
+# split over workgroups (pinned: tile 128 with the split algorithm)
+SPLITS = [((128, 1024, 1024), "NN", "f16", "f16", "bias_relu", 1.0, 0.0),
+          ((200, 520, 2048), "NT", "bf16", "f32", "bias", 2.0, -1.0),
+          ((256, 392, 1536), "TN", "f16", "f32", "relu", 1.0, 1.0),
+          ((96, 264, 4096), "TT", "bf16", "bf16", "bias_relu", 0.5, 0.0)]
+
+
+@pytest.mark.parametrize("case", range(len(SPLITS)))
+def test_fast128_split_exact(case, monkeypatch):
+    monkeypatch.setitem(FORCE, "algo", "split")
+    monkeypatch.setitem(FORCE, "tile", 128)
+    (M, N, K), lay, ab, cd, epi, alpha, beta = SPLITS[case]
+    p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta, key=(175, case))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    d = pl.describe()
+    print(f"{p.label()} -> {d}", flush=True)
+    assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
+    check(p, x, D, reference(p, x), exact=True)

@@ -42,6 +42,7 @@ struct gemm_plan {
     bool pk_tr;
     const KernelEntry *fast_pk_tr;   // direct-load kernel on a transposed copy of A
     const KernelEntry *fast_part_tr; // its K-split variant (nullptr: no split)
+    const KernelEntry *fast_part128; // K split of the 128x128 tiles (nullptr: none)
     int64_t pk_ld_a, pk_ld_b;        // leading dimensions of the copies (whole 128-byte lines)
     int64_t pk_kpad;                 // K rounded up to whole slabs: the copies are zero there
     int64_t pk_off_b, pk_bytes;      // byte offset of B's copy in the workspace, total size
@@ -268,6 +269,7 @@ static gemm_status_t scratch_address(uint8_t **out) {
 constexpr int64_t KMAJOR_MIN_N_BYTES = 6144;
 constexpr int64_t FAST128_MAX_T256 = 128;
 constexpr int64_t SHORT_M_MIN_CHUNK = 4;
+constexpr int64_t SPLIT128_MIN_SLABS = 64;
 static bool kmajor_pays(int64_t M, int64_t N, int64_t K, int eab) {
     (void)M; (void)K;
     return N * eab >= KMAJOR_MIN_N_BYTES;
@@ -283,6 +285,18 @@ static bool fast128_pays(int64_t M, int64_t N, int64_t nprod) {
     const int64_t nb = nprod > 1 ? nprod : 1;
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * nb;
     return t256 <= FAST128_MAX_T256;
+}
+
+// Whether a short product (64 < M <= 256, below that the skinny kernel) takes the 128x128
+// tiles with K split rather than the 256x256 ones with their finer split or the 128x128 tiles
+// unsplit: from 64 slabs of K.  Measured (fp16 NN, graph-timed; 256-wide split -> 128-wide
+// split): 96 x 4096 x 4096 27.3 -> 17.0 us, 128 x 4096 x 4096 28.3 -> 18.2, 256 x 4096 x 4096
+// 35.8 -> 23.0, 128 x 8192 x 8192 45.1 -> 36.2, 256 x 14336 x 4096 53.8 -> 46.8, 256 x 1024 x
+// 4096 (unsplit 128-wide) 25.0 -> 18.5; at 32 slabs the unsplit 128-wide tiles stay faster
+// (128 x 4096 x 2048 15.0 vs 18.8 us).
+static bool split128_pays(int64_t M, int64_t N, int64_t slabs) {
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    return t128 < 256 && slabs >= SPLIT128_MIN_SLABS && M > 64;
 }
 
 struct Scratch {
@@ -494,7 +508,9 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
     // fast kernel with K split (needs its workspace; a first run inside a capture runs whole)
     void *spw = nullptr;
     const bool k_tr = p->fast_pk_tr && k == p->fast_pk_tr;   // A from its transposed copy
-    if ((k == p->fast || k == p->fast_pk || k_tr) && !sk && p->fast_part) {
+    // the partial products' kernel: the same tiles and layout as the kernel chosen above
+    const KernelEntry *part_k = k->bm == 128 ? p->fast_part128 : k_tr ? p->fast_part_tr : p->fast_part;
+    if ((k == p->fast || k == p->fast_pk || k_tr) && !sk && part_k) {
         const gemm_status_t st = workspace(sc, reinterpret_cast<void **>(&p->ws), &p->ws_dev, split_bytes, hs, &spw);
         if (sc && st != GEMM_STATUS_SUCCESS) return st;
     }
@@ -522,8 +538,7 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
         part.stride_c = p->M * p->N;
         part.stride_bias = 0;
         const unsigned g1 = (unsigned)((int64_t)prm.tiles_m * prm.tiles_n * S);
-        const KernelEntry *pk = k_tr ? p->fast_part_tr : p->fast_part;
-        if (!dry && pk->launch(part, g1, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
+        if (!dry && part_k->launch(part, g1, hs) != hipSuccess) return GEMM_STATUS_HIP_ERROR;
         GemmParams fin = prm;
         fin.tiles_m = S;
         fin.ws = static_cast<float *>(spw);
@@ -824,8 +839,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         int64_t sp = tiles > 0 ? 256 / tiles : 0;
         const bool short_i8 = M <= 64 && (ab_type == GEMM_I8 || op_a == GEMM_OP_T);
         // one row of 256-wide tiles: chunks down to 4 slabs (fp16 96 x 4096 x 4096: general
-        // kernel 77 us, split 16 ways 28 us; 128 x 4096 x 4096 64 -> 29 us; 256 x 4096 x 4096
-        // 128-wide tiles 39 -> 37 us)
+        // kernel 77 us, split 16 ways 28 us; 128 x 4096 x 4096 64 -> 29 us); with 16-bit inputs
+        // read in place the 128-wide tiles' split below takes most of these products instead
         const bool short_m = M <= 256;
         const int64_t min_chunk = force_split ? 1 : short_i8 ? 2 : short_m ? SHORT_M_MIN_CHUNK : 16;
         if (sp > slabs / min_chunk) sp = slabs / min_chunk;
@@ -863,6 +878,27 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
          (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod))))
         fast128 = f128t(op_a, op_b);
     if (fast128) fast = fast128;
+    // short products (M <= 256) on the 128x128 tiles with K split over workgroups: t128 tiles
+    // times S chunks (whole slabs, at least 4 each) of about one workgroup per CU; the partial
+    // sums are S * M * N fp32 values (a quarter of those of the 256-wide tiles' 16-way split)
+    int split128 = 0;
+    const Fast128Lookup f128p = fast128_table(ab_type, part_cd);
+    if (f128t && f128p && direct_ok && M <= 256 && nprod <= 1 && K % slab_k == 0 &&
+        !desc->transform_a && !desc->transform_b && !diag_a && !diag_b && !ctable &&
+        finish_table(ab_type, cd_type) &&
+        ((tile == 128 && algo == GEMM_ALGO_SPLIT) ||
+         (tile == 0 && algo == GEMM_ALGO_AUTO && split128_pays(M, N, K / slab_k)))) {
+        const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+        const int64_t slabs = K / slab_k;
+        int64_t sp = (256 + t128 - 1) / t128;
+        if (sp > slabs / SHORT_M_MIN_CHUNK) sp = slabs / SHORT_M_MIN_CHUNK;
+        while (sp > 1 && slabs % sp) --sp;
+        if (sp >= 2) {
+            split128 = (int)sp;
+            fast = fast128 = f128t(op_a, op_b);
+            split_s = 0;
+        }
+    }
     // the register-staged variant takes every layout the direct loads cannot (odd leading
     // dimensions or strides, unaligned pointers, M/N-contiguous extents off the 16-byte grid)
     const KernelEntry *fast_rs = nullptr;
@@ -1011,6 +1047,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->pk_tr = pk_tr;
     p->fast_pk_tr = fast_pk_tr;
     p->fast_part_tr = nullptr;
+    p->fast_part128 = nullptr;
     p->pk_ld_a = pk_ld_a; p->pk_ld_b = pk_ld_b;
     p->pk_kpad = pk_kpad;
     p->pk_off_b = pk_off_b; p->pk_bytes = pk_bytes;
@@ -1049,6 +1086,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if (pk_tr) p->fast_part_tr = fast_table(ab_type, ab_type == GEMM_I8 ? GEMM_I32 : GEMM_F32)(GEMM_OP_N, op_b, 0);
         p->finish = finish_table(ab_type, cd_type);
         p->ksplit = split_s;
+    }
+    if (split128 && !skinny) {
+        p->fast_part128 = f128p(op_a, op_b);
+        p->finish = finish_table(ab_type, cd_type);
+        p->ksplit = split128;
     }
     // a plan that always copies an operand (off the 16-byte grid, or carrying a load transform
     // that the copy applies) shows the direct kernel on the copies
