@@ -73,6 +73,7 @@ const KernelEntry *fast128_f16_f16(int a, int b) { return fast128(a, b); }
 const KernelEntry *fast128_f16_f32(int a, int b) { return fast128(a, b); }
 const KernelEntry *fast128_bf16_bf16(int a, int b) { return fast128(a, b); }
 const KernelEntry *fast128_bf16_f32(int a, int b) { return fast128(a, b); }
+const KernelEntry *fast128_i8_i32(int a, int b) { return fast128(a, b); }
 const KernelEntry *skinny_f16_f16(int b, int m, int n) { return skinny(b, m, n); }
 const KernelEntry *skinny_f16_f32(int b, int m, int n) { return skinny(b, m, n); }
 const KernelEntry *skinny_bf16_bf16(int b, int m, int n) { return skinny(b, m, n); }

@@ -299,9 +299,8 @@ def test_fast128_tiles_chosen_for_mid_size_products():
     for (M, N, K) in [(3072, 3072, 3072), (4096, 4096, 4096), (512, 512, 32)]:
         assert not tge.Plan(M, N, K).describe().startswith("gemm_fast_128x128 "), (M, N, K)
     assert tge.Plan(2048, 2048, 2048, ab="bf16", cd="f32", op_a="T").describe().startswith("gemm_fast_128x128 ")
-    # not for int8, load transforms, operands off the 16-byte grid, or a long K that splits
-    assert "128x128" in tge.Plan(2048, 2048, 2048, ab="i8", cd="i32").describe()
-    assert not tge.Plan(2048, 2048, 2048, ab="i8", cd="i32").describe().startswith("gemm_fast_128x128 ")
+    assert tge.Plan(2048, 2048, 2048, ab="i8", cd="i32").describe().startswith("gemm_fast_128x128 ")
+    # not for load transforms, operands off the 16-byte grid, or a long K that splits
     assert not tge.Plan(2048, 2048, 2048, transform_a="relu").describe().startswith("gemm_fast_128x128 ")
     assert not tge.Plan(2048, 2048, 2048, lda=2049).describe().startswith("gemm_fast_128x128 ")
     assert " ksplit " in tge.Plan(2048, 2048, 8192).describe()

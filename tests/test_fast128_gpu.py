@@ -142,3 +142,37 @@ def test_fast128_split_exact(case, monkeypatch):
     print(f"{p.label()} -> {d}", flush=True)
     assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
     check(p, x, D, reference(p, x), exact=True)
+
+
+# int8 -> int32 (alpha 1, beta 0 or 1): M and N multiples of 16 so that every layout is read in
+# place (and K a multiple of 16: rows of whole chunks); K tails of 0, 112 and 0 elements
+I8_SHAPES = [((304, 272, 384), "bias_relu", 0.0), ((1008, 784, 1008), "bias", 1.0), ((128, 128, 128), "none", 1.0)]
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("shape", range(len(I8_SHAPES)))
+def test_fast128_int8_exact(shape, lay, tile128):
+    (M, N, K), epi, beta = I8_SHAPES[shape]
+    p = synth.Problem(M, N, K, lay[0], lay[1], "i8", "i32", epi, 1.0, beta,
+                      a_dist=("int", -128, 127), b_dist=("int", -128, 127), c_dist=("int", -1000, 1000),
+                      bias_dist=("int", -(1 << 20), 1 << 20), key=(176, shape * 4 + LAYOUTS.index(lay)))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    d = pl.describe()
+    print(f"{p.label()} -> {d}", flush=True)
+    assert d.startswith("gemm_fast_128x128 "), d
+    check(p, x, D, reference(p, x), exact=True)
+
+
+def test_fast128_int8_split_exact(monkeypatch):
+    monkeypatch.setitem(FORCE, "algo", "split")
+    monkeypatch.setitem(FORCE, "tile", 128)
+    p = synth.Problem(200, 528, 8192, "N", "T", "i8", "i32", "bias", 1.0, 1.0,
+                      a_dist=("int", -128, 127), b_dist=("int", -128, 127), c_dist=("int", -1000, 1000),
+                      bias_dist=("int", -(1 << 20), 1 << 20), key=(177, 0))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    d = pl.describe()
+    print(d, flush=True)
+    assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
+    check(p, x, D, reference(p, x), exact=True)

@@ -132,6 +132,7 @@ Fast128Lookup fast128_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F32) return tge::fast128_f16_f32;
     if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::fast128_bf16_bf16;
     if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::fast128_bf16_f32;
+    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::fast128_i8_i32;
     return nullptr;
 }
 
@@ -867,8 +868,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
                            strides16 && (op_a == GEMM_OP_N || M % ve == 0) && (op_b == GEMM_OP_T || N % ve == 0);
     if (ft && want_fast && direct_ok)
         fast = ft(op_a, op_b, 0);
-    // 128x128 tiles of the fast kernel (16-bit inputs, operands read in place, no load
-    // transforms on op(A)/op(B)), for products whose 256x256 tiles would leave most CUs idle;
+    // 128x128 tiles of the fast kernel (operands read in place, no load transforms on
+    // op(A)/op(B)), for products whose 256x256 tiles would leave most CUs idle;
     // an explicit tile of 128 with the fast or automatic algorithm pins it
     const Fast128Lookup f128t = fast128_table(ab_type, cd_type);
     const KernelEntry *fast128 = nullptr;

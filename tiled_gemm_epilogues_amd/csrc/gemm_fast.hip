@@ -1,7 +1,7 @@
 // Fast path for large fp16/bf16/int8 GEMMs on gfx950: 256x256 output tile per workgroup, 4 waves
 // of 128x128 (8x8 MFMA 16x16 tiles, or 4x4 32x32 tiles; 256 accumulators per lane in AGPRs), K
 // walked in slabs of 128 bytes (64 fp16/bf16, 128 int8).  A 128x128 instance (4 waves of 64x64,
-// two workgroups per CU; 16-bit inputs, direct loads, 16x16 shape) serves mid-size products.
+// two workgroups per CU; direct loads, 16x16 shape) serves mid-size products.
 //
 // The blocking follows "Flexible Performant GEMM Kernels on GPUs" (section 3: tiles copied up
 // the memory hierarchy, global -> shared -> registers, then matrix-multiply-accumulate) and the
@@ -98,9 +98,17 @@ __device__ __forceinline__ int off_kc(int r, int c) { return r * 128 + ((c ^ swz
 // row bit of the swizzle moves the second group to the other half of the banks (the 32x32
 // shape keeps the k groups of a pass in one row block, and adds whole k-slices to a base
 // address, which must not change the swizzle).
-template <int E, int MF>
+template <int E, int MF, int TL = 256>
 __device__ __forceinline__ int swz_mc(int k) {
-    if constexpr (E == 2) {
+    if constexpr (E == 1 && TL == 128) {
+        // 8-bit rows of 128 B (8 chunks; a row spans half the banks, rows k and k+2 the same
+        // half): the 16 lanes of a k group read 8 consecutive rows at one chunk, so rows of one
+        // half (k, k+2, k+4, k+6) take 4 different chunks; the k group served with it, 32 rows
+        // on, takes the other 4.  Invariant under adding 8 or 64 to a fragment's base row (the
+        // second transposing read, the k-slice offset).
+        static_assert(MF == 16, "16x16 shape");
+        return ((k >> 1) & 3) ^ (((k >> 5) & 1) << 2);
+    } else if constexpr (E == 2) {
         const int q = k & 3;
         return (4 * q + 2 * (q >> 1)) ^ (MF == 16 ? ((k >> 4) & 1) << 1 : 0);
     } else {
@@ -109,7 +117,7 @@ __device__ __forceinline__ int swz_mc(int k) {
     }
 }
 template <int E, int MF, int TL>
-__device__ __forceinline__ int off_mc(int k, int c) { return k * TL * E + ((c ^ swz_mc<E, MF>(k)) << 4); }
+__device__ __forceinline__ int off_mc(int k, int c) { return k * TL * E + ((c ^ swz_mc<E, MF, TL>(k)) << 4); }
 
 // k group of the 16 lanes l/16 = g of a 16x16 MFMA fragment.  A 16-byte read (ds_read_b128)
 // is served as lanes l and l+32 together, so the groups g and g+2 must read chunks of opposite
@@ -168,7 +176,7 @@ struct Loader {
             } else {
                 constexpr int CPR = TL * E / 16;                   // chunks per [k] row
                 const int k = blk * (64 / CPR) + lane / CPR;       // slab row (k)
-                const int c = (lane % CPR) ^ swz_mc<E, MF>(k);
+                const int c = (lane % CPR) ^ swz_mc<E, MF, TL>(k);
                 if constexpr (RS) {
                     const int col = min(row0 + c * VE, ext - 1);   // starts inside the row
                     voff[i] = (uint32_t)(k * ld + col) * (uint32_t)E;
@@ -289,7 +297,7 @@ struct Frag {
                 const int q = (lane & 15) >> 2;
                 const int k = 8 * kgrp<MF>(lg) + q;
                 const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
-                addr[t][0] = opbase + (uint32_t)(k * ROWB + (((col >> 3) ^ swz_mc<2, MF>(k)) << 4) + (col & 7) * 2);
+                addr[t][0] = opbase + (uint32_t)(k * ROWB + (((col >> 3) ^ swz_mc<2, MF, TL>(k)) << 4) + (col & 7) * 2);
             } else {
                 // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
                 // the 8-byte chunks addressed by lanes i/8 + 2e, e = 0..7.  Lane a of the group
@@ -297,7 +305,7 @@ struct Frag {
                 const int a = lane & 15;
                 const int k = 16 * kgrp<MF>(lg) + (a >> 1);
                 const int col = wrow + MF * t + (MF == 32 ? 16 * ((lane >> 4) & 1) : 0) + 8 * (a & 1);
-                addr[t][0] = opbase + (uint32_t)(k * ROWB + (((col >> 4) ^ swz_mc<1, MF>(k)) << 4) + (col & 15));
+                addr[t][0] = opbase + (uint32_t)(k * ROWB + (((col >> 4) ^ swz_mc<1, MF, TL>(k)) << 4) + (col & 15));
             }
         }
     }
@@ -530,7 +538,7 @@ struct Sched {
 // loads, no load transforms).
 template <class TI, class TO, bool AK, bool BK, int MF, bool XF, bool RS = false, int TL = 256>
 __global__ __launch_bounds__(NT, TL == 256 ? 1 : 2) void gemm_fast(GemmParams p) {
-    static_assert(TL == 256 || (TL == 128 && MF == 16 && !XF && !RS && TI::E == 2), "tile variants");
+    static_assert(TL == 256 || (TL == 128 && MF == 16 && !XF && !RS), "tile variants");
     using acc_t = typename TI::acc_t;
     using accv_t = typename std::conditional<MF == 32, typename TI::accv_t, typename TI::accv16_t>::type;
     using SH = Shape<MF, TL>;
@@ -833,7 +841,7 @@ const KernelEntry *lookup_fast(int op_a, int op_b, int rs) {
     return &e[(rs ? 4 : 0) + op_a * 2 + op_b];
 }
 
-// 128 x 128 tiles for mid-size products (16-bit inputs, direct loads, no load transforms): 4
+// 128 x 128 tiles for mid-size products (direct loads, no load transforms): 4
 // waves of 64 x 64 and two workgroups per CU, so that a product with a few hundred 128-wide
 // tiles fills the chip that its few dozen 256-wide tiles would leave mostly idle.
 template <class TI, class TO, bool AT, bool BT>
@@ -871,6 +879,7 @@ const KernelEntry *fast_bf16_f32(int a, int b, int rs) { return lookup_fast<TBF1
 const KernelEntry *fast128_bf16_f32(int a, int b) { return lookup_fast128<TBF16, OF32>(a, b); }
 #elif defined(TGE_PAIR_I8_I32)
 const KernelEntry *fast_i8_i32(int a, int b, int rs) { return lookup_fast<TI8, OI32>(a, b, rs); }
+const KernelEntry *fast128_i8_i32(int a, int b) { return lookup_fast128<TI8, OI32>(a, b); }
 #else
 #error "define one TGE_PAIR_* macro with a 16- or 8-bit input type"
 #endif

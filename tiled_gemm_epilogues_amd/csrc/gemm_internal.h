@@ -72,12 +72,13 @@ const KernelEntry *fast_bf16_bf16(int op_a, int op_b, int rs);
 const KernelEntry *fast_bf16_f32(int op_a, int op_b, int rs);
 const KernelEntry *fast_i8_i32(int op_a, int op_b, int rs);
 // The same kernel with 128x128 tiles (4 waves of 64x64, two workgroups per CU) for mid-size
-// products: 16-bit inputs, direct loads only (the same alignment preconditions), no load
-// transforms on op(A)/op(B).
+// products: direct loads only (the same alignment preconditions), no load transforms on
+// op(A)/op(B).
 const KernelEntry *fast128_f16_f16(int op_a, int op_b);
 const KernelEntry *fast128_f16_f32(int op_a, int op_b);
 const KernelEntry *fast128_bf16_bf16(int op_a, int op_b);
 const KernelEntry *fast128_bf16_f32(int op_a, int op_b);
+const KernelEntry *fast128_i8_i32(int op_a, int op_b);
 
 // Byte-exact copy of an operand into rows that are 16-byte aligned and zero-padded to whole
 // 16-byte chunks (gemm_repack.hip), for operands the direct loads cannot take: row r < rows of
