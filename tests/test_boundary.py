@@ -300,9 +300,15 @@ def test_fast128_tiles_chosen_for_mid_size_products():
         assert not tge.Plan(M, N, K).describe().startswith("gemm_fast_128x128 "), (M, N, K)
     assert tge.Plan(2048, 2048, 2048, ab="bf16", cd="f32", op_a="T").describe().startswith("gemm_fast_128x128 ")
     assert tge.Plan(2048, 2048, 2048, ab="i8", cd="i32").describe().startswith("gemm_fast_128x128 ")
-    # not for load transforms, operands off the 16-byte grid, or a long K that splits
-    assert not tge.Plan(2048, 2048, 2048, transform_a="relu").describe().startswith("gemm_fast_128x128 ")
-    assert not tge.Plan(2048, 2048, 2048, lda=2049).describe().startswith("gemm_fast_128x128 ")
+    # load transforms and operands off the 16-byte grid: the 128-wide tiles on the copies
+    for kw, shows in [(dict(transform_a="relu"), "repack A"), (dict(lda=2049), "repack A"),
+                      (dict(ldb=2050, op_b="T"), "repack B"), (dict(op_a="T", M=2044), "repack A (A to K-major)")]:
+        args = dict(M=2048, N=2048, K=2048)
+        args.update(kw)
+        d = tge.Plan(**args).describe()
+        assert d.startswith("gemm_fast_128x128 ") and shows in d, (kw, d)
+    # not for the general algorithm, or a long K that splits
+    assert not tge.Plan(1024, 1024, 1024, lda=1025, algo="general").describe().startswith("gemm_fast")
     assert " ksplit " in tge.Plan(2048, 2048, 8192).describe()
     # short products (64 < M <= 256) from 64 slabs of K split it over the 128-wide tiles
     for (M, N, K) in [(96, 4096, 4096), (256, 4096, 4096), (128, 8192, 8192)]:

@@ -101,7 +101,7 @@ def test_fast128_chosen_for_mid_size_products():
 
 def test_fast128_noalloc_and_unaligned_pointer(tile128):
     # no workspace: the no-allocation run is the same run; a pointer off 16 bytes at run time
-    # takes the 256-wide kernel on an aligned copy instead, with the same result
+    # takes the same tiles on an aligned copy instead, with the same result
     p = synth.exact_integer_problem(520, 264, 512, "N", "N", "f16", "f32", "bias", 1.0, 0.5,
                                     key=(174, 0))
     x = synth.make_inputs(p)
@@ -176,3 +176,52 @@ def test_fast128_int8_split_exact(monkeypatch):
     print(d, flush=True)
     assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
     check(p, x, D, reference(p, x), exact=True)
+
+
+# (M, N, K, layout, ab, cd, epilogue, alpha, beta, ld_pad, transform_a, what the description must
+# show): operands the direct loads cannot read in place (odd leading dimensions, an M/N-contiguous
+# extent off the 16-byte grid) or carrying a load transform, copied, the 128-wide tiles on the copies
+COPIES = [((520, 392, 360), "NN", "f16", "f16", "bias_relu", 1.0, 0.0, 3, "none", "repack AB"),
+          ((300, 264, 1000), "NT", "bf16", "f32", "bias", 2.0, -1.0, 1, "none", "repack AB"),
+          ((521, 264, 512), "TN", "f16", "f32", "relu", 1.0, 1.0, 0, "none", "repack A (A to K-major)"),
+          ((264, 250, 640), "TT", "bf16", "bf16", "none", 0.5, 0.0, 2, "none", "repack AB"),
+          ((392, 520, 256), "NN", "f16", "f16", "bias", 1.0, 0.5, 0, "relu", "repack A"),
+          ((400, 304, 768), "TN", "bf16", "f32", "bias_relu", 1.0, 0.0, 0, "relu", "repack A (A to K-major)"),
+          ((300, 256, 1280), "NT", "i8", "i32", "bias", 1.0, 1.0, 5, "none", "repack AB"),
+          ((600, 520, 640), "TN", "i8", "i32", "bias_relu", 1.0, 0.0, 0, "relu", "repack AB (A to K-major)")]
+
+
+@pytest.mark.parametrize("case", range(len(COPIES)))
+def test_fast128_on_copies_exact(case, tile128):
+    (M, N, K), lay, ab, cd, epi, alpha, beta, pad, xa, shows = COPIES[case]
+    p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta, key=(178, case),
+                                    ld_pad=pad, transform_a=xa)
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    d = pl.describe()
+    print(f"{p.label()} -> {d}", flush=True)
+    assert d.startswith("gemm_fast_128x128 ") and shows in d, d
+    check(p, x, D, reference(p, x), exact=True)
+
+
+def test_fast128_on_copies_chosen_and_noalloc():
+    # the plan's own choice for a mid-size product with an odd leading dimension; the
+    # no-allocation run takes its copy from the scratch, with the same result
+    p = synth.exact_integer_problem(2048, 2048, 2048, "N", "N", "f16", "f32", "bias_relu", 1.0, 0.5,
+                                    key=(179, 0), ld_pad=1)
+    x = synth.make_inputs(p)
+    pl = tge.Plan(p.M, p.N, p.K, p.op_a, p.op_b, p.lda, p.ldb, p.ldc, p.ab, p.cd, p.epi)
+    d = pl.describe()
+    print(d, flush=True)
+    assert d.startswith("gemm_fast_128x128 ") and "repack AB" in d, d
+    A, B = to_dev(p.a_store, x["A"]), to_dev(p.b_store, x["B"])
+    C, bias = to_dev(p.cd, x["C"]), to_dev(p.bias_dt, x["bias"])
+    outs = []
+    for runner in (pl.run, pl.run_noalloc, pl.run_noalloc):
+        D = to_dev(p.cd, np.full(p.M * p.ldc, sentinel(p.cd), dtype=synth.RAW_NP[p.cd]))
+        runner(A, B, C, D, bias, p.alpha, p.beta)
+        torch.cuda.synchronize()
+        outs.append(to_host(p.cd, D).reshape(p.M, p.ldc))
+    # (the sentinel past column N is a NaN)
+    assert np.array_equal(outs[0], outs[1], equal_nan=True) and np.array_equal(outs[1], outs[2], equal_nan=True)
+    check(p, x, outs[0], reference(p, x, threads=16), exact=True)

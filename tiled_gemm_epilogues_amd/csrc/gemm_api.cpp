@@ -900,6 +900,12 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
             split_s = 0;
         }
     }
+    // the same choice for copies of operands the direct loads cannot read in place, or that
+    // carry a load transform (the copy applies it): the 128x128 tiles run on the copies
+    const bool want128 = f128t && !diag_a && !diag_b && !ctable && algo != GEMM_ALGO_GENERAL && !split_s &&
+                         !split128 &&
+                         ((tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST)) ||
+                          (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod)));
     // the register-staged variant takes every layout the direct loads cannot (odd leading
     // dimensions or strides, unaligned pointers, M/N-contiguous extents off the 16-byte grid)
     const KernelEntry *fast_rs = nullptr;
@@ -915,7 +921,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     bool pk_tr = false;
     int64_t pk_ld_a = 0, pk_ld_b = 0, pk_off_b = 0, pk_bytes = 0, pk_kpad = 0;
     // (one batch mode only: the copies lay products out along one stride)
-    if (ft && want_fast && K >= 128 / eab && !diag_a && !diag_b && !staged && batch2 <= 1) {
+    if (ft && (want_fast || want128) && K >= 128 / eab && !diag_a && !diag_b && !staged && batch2 <= 1) {
         // the copies hold K rounded up to whole slabs, zero past K: when both operands are
         // copied the kernel runs on that K and needs no guarded tail slab
         const int64_t slab = 128 / eab;
@@ -943,7 +949,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         // large enough to repay the copy (GEMM_ALGO_FAST_KMAJOR: always; GEMM_ALGO_FAST: never)
         // (the 128x128 tiles run the 16x16 schedule on this layout in place)
         if (pk_tr && !need_a && (algo == GEMM_ALGO_FAST_KMAJOR ||
-                                 (algo == GEMM_ALGO_AUTO && !fast128 && kmajor_pays(M, N, K, eab))))
+                                 (algo == GEMM_ALGO_AUTO && !fast128 && !want128 && kmajor_pays(M, N, K, eab))))
             pk_want = 1;
         // the copies obey the 32-bit offset limit of the kernels; the copy grid (workgroups of
         // 4 rows x 1 KiB) fits 31 bits
@@ -953,8 +959,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if (one_a < lim && one_b < lim && blocks(rows_a, pk_ld_a, na) + blocks(rows_b, pk_ld_b, nbb) < lim) {
             pk_off_b = (na * one_a + 255) / 256 * 256;
             pk_bytes = pk_off_b + nbb * one_b;
-            fast_pk = ft(op_a, op_b, 0);
-            if (pk_tr) fast_pk_tr = ft(GEMM_OP_N, op_b, 0);
+            fast_pk = want128 ? f128t(op_a, op_b) : ft(op_a, op_b, 0);
+            if (pk_tr) fast_pk_tr = want128 ? f128t(GEMM_OP_N, op_b) : ft(GEMM_OP_N, op_b, 0);
         } else {
             pk_need = pk_want = 0;
             pk_tr = false;
@@ -1014,7 +1020,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if (blocks < lim && gemm_plan_create_desc(&rp, &r) == GEMM_STATUS_SUCCESS) {
             // (a real product small enough that only the 128-wide tiles would take it keeps
             // the complex kernel: the rewrite pass would cost more than it saves)
-            if ((rp->fast && !rp->fast_is_skinny && rp->fast->bm == 256) || rp->fast_pk || rp->fast_rs) {
+            if ((rp->fast && !rp->fast_is_skinny && rp->fast->bm == 256) || (rp->fast_pk && rp->fast_pk->bm == 256) ||
+                rp->fast_rs) {
                 cx = rp;
                 const int64_t bytes_a = op_a == GEMM_OP_T ? na * 2 * K * cx_ld_a * 2 : 0;
                 cx_off_b = (bytes_a + 255) / 256 * 256;
@@ -1100,7 +1107,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
                                                (desc->transform_b ? 2 : 0)) : 0;
     const bool shows_pk = pk_shown != 0;
     const bool shows_tr = pk_tr && (pk_shown & 1);
-    const KernelEntry *shown = shows_tr ? fast_pk_tr : fast ? fast : shows_pk ? fast_pk : fast_rs ? fast_rs : k;
+    const KernelEntry *shown = shows_tr ? fast_pk_tr : fast && !(shows_pk && fast_pk->bm != fast->bm) ? fast
+                               : shows_pk ? fast_pk : fast_rs ? fast_rs : k;
     p->tiles_m = skinny ? p->ksplit : (int)((M + shown->bm - 1) / shown->bm);
     p->tiles_n = (int)((N + shown->bn - 1) / shown->bn);
     p->group_m = 8;
