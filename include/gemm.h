@@ -192,8 +192,9 @@ typedef struct gemm_plan *gemm_plan_t;
  * stride_a / stride_b moves its vector); algo pins the kernel route (see gemm_algo_t;
  * GEMM_ALGO_AUTO for the plan's own choice) and tile the workgroup tile of the general kernel
  * (256, 128 or 64; 0 for the plan's own choice; 256 also selects the fast kernel where it
- * applies, and 128 with GEMM_ALGO_AUTO or FAST its 128 x 128 tiles for 16-bit inputs whose
- * operands it reads in place; the plan's own choice takes those for mid-size products); batch2 and the stride2 fields add a second batch mode (0 or 1: none): the launch
+ * applies, and 128 with GEMM_ALGO_AUTO or FAST its 128 x 128 tiles for 16-bit and int8 inputs,
+ * read in place or from the aligned copies; the plan's own choice takes those for mid-size
+ * products); batch2 and the stride2 fields add a second batch mode (0 or 1: none): the launch
  * computes batch x batch2 products, product (b1, b2) reading and writing every operand moved by
  * b1 * stride + b2 * stride2 elements (a zero stride broadcasts the operand along that mode),
  * the index map of a tensor contraction whose batch index has two modes with their own
