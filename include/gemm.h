@@ -40,7 +40,8 @@
  * The first run of a skinny split-K plan ("gemm_skinny... ksplit S") must not be captured into a
  * graph (later runs may be); the first run of a fast-kernel split-K plan inside a capture runs
  * unsplit.  A split run enqueues the partial products and a finishing kernel.
- * A large 16- or 8-bit plan whose operand rows are off the 16-byte grid (an odd leading
+ * A 16- or 8-bit plan on the fast kernel (large and mid-size products) whose operand rows are
+ * off the 16-byte grid (an odd leading
  * dimension or batch stride, an unaligned pointer at run time, or an M/N-contiguous row length
  * that is not a multiple of 16 bytes), or with a load transform on op(A) or op(B), first copies
  * those operands into aligned, zero-padded rows of a workspace it owns (about the size of the
@@ -157,8 +158,8 @@ typedef enum { GEMM_OPERAND_DENSE = 0, GEMM_OPERAND_DIAGONAL = 1 } gemm_operand_
  * layouts (the rule is described by gemm_plan_describe's text); the others pin a route, for
  * comparisons and tests, and fall back to the general kernel where the pinned route's
  * preconditions do not hold:
- *   FAST         the 256x256 fast kernel (16- and 8-bit inputs), with its K split when the
- *                plan's rule asks for one;
+ *   FAST         the fast kernel (16- and 8-bit inputs; 256x256 tiles, 128x128 with a tile of
+ *                128), with its K split when the plan's rule asks for one;
  *   FAST_STAGED  the fast kernel, reading operands that are off the 16-byte grid in place
  *                through registers instead of copying them first;
  *   GENERAL      the general tiled kernel, never the fast, skinny or split routes;
