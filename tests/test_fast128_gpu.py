@@ -2,6 +2,8 @@
 in place): every layout and 16-bit type pair on ragged shapes (M and N off the tile, a K tail),
 the epilogue variants, batches of one and two modes, and the plan's own choice of the variant,
 against the oracle through the C ABI.  Exact-integer inputs make every comparison bit-exact."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -225,3 +227,26 @@ def test_fast128_on_copies_chosen_and_noalloc():
     # (the sentinel past column N is a NaN)
     assert np.array_equal(outs[0], outs[1], equal_nan=True) and np.array_equal(outs[1], outs[2], equal_nan=True)
     check(p, x, outs[0], reference(p, x, threads=16), exact=True)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_fast128_on_copies_batched(shared, tile128):
+    # a batch whose operands are copied (odd leading dimensions): one copy per product, or one
+    # for all when the stride is 0
+    M, N, K = 264, 392, 256
+    lda, ldb, ldc = K + 1, K + 1, N + 3
+    p = synth.exact_integer_problem(M, N, K, "N", "T", "bf16", "f32", "bias", 1.0, 1.0,
+                                    key=(180, int(shared)), batch=3, stride_a=M * lda + 8,
+                                    stride_b=0 if shared else N * ldb + 5, stride_c=M * ldc + 16,
+                                    stride_bias=N)
+    p = replace(p, lda=lda, ldb=ldb, ldc=ldc)
+    x = synth.make_inputs(p)
+    Df, pl = run_batched(p, x)
+    d = pl.describe()
+    print(d, flush=True)
+    assert d.startswith("gemm_fast_128x128 ") and "repack AB" in d and "batch 3" in d, d
+    ref = reference_batched(p, x)
+    for b in range(p.batch):
+        off = batch_offset(p, b)
+        Db = Df[off: off + p.M * p.ldc].reshape(p.M, p.ldc)
+        check(p, x, Db, ref[b], exact=True)
