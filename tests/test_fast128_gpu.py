@@ -250,3 +250,41 @@ def test_fast128_on_copies_batched(shared, tile128):
         off = batch_offset(p, b)
         Db = Df[off: off + p.M * p.ldc].reshape(p.M, p.ldc)
         check(p, x, Db, ref[b], exact=True)
+
+
+# Seeded draws of shape, layout, type pair, leading-dimension padding per operand, pointer offset
+# and load transforms on the 128x128 tiles (read in place, or from the aligned copies): exact
+# inputs (small integers; int8 over its whole range with alpha 1), so every case must match the
+# oracle bit for bit.
+RANDOM_PAIRS = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("i8", "i32")]
+RANDOM_SCALARS = [(1.0, 0.0), (2.0, -1.0), (-0.5, 0.5), (1.0, 1.0)]
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_fast128_random_shapes_exact(case, tile128):
+    rng = np.random.default_rng(np.random.SeedSequence([181, case]))
+    ab, cd = RANDOM_PAIRS[case % len(RANDOM_PAIRS)]
+    lay = LAYOUTS[int(rng.integers(4))]
+    M, N = (int(v) for v in rng.integers(16, 700, size=2))
+    K = int(rng.integers(128 if ab == "i8" else 64, 700))
+    epi = ["none", "relu", "bias", "bias_relu"][int(rng.integers(4))]
+    xa, xb = ("relu" if rng.random() < 0.25 else "none" for _ in range(2))
+    if ab == "i8":
+        beta = float(rng.integers(2))
+        p = synth.Problem(M, N, K, lay[0], lay[1], "i8", "i32", epi, 1.0, beta,
+                          a_dist=("int", -128, 127), b_dist=("int", -128, 127), c_dist=("int", -1000, 1000),
+                          bias_dist=("int", -(1 << 20), 1 << 20), key=(182, case),
+                          transform_a=xa, transform_b=xb)
+    else:
+        alpha, beta = RANDOM_SCALARS[int(rng.integers(4))]
+        p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta, key=(182, case),
+                                        transform_a=xa, transform_b=xb)
+    pa, pb, pc = (int(v) for v in rng.integers(0, 10, size=3))
+    p = replace(p, lda=p.lda + pa, ldb=p.ldb + pb, ldc=p.ldc + pc)
+    offset = int(rng.integers(2))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x, offset=offset)
+    d = pl.describe()
+    print(p.label(), "lda", p.lda, "ldb", p.ldb, "ldc", p.ldc, "offset", offset, "->", d, flush=True)
+    assert d.startswith("gemm_fast_128x128 "), d
+    check(p, x, D, reference(p, x), exact=True)
