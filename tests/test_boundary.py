@@ -307,6 +307,13 @@ def test_fast128_tiles_chosen_for_mid_size_products():
         args.update(kw)
         d = tge.Plan(**args).describe()
         assert d.startswith("gemm_fast_128x128 ") and shows in d, (kw, d)
+    # below about 2^31 multiply-adds the copy costs more than the tiles gain: the general kernel
+    for kw in [dict(M=1024, N=1024, K=1024, lda=1025), dict(M=17, N=1, K=1161, op_a="T", lda=18),
+               dict(M=1024, N=1024, K=1024, transform_a="relu")]:
+        assert tge.Plan(**kw).describe().startswith("gemm_mfma_"), kw
+    # (pinned, the 128-wide tiles take the copies at any size)
+    d = tge.Plan(1024, 1024, 1024, lda=1025, algo="fast", tile=128).describe()
+    assert d.startswith("gemm_fast_128x128 ") and "repack A" in d, d
     # not for the general algorithm, or a long K that splits
     assert not tge.Plan(1024, 1024, 1024, lda=1025, algo="general").describe().startswith("gemm_fast")
     assert " ksplit " in tge.Plan(2048, 2048, 8192).describe()

@@ -719,3 +719,35 @@ def test_fast_k_split_full_size_points(lay):
     D, pl = run(p, x)
     assert "gemm_fast_256x256 " in pl.describe() and "ksplit 4" in pl.describe(), pl.describe()
     check_points(p, x, D)
+
+
+# ---- the plan's own choice over a wide range of sizes ------------------------------------------
+# Seeded draws: M and N log-uniform up to 4096, K up to 8192 (at most 2^33 multiply-adds), half
+# of them rounded up to whole 16-byte chunks and 128-deep slabs, a quarter with padded leading
+# dimensions, so that the automatic routes are met (general kernel, skinny kernel, 128-wide fast
+# tiles, the 256-wide tiles' K split, aligned copies): exact inputs, bit-exact against the oracle.
+@pytest.mark.parametrize("case", range(40))
+def test_auto_route_random_sizes_exact(case):
+    rng = np.random.default_rng(np.random.SeedSequence([183, case]))
+    pairs = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("i8", "i32")]
+    ab, cd = pairs[case % len(pairs)]
+    lay = LAYOUTS[int(rng.integers(4))]
+    while True:
+        M, N = (int(round(float(np.exp(rng.uniform(0.0, np.log(4096)))))) for _ in range(2))
+        K = int(round(float(np.exp(rng.uniform(0.0, np.log(8192))))))
+        if M * N * K <= 1 << 33:
+            break
+    if rng.random() < 0.5:
+        M, N, K = -(-M // 16) * 16, -(-N // 16) * 16, -(-K // 128) * 128
+    epi = EPIS[int(rng.integers(4))]
+    alpha, beta = SCALARS[int(rng.integers(4))]
+    p = _exact(M, N, K, lay, ab, cd, epi, alpha, beta, key=(184, case))
+    if rng.random() < 0.25:
+        pa, pb, pc = (int(v) for v in rng.integers(1, 10, size=3))
+        p = replace(p, lda=p.lda + pa, ldb=p.ldb + pb, ldc=p.ldc + pc)
+    offset = int(rng.integers(2))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x, offset=offset)
+    print(p.label(), "lda", p.lda, "ldb", p.ldb, "ldc", p.ldc, "offset", offset, "->", pl.describe(),
+          flush=True)
+    check(p, x, D, reference(p, x, threads=16), exact=True)

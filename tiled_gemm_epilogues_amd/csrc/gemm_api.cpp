@@ -288,6 +288,15 @@ static bool fast128_pays(int64_t M, int64_t N, int64_t nprod) {
     return t256 <= FAST128_MAX_T256;
 }
 
+// Whether the 128x128 tiles on aligned copies of the operands (an extra pass over them, one
+// more kernel) beat the general kernel reading them in place: from about 2^31 multiply-adds.
+// Measured (fp16 NN, odd leading dimensions, graph-timed; general -> copies and 128-wide tiles):
+// 1024^3 17.8 vs 18.6 us, 1280^3 26.9 -> 25.6, 1536^3 33.5 -> 27.9, 2048^3 50.6 -> 35.5.
+constexpr double COPY128_MIN_MACS = 2147483648.0;
+static bool copy128_pays(int64_t M, int64_t N, int64_t K, int64_t nprod) {
+    return (double)M * (double)N * (double)K * (double)(nprod > 1 ? nprod : 1) >= COPY128_MIN_MACS;
+}
+
 // Whether a short product (64 < M <= 256, below that the skinny kernel) takes the 128x128
 // tiles with K split rather than the 256x256 ones with their finer split or the 128x128 tiles
 // unsplit: from 64 slabs of K.  Measured (fp16 NN, graph-timed; 256-wide split -> 128-wide
@@ -901,11 +910,13 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         }
     }
     // the same choice for copies of operands the direct loads cannot read in place, or that
-    // carry a load transform (the copy applies it): the 128x128 tiles run on the copies
+    // carry a load transform (the copy applies it): the 128x128 tiles run on the copies, for
+    // products large enough to repay the copy
     const bool want128 = f128t && !diag_a && !diag_b && !ctable && algo != GEMM_ALGO_GENERAL && !split_s &&
                          !split128 &&
                          ((tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST)) ||
-                          (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod)));
+                          (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod) &&
+                           copy128_pays(M, N, K, nprod)));
     // the register-staged variant takes every layout the direct loads cannot (odd leading
     // dimensions or strides, unaligned pointers, M/N-contiguous extents off the 16-byte grid)
     const KernelEntry *fast_rs = nullptr;
