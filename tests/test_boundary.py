@@ -380,8 +380,16 @@ def test_fast_k_split_described():
     # few 256x256 tiles and K >= 4096: K cut into chunks of at least 16 slabs, tiles x S >= 128
     d = tge.Plan(2048, 2048, 8192, "N", "N").describe()
     assert "gemm_fast_256x256 " in d and "ksplit 4" in d, d
-    d = tge.Plan(1024, 1024, 8192, "N", "T", ab="bf16", cd="f32").describe()
-    assert "gemm_fast_256x256 " in d and "ksplit 8" in d, d
+    # fewer 128x128 tiles than CUs and at least 48 slabs: those tiles split K instead (about one
+    # workgroup per CU, chunks of at least 4 slabs)
+    for (M, N, K, lay, ab, cd, S) in [(1024, 1024, 8192, "NT", "bf16", "f32", 4), (512, 512, 8192, "NN", "f16", "f16", 16),
+                                      (768, 768, 3072, "TN", "f16", "f16", 8), (288, 416, 7168, "NN", "f16", "f32", 16),
+                                      (512, 512, 6144, "NN", "i8", "i32", 12)]:
+        d = tge.Plan(M, N, K, lay[0], lay[1], ab=ab, cd=cd).describe()
+        assert d.startswith("gemm_fast_128x128 ") and f"ksplit {S}" in d, d
+    # 32 slabs: unsplit
+    d = tge.Plan(640, 640, 2048).describe()
+    assert d.startswith("gemm_fast_128x128 ") and "ksplit" not in d, d
     # 2048^3 (K = 2048) stays on the general kernel; enough tiles: no split
     assert "ksplit" not in tge.Plan(2048, 2048, 2048, "N", "N").describe()
     assert "ksplit" not in tge.Plan(8192, 8192, 8192, "N", "N").describe()

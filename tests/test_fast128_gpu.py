@@ -129,7 +129,10 @@ def test_fast128_noalloc_and_unaligned_pointer(tile128):
 SPLITS = [((128, 1024, 1024), "NN", "f16", "f16", "bias_relu", 1.0, 0.0),
           ((200, 520, 2048), "NT", "bf16", "f32", "bias", 2.0, -1.0),
           ((256, 392, 1536), "TN", "f16", "f32", "relu", 1.0, 1.0),
-          ((96, 264, 4096), "TT", "bf16", "bf16", "bias_relu", 0.5, 0.0)]
+          ((96, 264, 4096), "TT", "bf16", "bf16", "bias_relu", 0.5, 0.0),
+          ((520, 520, 3072), "NN", "f16", "f16", "bias", 2.0, 0.5),
+          ((1000, 776, 4096), "TN", "bf16", "f32", "bias_relu", 1.0, -1.0),
+          ((2048, 2048, 1024), "NT", "f16", "f32", "relu", 1.0, 0.0)]
 
 
 @pytest.mark.parametrize("case", range(len(SPLITS)))
@@ -288,3 +291,18 @@ def test_fast128_random_shapes_exact(case, tile128):
     print(p.label(), "lda", p.lda, "ldb", p.ldb, "ldc", p.ldc, "offset", offset, "->", d, flush=True)
     assert d.startswith("gemm_fast_128x128 "), d
     check(p, x, D, reference(p, x), exact=True)
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_fast128_split_chosen_exact(case):
+    # the plan's own choice: fewer 128x128 tiles than CUs and at least 48 slabs of K
+    (M, N, K), lay, ab, cd, epi, alpha, beta = [((600, 600, 4096), "NT", "f16", "f16", "bias_relu", 1.0, 0.0),
+                                                ((768, 768, 3072), "TN", "bf16", "f32", "bias", 1.0, 1.0),
+                                                ((384, 1040, 8192), "TT", "f16", "f32", "relu", 0.5, -0.5)][case]
+    p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta, key=(185, case))
+    x = synth.make_inputs(p)
+    D, pl = run(p, x)
+    d = pl.describe()
+    print(f"{p.label()} -> {d}", flush=True)
+    assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
+    check(p, x, D, reference(p, x, threads=16), exact=True)

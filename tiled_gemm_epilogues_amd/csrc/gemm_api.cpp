@@ -270,7 +270,7 @@ static gemm_status_t scratch_address(uint8_t **out) {
 constexpr int64_t KMAJOR_MIN_N_BYTES = 6144;
 constexpr int64_t FAST128_MAX_T256 = 128;
 constexpr int64_t SHORT_M_MIN_CHUNK = 4;
-constexpr int64_t SPLIT128_MIN_SLABS = 64;
+constexpr int64_t SPLIT128_MIN_SLABS = 48;
 static bool kmajor_pays(int64_t M, int64_t N, int64_t K, int eab) {
     (void)M; (void)K;
     return N * eab >= KMAJOR_MIN_N_BYTES;
@@ -297,13 +297,18 @@ static bool copy128_pays(int64_t M, int64_t N, int64_t K, int64_t nprod) {
     return (double)M * (double)N * (double)K * (double)(nprod > 1 ? nprod : 1) >= COPY128_MIN_MACS;
 }
 
-// Whether a short product (64 < M <= 256, below that the skinny kernel) takes the 128x128
-// tiles with K split rather than the 256x256 ones with their finer split or the 128x128 tiles
-// unsplit: from 64 slabs of K.  Measured (fp16 NN, graph-timed; 256-wide split -> 128-wide
-// split): 96 x 4096 x 4096 27.3 -> 17.0 us, 128 x 4096 x 4096 28.3 -> 18.2, 256 x 4096 x 4096
-// 35.8 -> 23.0, 128 x 8192 x 8192 45.1 -> 36.2, 256 x 14336 x 4096 53.8 -> 46.8, 256 x 1024 x
-// 4096 (unsplit 128-wide) 25.0 -> 18.5; at 32 slabs the unsplit 128-wide tiles stay faster
-// (128 x 4096 x 2048 15.0 vs 18.8 us).
+// Whether a product with fewer 128x128 tiles than CUs (M > 64, below that the skinny kernel)
+// takes those tiles with K split rather than the 256x256 ones with their finer split or the
+// 128x128 tiles unsplit: from 48 slabs of K.  Measured (fp16 NN unless noted, graph-timed;
+// 256-wide split -> 128-wide split): 96 x 4096 x 4096 27.3 -> 17.0 us, 128 x 4096 x 4096
+// 28.3 -> 18.2, 256 x 4096 x 4096 35.8 -> 23.0, 128 x 8192 x 8192 45.1 -> 36.2, 256 x 14336 x
+// 4096 53.8 -> 46.8, 1024^2 x 8192 39.4 -> 31.5, 1024 x 2048 x 8192 55.1 -> 51.9; (unsplit
+// 128-wide -> split) 256 x 1024 x 4096 25.0 -> 18.5, 512^2 x 8192 71.5 -> 21.2, 288 x 416 x
+// 7168 72.6 -> 16.5, 640^2 x 4096 41.8 -> 18.5, 1024^2 x 4096 41.1 -> 23.8, 2048 x 1024 x 4096
+// 40.1 -> 32.8, 768^2 x 3072 32.2 -> 22.3, 1024^2 x 3072 32.8 -> 23.5, bf16 -> fp32 1024^2 x
+// 8192 73.2 -> 32.2, int8 512^2 x 6144 20.1 -> 16.6; 256 x 2048 x 3072 is the one 48-slab
+// case measured slower (19.9 vs 20.5 us).  At 32 slabs the results are mixed (128 x 4096 x
+// 2048 15.0 vs 18.8 us, 640^2 x 2048 14.7 vs 16.2; 1024^2 x 2048 23.0 vs 21.3): unsplit.
 static bool split128_pays(int64_t M, int64_t N, int64_t slabs) {
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     return t128 < 256 && slabs >= SPLIT128_MIN_SLABS && M > 64;
@@ -843,7 +848,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if ((ab_type == GEMM_F16 || ab_type == GEMM_BF16 || ab_type == GEMM_I8) && nprod <= 1 &&
         !ctable && !diag_a && !diag_b && !desc->transform_a && !desc->transform_b &&
         K % slab_k == 0 && !staged &&
-        algo != GEMM_ALGO_NOSPLIT && algo != GEMM_ALGO_GENERAL && algo != GEMM_ALGO_SKINNY) {
+        algo != GEMM_ALGO_NOSPLIT && algo != GEMM_ALGO_GENERAL && algo != GEMM_ALGO_SKINNY &&
+        !(tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST))) {
         const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t slabs = K / slab_k;
         int64_t sp = tiles > 0 ? 256 / tiles : 0;
@@ -888,19 +894,20 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
          (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod))))
         fast128 = f128t(op_a, op_b);
     if (fast128) fast = fast128;
-    // short products (M <= 256) on the 128x128 tiles with K split over workgroups: t128 tiles
-    // times S chunks (whole slabs, at least 4 each) of about one workgroup per CU; the partial
-    // sums are S * M * N fp32 values (a quarter of those of the 256-wide tiles' 16-way split)
+    // products with fewer 128x128 tiles than CUs and a long K on those tiles with K split over
+    // workgroups: t128 tiles times S chunks (whole slabs, at least 4 each) of about one
+    // workgroup per CU; the partial sums are S * M * N fp32 values (int32 for int8)
     int split128 = 0;
     const Fast128Lookup f128p = fast128_table(ab_type, part_cd);
-    if (f128t && f128p && direct_ok && M <= 256 && nprod <= 1 && K % slab_k == 0 &&
+    const bool pin_split128 = tile == 128 && algo == GEMM_ALGO_SPLIT;
+    if (f128t && f128p && direct_ok && nprod <= 1 && K % slab_k == 0 &&
         !desc->transform_a && !desc->transform_b && !diag_a && !diag_b && !ctable &&
         finish_table(ab_type, cd_type) &&
-        ((tile == 128 && algo == GEMM_ALGO_SPLIT) ||
-         (tile == 0 && algo == GEMM_ALGO_AUTO && split128_pays(M, N, K / slab_k)))) {
+        (pin_split128 || (tile == 0 && algo == GEMM_ALGO_AUTO && split128_pays(M, N, K / slab_k)))) {
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         const int64_t slabs = K / slab_k;
         int64_t sp = (256 + t128 - 1) / t128;
+        if (pin_split128 && sp < 2) sp = 2;
         if (sp > slabs / SHORT_M_MIN_CHUNK) sp = slabs / SHORT_M_MIN_CHUNK;
         while (sp > 1 && slabs % sp) --sp;
         if (sp >= 2) {
