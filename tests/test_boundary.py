@@ -387,6 +387,9 @@ def test_fast_k_split_described():
                                       (512, 512, 6144, "NN", "i8", "i32", 12)]:
         d = tge.Plan(M, N, K, lay[0], lay[1], ab=ab, cd=cd).describe()
         assert d.startswith("gemm_fast_128x128 ") and f"ksplit {S}" in d, d
+    # empty products with the split pinned plan without a split (no launch)
+    for (M, N) in [(0, 512), (512, 0)]:
+        assert "ksplit" not in tge.Plan(M, N, 4096, algo="split", tile=128).describe()
     # 32 slabs: unsplit
     d = tge.Plan(640, 640, 2048).describe()
     assert d.startswith("gemm_fast_128x128 ") and "ksplit" not in d, d

@@ -306,3 +306,35 @@ def test_fast128_split_chosen_exact(case):
     print(f"{p.label()} -> {d}", flush=True)
     assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
     check(p, x, D, reference(p, x, threads=16), exact=True)
+
+
+# (M, N, K, layout, ab, cd, epilogue, alpha, beta, ld_pad, pointer offset, what the description
+# must show): the K split of the 128x128 tiles on aligned copies (odd leading dimensions, M/N
+# off the 16-byte grid, a pointer off it at run time), A stored transposed copied K-major
+SPLIT_COPIES = [((512, 520, 3072), "NN", "f16", "f16", "bias_relu", 1.0, 0.0, 1, 0, "repack AB"),
+                ((300, 264, 6144), "NT", "bf16", "f32", "bias", 2.0, -1.0, 3, 0, "repack AB"),
+                ((768, 770, 3072), "TN", "f16", "f16", "relu", 1.0, 1.0, 0, 0, "repack B"),
+                ((770, 768, 3072), "TN", "f16", "f32", "bias", 0.5, 0.5, 0, 0, "repack A (A to K-major)"),
+                ((600, 528, 6144), "NN", "i8", "i32", "bias", 1.0, 1.0, 1, 0, "repack AB"),
+                ((768, 768, 3072), "TN", "bf16", "bf16", "bias_relu", 1.0, 0.0, 0, 1, ""),
+                ((520, 600, 4096), "NT", "f16", "f32", "none", 1.0, 0.0, 0, 1, "")]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_COPIES)))
+def test_fast128_split_on_copies_exact(case):
+    (M, N, K), lay, ab, cd, epi, alpha, beta, pad, offset, shows = SPLIT_COPIES[case]
+    if ab == "i8":
+        p = synth.Problem(M, N, K, lay[0], lay[1], "i8", "i32", epi, 1.0, beta,
+                          a_dist=("int", -128, 127), b_dist=("int", -128, 127), c_dist=("int", -1000, 1000),
+                          bias_dist=("int", -(1 << 20), 1 << 20), key=(186, case))
+        if pad:
+            p = replace(p, lda=p.lda + pad, ldb=p.ldb + pad, ldc=p.ldc + pad)
+    else:
+        p = synth.exact_integer_problem(M, N, K, lay[0], lay[1], ab, cd, epi, alpha, beta, key=(186, case),
+                                        ld_pad=pad)
+    x = synth.make_inputs(p)
+    D, pl = run(p, x, offset=offset)
+    d = pl.describe()
+    print(f"{p.label()} offset {offset} -> {d}", flush=True)
+    assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d and shows in d, d
+    check(p, x, D, reference(p, x, threads=16), exact=True)

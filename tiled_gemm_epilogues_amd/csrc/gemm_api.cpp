@@ -43,6 +43,7 @@ struct gemm_plan {
     const KernelEntry *fast_pk_tr;   // direct-load kernel on a transposed copy of A
     const KernelEntry *fast_part_tr; // its K-split variant (nullptr: no split)
     const KernelEntry *fast_part128; // K split of the 128x128 tiles (nullptr: none)
+    const KernelEntry *fast_part128_tr; // the same on a transposed copy of A
     int64_t pk_ld_a, pk_ld_b;        // leading dimensions of the copies (whole 128-byte lines)
     int64_t pk_kpad;                 // K rounded up to whole slabs: the copies are zero there
     int64_t pk_off_b, pk_bytes;      // byte offset of B's copy in the workspace, total size
@@ -524,7 +525,8 @@ static gemm_status_t run_impl(gemm_plan_t p, const void *A, const void *B, const
     void *spw = nullptr;
     const bool k_tr = p->fast_pk_tr && k == p->fast_pk_tr;   // A from its transposed copy
     // the partial products' kernel: the same tiles and layout as the kernel chosen above
-    const KernelEntry *part_k = k->bm == 128 ? p->fast_part128 : k_tr ? p->fast_part_tr : p->fast_part;
+    const KernelEntry *part_k = k->bm == 128 ? (k_tr ? p->fast_part128_tr : p->fast_part128)
+                                             : k_tr ? p->fast_part_tr : p->fast_part;
     if ((k == p->fast || k == p->fast_pk || k_tr) && !sk && part_k) {
         const gemm_status_t st = workspace(sc, reinterpret_cast<void **>(&p->ws), &p->ws_dev, split_bytes, hs, &spw);
         if (sc && st != GEMM_STATUS_SUCCESS) return st;
@@ -897,10 +899,12 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // products with fewer 128x128 tiles than CUs and a long K on those tiles with K split over
     // workgroups: t128 tiles times S chunks (whole slabs, at least 4 each) of about one
     // workgroup per CU; the partial sums are S * M * N fp32 values (int32 for int8)
-    int split128 = 0;
+    // (operands the direct loads cannot read in place: the same split on their aligned copies,
+    // settled with the copies below)
+    int split128 = 0, split128_copy = 0;
     const Fast128Lookup f128p = fast128_table(ab_type, part_cd);
     const bool pin_split128 = tile == 128 && algo == GEMM_ALGO_SPLIT;
-    if (f128t && f128p && direct_ok && nprod <= 1 && K % slab_k == 0 &&
+    if (f128t && f128p && M > 0 && N > 0 && K > 0 && nprod <= 1 && K % slab_k == 0 &&
         !desc->transform_a && !desc->transform_b && !diag_a && !diag_b && !ctable &&
         finish_table(ab_type, cd_type) &&
         (pin_split128 || (tile == 0 && algo == GEMM_ALGO_AUTO && split128_pays(M, N, K / slab_k)))) {
@@ -910,20 +914,23 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         if (pin_split128 && sp < 2) sp = 2;
         if (sp > slabs / SHORT_M_MIN_CHUNK) sp = slabs / SHORT_M_MIN_CHUNK;
         while (sp > 1 && slabs % sp) --sp;
-        if (sp >= 2) {
+        if (sp >= 2 && direct_ok) {
             split128 = (int)sp;
             fast = fast128 = f128t(op_a, op_b);
             split_s = 0;
+        } else if (sp >= 2) {
+            split128_copy = (int)sp;
         }
     }
-    // the same choice for copies of operands the direct loads cannot read in place, or that
-    // carry a load transform (the copy applies it): the 128x128 tiles run on the copies, for
+    // the same choice for copies of operands the direct loads cannot read in place (also those
+    // of a pointer found off the 16-byte grid at run time), or that carry a load transform (the
+    // copy applies it): the 128x128 tiles run on the copies, with their K split, or unsplit for
     // products large enough to repay the copy
-    const bool want128 = f128t && !diag_a && !diag_b && !ctable && algo != GEMM_ALGO_GENERAL && !split_s &&
-                         !split128 &&
-                         ((tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST)) ||
-                          (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod) &&
-                           copy128_pays(M, N, K, nprod)));
+    const bool want128 = f128t && !diag_a && !diag_b && !ctable && algo != GEMM_ALGO_GENERAL &&
+                         (split128 || split128_copy ||
+                          (!split_s && ((tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST)) ||
+                                        (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod) &&
+                                         copy128_pays(M, N, K, nprod)))));
     // the register-staged variant takes every layout the direct loads cannot (odd leading
     // dimensions or strides, unaligned pointers, M/N-contiguous extents off the 16-byte grid)
     const KernelEntry *fast_rs = nullptr;
@@ -979,6 +986,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
             pk_bytes = pk_off_b + nbb * one_b;
             fast_pk = want128 ? f128t(op_a, op_b) : ft(op_a, op_b, 0);
             if (pk_tr) fast_pk_tr = want128 ? f128t(GEMM_OP_N, op_b) : ft(GEMM_OP_N, op_b, 0);
+            if (split128_copy && want128) {
+                split128 = split128_copy;
+                split_s = 0;
+            }
         } else {
             pk_need = pk_want = 0;
             pk_tr = false;
@@ -1074,6 +1085,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->fast_pk_tr = fast_pk_tr;
     p->fast_part_tr = nullptr;
     p->fast_part128 = nullptr;
+    p->fast_part128_tr = nullptr;
     p->pk_ld_a = pk_ld_a; p->pk_ld_b = pk_ld_b;
     p->pk_kpad = pk_kpad;
     p->pk_off_b = pk_off_b; p->pk_bytes = pk_bytes;
@@ -1115,6 +1127,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     }
     if (split128 && !skinny) {
         p->fast_part128 = f128p(op_a, op_b);
+        if (pk_tr) p->fast_part128_tr = f128p(GEMM_OP_N, op_b);
         p->finish = finish_table(ab_type, cd_type);
         p->ksplit = split128;
     }
