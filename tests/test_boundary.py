@@ -411,14 +411,20 @@ def test_fast_k_split_described():
     d = tge.Plan(2048, 3072, 8192, "N", "N", ab="i8", cd="i32").describe()
     assert "gemm_fast_256x256 " in d and "ksplit 2" in d, d
     assert "ksplit" not in tge.Plan(2048, 2048, 4096, "N", "N", ab="i8", cd="i32").describe()
-    # short int8 products (no skinny kernel): chunks down to 2 slabs
+    # short int8 products (no skinny kernel): the 128x128 tiles split K from 8 slabs
     d = tge.Plan(16, 4096, 4096, "N", "N", ab="i8", cd="i32").describe()
-    assert "gemm_fast_256x256 " in d and "ksplit 16" in d, d
+    assert d.startswith("gemm_fast_128x128 ") and "ksplit 8" in d, d
     d = tge.Plan(64, 8192, 4096, "N", "T", ab="i8", cd="i32").describe()
-    assert "gemm_fast_256x256 " in d and "ksplit 8" in d, d
+    assert d.startswith("gemm_fast_128x128 ") and "ksplit 4" in d, d
+    d = tge.Plan(16, 4096, 1024, "N", "N", ab="i8", cd="i32").describe()
+    assert d.startswith("gemm_fast_128x128 ") and "ksplit 2" in d, d
+    assert "ksplit" not in tge.Plan(16, 4096, 512, "N", "N", ab="i8", cd="i32").describe()
     # ... and short 16-bit products with A transposed (the skinny kernel needs A not transposed)
     d = tge.Plan(16, 4096, 4096, "T", "N").describe()
-    assert "gemm_fast_256x256 " in d and "ksplit 16" in d, d
+    assert d.startswith("gemm_fast_128x128 ") and "ksplit 8" in d, d
+    # the 256-wide tiles' split of short products, pinned: chunks down to 2 slabs
+    d = tge.Plan(16, 4096, 4096, "N", "N", ab="i8", cd="i32", algo="split").describe()
+    assert "gemm_fast_256x256 " in d and " ksplit " in d, d
     assert "gemm_skinny" in tge.Plan(16, 4096, 4096, "N", "N").describe()
     # an operand off the 16-byte grid is copied first, then split as well
     d = tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
@@ -470,7 +476,7 @@ def test_short_products_split_only_from_eight_slabs():
         assert "ksplit" not in d, d
     for shape, ab in [((32, 1024, 1024), "f16"), ((16, 4096, 1024), "i8"), ((64, 1024, 512), "f16")]:
         d = tge.Plan(*shape, "T", "N", ab=ab, cd="i32" if ab == "i8" else "f16").describe()
-        assert "gemm_fast_256x256 " in d and " ksplit " in d, d
+        assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
 
 
 def test_empty_skinny_shapes_plan_and_run_without_launch():

@@ -639,8 +639,8 @@ def test_fast_k_split_int8_exact(lay, shape, monkeypatch):
                                    (33, 4096, 8192)])
 @pytest.mark.parametrize("lay", LAYOUTS)
 def test_fast_k_split_short_int8_exact(lay, shape):
-    # the plan's own choice for short int8 products: the fast kernel with K split into chunks
-    # of 2 slabs or more, int32 partial sums, the integer finishing kernel; bias, beta = 1, ReLU
+    # the plan's own choice for short int8 products: the 128x128 tiles with K split into chunks
+    # of 4 slabs or more, int32 partial sums, the integer finishing kernel; bias, beta = 1, ReLU
     M, N, K = shape
     i = LAYOUTS.index(lay) + 4 * [(16, 4096, 4096), (5, 1000, 2048), (64, 520, 1024),
                                   (33, 4096, 8192)].index(shape)
@@ -648,7 +648,7 @@ def test_fast_k_split_short_int8_exact(lay, shape):
     x = synth.make_inputs(p)
     print(p.label(), flush=True)
     D, pl = run(p, x)
-    assert "gemm_fast_256x256 " in pl.describe() and " ksplit " in pl.describe() + " ", \
+    assert pl.describe().startswith("gemm_fast_128x128 ") and " ksplit " in pl.describe() + " ", \
         pl.describe()
     check(p, x, D, reference(p, x), exact=True)
 
@@ -657,15 +657,15 @@ def test_fast_k_split_short_int8_exact(lay, shape):
 @pytest.mark.parametrize("lb", ["N", "T"])
 @pytest.mark.parametrize("ab,cd", [("f16", "f16"), ("bf16", "f32")])
 def test_fast_k_split_short_transposed_a_exact(ab, cd, lb, shape):
-    # short 16-bit products with A transposed (no skinny kernel): the plan's K split into chunks
-    # of 2 slabs or more
+    # short 16-bit products with A transposed (no skinny kernel): the plan's K split over the
+    # 128x128 tiles
     M, N, K = shape
     i = (lb == "T") + 2 * [(16, 4096, 4096), (5, 1000, 2048), (64, 520, 1024)].index(shape)
     p = _exact(M, N, K, "T" + lb, ab, cd, EPIS[i % 4], *SCALARS[i % 4], key=(132, i))
     x = synth.make_inputs(p)
     print(p.label(), flush=True)
     D, pl = run(p, x)
-    assert "gemm_fast_256x256 " in pl.describe() and " ksplit " in pl.describe(), pl.describe()
+    assert pl.describe().startswith("gemm_fast_128x128 ") and " ksplit " in pl.describe(), pl.describe()
     check(p, x, D, reference(p, x), exact=True)
 
 

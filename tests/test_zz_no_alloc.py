@@ -63,7 +63,7 @@ ROUTES = {
     "fast128_split": (((2048, 2048, 8192), "NN", "f16", "f16"), ((1024, 1024, 8192), "NT", "bf16", "f32"),
                       "gemm_fast_128x128", " ksplit "),
     "short_int8_split": (((64, 8192, 4096), "NT", "i8", "i32"), ((16, 4096, 2048), "NN", "i8", "i32"),
-                         "gemm_fast_256x256", " ksplit "),
+                         "gemm_fast_128x128", " ksplit "),
     "repack": (((4095, 3073, 2047), "NN", "bf16", "f32"), ((1001, 777, 513), "TN", "bf16", "f32"),
                "gemm_fast_256x256", "repack"),
     "no_scratch": (((1024, 1024, 1024), "NN", "f16", "f16"), ((512, 384, 256), "TT", "f16", "f16"),

@@ -298,8 +298,8 @@ static bool copy128_pays(int64_t M, int64_t N, int64_t K, int64_t nprod) {
     return (double)M * (double)N * (double)K * (double)(nprod > 1 ? nprod : 1) >= COPY128_MIN_MACS;
 }
 
-// Whether a product with fewer 128x128 tiles than CUs (M > 64, below that the skinny kernel)
-// takes those tiles with K split rather than the 256x256 ones with their finer split or the
+// Whether a product with fewer 128x128 tiles than CUs (M > 64, and shorter ones the skinny
+// kernel cannot take: below) takes those tiles with K split rather than the 256x256 ones with their finer split or the
 // 128x128 tiles unsplit: from 48 slabs of K.  Measured (fp16 NN unless noted, graph-timed;
 // 256-wide split -> 128-wide split): 96 x 4096 x 4096 27.3 -> 17.0 us, 128 x 4096 x 4096
 // 28.3 -> 18.2, 256 x 4096 x 4096 35.8 -> 23.0, 128 x 8192 x 8192 45.1 -> 36.2, 256 x 14336 x
@@ -314,9 +314,15 @@ static bool copy128_pays(int64_t M, int64_t N, int64_t K, int64_t nprod) {
 // 4096 56.7 -> 50.5 us (256-wide split 4 ways), bf16 -> fp32 55.0 -> 48.3, int8 2048^2 x 8192
 // 56.0 -> 49.2; 2048^2 x 8192 76.5 vs 76.1 (even); at 48 slabs unsplit (2048^2 x 3072 37.2 vs
 // 41.3), and with more tiles the 256-wide tiles stay ahead (2048 x 3072 x 4096 65.6 vs 74.5).
-static bool split128_pays(int64_t M, int64_t N, int64_t slabs) {
+// Short products (M <= 64) the skinny kernel cannot take (int8 inputs, or A transposed) split
+// from 8 slabs, as they did on the 256-wide tiles: 256-wide split -> 128-wide split, int8 16 x
+// 4096 x 4096 17.1 -> 10.2 us, 64 x 8192 x 4096 NT 24.9 -> 16.0, 32 x 4096 x 8192 NT 21.2 ->
+// 13.7, 16 x 4096 x 1024 14.1 -> 8.8; fp16 16 x 4096 x 4096 TN 26.7 -> 13.8, 32 x 1024 x 1024
+// TN 18.6 -> 8.6; bf16 -> fp32 64 x 8192 x 4096 TT 30.4 -> 21.1.
+static bool split128_pays(int64_t M, int64_t N, int64_t slabs, bool skinny_cannot) {
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    return M > 64 && ((t128 < 256 && slabs >= SPLIT128_MIN_SLABS) || (t128 == 256 && slabs >= 64));
+    if (M <= 64) return skinny_cannot && t128 < 256 && slabs >= 8;
+    return (t128 < 256 && slabs >= SPLIT128_MIN_SLABS) || (t128 == 256 && slabs >= 64);
 }
 
 struct Scratch {
@@ -900,8 +906,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
          (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod))))
         fast128 = f128t(op_a, op_b);
     if (fast128) fast = fast128;
-    // products with fewer 128x128 tiles than CUs and a long K on those tiles with K split over
-    // workgroups: t128 tiles times S chunks (whole slabs, at least 4 each) of about one
+    // products with fewer 128x128 tiles than CUs and a long K (short ones the skinny kernel
+    // cannot take from 8 slabs) on those tiles with K split over workgroups: t128 tiles times S chunks (whole slabs, at least 4 each) of about one
     // workgroup per CU; the partial sums are S * M * N fp32 values (int32 for int8)
     // (operands the direct loads cannot read in place: the same split on their aligned copies,
     // settled with the copies below)
@@ -911,7 +917,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (f128t && f128p && M > 0 && N > 0 && K > 0 && nprod <= 1 && K % slab_k == 0 &&
         !desc->transform_a && !desc->transform_b && !diag_a && !diag_b && !ctable &&
         finish_table(ab_type, cd_type) &&
-        (pin_split128 || (tile == 0 && algo == GEMM_ALGO_AUTO && split128_pays(M, N, K / slab_k)))) {
+        (pin_split128 || (tile == 0 && algo == GEMM_ALGO_AUTO &&
+                          split128_pays(M, N, K / slab_k, ab_type == GEMM_I8 || op_a == GEMM_OP_T)))) {
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         const int64_t slabs = K / slab_k;
         int64_t sp = (256 + t128 - 1) / t128;
