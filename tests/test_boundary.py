@@ -383,12 +383,15 @@ def test_fast_k_split_described():
     assert "gemm_fast_256x256 " in d and "ksplit 2" in d, d
     d = tge.Plan(2560, 2560, 8192, "N", "T").describe()
     assert "gemm_fast_256x256 " in d and "ksplit 2" in d, d
-    # one 128x128 tile per CU and 64 slabs or more: those tiles split in two
-    for (M, N, K, ab, cd) in [(2048, 2048, 4096, "f16", "f16"), (2048, 2048, 8192, "f16", "f16"),
-                              (4096, 1024, 4096, "bf16", "f32"), (2048, 2048, 8192, "i8", "i32")]:
+    # one 128x128 tile per CU and 64 to 127 slabs: those tiles split in two
+    for (M, N, K, ab, cd) in [(2048, 2048, 4096, "f16", "f16"), (4096, 1024, 4096, "bf16", "f32"),
+                              (2048, 2048, 8192, "i8", "i32")]:
         d = tge.Plan(M, N, K, ab=ab, cd=cd).describe()
         assert d.startswith("gemm_fast_128x128 ") and "ksplit 2" in d, (M, N, K, ab, d)
     assert "ksplit" not in tge.Plan(2048, 2048, 3072).describe()
+    # from 128 slabs the 256-wide tiles' split (chunks of 32 slabs)
+    d = tge.Plan(2048, 2048, 8192).describe()
+    assert d.startswith("gemm_fast_256x256 ") and "ksplit 4" in d, d
     # fewer 128x128 tiles than CUs and at least 48 slabs: those tiles split K instead (about one
     # workgroup per CU, chunks of at least 4 slabs)
     for (M, N, K, lay, ab, cd, S) in [(1024, 1024, 8192, "NT", "bf16", "f32", 4), (512, 512, 8192, "NN", "f16", "f16", 16),
@@ -428,7 +431,9 @@ def test_fast_k_split_described():
     assert "gemm_skinny" in tge.Plan(16, 4096, 4096, "N", "N").describe()
     # an operand off the 16-byte grid is copied first, then split as well
     d = tge.Plan(2048, 2048, 8192, "N", "N", 8193, 2048, 2048).describe()
-    assert "ksplit 2" in d and "repack A" in d, d
+    assert "ksplit 4" in d and "repack A" in d, d
+    d = tge.Plan(2048, 2048, 4096, "N", "N", 4097, 2048, 2048).describe()
+    assert d.startswith("gemm_fast_128x128 ") and "ksplit 2" in d and "repack A" in d, d
     d = tge.Plan(2048, 3072, 4096, "N", "N", 4097, 3072, 3072).describe()
     assert d.startswith("gemm_fast_256x256 ") and "ksplit 2" in d and "repack A" in d, d
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", algo="nosplit").describe()

@@ -711,15 +711,15 @@ def test_fast_k_split_graph_capture(monkeypatch):
 
 @pytest.mark.parametrize("lay", ["NN", "TT"])
 def test_fast_k_split_full_size_points(lay):
-    # the plan's own choice at 2048 x 2048 x 8192 (256 tiles of 128x128, K split in two) and
-    # 2048 x 3072 x 8192 (96 tiles of 256x256, K split in two), random fp16 inputs, bias + ReLU:
+    # the plan's own choice at 2048 x 2048 x 8192 (64 tiles of 256x256, K split 4 ways) and
+    # 2048 x 2048 x 4096 (256 tiles of 128x128, K split in two), random fp16 inputs, bias + ReLU:
     # sampled outputs against the oracle's per-point reference
-    N, kern = (2048, "gemm_fast_128x128 ") if lay == "NN" else (3072, "gemm_fast_256x256 ")
-    p = synth.Problem(2048, N, 8192, lay[0], lay[1], "f16", "f16", "bias_relu", 1.0, 0.0,
+    K, kern, split = (8192, "gemm_fast_256x256 ", "ksplit 4") if lay == "NN" else (4096, "gemm_fast_128x128 ", "ksplit 2")
+    p = synth.Problem(2048, 2048, K, lay[0], lay[1], "f16", "f16", "bias_relu", 1.0, 0.0,
                       key=(129, lay == "TT"))
     x = synth.make_inputs(p)
     D, pl = run(p, x)
-    assert pl.describe().startswith(kern) and "ksplit 2" in pl.describe(), pl.describe()
+    assert pl.describe().startswith(kern) and split in pl.describe(), pl.describe()
     check_points(p, x, D)
 
 

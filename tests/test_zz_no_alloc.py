@@ -60,7 +60,7 @@ ROUTES = {
                      "gemm_skinny", " ksplit "),
     "fast_split": (((2560, 2560, 8192), "NT", "f16", "f16"), ((2048, 3072, 4096), "NN", "bf16", "f32"),
                    "gemm_fast_256x256", " ksplit "),
-    "fast128_split": (((2048, 2048, 8192), "NN", "f16", "f16"), ((1024, 1024, 8192), "NT", "bf16", "f32"),
+    "fast128_split": (((2048, 2048, 4096), "NN", "f16", "f16"), ((1024, 1024, 8192), "NT", "bf16", "f32"),
                       "gemm_fast_128x128", " ksplit "),
     "short_int8_split": (((64, 8192, 4096), "NT", "i8", "i32"), ((16, 4096, 2048), "NN", "i8", "i32"),
                          "gemm_fast_128x128", " ksplit "),

@@ -310,10 +310,12 @@ static bool copy128_pays(int64_t M, int64_t N, int64_t K, int64_t nprod) {
 // 8192 73.2 -> 32.2, int8 512^2 x 6144 20.1 -> 16.6; 256 x 2048 x 3072 is the one 48-slab
 // case measured slower (19.9 vs 20.5 us).  At 32 slabs the results are mixed (128 x 4096 x
 // 2048 15.0 vs 18.8 us, 640^2 x 2048 14.7 vs 16.2; 1024^2 x 2048 23.0 vs 21.3): unsplit.
-// Exactly one 128x128 tile per CU splits in two (two workgroups per CU) from 64 slabs: 2048^2 x
-// 4096 56.7 -> 50.5 us (256-wide split 4 ways), bf16 -> fp32 55.0 -> 48.3, int8 2048^2 x 8192
-// 56.0 -> 49.2; 2048^2 x 8192 76.5 vs 76.1 (even); at 48 slabs unsplit (2048^2 x 3072 37.2 vs
-// 41.3), and with more tiles the 256-wide tiles stay ahead (2048 x 3072 x 4096 65.6 vs 74.5).
+// Exactly one 128x128 tile per CU splits in two (two workgroups per CU) from 64 slabs, where the
+// 256-wide tiles' split would cut chunks shorter than 32 slabs: 2048^2 x 4096 56.7 -> 50.5 us
+// (256-wide split 4 ways), bf16 -> fp32 55.0 -> 48.3, int8 2048^2 x 8192 56.0 -> 49.2; from 128
+// slabs even (2048^2 x 8192 76.5 vs 76.1: the 256-wide split stays); at 48 slabs unsplit
+// (2048^2 x 3072 37.2 vs 41.3), and with more tiles the 256-wide tiles stay ahead (2048 x 3072 x
+// 4096 65.6 vs 74.5).
 // Short products (M <= 64) the skinny kernel cannot take (int8 inputs, or A transposed) split
 // from 8 slabs, as they did on the 256-wide tiles: 256-wide split -> 128-wide split, int8 16 x
 // 4096 x 4096 17.1 -> 10.2 us, 64 x 8192 x 4096 NT 24.9 -> 16.0, 32 x 4096 x 8192 NT 21.2 ->
@@ -322,7 +324,7 @@ static bool copy128_pays(int64_t M, int64_t N, int64_t K, int64_t nprod) {
 static bool split128_pays(int64_t M, int64_t N, int64_t slabs, bool skinny_cannot) {
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (M <= 64) return skinny_cannot && t128 < 256 && slabs >= 8;
-    return (t128 < 256 && slabs >= SPLIT128_MIN_SLABS) || (t128 == 256 && slabs >= 64);
+    return (t128 < 256 && slabs >= SPLIT128_MIN_SLABS) || (t128 == 256 && slabs >= 64 && slabs < 128);
 }
 
 struct Scratch {
