@@ -437,6 +437,10 @@ def test_fast_k_split_described():
     d = tge.Plan(2048, 3072, 4096, "N", "N", 4097, 3072, 3072).describe()
     assert d.startswith("gemm_fast_256x256 ") and "ksplit 2" in d and "repack A" in d, d
     assert "ksplit" not in tge.Plan(2048, 2048, 8192, "N", "N", algo="nosplit").describe()
+    # the plan's own choice of kernel and tile otherwise
+    for (M, N, K) in [(2048, 2048, 2048), (512, 512, 8192), (8192, 8192, 8192)]:
+        d_auto, d_ns = tge.Plan(M, N, K).describe(), tge.Plan(M, N, K, algo="nosplit").describe()
+        assert d_ns.split(" grid ")[0] == d_auto.split(" grid ")[0] and "ksplit" not in d_ns, (d_auto, d_ns)
 
 
 def test_noalloc_rejects_runs_beyond_the_scratch_before_any_device_call():

@@ -836,6 +836,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // an explicit algorithm in the description (gemm_algo_t) overrides the choices below
     const int algo = desc->algo;
     const bool staged = algo == GEMM_ALGO_FAST_STAGED;
+    // the plan's own choice of kernel and tile (GEMM_ALGO_NOSPLIT: the same without a K split)
+    const bool own = algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_NOSPLIT;
     // the fast kernel does ~3x the work per CU-round of the general 128x128 kernel: take it
     // when its rounds of 256x256 tiles cost less than 3x as many rounds of 128x128 tiles
     const int64_t nb = nprod > 1 ? nprod : 1;
@@ -863,7 +865,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         !ctable && !diag_a && !diag_b && !desc->transform_a && !desc->transform_b &&
         K % slab_k == 0 && !staged &&
         algo != GEMM_ALGO_NOSPLIT && algo != GEMM_ALGO_GENERAL && algo != GEMM_ALGO_SKINNY &&
-        !(tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST))) {
+        !(tile == 128 && (own || algo == GEMM_ALGO_FAST))) {
         const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t slabs = K / slab_k;
         int64_t sp = tiles > 0 ? 256 / tiles : 0;
@@ -904,8 +906,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     const KernelEntry *fast128 = nullptr;
     if (f128t && direct_ok && !desc->transform_a && !desc->transform_b && !diag_a && !diag_b && !ctable &&
         algo != GEMM_ALGO_GENERAL && !split_s &&
-        ((tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST)) ||
-         (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod))))
+        ((tile == 128 && (own || algo == GEMM_ALGO_FAST)) || (tile == 0 && own && fast128_pays(M, N, nprod))))
         fast128 = f128t(op_a, op_b);
     if (fast128) fast = fast128;
     // products with fewer 128x128 tiles than CUs and a long K (short ones the skinny kernel
@@ -941,8 +942,8 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // products large enough to repay the copy
     const bool want128 = f128t && !diag_a && !diag_b && !ctable && algo != GEMM_ALGO_GENERAL &&
                          (split128 || split128_copy ||
-                          (!split_s && ((tile == 128 && (algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_FAST)) ||
-                                        (tile == 0 && algo == GEMM_ALGO_AUTO && fast128_pays(M, N, nprod) &&
+                          (!split_s && ((tile == 128 && (own || algo == GEMM_ALGO_FAST)) ||
+                                        (tile == 0 && own && fast128_pays(M, N, nprod) &&
                                          copy128_pays(M, N, K, nprod)))));
     // the register-staged variant takes every layout the direct loads cannot (odd leading
     // dimensions or strides, unaligned pointers, M/N-contiguous extents off the 16-byte grid)
@@ -987,7 +988,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         // large enough to repay the copy (GEMM_ALGO_FAST_KMAJOR: always; GEMM_ALGO_FAST: never)
         // (the 128x128 tiles run the 16x16 schedule on this layout in place)
         if (pk_tr && !need_a && (algo == GEMM_ALGO_FAST_KMAJOR ||
-                                 (algo == GEMM_ALGO_AUTO && !fast128 && !want128 && kmajor_pays(M, N, K, eab))))
+                                 (own && !fast128 && !want128 && kmajor_pays(M, N, K, eab))))
             pk_want = 1;
         // the copies obey the 32-bit offset limit of the kernels; the copy grid (workgroups of
         // 4 rows x 1 KiB) fits 31 bits
