@@ -51,7 +51,9 @@ int main() {
                             d.kind_a = (v == 7 && K == M) ? GEMM_OPERAND_DIAGONAL : GEMM_OPERAND_DENSE;
                             d.kind_b = GEMM_OPERAND_DENSE;
                             d.algo = (gemm_algo_t)(v % 8);
-                            d.tile = v == 6 ? 128 : 0;
+                            // tile 128 with NOSPLIT, and with SPLIT for half the shapes (the
+                            // 128x128 tiles' pinned K split)
+                            d.tile = (v == 6 || (v == 5 && (M + N) % 2 == 0)) ? 128 : 0;
                             gemm_plan_t p = nullptr;
                             const gemm_status_t st = gemm_plan_create_desc(&p, &d);
                             expect((st == GEMM_STATUS_SUCCESS) == (p != nullptr), "plan iff success");
