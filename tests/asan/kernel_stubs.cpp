@@ -78,6 +78,7 @@ const KernelEntry *skinny_f16_f16(int b, int m, int n) { return skinny(b, m, n);
 const KernelEntry *skinny_f16_f32(int b, int m, int n) { return skinny(b, m, n); }
 const KernelEntry *skinny_bf16_bf16(int b, int m, int n) { return skinny(b, m, n); }
 const KernelEntry *skinny_bf16_f32(int b, int m, int n) { return skinny(b, m, n); }
+const KernelEntry *skinny_i8_i32(int b, int m, int n) { return b == 1 ? skinny(b, m, n) : nullptr; }
 const KernelEntry *complex_cf16_cf32(int a, int b) { return cplx(a, b); }
 const KernelEntry *complex_cf16_cf16(int a, int b) { return cplx(a, b); }
 const KernelEntry *complex_df16_df32(int a, int b) { return cplx(a, b); }

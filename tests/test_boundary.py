@@ -425,6 +425,17 @@ def test_fast_k_split_described():
     # ... and short 16-bit products with A transposed (the skinny kernel needs A not transposed)
     d = tge.Plan(16, 4096, 4096, "T", "N").describe()
     assert d.startswith("gemm_fast_128x128 ") and "ksplit 8" in d, d
+    # int8 with B transposed up to 32 rows: the memory-bound kernel (int32 partial sums when it
+    # splits K; a batch runs unsplit)
+    d = tge.Plan(16, 4096, 4096, "N", "T", ab="i8", cd="i32").describe()
+    assert d.startswith("gemm_skinny_m16_n16 "), d
+    d = tge.Plan(32, 8192, 4096, "N", "T", ab="i8", cd="i32").describe()
+    assert d.startswith("gemm_skinny_m32 ") and "ksplit 2" in d, d
+    d = tge.Plan(40, 8192, 4096, "N", "T", ab="i8", cd="i32").describe()
+    assert d.startswith("gemm_fast_128x128 ") and " ksplit " in d, d
+    d = tge.Plan(32, 4096, 4096, "N", "T", ab="i8", cd="i32", batch=3, stride_a=32 * 4096,
+                 stride_b=0, stride_c=32 * 4096, stride_bias=0).describe()
+    assert d.startswith("gemm_skinny") and "ksplit" not in d, d
     # the 256-wide tiles' split of short products, pinned: chunks down to 2 slabs
     d = tge.Plan(16, 4096, 4096, "N", "N", ab="i8", cd="i32", algo="split").describe()
     assert "gemm_fast_256x256 " in d and " ksplit " in d, d

@@ -648,8 +648,12 @@ def test_fast_k_split_short_int8_exact(lay, shape):
     x = synth.make_inputs(p)
     print(p.label(), flush=True)
     D, pl = run(p, x)
-    assert pl.describe().startswith("gemm_fast_128x128 ") and " ksplit " in pl.describe() + " ", \
-        pl.describe()
+    if lay == "NT" and M <= 32:
+        # B transposed, up to 32 rows: the memory-bound kernel takes it
+        assert pl.describe().startswith("gemm_skinny"), pl.describe()
+    else:
+        assert pl.describe().startswith("gemm_fast_128x128 ") and " ksplit " in pl.describe() + " ", \
+            pl.describe()
     check(p, x, D, reference(p, x), exact=True)
 
 

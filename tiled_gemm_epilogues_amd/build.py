@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libtge.so")
 
 PAIRS = ["F32_F32", "F16_F16", "F16_F32", "BF16_BF16", "BF16_F32", "I8_I32"]
 FAST_PAIRS = ["F16_F16", "F16_F32", "BF16_BF16", "BF16_F32", "I8_I32"]
-SKINNY_PAIRS = ["F16_F16", "F16_F32", "BF16_BF16", "BF16_F32"]
+SKINNY_PAIRS = ["F16_F16", "F16_F32", "BF16_BF16", "BF16_F32", "I8_I32"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -155,6 +155,7 @@ SkinnyLookup skinny_table(int ab, int cd) {
     if (ab == GEMM_F16 && cd == GEMM_F32) return tge::skinny_f16_f32;
     if (ab == GEMM_BF16 && cd == GEMM_BF16) return tge::skinny_bf16_bf16;
     if (ab == GEMM_BF16 && cd == GEMM_F32) return tge::skinny_bf16_f32;
+    if (ab == GEMM_I8 && cd == GEMM_I32) return tge::skinny_i8_i32;
     return nullptr;
 }
 
@@ -1013,12 +1014,18 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     // skinny path: M <= 64, memory bound; preferred over both tiled kernels when it applies
     bool skinny = false;
     SkinnyLookup st = skinny_table(ab_type, cd_type);
-    bool want_skinny = M <= 64;
+    // int8 (B transposed) up to 32 rows: from 64 the 128x128 tiles' K split measured as fast
+    // (int8 NT, cache-hot, skinny vs split: 16 x 4096 x 4096 8.3 vs 10.1 us, 16 x 4096 x 1024 4.1
+    // vs 8.5, 32 x 4096 x 8192 12.7 vs 13.8, 5 x 1000 x 2048 6.7 vs 8.5, 16 x 16384 x 4096 15.8
+    // vs 18.7; 64 x 8192 x 4096 16.8 vs 16.2, 64 x 1024 x 2048 9.7 vs 9.0)
+    bool want_skinny = M <= (ab_type == GEMM_I8 ? 32 : 64);
     if (algo == GEMM_ALGO_GENERAL) want_skinny = false;
     if (algo == GEMM_ALGO_FAST || algo == GEMM_ALGO_FAST_KMAJOR || staged || force_split) want_skinny = false;
     if (algo == GEMM_ALGO_SKINNY) want_skinny = true;
-    if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % 32 == 0 &&
-        (lda * 2) % 16 == 0 && (ldb * 2) % 16 == 0 && strides16 && (op_b == GEMM_OP_T || N % 8 == 0)) {
+    // (K in whole 64-byte chunks; int8 inputs with B transposed only)
+    if (st && want_skinny && M >= 1 && M <= 64 && op_a == GEMM_OP_N && K % (64 / eab) == 0 &&
+        (lda * eab) % 16 == 0 && (ldb * eab) % 16 == 0 && strides16 &&
+        (op_b == GEMM_OP_T || (eab == 2 && N % 8 == 0))) {
         // B transposed, M <= 16: 16-column blocks when they make one round of 192 to 256
         // workgroups and the 64-column ones would need a k split (no partial sums, no second
         // kernel).  Each narrow block reads as many bytes of A as of B, so larger M, or a
@@ -1027,8 +1034,11 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         const int64_t nblk = ((N + 15) / 16) * nbk;
         const bool narrow = op_b == GEMM_OP_T && M <= 16 && ((N + 63) / 64) * nbk < 256 &&
                             nblk >= 192 && nblk <= 256;
-        fast = st(op_b, (int)((M + 15) / 16), narrow ? 1 : 0);
-        skinny = fast != nullptr;
+        const KernelEntry *sk = st(op_b, (int)((M + 15) / 16), narrow ? 1 : 0);
+        if (sk) {
+            fast = sk;
+            skinny = true;
+        }
     }
 
     // complex and dual numbers where the real fast kernels apply: the product as a real fp16
@@ -1120,12 +1130,14 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     p->cv_dev = -1;
     p->cv_ws = nullptr;
     // (an empty problem, N == 0 or a batch of 0, launches nothing and is never split)
-    if (skinny && fast->bn == 64 && N > 0 && nprod > 0 && algo != GEMM_ALGO_NOSPLIT) {
+    // (int8: one product, whose int32 partial sums the integer finishing kernel adds)
+    if (skinny && fast->bn == 64 && N > 0 && nprod > 0 && algo != GEMM_ALGO_NOSPLIT &&
+        !(ab_type == GEMM_I8 && nprod > 1)) {
         // split K over workgroups until there is about one workgroup per CU, keeping at least
-        // eight 32-deep chunks per wave
+        // eight 64-byte chunks per wave
         const int64_t blocks = ((N + 63) / 64) * (nprod > 1 ? nprod : 1);
         int64_t sp = (256 + blocks - 1) / blocks;
-        const int64_t most = K / 32 / 32;
+        const int64_t most = K / (64 / eab) / 32;
         if (sp > most) sp = most;
         if (sp > 64) sp = 64;
         p->ksplit = sp > 1 ? (int)sp : 1;

@@ -148,8 +148,9 @@ const KernelEntry *complex_df16_df32(int op_a, int op_b);
 const KernelEntry *complex_df16_df16(int op_a, int op_b);
 
 // Memory-bound path for M <= 64 (gemm_skinny.hip); mt = ceil(M / 16).  Preconditions: 16-bit
-// inputs, op_a == N, K % 32 == 0, 16-byte aligned A/B pointers and leading dimensions,
-// N % 8 == 0 when B is not transposed.  One workgroup per bn (64) columns and k split: the
+// inputs, or int8 inputs with B transposed (op_b == T); op_a == N, K a whole number of 64-byte
+// chunks (K % 32 == 0 for 16-bit inputs, K % 64 == 0 for int8), 16-byte aligned A/B pointers and
+// leading dimensions, N % 8 == 0 when B is not transposed.  One workgroup per bn (64) columns and k split: the
 // launch sets tiles_m = S (k splits), tiles_n = ceil(N / bn), grid = S * tiles_n * batch, and
 // with S > 1 passes the workspace ws (batch * S * M * N floats); the entry then enqueues a
 // second, finishing kernel.  narrow = 1 (B transposed only): 16 columns per workgroup, S = 1.
@@ -157,6 +158,7 @@ const KernelEntry *skinny_f16_f16(int op_b, int mt, int narrow);
 const KernelEntry *skinny_f16_f32(int op_b, int mt, int narrow);
 const KernelEntry *skinny_bf16_bf16(int op_b, int mt, int narrow);
 const KernelEntry *skinny_bf16_f32(int op_b, int mt, int narrow);
+const KernelEntry *skinny_i8_i32(int op_b, int mt, int narrow);   // op_b == T only; S > 1: one product
 
 // The finishing step alone: D = epilogue(sum over the p.tiles_m splits of ws, in split order),
 // ws laid out [product][split][M][N] floats; p otherwise as for the product (C, bias, ldc,

@@ -11,19 +11,22 @@
 //    16 output columns per workgroup instead, each of its rows still in whole lines: with
 //    enough such blocks to fill the chip the plan takes that narrow variant and no k split;
 //  * each wave streams its K range through a private ring of LDS slots with direct-to-LDS
-//    loads (no barriers inside the loop: a wave only waits for its own loads): per 32-wide k
-//    chunk, 4 KiB of B (32 k x 64 columns) and 1 KiB of A per 16 rows;
+//    loads (no barriers inside the loop: a wave only waits for its own loads): per k chunk of
+//    64 bytes (32 k of 16-bit inputs, 64 of int8), 4 KiB of B (64 columns) and 1 KiB of A per
+//    16 rows;
 //  * fragments: A (K-contiguous) and a transposed B with ds_read_b128, a non-transposed B with
-//    the transposing read ds_read_b64_tr_b16; MFMA 16x16x32 with fp32 accumulation;
+//    the transposing read ds_read_b64_tr_b16; MFMA 16x16x32 with fp32 accumulation (int8:
+//    16x16x64 with int32 accumulation, the same 16 bytes of k per lane and operand);
 //  * the four waves' partial sums are added through LDS; then either the fused epilogue
 //    (alpha, beta*C, bias[j], ReLU, convert) and the store, or, with S > 1, the workgroup's
 //    sums go to a workspace and a second small kernel adds the S splits in split order and
 //    applies the epilogue (the kernel boundary orders the two; no device-wide fences, which
 //    cost more than the whole product here).
 //
-// Preconditions (checked by the host): 16-bit inputs, op(A) = A (not transposed), M <= 64,
-// K % 32 == 0, A/B pointers and leading dimensions 16-byte aligned, N % 8 == 0 when B is not
-// transposed; with S > 1 a workspace of S * M * N floats per product of the batch.
+// Preconditions (checked by the host): 16-bit inputs, or int8 inputs with B transposed; op(A) =
+// A (not transposed), M <= 64, K a whole number of 64-byte chunks, A/B pointers and leading
+// dimensions 16-byte aligned, N % 8 == 0 when B is not transposed; with S > 1 a workspace of
+// S * M * N floats (int32 for int8) per product of the batch (one product for int8).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,10 +47,18 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 constexpr int NT = 256;
 constexpr int NB = 64;         // output columns per workgroup: whole 128-byte lines of a row of B
 constexpr int NB_NARROW = 16;  // output columns per workgroup of the narrow variant (B transposed)
-constexpr int KCH = 32;        // k per chunk (one MFMA step)
+// k per chunk (one MFMA step): 64 bytes of every row of A and of a transposed B
+template <class TI>
+constexpr int kch() { return 64 / TI::E; }
+
+// accumulators of one 16x16 MFMA tile: fp32, int32 for int8
+template <class TI>
+struct SkAcc { using type = f32x4; };
+template <>
+struct SkAcc<TI8> { using type = i32x4; };
 
 template <class TI>
-__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c);
+__device__ __forceinline__ typename SkAcc<TI>::type mma16(u32x4 a, u32x4 b, typename SkAcc<TI>::type c);
 template <>
 __device__ __forceinline__ f32x4 mma16<TF16>(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -55,6 +66,10 @@ __device__ __forceinline__ f32x4 mma16<TF16>(u32x4 a, u32x4 b, f32x4 c) {
 template <>
 __device__ __forceinline__ f32x4 mma16<TBF16>(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ i32x4 mma16<TI8>(u32x4 a, u32x4 b, i32x4 c) {
+    return TI8::mma16(a, b, c);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -91,6 +106,11 @@ __device__ __forceinline__ void wait_vm_atmost(int n) {
 template <class TI, class TO, int MT, bool BT, int CB>
 __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     static_assert(CB == NB || (CB == NB_NARROW && BT), "narrow blocks need rows of B along K");
+    static_assert(TI::E == 2 || BT, "int8: B transposed only (no transposing byte reads here)");
+    constexpr int ES = TI::E;                           // input element bytes
+    constexpr int KCH = kch<TI>();
+    constexpr bool INT = ES == 1;
+    using AV = typename SkAcc<TI>::type;
     constexpr int G = CB / 16;                          // 16-column groups (MFMA N tiles)
     constexpr int BCH = G;                              // 1 KiB loads per chunk of B (CB x 32 k)
     constexpr int DPC = BCH + MT;                       // load instructions per chunk
@@ -108,12 +128,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int per = p.tiles_m * p.tiles_n;
     const int prod = blockIdx.x / per;                  // product of the batch
-    const int lid = select_batch<2, (int)sizeof(typename TO::T)>(p, blockIdx.x, per);
+    const int lid = select_batch<ES, (int)sizeof(typename TO::T)>(p, blockIdx.x, per);
     const int S = p.tiles_m;
     const int split = lid / p.tiles_n, cb = lid - split * p.tiles_n;
     const int n0 = cb * CB;
-    const uint16_t *A = static_cast<const uint16_t *>(p.A);
-    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+    const uint8_t *A = static_cast<const uint8_t *>(p.A);
+    const uint8_t *B = static_cast<const uint8_t *>(p.B);
 
     // chunks [c0, c1) of this wave: the split's share of K, divided over the four waves
     const int nch_all = p.K / KCH;
@@ -138,7 +158,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         if constexpr (BT) {
             // B stored N x K: CB rows (n) of 64 B; instruction i -> rows 16i + lane/4
             const int n = min(n0 + 16 * i + (lane >> 2), p.N - 1);
-            voffB[i] = (uint32_t)(n * p.ldb + ((lane & 3) ^ sw64) * 8) * 2u;
+            voffB[i] = (uint32_t)(n * p.ldb * ES + ((lane & 3) ^ sw64) * 16);
         } else {
             // B stored K x N: 32 rows (k) of 128 B (whole lines); instruction i -> rows 8i + lane/8,
             // 8 columns per piece (columns past N read the last 8 valid ones: never stored)
@@ -151,16 +171,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     for (int t = 0; t < MT; ++t) {
         // A rows 16t + lane/4 (clamped) of the 64 B k chunk
         const int m = min(16 * t + (lane >> 2), p.M - 1);
-        voffA[t] = (uint32_t)(m * p.lda + ((lane & 3) ^ sw64) * 8) * 2u;
+        voffA[t] = (uint32_t)(m * p.lda * ES + ((lane & 3) ^ sw64) * 16);
     }
     auto issue = [&](int c, int slot) {
         const int k0 = c * KCH;
-        const uint16_t *bb = BT ? B + k0 : B + (size_t)k0 * p.ldb;
+        const uint8_t *bb = BT ? B + k0 * ES : B + (size_t)k0 * p.ldb * ES;
         const uint32_t dst = lring + (uint32_t)(slot * SLOT);
 #pragma unroll
         for (int i = 0; i < BCH; ++i) dma16(bb, voffB[i], dst + 1024u * i);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) dma16(A + k0, voffA[t], dst + 1024u * (BCH + t));
+        for (int t = 0; t < MT; ++t) dma16(A + k0 * ES, voffA[t], dst + 1024u * (BCH + t));
     };
 
     // fragment read offsets inside a slot.  A chunk (16 rows x 64 B, row r at 64 r): lane l
@@ -179,11 +199,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         offB[g] = BT ? offA + 1024u * g
                      : (uint32_t)(rb * 128 + (((2 * g + ((lane & 3) >> 1)) ^ swb) * 16) + (lane & 1) * 8);
 
-    f32x4 acc[MT][G];
+    AV acc[MT][G];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < G; ++g) acc[t][g] = AV{0, 0, 0, 0};
 
     const int npro = min(DEPTH, nch);
     for (int c = 0; c < npro; ++c) issue(c0 + c, c);
@@ -215,9 +235,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
         for (int t = 0; t < MT; ++t) af[t] = *(const lds_u32x4 *)(uintptr_t)(sl + 1024u * (BCH + t) + offA);
         // load transforms (no-ops when disabled)
 #pragma unroll
-        for (int g = 0; g < G; ++g) bf[g] = zero_negative<2>(bf[g], p.xform_b);
+        for (int g = 0; g < G; ++g) bf[g] = zero_negative<ES>(bf[g], p.xform_b);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) af[t] = zero_negative<2>(af[t], p.xform_a);
+        for (int t = 0; t < MT; ++t) af[t] = zero_negative<ES>(af[t], p.xform_a);
         // the slot is refilled below: its reads must have returned first
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -231,14 +251,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     // theirs in LDS, then wave w adds up column group w in wave order (the narrow variant has
     // one group: wave 0 adds it, the others are done)
     __syncthreads();
-    f32x4 *part = reinterpret_cast<f32x4 *>(smem);    // [wave][MT][group][64 lanes]
+    AV *part = reinterpret_cast<AV *>(smem);          // [wave][MT][group][64 lanes]
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int g = 0; g < G; ++g) part[((wave * MT + t) * G + g) * 64 + lane] = acc[t][g];
     __syncthreads();
     if (wave >= G) return;
-    f32x4 sum[MT];
+    AV sum[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         sum[t] = part[((0 * MT + t) * G + wave) * 64 + lane];
@@ -251,7 +271,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     if (S > 1) {
         // split K: this split's sums to the workspace, for the finishing kernel
         if (n >= p.N) return;
-        float *ws = p.ws + ((int64_t)prod * S + split) * p.M * p.N;
+        using W = typename std::conditional<INT, int, float>::type;
+        W *ws = reinterpret_cast<W *>(p.ws) + ((int64_t)prod * S + split) * p.M * p.N;
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -265,9 +286,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_skinny(GemmParams p) {
     // epilogue
     using T = typename TO::T;
     if (n >= p.N) return;
-    const float bv = p.has_bias ? static_cast<const float *>(p.bias)[n] : 0.0f;
     const T *C = static_cast<const T *>(p.C);
     T *D = static_cast<T *>(p.D);
+    if constexpr (INT) {
+        // int32: acc + C (beta 0 or 1) + bias[n], wrapping as two's complement; then ReLU
+        const uint32_t bi = p.has_bias ? (uint32_t)static_cast<const int *>(p.bias)[n] : 0u;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * t + 4 * (lane >> 4) + r;
+                if (m >= p.M) continue;
+                const int64_t idx = (int64_t)m * p.ldc + n;
+                uint32_t x = (uint32_t)sum[t][r];
+                if (p.has_beta) x += (uint32_t)c_in_i((int)C[idx], p.xform_c);
+                x += bi;
+                int y = (int)x;
+                if (p.relu) y = y > 0 ? y : 0;
+                D[idx] = (T)y;
+            }
+        return;
+    }
+    const float bv = p.has_bias ? static_cast<const float *>(p.bias)[n] : 0.0f;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -350,7 +390,10 @@ hipError_t launch_finish(const GemmParams &p, hipStream_t s) {
 template <class TI, class TO, int MT, bool BT, int CB = NB>
 hipError_t launch_skinny(const GemmParams &p, unsigned grid, hipStream_t s) {
     hipLaunchKernelGGL((gemm_skinny<TI, TO, MT, BT, CB>), dim3(grid), dim3(NT), 0, s, p);
-    if (p.tiles_m > 1) return launch_finish<TO>(p, s);
+    if (p.tiles_m > 1) {
+        if constexpr (TI::E == 1) return finish_i8_i32(p, s);   // int32 partial sums
+        else return launch_finish<TO>(p, s);
+    }
     return hipGetLastError();
 }
 
@@ -358,24 +401,30 @@ hipError_t launch_skinny(const GemmParams &p, unsigned grid, hipStream_t s) {
 // narrow = 1: the 16-column variant (B transposed only)
 template <class TI, class TO>
 const KernelEntry *lookup_skinny(int op_b, int mt, int narrow) {
+    constexpr int KC = kch<TI>();
     static const KernelEntry nar[4] = {
-        {launch_skinny<TI, TO, 1, true, NB_NARROW>, 16, NB_NARROW, KCH, 1, 4, "gemm_skinny_m16_n16"},
-        {launch_skinny<TI, TO, 2, true, NB_NARROW>, 32, NB_NARROW, KCH, 1, 4, "gemm_skinny_m32_n16"},
-        {launch_skinny<TI, TO, 3, true, NB_NARROW>, 48, NB_NARROW, KCH, 1, 4, "gemm_skinny_m48_n16"},
-        {launch_skinny<TI, TO, 4, true, NB_NARROW>, 64, NB_NARROW, KCH, 1, 4, "gemm_skinny_m64_n16"}};
+        {launch_skinny<TI, TO, 1, true, NB_NARROW>, 16, NB_NARROW, KC, 1, 4, "gemm_skinny_m16_n16"},
+        {launch_skinny<TI, TO, 2, true, NB_NARROW>, 32, NB_NARROW, KC, 1, 4, "gemm_skinny_m32_n16"},
+        {launch_skinny<TI, TO, 3, true, NB_NARROW>, 48, NB_NARROW, KC, 1, 4, "gemm_skinny_m48_n16"},
+        {launch_skinny<TI, TO, 4, true, NB_NARROW>, 64, NB_NARROW, KC, 1, 4, "gemm_skinny_m64_n16"}};
     if (narrow) return (op_b == 1 && mt >= 1 && mt <= 4) ? &nar[mt - 1] : nullptr;
-    static const KernelEntry e[2][4] = {
-        {{launch_skinny<TI, TO, 1, false>, 16, NB, KCH, 1, 4, "gemm_skinny_m16"},
-         {launch_skinny<TI, TO, 2, false>, 32, NB, KCH, 1, 4, "gemm_skinny_m32"},
-         {launch_skinny<TI, TO, 3, false>, 48, NB, KCH, 1, 4, "gemm_skinny_m48"},
-         {launch_skinny<TI, TO, 4, false>, 64, NB, KCH, 1, 4, "gemm_skinny_m64"}},
-        {{launch_skinny<TI, TO, 1, true>, 16, NB, KCH, 1, 4, "gemm_skinny_m16"},
-         {launch_skinny<TI, TO, 2, true>, 32, NB, KCH, 1, 4, "gemm_skinny_m32"},
-         {launch_skinny<TI, TO, 3, true>, 48, NB, KCH, 1, 4, "gemm_skinny_m48"},
-         {launch_skinny<TI, TO, 4, true>, 64, NB, KCH, 1, 4, "gemm_skinny_m64"}},
-    };
     if (op_b < 0 || op_b > 1 || mt < 1 || mt > 4) return nullptr;
-    return &e[op_b][mt - 1];
+    static const KernelEntry t[4] = {
+        {launch_skinny<TI, TO, 1, true>, 16, NB, KC, 1, 4, "gemm_skinny_m16"},
+        {launch_skinny<TI, TO, 2, true>, 32, NB, KC, 1, 4, "gemm_skinny_m32"},
+        {launch_skinny<TI, TO, 3, true>, 48, NB, KC, 1, 4, "gemm_skinny_m48"},
+        {launch_skinny<TI, TO, 4, true>, 64, NB, KC, 1, 4, "gemm_skinny_m64"}};
+    if (op_b == 1) return &t[mt - 1];
+    if constexpr (TI::E == 1) {
+        return nullptr;   // int8 with B not transposed: not this kernel
+    } else {
+        static const KernelEntry n[4] = {
+            {launch_skinny<TI, TO, 1, false>, 16, NB, KC, 1, 4, "gemm_skinny_m16"},
+            {launch_skinny<TI, TO, 2, false>, 32, NB, KC, 1, 4, "gemm_skinny_m32"},
+            {launch_skinny<TI, TO, 3, false>, 48, NB, KC, 1, 4, "gemm_skinny_m48"},
+            {launch_skinny<TI, TO, 4, false>, 64, NB, KC, 1, 4, "gemm_skinny_m64"}};
+        return &n[mt - 1];
+    }
 }
 
 }  // namespace
@@ -392,8 +441,11 @@ hipError_t finish_bf16_bf16(const GemmParams &p, hipStream_t s) { return launch_
 #elif defined(TGE_PAIR_BF16_F32)
 const KernelEntry *skinny_bf16_f32(int b, int mt, int nw) { return lookup_skinny<TBF16, OF32>(b, mt, nw); }
 hipError_t finish_bf16_f32(const GemmParams &p, hipStream_t s) { return launch_finish<OF32>(p, s); }
+#elif defined(TGE_PAIR_I8_I32)
+// (B transposed only; the finishing step is finish_i8_i32)
+const KernelEntry *skinny_i8_i32(int b, int mt, int nw) { return lookup_skinny<TI8, OI32>(b, mt, nw); }
 #else
-#error "define one 16-bit TGE_PAIR_* macro"
+#error "define one TGE_PAIR_* macro"
 #endif
 
 }  // namespace tge
