@@ -163,7 +163,9 @@ typedef enum { GEMM_OPERAND_DENSE = 0, GEMM_OPERAND_DIAGONAL = 1 } gemm_operand_
  *   FAST_STAGED  the fast kernel, reading operands that are off the 16-byte grid in place
  *                through registers instead of copying them first;
  *   GENERAL      the general tiled kernel, never the fast, skinny or split routes;
- *   SKINNY       the memory-bound kernel for M <= 64 wherever its preconditions hold;
+ *   SKINNY       the memory-bound kernel for M <= 64 wherever its preconditions hold (op(A) = A,
+ *                16-byte aligned rows, K a whole number of 64-byte chunks; 16-bit inputs, or
+ *                int8 with B transposed);
  *   SPLIT        the fast kernel with K split into any number >= 2 of whole-slab chunks;
  *   NOSPLIT      the plan's own choice without a K split;
  *   FAST_KMAJOR  as FAST, and with A stored transposed and B not, A is first copied transposed
