@@ -911,10 +911,10 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
         fast128 = f128t(op_a, op_b);
     if (fast128) fast = fast128;
     // products with fewer 128x128 tiles than CUs and a long K (short ones the skinny kernel
-    // cannot take from 8 slabs) on those tiles with K split over workgroups: t128 tiles times S chunks (whole slabs, at least 4 each) of about one
-    // workgroup per CU; the partial sums are S * M * N fp32 values (int32 for int8)
-    // (operands the direct loads cannot read in place: the same split on their aligned copies,
-    // settled with the copies below)
+    // cannot take from 8 slabs) on those tiles with K split over workgroups: t128 tiles times
+    // S chunks (whole slabs, at least 4 each) of about one workgroup per CU; the partial sums
+    // are S * M * N fp32 values (int32 for int8).  Operands the direct loads cannot read in
+    // place: the same split on their aligned copies, settled with the copies below.
     int split128 = 0, split128_copy = 0;
     const Fast128Lookup f128p = fast128_table(ab_type, part_cd);
     const bool pin_split128 = tile == 128 && algo == GEMM_ALGO_SPLIT;
