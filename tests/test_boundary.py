@@ -395,7 +395,7 @@ def test_fast_k_split_described():
     # fewer 128x128 tiles than CUs and at least 48 slabs: those tiles split K instead (about one
     # workgroup per CU, chunks of at least 4 slabs)
     for (M, N, K, lay, ab, cd, S) in [(1024, 1024, 8192, "NT", "bf16", "f32", 4), (512, 512, 8192, "NN", "f16", "f16", 16),
-                                      (768, 768, 3072, "TN", "f16", "f16", 8), (288, 416, 7168, "NN", "f16", "f32", 16),
+                                      (768, 768, 3072, "TN", "f16", "f16", 6), (288, 416, 7168, "NN", "f16", "f32", 16),
                                       (512, 512, 6144, "NN", "i8", "i32", 12)]:
         d = tge.Plan(M, N, K, lay[0], lay[1], ab=ab, cd=cd).describe()
         assert d.startswith("gemm_fast_128x128 ") and f"ksplit {S}" in d, d

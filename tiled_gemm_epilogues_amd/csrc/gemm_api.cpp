@@ -307,7 +307,7 @@ static bool copy128_pays(int64_t M, int64_t N, int64_t K, int64_t nprod) {
 // 4096 53.8 -> 46.8, 1024^2 x 8192 39.4 -> 31.5, 1024 x 2048 x 8192 55.1 -> 51.9; (unsplit
 // 128-wide -> split) 256 x 1024 x 4096 25.0 -> 18.5, 512^2 x 8192 71.5 -> 21.2, 288 x 416 x
 // 7168 72.6 -> 16.5, 640^2 x 4096 41.8 -> 18.5, 1024^2 x 4096 41.1 -> 23.8, 2048 x 1024 x 4096
-// 40.1 -> 32.8, 768^2 x 3072 32.2 -> 22.3, 1024^2 x 3072 32.8 -> 23.5, bf16 -> fp32 1024^2 x
+// 40.1 -> 32.8, 768^2 x 3072 32.2 -> 20.9, 1024^2 x 3072 32.8 -> 23.5, bf16 -> fp32 1024^2 x
 // 8192 73.2 -> 32.2, int8 512^2 x 6144 20.1 -> 16.6; 256 x 2048 x 3072 is the one 48-slab
 // case measured slower (19.9 vs 20.5 us).  At 32 slabs the results are mixed (128 x 4096 x
 // 2048 15.0 vs 18.8 us, 640^2 x 2048 14.7 vs 16.2; 1024^2 x 2048 23.0 vs 21.3): unsplit.
@@ -912,7 +912,9 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
     if (fast128) fast = fast128;
     // products with fewer 128x128 tiles than CUs and a long K (short ones the skinny kernel
     // cannot take from 8 slabs) on those tiles with K split over workgroups: t128 tiles times
-    // S chunks (whole slabs, at least 4 each) of about one workgroup per CU; the partial sums
+    // S chunks (whole slabs, at least 4 each) of at most one workgroup per CU (more, and some
+    // CUs run two while the rest idle: fp16 768^2 x 4096 S = 8 23.9 us, S = 4 20.8; 768^2 x
+    // 3072 S = 8 22.6, S = 6 20.9; 640 x 896 x 4096 S = 8 22.6, S = 4 21.2); the partial sums
     // are S * M * N fp32 values (int32 for int8).  Operands the direct loads cannot read in
     // place: the same split on their aligned copies, settled with the copies below.
     int split128 = 0, split128_copy = 0;
@@ -925,7 +927,7 @@ gemm_status_t gemm_plan_create_desc(gemm_plan_t *out, const gemm_desc_t *desc) {
                           split128_pays(M, N, K / slab_k, ab_type == GEMM_I8 || op_a == GEMM_OP_T)))) {
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         const int64_t slabs = K / slab_k;
-        int64_t sp = (256 + t128 - 1) / t128;
+        int64_t sp = 256 / t128;
         if (sp < 2) sp = 2;
         if (sp > slabs / SHORT_M_MIN_CHUNK) sp = slabs / SHORT_M_MIN_CHUNK;
         while (sp > 1 && slabs % sp) --sp;
