@@ -399,6 +399,11 @@ def test_fast_k_split_described():
                                       (512, 512, 6144, "NN", "i8", "i32", 12)]:
         d = tge.Plan(M, N, K, lay[0], lay[1], ab=ab, cd=cd).describe()
         assert d.startswith("gemm_fast_128x128 ") and f"ksplit {S}" in d, d
+    # at most one workgroup per CU: S is the largest divisor of the slabs with tiles x S <= 256
+    for (M, N, K, S) in [(768, 768, 4096, 4), (640, 896, 4096, 4), (1536, 1024, 3072, 2), (512, 512, 8192, 16)]:
+        d = tge.Plan(M, N, K).describe()
+        t128 = ((M + 127) // 128) * ((N + 127) // 128)
+        assert f"ksplit {S}" in d and t128 * S <= 256, (M, N, K, d)
     # empty products with the split pinned plan without a split (no launch)
     for (M, N) in [(0, 512), (512, 0)]:
         assert "ksplit" not in tge.Plan(M, N, 4096, algo="split", tile=128).describe()
